@@ -1,0 +1,133 @@
+"""fp64 CPU oracle for the Gated DeltaNet forward.
+
+TEST INFRASTRUCTURE ONLY: ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the product package
+(``gated_deltanet_chunked_chunk_amd``) never does, and shares no code with it.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain C, double precision, one
+thread per (sequence, v-head) unit).  This module only compiles that file
+with gcc and marshals numpy arrays across ctypes.
+
+Functions and what pins them (tests under ``tests/test_oracle_*.py``):
+
+* ``fwd``            -- per-token gated delta rule (see the C file header).
+  Pinned by exact-rational brute force on tiny inputs, closed forms (single
+  token, beta = 0, strong decay, orthonormal-key retrieval, K = V = 1), an
+  independent chunked WY form, and invariants (split-call continuity,
+  varlen = separate calls, grouped heads = repeated heads, V-column
+  independence).
+* ``chunk_cumsum``   -- chunk-local running sum of g.  Pinned by constant-g
+  closed forms and by numpy's cumsum per chunk.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gdn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so next to its source (gcc, -O2, pthreads)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+               "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path: str):
+    """ctypes handle with the oracle's signatures bound (used by the pin tests to
+    load deliberately broken copies of the C source)."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.gdn_oracle_fwd.restype = ctypes.c_int
+    lib.gdn_oracle_fwd.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        P, P, P, P, P, ctypes.c_double, P, P, ctypes.c_int, P, P, ctypes.c_int]
+    lib.gdn_oracle_chunk_cumsum.restype = ctypes.c_int
+    lib.gdn_oracle_chunk_cumsum.argtypes = [
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def _f32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
+        output_final_state=True, n_threads=None, lib=None):
+    """Reference forward.  Shapes follow the pages' high-level API:
+    q, k [B,T,Hqk,K]; v [B,T,Hv,V]; g, beta [B,T,Hv]; initial_state
+    [N,Hv,K,V] (K x V = S^T); cu_seqlens int [N+1] (B must be 1).
+    Returns (o float64 [B,T,Hv,V], final_state float64 [N,Hv,K,V] or None).
+    """
+    q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
+    B, T, Hqk, K = q.shape
+    V = v.shape[-1]
+    Hv = v.shape[2]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise ValueError("oracle.fwd: inconsistent shapes")
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+    else:
+        cu = None
+        N = B
+    h0 = None if initial_state is None else _f32(initial_state)
+    if h0 is not None and h0.shape != (N, Hv, K, V):
+        raise ValueError("oracle.fwd: initial_state must be [N,Hv,K,V]")
+    if scale is None:
+        scale = K ** -0.5
+    o = np.zeros((B, T, Hv, V), dtype=np.float64)
+    ht = np.zeros((N, Hv, K, V), dtype=np.float64) if output_final_state else None
+    rc = (lib or _load()).gdn_oracle_fwd(B, T, Hqk, Hv, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                float(scale), _ptr(h0), _ptr(cu), N, _ptr(o), _ptr(ht),
+                                int(n_threads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle.fwd failed with code {rc}")
+    return o, ht
+
+
+def chunk_cumsum(g, chunk=64, cu_seqlens=None, lib=None):
+    """Chunk-local running sum of g [B,T,H] (float64 result)."""
+    g = _f32(g)
+    B, T, H = g.shape
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+    else:
+        cu, N = None, B
+    out = np.zeros((B, T, H), dtype=np.float64)
+    rc = (lib or _load()).gdn_oracle_chunk_cumsum(B, T, H, chunk, _ptr(g), _ptr(cu), N, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle.chunk_cumsum failed with code {rc}")
+    return out
