@@ -1,0 +1,165 @@
+"""Python entry points over libgdn.  Argument marshalling only: shapes, dtypes
+and devices are checked, outputs and the workspace are allocated with torch,
+and every step of the computation runs in the library's HIP kernels on the
+caller's current stream.
+
+The high-level signature follows the pages' API (aisparkup.com FlashQLA wiki,
+"high-level API"; summarylog.com essay, usage example):
+``chunk_gated_delta_rule(q, k, v, g, beta, scale, initial_state,
+output_final_state, cu_seqlens) -> (o, final_state)``.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+
+def _cu_host(cu_seqlens) -> Optional[torch.Tensor]:
+    if cu_seqlens is None:
+        return None
+    if isinstance(cu_seqlens, torch.Tensor):
+        # a device tensor needs one device-to-host copy for planning (a sync)
+        return cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    return torch.as_tensor(list(cu_seqlens), dtype=torch.int32)
+
+
+def make_desc(B, T, H_qk, H_v, K, V, *, scale, cu_host=None, has_h0=False, want_ht=False, o_dtype="bf16",
+              cp="auto", cp_lambda=0.0, cp_segment_chunks=0, cp_warmup_chunks=0, chunk=64) -> L.FwdDesc:
+    d = L.FwdDesc()
+    d.B, d.T, d.H_qk, d.H_v, d.K, d.V = int(B), int(T), int(H_qk), int(H_v), int(K), int(V)
+    if cu_host is not None:
+        d.num_seqs = int(cu_host.numel()) - 1
+        d.cu_seqlens_host = ctypes.cast(ctypes.c_void_p(cu_host.data_ptr()), ctypes.POINTER(ctypes.c_int32))
+    else:
+        d.num_seqs = int(B)
+        d.cu_seqlens_host = None
+    d.scale = float(scale)
+    d.has_h0 = int(bool(has_h0))
+    d.want_ht = int(bool(want_ht))
+    d.o_dtype = {"bf16": L.GDN_DTYPE_BF16, "f32": L.GDN_DTYPE_F32}[o_dtype]
+    d.chunk = int(chunk)
+    if cp not in L.CP_MODES:
+        raise ValueError(f"cp must be one of {sorted(L.CP_MODES)}")
+    d.cp_mode = L.CP_MODES[cp]
+    d.cp_lambda = float(cp_lambda)
+    d.cp_segment_chunks = int(cp_segment_chunks)
+    d.cp_warmup_chunks = int(cp_warmup_chunks)
+    return d
+
+
+def plan(desc: L.FwdDesc) -> dict:
+    """Host-only planning (no GPU needed): resolved CP layout and workspace size."""
+    info = L.FwdPlanInfo()
+    L.check(L.lib().gdn_fwd_plan(ctypes.byref(desc), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in L.FwdPlanInfo._fields_} | {"cp": L.CP_NAMES[info.cp_mode]}
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    buf = torch.empty(max(nbytes, 1) + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + max(nbytes, 1)]
+
+
+def _need(t: torch.Tensor, name: str, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                           beta: torch.Tensor, scale: Optional[float] = None,
+                           initial_state: Optional[torch.Tensor] = None, output_final_state: bool = False,
+                           cu_seqlens=None, *, cp: str = "auto", o_dtype: Optional[str] = None,
+                           cp_lambda: float = 0.0, cp_segment_chunks: int = 0, cp_warmup_chunks: int = 0,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Gated DeltaNet chunked-prefill forward on the GPU.
+
+    q, k: bf16 [B, T, H_qk, K]; v: bf16 [B, T, H_v, V]; g, beta: fp32 [B, T, H_v];
+    initial_state: fp32 [N, H_v, K, V] (S^T per head); cu_seqlens: int32 offsets
+    [N + 1] (B must be 1).  Returns (o [B, T, H_v, V], final_state or None).
+    ``cp`` selects the intra-GPU context parallelism: "auto", "warmup", "exact", "off".
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_gated_delta_rule runs on a GPU tensor; there is no CPU path")
+    _need(q, "q", torch.bfloat16, dev)
+    _need(k, "k", torch.bfloat16, dev)
+    _need(v, "v", torch.bfloat16, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
+        raise ValueError(f"bad shapes q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    B, T, Hqk, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    if g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise ValueError(f"g and beta must be [B, T, H_v] = {(B, T, Hv)}")
+    cu_host = _cu_host(cu_seqlens)
+    cu_dev = None
+    if cu_host is not None:
+        cu_dev = cu_seqlens if (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device == dev
+                                and cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()) \
+            else cu_host.to(dev)
+    N = (cu_host.numel() - 1) if cu_host is not None else B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, dev)
+        if initial_state.shape != (N, Hv, K, V):
+            raise ValueError(f"initial_state must be [N, H_v, K, V] = {(N, Hv, K, V)}")
+    if scale is None:
+        scale = K ** -0.5
+    if o_dtype is None:
+        o_dtype = "bf16"
+    desc = make_desc(B, T, Hqk, Hv, K, V, scale=scale, cu_host=cu_host, has_h0=initial_state is not None,
+                     want_ht=output_final_state, o_dtype=o_dtype, cp=cp, cp_lambda=cp_lambda,
+                     cp_segment_chunks=cp_segment_chunks, cp_warmup_chunks=cp_warmup_chunks)
+    info = plan(desc)
+    o_t = torch.float32 if o_dtype == "f32" else torch.bfloat16
+    if out is None:
+        out = torch.empty(B, T, Hv, V, dtype=o_t, device=dev)
+    else:
+        _need(out, "out", o_t, dev)
+    ht = torch.empty(N, Hv, K, V, dtype=torch.float32, device=dev) if output_final_state else None
+    if workspace is None or workspace.numel() < info["workspace_bytes"] or workspace.data_ptr() % 256:
+        workspace = _workspace(info["workspace_bytes"], dev)
+    ptrs = L.FwdPtrs(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                     initial_state.data_ptr() if initial_state is not None else None,
+                     cu_dev.data_ptr() if cu_dev is not None else None,
+                     out.data_ptr(), ht.data_ptr() if ht is not None else None)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        L.check(L.lib().gdn_fwd(ctypes.byref(desc), ctypes.byref(ptrs), ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel(), ctypes.c_void_p(stream)))
+    return out, ht
+
+
+def chunk_cumsum(g: torch.Tensor, chunk: int = 64, cu_seqlens=None, out: Optional[torch.Tensor] = None):
+    """Chunk-local running sum of g [B, T, H] (fp32), restarting at every chunk
+    and sequence start: the transformed g of the pages' low-level forward."""
+    dev = g.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_cumsum runs on a GPU tensor")
+    _need(g, "g", torch.float32, dev)
+    B, T, H = g.shape
+    cu_dev, N = None, B
+    if cu_seqlens is not None:
+        cu_dev = torch.as_tensor(cu_seqlens, dtype=torch.int32).to(dev).contiguous()
+        N = cu_dev.numel() - 1
+    if out is None:
+        out = torch.empty_like(g)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        L.check(L.lib().gdn_chunk_cumsum(ctypes.c_void_p(g.data_ptr()), ctypes.c_void_p(out.data_ptr()), B, T, H,
+                                         int(chunk), ctypes.c_void_p(cu_dev.data_ptr()) if cu_dev is not None
+                                         else None, N, ctypes.c_void_p(stream)))
+    return out
+
+
+__all__: Sequence[str] = ("chunk_gated_delta_rule", "chunk_cumsum", "plan", "make_desc")

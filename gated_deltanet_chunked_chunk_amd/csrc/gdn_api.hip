@@ -1,0 +1,288 @@
+// libgdn C ABI: argument validation, context-parallel planning, workspace
+// layout and kernel launches.  Planning is host-only and makes no HIP call.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+constexpr size_t kAlign = 256;
+
+struct Plan {
+    int64_t rows = 0;            // B * T
+    int32_t N = 0;
+    int32_t total_chunks = 0;
+    int32_t max_chunks = 0;
+    int32_t L = 1;
+    int32_t num_segments = 0;
+    int32_t cp_mode = GDN_CP_OFF;
+    int32_t warmup = 0;
+    size_t workspace = 0;
+};
+
+int32_t count_segments(const gdn_fwd_desc *d, int32_t L) {
+    int64_t total = 0;
+    if (d->cu_seqlens_host) {
+        for (int32_t n = 0; n < d->num_seqs; ++n)
+            total += gdn::seq_segments((int64_t)d->cu_seqlens_host[n + 1] - d->cu_seqlens_host[n], L);
+    } else {
+        total = (int64_t)d->B * gdn::seq_segments(d->T, L);
+    }
+    return total > INT32_MAX ? INT32_MAX : (int32_t)total;
+}
+
+// AUTO: pick L minimising (waves of workgroups over the CUs) x (L + expected
+// warm-up), assuming one resident workgroup per CU and a two-chunk warm-up.
+int32_t auto_segment_chunks(const gdn_fwd_desc *d, int32_t max_chunks) {
+    static const int32_t cands[] = {8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256};
+    int32_t bestL = std::max(1, max_chunks);
+    double best = (double)((int64_t)d->H_v * count_segments(d, bestL) + gdn::kNumCUs - 1) / gdn::kNumCUs;
+    best = std::ceil(best) * bestL;
+    for (int32_t L : cands) {
+        if (L >= max_chunks) break;
+        const double waves = std::ceil((double)d->H_v * count_segments(d, L) / gdn::kNumCUs);
+        const double cost = waves * (L + 2);
+        if (cost < best) {
+            best = cost;
+            bestL = L;
+        }
+    }
+    return bestL;
+}
+
+int make_plan(const gdn_fwd_desc *d, Plan *P) {
+    if (!d) return fail(GDN_EINVAL, "descriptor is NULL");
+    if (d->B < 0 || d->T < 0) return fail(GDN_EINVAL, "B and T must be >= 0 (got B=%lld T=%lld)", (long long)d->B,
+                                          (long long)d->T);
+    if (d->H_qk <= 0 || d->H_v <= 0) return fail(GDN_EINVAL, "H_qk and H_v must be > 0");
+    if (d->H_v % d->H_qk != 0)
+        return fail(GDN_EINVAL, "H_v (%d) must be a multiple of H_qk (%d)", d->H_v, d->H_qk);
+    if (d->K <= 0 || d->V <= 0) return fail(GDN_EINVAL, "K and V must be > 0");
+    if (d->o_dtype != GDN_DTYPE_BF16 && d->o_dtype != GDN_DTYPE_F32) return fail(GDN_EINVAL, "unknown o_dtype %d",
+                                                                                 d->o_dtype);
+    if (d->cp_mode < GDN_CP_OFF || d->cp_mode > GDN_CP_AUTO) return fail(GDN_EINVAL, "unknown cp_mode %d", d->cp_mode);
+    if (!(std::isfinite(d->scale))) return fail(GDN_EINVAL, "scale must be finite");
+    if (!(d->cp_lambda >= 0.f) || !std::isfinite(d->cp_lambda)) return fail(GDN_EINVAL, "cp_lambda must be >= 0");
+    if (d->cp_segment_chunks < 0) return fail(GDN_EINVAL, "cp_segment_chunks must be >= 0");
+    if (d->K != gdn::kDimK || d->V != gdn::kDimV)
+        return fail(GDN_EUNSUPPORTED, "only K = V = 128 is built (got K=%d V=%d)", d->K, d->V);
+    if (d->chunk != gdn::kChunk) return fail(GDN_EUNSUPPORTED, "only chunk = 64 is built (got %d)", d->chunk);
+    if (d->cp_mode == GDN_CP_EXACT) return fail(GDN_EUNSUPPORTED, "cp_mode EXACT is not built yet");
+    if (d->T > INT32_MAX || d->B > INT32_MAX) return fail(GDN_EINVAL, "B and T must fit in int32");
+
+    int64_t max_len = 0, total_chunks = 0;
+    if (d->cu_seqlens_host) {
+        if (d->B != 1) return fail(GDN_EINVAL, "cu_seqlens requires B == 1 (got B=%lld)", (long long)d->B);
+        if (d->num_seqs < 0) return fail(GDN_EINVAL, "num_seqs must be >= 0");
+        const int32_t *cu = d->cu_seqlens_host;
+        if (cu[0] != 0) return fail(GDN_EINVAL, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+        for (int32_t n = 0; n < d->num_seqs; ++n) {
+            if (cu[n + 1] < cu[n])
+                return fail(GDN_EINVAL, "cu_seqlens must be non-decreasing (cu[%d]=%d > cu[%d]=%d)", n, cu[n], n + 1,
+                            cu[n + 1]);
+            const int64_t len = (int64_t)cu[n + 1] - cu[n];
+            max_len = std::max(max_len, len);
+            total_chunks += gdn::seq_chunks(len);
+        }
+        if (cu[d->num_seqs] != d->T)
+            return fail(GDN_EINVAL, "cu_seqlens[-1] (%d) must equal T (%lld)", cu[d->num_seqs], (long long)d->T);
+    } else {
+        if (d->num_seqs != d->B)
+            return fail(GDN_EINVAL, "num_seqs (%d) must equal B (%lld) without cu_seqlens", d->num_seqs,
+                        (long long)d->B);
+        max_len = d->T;
+        total_chunks = d->B * (int64_t)gdn::seq_chunks(d->T);
+    }
+    if (total_chunks > INT32_MAX) return fail(GDN_EINVAL, "too many chunks");
+
+    P->rows = d->B * d->T;
+    P->N = d->num_seqs;
+    P->total_chunks = (int32_t)total_chunks;
+    P->max_chunks = gdn::seq_chunks(max_len);
+    P->warmup = d->cp_warmup_chunks > 0 ? d->cp_warmup_chunks : gdn::kDefaultWarmup;
+
+    int32_t mode = d->cp_mode;
+    int32_t L = std::max(1, P->max_chunks);
+    if (mode == GDN_CP_OFF) {
+        P->warmup = 0;
+    } else {
+        if (d->cp_segment_chunks > 0) {
+            L = d->cp_segment_chunks;
+        } else if (d->cp_lambda > 0.f) {
+            L = (int32_t)std::lround(d->cp_lambda * std::sqrt((double)P->max_chunks));
+        } else {
+            L = auto_segment_chunks(d, P->max_chunks);
+        }
+        L = std::max(1, std::min(L, std::max(1, P->max_chunks)));
+        if (mode == GDN_CP_AUTO) mode = GDN_CP_WARMUP;
+        if (L >= P->max_chunks) {
+            mode = GDN_CP_OFF;
+            P->warmup = 0;
+        }
+    }
+    P->L = L;
+    P->cp_mode = mode;
+    P->num_segments = count_segments(d, L);
+    if ((int64_t)P->num_segments * d->H_v > INT32_MAX) return fail(GDN_EINVAL, "grid too large");
+    P->workspace = 0;  // OFF / WARMUP keep everything on chip
+    return GDN_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char *gdn_status_str(int status) {
+    switch (status) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_EINVAL: return "GDN_EINVAL: invalid argument";
+        case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED: not supported by this build";
+        case GDN_EWORKSPACE: return "GDN_EWORKSPACE: workspace too small or misaligned";
+        case GDN_EHIP: return "GDN_EHIP: HIP runtime error";
+        default: return "unknown gdn status";
+    }
+}
+
+const char *gdn_last_error(void) { return g_last_error.c_str(); }
+
+int gdn_fwd_plan(const gdn_fwd_desc *d, gdn_fwd_plan_info *out) {
+    Plan P;
+    const int rc = make_plan(d, &P);
+    if (rc != GDN_OK) return rc;
+    if (out) {
+        out->workspace_bytes = P.workspace;
+        out->total_chunks = P.total_chunks;
+        out->segment_chunks = P.L;
+        out->num_segments = P.num_segments;
+        out->warmup_chunks = P.cp_mode == GDN_CP_WARMUP ? P.warmup : 0;
+        out->cp_mode = P.cp_mode;
+        out->workgroups = P.num_segments * d->H_v;
+    }
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_t workspace_bytes, void *stream) {
+    Plan P;
+    int rc = make_plan(d, &P);
+    if (rc != GDN_OK) return rc;
+    if (!p) return fail(GDN_EINVAL, "pointer struct is NULL");
+    const bool varlen = d->cu_seqlens_host != nullptr;
+    if (varlen != (p->cu_seqlens != nullptr))
+        return fail(GDN_EINVAL, "device cu_seqlens and host cu_seqlens_host must be given together");
+    if ((d->has_h0 != 0) != (p->initial_state != nullptr))
+        return fail(GDN_EINVAL, "initial_state pointer must be given iff has_h0");
+    if ((d->want_ht != 0) != (p->final_state != nullptr))
+        return fail(GDN_EINVAL, "final_state pointer must be given iff want_ht");
+
+    const size_t rows = (size_t)P.rows;
+    const size_t n_qk = rows * d->H_qk * d->K, n_v = rows * d->H_v * d->V, n_g = rows * d->H_v;
+    const size_t n_state = (size_t)d->num_seqs * d->H_v * d->K * d->V;
+    const size_t osz = d->o_dtype == GDN_DTYPE_F32 ? 4 : 2;
+    if (rows > 0) {
+        if (!p->q || !p->k || !p->v || !p->g || !p->beta || !p->o)
+            return fail(GDN_EINVAL, "q, k, v, g, beta and o must be non-NULL");
+        if (((uintptr_t)p->q | (uintptr_t)p->k | (uintptr_t)p->v) & 15)
+            return fail(GDN_EINVAL, "q, k and v must be 16-byte aligned");
+        if (((uintptr_t)p->g | (uintptr_t)p->beta) & 3) return fail(GDN_EINVAL, "g and beta must be 4-byte aligned");
+        if ((uintptr_t)p->o & (osz - 1)) return fail(GDN_EINVAL, "o is misaligned");
+    }
+    struct Buf { const void *ptr; size_t bytes; const char *name; };
+    const Buf in[] = {{p->q, n_qk * 2, "q"}, {p->k, n_qk * 2, "k"}, {p->v, n_v * 2, "v"},
+                      {p->g, n_g * 4, "g"}, {p->beta, n_g * 4, "beta"},
+                      {p->initial_state, n_state * 4, "initial_state"},
+                      {p->cu_seqlens, varlen ? (size_t)(d->num_seqs + 1) * 4 : 0, "cu_seqlens"},
+                      {workspace, P.workspace, "workspace"}};
+    for (const Buf &b : in) {
+        if (overlaps(p->o, n_v * osz, b.ptr, b.bytes)) return fail(GDN_EINVAL, "o overlaps %s", b.name);
+        if (overlaps(p->final_state, n_state * 4, b.ptr, b.bytes))
+            return fail(GDN_EINVAL, "final_state overlaps %s", b.name);
+    }
+    if (overlaps(p->o, n_v * osz, p->final_state, n_state * 4)) return fail(GDN_EINVAL, "o overlaps final_state");
+    if ((P.workspace > 0 && !workspace) || workspace_bytes < P.workspace)
+        return fail(GDN_EWORKSPACE, "workspace needs %zu bytes (got %zu at %p)", P.workspace, workspace_bytes,
+                    workspace);
+    if (P.workspace > 0 && ((uintptr_t)workspace & (kAlign - 1)))
+        return fail(GDN_EWORKSPACE, "workspace must be 256-byte aligned");
+
+    gdn::FwdParams fp{};
+    fp.q = (const uint16_t *)p->q;
+    fp.k = (const uint16_t *)p->k;
+    fp.v = (const uint16_t *)p->v;
+    fp.g = p->g;
+    fp.beta = p->beta;
+    fp.h0 = p->initial_state;
+    fp.cu = p->cu_seqlens;
+    fp.o = p->o;
+    fp.ht = p->final_state;
+    fp.T = d->T;
+    fp.rows = P.rows;
+    fp.B = (int32_t)d->B;
+    fp.N = d->num_seqs;
+    fp.Hqk = d->H_qk;
+    fp.Hv = d->H_v;
+    fp.group = d->H_v / d->H_qk;
+    fp.num_segments = P.num_segments;
+    fp.L = P.L;
+    fp.cp_mode = P.cp_mode;
+    fp.warmup_cap = P.warmup;
+    fp.o_f32 = d->o_dtype == GDN_DTYPE_F32;
+    fp.scale = d->scale;
+
+    if (P.num_segments == 0 || d->H_v == 0) {
+        g_last_error.clear();
+        return GDN_OK;
+    }
+    const int err = gdn::launch_fwd_main(fp, stream);
+    if (err) return fail(GDN_EHIP, "forward launch failed: %s", gdn::hip_error_text(err));
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+int gdn_chunk_cumsum(const float *g, float *out, int64_t B, int64_t T, int32_t H, int32_t chunk,
+                     const int32_t *cu_seqlens, int32_t num_seqs, void *stream) {
+    if (B < 0 || T < 0 || H <= 0) return fail(GDN_EINVAL, "bad shape B=%lld T=%lld H=%d", (long long)B,
+                                              (long long)T, H);
+    if (chunk <= 0) return fail(GDN_EINVAL, "chunk must be > 0");
+    if (cu_seqlens && B != 1) return fail(GDN_EINVAL, "cu_seqlens requires B == 1");
+    if (!cu_seqlens && num_seqs != B) return fail(GDN_EINVAL, "num_seqs must equal B without cu_seqlens");
+    if (B * T > 0 && (!g || !out)) return fail(GDN_EINVAL, "g and out must be non-NULL");
+    const size_t bytes = (size_t)(B * T * H) * 4;
+    if (out != g && overlaps(out, bytes, g, bytes)) return fail(GDN_EINVAL, "out partially overlaps g");
+    const int err = gdn::launch_chunk_cumsum(g, out, B, T, H, chunk, cu_seqlens, num_seqs, stream);
+    if (err) return fail(GDN_EHIP, "cumsum launch failed: %s", gdn::hip_error_text(err));
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+}  // extern "C"

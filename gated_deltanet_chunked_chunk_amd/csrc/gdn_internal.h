@@ -1,0 +1,64 @@
+// Internal declarations shared by the host planner (gdn_api.cpp) and the
+// kernels (gdn_fwd.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+constexpr int kChunk = 64;     // chunk length C
+constexpr int kDimK = 128;     // key/query head dim K
+constexpr int kDimV = 128;     // value head dim V
+constexpr int kNumCUs = 256;   // MI355X compute units (occupancy model of the AUTO planner)
+constexpr int kDefaultWarmup = 8;
+// ln(2^-24): once the summed log-gates of a warm-up window fall below this, the
+// zero-start state differs from the true one by less than fp32 resolution.
+constexpr float kLnNoiseFloor = -16.635532333438686f;
+
+// One context-parallel segment of one sequence: chunks [c_begin, c_begin + c_count).
+struct SegEntry {
+    int32_t n;         // sequence index (-1: no such segment)
+    int32_t c_begin;   // first chunk of the segment, counted from the sequence start
+    int32_t c_count;   // chunks in the segment (0 only for an empty sequence)
+    int32_t seq_len;   // tokens in the sequence
+    int64_t row0;      // row of the sequence's first token in the flattened [B*T] axis
+    int32_t last;      // 1 if this segment ends its sequence (writes final_state)
+    int32_t pad;
+};
+
+// Integer segment rule, identical on host and device: a sequence of `len`
+// tokens has ceil(len / C) chunks and max(1, ceil(chunks / L)) segments.
+__host__ __device__ inline int32_t seq_chunks(int64_t len) {
+    return (int32_t)((len + kChunk - 1) / kChunk);
+}
+__host__ __device__ inline int32_t seq_segments(int64_t len, int32_t L) {
+    const int32_t nt = seq_chunks(len);
+    const int32_t s = (nt + L - 1) / L;
+    return s > 0 ? s : 1;
+}
+
+struct FwdParams {
+    const uint16_t *q, *k, *v;   // bf16 bits
+    const float *g, *beta, *h0;
+    const int32_t *cu;           // device offsets or nullptr
+    void *o;
+    float *ht;
+    int64_t T;                   // tokens per batch row
+    int64_t rows;                // B * T
+    int32_t B, N, Hqk, Hv, group;
+    int32_t num_segments;
+    int32_t L;                   // segment length in chunks
+    int32_t cp_mode;             // resolved gdn_cp_mode
+    int32_t warmup_cap;
+    int32_t o_f32;
+    float scale;
+};
+
+// Launchers (gdn_fwd.hip).  Each returns the hipError_t of its launch as int.
+int launch_fwd_main(const FwdParams &p, void *stream);
+int launch_chunk_cumsum(const float *g, float *out, int64_t B, int64_t T, int32_t H, int32_t chunk,
+                        const int32_t *cu, int32_t N, void *stream);
+const char *hip_error_text(int err);
+
+}  // namespace gdn

@@ -1,0 +1,150 @@
+/*
+ * libgdn -- Gated DeltaNet chunked-prefill forward on AMD Instinct MI355X
+ * (gfx950).  Plain C ABI: no C++ or framework types cross it.
+ *
+ * The operation (FlashQLA pages, aisparkup.com wiki "high-level API" and
+ * "low-level API"; agentlenshq.com blog "GDN chunked-prefill optimisation"):
+ * for every sequence n and value head j, with key/query head
+ * i = j / (H_v / H_qk), run the gated delta rule
+ *
+ *     S_t = exp(g_t) S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = scale * S_t q_t
+ *
+ * from S_0 = initial_state (or zero) and return o and the final state.  The
+ * library evaluates it chunk by chunk (chunks of 64 tokens, WY form), with
+ * optional intra-GPU context parallelism (AutoCP, blog section "gate-driven
+ * automatic intra-card context parallelism": the chunk axis of a sequence is
+ * cut into segments of L chunks; a segment either starts from a state rebuilt
+ * by a short warm-up over the preceding chunks, whose influence decays with
+ * the gates, or from the exact state given by per-segment transition maps).
+ *
+ * Conventions for every entry point
+ *   - All tensors are dense, row-major, in device memory unless a field says
+ *     host.  Layouts (element types in brackets):
+ *        q, k   [B, T, H_qk, K]  (bf16)     v      [B, T, H_v, V] (bf16)
+ *        g, beta [B, T, H_v]      (fp32)     o      [B, T, H_v, V] (bf16 or fp32)
+ *        initial_state, final_state [N, H_v, K, V] (fp32), stored as S^T
+ *        cu_seqlens [N + 1] (int32): packed sequences, B must be 1
+ *   - The caller owns every buffer, including the workspace; the library
+ *     never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the null stream) and runs asynchronously.
+ *   - Inputs are read-only.  o must not overlap any input; final_state must
+ *     not overlap initial_state or any other tensor.
+ *   - Return value: GDN_OK (0) or a negative gdn_status.  Arguments are fully
+ *     validated before anything is enqueued, so a failed call launches
+ *     nothing.  gdn_last_error() gives a message for the calling thread's
+ *     last failure.  No exception crosses the ABI.
+ *   - NaN/Inf inputs propagate; they are not trapped.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_EINVAL = -1,        /* bad shape, pointer, offsets or aliasing */
+    GDN_EUNSUPPORTED = -2,  /* valid request this build does not implement (K, V, chunk) */
+    GDN_EWORKSPACE = -3,    /* workspace missing or smaller than gdn_fwd_plan asked for */
+    GDN_EHIP = -4           /* a HIP launch or query failed; message has the HIP text */
+} gdn_status;
+
+typedef enum { GDN_DTYPE_BF16 = 0, GDN_DTYPE_F32 = 1 } gdn_dtype;
+
+/* Intra-GPU context parallelism over the chunk axis.
+ *   OFF    one workgroup per (sequence, v-head) runs every chunk in order.
+ *   WARMUP segments of L chunks; a segment not at its sequence start first
+ *          runs the state pass (no output) from a zero state over up to
+ *          cp_warmup_chunks preceding chunks, stopping early once the summed
+ *          log-gates of the window fall below ln(2^-24) (the fp32 noise floor);
+ *          a window that reaches the sequence start begins from
+ *          initial_state and is then exact.  Approximate otherwise: the state
+ *          error is at most exp(sum of window gates) times the state norm.
+ *   EXACT  segments of L chunks; a pre-pass computes each segment's
+ *          zero-start state S and transition map M, a combine pass chains
+ *          H <- M H + S across segments, and the main pass starts every
+ *          segment from its exact state.
+ *   AUTO   WARMUP with L chosen from the occupancy of the GPU. */
+typedef enum { GDN_CP_OFF = 0, GDN_CP_EXACT = 1, GDN_CP_WARMUP = 2, GDN_CP_AUTO = 3 } gdn_cp_mode;
+
+typedef struct {
+    int64_t B;                  /* batch rows (1 when cu_seqlens is used) */
+    int64_t T;                  /* tokens per row (total packed tokens when varlen) */
+    int32_t H_qk, H_v;          /* key/query heads, value heads; H_v % H_qk == 0 */
+    int32_t K, V;               /* head dims; this build supports K = V = 128 */
+    int32_t num_seqs;           /* N: B, or len(cu_seqlens) - 1 when varlen */
+    const int32_t *cu_seqlens_host; /* host copy of the offsets, required for varlen planning; NULL otherwise */
+    float scale;                /* output scale (callers usually pass K^-1/2) */
+    int32_t has_h0;             /* initial_state given */
+    int32_t want_ht;            /* final_state requested */
+    int32_t o_dtype;            /* gdn_dtype of o */
+    int32_t chunk;              /* chunk length; must be 64 */
+    int32_t cp_mode;            /* gdn_cp_mode */
+    float cp_lambda;            /* >0: segment length L = round(lambda * sqrt(chunks of the longest sequence)) */
+    int32_t cp_segment_chunks;  /* >0: fixed L (overrides cp_lambda and AUTO) */
+    int32_t cp_warmup_chunks;   /* WARMUP/AUTO window cap; <=0 means 8 */
+} gdn_fwd_desc;
+
+typedef struct {
+    size_t workspace_bytes;     /* bytes gdn_fwd needs at `workspace` (256-byte aligned) */
+    int32_t total_chunks;       /* sum over sequences of ceil(len / chunk) */
+    int32_t segment_chunks;     /* L actually used (= longest sequence's chunk count when CP is off) */
+    int32_t num_segments;       /* segments over all sequences (per v-head) */
+    int32_t warmup_chunks;      /* window cap used by WARMUP/AUTO, 0 otherwise */
+    int32_t cp_mode;            /* resolved mode (AUTO becomes WARMUP or OFF) */
+    int32_t workgroups;         /* main-kernel workgroups = num_segments * H_v */
+} gdn_fwd_plan_info;
+
+typedef struct {
+    const void *q, *k, *v;          /* bf16 */
+    const float *g, *beta;          /* fp32 */
+    const float *initial_state;     /* fp32, NULL iff has_h0 == 0 */
+    const int32_t *cu_seqlens;      /* device offsets, NULL iff the call is not varlen */
+    void *o;                        /* bf16 or fp32 per o_dtype */
+    float *final_state;             /* fp32, NULL iff want_ht == 0 */
+} gdn_fwd_ptrs;
+
+/* ABI version this library was built with (GDN_ABI_VERSION). */
+int gdn_abi_version(void);
+
+/* Static text for a gdn_status value. */
+const char *gdn_status_str(int status);
+
+/* Message for the calling thread's most recent failure ("" if none). */
+const char *gdn_last_error(void);
+
+/* Host-only planning: validates the descriptor (shapes, offsets, support),
+ * resolves the context-parallel layout and sizes the workspace.  Makes no HIP
+ * call, so it works without a GPU.  `out` may be NULL (validation only). */
+int gdn_fwd_plan(const gdn_fwd_desc *d, gdn_fwd_plan_info *out);
+
+/* Forward pass: o and (optionally) final_state from the inputs in `p`.
+ * Re-plans `d` (same validation as gdn_fwd_plan), checks pointers and
+ * aliasing, then enqueues the kernels on `stream`.  `workspace` must hold at
+ * least gdn_fwd_plan's workspace_bytes and be 256-byte aligned; it may be NULL
+ * when that size is 0 (CP modes OFF, WARMUP and AUTO keep all intermediates
+ * on chip).  Its contents on entry do not matter and are scratch afterwards. */
+int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_t workspace_bytes,
+            void *stream);
+
+/* Chunk-local running sum of the log-gates (the transformed g returned by the
+ * pages' low-level forward, aisparkup.com wiki "low-level API"):
+ * out[t] = sum of g over the tokens of t's chunk up to and including t.
+ * Chunks of `chunk` tokens start at every sequence start.
+ * g, out: fp32 [B, T, H] device; cu_seqlens: device int32 [num_seqs + 1] or
+ * NULL (then num_seqs must equal B).  out may equal g (in place). */
+int gdn_chunk_cumsum(const float *g, float *out, int64_t B, int64_t T, int32_t H, int32_t chunk,
+                     const int32_t *cu_seqlens, int32_t num_seqs, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

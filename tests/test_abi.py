@@ -1,0 +1,135 @@
+"""CPU-side checks of the C ABI: the library loads, exports what include/gdn.h
+declares, and its host-only planner validates and plans without touching a
+GPU.  No compute entry point is called here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import gated_deltanet_chunked_chunk_amd as G
+from gated_deltanet_chunked_chunk_amd import _lib as L
+from gated_deltanet_chunked_chunk_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = L.lib()
+    declared = header_functions()
+    assert set(declared) == set(L.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    lib = L.lib()
+    assert lib.gdn_abi_version() == 1
+    for st in (0, -1, -2, -3, -4):
+        assert lib.gdn_status_str(st)
+    assert b"unknown" in lib.gdn_status_str(42)
+
+
+def desc(**kw):
+    base = dict(B=1, T=4096, H_qk=2, H_v=4, K=128, V=128)
+    base.update({k: kw.pop(k) for k in list(kw) if k in base})
+    kw.setdefault("scale", 128 ** -0.5)
+    return G.make_desc(base["B"], base["T"], base["H_qk"], base["H_v"], base["K"], base["V"], **kw)
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(H_v=3), L.GDN_EINVAL),
+    (dict(H_qk=0), L.GDN_EINVAL),
+    (dict(T=-1), L.GDN_EINVAL),
+    (dict(K=64), L.GDN_EUNSUPPORTED),
+    (dict(V=256), L.GDN_EUNSUPPORTED),
+    (dict(chunk=32), L.GDN_EUNSUPPORTED),
+    (dict(cp="exact"), L.GDN_EUNSUPPORTED),
+])
+def test_plan_rejects(bad, status):
+    d = desc(**bad)
+    info = L.FwdPlanInfo()
+    rc = L.lib().gdn_fwd_plan(ctypes.byref(d), ctypes.byref(info))
+    assert rc == status
+    assert L.lib().gdn_last_error()
+
+
+def test_plan_rejects_bad_cu_seqlens():
+    for cu, T in (([1, 5, 10], 10), ([0, 5, 4, 10], 10), ([0, 5, 9], 10)):
+        t = torch.tensor(cu, dtype=torch.int32)
+        d = desc(T=T, cu_host=t)
+        assert L.lib().gdn_fwd_plan(ctypes.byref(d), None) == L.GDN_EINVAL
+    t = torch.tensor([0, 5, 10], dtype=torch.int32)
+    d = desc(T=10, B=2, cu_host=t)
+    assert L.lib().gdn_fwd_plan(ctypes.byref(d), None) == L.GDN_EINVAL
+
+
+def test_plan_for_workloads():
+    d = desc(T=32768, H_qk=16, H_v=16)
+    p = G.plan(d)
+    assert p["total_chunks"] == 512 and p["cp"] == "warmup"
+    assert p["num_segments"] * p["segment_chunks"] >= 512
+    assert p["workgroups"] == p["num_segments"] * 16
+    d = desc(T=32768, H_qk=16, H_v=16, cp="off")
+    p = G.plan(d)
+    assert p["cp"] == "off" and p["num_segments"] == 1 and p["segment_chunks"] == 512
+    d = desc(T=32768, H_qk=2, H_v=8, cp="warmup", cp_segment_chunks=16)
+    p = G.plan(d)
+    assert p["num_segments"] == 32 and p["warmup_chunks"] == 8
+    d = desc(T=32768, H_qk=2, H_v=8, cp="warmup", cp_lambda=1.0)
+    assert G.plan(d)["segment_chunks"] == 23  # round(1.0 * sqrt(512))
+
+
+def test_plan_varlen_segments():
+    x = W.make_inputs(W.WORKLOADS["gdn_fwd_varlen16_65536_h8x24"], T=65536)
+    cu = x["cu_seqlens"]
+    d = desc(T=65536, H_qk=8, H_v=24, cu_host=cu, cp="warmup", cp_segment_chunks=16)
+    p = G.plan(d)
+    lens = (cu[1:] - cu[:-1]).tolist()
+    chunks = [-(-n // 64) for n in lens]
+    assert p["total_chunks"] == sum(chunks)
+    assert p["num_segments"] == sum(max(1, -(-c // 16)) for c in chunks)
+
+
+def test_plan_empty_and_zero_length():
+    t = torch.tensor([0, 0, 0], dtype=torch.int32)
+    d = desc(T=0, cu_host=t)
+    p = G.plan(d)
+    assert p["total_chunks"] == 0 and p["num_segments"] == 2  # one empty segment per sequence
+
+
+def test_fwd_validation_happens_before_any_launch():
+    """Invalid pointer sets fail in validation (no HIP call is reached)."""
+    lib = L.lib()
+    d = desc(T=128, has_h0=True, want_ht=True)
+    ws = ctypes.create_string_buffer(4096)
+    ptrs = L.FwdPtrs(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None, None, 0x6000, 0x7000)
+    # has_h0 without a pointer
+    assert lib.gdn_fwd(ctypes.byref(d), ctypes.byref(ptrs), ws, 4096, None) == L.GDN_EINVAL
+    # misaligned q
+    ptrs = L.FwdPtrs(0x1001, 0x2000, 0x3000, 0x4000, 0x5000, 0x8000, None, 0x6000, 0x7000)
+    assert lib.gdn_fwd(ctypes.byref(d), ctypes.byref(ptrs), ws, 4096, None) == L.GDN_EINVAL
+    # o overlapping v
+    base = 0x100000
+    ptrs = L.FwdPtrs(base, base * 2, base * 3, base * 4, base * 5, base * 6, None, base * 3 + 256, base * 8)
+    assert lib.gdn_fwd(ctypes.byref(d), ctypes.byref(ptrs), ws, 4096, None) == L.GDN_EINVAL
+    assert b"o overlaps v" in lib.gdn_last_error()
+    # final_state overlapping initial_state
+    ptrs = L.FwdPtrs(base, base * 2, base * 3, base * 4, base * 5, base * 6, None, base * 7, base * 6)
+    assert lib.gdn_fwd(ctypes.byref(d), ctypes.byref(ptrs), ws, 4096, None) == L.GDN_EINVAL
+    # device offsets without host offsets
+    ptrs = L.FwdPtrs(base, base * 2, base * 3, base * 4, base * 5, base * 6, base * 10, base * 7, base * 9)
+    assert lib.gdn_fwd(ctypes.byref(d), ctypes.byref(ptrs), None, 0, None) == L.GDN_EINVAL
+
+
+def test_python_api_refuses_cpu_tensors():
+    x = W.random_inputs(1, 64, 1, 1)
+    with pytest.raises(ValueError):
+        G.chunk_gated_delta_rule(x["q"], x["k"], x["v"], x["g"], x["beta"])
