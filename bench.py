@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Benchmark: GDN chunked-prefill forward on one MI355X.
+
+One step = one gdn_fwd call (the whole forward: every chunk of every v-head,
+o and final_state) over the 1 x 32768-token, 16 qk / 16 v-head workload, with
+inputs resident in HBM.  Prints ONE JSON line on stdout:
+
+  value        tokens per second over the timed steps (higher is better)
+  ms_per_step  mean latency of one forward
+  roofline     the forward kernel's algorithmic HBM bytes per launch over its
+               mean launch duration (HIP events on the launch stream), against
+               the 8 TB/s HBM peak; `traffic` = measured HBM bytes per launch
+               from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by a copy-kernel
+               calibration) when the stored counters match the current kernel
+               source, else null
+  cpu_baseline the fp64 oracle on a bounded prefix of the same workload, timed
+               on this host's cores
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+       [--cp auto|warmup|off] [--no-cpu-baseline] [--cpu-seconds 10]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# Pages' FlashQLA forward latency for this exact workload (1 x 32768, h_qk=16, h_v=16)
+# on an NVIDIA H200 (agentlenshq.com FlashQLA blog, benchmark table): context only.
+PAGES_MS = {"gdn_fwd_1x32768_h16x16": 0.493, "gdn_fwd_1x32768_h2x8": 0.310}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "gated_deltanet_chunked_chunk_amd", "csrc", f)
+                  for f in ("gdn_fwd.hip", "gdn_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(x) -> int:
+    """HBM bytes the forward must move at minimum: read q, k, v (bf16), g, beta
+    (fp32), initial_state (fp32) once; write o (bf16) and final_state (fp32) once."""
+    q, v, g = x["q"], x["v"], x["g"]
+    n = q.numel() * 2 * 2 + v.numel() * 2 * 2 + g.numel() * 4 * 2
+    if x["initial_state"] is not None:
+        n += x["initial_state"].numel() * 4 * 2  # h0 read + final_state write
+    return int(n)
+
+
+def stored_traffic(workload: str):
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload)
+    if not e or e.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(x, w, target_s: float):
+    import numpy as np  # noqa: F401
+    import oracle
+    from gated_deltanet_chunked_chunk_amd import workloads as W
+    threads = min(16, oracle.default_threads())
+    host = {k: W.to_f32_numpy(x[k]) for k in ("q", "k", "v", "g", "beta", "initial_state")}
+
+    def run(T):
+        t0 = time.perf_counter()
+        oracle.fwd(host["q"][:, :T], host["k"][:, :T], host["v"][:, :T], host["g"][:, :T], host["beta"][:, :T],
+                   scale=x["scale"], initial_state=host["initial_state"], n_threads=threads)
+        return time.perf_counter() - t0
+
+    t_cal = run(256)
+    T = int(min(w.T, max(256, 256 * target_s / max(t_cal, 1e-6))))
+    T = max(256, T // 64 * 64)
+    dt = run(T)
+    return {"value": T * w.B / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {T} of {w.T} tokens, all {w.H_v} v-heads, fp64 per-token recurrence, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gdn_fwd_1x32768_h16x16")
+    ap.add_argument("--cp", default="auto")
+    ap.add_argument("--o-dtype", default="bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (reference for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the forward shards over (sequence, head-group) "
+              "with no communication; see the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_deltanet_chunked_chunk_amd import PreparedForward
+    from gated_deltanet_chunked_chunk_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # a plain copy of known size: 1 GiB read + 1 GiB written per launch
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4}))
+        return
+
+    w = W.WORKLOADS[args.workload]
+    x = W.make_inputs(w, device=dev)
+    call = PreparedForward(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
+                           initial_state=x["initial_state"], output_final_state=w.want_ht,
+                           cu_seqlens=x["cu_seqlens"], cp=args.cp, o_dtype=args.o_dtype)
+    info = call.info
+    tokens = w.B * w.T if x["cu_seqlens"] is None else int(x["cu_seqlens"][-1])
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = sum(per_launch_ms) / len(per_launch_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    value = tokens / (ms_per_step * 1e-3)
+
+    alg = algorithmic_bytes(x)
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.workload),
+                "kernel": "gdn_fwd_main_kernel", "algorithmic_bytes_per_launch": alg,
+                "mean_launch_ms": round(kern_ms, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, w, args.cpu_seconds)
+
+    pages = PAGES_MS.get(args.workload)
+    line = {
+        "metric": "GDN fwd latency (ms) & tokens/s at 1x32768; % of HBM/MFMA roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": round(value / (tokens / (pages * 1e-3)), 3) if pages else None,
+        "dtype": "bf16", "data": "synthetic (seeded random q,k,v,g,beta,initial_state of the workload's shapes)",
+        "config": {"workload": args.workload, "B": w.B, "T": w.T, "H_qk": w.H_qk, "H_v": w.H_v, "K": w.K,
+                   "V": w.V, "cp": info["cp"], "segment_chunks": info["segment_chunks"],
+                   "workgroups": info["workgroups"], "o_dtype": args.o_dtype},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -116,6 +116,12 @@ int make_plan(const gdn_fwd_desc *d, Plan *P) {
         total_chunks = d->B * (int64_t)gdn::seq_chunks(d->T);
     }
     if (total_chunks > INT32_MAX) return fail(GDN_EINVAL, "too many chunks");
+    // each sequence of each head is read through one buffer resource whose
+    // byte range must stay below 2^31
+    const int64_t row_bytes = std::max<int64_t>((int64_t)d->H_qk * d->K * 2, (int64_t)d->H_v * d->V * 2);
+    if ((max_len + gdn::kChunk) * row_bytes >= ((int64_t)1 << 31))
+        return fail(GDN_EUNSUPPORTED, "a sequence of %lld tokens exceeds the 2 GiB per-sequence range",
+                    (long long)max_len);
 
     P->rows = d->B * d->T;
     P->N = d->num_seqs;
@@ -215,7 +221,7 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
         if (((uintptr_t)p->q | (uintptr_t)p->k | (uintptr_t)p->v) & 15)
             return fail(GDN_EINVAL, "q, k and v must be 16-byte aligned");
         if (((uintptr_t)p->g | (uintptr_t)p->beta) & 3) return fail(GDN_EINVAL, "g and beta must be 4-byte aligned");
-        if ((uintptr_t)p->o & (osz - 1)) return fail(GDN_EINVAL, "o is misaligned");
+        if ((uintptr_t)p->o & 15) return fail(GDN_EINVAL, "o must be 16-byte aligned");
     }
     struct Buf { const void *ptr; size_t bytes; const char *name; };
     const Buf in[] = {{p->q, n_qk * 2, "q"}, {p->k, n_qk * 2, "k"}, {p->v, n_v * 2, "v"},

@@ -21,18 +21,20 @@
 //
 // Precision (the pages' "restructure without losing precision", summarylog.com
 // essay, "formula restructuring"): products of two exact bf16 inputs (K K^T,
-// Q K^T, T K, Q H) use one bf16 MFMA; operands that carry fp32 values which
-// feed the output with full weight are split into hi + lo bf16 pairs:
-// T diag(beta), P, v', the decayed v', and H.  Decays and beta are applied as
-// fp32 row/column scales; every exponent is a non-positive difference
-// G_i - G_s (masked before the exp), so nothing overflows.
+// Q K^T, K^T T~^T, Q H) use one bf16 MFMA; operands that carry fp32 values
+// which feed the output with full weight are split into hi + lo bf16 pairs:
+// T diag(beta), P, v', the decayed v', and H.  Decays and beta are fp32
+// row/column scales; every exponent is a non-positive difference G_i - G_s
+// (masked before the exp), so nothing overflows.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16.  Lane l holds A row (l % 32) / B column
-// (l % 32), 8 k-slots for lane half (l / 32); accumulator element 4i + j holds
-// row 8i + 4(l/32) + j, column l % 32.  An accumulator tile read as a B operand
-// therefore sees, in k-step s, the k indices 16s + {4h..4h+3, 8+4h..8+4h+3}
-// (h = l/32); A operands that meet such a B are read from LDS with the same
-// permutation (two 8-byte reads per lane).
+// (l % 32), 8 k-slots for lane half h = l / 32; accumulator element 4i + j
+// holds row 8i + 4h + j, column l % 32.  An accumulator tile read as a B
+// operand therefore sees, in k-step s, the k indices 16s + {4h..4h+3,
+// 8+4h..8+4h+3}; A operands that meet such a B are read with the same
+// permutation.  W and P are produced transposed (W^T = K^T T~^T, P^T = K Q^T)
+// so that each lane's accumulator already is its A fragment for W H and P v';
+// those fragments go through LDS fragment-major (16 bytes per lane).
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
@@ -43,6 +45,8 @@ typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = kChunk;   // 64
 constexpr int DK = kDimK;    // 128
@@ -50,20 +54,22 @@ constexpr int DV = kDimV;    // 128
 constexpr int NTHREADS = 256;
 constexpr int KS = DK + 8;   // bf16 row stride of 128-wide tiles (272 B)
 constexpr int CS = CH + 8;   // bf16 row stride of 64-wide tiles (144 B)
-constexpr int AS = CH + 1;   // fp32 row stride of the 64 x 64 A / T tile
+constexpr int AS = CH + 4;   // fp32 row stride of the 64 x 64 A / T tile (16-byte aligned rows)
+constexpr int OS = 32 + 4;   // fp32 row stride of a wave's 64 x 32 output staging tile
 
 struct __attribute__((aligned(16))) Smem {
     bf16 k[CH * KS];       // K, row = token
-    bf16 kt[DK * CS];      // K^T, row = key dim
     bf16 q[CH * KS];       // Q
+    bf16 kt[DK * CS];      // K^T, row = key dim
     bf16 vt[DV * CS];      // V^T, row = value dim
-    bf16 w[CH * KS];       // -W
-    bf16 tt[CH * CS];      // T diag(beta gamma)
-    bf16 th[2][CH * CS];   // T diag(beta), hi and lo
-    bf16 p[2][CH * CS];    // P, hi and lo
-    float a[CH * AS];      // A, inverted in place into T
-    float scr[32 * 33];    // inverse scratch
-    float graw[CH], beta[CH], gcum[CH], gam[CH], dec[CH];
+    union {
+        float a[CH * AS];             // A, inverted in place into T
+        float ostage[4][CH * OS];     // per-wave output tile on its way to HBM
+    };
+    bf16x8 wf[2][8][64];              // -W as A fragments [row block][k step][lane]
+    bf16x8 pf[2][3][2][64];           // P as A fragments [hi, lo][tile][k step][lane]
+    float scr[2][16 * 17];            // inverse scratch, one per merging wave
+    float graw[CH], beta[CH], gcum[CH], gam[CH], dec[CH], bg[CH];
 };
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -93,67 +99,72 @@ __device__ __forceinline__ void split8(const f32x16 &acc, int s, bf16x8 &hi, bf1
     }
 }
 
-__device__ __forceinline__ float bf2f(uint16_t u) {
-    return __uint_as_float((uint32_t)u << 16);
+__device__ __forceinline__ void split8v(const float *x, bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bf16 h = (bf16)x[e];
+        hi[e] = h;
+        lo[e] = (bf16)(x[e] - (float)h);
+    }
 }
 
 // ---------------------------------------------------------------- chunk loads
+// Buffer resources span exactly one sequence of one head, so rows past the
+// sequence end come back as zeros (hardware range check): a partial last
+// chunk behaves as if padded with g = beta = 0, k = q = v = 0.
+struct Inputs {
+    __amdgpu_buffer_rsrc_t k, q, v, g, b;
+    unsigned kstride, vstride, gstride;  // bytes per token row
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 // Thread t stages rows 4*(t % 16) .. +3, columns 8*(t / 16) .. +7 of each
-// 64 x 128 tile (16-byte global loads; rows past the sequence end read as 0).
+// 64 x 128 tile (16-byte loads).
 struct Stage {
-    uint4 k[4], q[4], v[4];
+    u32x4 k[4], q[4], v[4];
     float g, b;
 };
 
-__device__ __forceinline__ void load_chunk(const FwdParams &p, Stage &st, int64_t row0, int c, int seq_len,
-                                           int i_qk, int j, bool need_q, const int t) {
+__device__ __forceinline__ void load_chunk(const Inputs &in, Stage &st, int c, bool need_q, int t) {
     const int rg = t & 15, cg = t >> 4;
-    const int tok0 = c * CH;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int tok = tok0 + 4 * rg + r;
-        if (tok < seq_len) {
-            const int64_t row = row0 + tok;
-            st.k[r] = *reinterpret_cast<const uint4 *>(p.k + (row * p.Hqk + i_qk) * DK + 8 * cg);
-            st.v[r] = *reinterpret_cast<const uint4 *>(p.v + (row * p.Hv + j) * DV + 8 * cg);
-            st.q[r] = need_q ? *reinterpret_cast<const uint4 *>(p.q + (row * p.Hqk + i_qk) * DK + 8 * cg)
-                             : make_uint4(0, 0, 0, 0);
-        } else {
-            st.k[r] = st.v[r] = st.q[r] = make_uint4(0, 0, 0, 0);
-        }
+        // offsets are unsigned: past the range they wrap to large values,
+        // which the range check also turns into zeros
+        const unsigned tok = (unsigned)(c * CH + 4 * rg + r);
+        st.k[r] = __builtin_amdgcn_raw_buffer_load_b128(in.k, (int)(tok * in.kstride + 16u * cg), 0, 0);
+        st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(in.v, (int)(tok * in.vstride + 16u * cg), 0, 0);
+        if (need_q) st.q[r] = __builtin_amdgcn_raw_buffer_load_b128(in.q, (int)(tok * in.kstride + 16u * cg), 0, 0);
     }
     if (t < CH) {
-        const int tok = tok0 + t;
-        if (tok < seq_len) {
-            const int64_t row = row0 + tok;
-            st.g = p.g[row * p.Hv + j];
-            st.b = p.beta[row * p.Hv + j];
-        } else {
-            st.g = 0.f;
-            st.b = 0.f;
-        }
+        const unsigned tok = (unsigned)(c * CH + t);
+        // the b32 loads return raw bits
+        st.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.g, (int)(tok * in.gstride), 0, 0));
+        st.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.b, (int)(tok * in.gstride), 0, 0));
     }
 }
 
-__device__ __forceinline__ uint16_t half_of(const uint4 &x, int e) {
-    const uint32_t w = (e < 2) ? x.x : (e < 4) ? x.y : (e < 6) ? x.z : x.w;
-    return (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffff));
+__device__ __forceinline__ uint32_t half_of(const u32x4 &x, int e) {
+    return (x[e >> 1] >> (16 * (e & 1))) & 0xffffu;
 }
 
 __device__ __forceinline__ void store_chunk(Smem &s, const Stage &st, bool need_q, const int t) {
     const int rg = t & 15, cg = t >> 4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<uint4 *>(&s.k[(4 * rg + r) * KS + 8 * cg]) = st.k[r];
-        if (need_q) *reinterpret_cast<uint4 *>(&s.q[(4 * rg + r) * KS + 8 * cg]) = st.q[r];
+        *reinterpret_cast<u32x4 *>(&s.k[(4 * rg + r) * KS + 8 * cg]) = st.k[r];
+        if (need_q) *reinterpret_cast<u32x4 *>(&s.q[(4 * rg + r) * KS + 8 * cg]) = st.q[r];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const uint32_t k01 = (uint32_t)half_of(st.k[0], e) | ((uint32_t)half_of(st.k[1], e) << 16);
-        const uint32_t k23 = (uint32_t)half_of(st.k[2], e) | ((uint32_t)half_of(st.k[3], e) << 16);
+        const uint32_t k01 = half_of(st.k[0], e) | (half_of(st.k[1], e) << 16);
+        const uint32_t k23 = half_of(st.k[2], e) | (half_of(st.k[3], e) << 16);
         *reinterpret_cast<uint2 *>(&s.kt[(8 * cg + e) * CS + 4 * rg]) = make_uint2(k01, k23);
-        const uint32_t v01 = (uint32_t)half_of(st.v[0], e) | ((uint32_t)half_of(st.v[1], e) << 16);
-        const uint32_t v23 = (uint32_t)half_of(st.v[2], e) | ((uint32_t)half_of(st.v[3], e) << 16);
+        const uint32_t v01 = half_of(st.v[0], e) | (half_of(st.v[1], e) << 16);
+        const uint32_t v23 = half_of(st.v[2], e) | (half_of(st.v[3], e) << 16);
         *reinterpret_cast<uint2 *>(&s.vt[(8 * cg + e) * CS + 4 * rg]) = make_uint2(v01, v23);
     }
     if (t < CH) {
@@ -163,11 +174,15 @@ __device__ __forceinline__ void store_chunk(Smem &s, const Stage &st, bool need_
 }
 
 // ---------------------------------------------------------------- chunk prep
-// Cumsum (wave 0) and masked, beta-weighted K K^T (waves 1..3) into s.a.
-__device__ __forceinline__ void prep_cumsum_kkt(Smem &s, const int tid) {
+// Cumsum (wave 0), masked beta-weighted K K^T into s.a (waves 1..3), and the
+// causal decayed P^T = K Q^T as hi/lo A fragments (waves 0..2, output chunks).
+// P^T tile t covers (s block, i block) = (0,0), (0,1), (1,1).
+__device__ __forceinline__ void prep_products(Smem &s, const int tid, const bool out) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    f32x16 acc = {};
-    int rbi = 0, rbs = 0;
+    const int m = lane & 31, h = lane >> 5;
+    f32x16 acck = {}, accp = {};
+    const int rbi = (wave >= 2) ? 1 : 0, rbs = (wave == 3) ? 1 : 0;  // K K^T tile of waves 1..3
+    const int psb = (wave == 2) ? 1 : 0, prb = (wave >= 1) ? 1 : 0;  // P^T tile of waves 0..2
     if (wave == 0) {
         float x = s.graw[lane];
 #pragma unroll
@@ -176,146 +191,182 @@ __device__ __forceinline__ void prep_cumsum_kkt(Smem &s, const int tid) {
             if (lane >= off) x += y;
         }
         const float glast = __shfl(x, 63, 64);
+        const float gm = __expf(x);
         s.gcum[lane] = x;
-        s.gam[lane] = __expf(x);
+        s.gam[lane] = gm;
         s.dec[lane] = __expf(glast - x);
+        s.bg[lane] = s.beta[lane] * gm;
     } else {
-        // blocks (row, col) of K K^T: (0,0), (1,0), (1,1)
-        rbi = (wave >= 2) ? 1 : 0;
-        rbs = (wave == 3) ? 1 : 0;
-        const int m = lane & 31, h = lane >> 5;
         const bf16 *ra = &s.k[(32 * rbi + m) * KS + 8 * h];
         const bf16 *rb = &s.k[(32 * rbs + m) * KS + 8 * h];
 #pragma unroll
-        for (int kk = 0; kk < DK / 16; ++kk) acc = mfma(lds8(ra + 16 * kk), lds8(rb + 16 * kk), acc);
+        for (int kk = 0; kk < DK / 16; ++kk) acck = mfma(lds8(ra + 16 * kk), lds8(rb + 16 * kk), acck);
+    }
+    if (out && wave <= 2) {
+        const bf16 *ra = &s.k[(32 * psb + m) * KS + 8 * h];
+        const bf16 *rb = &s.q[(32 * prb + m) * KS + 8 * h];
+#pragma unroll
+        for (int kk = 0; kk < DK / 16; ++kk) accp = mfma(lds8(ra + 16 * kk), lds8(rb + 16 * kk), accp);
     }
     __syncthreads();
     if (wave != 0) {
-        const int n = lane & 31, h = lane >> 5;
-        const int col = 32 * rbs + n;
+        const int col = 32 * rbs + m;
         const float gs = s.gcum[col];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int row = 32 * rbi + 8 * (e >> 2) + 4 * h + (e & 3);
             float val = 0.f;
-            if (col < row) val = s.beta[row] * __expf(s.gcum[row] - gs) * acc[e];
+            if (col < row) val = s.beta[row] * __expf(s.gcum[row] - gs) * acck[e];
             s.a[row * AS + col] = val;
         }
     }
+    if (out && wave <= 2) {
+        const int i = 32 * prb + m;
+        const float gi = s.gcum[i];
+        float pv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int srow = 32 * psb + 8 * (e >> 2) + 4 * h + (e & 3);
+            pv[e] = (srow <= i) ? __expf(gi - s.gcum[srow]) * accp[e] : 0.f;
+        }
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+            bf16x8 hi, lo;
+            split8v(pv + 8 * kp, hi, lo);
+            s.pf[0][wave][kp][lane] = hi;
+            s.pf[1][wave][kp][lane] = lo;
+        }
+    }
     __syncthreads();
 }
 
-// In-place inverse of the unit lower-triangular (I + A) held as A in s.a:
-// 16 x 16 diagonal blocks by forward substitution, then two levels of
-// block merges  T_lo,hi = -T_lo,lo A_lo,hi T_hi,hi.  All fp32.
+// In-place inverse of the unit lower-triangular (I + A) held as A in s.a.
+// Level 0: the four 16 x 16 diagonal blocks by forward substitution (one lane
+// per column).  Level 1: T_10 = -T_11 A_10 T_00 inside each 32 x 32 diagonal
+// block.  Level 2 (MFMA, hi/lo bf16): T_lo,hi = -T_lo,lo A_lo,hi T_hi,hi.
+// Entries above the diagonal of each diagonal block hold zeros throughout.
 __device__ __forceinline__ void prep_inverse(Smem &s, const int tid) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    // level 0: diagonal block `wave`, lane = column
-    if (lane < 16) {
-        const int b0 = 16 * wave;
+    if (wave < 2 && lane < 32) {
+        const int o = 32 * wave + 16 * (lane >> 4), c = lane & 15;
         float t[16];
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-            float acc = (ii == lane) ? 1.f : 0.f;
+            const float *arow = &s.a[(o + ii) * AS + o];
+            float acc = (ii == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int ss = 0; ss < ii; ++ss) acc -= s.a[(b0 + ii) * AS + b0 + ss] * t[ss];
+            for (int ss = 0; ss < ii; ++ss) acc -= arow[ss] * t[ss];
             t[ii] = acc;
         }
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) s.a[(b0 + ii) * AS + b0 + lane] = t[ii];
+        for (int ii = 0; ii < 16; ++ii) s.a[(o + ii) * AS + o + c] = t[ii];
     }
     __syncthreads();
-    // level 1: T_10 (wave 0) and T_32 (wave 1), 16 x 16 each
-    float x[4];
-    const int c = lane & 15, r0 = 4 * (lane >> 4);
+    const int c = lane & 15, r4 = 4 * (lane >> 4);
     if (wave < 2) {
-        const int hb = 32 * wave;  // block origin of the 32 x 32 diagonal block
+        const int b = 32 * wave;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
+            const float *arow = &s.a[(b + 16 + r4 + rr) * AS + b];
             float acc = 0.f;
-            for (int ss = c; ss < 16; ++ss)  // T_00 is lower triangular
-                acc += s.a[(hb + 16 + r0 + rr) * AS + hb + ss] * s.a[(hb + ss) * AS + hb + c];
-            x[rr] = acc;
-        }
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) s.scr[wave * 256 + (r0 + rr) * 16 + c] = x[rr];
-    }
-    __syncthreads();
-    if (wave < 2) {
-        const int hb = 32 * wave;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = r0 + rr;
-            float acc = 0.f;
-            for (int ss = 0; ss <= r; ++ss)
-                acc += s.a[(hb + 16 + r) * AS + hb + 16 + ss] * s.scr[wave * 256 + ss * 16 + c];
-            s.a[(hb + 16 + r) * AS + hb + c] = -acc;
+            for (int ss = 0; ss < 16; ++ss) acc += arow[ss] * s.a[(b + ss) * AS + b + c];
+            s.scr[wave][(r4 + rr) * 17 + c] = acc;
         }
     }
     __syncthreads();
-    // level 2: rows 32..63, cols 0..31:  Y = A_lohi T_hi ; T_lohi = -T_lo Y
-    const int t = tid;
-    const int cc = t & 31, rq = 4 * (t >> 5);
-    float y[4];
+    if (wave < 2) {
+        const int b = 32 * wave;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        float acc = 0.f;
-        for (int ss = cc; ss < 32; ++ss) acc += s.a[(32 + rq + rr) * AS + ss] * s.a[ss * AS + cc];
-        y[rr] = acc;
+        for (int rr = 0; rr < 4; ++rr) {
+            const float *trow = &s.a[(b + 16 + r4 + rr) * AS + b + 16];
+            float acc = 0.f;
+#pragma unroll
+            for (int ss = 0; ss < 16; ++ss) acc += trow[ss] * s.scr[wave][ss * 17 + c];
+            s.a[(b + 16 + r4 + rr) * AS + b + c] = -acc;
+        }
     }
     __syncthreads();
+    if (wave == 0) {
+        const int m = lane & 31, h = lane >> 5;
+        f32x16 y = {};
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) s.scr[(rq + rr) * 33 + cc] = y[rr];
-    __syncthreads();
+        for (int kk = 0; kk < 2; ++kk) {
+            const float *ar = &s.a[(32 + m) * AS + 16 * kk + 8 * h];
+            float av[8], bv[8];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int r = rq + rr;
-        float acc = 0.f;
-        for (int ss = 0; ss <= r; ++ss) acc += s.a[(32 + r) * AS + 32 + ss] * s.scr[ss * 33 + cc];
-        s.a[(32 + r) * AS + cc] = -acc;
+            for (int e = 0; e < 8; ++e) {
+                av[e] = ar[e];
+                bv[e] = s.a[(16 * kk + 8 * h + e) * AS + m];
+            }
+            bf16x8 ah, al, bh, bl;
+            split8v(av, ah, al);
+            split8v(bv, bh, bl);
+            y = mfma(ah, bh, y);
+            y = mfma(ah, bl, y);
+            y = mfma(al, bh, y);
+        }
+        f32x16 z = {};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const float *tr = &s.a[(32 + m) * AS + 32 + 16 * kk + 4 * h];
+            float av[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                av[e] = tr[e];
+                av[4 + e] = tr[8 + e];
+            }
+            bf16x8 ah, al, bh, bl;
+            split8v(av, ah, al);
+            split8(y, kk, bh, bl);
+            z = mfma(ah, bh, z);
+            z = mfma(ah, bl, z);
+            z = mfma(al, bh, z);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s.a[(32 + 8 * (e >> 2) + 4 * h + (e & 3)) * AS + m] = -z[e];
     }
     __syncthreads();
 }
 
-// T diag(beta gamma) (bf16) and T diag(beta) (hi, lo) from T in s.a.
-__device__ __forceinline__ void prep_scaled_t(Smem &s, const int tid) {
-    const int t = tid;
-    const int i = t >> 2, s0 = 16 * (t & 3);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int col = s0 + e;
-        const float tv = (col < i) ? s.a[i * AS + col] : (col == i ? 1.f : 0.f);
-        const float tb = tv * s.beta[col];
-        s.tt[i * CS + col] = (bf16)(tb * s.gam[col]);
-        const bf16 hi = (bf16)tb;
-        s.th[0][i * CS + col] = hi;
-        s.th[1][i * CS + col] = (bf16)(tb - (float)hi);
-    }
-}
-
-// P = causal e^{G_i - G_s} Q K^T, hi and lo (waves 0..2: blocks (0,0), (1,0), (1,1)).
-__device__ __forceinline__ void prep_p(Smem &s, const int tid) {
+// W^T = K^T (T diag(beta gamma))^T for this wave's 32 key dims -> -W A
+// fragments in LDS; U = (T diag(beta)) V for this wave's 32 value columns.
+__device__ __forceinline__ void prep_wu(Smem &s, const int tid, f32x16 (&u)[2]) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    if (wave >= 3) return;
-    const int rbi = (wave >= 1) ? 1 : 0;
-    const int rbs = (wave == 2) ? 1 : 0;
     const int m = lane & 31, h = lane >> 5;
-    const bf16 *ra = &s.q[(32 * rbi + m) * KS + 8 * h];
-    const bf16 *rb = &s.k[(32 * rbs + m) * KS + 8 * h];
-    f32x16 acc = {};
 #pragma unroll
-    for (int kk = 0; kk < DK / 16; ++kk) acc = mfma(lds8(ra + 16 * kk), lds8(rb + 16 * kk), acc);
-    const int col = 32 * rbs + m;
-    const float gs = s.gcum[col];
+    for (int rb = 0; rb < 2; ++rb) {
+        f32x16 w = {};
+        u[rb] = f32x16{};
+        const int nk = (rb == 0) ? 2 : 4;  // T is lower triangular
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int row = 32 * rbi + 8 * (e >> 2) + 4 * h + (e & 3);
-        float val = 0.f;
-        if (col <= row) val = __expf(s.gcum[row] - gs) * acc[e];
-        const bf16 hi = (bf16)val;
-        s.p[0][row * CS + col] = hi;
-        s.p[1][row * CS + col] = (bf16)(val - (float)hi);
+        for (int kk = 0; kk < nk; ++kk) {
+            const float *tr = &s.a[(32 * rb + m) * AS + 16 * kk + 8 * h];
+            const float *bgp = &s.bg[16 * kk + 8 * h];
+            const float *bp = &s.beta[16 * kk + 8 * h];
+            bf16x8 tw, th, tl;
+            float tb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float tv = tr[e];
+                tw[e] = (bf16)(tv * bgp[e]);
+                tb[e] = tv * bp[e];
+            }
+            split8v(tb, th, tl);
+            w = mfma(lds8(&s.kt[(32 * wave + m) * CS + 16 * kk + 8 * h]), tw, w);
+            const bf16x8 vv = lds8(&s.vt[(32 * wave + m) * CS + 16 * kk + 8 * h]);
+            u[rb] = mfma(th, vv, u[rb]);
+            u[rb] = mfma(tl, vv, u[rb]);
+        }
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+            bf16x8 f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = (bf16)(-w[8 * kp + e]);
+            s.wf[rb][2 * wave + kp][lane] = f;
+        }
     }
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------- segment lookup
@@ -372,6 +423,45 @@ __device__ __forceinline__ SegEntry find_segment(const FwdParams &p, int seg, in
     return e;
 }
 
+// ---------------------------------------------------------------- output store
+// One chunk's output tile of this wave (64 rows x 32 value columns, in the
+// accumulator layout) goes through a wave-private LDS staging tile so that
+// every lane writes 16 contiguous bytes.
+__device__ __forceinline__ void write_o(Smem &s, const FwdParams &p, const SegEntry &e, int j, int c,
+                                        const f32x16 (&ov)[2], const int wave, const int ln) {
+    const int m = ln & 31, h = ln >> 5;
+    float *stg = s.ostage[wave];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) stg[(32 * rb + 8 * (r >> 2) + 4 * h + (r & 3)) * OS + m] = ov[rb][r];
+    // the staging tile is private to this wave: LDS keeps the wave's own
+    // write/read order; the fence keeps the compiler's
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const int valid = e.seq_len - c * CH;
+    const int64_t obase = ((e.row0 + (int64_t)c * CH) * p.Hv + j) * DV + 32 * wave;
+    if (p.o_f32) {
+#pragma unroll
+        for (int pass = 0; pass < 8; ++pass) {
+            const int row = 8 * pass + (ln >> 3), c4 = 4 * (ln & 7);
+            if (row < valid)
+                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.o) + obase + (int64_t)row * p.Hv * DV + c4) =
+                    *reinterpret_cast<const f32x4 *>(&stg[row * OS + c4]);
+        }
+    } else {
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int row = 16 * pass + (ln >> 2), c8 = 8 * (ln & 3);
+            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&stg[row * OS + c8]);
+            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&stg[row * OS + c8 + 4]);
+            const bf16x8 y = {(bf16)x0[0], (bf16)x0[1], (bf16)x0[2], (bf16)x0[3],
+                              (bf16)x1[0], (bf16)x1[1], (bf16)x1[2], (bf16)x1[3]};
+            if (row < valid)
+                *reinterpret_cast<bf16x8 *>(reinterpret_cast<bf16 *>(p.o) + obase + (int64_t)row * p.Hv * DV + c8) = y;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- main kernel
 __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -379,14 +469,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) 
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int n32 = lane & 31, h = lane >> 5;
     const int seg = blockIdx.x / p.Hv;
     const int j = blockIdx.x % p.Hv;
     if (seg >= p.num_segments) return;
     const SegEntry e = find_segment(p, seg, lane);
     if (e.n < 0) return;  // beyond the planned segments: nothing to do
     const int i_qk = j / p.group;
-    const int vcol = 32 * wave + n32;  // this lane's value column
 
     // ---- where this segment's state pass starts
     int c_first = e.c_begin;
@@ -410,69 +498,61 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) 
             ++w;
             if (acc <= kLnNoiseFloor) break;
         }
-        // every wave computed the same window (same data, same order)
         from_h0 = (c_first == 0);
     }
     const int c_end = e.c_begin + e.c_count;
 
-    // ---- state H[:, vcol] in four 32 x 32 accumulator tiles (rows = key dim)
+    // ---- state H[:, this lane's value column] in four 32 x 32 accumulator tiles
     f32x16 hacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-    if (from_h0 && p.h0) {
-        const float *h0 = p.h0 + ((int64_t)e.n * p.Hv + j) * DK * DV + vcol;
+    {
+        const int m = lane & 31, h = lane >> 5;
+        if (from_h0 && p.h0) {
+            const float *h0 = p.h0 + ((int64_t)e.n * p.Hv + j) * DK * DV + 32 * wave + m;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+            for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                hacc[mb][r] = h0[(32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * DV];
+                for (int r = 0; r < 16; ++r) hacc[mb][r] = h0[(32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * DV];
+        }
     }
 
     if (c_first < c_end) {
+        Inputs in;
+        in.kstride = (unsigned)p.Hqk * DK * 2;
+        in.vstride = (unsigned)p.Hv * DV * 2;
+        in.gstride = (unsigned)p.Hv * 4;
+        in.k = make_rsrc(p.k + (e.row0 * p.Hqk + i_qk) * DK, (int64_t)e.seq_len * in.kstride);
+        in.q = make_rsrc(p.q + (e.row0 * p.Hqk + i_qk) * DK, (int64_t)e.seq_len * in.kstride);
+        in.v = make_rsrc(p.v + (e.row0 * p.Hv + j) * DV, (int64_t)e.seq_len * in.vstride);
+        in.g = make_rsrc(p.g + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
+        in.b = make_rsrc(p.beta + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
+
         Stage st;
-        load_chunk(p, st, e.row0, c_first, e.seq_len, i_qk, j, c_first >= e.c_begin, threadIdx.x);
+        load_chunk(in, st, c_first, c_first >= e.c_begin, threadIdx.x);
+        // A chunk's output waits in registers and is stored at the top of the
+        // next iteration, after that iteration's prefetched inputs have been
+        // consumed: memory-counter waits for the prefetch then never have to
+        // cover freshly issued output stores.
+        f32x16 ov[2];
+        int pend = -1;  // chunk whose output is held in ov, or -1
         for (int c = c_first; c < c_end; ++c) {
             // The thread index is made opaque once per chunk so that the
             // compiler recomputes lane-derived LDS addresses inside the loop
             // instead of hoisting hundreds of them into registers.
             int tid = threadIdx.x;
             asm volatile("" : "+v"(tid));
-            const int lane = tid & 63;
-            const int n32 = lane & 31, h = lane >> 5;
+            const int ln = tid & 63;
+            const int m = ln & 31, h = ln >> 5;
             const bool out = (c >= e.c_begin);  // warm-up chunks only advance the state
             store_chunk(s, st, out, tid);
             __syncthreads();
-            if (c + 1 < c_end) load_chunk(p, st, e.row0, c + 1, e.seq_len, i_qk, j, c + 1 >= e.c_begin, tid);
+            if (pend >= 0) write_o(s, p, e, j, pend, ov, wave, ln);  // staging aliases s.a, free until the masks
+            pend = -1;
+            if (c + 1 < c_end) load_chunk(in, st, c + 1, c + 1 >= e.c_begin, tid);
 
-            prep_cumsum_kkt(s, tid);
+            prep_products(s, tid, out);
             prep_inverse(s, tid);
-            prep_scaled_t(s, tid);
-            if (out) prep_p(s, tid);
-            __syncthreads();
-
-            // W (this wave's 32 key columns, all 64 rows) -> -W in LDS;  U (this wave's value columns)
             f32x16 u[2];
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                f32x16 wacc = {};
-                u[rb] = f32x16{};
-                const bf16 *ta = &s.tt[(32 * rb + n32) * CS + 8 * h];
-                const bf16 *ha = &s.th[0][(32 * rb + n32) * CS + 8 * h];
-                const bf16 *la = &s.th[1][(32 * rb + n32) * CS + 8 * h];
-                const bf16 *kb = &s.kt[(32 * wave + n32) * CS + 8 * h];
-                const bf16 *vb = &s.vt[(32 * wave + n32) * CS + 8 * h];
-                const int nk = (rb == 0) ? 2 : 4;  // T is lower triangular
-                for (int kk = 0; kk < nk; ++kk) {
-                    wacc = mfma(lds8(ta + 16 * kk), lds8(kb + 16 * kk), wacc);
-                    const bf16x8 vv = lds8(vb + 16 * kk);
-                    u[rb] = mfma(lds8(ha + 16 * kk), vv, u[rb]);
-                    u[rb] = mfma(lds8(la + 16 * kk), vv, u[rb]);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    s.w[row * KS + 32 * wave + n32] = (bf16)(-wacc[r]);
-                }
-            }
-            __syncthreads();
+            prep_wu(s, tid, u);
 
             // ---- critical chain: v' = U - W H   (and Q H for the output)
             f32x16 vp[2] = {u[0], u[1]};
@@ -483,21 +563,21 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) 
                 split8(hacc[kk >> 1], kk & 1, hh, hl);
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
-                    const bf16x8 a = lds8_perm(&s.w[(32 * rb + n32) * KS], 16 * kk, h);
+                    const bf16x8 a = s.wf[rb][kk][ln];
                     vp[rb] = mfma(a, hh, vp[rb]);
                     vp[rb] = mfma(a, hl, vp[rb]);
                 }
                 if (out) {
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb) {
-                        const bf16x8 a = lds8_perm(&s.q[(32 * rb + n32) * KS], 16 * kk, h);
+                        const bf16x8 a = lds8_perm(&s.q[(32 * rb + m) * KS], 16 * kk, h);
                         qh[rb] = mfma(a, hh, qh[rb]);
                         qh[rb] = mfma(a, hl, qh[rb]);
                     }
                 }
             }
             if (out) {
-                // O = scale (diag(gamma) Q H + P v')
+                // O = scale (diag(gamma) Q H + P v'), staged through LDS per wave
                 f32x16 pv[2] = {f32x16{}, f32x16{}};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
@@ -506,39 +586,29 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) 
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb) {
                         if (rb == 0 && kk >= 2) continue;  // P is lower triangular
-                        const bf16x8 ah = lds8_perm(&s.p[0][(32 * rb + n32) * CS], 16 * kk, h);
-                        const bf16x8 al = lds8_perm(&s.p[1][(32 * rb + n32) * CS], 16 * kk, h);
+                        const int t = (rb == 0) ? 0 : (kk < 2 ? 1 : 2);
+                        const bf16x8 ah = s.pf[0][t][kk & 1][ln];
+                        const bf16x8 al = s.pf[1][t][kk & 1][ln];
                         pv[rb] = mfma(ah, vh, pv[rb]);
                         pv[rb] = mfma(ah, vl, pv[rb]);
                         pv[rb] = mfma(al, vh, pv[rb]);
                     }
                 }
-                const int valid = e.seq_len - c * CH;
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
+                for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (row < valid) {
-                            const float ov = p.scale * (s.gam[row] * qh[rb][r] + pv[rb][r]);
-                            const int64_t off = ((e.row0 + (int64_t)c * CH + row) * p.Hv + j) * DV + 32 * wave + n32;
-                            if (p.o_f32)
-                                reinterpret_cast<float *>(p.o)[off] = ov;
-                            else
-                                reinterpret_cast<bf16 *>(p.o)[off] = (bf16)ov;
-                        }
+                        ov[rb][r] = p.scale * (s.gam[row] * qh[rb][r] + pv[rb][r]);
                     }
-                }
+                pend = c;
             }
             // ---- H <- gamma_last H + K^T diag(gamma_last / gamma) v'
             const float glast = s.gam[CH - 1];
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    vp[rb][r] *= s.dec[row];
-                }
+                for (int r = 0; r < 16; ++r) vp[rb][r] *= s.dec[32 * rb + 8 * (r >> 2) + 4 * h + (r & 3)];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) hacc[mb] *= glast;
 #pragma unroll
@@ -547,23 +617,23 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) 
                 split8(vp[kk >> 1], kk & 1, vh, vl);
 #pragma unroll
                 for (int mb = 0; mb < 4; ++mb) {
-                    const bf16x8 a = lds8_perm(&s.kt[(32 * mb + n32) * CS], 16 * kk, h);
+                    const bf16x8 a = lds8_perm(&s.kt[(32 * mb + m) * CS], 16 * kk, h);
                     hacc[mb] = mfma(a, vh, hacc[mb]);
                     hacc[mb] = mfma(a, vl, hacc[mb]);
                 }
             }
             __syncthreads();  // LDS is rewritten by the next chunk
         }
+        if (pend >= 0) write_o(s, p, e, j, pend, ov, wave, threadIdx.x & 63);
     }
 
     if (e.last && p.ht) {
+        const int m = lane & 31, h = lane >> 5;
+        float *ht = p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV + 32 * wave + m;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int krow = 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-                p.ht[(((int64_t)e.n * p.Hv + j) * DK + krow) * DV + vcol] = hacc[mb][r];
-            }
+            for (int r = 0; r < 16; ++r) ht[(32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * DV] = hacc[mb][r];
     }
 }
 
