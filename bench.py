@@ -66,6 +66,36 @@ def stored_traffic(workload: str):
     return e.get("bytes_per_launch")
 
 
+def _counter_mean(csv_path: str, counter: str, kernel_substr: str) -> float:
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path))
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for '{kernel_substr}' in {csv_path}")
+    return sum(vals) / len(vals)
+
+
+def ingest_counters(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str):
+    """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of the
+    forward and of the 1 GiB copy calibration into HBM bytes per launch, and
+    store them with the hash of the kernel source they were taken on."""
+    gib = float(1 << 30)
+    f_fac = gib / (_counter_mean(copy_fetch_csv, "FETCH_SIZE", "copyBuffer") * 1024.0)
+    w_fac = gib / (_counter_mean(copy_write_csv, "WRITE_SIZE", "copyBuffer") * 1024.0)
+    fetch = _counter_mean(fetch_csv, "FETCH_SIZE", "gdn_fwd_main_kernel") * 1024.0 * f_fac
+    write = _counter_mean(write_csv, "WRITE_SIZE", "gdn_fwd_main_kernel") * 1024.0 * w_fac
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        d = {}
+    d[workload] = {"bytes_per_launch": int(round(fetch + write)), "fetch_bytes": int(round(fetch)),
+                   "write_bytes": int(round(write)), "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4),
+                   "kernel_source_sha": kernel_source_hash()}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(d, open(TRAFFIC_FILE, "w"), indent=2, sort_keys=True)
+    print(json.dumps(d[workload]))
+
+
 def cpu_baseline(x, w, target_s: float):
     import numpy as np  # noqa: F401
     import oracle
@@ -99,7 +129,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="store HBM bytes per launch from rocprofv3 counter CSVs (no GPU needed)")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(args.workload, *args.ingest_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the forward shards over (sequence, head-group) "
               "with no communication; see the design notes); run with --gpus 1", file=sys.stderr)
