@@ -40,6 +40,7 @@ struct Plan {
     int32_t cp_mode = GDN_CP_OFF;
     int32_t warmup = 0;
     size_t workspace = 0;
+    size_t state_bytes = 0;
 };
 
 int32_t count_segments(const gdn_fwd_desc *d, int32_t L) {
@@ -89,7 +90,6 @@ int make_plan(const gdn_fwd_desc *d, Plan *P) {
     if (d->K != gdn::kDimK || d->V != gdn::kDimV)
         return fail(GDN_EUNSUPPORTED, "only K = V = 128 is built (got K=%d V=%d)", d->K, d->V);
     if (d->chunk != gdn::kChunk) return fail(GDN_EUNSUPPORTED, "only chunk = 64 is built (got %d)", d->chunk);
-    if (d->cp_mode == GDN_CP_EXACT) return fail(GDN_EUNSUPPORTED, "cp_mode EXACT is not built yet");
     if (d->T > INT32_MAX || d->B > INT32_MAX) return fail(GDN_EINVAL, "B and T must fit in int32");
 
     int64_t max_len = 0, total_chunks = 0;
@@ -152,7 +152,13 @@ int make_plan(const gdn_fwd_desc *d, Plan *P) {
     P->cp_mode = mode;
     P->num_segments = count_segments(d, L);
     if ((int64_t)P->num_segments * d->H_v > INT32_MAX) return fail(GDN_EINVAL, "grid too large");
-    P->workspace = 0;  // OFF / WARMUP keep everything on chip
+    // OFF / WARMUP keep everything on chip; EXACT stores per-segment S, M and
+    // start states (three [segments][H_v][K][V] fp32 arrays)
+    P->workspace = 0;
+    if (P->cp_mode == GDN_CP_EXACT) {
+        P->state_bytes = (size_t)P->num_segments * d->H_v * d->K * d->V * sizeof(float);
+        P->workspace = 3 * P->state_bytes;
+    }
     return GDN_OK;
 }
 
@@ -264,10 +270,19 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
     fp.warmup_cap = P.warmup;
     fp.o_f32 = d->o_dtype == GDN_DTYPE_F32;
     fp.scale = d->scale;
+    if (P.cp_mode == GDN_CP_EXACT) {
+        fp.ws_s = (float *)workspace;
+        fp.ws_m = (float *)((char *)workspace + P.state_bytes);
+        fp.ws_h = (float *)((char *)workspace + 2 * P.state_bytes);
+    }
 
     if (P.num_segments == 0 || d->H_v == 0) {
         g_last_error.clear();
         return GDN_OK;
+    }
+    if (P.cp_mode == GDN_CP_EXACT) {
+        const int err = gdn::launch_cp_exact(fp, stream);
+        if (err) return fail(GDN_EHIP, "context-parallel pre-pass launch failed: %s", gdn::hip_error_text(err));
     }
     const int err = gdn::launch_fwd_main(fp, stream);
     if (err) return fail(GDN_EHIP, "forward launch failed: %s", gdn::hip_error_text(err));

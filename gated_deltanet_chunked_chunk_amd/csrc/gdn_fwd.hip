@@ -70,6 +70,11 @@ struct __attribute__((aligned(16))) Smem {
     bf16x8 pf[2][3][2][64];           // P as A fragments [hi, lo][tile][k step][lane]
     float scr[2][16 * 17];            // inverse scratch, one per merging wave
     float graw[CH], beta[CH], gcum[CH], gam[CH], dec[CH], bg[CH];
+    // e^{G_i - G_s} = ep[i] * em[s] with ep = e^{G - G_ref}, em = e^{G_ref - G},
+    // G_ref = G_31; rowa = beta * ep.  Used when every |G - G_ref| < 80 (no
+    // overflow in either factor), flagged by fact_ok.
+    float ep[CH], em[CH], rowa[CH];
+    int fact_ok;
 };
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -191,11 +196,20 @@ __device__ __forceinline__ void prep_products(Smem &s, const int tid, const bool
             if (lane >= off) x += y;
         }
         const float glast = __shfl(x, 63, 64);
+        const float gref = __shfl(x, 31, 64);
         const float gm = __expf(x);
+        const float d = x - gref;
+        const float bt = s.beta[lane];
+        const float epv = __expf(d);
         s.gcum[lane] = x;
         s.gam[lane] = gm;
         s.dec[lane] = __expf(glast - x);
-        s.bg[lane] = s.beta[lane] * gm;
+        s.bg[lane] = bt * gm;
+        s.ep[lane] = epv;
+        s.em[lane] = __expf(-d);
+        s.rowa[lane] = bt * epv;
+        const bool ok = __all(fabsf(d) < 80.f);
+        if (lane == 0) s.fact_ok = ok ? 1 : 0;
     } else {
         const bf16 *ra = &s.k[(32 * rbi + m) * KS + 8 * h];
         const bf16 *rb = &s.k[(32 * rbs + m) * KS + 8 * h];
@@ -209,25 +223,64 @@ __device__ __forceinline__ void prep_products(Smem &s, const int tid, const bool
         for (int kk = 0; kk < DK / 16; ++kk) accp = mfma(lds8(ra + 16 * kk), lds8(rb + 16 * kk), accp);
     }
     __syncthreads();
+    const bool fact = __builtin_amdgcn_readfirstlane(s.fact_ok) != 0;
     if (wave != 0) {
+        // A_is = beta_i e^{G_i - G_s} k_i.k_s for s < i (rows of this lane: 4 runs of 4)
         const int col = 32 * rbs + m;
-        const float gs = s.gcum[col];
+        float v[16];
+        if (fact) {
+            const float cf = s.em[col];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const f32x4 ra4 = *reinterpret_cast<const f32x4 *>(&s.rowa[32 * rbi + 8 * ii + 4 * h]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[4 * ii + j] = ra4[j] * cf * acck[4 * ii + j];
+            }
+        } else {
+            const float gs = s.gcum[col];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[32 * rbi + 8 * ii + 4 * h]);
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&s.beta[32 * rbi + 8 * ii + 4 * h]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = 32 * rbi + 8 * ii + 4 * h + j;
+                    v[4 * ii + j] = (col < row) ? b4[j] * __expf(g4[j] - gs) * acck[4 * ii + j] : 0.f;
+                }
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int row = 32 * rbi + 8 * (e >> 2) + 4 * h + (e & 3);
-            float val = 0.f;
-            if (col < row) val = s.beta[row] * __expf(s.gcum[row] - gs) * acck[e];
-            s.a[row * AS + col] = val;
+            s.a[row * AS + col] = (col < row) ? v[e] : 0.f;
         }
     }
     if (out && wave <= 2) {
+        // P^T_si = e^{G_i - G_s} q_i.k_s for s <= i (i = this lane's column)
         const int i = 32 * prb + m;
-        const float gi = s.gcum[i];
         float pv[16];
+        if (fact) {
+            const float cf = s.ep[i];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int srow = 32 * psb + 8 * (e >> 2) + 4 * h + (e & 3);
-            pv[e] = (srow <= i) ? __expf(gi - s.gcum[srow]) * accp[e] : 0.f;
+            for (int ii = 0; ii < 4; ++ii) {
+                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(&s.em[32 * psb + 8 * ii + 4 * h]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int srow = 32 * psb + 8 * ii + 4 * h + j;
+                    pv[4 * ii + j] = (srow <= i) ? cf * e4[j] * accp[4 * ii + j] : 0.f;
+                }
+            }
+        } else {
+            const float gi = s.gcum[i];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[32 * psb + 8 * ii + 4 * h]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int srow = 32 * psb + 8 * ii + 4 * h + j;
+                    pv[4 * ii + j] = (srow <= i) ? __expf(gi - g4[j]) * accp[4 * ii + j] : 0.f;
+                }
+            }
         }
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
@@ -252,10 +305,18 @@ __device__ __forceinline__ void prep_inverse(Smem &s, const int tid) {
         float t[16];
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-            const float *arow = &s.a[(o + ii) * AS + o];
+            float ar[16];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                if (4 * q4 < ii) {
+                    const f32x4 x = *reinterpret_cast<const f32x4 *>(&s.a[(o + ii) * AS + o + 4 * q4]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ar[4 * q4 + j] = x[j];
+                }
+            }
             float acc = (ii == c) ? 1.f : 0.f;
 #pragma unroll
-            for (int ss = 0; ss < ii; ++ss) acc -= arow[ss] * t[ss];
+            for (int ss = 0; ss < ii; ++ss) acc -= ar[ss] * t[ss];
             t[ii] = acc;
         }
 #pragma unroll
@@ -265,24 +326,36 @@ __device__ __forceinline__ void prep_inverse(Smem &s, const int tid) {
     const int c = lane & 15, r4 = 4 * (lane >> 4);
     if (wave < 2) {
         const int b = 32 * wave;
+        float tc[16];  // column c of T_00
+#pragma unroll
+        for (int ss = 0; ss < 16; ++ss) tc[ss] = s.a[(b + ss) * AS + b + c];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const float *arow = &s.a[(b + 16 + r4 + rr) * AS + b];
             float acc = 0.f;
 #pragma unroll
-            for (int ss = 0; ss < 16; ++ss) acc += arow[ss] * s.a[(b + ss) * AS + b + c];
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + r4 + rr) * AS + b + 4 * q4]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc += x[j] * tc[4 * q4 + j];
+            }
             s.scr[wave][(r4 + rr) * 17 + c] = acc;
         }
     }
     __syncthreads();
     if (wave < 2) {
         const int b = 32 * wave;
+        float xc[16];  // column c of X = A_10 T_00
+#pragma unroll
+        for (int ss = 0; ss < 16; ++ss) xc[ss] = s.scr[wave][ss * 17 + c];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-            const float *trow = &s.a[(b + 16 + r4 + rr) * AS + b + 16];
             float acc = 0.f;
 #pragma unroll
-            for (int ss = 0; ss < 16; ++ss) acc += trow[ss] * s.scr[wave][ss * 17 + c];
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + r4 + rr) * AS + b + 16 + 4 * q4]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc += x[j] * xc[4 * q4 + j];
+            }
             s.a[(b + 16 + r4 + rr) * AS + b + c] = -acc;
         }
     }
@@ -462,6 +535,27 @@ __device__ __forceinline__ void write_o(Smem &s, const FwdParams &p, const SegEn
     }
 }
 
+// ---------------------------------------------------------------- state I/O
+// A K x V fp32 state (row = key dim) <-> this wave's four accumulator tiles
+// (value columns 32 wave .. 32 wave + 31); each access is one 128-byte row piece.
+__device__ __forceinline__ void load_state(f32x16 (&t)[4], const float *src, const int wave, const int lane) {
+    const int m = lane & 31, h = lane >> 5;
+    const float *b = src + 32 * wave + m;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[mb][r] = b[(32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * DV];
+}
+
+__device__ __forceinline__ void store_state(const f32x16 (&t)[4], float *dst, const int wave, const int lane) {
+    const int m = lane & 31, h = lane >> 5;
+    float *b = dst + 32 * wave + m;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) b[(32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * DV] = t[mb][r];
+}
+
 // ---------------------------------------------------------------- main kernel
 __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -505,14 +599,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) 
     // ---- state H[:, this lane's value column] in four 32 x 32 accumulator tiles
     f32x16 hacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
     {
-        const int m = lane & 31, h = lane >> 5;
-        if (from_h0 && p.h0) {
-            const float *h0 = p.h0 + ((int64_t)e.n * p.Hv + j) * DK * DV + 32 * wave + m;
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) hacc[mb][r] = h0[(32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * DV];
-        }
+        const float *src = nullptr;
+        if (from_h0 && p.h0) src = p.h0 + ((int64_t)e.n * p.Hv + j) * DK * DV;
+        if (!from_h0 && p.cp_mode == 1 /* EXACT */) src = p.ws_h + ((int64_t)seg * p.Hv + j) * DK * DV;
+        if (src) load_state(hacc, src, wave, lane);
     }
 
     if (c_first < c_end) {
@@ -627,13 +717,169 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) 
         if (pend >= 0) write_o(s, p, e, j, pend, ov, wave, threadIdx.x & 63);
     }
 
-    if (e.last && p.ht) {
+    if (e.last && p.ht) store_state(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
+}
+
+// ---------------------------------------------------------------- exact context parallelism
+// Pre-pass (blog, AutoCP: the per-segment M and S).  For every segment that is
+// not the last of its sequence: S = the state pass over the segment from a
+// zero state, and M = the same pass without inputs (U = 0) from the identity,
+// i.e. the product of the chunk maps X -> gamma_last X - K^T diag(gamma_last /
+// gamma) W X.  Then the segment's end state is M H_start + S.
+__global__ void __launch_bounds__(NTHREADS, 1) gdn_cp_prepass_kernel(FwdParams p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    Smem &s = *reinterpret_cast<Smem *>(smem_raw);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int seg = blockIdx.x / p.Hv;
+    const int j = blockIdx.x % p.Hv;
+    if (seg >= p.num_segments) return;
+    const SegEntry e = find_segment(p, seg, lane);
+    if (e.n < 0 || e.last) return;  // a last segment's map is never used
+    const int i_qk = j / p.group;
+
+    f32x16 hs[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    f32x16 hm[4];
+    {
         const int m = lane & 31, h = lane >> 5;
-        float *ht = p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV + 32 * wave + m;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) ht[(32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * DV] = hacc[mb][r];
+            for (int r = 0; r < 16; ++r)
+                hm[mb][r] = (32 * mb + 8 * (r >> 2) + 4 * h + (r & 3) == 32 * wave + m) ? 1.f : 0.f;
+    }
+    const int c_end = e.c_begin + e.c_count;
+    Inputs in;
+    in.kstride = (unsigned)p.Hqk * DK * 2;
+    in.vstride = (unsigned)p.Hv * DV * 2;
+    in.gstride = (unsigned)p.Hv * 4;
+    in.k = make_rsrc(p.k + (e.row0 * p.Hqk + i_qk) * DK, (int64_t)e.seq_len * in.kstride);
+    in.q = in.k;  // not read: no output here
+    in.v = make_rsrc(p.v + (e.row0 * p.Hv + j) * DV, (int64_t)e.seq_len * in.vstride);
+    in.g = make_rsrc(p.g + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
+    in.b = make_rsrc(p.beta + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
+
+    Stage st;
+    load_chunk(in, st, e.c_begin, false, threadIdx.x);
+    for (int c = e.c_begin; c < c_end; ++c) {
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int ln = tid & 63;
+        const int m = ln & 31, h = ln >> 5;
+        store_chunk(s, st, false, tid);
+        __syncthreads();
+        if (c + 1 < c_end) load_chunk(in, st, c + 1, false, tid);
+        prep_products(s, tid, false);
+        prep_inverse(s, tid);
+        f32x16 u[2];
+        prep_wu(s, tid, u);
+
+        f32x16 vs[2] = {u[0], u[1]};
+        f32x16 vm[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            bf16x8 sh, sl, mh, ml;
+            split8(hs[kk >> 1], kk & 1, sh, sl);
+            split8(hm[kk >> 1], kk & 1, mh, ml);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) {
+                const bf16x8 a = s.wf[rb][kk][ln];
+                vs[rb] = mfma(a, sh, vs[rb]);
+                vs[rb] = mfma(a, sl, vs[rb]);
+                vm[rb] = mfma(a, mh, vm[rb]);
+                vm[rb] = mfma(a, ml, vm[rb]);
+            }
+        }
+        const float glast = s.gam[CH - 1];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float d = s.dec[32 * rb + 8 * (r >> 2) + 4 * h + (r & 3)];
+                vs[rb][r] *= d;
+                vm[rb][r] *= d;
+            }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            hs[mb] *= glast;
+            hm[mb] *= glast;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8 sh, sl, mh, ml;
+            split8(vs[kk >> 1], kk & 1, sh, sl);
+            split8(vm[kk >> 1], kk & 1, mh, ml);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const bf16x8 a = lds8_perm(&s.kt[(32 * mb + m) * CS], 16 * kk, h);
+                hs[mb] = mfma(a, sh, hs[mb]);
+                hs[mb] = mfma(a, sl, hs[mb]);
+                hm[mb] = mfma(a, mh, hm[mb]);
+                hm[mb] = mfma(a, ml, hm[mb]);
+            }
+        }
+        __syncthreads();
+    }
+    const int64_t off = ((int64_t)seg * p.Hv + j) * DK * DV;
+    store_state(hs, p.ws_s + off, wave, lane);
+    store_state(hm, p.ws_m + off, wave, lane);
+}
+
+// Combine (sequential over a sequence's segments): H_start[0] = initial state,
+// H_start[r+1] = M_r H_start[r] + S_r.  One workgroup per (sequence, v-head);
+// wave w owns value columns 32w..32w+31, M_r H on MFMA with hi/lo operands.
+__global__ void __launch_bounds__(NTHREADS, 1) gdn_cp_combine_kernel(FwdParams p) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int m = lane & 31, h = lane >> 5;
+    const int n = blockIdx.x / p.Hv;
+    const int j = blockIdx.x % p.Hv;
+    if (n >= p.N) return;
+    // first segment of sequence n and its segment count
+    int seg0 = 0, R = 0;
+    if (!p.cu) {
+        R = seq_segments(p.T, p.L);
+        seg0 = n * R;
+    } else {
+        int base = 0;
+        for (int n0 = 0; n0 < n; n0 += 64) {
+            const int nn = n0 + lane;
+            int cnt = (nn < n) ? seq_segments((int64_t)p.cu[nn + 1] - p.cu[nn], p.L) : 0;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+            base += __builtin_amdgcn_readfirstlane(cnt);
+        }
+        seg0 = base;
+        R = seq_segments((int64_t)p.cu[n + 1] - p.cu[n], p.L);
+    }
+    if (R <= 1) return;
+    f32x16 H[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    if (p.h0) load_state(H, p.h0 + ((int64_t)n * p.Hv + j) * DK * DV, wave, lane);
+    for (int r = 0; r + 1 < R; ++r) {
+        const int64_t off = ((int64_t)(seg0 + r) * p.Hv + j) * DK * DV;
+        const float *M = p.ws_m + off;
+        f32x16 X[4];
+        load_state(X, p.ws_s + off, wave, lane);  // start from S_r, accumulate M_r H
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            bf16x8 bh, bl;
+            split8(H[kk >> 1], kk & 1, bh, bl);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const float *row = M + (int64_t)(32 * mb + m) * DK + 16 * kk + 4 * h;
+                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(row);
+                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(row + 8);
+                const float av[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                bf16x8 ah, al;
+                split8v(av, ah, al);
+                X[mb] = mfma(ah, bh, X[mb]);
+                X[mb] = mfma(ah, bl, X[mb]);
+                X[mb] = mfma(al, bh, X[mb]);
+            }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) H[mb] = X[mb];
+        store_state(H, p.ws_h + ((int64_t)(seg0 + r + 1) * p.Hv + j) * DK * DV, wave, lane);
     }
 }
 
@@ -680,6 +926,21 @@ int launch_fwd_main(const FwdParams &p, void *stream) {
     if (attr_rc != 0) return attr_rc;
     const unsigned grid = (unsigned)p.num_segments * (unsigned)p.Hv;
     hipLaunchKernelGGL(gdn_fwd_main_kernel, dim3(grid), dim3(NTHREADS), smem, (hipStream_t)stream, p);
+    return (int)hipGetLastError();
+}
+
+int launch_cp_exact(const FwdParams &p, void *stream) {
+    static const size_t smem = sizeof(Smem);
+    static const int attr_rc =
+        (int)hipFuncSetAttribute((const void *)gdn_cp_prepass_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)smem);
+    if (attr_rc != 0) return attr_rc;
+    const unsigned grid = (unsigned)p.num_segments * (unsigned)p.Hv;
+    hipLaunchKernelGGL(gdn_cp_prepass_kernel, dim3(grid), dim3(NTHREADS), smem, (hipStream_t)stream, p);
+    int err = (int)hipGetLastError();
+    if (err) return err;
+    hipLaunchKernelGGL(gdn_cp_combine_kernel, dim3((unsigned)p.N * (unsigned)p.Hv), dim3(NTHREADS), 0,
+                       (hipStream_t)stream, p);
     return (int)hipGetLastError();
 }
 

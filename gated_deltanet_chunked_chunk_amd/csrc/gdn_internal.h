@@ -53,10 +53,14 @@ struct FwdParams {
     int32_t warmup_cap;
     int32_t o_f32;
     float scale;
+    // exact context parallelism (workspace, each [num_segments][Hv][K][V] fp32):
+    // per-segment zero-start state S, transition map M, and segment-start state H
+    float *ws_s, *ws_m, *ws_h;
 };
 
 // Launchers (gdn_fwd.hip).  Each returns the hipError_t of its launch as int.
 int launch_fwd_main(const FwdParams &p, void *stream);
+int launch_cp_exact(const FwdParams &p, void *stream);  // pre-pass + combine
 int launch_chunk_cumsum(const float *g, float *out, int64_t B, int64_t T, int32_t H, int32_t chunk,
                         const int32_t *cu, int32_t N, void *stream);
 const char *hip_error_text(int err);

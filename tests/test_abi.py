@@ -51,7 +51,6 @@ def desc(**kw):
     (dict(K=64), L.GDN_EUNSUPPORTED),
     (dict(V=256), L.GDN_EUNSUPPORTED),
     (dict(chunk=32), L.GDN_EUNSUPPORTED),
-    (dict(cp="exact"), L.GDN_EUNSUPPORTED),
 ])
 def test_plan_rejects(bad, status):
     d = desc(**bad)
@@ -85,6 +84,17 @@ def test_plan_for_workloads():
     assert p["num_segments"] == 32 and p["warmup_chunks"] == 8
     d = desc(T=32768, H_qk=2, H_v=8, cp="warmup", cp_lambda=1.0)
     assert G.plan(d)["segment_chunks"] == 23  # round(1.0 * sqrt(512))
+
+
+def test_plan_exact_workspace():
+    d = desc(T=32768, H_qk=2, H_v=8, cp="exact", cp_segment_chunks=16)
+    p = G.plan(d)
+    assert p["cp"] == "exact" and p["num_segments"] == 32
+    # per-segment S, M and start state: three [segments][H_v][K][V] fp32 arrays
+    assert p["workspace_bytes"] == 3 * 32 * 8 * 128 * 128 * 4
+    d = desc(T=32768, H_qk=2, H_v=8, cp="exact", cp_segment_chunks=512)
+    p = G.plan(d)
+    assert p["cp"] == "off" and p["workspace_bytes"] == 0
 
 
 def test_plan_varlen_segments():

@@ -104,6 +104,29 @@ def test_warmup_cp(L, g_mu):
     check(f"warmup L={L} mu={g_mu}", o, ht, o_ref, ht_ref, REL_WARMUP)
 
 
+@pytest.mark.parametrize("L", [1, 3, 8])
+@pytest.mark.parametrize("g_mu", [2.0, 6.0])
+def test_exact_cp(L, g_mu):
+    """Exact CP (per-segment M and S, combine, main pass) holds the exact bar,
+    also for weak gates (mu = 6) where a warm-up window would not converge."""
+    x = W.random_inputs(1, 64 * 40 + 17, 2, 8, seed=7, g_mu=g_mu, h0_std=0.1, device=DEV)
+    o_ref, ht_ref = run_oracle(x)
+    o, ht = run_gpu(x, o_dtype="f32", cp="exact", cp_segment_chunks=L)
+    check(f"exact L={L} mu={g_mu}", o, ht, o_ref, ht_ref, REL_EXACT)
+
+
+def test_exact_cp_varlen_and_batch():
+    lens = [0, 1, 63, 700, 129, 0, 256]
+    x = W.random_inputs(1, sum(lens), 2, 4, seed=19, g_mu=4.0, h0_std=0.1, lengths=lens, device=DEV)
+    o_ref, ht_ref = run_oracle(x)
+    o, ht = run_gpu(x, o_dtype="f32", cp="exact", cp_segment_chunks=2)
+    check("exact varlen", o, ht, o_ref, ht_ref, REL_EXACT)
+    y = W.random_inputs(3, 64 * 9 + 3, 1, 2, seed=20, g_mu=5.0, h0_std=0.1, device=DEV)
+    o_ref, ht_ref = run_oracle(y)
+    o, ht = run_gpu(y, o_dtype="f32", cp="exact", cp_segment_chunks=4)
+    check("exact batch", o, ht, o_ref, ht_ref, REL_EXACT)
+
+
 def test_warmup_window_reaching_sequence_start_is_exact():
     # weak gates: the window never reaches the noise floor, but with a cap that
     # covers the whole prefix every segment restarts from the initial state
@@ -244,21 +267,23 @@ def test_chunk_cumsum():
 # ------------------------------------------------------------------ full-size workloads, sampled heads
 
 FULL = [
-    ("gdn_fwd_1x32768_h16x16", [0, 9], [0, 9]),
-    ("gdn_fwd_1x32768_h2x8", [0, 1, 2, 3], [0]),
-    ("gdn_fwd_varlen16_65536_h8x24", [0, 23], [0, 7]),
+    ("gdn_fwd_1x32768_h16x16", [0, 9], [0, 9], "auto"),
+    ("gdn_fwd_1x32768_h2x8", [0, 1, 2, 3], [0], "warmup"),
+    ("gdn_fwd_1x32768_h2x8", [4, 5, 6, 7], [1], "exact"),
+    ("gdn_fwd_varlen16_65536_h8x24", [0, 23], [0, 7], "auto"),
 ]
 
 
-@pytest.mark.parametrize("name,heads,qk", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled_heads(name, heads, qk):
-    """Full-size workloads in the benchmark's launch configuration (cp='auto',
-    bf16 o) and in fp32-o mode; the oracle runs only the sampled v-heads (with
-    their qk heads) over the whole sequence."""
+@pytest.mark.parametrize("name,heads,qk,cp", FULL, ids=[f"{f[0]}-{f[3]}" for f in FULL])
+def test_full_size_sampled_heads(name, heads, qk, cp):
+    """Full-size workloads in the benchmark's launch configuration (bf16 o) and
+    in fp32-o mode; the oracle runs only the sampled v-heads (with their qk
+    heads) over the whole sequence."""
     w = W.WORKLOADS[name]
     x = W.make_inputs(w, device=DEV)
     o_ref, ht_ref = run_oracle(x, heads=heads, qk_heads=qk)
-    o, ht = run_gpu(x, o_dtype="f32", cp="auto")
-    check(f"{name} f32", o[:, :, heads], ht[:, heads], o_ref, ht_ref, REL_WARMUP)
-    ob, htb = run_gpu(x, o_dtype="bf16", cp="auto")
-    check(f"{name} bf16", ob[:, :, heads], htb[:, heads], o_ref, ht_ref, REL_WARMUP, bf16_o=True)
+    bar = REL_EXACT if cp == "exact" else REL_WARMUP
+    o, ht = run_gpu(x, o_dtype="f32", cp=cp)
+    check(f"{name} {cp} f32", o[:, :, heads], ht[:, heads], o_ref, ht_ref, bar)
+    ob, htb = run_gpu(x, o_dtype="bf16", cp=cp)
+    check(f"{name} {cp} bf16", ob[:, :, heads], htb[:, heads], o_ref, ht_ref, bar, bf16_o=True)
