@@ -496,45 +496,6 @@ __device__ __forceinline__ SegEntry find_segment(const FwdParams &p, int seg, in
     return e;
 }
 
-// ---------------------------------------------------------------- output store
-// One chunk's output tile of this wave (64 rows x 32 value columns, in the
-// accumulator layout) goes through a wave-private LDS staging tile so that
-// every lane writes 16 contiguous bytes.
-__device__ __forceinline__ void write_o(Smem &s, const FwdParams &p, const SegEntry &e, int j, int c,
-                                        const f32x16 (&ov)[2], const int wave, const int ln) {
-    const int m = ln & 31, h = ln >> 5;
-    float *stg = s.ostage[wave];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) stg[(32 * rb + 8 * (r >> 2) + 4 * h + (r & 3)) * OS + m] = ov[rb][r];
-    // the staging tile is private to this wave: LDS keeps the wave's own
-    // write/read order; the fence keeps the compiler's
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    const int valid = e.seq_len - c * CH;
-    const int64_t obase = ((e.row0 + (int64_t)c * CH) * p.Hv + j) * DV + 32 * wave;
-    if (p.o_f32) {
-#pragma unroll
-        for (int pass = 0; pass < 8; ++pass) {
-            const int row = 8 * pass + (ln >> 3), c4 = 4 * (ln & 7);
-            if (row < valid)
-                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.o) + obase + (int64_t)row * p.Hv * DV + c4) =
-                    *reinterpret_cast<const f32x4 *>(&stg[row * OS + c4]);
-        }
-    } else {
-#pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
-            const int row = 16 * pass + (ln >> 2), c8 = 8 * (ln & 3);
-            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&stg[row * OS + c8]);
-            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&stg[row * OS + c8 + 4]);
-            const bf16x8 y = {(bf16)x0[0], (bf16)x0[1], (bf16)x0[2], (bf16)x0[3],
-                              (bf16)x1[0], (bf16)x1[1], (bf16)x1[2], (bf16)x1[3]};
-            if (row < valid)
-                *reinterpret_cast<bf16x8 *>(reinterpret_cast<bf16 *>(p.o) + obase + (int64_t)row * p.Hv * DV + c8) = y;
-        }
-    }
-}
-
 // ---------------------------------------------------------------- state I/O
 // A K x V fp32 state (row = key dim) <-> this wave's four accumulator tiles
 // (value columns 32 wave .. 32 wave + 31); each access is one 128-byte row piece.
@@ -556,10 +517,604 @@ __device__ __forceinline__ void store_state(const f32x16 (&t)[4], float *dst, co
         for (int r = 0; r < 16; ++r) b[(32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * DV] = t[mb][r];
 }
 
-// ---------------------------------------------------------------- main kernel
-__global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) {
+// ---------------------------------------------------------------- the forward kernel (8 waves)
+// One workgroup of eight waves owns one (segment, v-head).  Wave w holds value
+// columns 16w .. 16w+15 of the state in eight 16 x 16 accumulator tiles
+// (v_mfma_f32_16x16x32_bf16: lane l holds A row / B column l % 16 with the 8
+// k-slots 8 (l / 16) .. +7; accumulator element j holds row 4 (l / 16) + j,
+// column l % 16).  Two accumulator tiles stacked along k read as one B
+// operand see, in a 32-wide k step, the k indices 4g..4g+3 and 16+4g..16+4g+3
+// (g = l / 16); A operands that meet such a B use the same permutation.
+// The chunk-local preparation is spread over all eight waves, and Q H (which
+// needs only the chunk-start state) is computed by the waves that are idle
+// while others run the cumsum/products and the inverse.
+constexpr int NT8 = 512;
+constexpr int OS8 = 16 + 4;  // fp32 row stride of a wave's 64 x 16 output staging tile
+constexpr int TS8 = 32 + 4;  // fp32 row stride of the transposed 32 x 32 diagonal blocks
+
+struct __attribute__((aligned(16))) Smem8 {
+    union {
+        bf16 k[CH * KS];              // K, row = token (products)
+        bf16x8 thf[2][6][64];         // T diag(beta), hi and lo A fragments (W/U phase)
+    };
+    bf16 q[CH * KS];                  // Q
+    bf16 kt[DK * CS];                 // K^T, row = key dim
+    bf16 vt[DV * CS];                 // V^T, row = value dim
+    union {
+        float a[CH * AS];             // A, inverted in place into T
+        float ostage[8][CH * OS8];    // per-wave output tile on its way to HBM
+    };
+    bf16x8 wf[4][4][64];              // -W as A fragments [row tile][k step][lane]
+    bf16x8 pf[2][6][64];              // P as A fragments [hi, lo][fragment][lane]
+    // the two 32 x 32 diagonal blocks of A, then of T, transposed ([block][col][row])
+    float tt[2][32 * TS8];
+    float graw[CH], beta[CH], gcum[CH], gam[CH], dec[CH], bg[CH];
+    float ep[CH], em[CH], rowa[CH];   // e^{G - G_31}, e^{G_31 - G}, beta e^{G - G_31}
+    int fact_ok;                      // every |G - G_31| < 80: the factored decays are finite
+};
+
+// The six 16-row x 32-column tiles of a 64 x 64 lower-triangular matrix that
+// hold non-zeros: (row tile, k step) = (0,0) (1,0) (2,0) (3,0) (2,1) (3,1).
+__device__ __forceinline__ int frag_rt(int f) { return f < 4 ? f : f - 2; }
+__device__ __forceinline__ int frag_ks(int f) { return f < 4 ? 0 : 1; }
+__device__ __forceinline__ int frag_of(int rt, int ks) { return ks == 0 ? rt : rt + 2; }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two stacked accumulator tiles as the hi and lo bf16 B operand of one k step.
+__device__ __forceinline__ void split_pair(const f32x4 &t0, const f32x4 &t1, bf16x8 &hi, bf16x8 &lo) {
+    const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    split8v(x, hi, lo);
+}
+
+// A-operand read matching split_pair's k order: row + base + 4g .. +3 and
+// row + base + 16 + 4g .. +3.
+__device__ __forceinline__ bf16x8 lds8_perm16(const bf16 *row, int base, int g) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row + base + 4 * g);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(row + base + 16 + 4 * g);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Inclusive wave-wide prefix sum with DPP (row shifts inside each 16-lane row,
+// then row broadcasts across rows).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_f<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_f<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_f<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_f<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_f<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_f<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// ---- staging of one chunk: waves 0..3 take K (natural and transposed) and
+// g, beta; waves 4..7 take V (transposed) and Q.  Thread t' = t mod 256 holds
+// rows 4 (t' % 16) .. +3, columns 8 (t' / 16) .. +7 of its tiles.
+struct Stage8 {
+    u32x4 x[4], y[4];
+    float g, b;
+};
+
+__device__ __forceinline__ void load_chunk8(const Inputs &in, Stage8 &st, int c, bool need_q, int t, int wave) {
+    const int tt = t & 255;
+    const int rg = tt & 15, cg = tt >> 4;
+    const bool kv = wave < 4;  // wave-uniform role: K (waves 0..3) or V and Q (waves 4..7)
+    const __amdgpu_buffer_rsrc_t rx = kv ? in.k : in.v;
+    const unsigned sx = kv ? in.kstride : in.vstride;
+    const bool ld_q = !kv && need_q;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const unsigned tok = (unsigned)(c * CH + 4 * rg + r);
+        st.x[r] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(tok * sx + 16u * cg), 0, 0);
+        u32x4 y = {0u, 0u, 0u, 0u};
+        if (ld_q) y = __builtin_amdgcn_raw_buffer_load_b128(in.q, (int)(tok * in.kstride + 16u * cg), 0, 0);
+        st.y[r] = y;
+    }
+    float gv = 0.f, bv = 0.f;
+    if (t < CH) {
+        const unsigned tok = (unsigned)(c * CH + t);
+        gv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.g, (int)(tok * in.gstride), 0, 0));
+        bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.b, (int)(tok * in.gstride), 0, 0));
+    }
+    st.g = gv;
+    st.b = bv;
+}
+
+__device__ __forceinline__ void store_chunk8(Smem8 &s, const Stage8 &st, bool need_q, int t, int wave) {
+    const int tt = t & 255;
+    const int rg = tt & 15, cg = tt >> 4;
+    uint2 tr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        tr[e] = make_uint2(half_of(st.x[0], e) | (half_of(st.x[1], e) << 16),
+                           half_of(st.x[2], e) | (half_of(st.x[3], e) << 16));
+    if (wave < 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4 *>(&s.k[(4 * rg + r) * KS + 8 * cg]) = st.x[r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.kt[(8 * cg + e) * CS + 4 * rg]) = tr[e];
+    } else {
+        if (need_q) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4 *>(&s.q[(4 * rg + r) * KS + 8 * cg]) = st.y[r];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.vt[(8 * cg + e) * CS + 4 * rg]) = tr[e];
+    }
+    if (t < CH) {
+        s.graw[t] = st.g;
+        s.beta[t] = st.b;
+    }
+}
+
+// ---- Q H for this wave's value columns: qh[rt] covers rows 16 rt .. +15.
+// Operand reads are issued in batches ahead of the products that use them.
+__device__ __forceinline__ void chain_qh(const Smem8 &s, const f32x4 (&hacc)[8], f32x4 (&qh)[4], const int ln) {
+    const int m = ln & 15, g = ln >> 4;
+    bf16x8 hh[4], hl[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) split_pair(hacc[2 * kk], hacc[2 * kk + 1], hh[kk], hl[kk]);
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+        bf16x8 a[2][4];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) a[r][kk] = lds8_perm16(&s.q[(16 * (2 * r2 + r) + m) * KS], 32 * kk, g);
+        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+        for (int r = 0; r < 2; ++r) qh[2 * r2 + r] = f32x4{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                qh[2 * r2 + r] = mfma16(a[r][kk], hh[kk], qh[2 * r2 + r]);
+                qh[2 * r2 + r] = mfma16(a[r][kk], hl[kk], qh[2 * r2 + r]);
+            }
+    }
+}
+
+// ---- cumsum, decay factors, masked beta-weighted K K^T (into s.a, and the
+// diagonal 32 x 32 blocks transposed into s.tt) and the causal decayed P as A
+// fragments.  Roles (wave w runs on SIMD w mod 4):
+//   wave 0: cumsum and factors, then its own Q H (it carries the inverse later)
+//   waves 1..3: K K^T 32 x 32 tiles (0,0) (1,0) (1,1)
+//   waves 4..7: the six P fragments (4: 0, 4; 5: 1, 5; 6: 2; 7: 3)
+// A P fragment (rt, ks) stacks the P^T = K Q^T tiles (s tile 2 ks, i tile rt)
+// and (2 ks + 1, rt); the accumulator of each tile is the fragment half.
+__device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const int wave, const bool out,
+                                               const f32x4 (&hacc)[8], f32x4 (&qh)[4]) {
+    const int lane = tid & 63;
+    const int m32 = lane & 31, h32 = lane >> 5;
+    const int m = lane & 15, g = lane >> 4;
+    f32x16 acck = {};
+    const int rbi = (wave >= 2) ? 1 : 0, rbs = (wave == 3) ? 1 : 0;
+    int pfr[2] = {-1, -1};
+    if (wave == 4) { pfr[0] = 0; pfr[1] = 4; }
+    if (wave == 5) { pfr[0] = 1; pfr[1] = 5; }
+    if (wave == 6) pfr[0] = 2;
+    if (wave == 7) pfr[0] = 3;
+    f32x4 accp[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
+
+    if (wave == 0) {
+        const float x = wave_prefix_sum(s.graw[lane]);
+        const float glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+        const float gref = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+        const float gm = __expf(x);
+        const float d = x - gref;
+        const float bt = s.beta[lane];
+        const float epv = __expf(d);
+        s.gcum[lane] = x;
+        s.gam[lane] = gm;
+        s.dec[lane] = __expf(glast - x);
+        s.bg[lane] = bt * gm;
+        s.ep[lane] = epv;
+        s.em[lane] = __expf(-d);
+        s.rowa[lane] = bt * epv;
+        const bool ok = __all(fabsf(d) < 80.f);
+        if (lane == 0) s.fact_ok = ok ? 1 : 0;
+        if (out) chain_qh(s, hacc, qh, lane);
+    }
+    if (wave >= 1 && wave <= 3) {
+        const bf16 *ra = &s.k[(32 * rbi + m32) * KS + 8 * h32];
+        const bf16 *rb = &s.k[(32 * rbs + m32) * KS + 8 * h32];
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            bf16x8 xa[4], xb[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                xa[kk] = lds8(ra + 16 * (4 * k2 + kk));
+                xb[kk] = lds8(rb + 16 * (4 * k2 + kk));
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acck = mfma(xa[kk], xb[kk], acck);
+        }
+    }
+    if (out) {
+#pragma unroll
+        for (int pi = 0; pi < 2; ++pi) {
+            if (pfr[pi] < 0) continue;
+            const int rt = frag_rt(pfr[pi]), ks = frag_ks(pfr[pi]);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int st = 2 * ks + half;
+                if (st > rt) continue;  // tile entirely above the diagonal
+                const bf16 *ra = &s.k[(16 * st + m) * KS + 8 * g];
+                const bf16 *rb = &s.q[(16 * rt + m) * KS + 8 * g];
+                bf16x8 xa[4], xb[4];
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    xa[kk] = lds8(ra + 32 * kk);
+                    xb[kk] = lds8(rb + 32 * kk);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) accp[pi][half] = mfma16(xa[kk], xb[kk], accp[pi][half]);
+            }
+        }
+    }
+    __syncthreads();
+    const bool fact = __builtin_amdgcn_readfirstlane(s.fact_ok) != 0;
+    if (wave >= 1 && wave <= 3) {
+        const int col = 32 * rbs + m32;
+        float v[16];
+        if (fact) {
+            const float cf = s.em[col];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const f32x4 ra4 = *reinterpret_cast<const f32x4 *>(&s.rowa[32 * rbi + 8 * ii + 4 * h32]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[4 * ii + j] = ra4[j] * cf * acck[4 * ii + j];
+            }
+        } else {
+            const float gs = s.gcum[col];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[32 * rbi + 8 * ii + 4 * h32]);
+                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&s.beta[32 * rbi + 8 * ii + 4 * h32]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[4 * ii + j] = b4[j] * __expf(g4[j] - gs) * acck[4 * ii + j];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = 32 * rbi + 8 * (e >> 2) + 4 * h32 + (e & 3);
+            v[e] = (col < row) ? v[e] : 0.f;
+            s.a[row * AS + col] = v[e];
+        }
+        if (rbi == rbs) {  // diagonal 32 x 32 block: also store it transposed
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                *reinterpret_cast<f32x4 *>(&s.tt[rbi][m32 * TS8 + 8 * ii + 4 * h32]) =
+                    f32x4{v[4 * ii], v[4 * ii + 1], v[4 * ii + 2], v[4 * ii + 3]};
+        }
+    }
+    if (out) {
+#pragma unroll
+        for (int pi = 0; pi < 2; ++pi) {
+            if (pfr[pi] < 0) continue;
+            const int rt = frag_rt(pfr[pi]), ks = frag_ks(pfr[pi]);
+            const int i = 16 * rt + m;  // this lane's query row
+            float pv[8];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int s0 = 32 * ks + 16 * half + 4 * g;  // key rows of this lane's 4 slots
+                if (fact) {
+                    const float cf = s.ep[i];
+                    const f32x4 e4 = *reinterpret_cast<const f32x4 *>(&s.em[s0]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pv[4 * half + j] = (s0 + j <= i) ? cf * e4[j] * accp[pi][half][j] : 0.f;
+                } else {
+                    const float gi = s.gcum[i];
+                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[s0]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pv[4 * half + j] = (s0 + j <= i) ? __expf(gi - g4[j]) * accp[pi][half][j] : 0.f;
+                }
+            }
+            bf16x8 hi, lo;
+            split8v(pv, hi, lo);
+            s.pf[0][pfr[pi]][lane] = hi;
+            s.pf[1][pfr[pi]][lane] = lo;
+        }
+    }
+    __syncthreads();
+}
+
+// DPP row-local helpers for the 4-lane groups of the level-0 solve
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// ---- in-place inverse of (I + A), T = (I + A)^{-1}, in s.a (row-major) and
+// s.tt (transposed diagonal 32 x 32 blocks, needed by the merges):
+//   level 0 (waves 0..3, one 16 x 16 diagonal block each): forward
+//     substitution with lane = 4 c + p; the four lanes of column c split
+//     each row's dot product over s = p mod 4 and add it with two DPP steps;
+//   level 1 (waves 0, 1): T_10 = -T_11 (A_10 T_00) inside each 32 x 32
+//     diagonal block, two chained 16 x 16 MFMA products (hi/lo operands);
+//   level 2 (wave 0): T_lo,hi = -T_lo,lo (A_lo,hi T_hi,hi), 32 x 32 MFMA.
+// The other waves compute their Q H meanwhile (waves 4..7 during level 0,
+// 2 and 3 during level 1, 1 during level 2), never on a step's critical wave.
+__device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int wave, const bool out,
+                                              const f32x4 (&hacc)[8], f32x4 (&qh)[4]) {
+    const int lane = tid & 63;
+    if (wave >= 4) {
+        if (out) chain_qh(s, hacc, qh, lane);
+    } else {
+        // level 0: block o = 16 wave; the transposed 16 x 16 block lives in
+        // s.tt[wave / 2] at offset 16 (wave % 2) along both axes
+        const int c = lane >> 2, p = lane & 3;
+        const int bo = 16 * (wave & 1);
+        float *tb = s.tt[wave >> 1];
+        // this lane's coefficients A[i][p + 4e] for all rows i: rows p + 4e of A^T
+        float ac[4][16];
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&tb[(bo + p + 4 * e4) * TS8 + bo + 4 * q4]);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) ac[e4][4 * q4 + jj] = x[jj];
+            }
+        float t[4] = {0.f, 0.f, 0.f, 0.f};  // T[p + 4 e][c]
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+            float part = 0.f;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                if (p + 4 * e4 < ii) part += ac[e4][ii] * t[e4];  // (p + 4 e4 < ii) is lane-dependent
+            part += quad_dpp<0xb1>(part);  // quad_perm [1,0,3,2]
+            part += quad_dpp<0x4e>(part);  // quad_perm [2,3,0,1]
+            const float tv = ((ii == c) ? 1.f : 0.f) - part;
+            if (p == (ii & 3)) t[ii >> 2] = tv;
+        }
+        const int o = 16 * wave;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+            s.a[(o + p + 4 * e4) * AS + o + c] = t[e4];
+            tb[(bo + c) * TS8 + bo + p + 4 * e4] = t[e4];
+        }
+    }
+    __syncthreads();
+    const int m = lane & 15, g = lane >> 4;
+    if (wave == 2 || wave == 3) {
+        if (out) chain_qh(s, hacc, qh, lane);
+    } else if (wave < 2) {
+        // level 1 in diagonal block b = 32 wave:  X = A_10 T_00 ; T_10 = -T_11 X
+        const int b = 32 * wave;
+        const float *tb = s.tt[wave];
+        float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (g < 2) {  // k = 0..15 on lane groups 0, 1; groups 2, 3 carry zeros
+            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + m) * AS + b + 8 * g]);
+            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + m) * AS + b + 8 * g + 4]);
+            const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&tb[m * TS8 + 8 * g]);       // T_00[k][m]
+            const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&tb[m * TS8 + 8 * g + 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                av[e] = a0[e];
+                av[4 + e] = a1[e];
+                bv[e] = b0[e];
+                bv[4 + e] = b1[e];
+            }
+        }
+        bf16x8 ah, al, bh, bl;
+        split8v(av, ah, al);
+        split8v(bv, bh, bl);
+        f32x4 x = {};
+        x = mfma16(ah, bh, x);
+        x = mfma16(ah, bl, x);
+        x = mfma16(al, bh, x);
+        // T_11 X: X (rows 4 g + j) is the first half of the B operand's k
+        // order, the second half is zero
+        const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + m) * AS + b + 16 + 4 * g]);
+        const float tvv[8] = {t4[0], t4[1], t4[2], t4[3], 0.f, 0.f, 0.f, 0.f};
+        const float xv[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
+        split8v(tvv, ah, al);
+        split8v(xv, bh, bl);
+        f32x4 z = {};
+        z = mfma16(ah, bh, z);
+        z = mfma16(ah, bl, z);
+        z = mfma16(al, bh, z);
+        float *tbw = s.tt[wave];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s.a[(b + 16 + 4 * g + j) * AS + b + m] = -z[j];
+        *reinterpret_cast<f32x4 *>(&tbw[m * TS8 + 16 + 4 * g]) = f32x4{-z[0], -z[1], -z[2], -z[3]};
+    }
+    __syncthreads();
+    if (wave == 1) {
+        if (out) chain_qh(s, hacc, qh, lane);
+    } else if (wave == 0) {
+        const int m32 = lane & 31, h = lane >> 5;
+        const float *tb = s.tt[0];  // T_hi,hi transposed
+        f32x16 y = {};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const float *ar = &s.a[(32 + m32) * AS + 16 * kk + 8 * h];
+            const float *br = &tb[m32 * TS8 + 16 * kk + 8 * h];
+            float av[8], bv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                av[e] = ar[e];
+                bv[e] = br[e];
+            }
+            bf16x8 ah, al, bh, bl;
+            split8v(av, ah, al);
+            split8v(bv, bh, bl);
+            y = mfma(ah, bh, y);
+            y = mfma(ah, bl, y);
+            y = mfma(al, bh, y);
+        }
+        f32x16 z = {};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const float *tr = &s.a[(32 + m32) * AS + 32 + 16 * kk + 4 * h];
+            float av[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                av[e] = tr[e];
+                av[4 + e] = tr[8 + e];
+            }
+            bf16x8 ah, al, bh, bl;
+            split8v(av, ah, al);
+            split8(y, kk, bh, bl);
+            z = mfma(ah, bh, z);
+            z = mfma(ah, bl, z);
+            z = mfma(al, bh, z);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s.a[(32 + 8 * (e >> 2) + 4 * h + (e & 3)) * AS + m32] = -z[e];
+    }
+    __syncthreads();
+}
+
+// ---- W and U.  First the six T diag(beta) hi/lo A fragments (waves 0..5,
+// one each); then each wave writes two -W A fragments from W^T = K^T
+// (T diag(beta gamma))^T tiles and forms U = (T diag(beta)) V for its columns.
+__device__ __forceinline__ void prep8_wu(Smem8 &s, const int tid, const int wave, f32x4 (&u)[4]) {
+    const int lane = tid & 63;
+    const int m = lane & 15, g = lane >> 4;
+    if (wave < 6) {
+        const int rt = frag_rt(wave), ks = frag_ks(wave);
+        const float *tr = &s.a[(16 * rt + m) * AS + 32 * ks + 8 * g];
+        const float *bp = &s.beta[32 * ks + 8 * g];
+        float tb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tb[e] = tr[e] * bp[e];
+        bf16x8 hi, lo;
+        split8v(tb, hi, lo);
+        s.thf[0][wave][lane] = hi;
+        s.thf[1][wave][lane] = lo;
+    }
+    // W^T tiles for this wave's two fragments (row tile rt, key steps kk0, kk0 + 1)
+    const int rt = wave >> 1, kk0 = 2 * (wave & 1);
+    const int nks = (rt < 2) ? 1 : 2;  // T is lower triangular
+    bf16x8 tw[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        if (ks >= nks) continue;
+        const float *tr = &s.a[(16 * rt + m) * AS + 32 * ks + 8 * g];
+        const float *bgp = &s.bg[32 * ks + 8 * g];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tw[ks][e] = (bf16)(tr[e] * bgp[e]);
+    }
+    bf16x8 ka[2][2][2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks >= nks) continue;
+            ka[f][ks][0] = lds8(&s.kt[(32 * (kk0 + f) + m) * CS + 32 * ks + 8 * g]);
+            ka[f][ks][1] = lds8(&s.kt[(32 * (kk0 + f) + 16 + m) * CS + 32 * ks + 8 * g]);
+        }
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const int kk = kk0 + f;  // key-dim step of 32: W^T tiles dt = 2 kk and 2 kk + 1
+        f32x4 w0 = {}, w1 = {};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks >= nks) continue;
+            w0 = mfma16(ka[f][ks][0], tw[ks], w0);
+            w1 = mfma16(ka[f][ks][1], tw[ks], w1);
+        }
+        s.wf[rt][kk][lane] = bf16x8{(bf16)(-w0[0]), (bf16)(-w0[1]), (bf16)(-w0[2]), (bf16)(-w0[3]),
+                                    (bf16)(-w1[0]), (bf16)(-w1[1]), (bf16)(-w1[2]), (bf16)(-w1[3])};
+    }
+    __syncthreads();  // T diag(beta) fragments complete
+#pragma unroll
+    for (int r = 0; r < 4; ++r) u[r] = f32x4{};
+    const bf16x8 vv[2] = {lds8(&s.vt[(16 * wave + m) * CS + 8 * g]), lds8(&s.vt[(16 * wave + m) * CS + 32 + 8 * g])};
+#pragma unroll
+    for (int f3 = 0; f3 < 2; ++f3) {
+        bf16x8 th[3][2];
+#pragma unroll
+        for (int fq = 0; fq < 3; ++fq) {
+            th[fq][0] = s.thf[0][3 * f3 + fq][lane];
+            th[fq][1] = s.thf[1][3 * f3 + fq][lane];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+        for (int fq = 0; fq < 3; ++fq) {
+            const int f = 3 * f3 + fq;
+            const int frt = frag_rt(f), fks = frag_ks(f);
+            u[frt] = mfma16(th[fq][0], vv[fks], u[frt]);
+            u[frt] = mfma16(th[fq][1], vv[fks], u[frt]);
+        }
+    }
+    __syncthreads();  // -W fragments complete; k / T fragments free for the next chunk
+}
+
+// ---- state I/O: K x V fp32 state <-> this wave's eight 16 x 16 tiles
+__device__ __forceinline__ void load_state8(f32x4 (&t)[8], const float *src, const int wave, const int lane) {
+    const int m = lane & 15, g = lane >> 4;
+    const float *b = src + 16 * wave + m;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[dt][j] = b[(16 * dt + 4 * g + j) * DV];
+}
+
+__device__ __forceinline__ void store_state8(const f32x4 (&t)[8], float *dst, const int wave, const int lane) {
+    const int m = lane & 15, g = lane >> 4;
+    float *b = dst + 16 * wave + m;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[(16 * dt + 4 * g + j) * DV] = t[dt][j];
+}
+
+// ---- one chunk's output tile of this wave (64 rows x 16 value columns)
+// through a wave-private LDS staging tile: every lane stores 16 contiguous bytes.
+__device__ __forceinline__ void write_o8(Smem8 &s, const FwdParams &p, const SegEntry &e, int j, int c,
+                                         const f32x4 (&ov)[4], const int wave, const int ln) {
+    const int m = ln & 15, g = ln >> 4;
+    float *stg = s.ostage[wave];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) stg[(16 * rt + 4 * g + jj) * OS8 + m] = ov[rt][jj];
+    // the staging tile is private to this wave: LDS keeps the wave's own
+    // write/read order; the fence keeps the compiler's
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const int valid = e.seq_len - c * CH;
+    const int64_t obase = ((e.row0 + (int64_t)c * CH) * p.Hv + j) * DV + 16 * wave;
+    if (p.o_f32) {
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int row = 16 * pass + (ln >> 2), c4 = 4 * (ln & 3);
+            if (row < valid)
+                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.o) + obase + (int64_t)row * p.Hv * DV + c4) =
+                    *reinterpret_cast<const f32x4 *>(&stg[row * OS8 + c4]);
+        }
+    } else {
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int row = 32 * pass + (ln >> 1), c8 = 8 * (ln & 1);
+            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&stg[row * OS8 + c8]);
+            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&stg[row * OS8 + c8 + 4]);
+            const bf16x8 y = {(bf16)x0[0], (bf16)x0[1], (bf16)x0[2], (bf16)x0[3],
+                              (bf16)x1[0], (bf16)x1[1], (bf16)x1[2], (bf16)x1[3]};
+            if (row < valid)
+                *reinterpret_cast<bf16x8 *>(reinterpret_cast<bf16 *>(p.o) + obase + (int64_t)row * p.Hv * DV + c8) = y;
+        }
+    }
+}
+
+// One workgroup per CU (its LDS footprint), two waves per SIMD: schedule for that.
+__global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) gdn_fwd_kernel(FwdParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    Smem &s = *reinterpret_cast<Smem *>(smem_raw);
+    Smem8 &s = *reinterpret_cast<Smem8 *>(smem_raw);
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -596,13 +1151,15 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) 
     }
     const int c_end = e.c_begin + e.c_count;
 
-    // ---- state H[:, this lane's value column] in four 32 x 32 accumulator tiles
-    f32x16 hacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+    // ---- state: value columns 16 wave .. +15, eight 16-row tiles of key dims
+    f32x4 hacc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) hacc[dt] = f32x4{};
     {
         const float *src = nullptr;
         if (from_h0 && p.h0) src = p.h0 + ((int64_t)e.n * p.Hv + j) * DK * DV;
         if (!from_h0 && p.cp_mode == 1 /* EXACT */) src = p.ws_h + ((int64_t)seg * p.Hv + j) * DK * DV;
-        if (src) load_state(hacc, src, wave, lane);
+        if (src) load_state8(hacc, src, wave, lane);
     }
 
     if (c_first < c_end) {
@@ -616,13 +1173,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) 
         in.g = make_rsrc(p.g + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
         in.b = make_rsrc(p.beta + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
 
-        Stage st;
-        load_chunk(in, st, c_first, c_first >= e.c_begin, threadIdx.x);
+        Stage8 st;
+        load_chunk8(in, st, c_first, c_first >= e.c_begin, threadIdx.x, wave);
         // A chunk's output waits in registers and is stored at the top of the
         // next iteration, after that iteration's prefetched inputs have been
         // consumed: memory-counter waits for the prefetch then never have to
         // cover freshly issued output stores.
-        f32x16 ov[2];
+        f32x4 ov[4];
         int pend = -1;  // chunk whose output is held in ov, or -1
         for (int c = c_first; c < c_end; ++c) {
             // The thread index is made opaque once per chunk so that the
@@ -631,93 +1188,107 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_fwd_main_kernel(FwdParams p) 
             int tid = threadIdx.x;
             asm volatile("" : "+v"(tid));
             const int ln = tid & 63;
-            const int m = ln & 31, h = ln >> 5;
+            const int m = ln & 15, g = ln >> 4;
             const bool out = (c >= e.c_begin);  // warm-up chunks only advance the state
-            store_chunk(s, st, out, tid);
+            store_chunk8(s, st, out, tid, wave);
             __syncthreads();
-            if (pend >= 0) write_o(s, p, e, j, pend, ov, wave, ln);  // staging aliases s.a, free until the masks
+            if (pend >= 0) write_o8(s, p, e, j, pend, ov, wave, ln);  // staging aliases s.a, free until the masks
             pend = -1;
-            if (c + 1 < c_end) load_chunk(in, st, c + 1, c + 1 >= e.c_begin, tid);
-
-            prep_products(s, tid, out);
-            prep_inverse(s, tid);
-            f32x16 u[2];
-            prep_wu(s, tid, u);
-
-            // ---- critical chain: v' = U - W H   (and Q H for the output)
-            f32x16 vp[2] = {u[0], u[1]};
-            f32x16 qh[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                bf16x8 hh, hl;
-                split8(hacc[kk >> 1], kk & 1, hh, hl);
+            for (int rt = 0; rt < 4; ++rt) ov[rt] = f32x4{};  // written out: not carried further
+            if (c + 1 < c_end) load_chunk8(in, st, c + 1, c + 1 >= e.c_begin, tid, wave);
+
+            f32x4 qh[4];
+            prep8_products(s, tid, wave, out, hacc, qh);
+            prep8_inverse(s, tid, wave, out, hacc, qh);
+            f32x4 u[4];
+            prep8_wu(s, tid, wave, u);
+
+            // ---- critical chain: v' = U - W H
+            f32x4 vp[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    const bf16x8 a = s.wf[rb][kk][ln];
-                    vp[rb] = mfma(a, hh, vp[rb]);
-                    vp[rb] = mfma(a, hl, vp[rb]);
+            for (int k2 = 0; k2 < 2; ++k2) {
+                bf16x8 hh[2], hl[2], wa[2][4];
+#pragma unroll
+                for (int kq = 0; kq < 2; ++kq) {
+                    const int kk = 2 * k2 + kq;
+                    split_pair(hacc[2 * kk], hacc[2 * kk + 1], hh[kq], hl[kq]);
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) wa[kq][rt] = s.wf[rt][kk][ln];
                 }
-                if (out) {
+                __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) {
-                        const bf16x8 a = lds8_perm(&s.q[(32 * rb + m) * KS], 16 * kk, h);
-                        qh[rb] = mfma(a, hh, qh[rb]);
-                        qh[rb] = mfma(a, hl, qh[rb]);
+                for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) {
+                        vp[rt] = mfma16(wa[kq][rt], hh[kq], vp[rt]);
+                        vp[rt] = mfma16(wa[kq][rt], hl[kq], vp[rt]);
                     }
-                }
             }
             if (out) {
-                // O = scale (diag(gamma) Q H + P v'), staged through LDS per wave
-                f32x16 pv[2] = {f32x16{}, f32x16{}};
+                // O = scale (diag(gamma) Q H + P v')
+                f32x4 pv[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+                bf16x8 pa[2][6];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
+                for (int f = 0; f < 6; ++f) {
+                    pa[0][f] = s.pf[0][f][ln];
+                    pa[1][f] = s.pf[1][f][ln];
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
                     bf16x8 vh, vl;
-                    split8(vp[kk >> 1], kk & 1, vh, vl);
+                    split_pair(vp[2 * ks], vp[2 * ks + 1], vh, vl);
 #pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) {
-                        if (rb == 0 && kk >= 2) continue;  // P is lower triangular
-                        const int t = (rb == 0) ? 0 : (kk < 2 ? 1 : 2);
-                        const bf16x8 ah = s.pf[0][t][kk & 1][ln];
-                        const bf16x8 al = s.pf[1][t][kk & 1][ln];
-                        pv[rb] = mfma(ah, vh, pv[rb]);
-                        pv[rb] = mfma(ah, vl, pv[rb]);
-                        pv[rb] = mfma(al, vh, pv[rb]);
+                    for (int rt = 0; rt < 4; ++rt) {
+                        if (ks == 1 && rt < 2) continue;  // P is lower triangular
+                        const int f = frag_of(rt, ks);
+                        pv[rt] = mfma16(pa[0][f], vh, pv[rt]);
+                        pv[rt] = mfma16(pa[0][f], vl, pv[rt]);
+                        pv[rt] = mfma16(pa[1][f], vh, pv[rt]);
                     }
                 }
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
+                for (int rt = 0; rt < 4; ++rt) {
+                    const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&s.gam[16 * rt + 4 * g]);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = 32 * rb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        ov[rb][r] = p.scale * (s.gam[row] * qh[rb][r] + pv[rb][r]);
-                    }
+                    for (int jj = 0; jj < 4; ++jj) ov[rt][jj] = p.scale * (gm4[jj] * qh[rt][jj] + pv[rt][jj]);
+                }
                 pend = c;
             }
             // ---- H <- gamma_last H + K^T diag(gamma_last / gamma) v'
             const float glast = s.gam[CH - 1];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
+            for (int rt = 0; rt < 4; ++rt) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s.dec[16 * rt + 4 * g]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) vp[rb][r] *= s.dec[32 * rb + 8 * (r >> 2) + 4 * h + (r & 3)];
+                for (int jj = 0; jj < 4; ++jj) vp[rt][jj] *= d4[jj];
+            }
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) hacc[mb] *= glast;
+            for (int dt = 0; dt < 8; ++dt) hacc[dt] *= glast;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+            for (int ks = 0; ks < 2; ++ks) {
                 bf16x8 vh, vl;
-                split8(vp[kk >> 1], kk & 1, vh, vl);
+                split_pair(vp[2 * ks], vp[2 * ks + 1], vh, vl);
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    const bf16x8 a = lds8_perm(&s.kt[(32 * mb + m) * CS], 16 * kk, h);
-                    hacc[mb] = mfma(a, vh, hacc[mb]);
-                    hacc[mb] = mfma(a, vl, hacc[mb]);
+                for (int d2 = 0; d2 < 2; ++d2) {
+                    bf16x8 ka[4];
+#pragma unroll
+                    for (int dq = 0; dq < 4; ++dq) ka[dq] = lds8_perm16(&s.kt[(16 * (4 * d2 + dq) + m) * CS], 32 * ks, g);
+                    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+                    for (int dq = 0; dq < 4; ++dq) {
+                        hacc[4 * d2 + dq] = mfma16(ka[dq], vh, hacc[4 * d2 + dq]);
+                        hacc[4 * d2 + dq] = mfma16(ka[dq], vl, hacc[4 * d2 + dq]);
+                    }
                 }
             }
             __syncthreads();  // LDS is rewritten by the next chunk
         }
-        if (pend >= 0) write_o(s, p, e, j, pend, ov, wave, threadIdx.x & 63);
+        if (pend >= 0) write_o8(s, p, e, j, pend, ov, wave, threadIdx.x & 63);
     }
 
-    if (e.last && p.ht) store_state(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
+    if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
 }
 
 // ---------------------------------------------------------------- exact context parallelism
@@ -919,13 +1490,13 @@ __global__ void __launch_bounds__(256) gdn_chunk_cumsum_kernel(const float *g, f
 
 // ---------------------------------------------------------------- launchers
 int launch_fwd_main(const FwdParams &p, void *stream) {
-    static const size_t smem = sizeof(Smem);
+    static const size_t smem = sizeof(Smem8);
     static const int attr_rc =
-        (int)hipFuncSetAttribute((const void *)gdn_fwd_main_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)hipFuncSetAttribute((const void *)gdn_fwd_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)smem);
     if (attr_rc != 0) return attr_rc;
     const unsigned grid = (unsigned)p.num_segments * (unsigned)p.Hv;
-    hipLaunchKernelGGL(gdn_fwd_main_kernel, dim3(grid), dim3(NTHREADS), smem, (hipStream_t)stream, p);
+    hipLaunchKernelGGL(gdn_fwd_kernel, dim3(grid), dim3(NT8), smem, (hipStream_t)stream, p);
     return (int)hipGetLastError();
 }
 
