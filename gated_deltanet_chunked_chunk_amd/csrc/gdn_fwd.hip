@@ -550,7 +550,6 @@ struct __attribute__((aligned(16))) Smem8 {
     float tt[2][32 * TS8];
     float graw[CH], beta[CH], gcum[CH], gam[CH], dec[CH], bg[CH];
     float ep[CH], em[CH], rowa[CH];   // e^{G - G_31}, e^{G_31 - G}, beta e^{G - G_31}
-    int fact_ok;                      // every |G - G_31| < 80: the factored decays are finite
 };
 
 // The six 16-row x 32-column tiles of a 64 x 64 lower-triangular matrix that
@@ -683,10 +682,14 @@ __device__ __forceinline__ void chain_qh(const Smem8 &s, const f32x4 (&hacc)[8],
 
 // ---- cumsum, decay factors, masked beta-weighted K K^T (into s.a, and the
 // diagonal 32 x 32 blocks transposed into s.tt) and the causal decayed P as A
-// fragments.  Roles (wave w runs on SIMD w mod 4):
-//   wave 0: cumsum and factors, then its own Q H (it carries the inverse later)
+// fragments.  Every wave forms the chunk's cumulative gates and decay factors
+// itself (a DPP scan, lane = token) and writes them to the shared arrays: all
+// waves write identical values, and each reads back only what it wrote, so no
+// barrier separates the scan from the products.  Roles (wave w on SIMD w % 4):
+//   wave 0: Q H (it carries the inverse later)
 //   waves 1..3: K K^T 32 x 32 tiles (0,0) (1,0) (1,1)
-//   waves 4..7: the six P fragments (4: 0, 4; 5: 1, 5; 6: 2; 7: 3)
+//   waves 4..7: the ten non-zero 16 x 16 tiles of P, as P fragments
+//               (4: 0 and 5; 5: 1 and 4; 6: 2; 7: 3)
 // A P fragment (rt, ks) stacks the P^T = K Q^T tiles (s tile 2 ks, i tile rt)
 // and (2 ks + 1, rt); the accumulator of each tile is the fragment half.
 __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const int wave, const bool out,
@@ -697,13 +700,14 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
     f32x16 acck = {};
     const int rbi = (wave >= 2) ? 1 : 0, rbs = (wave == 3) ? 1 : 0;
     int pfr[2] = {-1, -1};
-    if (wave == 4) { pfr[0] = 0; pfr[1] = 4; }
-    if (wave == 5) { pfr[0] = 1; pfr[1] = 5; }
+    if (wave == 4) { pfr[0] = 0; pfr[1] = 5; }
+    if (wave == 5) { pfr[0] = 1; pfr[1] = 4; }
     if (wave == 6) pfr[0] = 2;
     if (wave == 7) pfr[0] = 3;
     f32x4 accp[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
 
-    if (wave == 0) {
+    bool fact;
+    {
         const float x = wave_prefix_sum(s.graw[lane]);
         const float glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
         const float gref = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
@@ -718,8 +722,9 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
         s.ep[lane] = epv;
         s.em[lane] = __expf(-d);
         s.rowa[lane] = bt * epv;
-        const bool ok = __all(fabsf(d) < 80.f);
-        if (lane == 0) s.fact_ok = ok ? 1 : 0;
+        fact = __all(fabsf(d) < 80.f);  // the factored decays are finite
+    }
+    if (wave == 0) {
         if (out) chain_qh(s, hacc, qh, lane);
     }
     if (wave >= 1 && wave <= 3) {
@@ -737,33 +742,6 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) acck = mfma(xa[kk], xb[kk], acck);
         }
-    }
-    if (out) {
-#pragma unroll
-        for (int pi = 0; pi < 2; ++pi) {
-            if (pfr[pi] < 0) continue;
-            const int rt = frag_rt(pfr[pi]), ks = frag_ks(pfr[pi]);
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int st = 2 * ks + half;
-                if (st > rt) continue;  // tile entirely above the diagonal
-                const bf16 *ra = &s.k[(16 * st + m) * KS + 8 * g];
-                const bf16 *rb = &s.q[(16 * rt + m) * KS + 8 * g];
-                bf16x8 xa[4], xb[4];
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) {
-                    xa[kk] = lds8(ra + 32 * kk);
-                    xb[kk] = lds8(rb + 32 * kk);
-                }
-                __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) accp[pi][half] = mfma16(xa[kk], xb[kk], accp[pi][half]);
-            }
-        }
-    }
-    __syncthreads();
-    const bool fact = __builtin_amdgcn_readfirstlane(s.fact_ok) != 0;
-    if (wave >= 1 && wave <= 3) {
         const int col = 32 * rbs + m32;
         float v[16];
         if (fact) {
@@ -797,7 +775,28 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
                     f32x4{v[4 * ii], v[4 * ii + 1], v[4 * ii + 2], v[4 * ii + 3]};
         }
     }
-    if (out) {
+    if (out && wave >= 4) {
+#pragma unroll
+        for (int pi = 0; pi < 2; ++pi) {
+            if (pfr[pi] < 0) continue;
+            const int rt = frag_rt(pfr[pi]), ks = frag_ks(pfr[pi]);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int st = 2 * ks + half;
+                if (st > rt) continue;  // tile entirely above the diagonal
+                const bf16 *ra = &s.k[(16 * st + m) * KS + 8 * g];
+                const bf16 *rb = &s.q[(16 * rt + m) * KS + 8 * g];
+                bf16x8 xa[4], xb[4];
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    xa[kk] = lds8(ra + 32 * kk);
+                    xb[kk] = lds8(rb + 32 * kk);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) accp[pi][half] = mfma16(xa[kk], xb[kk], accp[pi][half]);
+            }
+        }
 #pragma unroll
         for (int pi = 0; pi < 2; ++pi) {
             if (pfr[pi] < 0) continue;
@@ -841,11 +840,11 @@ __device__ __forceinline__ float quad_dpp(float v) {
 //   level 0 (waves 0..3, one 16 x 16 diagonal block each): forward
 //     substitution with lane = 4 c + p; the four lanes of column c split
 //     each row's dot product over s = p mod 4 and add it with two DPP steps;
-//   level 1 (waves 0, 1): T_10 = -T_11 (A_10 T_00) inside each 32 x 32
+//   level 1 (waves 0, 2): T_10 = -T_11 (A_10 T_00) inside each 32 x 32
 //     diagonal block, two chained 16 x 16 MFMA products (hi/lo operands);
 //   level 2 (wave 0): T_lo,hi = -T_lo,lo (A_lo,hi T_hi,hi), 32 x 32 MFMA.
 // The other waves compute their Q H meanwhile (waves 4..7 during level 0,
-// 2 and 3 during level 1, 1 during level 2), never on a step's critical wave.
+// 1 and 3 during level 1, 2 during level 2; wave 0 did during the products).
 __device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int wave, const bool out,
                                               const f32x4 (&hacc)[8], f32x4 (&qh)[4]) {
     const int lane = tid & 63;
@@ -888,12 +887,13 @@ __device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int
     }
     __syncthreads();
     const int m = lane & 15, g = lane >> 4;
-    if (wave == 2 || wave == 3) {
+    if (wave == 1 || wave == 3) {
         if (out) chain_qh(s, hacc, qh, lane);
-    } else if (wave < 2) {
-        // level 1 in diagonal block b = 32 wave:  X = A_10 T_00 ; T_10 = -T_11 X
-        const int b = 32 * wave;
-        const float *tb = s.tt[wave];
+    } else if (wave == 0 || wave == 2) {
+        // level 1 in diagonal block b = 32 blk:  X = A_10 T_00 ; T_10 = -T_11 X
+        const int blk = wave >> 1;
+        const int b = 32 * blk;
+        const float *tb = s.tt[blk];
         float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (g < 2) {  // k = 0..15 on lane groups 0, 1; groups 2, 3 carry zeros
             const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + m) * AS + b + 8 * g]);
@@ -926,13 +926,13 @@ __device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int
         z = mfma16(ah, bh, z);
         z = mfma16(ah, bl, z);
         z = mfma16(al, bh, z);
-        float *tbw = s.tt[wave];
+        float *tbw = s.tt[blk];
 #pragma unroll
         for (int j = 0; j < 4; ++j) s.a[(b + 16 + 4 * g + j) * AS + b + m] = -z[j];
         *reinterpret_cast<f32x4 *>(&tbw[m * TS8 + 16 + 4 * g]) = f32x4{-z[0], -z[1], -z[2], -z[3]};
     }
     __syncthreads();
-    if (wave == 1) {
+    if (wave == 2) {
         if (out) chain_qh(s, hacc, qh, lane);
     } else if (wave == 0) {
         const int m32 = lane & 31, h = lane >> 5;
@@ -1112,7 +1112,7 @@ __device__ __forceinline__ void write_o8(Smem8 &s, const FwdParams &p, const Seg
 }
 
 // One workgroup per CU (its LDS footprint), two waves per SIMD: schedule for that.
-__global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) gdn_fwd_kernel(FwdParams p) {
+__global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) gdn_fwd_main_kernel(FwdParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     Smem8 &s = *reinterpret_cast<Smem8 *>(smem_raw);
 
@@ -1492,11 +1492,11 @@ __global__ void __launch_bounds__(256) gdn_chunk_cumsum_kernel(const float *g, f
 int launch_fwd_main(const FwdParams &p, void *stream) {
     static const size_t smem = sizeof(Smem8);
     static const int attr_rc =
-        (int)hipFuncSetAttribute((const void *)gdn_fwd_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)hipFuncSetAttribute((const void *)gdn_fwd_main_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)smem);
     if (attr_rc != 0) return attr_rc;
     const unsigned grid = (unsigned)p.num_segments * (unsigned)p.Hv;
-    hipLaunchKernelGGL(gdn_fwd_kernel, dim3(grid), dim3(NT8), smem, (hipStream_t)stream, p);
+    hipLaunchKernelGGL(gdn_fwd_main_kernel, dim3(grid), dim3(NT8), smem, (hipStream_t)stream, p);
     return (int)hipGetLastError();
 }
 
