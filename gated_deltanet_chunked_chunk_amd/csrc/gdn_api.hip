@@ -116,9 +116,10 @@ int make_plan(const gdn_fwd_desc *d, Plan *P) {
         total_chunks = d->B * (int64_t)gdn::seq_chunks(d->T);
     }
     if (total_chunks > INT32_MAX) return fail(GDN_EINVAL, "too many chunks");
-    // each sequence of each head is read through one buffer resource whose
-    // byte range must stay below 2^31
-    const int64_t row_bytes = std::max<int64_t>((int64_t)d->H_qk * d->K * 2, (int64_t)d->H_v * d->V * 2);
+    // each sequence of each head is read (and its output written) through one
+    // buffer resource whose byte range must stay below 2^31
+    const int64_t osz = d->o_dtype == GDN_DTYPE_F32 ? 4 : 2;
+    const int64_t row_bytes = std::max<int64_t>((int64_t)d->H_qk * d->K * 2, (int64_t)d->H_v * d->V * osz);
     if ((max_len + gdn::kChunk) * row_bytes >= ((int64_t)1 << 31))
         return fail(GDN_EUNSUPPORTED, "a sequence of %lld tokens exceeds the 2 GiB per-sequence range",
                     (long long)max_len);

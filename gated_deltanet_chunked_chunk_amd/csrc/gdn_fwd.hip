@@ -47,6 +47,7 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int CH = kChunk;   // 64
 constexpr int DK = kDimK;    // 128
@@ -529,7 +530,6 @@ __device__ __forceinline__ void store_state(const f32x16 (&t)[4], float *dst, co
 // needs only the chunk-start state) is computed by the waves that are idle
 // while others run the cumsum/products and the inverse.
 constexpr int NT8 = 512;
-constexpr int OS8 = 16 + 4;  // fp32 row stride of a wave's 64 x 16 output staging tile
 constexpr int TS8 = 32 + 4;  // fp32 row stride of the transposed 32 x 32 diagonal blocks
 
 struct __attribute__((aligned(16))) Smem8 {
@@ -540,10 +540,7 @@ struct __attribute__((aligned(16))) Smem8 {
     bf16 q[CH * KS];                  // Q
     bf16 kt[DK * CS];                 // K^T, row = key dim
     bf16 vt[DV * CS];                 // V^T, row = value dim
-    union {
-        float a[CH * AS];             // A, inverted in place into T
-        float ostage[8][CH * OS8];    // per-wave output tile on its way to HBM
-    };
+    float a[CH * AS];                 // A, inverted in place into T
     bf16x8 wf[4][4][64];              // -W as A fragments [row tile][k step][lane]
     bf16x8 pf[2][6][64];              // P as A fragments [hi, lo][fragment][lane]
     // the two 32 x 32 diagonal blocks of A, then of T, transposed ([block][col][row])
@@ -583,6 +580,12 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
 }
 
+// Permutation inside each quad of lanes (quad_perm control)
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
 __device__ __forceinline__ float wave_prefix_sum(float x) {
     x += dpp_f<0x111, 0xf>(x);  // row_shr:1
     x += dpp_f<0x112, 0xf>(x);  // row_shr:2
@@ -595,15 +598,24 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 
 // ---- staging of one chunk: waves 0..3 take K (natural and transposed) and
 // g, beta; waves 4..7 take V (transposed) and Q.  Thread t' = t mod 256 holds
-// rows 4 (t' % 16) .. +3, columns 8 (t' / 16) .. +7 of its tiles.
+// rows 4 rg .. +3, columns 8 cg .. +7 of its tiles, with cg = t' mod 8 +
+// 8 (t' / 128) and rg = (t' / 8) mod 16: eight consecutive lanes cover one
+// 128-byte row segment, so each load instruction touches 8 full 128-byte
+// lines rather than 16 half lines.
+__device__ __forceinline__ void stage_coords(int t, int &rg, int &cg) {
+    const int tt = t & 255;
+    cg = (tt & 7) | ((tt >> 4) & 8);
+    rg = (tt >> 3) & 15;
+}
+
 struct Stage8 {
     u32x4 x[4], y[4];
     float g, b;
 };
 
 __device__ __forceinline__ void load_chunk8(const Inputs &in, Stage8 &st, int c, bool need_q, int t, int wave) {
-    const int tt = t & 255;
-    const int rg = tt & 15, cg = tt >> 4;
+    int rg, cg;
+    stage_coords(t, rg, cg);
     const bool kv = wave < 4;  // wave-uniform role: K (waves 0..3) or V and Q (waves 4..7)
     const __amdgpu_buffer_rsrc_t rx = kv ? in.k : in.v;
     const unsigned sx = kv ? in.kstride : in.vstride;
@@ -627,8 +639,8 @@ __device__ __forceinline__ void load_chunk8(const Inputs &in, Stage8 &st, int c,
 }
 
 __device__ __forceinline__ void store_chunk8(Smem8 &s, const Stage8 &st, bool need_q, int t, int wave) {
-    const int tt = t & 255;
-    const int rg = tt & 15, cg = tt >> 4;
+    int rg, cg;
+    stage_coords(t, rg, cg);
     uint2 tr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -690,10 +702,13 @@ __device__ __forceinline__ void chain_qh(const Smem8 &s, const f32x4 (&hacc)[8],
 //   waves 1..3: K K^T 32 x 32 tiles (0,0) (1,0) (1,1)
 //   waves 4..7: the ten non-zero 16 x 16 tiles of P, as P fragments
 //               (4: 0 and 5; 5: 1 and 4; 6: 2; 7: 3)
+// Waves 0..3 finish well before the P waves: they issue the previous chunk's
+// output stores (io_o) and the next chunk's loads (io_ld) while they wait.
 // A P fragment (rt, ks) stacks the P^T = K Q^T tiles (s tile 2 ks, i tile rt)
 // and (2 ks + 1, rt); the accumulator of each tile is the fragment half.
+template <typename IO, typename LD>
 __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const int wave, const bool out,
-                                               const f32x4 (&hacc)[8], f32x4 (&qh)[4]) {
+                                               const f32x4 (&hacc)[8], f32x4 (&qh)[4], IO &&io_o, LD &&io_ld) {
     const int lane = tid & 63;
     const int m32 = lane & 31, h32 = lane >> 5;
     const int m = lane & 15, g = lane >> 4;
@@ -826,14 +841,13 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
             s.pf[1][pfr[pi]][lane] = lo;
         }
     }
+    if (wave < 4) {
+        io_o();
+        io_ld();
+    }
     __syncthreads();
 }
 
-// DPP row-local helpers for the 4-lane groups of the level-0 solve
-template <int CTRL>
-__device__ __forceinline__ float quad_dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
-}
 
 // ---- in-place inverse of (I + A), T = (I + A)^{-1}, in s.a (row-major) and
 // s.tt (transposed diagonal 32 x 32 blocks, needed by the merges):
@@ -844,9 +858,12 @@ __device__ __forceinline__ float quad_dpp(float v) {
 //     diagonal block, two chained 16 x 16 MFMA products (hi/lo operands);
 //   level 2 (wave 0): T_lo,hi = -T_lo,lo (A_lo,hi T_hi,hi), 32 x 32 MFMA.
 // The other waves compute their Q H meanwhile (waves 4..7 during level 0,
-// 1 and 3 during level 1, 2 during level 2; wave 0 did during the products).
+// 1 and 3 during level 1, 2 during level 2; wave 0 did during the products);
+// waves 4..7 issue the previous chunk's output stores during level 1 and the
+// next chunk's loads during level 2.
+template <typename IO, typename LD>
 __device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int wave, const bool out,
-                                              const f32x4 (&hacc)[8], f32x4 (&qh)[4]) {
+                                              const f32x4 (&hacc)[8], f32x4 (&qh)[4], IO &&io_o, LD &&io_ld) {
     const int lane = tid & 63;
     if (wave >= 4) {
         if (out) chain_qh(s, hacc, qh, lane);
@@ -887,9 +904,11 @@ __device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int
     }
     __syncthreads();
     const int m = lane & 15, g = lane >> 4;
-    if (wave == 1 || wave == 3) {
+    if (wave >= 4) {
+        io_o();
+    } else if (wave == 1 || wave == 3) {
         if (out) chain_qh(s, hacc, qh, lane);
-    } else if (wave == 0 || wave == 2) {
+    } else {
         // level 1 in diagonal block b = 32 blk:  X = A_10 T_00 ; T_10 = -T_11 X
         const int blk = wave >> 1;
         const int b = 32 * blk;
@@ -932,7 +951,9 @@ __device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int
         *reinterpret_cast<f32x4 *>(&tbw[m * TS8 + 16 + 4 * g]) = f32x4{-z[0], -z[1], -z[2], -z[3]};
     }
     __syncthreads();
-    if (wave == 2) {
+    if (wave >= 4) {
+        io_ld();
+    } else if (wave == 2) {
         if (out) chain_qh(s, hacc, qh, lane);
     } else if (wave == 0) {
         const int m32 = lane & 31, h = lane >> 5;
@@ -1076,37 +1097,42 @@ __device__ __forceinline__ void store_state8(const f32x4 (&t)[8], float *dst, co
 
 // ---- one chunk's output tile of this wave (64 rows x 16 value columns)
 // through a wave-private LDS staging tile: every lane stores 16 contiguous bytes.
-__device__ __forceinline__ void write_o8(Smem8 &s, const FwdParams &p, const SegEntry &e, int j, int c,
-                                         const f32x4 (&ov)[4], const int wave, const int ln) {
+// ---- one chunk's output from the accumulator registers straight to HBM.
+// Lane (m, g) holds value column 16 wave + m of rows 16 rt + 4 g + jj; a 4 x 4
+// transpose inside each quad of lanes (two DPP butterfly stages) gives lane
+// m = 4 a + b row 16 rt + 4 g + b, columns 16 wave + 4 a .. +3, so each row
+// tile leaves in one 16-byte (fp32) or 8-byte (bf16) store per lane.  The
+// buffer resource spans this sequence of this head: rows past the sequence
+// end are dropped by the hardware range check.
+__device__ __forceinline__ void write_o_regs(const FwdParams &p, const __amdgpu_buffer_rsrc_t ro, const int c,
+                                             const f32x4 (&ov)[4], const int wave, const int ln) {
     const int m = ln & 15, g = ln >> 4;
-    float *stg = s.ostage[wave];
+    const int qa = m >> 2, qb = m & 3;
+    const unsigned es = p.o_f32 ? 4u : 2u;
+    const unsigned rstride = (unsigned)p.Hv * DV * es;
+    const unsigned col = (unsigned)(16 * wave + 4 * qa) * es;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt) {
+        float x[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) stg[(16 * rt + 4 * g + jj) * OS8 + m] = ov[rt][jj];
-    // the staging tile is private to this wave: LDS keeps the wave's own
-    // write/read order; the fence keeps the compiler's
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    const int valid = e.seq_len - c * CH;
-    const int64_t obase = ((e.row0 + (int64_t)c * CH) * p.Hv + j) * DV + 16 * wave;
-    if (p.o_f32) {
-#pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
-            const int row = 16 * pass + (ln >> 2), c4 = 4 * (ln & 3);
-            if (row < valid)
-                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.o) + obase + (int64_t)row * p.Hv * DV + c4) =
-                    *reinterpret_cast<const f32x4 *>(&stg[row * OS8 + c4]);
+        for (int jj = 0; jj < 4; ++jj) {  // stage 1: swap with lane b ^ 1 where bit 0 of b and jj differ
+            const float y = quad_dpp<0xb1>(ov[rt][jj ^ 1]);
+            x[jj] = ((qb ^ jj) & 1) ? y : ov[rt][jj];
         }
-    } else {
+        float w[4];
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int row = 32 * pass + (ln >> 1), c8 = 8 * (ln & 1);
-            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(&stg[row * OS8 + c8]);
-            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(&stg[row * OS8 + c8 + 4]);
-            const bf16x8 y = {(bf16)x0[0], (bf16)x0[1], (bf16)x0[2], (bf16)x0[3],
-                              (bf16)x1[0], (bf16)x1[1], (bf16)x1[2], (bf16)x1[3]};
-            if (row < valid)
-                *reinterpret_cast<bf16x8 *>(reinterpret_cast<bf16 *>(p.o) + obase + (int64_t)row * p.Hv * DV + c8) = y;
+        for (int jj = 0; jj < 4; ++jj) {  // stage 2: swap with lane b ^ 2 where bit 1 of b and jj differ
+            const float y = quad_dpp<0x4e>(x[jj ^ 2]);
+            w[jj] = ((qb ^ jj) & 2) ? y : x[jj];
+        }
+        const unsigned off = (unsigned)(c * CH + 16 * rt + 4 * g + qb) * rstride + col;
+        if (p.o_f32) {
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{__float_as_uint(w[0]), __float_as_uint(w[1]), __float_as_uint(w[2]), __float_as_uint(w[3])}, ro,
+                (int)off, 0, 0);
+        } else {
+            const bf16x4 h = {(bf16)w[0], (bf16)w[1], (bf16)w[2], (bf16)w[3]};
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), ro, (int)off, 0, 0);
         }
     }
 }
@@ -1172,6 +1198,9 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
         in.v = make_rsrc(p.v + (e.row0 * p.Hv + j) * DV, (int64_t)e.seq_len * in.vstride);
         in.g = make_rsrc(p.g + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
         in.b = make_rsrc(p.beta + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
+        const int64_t oes = p.o_f32 ? 4 : 2;
+        const __amdgpu_buffer_rsrc_t ro =
+            make_rsrc(static_cast<char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes, (int64_t)e.seq_len * p.Hv * DV * oes);
 
         Stage8 st;
         load_chunk8(in, st, c_first, c_first >= e.c_begin, threadIdx.x, wave);
@@ -1192,15 +1221,21 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             const bool out = (c >= e.c_begin);  // warm-up chunks only advance the state
             store_chunk8(s, st, out, tid, wave);
             __syncthreads();
-            if (pend >= 0) write_o8(s, p, e, j, pend, ov, wave, ln);  // staging aliases s.a, free until the masks
-            pend = -1;
+            // the previous chunk's output stores and the next chunk's loads,
+            // issued by each wave in a window where it would otherwise wait
+            auto io_o = [&]() {
+                if (pend >= 0) write_o_regs(p, ro, pend, ov, wave, ln);
+                pend = -1;
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) ov[rt] = f32x4{};  // written out: not carried further
-            if (c + 1 < c_end) load_chunk8(in, st, c + 1, c + 1 >= e.c_begin, tid, wave);
+                for (int rt = 0; rt < 4; ++rt) ov[rt] = f32x4{};  // written out: not carried further
+            };
+            auto io_ld = [&]() {
+                if (c + 1 < c_end) load_chunk8(in, st, c + 1, c + 1 >= e.c_begin, tid, wave);
+            };
 
             f32x4 qh[4];
-            prep8_products(s, tid, wave, out, hacc, qh);
-            prep8_inverse(s, tid, wave, out, hacc, qh);
+            prep8_products(s, tid, wave, out, hacc, qh, io_o, io_ld);
+            prep8_inverse(s, tid, wave, out, hacc, qh, io_o, io_ld);
             f32x4 u[4];
             prep8_wu(s, tid, wave, u);
 
@@ -1285,7 +1320,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             }
             __syncthreads();  // LDS is rewritten by the next chunk
         }
-        if (pend >= 0) write_o8(s, p, e, j, pend, ov, wave, threadIdx.x & 63);
+        if (pend >= 0) write_o_regs(p, ro, pend, ov, wave, threadIdx.x & 63);
     }
 
     if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);

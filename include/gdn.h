@@ -32,8 +32,8 @@
  *     not overlap initial_state or any other tensor.
  *   - q, k, v and o must be 16-byte aligned, g and beta 4-byte aligned.
  *   - One sequence of one head must span less than 2 GiB of its tensor's rows
- *     ((longest sequence + 64) * max(H_qk * K, H_v * V) * 2 bytes < 2^31),
- *     otherwise GDN_EUNSUPPORTED.
+ *     ((longest sequence + 64) * max(H_qk * K * 2, H_v * V * sizeof(o element))
+ *     bytes < 2^31), otherwise GDN_EUNSUPPORTED.
  *   - Return value: GDN_OK (0) or a negative gdn_status.  Arguments are fully
  *     validated before anything is enqueued, so a failed call launches
  *     nothing.  gdn_last_error() gives a message for the calling thread's
