@@ -538,16 +538,18 @@ struct __attribute__((aligned(16))) Smem8 {
         bf16x8 thf[2][6][64];         // T diag(beta), hi and lo A fragments (W/U phase)
     };
     bf16 q[CH * KS];                  // Q
-    bf16 kt[DK * CS];                 // K^T, row = key dim
+    bf16 kt[2][DK * CS];              // K^T, row = key dim (two chunks in flight)
     bf16 vt[DV * CS];                 // V^T, row = value dim
     float a[CH * AS];                 // A, inverted in place into T
     bf16x8 wf[4][4][64];              // -W as A fragments [row tile][k step][lane]
-    bf16x8 pf[2][6][64];              // P as A fragments [hi, lo][fragment][lane]
+    bf16x8 pf[2][2][6][64];           // P as A fragments [chunk parity][hi, lo][fragment][lane]
     // the two 32 x 32 diagonal blocks of A, then of T, transposed ([block][col][row])
     float tt[2][32 * TS8];
-    float graw[CH], beta[CH], gcum[CH], gam[CH], dec[CH], bg[CH];
+    float gam[2][CH], dec[2][CH];     // e^{G}, e^{G_last - G} (two chunks in flight)
+    float graw[CH], beta[CH], gcum[CH], bg[CH];
     float ep[CH], em[CH], rowa[CH];   // e^{G - G_31}, e^{G_31 - G}, beta e^{G - G_31}
 };
+static_assert(sizeof(Smem8) <= 160 * 1024, "one workgroup's LDS must fit a CU");
 
 // The six 16-row x 32-column tiles of a 64 x 64 lower-triangular matrix that
 // hold non-zeros: (row tile, k step) = (0,0) (1,0) (2,0) (3,0) (2,1) (3,1).
@@ -597,11 +599,17 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 }
 
 // ---- staging of one chunk: waves 0..3 take K (natural and transposed) and
-// g, beta; waves 4..7 take V (transposed) and Q.  Thread t' = t mod 256 holds
-// rows 4 rg .. +3, columns 8 cg .. +7 of its tiles, with cg = t' mod 8 +
-// 8 (t' / 128) and rg = (t' / 8) mod 16: eight consecutive lanes cover one
-// 128-byte row segment, so each load instruction touches 8 full 128-byte
-// lines rather than 16 half lines.
+// waves 4..7 take V (transposed); thread t' = t mod 256 holds rows
+// 4 rg .. +3, columns 8 cg .. +7 of its tile, with cg = t' mod 8 +
+// 8 (t' / 128) and rg = (t' / 8) mod 16, so eight consecutive lanes cover one
+// 128-byte row segment.  Q is spread over all 512 threads (two 16-byte pieces
+// each, consecutive lanes along a row) and g, beta over the first 64.
+// Every load is issued unconditionally: a piece that is not wanted (no next
+// chunk, a warm-up chunk's Q, threads past 64 for g and beta) gets an offset
+// beyond the buffer range and comes back as zeros without a memory access.
+// With no branch around them, the staging registers keep one allocation
+// across the loop, and no copy of in-flight load results (which would wait
+// for every outstanding memory operation) is ever needed.
 __device__ __forceinline__ void stage_coords(int t, int &rg, int &cg) {
     const int tt = t & 255;
     cg = (tt & 7) | ((tt >> 4) & 8);
@@ -609,36 +617,39 @@ __device__ __forceinline__ void stage_coords(int t, int &rg, int &cg) {
 }
 
 struct Stage8 {
-    u32x4 x[4], y[4];
+    u32x4 x[4], y[2];
     float g, b;
 };
 
-__device__ __forceinline__ void load_chunk8(const Inputs &in, Stage8 &st, int c, bool need_q, int t, int wave) {
+constexpr unsigned kOutOfRange = 0x80000000u;  // beyond every buffer range (all are below 2^31 bytes)
+
+__device__ __forceinline__ void load_chunk8(const Inputs &in, Stage8 &st, int c, bool need_q, int t, int wave,
+                                            bool valid) {
     int rg, cg;
     stage_coords(t, rg, cg);
-    const bool kv = wave < 4;  // wave-uniform role: K (waves 0..3) or V and Q (waves 4..7)
+    const bool kv = wave < 4;  // wave-uniform role: K (waves 0..3) or V (waves 4..7)
     const __amdgpu_buffer_rsrc_t rx = kv ? in.k : in.v;
     const unsigned sx = kv ? in.kstride : in.vstride;
-    const bool ld_q = !kv && need_q;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const unsigned tok = (unsigned)(c * CH + 4 * rg + r);
-        st.x[r] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(tok * sx + 16u * cg), 0, 0);
-        u32x4 y = {0u, 0u, 0u, 0u};
-        if (ld_q) y = __builtin_amdgcn_raw_buffer_load_b128(in.q, (int)(tok * in.kstride + 16u * cg), 0, 0);
-        st.y[r] = y;
+        const unsigned off = valid ? tok * sx + 16u * cg : kOutOfRange;
+        st.x[r] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
     }
-    float gv = 0.f, bv = 0.f;
-    if (t < CH) {
-        const unsigned tok = (unsigned)(c * CH + t);
-        gv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.g, (int)(tok * in.gstride), 0, 0));
-        bv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.b, (int)(tok * in.gstride), 0, 0));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int piece = t + NT8 * i;
+        const unsigned tok = (unsigned)(c * CH + (piece >> 4));
+        const unsigned off = (valid && need_q) ? tok * in.kstride + 16u * (piece & 15) : kOutOfRange;
+        st.y[i] = __builtin_amdgcn_raw_buffer_load_b128(in.q, (int)off, 0, 0);
     }
-    st.g = gv;
-    st.b = bv;
+    const unsigned tok = (unsigned)(c * CH + t);
+    const unsigned goff = (valid && t < CH) ? tok * in.gstride : kOutOfRange;
+    st.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.g, (int)goff, 0, 0));
+    st.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.b, (int)goff, 0, 0));
 }
 
-__device__ __forceinline__ void store_chunk8(Smem8 &s, const Stage8 &st, bool need_q, int t, int wave) {
+__device__ __forceinline__ void store_chunk8(Smem8 &s, const Stage8 &st, int t, int wave, int buf) {
     int rg, cg;
     stage_coords(t, rg, cg);
     uint2 tr[8];
@@ -650,14 +661,15 @@ __device__ __forceinline__ void store_chunk8(Smem8 &s, const Stage8 &st, bool ne
 #pragma unroll
         for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4 *>(&s.k[(4 * rg + r) * KS + 8 * cg]) = st.x[r];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.kt[(8 * cg + e) * CS + 4 * rg]) = tr[e];
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.kt[buf][(8 * cg + e) * CS + 4 * rg]) = tr[e];
     } else {
-        if (need_q) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4 *>(&s.q[(4 * rg + r) * KS + 8 * cg]) = st.y[r];
-        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.vt[(8 * cg + e) * CS + 4 * rg]) = tr[e];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int piece = t + NT8 * i;
+        *reinterpret_cast<u32x4 *>(&s.q[(piece >> 4) * KS + 8 * (piece & 15)]) = st.y[i];
     }
     if (t < CH) {
         s.graw[t] = st.g;
@@ -697,28 +709,26 @@ __device__ __forceinline__ void chain_qh(const Smem8 &s, const f32x4 (&hacc)[8],
 // fragments.  Every wave forms the chunk's cumulative gates and decay factors
 // itself (a DPP scan, lane = token) and writes them to the shared arrays: all
 // waves write identical values, and each reads back only what it wrote, so no
-// barrier separates the scan from the products.  Roles (wave w on SIMD w % 4):
-//   wave 0: Q H (it carries the inverse later)
+// barrier separates the scan from the products.  This runs beside the state
+// pass of the previous chunk and has no barrier of its own.  Roles (wave w on
+// SIMD w % 4):
 //   waves 1..3: K K^T 32 x 32 tiles (0,0) (1,0) (1,1)
-//   waves 4..7: the ten non-zero 16 x 16 tiles of P, as P fragments
-//               (4: 0 and 5; 5: 1 and 4; 6: 2; 7: 3)
-// Waves 0..3 finish well before the P waves: they issue the previous chunk's
-// output stores (io_o) and the next chunk's loads (io_ld) while they wait.
+//   waves 0, 4..7: the ten non-zero 16 x 16 tiles of P, as P fragments
+//               (0: 0 and 4; 4: 1; 5: 2; 6: 3; 7: 5)
 // A P fragment (rt, ks) stacks the P^T = K Q^T tiles (s tile 2 ks, i tile rt)
 // and (2 ks + 1, rt); the accumulator of each tile is the fragment half.
-template <typename IO, typename LD>
-__device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const int wave, const bool out,
-                                               const f32x4 (&hacc)[8], f32x4 (&qh)[4], IO &&io_o, LD &&io_ld) {
+__device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const int wave, const bool out, const int buf) {
     const int lane = tid & 63;
     const int m32 = lane & 31, h32 = lane >> 5;
     const int m = lane & 15, g = lane >> 4;
     f32x16 acck = {};
     const int rbi = (wave >= 2) ? 1 : 0, rbs = (wave == 3) ? 1 : 0;
     int pfr[2] = {-1, -1};
-    if (wave == 4) { pfr[0] = 0; pfr[1] = 5; }
-    if (wave == 5) { pfr[0] = 1; pfr[1] = 4; }
-    if (wave == 6) pfr[0] = 2;
-    if (wave == 7) pfr[0] = 3;
+    if (wave == 0) { pfr[0] = 0; pfr[1] = 4; }
+    if (wave == 4) pfr[0] = 1;
+    if (wave == 5) pfr[0] = 2;
+    if (wave == 6) pfr[0] = 3;
+    if (wave == 7) pfr[0] = 5;
     f32x4 accp[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
 
     bool fact;
@@ -731,16 +741,13 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
         const float bt = s.beta[lane];
         const float epv = __expf(d);
         s.gcum[lane] = x;
-        s.gam[lane] = gm;
-        s.dec[lane] = __expf(glast - x);
+        s.gam[buf][lane] = gm;
+        s.dec[buf][lane] = __expf(glast - x);
         s.bg[lane] = bt * gm;
         s.ep[lane] = epv;
         s.em[lane] = __expf(-d);
         s.rowa[lane] = bt * epv;
         fact = __all(fabsf(d) < 80.f);  // the factored decays are finite
-    }
-    if (wave == 0) {
-        if (out) chain_qh(s, hacc, qh, lane);
     }
     if (wave >= 1 && wave <= 3) {
         const bf16 *ra = &s.k[(32 * rbi + m32) * KS + 8 * h32];
@@ -790,7 +797,7 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
                     f32x4{v[4 * ii], v[4 * ii + 1], v[4 * ii + 2], v[4 * ii + 3]};
         }
     }
-    if (out && wave >= 4) {
+    if (out && (wave == 0 || wave >= 4)) {
 #pragma unroll
         for (int pi = 0; pi < 2; ++pi) {
             if (pfr[pi] < 0) continue;
@@ -837,15 +844,10 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
             }
             bf16x8 hi, lo;
             split8v(pv, hi, lo);
-            s.pf[0][pfr[pi]][lane] = hi;
-            s.pf[1][pfr[pi]][lane] = lo;
+            s.pf[buf][0][pfr[pi]][lane] = hi;
+            s.pf[buf][1][pfr[pi]][lane] = lo;
         }
     }
-    if (wave < 4) {
-        io_o();
-        io_ld();
-    }
-    __syncthreads();
 }
 
 
@@ -854,16 +856,13 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
 //   level 0 (waves 0..3, one 16 x 16 diagonal block each): forward
 //     substitution with lane = 4 c + p; the four lanes of column c split
 //     each row's dot product over s = p mod 4 and add it with two DPP steps;
-//   level 1 (waves 0, 2): T_10 = -T_11 (A_10 T_00) inside each 32 x 32
+//   level 1 (waves 0, 1): T_10 = -T_11 (A_10 T_00) inside each 32 x 32
 //     diagonal block, two chained 16 x 16 MFMA products (hi/lo operands);
-//   level 2 (wave 0): T_lo,hi = -T_lo,lo (A_lo,hi T_hi,hi), 32 x 32 MFMA.
+//   level 2 (wave 2): T_lo,hi = -T_lo,lo (A_lo,hi T_hi,hi), 32 x 32 MFMA.
 // The other waves compute their Q H meanwhile (waves 4..7 during level 0,
-// 1 and 3 during level 1, 2 during level 2; wave 0 did during the products);
-// waves 4..7 issue the previous chunk's output stores during level 1 and the
-// next chunk's loads during level 2.
-template <typename IO, typename LD>
+// 2 and 3 during level 1, 0 and 1 during level 2).
 __device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int wave, const bool out,
-                                              const f32x4 (&hacc)[8], f32x4 (&qh)[4], IO &&io_o, LD &&io_ld) {
+                                              const f32x4 (&hacc)[8], f32x4 (&qh)[4]) {
     const int lane = tid & 63;
     if (wave >= 4) {
         if (out) chain_qh(s, hacc, qh, lane);
@@ -904,13 +903,11 @@ __device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int
     }
     __syncthreads();
     const int m = lane & 15, g = lane >> 4;
-    if (wave >= 4) {
-        io_o();
-    } else if (wave == 1 || wave == 3) {
+    if (wave == 2 || wave == 3) {
         if (out) chain_qh(s, hacc, qh, lane);
-    } else {
+    } else if (wave < 2) {
         // level 1 in diagonal block b = 32 blk:  X = A_10 T_00 ; T_10 = -T_11 X
-        const int blk = wave >> 1;
+        const int blk = wave;
         const int b = 32 * blk;
         const float *tb = s.tt[blk];
         float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -951,11 +948,9 @@ __device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int
         *reinterpret_cast<f32x4 *>(&tbw[m * TS8 + 16 + 4 * g]) = f32x4{-z[0], -z[1], -z[2], -z[3]};
     }
     __syncthreads();
-    if (wave >= 4) {
-        io_ld();
-    } else if (wave == 2) {
+    if (wave < 2) {
         if (out) chain_qh(s, hacc, qh, lane);
-    } else if (wave == 0) {
+    } else if (wave == 2) {
         const int m32 = lane & 31, h = lane >> 5;
         const float *tb = s.tt[0];  // T_hi,hi transposed
         f32x16 y = {};
@@ -1002,7 +997,7 @@ __device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int
 // ---- W and U.  First the six T diag(beta) hi/lo A fragments (waves 0..5,
 // one each); then each wave writes two -W A fragments from W^T = K^T
 // (T diag(beta gamma))^T tiles and forms U = (T diag(beta)) V for its columns.
-__device__ __forceinline__ void prep8_wu(Smem8 &s, const int tid, const int wave, f32x4 (&u)[4]) {
+__device__ __forceinline__ void prep8_wu(Smem8 &s, const int tid, const int wave, f32x4 (&u)[4], const int buf) {
     const int lane = tid & 63;
     const int m = lane & 15, g = lane >> 4;
     if (wave < 6) {
@@ -1035,8 +1030,8 @@ __device__ __forceinline__ void prep8_wu(Smem8 &s, const int tid, const int wave
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             if (ks >= nks) continue;
-            ka[f][ks][0] = lds8(&s.kt[(32 * (kk0 + f) + m) * CS + 32 * ks + 8 * g]);
-            ka[f][ks][1] = lds8(&s.kt[(32 * (kk0 + f) + 16 + m) * CS + 32 * ks + 8 * g]);
+            ka[f][ks][0] = lds8(&s.kt[buf][(32 * (kk0 + f) + m) * CS + 32 * ks + 8 * g]);
+            ka[f][ks][1] = lds8(&s.kt[buf][(32 * (kk0 + f) + 16 + m) * CS + 32 * ks + 8 * g]);
         }
     __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
@@ -1137,6 +1132,90 @@ __device__ __forceinline__ void write_o_regs(const FwdParams &p, const __amdgpu_
     }
 }
 
+// ---- the state pass of one chunk (every wave, its 16 value columns):
+//   v' = U - W H;  O = scale (diag(gamma) Q H + P v');
+//   H <- gamma_last H + K^T diag(gamma_last / gamma) v'
+__device__ __forceinline__ void chain8(const Smem8 &s, const FwdParams &p, f32x4 (&hacc)[8], const f32x4 (&qh)[4],
+                                       const f32x4 (&u)[4], f32x4 (&ov)[4], const bool out, const int buf,
+                                       const int ln) {
+    const int m = ln & 15, g = ln >> 4;
+    f32x4 vp[4] = {u[0], u[1], u[2], u[3]};
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+        bf16x8 hh[2], hl[2], wa[2][4];
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+            const int kk = 2 * k2 + kq;
+            split_pair(hacc[2 * kk], hacc[2 * kk + 1], hh[kq], hl[kq]);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) wa[kq][rt] = s.wf[rt][kk][ln];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                vp[rt] = mfma16(wa[kq][rt], hh[kq], vp[rt]);
+                vp[rt] = mfma16(wa[kq][rt], hl[kq], vp[rt]);
+            }
+    }
+    if (out) {
+        f32x4 pv[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+        bf16x8 pa[2][6];
+#pragma unroll
+        for (int f = 0; f < 6; ++f) {
+            pa[0][f] = s.pf[buf][0][f][ln];
+            pa[1][f] = s.pf[buf][1][f][ln];
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 vh, vl;
+            split_pair(vp[2 * ks], vp[2 * ks + 1], vh, vl);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if (ks == 1 && rt < 2) continue;  // P is lower triangular
+                const int f = frag_of(rt, ks);
+                pv[rt] = mfma16(pa[0][f], vh, pv[rt]);
+                pv[rt] = mfma16(pa[0][f], vl, pv[rt]);
+                pv[rt] = mfma16(pa[1][f], vh, pv[rt]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&s.gam[buf][16 * rt + 4 * g]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) ov[rt][jj] = p.scale * (gm4[jj] * qh[rt][jj] + pv[rt][jj]);
+        }
+    }
+    const float glast = s.gam[buf][CH - 1];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s.dec[buf][16 * rt + 4 * g]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) vp[rt][jj] *= d4[jj];
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) hacc[dt] *= glast;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 vh, vl;
+        split_pair(vp[2 * ks], vp[2 * ks + 1], vh, vl);
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) {
+            bf16x8 ka[4];
+#pragma unroll
+            for (int dq = 0; dq < 4; ++dq) ka[dq] = lds8_perm16(&s.kt[buf][(16 * (4 * d2 + dq) + m) * CS], 32 * ks, g);
+            __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+            for (int dq = 0; dq < 4; ++dq) {
+                hacc[4 * d2 + dq] = mfma16(ka[dq], vh, hacc[4 * d2 + dq]);
+                hacc[4 * d2 + dq] = mfma16(ka[dq], vl, hacc[4 * d2 + dq]);
+            }
+        }
+    }
+}
+
 // One workgroup per CU (its LDS footprint), two waves per SIMD: schedule for that.
 __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) gdn_fwd_main_kernel(FwdParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
@@ -1202,14 +1281,25 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const __amdgpu_buffer_rsrc_t ro =
             make_rsrc(static_cast<char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes, (int64_t)e.seq_len * p.Hv * DV * oes);
 
+        // Software pipeline over chunks: iteration c runs the state pass of
+        // chunk c beside the products of chunk c + 1, then the inverse and W/U
+        // of chunk c + 1.  K^T, P and the decays are double-buffered by chunk
+        // parity; U and Q H of the next chunk wait in registers.
         Stage8 st;
-        load_chunk8(in, st, c_first, c_first >= e.c_begin, threadIdx.x, wave);
-        // A chunk's output waits in registers and is stored at the top of the
-        // next iteration, after that iteration's prefetched inputs have been
-        // consumed: memory-counter waits for the prefetch then never have to
-        // cover freshly issued output stores.
-        f32x4 ov[4];
-        int pend = -1;  // chunk whose output is held in ov, or -1
+        load_chunk8(in, st, c_first, c_first >= e.c_begin, threadIdx.x, wave, true);
+        f32x4 qh[4], u[4], ov[4];
+        {
+            int tid = threadIdx.x;
+            asm volatile("" : "+v"(tid));
+            const bool out0 = (c_first >= e.c_begin);
+            store_chunk8(s, st, tid, wave, c_first & 1);
+            __syncthreads();
+            load_chunk8(in, st, c_first + 1, c_first + 1 >= e.c_begin, tid, wave, c_first + 1 < c_end);
+            prep8_products(s, tid, wave, out0, c_first & 1);
+            __syncthreads();
+            prep8_inverse(s, tid, wave, out0, hacc, qh);
+            prep8_wu(s, tid, wave, u, c_first & 1);
+        }
         for (int c = c_first; c < c_end; ++c) {
             // The thread index is made opaque once per chunk so that the
             // compiler recomputes lane-derived LDS addresses inside the loop
@@ -1217,110 +1307,24 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             int tid = threadIdx.x;
             asm volatile("" : "+v"(tid));
             const int ln = tid & 63;
-            const int m = ln & 15, g = ln >> 4;
             const bool out = (c >= e.c_begin);  // warm-up chunks only advance the state
-            store_chunk8(s, st, out, tid, wave);
+            const bool more = (c + 1 < c_end);
+            const int b = c & 1, nb = b ^ 1;
+            if (more) store_chunk8(s, st, tid, wave, nb);
             __syncthreads();
-            // the previous chunk's output stores and the next chunk's loads,
-            // issued by each wave in a window where it would otherwise wait
-            auto io_o = [&]() {
-                if (pend >= 0) write_o_regs(p, ro, pend, ov, wave, ln);
-                pend = -1;
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) ov[rt] = f32x4{};  // written out: not carried further
-            };
-            auto io_ld = [&]() {
-                if (c + 1 < c_end) load_chunk8(in, st, c + 1, c + 1 >= e.c_begin, tid, wave);
-            };
-
-            f32x4 qh[4];
-            prep8_products(s, tid, wave, out, hacc, qh, io_o, io_ld);
-            prep8_inverse(s, tid, wave, out, hacc, qh, io_o, io_ld);
-            f32x4 u[4];
-            prep8_wu(s, tid, wave, u);
-
-            // ---- critical chain: v' = U - W H
-            f32x4 vp[4] = {u[0], u[1], u[2], u[3]};
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) {
-                bf16x8 hh[2], hl[2], wa[2][4];
-#pragma unroll
-                for (int kq = 0; kq < 2; ++kq) {
-                    const int kk = 2 * k2 + kq;
-                    split_pair(hacc[2 * kk], hacc[2 * kk + 1], hh[kq], hl[kq]);
-#pragma unroll
-                    for (int rt = 0; rt < 4; ++rt) wa[kq][rt] = s.wf[rt][kk][ln];
-                }
-                __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-                for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-                    for (int rt = 0; rt < 4; ++rt) {
-                        vp[rt] = mfma16(wa[kq][rt], hh[kq], vp[rt]);
-                        vp[rt] = mfma16(wa[kq][rt], hl[kq], vp[rt]);
-                    }
+            chain8(s, p, hacc, qh, u, ov, out, b, ln);
+            // chunk c's output and chunk c + 2's inputs: issued here and left
+            // in flight; the staging wait at the next iteration's top is the
+            // first to cover them
+            if (out) write_o_regs(p, ro, c, ov, wave, ln);
+            load_chunk8(in, st, c + 2, c + 2 >= e.c_begin, tid, wave, c + 2 < c_end);
+            if (more) {
+                prep8_products(s, tid, wave, c + 1 >= e.c_begin, nb);
+                __syncthreads();
+                prep8_inverse(s, tid, wave, c + 1 >= e.c_begin, hacc, qh);
+                prep8_wu(s, tid, wave, u, nb);
             }
-            if (out) {
-                // O = scale (diag(gamma) Q H + P v')
-                f32x4 pv[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-                bf16x8 pa[2][6];
-#pragma unroll
-                for (int f = 0; f < 6; ++f) {
-                    pa[0][f] = s.pf[0][f][ln];
-                    pa[1][f] = s.pf[1][f][ln];
-                }
-                __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    bf16x8 vh, vl;
-                    split_pair(vp[2 * ks], vp[2 * ks + 1], vh, vl);
-#pragma unroll
-                    for (int rt = 0; rt < 4; ++rt) {
-                        if (ks == 1 && rt < 2) continue;  // P is lower triangular
-                        const int f = frag_of(rt, ks);
-                        pv[rt] = mfma16(pa[0][f], vh, pv[rt]);
-                        pv[rt] = mfma16(pa[0][f], vl, pv[rt]);
-                        pv[rt] = mfma16(pa[1][f], vh, pv[rt]);
-                    }
-                }
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&s.gam[16 * rt + 4 * g]);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) ov[rt][jj] = p.scale * (gm4[jj] * qh[rt][jj] + pv[rt][jj]);
-                }
-                pend = c;
-            }
-            // ---- H <- gamma_last H + K^T diag(gamma_last / gamma) v'
-            const float glast = s.gam[CH - 1];
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s.dec[16 * rt + 4 * g]);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) vp[rt][jj] *= d4[jj];
-            }
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) hacc[dt] *= glast;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 vh, vl;
-                split_pair(vp[2 * ks], vp[2 * ks + 1], vh, vl);
-#pragma unroll
-                for (int d2 = 0; d2 < 2; ++d2) {
-                    bf16x8 ka[4];
-#pragma unroll
-                    for (int dq = 0; dq < 4; ++dq) ka[dq] = lds8_perm16(&s.kt[(16 * (4 * d2 + dq) + m) * CS], 32 * ks, g);
-                    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-                    for (int dq = 0; dq < 4; ++dq) {
-                        hacc[4 * d2 + dq] = mfma16(ka[dq], vh, hacc[4 * d2 + dq]);
-                        hacc[4 * d2 + dq] = mfma16(ka[dq], vl, hacc[4 * d2 + dq]);
-                    }
-                }
-            }
-            __syncthreads();  // LDS is rewritten by the next chunk
         }
-        if (pend >= 0) write_o_regs(p, ro, pend, ov, wave, threadIdx.x & 63);
     }
 
     if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
