@@ -94,24 +94,33 @@ __device__ __forceinline__ bf16x8 lds8_perm(const bf16 *row, int base, int h) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Accumulator registers 8s .. 8s+7 of a tile as bf16 hi and lo B operands.
-__device__ __forceinline__ void split8(const f32x16 &acc, int s, bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float x = acc[8 * s + e];
-        const bf16 h = (bf16)x;
-        hi[e] = h;
-        lo[e] = (bf16)(x - (float)h);
-    }
+// hi + lo bf16 split of fp32 values, two at a time: hi = RNE(x) for both in
+// one packed conversion; float(hi) is the packed word shifted or masked (no
+// unpacking conversion); lo = RNE(x - float(hi)) in a second packed conversion.
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+    const bf16x2 h = {(bf16)x0, (bf16)x1};
+    hi = __builtin_bit_cast(uint32_t, h);
+    asm("" : "+v"(hi));  // keep the packed word: re-deriving each half costs an extra conversion
+    const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+    const bf16x2 l = {(bf16)(x0 - h0), (bf16)(x1 - h1)};
+    lo = __builtin_bit_cast(uint32_t, l);
 }
 
 __device__ __forceinline__ void split8v(const float *x, bf16x8 &hi, bf16x8 &lo) {
+    uint32_t h[4], l[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const bf16 h = (bf16)x[e];
-        hi[e] = h;
-        lo[e] = (bf16)(x[e] - (float)h);
-    }
+    for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], h[i], l[i]);
+    hi = __builtin_bit_cast(bf16x8, (u32x4{h[0], h[1], h[2], h[3]}));
+    lo = __builtin_bit_cast(bf16x8, (u32x4{l[0], l[1], l[2], l[3]}));
+}
+
+// Accumulator registers 8s .. 8s+7 of a tile as bf16 hi and lo B operands.
+__device__ __forceinline__ void split8(const f32x16 &acc, int s, bf16x8 &hi, bf16x8 &lo) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = acc[8 * s + e];
+    split8v(x, hi, lo);
 }
 
 // ---------------------------------------------------------------- chunk loads
@@ -519,24 +528,24 @@ __device__ __forceinline__ void store_state(const f32x16 (&t)[4], float *dst, co
 }
 
 // ---------------------------------------------------------------- the forward kernel (8 waves)
-// One workgroup of eight waves owns one (segment, v-head).  Wave w holds value
-// columns 16w .. 16w+15 of the state in eight 16 x 16 accumulator tiles
-// (v_mfma_f32_16x16x32_bf16: lane l holds A row / B column l % 16 with the 8
-// k-slots 8 (l / 16) .. +7; accumulator element j holds row 4 (l / 16) + j,
-// column l % 16).  Two accumulator tiles stacked along k read as one B
-// operand see, in a 32-wide k step, the k indices 4g..4g+3 and 16+4g..16+4g+3
-// (g = l / 16); A operands that meet such a B use the same permutation.
-// The chunk-local preparation is spread over all eight waves, and Q H (which
-// needs only the chunk-start state) is computed by the waves that are idle
-// while others run the cumsum/products and the inverse.
+// One workgroup of eight waves owns one (segment, v-head).  Waves 0..3, the
+// state waves, hold the state: wave w has value columns 32 w .. 32 w + 31 as two
+// column tiles of eight 16 x 16 accumulator tiles (v_mfma_f32_16x16x32_bf16:
+// lane l holds A row / B column l % 16 with the 8 k-slots 8 (l / 16) .. +7;
+// accumulator element j holds row 4 (l / 16) + j, column l % 16).  Two
+// accumulator tiles stacked along k read as one B operand see, in a 32-wide k
+// step, the k indices 4g..4g+3 and 16+4g..16+4g+3 (g = l / 16); A operands
+// that meet such a B use the same permutation.  Every A operand a state wave
+// reads from LDS (W, P, Q, K^T fragments) serves both of its column tiles, so
+// each shared tile is read by four waves per chunk.  Waves 4..7, the
+// preparation waves, hold no state: they run the chunk-local preparation of
+// the next chunk (products, inverse, W) in step with the state pass of the
+// current one, one barrier-separated step at a time.
 constexpr int NT8 = 512;
 constexpr int TS8 = 32 + 4;  // fp32 row stride of the transposed 32 x 32 diagonal blocks
 
 struct __attribute__((aligned(16))) Smem8 {
-    union {
-        bf16 k[CH * KS];              // K, row = token (products)
-        bf16x8 thf[2][6][64];         // T diag(beta), hi and lo A fragments (W/U phase)
-    };
+    bf16 k[CH * KS];                  // K, row = token
     bf16 q[CH * KS];                  // Q
     bf16 kt[2][DK * CS];              // K^T, row = key dim (two chunks in flight)
     bf16 vt[DV * CS];                 // V^T, row = value dim
@@ -598,12 +607,12 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     return x;
 }
 
-// ---- staging of one chunk: waves 0..3 take K (natural and transposed) and
-// waves 4..7 take V (transposed); thread t' = t mod 256 holds rows
-// 4 rg .. +3, columns 8 cg .. +7 of its tile, with cg = t' mod 8 +
+// ---- staging of one chunk, by the preparation waves only (the state waves
+// keep their registers for the state).  Thread t' = t mod 256 holds rows
+// 4 rg .. +3, columns 8 cg .. +7 of K, V and Q, with cg = t' mod 8 +
 // 8 (t' / 128) and rg = (t' / 8) mod 16, so eight consecutive lanes cover one
-// 128-byte row segment.  Q is spread over all 512 threads (two 16-byte pieces
-// each, consecutive lanes along a row) and g, beta over the first 64.
+// 128-byte row segment; the first 64 threads also hold g and beta.  K goes to
+// LDS natural and transposed, V transposed, Q natural.
 // Every load is issued unconditionally: a piece that is not wanted (no next
 // chunk, a warm-up chunk's Q, threads past 64 for g and beta) gets an offset
 // beyond the buffer range and comes back as zeros without a memory access.
@@ -617,120 +626,74 @@ __device__ __forceinline__ void stage_coords(int t, int &rg, int &cg) {
 }
 
 struct Stage8 {
-    u32x4 x[4], y[2];
+    u32x4 k[4], v[4], q[4];
     float g, b;
 };
 
 constexpr unsigned kOutOfRange = 0x80000000u;  // beyond every buffer range (all are below 2^31 bytes)
 
-__device__ __forceinline__ void load_chunk8(const Inputs &in, Stage8 &st, int c, bool need_q, int t, int wave,
-                                            bool valid) {
+__device__ __forceinline__ void load_chunk8(const Inputs &in, Stage8 &st, int c, bool need_q, int t, bool valid) {
     int rg, cg;
     stage_coords(t, rg, cg);
-    const bool kv = wave < 4;  // wave-uniform role: K (waves 0..3) or V (waves 4..7)
-    const __amdgpu_buffer_rsrc_t rx = kv ? in.k : in.v;
-    const unsigned sx = kv ? in.kstride : in.vstride;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const unsigned tok = (unsigned)(c * CH + 4 * rg + r);
-        const unsigned off = valid ? tok * sx + 16u * cg : kOutOfRange;
-        st.x[r] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+        const unsigned ok = valid ? tok * in.kstride + 16u * cg : kOutOfRange;
+        const unsigned ov = valid ? tok * in.vstride + 16u * cg : kOutOfRange;
+        const unsigned oq = (valid && need_q) ? tok * in.kstride + 16u * cg : kOutOfRange;
+        st.k[r] = __builtin_amdgcn_raw_buffer_load_b128(in.k, (int)ok, 0, 0);
+        st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(in.v, (int)ov, 0, 0);
+        st.q[r] = __builtin_amdgcn_raw_buffer_load_b128(in.q, (int)oq, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int piece = t + NT8 * i;
-        const unsigned tok = (unsigned)(c * CH + (piece >> 4));
-        const unsigned off = (valid && need_q) ? tok * in.kstride + 16u * (piece & 15) : kOutOfRange;
-        st.y[i] = __builtin_amdgcn_raw_buffer_load_b128(in.q, (int)off, 0, 0);
-    }
-    const unsigned tok = (unsigned)(c * CH + t);
-    const unsigned goff = (valid && t < CH) ? tok * in.gstride : kOutOfRange;
+    const int tt = t & 255;
+    const unsigned tok = (unsigned)(c * CH + tt);
+    const unsigned goff = (valid && tt < CH) ? tok * in.gstride : kOutOfRange;
     st.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.g, (int)goff, 0, 0));
     st.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.b, (int)goff, 0, 0));
 }
 
-__device__ __forceinline__ void store_chunk8(Smem8 &s, const Stage8 &st, int t, int wave, int buf) {
+// Four rows x eight columns as eight packed column pieces (4 bf16 each)
+__device__ __forceinline__ void transpose4x8(const u32x4 (&x)[4], uint2 (&tr)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        tr[e] = make_uint2(half_of(x[0], e) | (half_of(x[1], e) << 16), half_of(x[2], e) | (half_of(x[3], e) << 16));
+}
+
+__device__ __forceinline__ void store_chunk8(Smem8 &s, const Stage8 &st, int t, int buf) {
     int rg, cg;
     stage_coords(t, rg, cg);
     uint2 tr[8];
+    transpose4x8(st.k, tr);
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        tr[e] = make_uint2(half_of(st.x[0], e) | (half_of(st.x[1], e) << 16),
-                           half_of(st.x[2], e) | (half_of(st.x[3], e) << 16));
-    if (wave < 4) {
+    for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4 *>(&s.k[(4 * rg + r) * KS + 8 * cg]) = st.k[r];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4 *>(&s.k[(4 * rg + r) * KS + 8 * cg]) = st.x[r];
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.kt[buf][(8 * cg + e) * CS + 4 * rg]) = tr[e];
+    transpose4x8(st.v, tr);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.kt[buf][(8 * cg + e) * CS + 4 * rg]) = tr[e];
-    } else {
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.vt[(8 * cg + e) * CS + 4 * rg]) = tr[e];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.vt[(8 * cg + e) * CS + 4 * rg]) = tr[e];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int piece = t + NT8 * i;
-        *reinterpret_cast<u32x4 *>(&s.q[(piece >> 4) * KS + 8 * (piece & 15)]) = st.y[i];
-    }
-    if (t < CH) {
-        s.graw[t] = st.g;
-        s.beta[t] = st.b;
+    for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4 *>(&s.q[(4 * rg + r) * KS + 8 * cg]) = st.q[r];
+    const int tt = t & 255;
+    if (tt < CH) {
+        s.graw[tt] = st.g;
+        s.beta[tt] = st.b;
     }
 }
 
-// ---- Q H for this wave's value columns: qh[rt] covers rows 16 rt .. +15.
-// Operand reads are issued in batches ahead of the products that use them.
-__device__ __forceinline__ void chain_qh(const Smem8 &s, const f32x4 (&hacc)[8], f32x4 (&qh)[4], const int ln) {
-    const int m = ln & 15, g = ln >> 4;
-    bf16x8 hh[4], hl[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) split_pair(hacc[2 * kk], hacc[2 * kk + 1], hh[kk], hl[kk]);
-#pragma unroll
-    for (int r2 = 0; r2 < 2; ++r2) {
-        bf16x8 a[2][4];
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) a[r][kk] = lds8_perm16(&s.q[(16 * (2 * r2 + r) + m) * KS], 32 * kk, g);
-        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-        for (int r = 0; r < 2; ++r) qh[2 * r2 + r] = f32x4{};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                qh[2 * r2 + r] = mfma16(a[r][kk], hh[kk], qh[2 * r2 + r]);
-                qh[2 * r2 + r] = mfma16(a[r][kk], hl[kk], qh[2 * r2 + r]);
-            }
-    }
-}
-
-// ---- cumsum, decay factors, masked beta-weighted K K^T (into s.a, and the
-// diagonal 32 x 32 blocks transposed into s.tt) and the causal decayed P as A
-// fragments.  Every wave forms the chunk's cumulative gates and decay factors
-// itself (a DPP scan, lane = token) and writes them to the shared arrays: all
-// waves write identical values, and each reads back only what it wrote, so no
-// barrier separates the scan from the products.  This runs beside the state
-// pass of the previous chunk and has no barrier of its own.  Roles (wave w on
-// SIMD w % 4):
-//   waves 1..3: K K^T 32 x 32 tiles (0,0) (1,0) (1,1)
-//   waves 0, 4..7: the ten non-zero 16 x 16 tiles of P, as P fragments
-//               (0: 0 and 4; 4: 1; 5: 2; 6: 3; 7: 5)
+// ---- preparation step 1 (waves 4..7, pw = wave - 4): the chunk's gate scan
+// and decay factors (every preparation wave forms them itself, lane = token,
+// and writes identical values to the shared arrays; each reads back only what
+// it wrote, so no barrier separates the scan from the products), then
+//   pw 0..2: one masked, beta-weighted K K^T 32 x 32 tile each ((0,0) (1,0)
+//            (1,1)) into s.a, the diagonal ones also transposed into s.tt;
+//   the causal decayed P as hi/lo A fragments of the ten non-zero 16 x 16
+//   tiles: pw 0 fragment 0, pw 1 fragment 4, pw 2 fragment 1, pw 3 fragments
+//   2, 3 and 5.
 // A P fragment (rt, ks) stacks the P^T = K Q^T tiles (s tile 2 ks, i tile rt)
 // and (2 ks + 1, rt); the accumulator of each tile is the fragment half.
-__device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const int wave, const bool out, const int buf) {
-    const int lane = tid & 63;
+__device__ __forceinline__ void prod8(Smem8 &s, const int lane, const int pw, const bool out, const int buf) {
     const int m32 = lane & 31, h32 = lane >> 5;
     const int m = lane & 15, g = lane >> 4;
-    f32x16 acck = {};
-    const int rbi = (wave >= 2) ? 1 : 0, rbs = (wave == 3) ? 1 : 0;
-    int pfr[2] = {-1, -1};
-    if (wave == 0) { pfr[0] = 0; pfr[1] = 4; }
-    if (wave == 4) pfr[0] = 1;
-    if (wave == 5) pfr[0] = 2;
-    if (wave == 6) pfr[0] = 3;
-    if (wave == 7) pfr[0] = 5;
-    f32x4 accp[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
-
     bool fact;
     {
         const float x = wave_prefix_sum(s.graw[lane]);
@@ -749,7 +712,9 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
         s.rowa[lane] = bt * epv;
         fact = __all(fabsf(d) < 80.f);  // the factored decays are finite
     }
-    if (wave >= 1 && wave <= 3) {
+    if (pw < 3) {
+        const int rbi = (pw >= 1) ? 1 : 0, rbs = (pw == 2) ? 1 : 0;
+        f32x16 acck = {};
         const bf16 *ra = &s.k[(32 * rbi + m32) * KS + 8 * h32];
         const bf16 *rb = &s.k[(32 * rbs + m32) * KS + 8 * h32];
 #pragma unroll
@@ -797,11 +762,21 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
                     f32x4{v[4 * ii], v[4 * ii + 1], v[4 * ii + 2], v[4 * ii + 3]};
         }
     }
-    if (out && (wave == 0 || wave >= 4)) {
+    if (out) {
+        int pfr[3] = {-1, -1, -1};
+        if (pw == 0) pfr[0] = 0;
+        if (pw == 1) pfr[0] = 4;
+        if (pw == 2) pfr[0] = 1;
+        if (pw == 3) {
+            pfr[0] = 2;
+            pfr[1] = 3;
+            pfr[2] = 5;
+        }
 #pragma unroll
-        for (int pi = 0; pi < 2; ++pi) {
+        for (int pi = 0; pi < 3; ++pi) {
             if (pfr[pi] < 0) continue;
             const int rt = frag_rt(pfr[pi]), ks = frag_ks(pfr[pi]);
+            f32x4 accp[2] = {f32x4{}, f32x4{}};
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int st = 2 * ks + half;
@@ -816,13 +791,8 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) accp[pi][half] = mfma16(xa[kk], xb[kk], accp[pi][half]);
+                for (int kk = 0; kk < DK / 32; ++kk) accp[half] = mfma16(xa[kk], xb[kk], accp[half]);
             }
-        }
-#pragma unroll
-        for (int pi = 0; pi < 2; ++pi) {
-            if (pfr[pi] < 0) continue;
-            const int rt = frag_rt(pfr[pi]), ks = frag_ks(pfr[pi]);
             const int i = 16 * rt + m;  // this lane's query row
             float pv[8];
 #pragma unroll
@@ -832,14 +802,13 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
                     const float cf = s.ep[i];
                     const f32x4 e4 = *reinterpret_cast<const f32x4 *>(&s.em[s0]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        pv[4 * half + j] = (s0 + j <= i) ? cf * e4[j] * accp[pi][half][j] : 0.f;
+                    for (int j = 0; j < 4; ++j) pv[4 * half + j] = (s0 + j <= i) ? cf * e4[j] * accp[half][j] : 0.f;
                 } else {
                     const float gi = s.gcum[i];
                     const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[s0]);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        pv[4 * half + j] = (s0 + j <= i) ? __expf(gi - g4[j]) * accp[pi][half][j] : 0.f;
+                        pv[4 * half + j] = (s0 + j <= i) ? __expf(gi - g4[j]) * accp[half][j] : 0.f;
                 }
             }
             bf16x8 hi, lo;
@@ -850,170 +819,154 @@ __device__ __forceinline__ void prep8_products(Smem8 &s, const int tid, const in
     }
 }
 
-
-// ---- in-place inverse of (I + A), T = (I + A)^{-1}, in s.a (row-major) and
-// s.tt (transposed diagonal 32 x 32 blocks, needed by the merges):
-//   level 0 (waves 0..3, one 16 x 16 diagonal block each): forward
-//     substitution with lane = 4 c + p; the four lanes of column c split
-//     each row's dot product over s = p mod 4 and add it with two DPP steps;
-//   level 1 (waves 0, 1): T_10 = -T_11 (A_10 T_00) inside each 32 x 32
-//     diagonal block, two chained 16 x 16 MFMA products (hi/lo operands);
-//   level 2 (wave 2): T_lo,hi = -T_lo,lo (A_lo,hi T_hi,hi), 32 x 32 MFMA.
-// The other waves compute their Q H meanwhile (waves 4..7 during level 0,
-// 2 and 3 during level 1, 0 and 1 during level 2).
-__device__ __forceinline__ void prep8_inverse(Smem8 &s, const int tid, const int wave, const bool out,
-                                              const f32x4 (&hacc)[8], f32x4 (&qh)[4]) {
-    const int lane = tid & 63;
-    if (wave >= 4) {
-        if (out) chain_qh(s, hacc, qh, lane);
-    } else {
-        // level 0: block o = 16 wave; the transposed 16 x 16 block lives in
-        // s.tt[wave / 2] at offset 16 (wave % 2) along both axes
-        const int c = lane >> 2, p = lane & 3;
-        const int bo = 16 * (wave & 1);
-        float *tb = s.tt[wave >> 1];
-        // this lane's coefficients A[i][p + 4e] for all rows i: rows p + 4e of A^T
-        float ac[4][16];
+// ---- T = (I + A)^{-1} in place in s.a (row-major), with the diagonal 32 x 32
+// blocks also kept transposed in s.tt for the merges.
+// Level 0 (preparation wave pw: diagonal 16 x 16 block pw): forward
+// substitution with lane = 4 c + p; the four lanes of column c split each
+// row's dot product over s = p mod 4 and add it with two DPP steps.
+__device__ __forceinline__ void inv8_l0(Smem8 &s, const int lane, const int pw) {
+    const int c = lane >> 2, p = lane & 3;
+    const int bo = 16 * (pw & 1);
+    float *tb = s.tt[pw >> 1];  // block pw sits in s.tt[pw / 2] at offset 16 (pw % 2) on both axes
+    // this lane's coefficients A[i][p + 4e] for all rows i: rows p + 4e of A^T
+    float ac[4][16];
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(&tb[(bo + p + 4 * e4) * TS8 + bo + 4 * q4]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) ac[e4][4 * q4 + jj] = x[jj];
+        }
+    float t[4] = {0.f, 0.f, 0.f, 0.f};  // T[p + 4 e][c]
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) {
+        float part = 0.f;
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(&tb[(bo + p + 4 * e4) * TS8 + bo + 4 * q4]);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) ac[e4][4 * q4 + jj] = x[jj];
-            }
-        float t[4] = {0.f, 0.f, 0.f, 0.f};  // T[p + 4 e][c]
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-            float part = 0.f;
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4)
-                if (p + 4 * e4 < ii) part += ac[e4][ii] * t[e4];  // (p + 4 e4 < ii) is lane-dependent
-            part += quad_dpp<0xb1>(part);  // quad_perm [1,0,3,2]
-            part += quad_dpp<0x4e>(part);  // quad_perm [2,3,0,1]
-            const float tv = ((ii == c) ? 1.f : 0.f) - part;
-            if (p == (ii & 3)) t[ii >> 2] = tv;
-        }
-        const int o = 16 * wave;
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            s.a[(o + p + 4 * e4) * AS + o + c] = t[e4];
-            tb[(bo + c) * TS8 + bo + p + 4 * e4] = t[e4];
-        }
+            if (p + 4 * e4 < ii) part += ac[e4][ii] * t[e4];  // (p + 4 e4 < ii) is lane-dependent
+        part += quad_dpp<0xb1>(part);  // quad_perm [1,0,3,2]
+        part += quad_dpp<0x4e>(part);  // quad_perm [2,3,0,1]
+        const float tv = ((ii == c) ? 1.f : 0.f) - part;
+        if (p == (ii & 3)) t[ii >> 2] = tv;
     }
-    __syncthreads();
-    const int m = lane & 15, g = lane >> 4;
-    if (wave == 2 || wave == 3) {
-        if (out) chain_qh(s, hacc, qh, lane);
-    } else if (wave < 2) {
-        // level 1 in diagonal block b = 32 blk:  X = A_10 T_00 ; T_10 = -T_11 X
-        const int blk = wave;
-        const int b = 32 * blk;
-        const float *tb = s.tt[blk];
-        float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (g < 2) {  // k = 0..15 on lane groups 0, 1; groups 2, 3 carry zeros
-            const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + m) * AS + b + 8 * g]);
-            const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + m) * AS + b + 8 * g + 4]);
-            const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&tb[m * TS8 + 8 * g]);       // T_00[k][m]
-            const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&tb[m * TS8 + 8 * g + 4]);
+    const int o = 16 * pw;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                av[e] = a0[e];
-                av[4 + e] = a1[e];
-                bv[e] = b0[e];
-                bv[4 + e] = b1[e];
-            }
-        }
-        bf16x8 ah, al, bh, bl;
-        split8v(av, ah, al);
-        split8v(bv, bh, bl);
-        f32x4 x = {};
-        x = mfma16(ah, bh, x);
-        x = mfma16(ah, bl, x);
-        x = mfma16(al, bh, x);
-        // T_11 X: X (rows 4 g + j) is the first half of the B operand's k
-        // order, the second half is zero
-        const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + m) * AS + b + 16 + 4 * g]);
-        const float tvv[8] = {t4[0], t4[1], t4[2], t4[3], 0.f, 0.f, 0.f, 0.f};
-        const float xv[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
-        split8v(tvv, ah, al);
-        split8v(xv, bh, bl);
-        f32x4 z = {};
-        z = mfma16(ah, bh, z);
-        z = mfma16(ah, bl, z);
-        z = mfma16(al, bh, z);
-        float *tbw = s.tt[blk];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s.a[(b + 16 + 4 * g + j) * AS + b + m] = -z[j];
-        *reinterpret_cast<f32x4 *>(&tbw[m * TS8 + 16 + 4 * g]) = f32x4{-z[0], -z[1], -z[2], -z[3]};
+    for (int e4 = 0; e4 < 4; ++e4) {
+        s.a[(o + p + 4 * e4) * AS + o + c] = t[e4];
+        tb[(bo + c) * TS8 + bo + p + 4 * e4] = t[e4];
     }
-    __syncthreads();
-    if (wave < 2) {
-        if (out) chain_qh(s, hacc, qh, lane);
-    } else if (wave == 2) {
-        const int m32 = lane & 31, h = lane >> 5;
-        const float *tb = s.tt[0];  // T_hi,hi transposed
-        f32x16 y = {};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const float *ar = &s.a[(32 + m32) * AS + 16 * kk + 8 * h];
-            const float *br = &tb[m32 * TS8 + 16 * kk + 8 * h];
-            float av[8], bv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                av[e] = ar[e];
-                bv[e] = br[e];
-            }
-            bf16x8 ah, al, bh, bl;
-            split8v(av, ah, al);
-            split8v(bv, bh, bl);
-            y = mfma(ah, bh, y);
-            y = mfma(ah, bl, y);
-            y = mfma(al, bh, y);
-        }
-        f32x16 z = {};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const float *tr = &s.a[(32 + m32) * AS + 32 + 16 * kk + 4 * h];
-            float av[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                av[e] = tr[e];
-                av[4 + e] = tr[8 + e];
-            }
-            bf16x8 ah, al, bh, bl;
-            split8v(av, ah, al);
-            split8(y, kk, bh, bl);
-            z = mfma(ah, bh, z);
-            z = mfma(ah, bl, z);
-            z = mfma(al, bh, z);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s.a[(32 + 8 * (e >> 2) + 4 * h + (e & 3)) * AS + m32] = -z[e];
-    }
-    __syncthreads();
 }
 
-// ---- W and U.  First the six T diag(beta) hi/lo A fragments (waves 0..5,
-// one each); then each wave writes two -W A fragments from W^T = K^T
-// (T diag(beta gamma))^T tiles and forms U = (T diag(beta)) V for its columns.
-__device__ __forceinline__ void prep8_wu(Smem8 &s, const int tid, const int wave, f32x4 (&u)[4], const int buf) {
-    const int lane = tid & 63;
+// Level 1 (preparation waves 0 and 1, diagonal 32 x 32 block blk):
+// T_10 = -T_11 (A_10 T_00), two chained 16 x 16 MFMA products (hi/lo).
+__device__ __forceinline__ void inv8_l1(Smem8 &s, const int lane, const int blk) {
     const int m = lane & 15, g = lane >> 4;
-    if (wave < 6) {
-        const int rt = frag_rt(wave), ks = frag_ks(wave);
-        const float *tr = &s.a[(16 * rt + m) * AS + 32 * ks + 8 * g];
-        const float *bp = &s.beta[32 * ks + 8 * g];
-        float tb[8];
+    const int b = 32 * blk;
+    float *tb = s.tt[blk];
+    float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (g < 2) {  // k = 0..15 on lane groups 0, 1; groups 2, 3 carry zeros
+        const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + m) * AS + b + 8 * g]);
+        const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + m) * AS + b + 8 * g + 4]);
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&tb[m * TS8 + 8 * g]);  // T_00[k][m]
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&tb[m * TS8 + 8 * g + 4]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tb[e] = tr[e] * bp[e];
-        bf16x8 hi, lo;
-        split8v(tb, hi, lo);
-        s.thf[0][wave][lane] = hi;
-        s.thf[1][wave][lane] = lo;
+        for (int e = 0; e < 4; ++e) {
+            av[e] = a0[e];
+            av[4 + e] = a1[e];
+            bv[e] = b0[e];
+            bv[4 + e] = b1[e];
+        }
     }
-    // W^T tiles for this wave's two fragments (row tile rt, key steps kk0, kk0 + 1)
-    const int rt = wave >> 1, kk0 = 2 * (wave & 1);
+    bf16x8 ah, al, bh, bl;
+    split8v(av, ah, al);
+    split8v(bv, bh, bl);
+    f32x4 x = {};
+    x = mfma16(ah, bh, x);
+    x = mfma16(ah, bl, x);
+    x = mfma16(al, bh, x);
+    // T_11 X: X (rows 4 g + j) is the first half of the B operand's k order,
+    // the second half is zero
+    const f32x4 t4 = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + m) * AS + b + 16 + 4 * g]);
+    const float tvv[8] = {t4[0], t4[1], t4[2], t4[3], 0.f, 0.f, 0.f, 0.f};
+    const float xv[8] = {x[0], x[1], x[2], x[3], 0.f, 0.f, 0.f, 0.f};
+    split8v(tvv, ah, al);
+    split8v(xv, bh, bl);
+    f32x4 z = {};
+    z = mfma16(ah, bh, z);
+    z = mfma16(ah, bl, z);
+    z = mfma16(al, bh, z);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.a[(b + 16 + 4 * g + j) * AS + b + m] = -z[j];
+    *reinterpret_cast<f32x4 *>(&tb[m * TS8 + 16 + 4 * g]) = f32x4{-z[0], -z[1], -z[2], -z[3]};
+}
+
+// Level 2 (all four preparation waves, one 16 x 16 quadrant (r, cq) of the
+// lower-left 32 x 32 block each, pw = 2 r + cq):
+//   T_lo,hi = -T_lo,lo (A_lo,hi T_hi,hi)
+// Part a reads every operand (Y = A_lo,hi T_hi,hi[:, 16 cq ..] as two 16 x 16
+// tiles, and the T_lo,lo rows of this quadrant); part b, after a barrier,
+// writes the quadrant over A_lo,hi's storage.
+struct L2Regs {
+    f32x4 y0, y1;
+    bf16x8 th, tl;
+};
+
+__device__ __forceinline__ void inv8_l2a(const Smem8 &s, const int lane, const int pw, L2Regs &r2) {
+    const int m = lane & 15, g = lane >> 4;
+    const int r = pw >> 1, cq = pw & 1;
+    float bv[8];
+    {
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&s.tt[0][(16 * cq + m) * TS8 + 8 * g]);  // T_hi,hi[k][16 cq + m]
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&s.tt[0][(16 * cq + m) * TS8 + 8 * g + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bv[e] = b0[e];
+            bv[4 + e] = b1[e];
+        }
+    }
+    bf16x8 bh, bl;
+    split8v(bv, bh, bl);
+    f32x4 y[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&s.a[(32 + 16 * i + m) * AS + 8 * g]);
+        const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&s.a[(32 + 16 * i + m) * AS + 8 * g + 4]);
+        const float av[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        bf16x8 ah, al;
+        split8v(av, ah, al);
+        y[i] = f32x4{};
+        y[i] = mfma16(ah, bh, y[i]);
+        y[i] = mfma16(ah, bl, y[i]);
+        y[i] = mfma16(al, bh, y[i]);
+    }
+    r2.y0 = y[0];
+    r2.y1 = y[1];
+    // T_lo,lo row 16 r + m at the k order of split_pair(y0, y1)
+    const f32x4 t0 = *reinterpret_cast<const f32x4 *>(&s.a[(32 + 16 * r + m) * AS + 32 + 4 * g]);
+    const f32x4 t1 = *reinterpret_cast<const f32x4 *>(&s.a[(32 + 16 * r + m) * AS + 48 + 4 * g]);
+    const float tv[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    split8v(tv, r2.th, r2.tl);
+}
+
+__device__ __forceinline__ void inv8_l2b(Smem8 &s, const int lane, const int pw, const L2Regs &r2) {
+    const int m = lane & 15, g = lane >> 4;
+    const int r = pw >> 1, cq = pw & 1;
+    bf16x8 yh, yl;
+    split_pair(r2.y0, r2.y1, yh, yl);
+    f32x4 z = {};
+    z = mfma16(r2.th, yh, z);
+    z = mfma16(r2.th, yl, z);
+    z = mfma16(r2.tl, yh, z);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s.a[(32 + 16 * r + 4 * g + j) * AS + 16 * cq + m] = -z[j];
+}
+
+// ---- -W A fragments (preparation wave pw: row tile rt = pw, all four key-dim
+// steps) from W^T = K^T (T diag(beta gamma))^T tiles.
+__device__ __forceinline__ void wfrag8(Smem8 &s, const int lane, const int pw, const int buf) {
+    const int m = lane & 15, g = lane >> 4;
+    const int rt = pw;
     const int nks = (rt < 2) ? 1 : 2;  // T is lower triangular
     bf16x8 tw[2];
 #pragma unroll
@@ -1024,88 +977,162 @@ __device__ __forceinline__ void prep8_wu(Smem8 &s, const int tid, const int wave
 #pragma unroll
         for (int e = 0; e < 8; ++e) tw[ks][e] = (bf16)(tr[e] * bgp[e]);
     }
-    bf16x8 ka[2][2][2];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int k2 = 0; k2 < 2; ++k2) {
+        bf16x8 ka[2][2][2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ks >= nks) continue;
-            ka[f][ks][0] = lds8(&s.kt[buf][(32 * (kk0 + f) + m) * CS + 32 * ks + 8 * g]);
-            ka[f][ks][1] = lds8(&s.kt[buf][(32 * (kk0 + f) + 16 + m) * CS + 32 * ks + 8 * g]);
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks >= nks) continue;
+                const int kk = 2 * k2 + f;
+                ka[f][ks][0] = lds8(&s.kt[buf][(32 * kk + m) * CS + 32 * ks + 8 * g]);
+                ka[f][ks][1] = lds8(&s.kt[buf][(32 * kk + 16 + m) * CS + 32 * ks + 8 * g]);
+            }
+        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const int kk = 2 * k2 + f;  // key-dim step of 32: W^T tiles dt = 2 kk and 2 kk + 1
+            f32x4 w0 = {}, w1 = {};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks >= nks) continue;
+                w0 = mfma16(ka[f][ks][0], tw[ks], w0);
+                w1 = mfma16(ka[f][ks][1], tw[ks], w1);
+            }
+            s.wf[rt][kk][lane] = bf16x8{(bf16)(-w0[0]), (bf16)(-w0[1]), (bf16)(-w0[2]), (bf16)(-w0[3]),
+                                        (bf16)(-w1[0]), (bf16)(-w1[1]), (bf16)(-w1[2]), (bf16)(-w1[3])};
         }
-    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        const int kk = kk0 + f;  // key-dim step of 32: W^T tiles dt = 2 kk and 2 kk + 1
-        f32x4 w0 = {}, w1 = {};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ks >= nks) continue;
-            w0 = mfma16(ka[f][ks][0], tw[ks], w0);
-            w1 = mfma16(ka[f][ks][1], tw[ks], w1);
-        }
-        s.wf[rt][kk][lane] = bf16x8{(bf16)(-w0[0]), (bf16)(-w0[1]), (bf16)(-w0[2]), (bf16)(-w0[3]),
-                                    (bf16)(-w1[0]), (bf16)(-w1[1]), (bf16)(-w1[2]), (bf16)(-w1[3])};
     }
-    __syncthreads();  // T diag(beta) fragments complete
+}
+
+// ---- U = (T diag(beta)) V for state wave sw's 32 value columns (two column
+// tiles); the six T diag(beta) fragments are formed in registers (hi/lo).
+__device__ __forceinline__ void u8(const Smem8 &s, const int lane, const int sw, f32x4 (&u)[4][2]) {
+    const int m = lane & 15, g = lane >> 4;
+    bf16x8 vv[2][2];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) u[r] = f32x4{};
-    const bf16x8 vv[2] = {lds8(&s.vt[(16 * wave + m) * CS + 8 * g]), lds8(&s.vt[(16 * wave + m) * CS + 32 + 8 * g])};
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-    for (int f3 = 0; f3 < 2; ++f3) {
-        bf16x8 th[3][2];
+        for (int fks = 0; fks < 2; ++fks) vv[ct][fks] = lds8(&s.vt[(32 * sw + 16 * ct + m) * CS + 32 * fks + 8 * g]);
+    f32x4 bp[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        bp[ks][0] = *reinterpret_cast<const f32x4 *>(&s.beta[32 * ks + 8 * g]);
+        bp[ks][1] = *reinterpret_cast<const f32x4 *>(&s.beta[32 * ks + 8 * g + 4]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) u[rt][ct] = f32x4{};
+#pragma unroll
+    for (int f3 = 0; f3 < 2; ++f3) {  // three fragments per batch of T reads
+        f32x4 tr[3][2];
 #pragma unroll
         for (int fq = 0; fq < 3; ++fq) {
-            th[fq][0] = s.thf[0][3 * f3 + fq][lane];
-            th[fq][1] = s.thf[1][3 * f3 + fq][lane];
+            const int f = 3 * f3 + fq;
+            const int rt = frag_rt(f), ks = frag_ks(f);
+            tr[fq][0] = *reinterpret_cast<const f32x4 *>(&s.a[(16 * rt + m) * AS + 32 * ks + 8 * g]);
+            tr[fq][1] = *reinterpret_cast<const f32x4 *>(&s.a[(16 * rt + m) * AS + 32 * ks + 8 * g + 4]);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
         for (int fq = 0; fq < 3; ++fq) {
             const int f = 3 * f3 + fq;
-            const int frt = frag_rt(f), fks = frag_ks(f);
-            u[frt] = mfma16(th[fq][0], vv[fks], u[frt]);
-            u[frt] = mfma16(th[fq][1], vv[fks], u[frt]);
+            const int rt = frag_rt(f), ks = frag_ks(f);
+            float tb[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                tb[e] = tr[fq][0][e] * bp[ks][0][e];
+                tb[4 + e] = tr[fq][1][e] * bp[ks][1][e];
+            }
+            bf16x8 th, tl;
+            split8v(tb, th, tl);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                u[rt][ct] = mfma16(th, vv[ct][ks], u[rt][ct]);
+                u[rt][ct] = mfma16(tl, vv[ct][ks], u[rt][ct]);
+            }
         }
     }
-    __syncthreads();  // -W fragments complete; k / T fragments free for the next chunk
 }
 
-// ---- state I/O: K x V fp32 state <-> this wave's eight 16 x 16 tiles
-__device__ __forceinline__ void load_state8(f32x4 (&t)[8], const float *src, const int wave, const int lane) {
-    const int m = lane & 15, g = lane >> 4;
-    const float *b = src + 16 * wave + m;
+// ---- state-wave pieces of the state pass (two column tiles each).  Every
+// piece issues all of its LDS operand reads in one batch before its first
+// MFMA, so the LDS latency is paid once per piece.
+// diag(gamma) Q H of a chunk from the state at its start: qh[rt][ct] covers
+// rows 16 rt .. +15 (it later accumulates P v' in place)
+__device__ __forceinline__ void qh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int buf,
+                                   const int ln) {
+    const int m = ln & 15, g = ln >> 4;
+    bf16x8 qa[4][4];  // [k step][row tile]
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) t[dt][j] = b[(16 * dt + 4 * g + j) * DV];
+        for (int rt = 0; rt < 4; ++rt) qa[kk][rt] = lds8_perm16(&s.q[(16 * rt + m) * KS], 32 * kk, g);
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 hh[2], hl[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh[ct], hl[ct]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                qh[rt][ct] = mfma16(qa[kk][rt], hh[ct], qh[rt][ct]);
+                qh[rt][ct] = mfma16(qa[kk][rt], hl[ct], qh[rt][ct]);
+            }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&s.gam[buf][16 * rt + 4 * g]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] *= gm4;
+    }
 }
 
-__device__ __forceinline__ void store_state8(const f32x4 (&t)[8], float *dst, const int wave, const int lane) {
-    const int m = lane & 15, g = lane >> 4;
-    float *b = dst + 16 * wave + m;
+// v' = U - W H (vp enters holding U)
+__device__ __forceinline__ void wh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int ln) {
+    bf16x8 wa[4][4];  // [k step][row tile]
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[(16 * dt + 4 * g + j) * DV] = t[dt][j];
+        for (int rt = 0; rt < 4; ++rt) wa[kk][rt] = s.wf[rt][kk][ln];
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 hh[2], hl[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh[ct], hl[ct]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                vp[rt][ct] = mfma16(wa[kk][rt], hh[ct], vp[rt][ct]);
+                vp[rt][ct] = mfma16(wa[kk][rt], hl[ct], vp[rt][ct]);
+            }
+    }
 }
 
-// ---- one chunk's output tile of this wave (64 rows x 16 value columns)
-// through a wave-private LDS staging tile: every lane stores 16 contiguous bytes.
 // ---- one chunk's output from the accumulator registers straight to HBM.
-// Lane (m, g) holds value column 16 wave + m of rows 16 rt + 4 g + jj; a 4 x 4
+// Lane (m, g) holds value column col0 + m of rows 16 rt + 4 g + jj; a 4 x 4
 // transpose inside each quad of lanes (two DPP butterfly stages) gives lane
-// m = 4 a + b row 16 rt + 4 g + b, columns 16 wave + 4 a .. +3, so each row
-// tile leaves in one 16-byte (fp32) or 8-byte (bf16) store per lane.  The
-// buffer resource spans this sequence of this head: rows past the sequence
-// end are dropped by the hardware range check.
+// m = 4 a + b row 16 rt + 4 g + b, columns col0 + 4 a .. +3, so each row tile
+// leaves in one 16-byte (fp32) or 8-byte (bf16) store per lane.  The buffer
+// resource spans this sequence of this head: rows past the sequence end are
+// dropped by the hardware range check.
 __device__ __forceinline__ void write_o_regs(const FwdParams &p, const __amdgpu_buffer_rsrc_t ro, const int c,
-                                             const f32x4 (&ov)[4], const int wave, const int ln) {
+                                             const f32x4 (&ov)[4], const int col0, const int ln) {
     const int m = ln & 15, g = ln >> 4;
     const int qa = m >> 2, qb = m & 3;
     const unsigned es = p.o_f32 ? 4u : 2u;
     const unsigned rstride = (unsigned)p.Hv * DV * es;
-    const unsigned col = (unsigned)(16 * wave + 4 * qa) * es;
+    const unsigned col = (unsigned)(col0 + 4 * qa) * es;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
         float x[4];
@@ -1132,87 +1159,105 @@ __device__ __forceinline__ void write_o_regs(const FwdParams &p, const __amdgpu_
     }
 }
 
-// ---- the state pass of one chunk (every wave, its 16 value columns):
-//   v' = U - W H;  O = scale (diag(gamma) Q H + P v');
-//   H <- gamma_last H + K^T diag(gamma_last / gamma) v'
-__device__ __forceinline__ void chain8(const Smem8 &s, const FwdParams &p, f32x4 (&hacc)[8], const f32x4 (&qh)[4],
-                                       const f32x4 (&u)[4], f32x4 (&ov)[4], const bool out, const int buf,
-                                       const int ln) {
-    const int m = ln & 15, g = ln >> 4;
-    f32x4 vp[4] = {u[0], u[1], u[2], u[3]};
+// O = scale (diag(gamma) Q H + P v') for the two column tiles, then stored;
+// P v' accumulates onto diag(gamma) Q H in place
+__device__ __forceinline__ void out8(const Smem8 &s, const FwdParams &p, const __amdgpu_buffer_rsrc_t ro,
+                                     const f32x4 (&vp)[4][2], f32x4 (&acc)[4][2], const int c, const int buf,
+                                     const int sw, const int ln) {
+    bf16x8 pa[6][2];  // the six P fragments, hi and lo
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-        bf16x8 hh[2], hl[2], wa[2][4];
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-            const int kk = 2 * k2 + kq;
-            split_pair(hacc[2 * kk], hacc[2 * kk + 1], hh[kq], hl[kq]);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) wa[kq][rt] = s.wf[rt][kk][ln];
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq)
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                vp[rt] = mfma16(wa[kq][rt], hh[kq], vp[rt]);
-                vp[rt] = mfma16(wa[kq][rt], hl[kq], vp[rt]);
-            }
+    for (int f = 0; f < 6; ++f) {
+        pa[f][0] = s.pf[buf][0][f][ln];
+        pa[f][1] = s.pf[buf][1][f][ln];
     }
-    if (out) {
-        f32x4 pv[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-        bf16x8 pa[2][6];
-#pragma unroll
-        for (int f = 0; f < 6; ++f) {
-            pa[0][f] = s.pf[buf][0][f][ln];
-            pa[1][f] = s.pf[buf][1][f][ln];
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 vh, vl;
-            split_pair(vp[2 * ks], vp[2 * ks + 1], vh, vl);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                if (ks == 1 && rt < 2) continue;  // P is lower triangular
-                const int f = frag_of(rt, ks);
-                pv[rt] = mfma16(pa[0][f], vh, pv[rt]);
-                pv[rt] = mfma16(pa[0][f], vl, pv[rt]);
-                pv[rt] = mfma16(pa[1][f], vh, pv[rt]);
-            }
-        }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&s.gam[buf][16 * rt + 4 * g]);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) ov[rt][jj] = p.scale * (gm4[jj] * qh[rt][jj] + pv[rt][jj]);
-        }
-    }
-    const float glast = s.gam[buf][CH - 1];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s.dec[buf][16 * rt + 4 * g]);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) vp[rt][jj] *= d4[jj];
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) hacc[dt] *= glast;
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 vh, vl;
-        split_pair(vp[2 * ks], vp[2 * ks + 1], vh, vl);
+        bf16x8 vh[2], vl[2];
 #pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2) {
-            bf16x8 ka[4];
+        for (int ct = 0; ct < 2; ++ct) split_pair(vp[2 * ks][ct], vp[2 * ks + 1][ct], vh[ct], vl[ct]);
 #pragma unroll
-            for (int dq = 0; dq < 4; ++dq) ka[dq] = lds8_perm16(&s.kt[buf][(16 * (4 * d2 + dq) + m) * CS], 32 * ks, g);
-            __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+        for (int rt = 0; rt < 4; ++rt) {
+            if (ks == 1 && rt < 2) continue;  // P is lower triangular
+            const int f = frag_of(rt, ks);
 #pragma unroll
-            for (int dq = 0; dq < 4; ++dq) {
-                hacc[4 * d2 + dq] = mfma16(ka[dq], vh, hacc[4 * d2 + dq]);
-                hacc[4 * d2 + dq] = mfma16(ka[dq], vl, hacc[4 * d2 + dq]);
+            for (int ct = 0; ct < 2; ++ct) {
+                acc[rt][ct] = mfma16(pa[f][0], vh[ct], acc[rt][ct]);
+                acc[rt][ct] = mfma16(pa[f][0], vl[ct], acc[rt][ct]);
+                acc[rt][ct] = mfma16(pa[f][1], vh[ct], acc[rt][ct]);
             }
         }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        f32x4 ov[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) ov[rt] = p.scale * acc[rt][ct];
+        write_o_regs(p, ro, c, ov, 32 * sw + 16 * ct, ln);
+    }
+}
+
+// H <- gamma_last H + K^T diag(gamma_last / gamma) v'
+__device__ __forceinline__ void hupd8(const Smem8 &s, f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int buf,
+                                      const int ln) {
+    const int m = ln & 15, g = ln >> 4;
+    bf16x8 ka[2][8];  // [token step][key-dim tile]
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) ka[ks][dt] = lds8_perm16(&s.kt[buf][(16 * dt + m) * CS], 32 * ks, g);
+    f32x4 d4[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) d4[rt] = *reinterpret_cast<const f32x4 *>(&s.dec[buf][16 * rt + 4 * g]);
+    const float glast = s.gam[buf][CH - 1];
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) vp[rt][ct][jj] *= d4[rt][jj];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) hacc[ct][dt] *= glast;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 vh[2], vl[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) split_pair(vp[2 * ks][ct], vp[2 * ks + 1][ct], vh[ct], vl[ct]);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                hacc[ct][dt] = mfma16(ka[ks][dt], vh[ct], hacc[ct][dt]);
+                hacc[ct][dt] = mfma16(ka[ks][dt], vl[ct], hacc[ct][dt]);
+            }
+    }
+}
+
+// ---- state I/O: K x V fp32 state <-> state wave sw's two column tiles
+__device__ __forceinline__ void load_state8(f32x4 (&t)[2][8], const float *src, const int sw, const int lane) {
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const float *b = src + 32 * sw + 16 * ct + m;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t[ct][dt][j] = b[(16 * dt + 4 * g + j) * DV];
+    }
+}
+
+__device__ __forceinline__ void store_state8(const f32x4 (&t)[2][8], float *dst, const int sw, const int lane) {
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        float *b = dst + 32 * sw + 16 * ct + m;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[(16 * dt + 4 * g + j) * DV] = t[ct][dt][j];
     }
 }
 
@@ -1223,6 +1268,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
+    const bool state_wave = wave < 4;  // waves 0..3 hold the state, 4..7 prepare chunks
     const int seg = blockIdx.x / p.Hv;
     const int j = blockIdx.x % p.Hv;
     if (seg >= p.num_segments) return;
@@ -1256,78 +1302,118 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
     const int c_end = e.c_begin + e.c_count;
 
-    // ---- state: value columns 16 wave .. +15, eight 16-row tiles of key dims
-    f32x4 hacc[8];
+    const bool has_chunks = c_first < c_end;  // wave-uniform and equal across the workgroup
+    if (!has_chunks && !(state_wave && e.last && p.ht)) return;
+
+    Inputs in;
+    in.kstride = (unsigned)p.Hqk * DK * 2;
+    in.vstride = (unsigned)p.Hv * DV * 2;
+    in.gstride = (unsigned)p.Hv * 4;
+    in.k = make_rsrc(p.k + (e.row0 * p.Hqk + i_qk) * DK, (int64_t)e.seq_len * in.kstride);
+    in.q = make_rsrc(p.q + (e.row0 * p.Hqk + i_qk) * DK, (int64_t)e.seq_len * in.kstride);
+    in.v = make_rsrc(p.v + (e.row0 * p.Hv + j) * DV, (int64_t)e.seq_len * in.vstride);
+    in.g = make_rsrc(p.g + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
+    in.b = make_rsrc(p.beta + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
+
+    // Iteration c runs the state pass of chunk c (state waves) in step with the
+    // preparation of chunk c + 1 (preparation waves); c = c_first - 1 only
+    // prepares the first chunk.  K^T, the P fragments and the decays are
+    // double-buffered by chunk parity; U and Q H of the next chunk wait in the
+    // state waves' registers.
+    //   step  state waves                      preparation waves
+    //   top   store chunk c + 1 (all waves)
+    //   1     v' = U - W H                     gate scan, K K^T, P fragments
+    //   2     O = scale (gamma Q H + P v')     inverse level 0
+    //   3     H update                         inverse level 1
+    //   4a    Q H of chunk c + 1               inverse level 2 reads
+    //   4b    -                                inverse level 2 writes
+    //   5     U of chunk c + 1                 -W fragments of chunk c + 1
+    // Both roles run their own copy of the loop with the same seven barriers
+    // per iteration (a barrier counts arrivals, wherever they come from), so
+    // each role's registers are allocated for its own live values only.
+    // The preparation waves stage every chunk: its loads are issued in step 4a
+    // two chunks ahead and its tiles stored at the top of the iteration.
+    if (state_wave) {
+        // ---- state: value columns 32 wave .. +31
+        f32x4 hacc[2][8];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) hacc[dt] = f32x4{};
-    {
-        const float *src = nullptr;
-        if (from_h0 && p.h0) src = p.h0 + ((int64_t)e.n * p.Hv + j) * DK * DV;
-        if (!from_h0 && p.cp_mode == 1 /* EXACT */) src = p.ws_h + ((int64_t)seg * p.Hv + j) * DK * DV;
-        if (src) load_state8(hacc, src, wave, lane);
-    }
-
-    if (c_first < c_end) {
-        Inputs in;
-        in.kstride = (unsigned)p.Hqk * DK * 2;
-        in.vstride = (unsigned)p.Hv * DV * 2;
-        in.gstride = (unsigned)p.Hv * 4;
-        in.k = make_rsrc(p.k + (e.row0 * p.Hqk + i_qk) * DK, (int64_t)e.seq_len * in.kstride);
-        in.q = make_rsrc(p.q + (e.row0 * p.Hqk + i_qk) * DK, (int64_t)e.seq_len * in.kstride);
-        in.v = make_rsrc(p.v + (e.row0 * p.Hv + j) * DV, (int64_t)e.seq_len * in.vstride);
-        in.g = make_rsrc(p.g + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
-        in.b = make_rsrc(p.beta + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
-        const int64_t oes = p.o_f32 ? 4 : 2;
-        const __amdgpu_buffer_rsrc_t ro =
-            make_rsrc(static_cast<char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes, (int64_t)e.seq_len * p.Hv * DV * oes);
-
-        // Software pipeline over chunks: iteration c runs the state pass of
-        // chunk c beside the products of chunk c + 1, then the inverse and W/U
-        // of chunk c + 1.  K^T, P and the decays are double-buffered by chunk
-        // parity; U and Q H of the next chunk wait in registers.
-        Stage8 st;
-        load_chunk8(in, st, c_first, c_first >= e.c_begin, threadIdx.x, wave, true);
-        f32x4 qh[4], u[4], ov[4];
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) hacc[ct][dt] = f32x4{};
         {
-            int tid = threadIdx.x;
-            asm volatile("" : "+v"(tid));
-            const bool out0 = (c_first >= e.c_begin);
-            store_chunk8(s, st, tid, wave, c_first & 1);
-            __syncthreads();
-            load_chunk8(in, st, c_first + 1, c_first + 1 >= e.c_begin, tid, wave, c_first + 1 < c_end);
-            prep8_products(s, tid, wave, out0, c_first & 1);
-            __syncthreads();
-            prep8_inverse(s, tid, wave, out0, hacc, qh);
-            prep8_wu(s, tid, wave, u, c_first & 1);
+            const float *src = nullptr;
+            if (from_h0 && p.h0) src = p.h0 + ((int64_t)e.n * p.Hv + j) * DK * DV;
+            if (!from_h0 && p.cp_mode == 1 /* EXACT */) src = p.ws_h + ((int64_t)seg * p.Hv + j) * DK * DV;
+            if (src) load_state8(hacc, src, wave, lane);
         }
-        for (int c = c_first; c < c_end; ++c) {
-            // The thread index is made opaque once per chunk so that the
-            // compiler recomputes lane-derived LDS addresses inside the loop
-            // instead of hoisting hundreds of them into registers.
+        const int64_t oes = p.o_f32 ? 4 : 2;
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes,
+                                                    (int64_t)e.seq_len * p.Hv * DV * oes);
+        f32x4 u[4][2], vp[4][2], qh[4][2];
+        for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
+            const bool chain = c >= c_first;  // state pass of chunk c
+            const bool prep = c + 1 < c_end;  // preparation of chunk c + 1
+            const bool out = c >= e.c_begin;  // chunk c produces output (not a warm-up chunk)
+            const int b = c & 1, nb = (c + 1) & 1;
+            __syncthreads();
+            // A fresh opaque lane index per step keeps the compiler from
+            // hoisting lane-derived LDS addresses out of their steps and
+            // holding them all live at once.
+            auto lane_now = []() {
+                int t = threadIdx.x;
+                asm volatile("" : "+v"(t));
+                return t & 63;
+            };
+            if (chain) {
+                const int ln = lane_now();
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) vp[rt][ct] = u[rt][ct];
+                wh8(s, hacc, vp, ln);
+            }
+            __syncthreads();
+            if (chain && out) out8(s, p, ro, vp, qh, c, b, wave, lane_now());
+            __syncthreads();
+            if (chain) hupd8(s, hacc, vp, b, lane_now());
+            __syncthreads();
+            if (prep && c + 1 >= e.c_begin) qh8(s, hacc, qh, nb, lane_now());
+            __syncthreads();
+            __syncthreads();
+            if (prep) u8(s, lane_now(), wave, u);
+            __syncthreads();
+        }
+        if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
+    } else {
+        const int pw = wave - 4;
+        Stage8 st;
+        if (has_chunks) load_chunk8(in, st, c_first, c_first >= e.c_begin, threadIdx.x, true);
+        for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
+            // opaque thread index, once per chunk: lane-derived LDS addresses
+            // are recomputed inside the loop rather than hoisted
             int tid = threadIdx.x;
             asm volatile("" : "+v"(tid));
             const int ln = tid & 63;
-            const bool out = (c >= e.c_begin);  // warm-up chunks only advance the state
-            const bool more = (c + 1 < c_end);
-            const int b = c & 1, nb = b ^ 1;
-            if (more) store_chunk8(s, st, tid, wave, nb);
+            const bool prep = c + 1 < c_end;  // preparation of chunk c + 1
+            const int nb = (c + 1) & 1;
+            if (prep) store_chunk8(s, st, tid, nb);
             __syncthreads();
-            chain8(s, p, hacc, qh, u, ov, out, b, ln);
-            // chunk c's output and chunk c + 2's inputs: issued here and left
-            // in flight; the staging wait at the next iteration's top is the
-            // first to cover them
-            if (out) write_o_regs(p, ro, c, ov, wave, ln);
-            load_chunk8(in, st, c + 2, c + 2 >= e.c_begin, tid, wave, c + 2 < c_end);
-            if (more) {
-                prep8_products(s, tid, wave, c + 1 >= e.c_begin, nb);
-                __syncthreads();
-                prep8_inverse(s, tid, wave, c + 1 >= e.c_begin, hacc, qh);
-                prep8_wu(s, tid, wave, u, nb);
-            }
+            if (prep) prod8(s, ln, pw, c + 1 >= e.c_begin, nb);
+            __syncthreads();
+            if (prep) inv8_l0(s, ln, pw);
+            __syncthreads();
+            if (prep && pw < 2) inv8_l1(s, ln, pw);
+            __syncthreads();
+            load_chunk8(in, st, c + 2, c + 2 >= e.c_begin, tid, c + 2 < c_end);
+            L2Regs l2;
+            if (prep) inv8_l2a(s, ln, pw, l2);
+            __syncthreads();
+            if (prep) inv8_l2b(s, ln, pw, l2);
+            __syncthreads();
+            if (prep) wfrag8(s, ln, pw, nb);
+            __syncthreads();
         }
     }
-
-    if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
 }
 
 // ---------------------------------------------------------------- exact context parallelism
