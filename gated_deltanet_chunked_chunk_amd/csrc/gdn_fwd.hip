@@ -1060,8 +1060,11 @@ __device__ __forceinline__ void u8(const Smem8 &s, const int lane, const int sw,
 // ---- state-wave pieces of the state pass (two column tiles each).  Every
 // piece issues all of its LDS operand reads in one batch before its first
 // MFMA, so the LDS latency is paid once per piece.
-// diag(gamma) Q H of a chunk from the state at its start: qh[rt][ct] covers
-// rows 16 rt .. +15 (it later accumulates P v' in place)
+// (diag(gamma) Q H)^T of a chunk from the state at its start, i.e. H^T Q^T
+// with the state split as the A operand and the Q fragments as the B operand:
+// qh[rt][ct] lane (m, g) holds value column 16 ct + 4 g + j (of this wave's 32)
+// of query row 16 rt + m.  It later accumulates (P v')^T in place, and each
+// lane then owns four consecutive output columns of one row.
 __device__ __forceinline__ void qh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int buf,
                                    const int ln) {
     const int m = ln & 15, g = ln >> 4;
@@ -1084,15 +1087,15 @@ __device__ __forceinline__ void qh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                qh[rt][ct] = mfma16(qa[kk][rt], hh[ct], qh[rt][ct]);
-                qh[rt][ct] = mfma16(qa[kk][rt], hl[ct], qh[rt][ct]);
+                qh[rt][ct] = mfma16(hh[ct], qa[kk][rt], qh[rt][ct]);
+                qh[rt][ct] = mfma16(hl[ct], qa[kk][rt], qh[rt][ct]);
             }
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-        const f32x4 gm4 = *reinterpret_cast<const f32x4 *>(&s.gam[buf][16 * rt + 4 * g]);
+        const float gm = s.gam[buf][16 * rt + m];  // this lane's query row
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] *= gm4;
+        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] *= gm;
     }
 }
 
@@ -1119,51 +1122,16 @@ __device__ __forceinline__ void wh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f
     }
 }
 
-// ---- one chunk's output from the accumulator registers straight to HBM.
-// Lane (m, g) holds value column col0 + m of rows 16 rt + 4 g + jj; a 4 x 4
-// transpose inside each quad of lanes (two DPP butterfly stages) gives lane
-// m = 4 a + b row 16 rt + 4 g + b, columns col0 + 4 a .. +3, so each row tile
-// leaves in one 16-byte (fp32) or 8-byte (bf16) store per lane.  The buffer
-// resource spans this sequence of this head: rows past the sequence end are
-// dropped by the hardware range check.
-__device__ __forceinline__ void write_o_regs(const FwdParams &p, const __amdgpu_buffer_rsrc_t ro, const int c,
-                                             const f32x4 (&ov)[4], const int col0, const int ln) {
-    const int m = ln & 15, g = ln >> 4;
-    const int qa = m >> 2, qb = m & 3;
-    const unsigned es = p.o_f32 ? 4u : 2u;
-    const unsigned rstride = (unsigned)p.Hv * DV * es;
-    const unsigned col = (unsigned)(col0 + 4 * qa) * es;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        float x[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {  // stage 1: swap with lane b ^ 1 where bit 0 of b and jj differ
-            const float y = quad_dpp<0xb1>(ov[rt][jj ^ 1]);
-            x[jj] = ((qb ^ jj) & 1) ? y : ov[rt][jj];
-        }
-        float w[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {  // stage 2: swap with lane b ^ 2 where bit 1 of b and jj differ
-            const float y = quad_dpp<0x4e>(x[jj ^ 2]);
-            w[jj] = ((qb ^ jj) & 2) ? y : x[jj];
-        }
-        const unsigned off = (unsigned)(c * CH + 16 * rt + 4 * g + qb) * rstride + col;
-        if (p.o_f32) {
-            __builtin_amdgcn_raw_buffer_store_b128(
-                u32x4{__float_as_uint(w[0]), __float_as_uint(w[1]), __float_as_uint(w[2]), __float_as_uint(w[3])}, ro,
-                (int)off, 0, 0);
-        } else {
-            const bf16x4 h = {(bf16)w[0], (bf16)w[1], (bf16)w[2], (bf16)w[3]};
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), ro, (int)off, 0, 0);
-        }
-    }
-}
-
-// O = scale (diag(gamma) Q H + P v') for the two column tiles, then stored;
-// P v' accumulates onto diag(gamma) Q H in place
+// O^T = scale ((diag(gamma) Q H)^T + v'^T P^T) for the two column tiles:
+// the split v' tiles serve as A operands and the P fragments as B operands.
+// Lane (m, g) then holds four consecutive value columns 16 ct + 4 g .. +3 of
+// query row 16 rt + m, stored as one 16-byte (fp32) or 8-byte (bf16) piece
+// through a buffer resource that spans this sequence of this head (rows past
+// the sequence end are dropped by the hardware range check).
 __device__ __forceinline__ void out8(const Smem8 &s, const FwdParams &p, const __amdgpu_buffer_rsrc_t ro,
                                      const f32x4 (&vp)[4][2], f32x4 (&acc)[4][2], const int c, const int buf,
                                      const int sw, const int ln) {
+    const int m = ln & 15, g = ln >> 4;
     bf16x8 pa[6][2];  // the six P fragments, hi and lo
 #pragma unroll
     for (int f = 0; f < 6; ++f) {
@@ -1182,19 +1150,27 @@ __device__ __forceinline__ void out8(const Smem8 &s, const FwdParams &p, const _
             const int f = frag_of(rt, ks);
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                acc[rt][ct] = mfma16(pa[f][0], vh[ct], acc[rt][ct]);
-                acc[rt][ct] = mfma16(pa[f][0], vl[ct], acc[rt][ct]);
-                acc[rt][ct] = mfma16(pa[f][1], vh[ct], acc[rt][ct]);
+                acc[rt][ct] = mfma16(vh[ct], pa[f][0], acc[rt][ct]);
+                acc[rt][ct] = mfma16(vl[ct], pa[f][0], acc[rt][ct]);
+                acc[rt][ct] = mfma16(vh[ct], pa[f][1], acc[rt][ct]);
             }
         }
     }
+    const unsigned es = p.o_f32 ? 4u : 2u;
+    const unsigned rstride = (unsigned)p.Hv * DV * es;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        f32x4 ov[4];
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) ov[rt] = p.scale * acc[rt][ct];
-        write_o_regs(p, ro, c, ov, 32 * sw + 16 * ct, ln);
-    }
+        for (int ct = 0; ct < 2; ++ct) {
+            const f32x4 w = p.scale * acc[rt][ct];
+            const unsigned off = (unsigned)(c * CH + 16 * rt + m) * rstride + (unsigned)(32 * sw + 16 * ct + 4 * g) * es;
+            if (p.o_f32) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (int)off, 0, 0);
+            } else {
+                const bf16x4 h = {(bf16)w[0], (bf16)w[1], (bf16)w[2], (bf16)w[3]};
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), ro, (int)off, 0, 0);
+            }
+        }
 }
 
 // H <- gamma_last H + K^T diag(gamma_last / gamma) v'
@@ -1349,7 +1325,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int64_t oes = p.o_f32 ? 4 : 2;
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes,
                                                     (int64_t)e.seq_len * p.Hv * DV * oes);
-        f32x4 u[4][2], vp[4][2], qh[4][2];
+        f32x4 vp[4][2], qh[4][2];  // vp: U of the next chunk, then v' of this one
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
             const bool chain = c >= c_first;  // state pass of chunk c
             const bool prep = c + 1 < c_end;  // preparation of chunk c + 1
@@ -1364,14 +1340,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
                 asm volatile("" : "+v"(t));
                 return t & 63;
             };
-            if (chain) {
-                const int ln = lane_now();
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) vp[rt][ct] = u[rt][ct];
-                wh8(s, hacc, vp, ln);
-            }
+            if (chain) wh8(s, hacc, vp, lane_now());
             __syncthreads();
             if (chain && out) out8(s, p, ro, vp, qh, c, b, wave, lane_now());
             __syncthreads();
@@ -1380,7 +1349,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             if (prep && c + 1 >= e.c_begin) qh8(s, hacc, qh, nb, lane_now());
             __syncthreads();
             __syncthreads();
-            if (prep) u8(s, lane_now(), wave, u);
+            if (prep) u8(s, lane_now(), wave, vp);
             __syncthreads();
         }
         if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
