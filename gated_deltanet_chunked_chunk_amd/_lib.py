@@ -8,6 +8,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
+ABI_VERSION = 2  # GDN_ABI_VERSION of include/gdn.h this binding matches
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_DTYPE_BF16, GDN_DTYPE_F32 = 0, 1
 CP_MODES = {"off": 0, "exact": 1, "warmup": 2, "auto": 3}
@@ -47,6 +48,7 @@ class FwdPtrs(ctypes.Structure):
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
         ("initial_state", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
         ("o", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
+        ("h", ctypes.c_void_p), ("A", ctypes.c_void_p),
     ]
 
 
@@ -72,6 +74,9 @@ def lib():
         L.gdn_fwd.restype = ctypes.c_int
         L.gdn_fwd.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(FwdPtrs), ctypes.c_void_p, ctypes.c_size_t,
                               ctypes.c_void_p]
+        if L.gdn_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.gdn_abi_version()}, this binding expects "
+                               f"{ABI_VERSION}; rebuild it")
         L.gdn_chunk_cumsum.restype = ctypes.c_int
         L.gdn_chunk_cumsum.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,

@@ -88,9 +88,38 @@ def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
     [N + 1] (B must be 1).  Returns (o [B, T, H_v, V], final_state or None).
     ``cp`` selects the intra-GPU context parallelism: "auto", "warmup", "exact", "off".
     """
+    o, ht, _, _ = _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens, cp=cp,
+                           o_dtype=o_dtype, cp_lambda=cp_lambda, cp_segment_chunks=cp_segment_chunks,
+                           cp_warmup_chunks=cp_warmup_chunks, out=out, workspace=workspace)
+    return o, ht
+
+
+def chunk_gated_delta_rule_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                               beta: torch.Tensor, scale: Optional[float] = None,
+                               initial_state: Optional[torch.Tensor] = None, cu_seqlens=None,
+                               output_final_state: bool = True, **kw):
+    """The pages' low-level forward (aisparkup.com FlashQLA wiki, "low-level
+    API"): returns (g, A, o, h, final_state) with
+      g  fp32 [B, T, H_v]: the chunk-local running sum of the gates;
+      A  fp32 [B, T, H_v, 64]: for each token, its row of its chunk's WY matrix
+         (I + A~)^{-1}, A~_is = beta_i exp(G_i - G_s) k_i.k_s (s < i);
+      o  [B, T, H_v, V] (bf16 unless o_dtype="f32");
+      h  fp32 [total_chunks, H_v, K, V]: S^T at the start of every chunk;
+      final_state fp32 [N, H_v, K, V] or None.
+    Everything except g comes from one gdn_fwd call; g from gdn_chunk_cumsum."""
+    o, ht, h, A = _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                           want_h=True, want_a=True, **kw)
+    g_cum = chunk_cumsum(g, 64, cu_seqlens)
+    return g_cum, A, o, h, ht
+
+
+def _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens, *, cp: str = "auto",
+             o_dtype: Optional[str] = None, cp_lambda: float = 0.0, cp_segment_chunks: int = 0,
+             cp_warmup_chunks: int = 0, out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, want_h: bool = False, want_a: bool = False):
     dev = q.device
     if dev.type != "cuda":
-        raise ValueError("chunk_gated_delta_rule runs on a GPU tensor; there is no CPU path")
+        raise ValueError("the forward runs on GPU tensors; there is no CPU path")
     _need(q, "q", torch.bfloat16, dev)
     _need(k, "k", torch.bfloat16, dev)
     _need(v, "v", torch.bfloat16, dev)
@@ -127,17 +156,20 @@ def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
     else:
         _need(out, "out", o_t, dev)
     ht = torch.empty(N, Hv, K, V, dtype=torch.float32, device=dev) if output_final_state else None
+    h = torch.empty(info["total_chunks"], Hv, K, V, dtype=torch.float32, device=dev) if want_h else None
+    A = torch.empty(B, T, Hv, 64, dtype=torch.float32, device=dev) if want_a else None
     if workspace is None or workspace.numel() < info["workspace_bytes"] or workspace.data_ptr() % 256:
         workspace = _workspace(info["workspace_bytes"], dev)
     ptrs = L.FwdPtrs(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                      initial_state.data_ptr() if initial_state is not None else None,
                      cu_dev.data_ptr() if cu_dev is not None else None,
-                     out.data_ptr(), ht.data_ptr() if ht is not None else None)
+                     out.data_ptr(), ht.data_ptr() if ht is not None else None,
+                     h.data_ptr() if h is not None else None, A.data_ptr() if A is not None else None)
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         L.check(L.lib().gdn_fwd(ctypes.byref(desc), ctypes.byref(ptrs), ctypes.c_void_p(workspace.data_ptr()),
                                 workspace.numel(), ctypes.c_void_p(stream)))
-    return out, ht
+    return out, ht, h, A
 
 
 class PreparedForward:
@@ -198,4 +230,5 @@ def chunk_cumsum(g: torch.Tensor, chunk: int = 64, cu_seqlens=None, out: Optiona
     return out
 
 
-__all__: Sequence[str] = ("chunk_gated_delta_rule", "chunk_cumsum", "plan", "make_desc", "PreparedForward")
+__all__: Sequence[str] = ("chunk_gated_delta_rule", "chunk_gated_delta_rule_fwd", "chunk_cumsum", "plan", "make_desc",
+                          "PreparedForward")

@@ -230,18 +230,23 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
         if (((uintptr_t)p->g | (uintptr_t)p->beta) & 3) return fail(GDN_EINVAL, "g and beta must be 4-byte aligned");
         if ((uintptr_t)p->o & 15) return fail(GDN_EINVAL, "o must be 16-byte aligned");
     }
+    const size_t n_h = (size_t)P.total_chunks * d->H_v * d->K * d->V, n_a = rows * d->H_v * gdn::kChunk;
+    if (((uintptr_t)p->h | (uintptr_t)p->A) & 15) return fail(GDN_EINVAL, "h and A must be 16-byte aligned");
     struct Buf { const void *ptr; size_t bytes; const char *name; };
     const Buf in[] = {{p->q, n_qk * 2, "q"}, {p->k, n_qk * 2, "k"}, {p->v, n_v * 2, "v"},
                       {p->g, n_g * 4, "g"}, {p->beta, n_g * 4, "beta"},
                       {p->initial_state, n_state * 4, "initial_state"},
                       {p->cu_seqlens, varlen ? (size_t)(d->num_seqs + 1) * 4 : 0, "cu_seqlens"},
                       {workspace, P.workspace, "workspace"}};
-    for (const Buf &b : in) {
-        if (overlaps(p->o, n_v * osz, b.ptr, b.bytes)) return fail(GDN_EINVAL, "o overlaps %s", b.name);
-        if (overlaps(p->final_state, n_state * 4, b.ptr, b.bytes))
-            return fail(GDN_EINVAL, "final_state overlaps %s", b.name);
+    const Buf outs[] = {{p->o, n_v * osz, "o"}, {p->final_state, n_state * 4, "final_state"},
+                        {p->h, p->h ? n_h * 4 : 0, "h"}, {p->A, p->A ? n_a * 4 : 0, "A"}};
+    for (const Buf &ob : outs) {
+        for (const Buf &b : in)
+            if (overlaps(ob.ptr, ob.bytes, b.ptr, b.bytes)) return fail(GDN_EINVAL, "%s overlaps %s", ob.name, b.name);
+        for (const Buf &b : outs)
+            if (&b != &ob && overlaps(ob.ptr, ob.bytes, b.ptr, b.bytes))
+                return fail(GDN_EINVAL, "%s overlaps %s", ob.name, b.name);
     }
-    if (overlaps(p->o, n_v * osz, p->final_state, n_state * 4)) return fail(GDN_EINVAL, "o overlaps final_state");
     if ((P.workspace > 0 && !workspace) || workspace_bytes < P.workspace)
         return fail(GDN_EWORKSPACE, "workspace needs %zu bytes (got %zu at %p)", P.workspace, workspace_bytes,
                     workspace);
@@ -271,6 +276,8 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
     fp.warmup_cap = P.warmup;
     fp.o_f32 = d->o_dtype == GDN_DTYPE_F32;
     fp.scale = d->scale;
+    fp.h_out = p->h;
+    fp.a_out = p->A;
     if (P.cp_mode == GDN_CP_EXACT) {
         fp.ws_s = (float *)workspace;
         fp.ws_m = (float *)((char *)workspace + P.state_bytes);

@@ -1212,6 +1212,41 @@ __device__ __forceinline__ void hupd8(const Smem8 &s, f32x4 (&hacc)[2][8], f32x4
     }
 }
 
+// ---- low-level outputs
+// First global chunk index of sequence n (chunks of all sequences in order).
+__device__ __forceinline__ int seq_chunk_base(const FwdParams &p, int n, int lane) {
+    if (!p.cu) return n * seq_chunks(p.T);
+    int base = 0;
+    for (int n0 = 0; n0 < n; n0 += 64) {
+        const int nn = n0 + lane;
+        int cnt = (nn < n) ? seq_chunks((int64_t)p.cu[nn + 1] - p.cu[nn]) : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+        base += __builtin_amdgcn_readfirstlane(cnt);
+    }
+    return base;
+}
+
+// One chunk's WY matrix T (s.a, complete) as rows of A: preparation wave pw,
+// thread t = 64 pw + lane stores row t / 4, columns 16 (t % 4) .. +15.  The
+// upper-right 32 x 32 block of s.a is never written by the inverse; its zeros
+// are supplied here.  Rows past the sequence end fall outside the buffer
+// resource and are dropped.
+__device__ __forceinline__ void store_t8(const Smem8 &s, const FwdParams &p, const __amdgpu_buffer_rsrc_t ra,
+                                         const int c, const int pw, const int lane) {
+    const int t = 64 * pw + lane;
+    const int row = t >> 2, c0 = 16 * (t & 3);
+    const unsigned rstride = (unsigned)p.Hv * CH * 4u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int col = c0 + 4 * i;
+        f32x4 x = *reinterpret_cast<const f32x4 *>(&s.a[row * AS + col]);
+        if (row < 32 && col >= 32) x = f32x4{};
+        const unsigned off = (unsigned)(c * CH + row) * rstride + (unsigned)col * 4u;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ra, (int)off, 0, 0);
+    }
+}
+
 // ---- state I/O: K x V fp32 state <-> state wave sw's two column tiles
 __device__ __forceinline__ void load_state8(f32x4 (&t)[2][8], const float *src, const int sw, const int lane) {
     const int m = lane & 15, g = lane >> 4;
@@ -1326,6 +1361,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes,
                                                     (int64_t)e.seq_len * p.Hv * DV * oes);
         f32x4 vp[4][2], qh[4][2];  // vp: U of the next chunk, then v' of this one
+        const int cbase = p.h_out ? seq_chunk_base(p, e.n, lane) : 0;
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
             const bool chain = c >= c_first;  // state pass of chunk c
             const bool prep = c + 1 < c_end;  // preparation of chunk c + 1
@@ -1346,7 +1382,10 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             __syncthreads();
             if (chain) hupd8(s, hacc, vp, b, lane_now());
             __syncthreads();
-            if (prep && c + 1 >= e.c_begin) qh8(s, hacc, qh, nb, lane_now());
+            if (prep && c + 1 >= e.c_begin) {
+                qh8(s, hacc, qh, nb, lane_now());
+                if (p.h_out) store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
+            }
             __syncthreads();
             __syncthreads();
             if (prep) u8(s, lane_now(), wave, vp);
@@ -1355,6 +1394,8 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
         if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
     } else {
         const int pw = wave - 4;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a_out ? p.a_out + ((int64_t)e.row0 * p.Hv + j) * CH : nullptr,
+                                                    p.a_out ? (int64_t)e.seq_len * p.Hv * CH * 4 : 0);
         Stage8 st;
         if (has_chunks) load_chunk8(in, st, c_first, c_first >= e.c_begin, threadIdx.x, true);
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
@@ -1379,6 +1420,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             __syncthreads();
             if (prep) inv8_l2b(s, ln, pw, l2);
             __syncthreads();
+            if (prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, ra, c + 1, pw, ln);
             if (prep) wfrag8(s, ln, pw, nb);
             __syncthreads();
         }

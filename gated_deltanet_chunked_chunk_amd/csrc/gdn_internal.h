@@ -56,6 +56,8 @@ struct FwdParams {
     // exact context parallelism (workspace, each [num_segments][Hv][K][V] fp32):
     // per-segment zero-start state S, transition map M, and segment-start state H
     float *ws_s, *ws_m, *ws_h;
+    // optional low-level outputs: per-chunk start states, per-chunk WY matrices
+    float *h_out, *a_out;
 };
 
 // Launchers (gdn_fwd.hip).  Each returns the hipError_t of its launch as int.

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
@@ -113,6 +113,20 @@ typedef struct {
     const int32_t *cu_seqlens;      /* device offsets, NULL iff the call is not varlen */
     void *o;                        /* bf16 or fp32 per o_dtype */
     float *final_state;             /* fp32, NULL iff want_ht == 0 */
+    /* Low-level outputs (wiki, "low-level API": g, A, o, h, final_state),
+     * optional (NULL = not produced), 16-byte aligned, caller-owned, and not
+     * overlapping any other tensor:
+     *   h  fp32 [total_chunks, H_v, K, V]: S^T at the start of every chunk,
+     *      chunks of all sequences in order (total_chunks from gdn_fwd_plan);
+     *   A  fp32 [B * T, H_v, chunk]: for the token in row i of its chunk, row
+     *      i of that chunk's WY matrix (I + A~)^{-1}, A~_is = beta_i
+     *      exp(G_i - G_s) k_i.k_s for s < i (unit diagonal, zeros above it).
+     * With WARMUP/AUTO context parallelism, h at a segment's chunks carries
+     * the warm-up approximation of the state (the same as o); h of a chunk
+     * that is only a warm-up chunk of a later segment is written by the
+     * segment that owns it. */
+    float *h;
+    float *A;
 } gdn_fwd_ptrs;
 
 /* ABI version this library was built with (GDN_ABI_VERSION). */

@@ -131,3 +131,65 @@ def chunk_cumsum(g, chunk=64, cu_seqlens=None, lib=None):
     if rc != 0:
         raise ValueError(f"oracle.chunk_cumsum failed with code {rc}")
     return out
+
+
+def _seqs(B, T, cu_seqlens):
+    """(batch row, first token, length) of every sequence, in order."""
+    if cu_seqlens is None:
+        return [(b, 0, T) for b in range(B)]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return [(0, int(cu[n]), int(cu[n + 1] - cu[n])) for n in range(len(cu) - 1)]
+
+
+def chunk_states(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, chunk=64, n_threads=None,
+                 lib=None):
+    """The state at the start of every chunk (the low-level forward's h; wiki,
+    "low-level API"), by its plain definition: for chunk c of sequence n, the
+    final state of the token-by-token recurrence (`fwd`) run over that
+    sequence's first c * chunk tokens from its initial state.  Chunks of all
+    sequences in order.  Returns float64 [total_chunks, Hv, K, V] (S^T)."""
+    q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
+    B, T, Hqk, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    h0 = None if initial_state is None else _f32(initial_state)
+    out = []
+    for n, (b, t0, L) in enumerate(_seqs(B, T, cu_seqlens)):
+        start = np.zeros((Hv, K, V)) if h0 is None else h0[n].astype(np.float64)
+        for c in range((L + chunk - 1) // chunk):
+            if c == 0:
+                out.append(start)
+                continue
+            t1 = t0 + c * chunk
+            _, ht = fwd(q[b:b + 1, t0:t1], k[b:b + 1, t0:t1], v[b:b + 1, t0:t1], g[b:b + 1, t0:t1],
+                        beta[b:b + 1, t0:t1], scale=scale, initial_state=None if h0 is None else h0[n:n + 1],
+                        n_threads=n_threads, lib=lib)
+            out.append(ht[0])
+    if not out:
+        return np.zeros((0, Hv, K, V))
+    return np.stack(out)
+
+
+def chunk_wy_inverse(k, g, beta, H_v, cu_seqlens=None, chunk=64):
+    """The WY matrix of every chunk (the low-level forward's A; wiki,
+    "low-level API"), by its definition: within a chunk, with G the running
+    sum of g from the chunk start, A~_is = beta_i exp(G_i - G_s) k_i.k_s for
+    s < i (0 elsewhere) and T = (I + A~)^{-1}; token i of the chunk gets row i
+    of T.  v-head j reads key head j // (H_v / H_qk).  A partial last chunk
+    uses its own rows only (its T is the leading block of the padded one).
+    Returns float64 [B, T, H_v, chunk]."""
+    k, g, beta = _f32(k), _f32(g), _f32(beta)
+    B, T, Hqk, K = k.shape
+    grp = H_v // Hqk
+    out = np.zeros((B, T, H_v, chunk))
+    for b, t0, L in _seqs(B, T, cu_seqlens):
+        for c0 in range(t0, t0 + L, chunk):
+            c1 = min(c0 + chunk, t0 + L)
+            n = c1 - c0
+            strict = np.tril(np.ones((n, n), dtype=bool), -1)
+            for j in range(H_v):
+                kc = k[b, c0:c1, j // grp].astype(np.float64)
+                G = np.cumsum(g[b, c0:c1, j].astype(np.float64))
+                decay = np.exp(np.where(strict, G[:, None] - G[None, :], 0.0))
+                A = np.where(strict, beta[b, c0:c1, j].astype(np.float64)[:, None] * decay * (kc @ kc.T), 0.0)
+                out[b, c0:c1, j, :n] = np.linalg.inv(np.eye(n) + A)
+    return out

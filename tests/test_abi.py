@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = L.lib()
-    assert lib.gdn_abi_version() == 1
+    assert lib.gdn_abi_version() == L.ABI_VERSION == 2
     for st in (0, -1, -2, -3, -4):
         assert lib.gdn_status_str(st)
     assert b"unknown" in lib.gdn_status_str(42)
@@ -137,6 +137,19 @@ def test_fwd_validation_happens_before_any_launch():
     # device offsets without host offsets
     ptrs = L.FwdPtrs(base, base * 2, base * 3, base * 4, base * 5, base * 6, base * 10, base * 7, base * 9)
     assert lib.gdn_fwd(ctypes.byref(d), ctypes.byref(ptrs), None, 0, None) == L.GDN_EINVAL
+    # low-level outputs: misaligned h, A overlapping o, h overlapping A
+    ptrs = L.FwdPtrs(base, base * 2, base * 3, base * 4, base * 5, base * 6, None, base * 7, base * 8,
+                     base * 9 + 8, None)
+    assert lib.gdn_fwd(ctypes.byref(d), ctypes.byref(ptrs), ws, 4096, None) == L.GDN_EINVAL
+    assert b"16-byte aligned" in lib.gdn_last_error()
+    ptrs = L.FwdPtrs(base, base * 2, base * 3, base * 4, base * 5, base * 6, None, base * 7, base * 8,
+                     None, base * 7 + 512)
+    assert lib.gdn_fwd(ctypes.byref(d), ctypes.byref(ptrs), ws, 4096, None) == L.GDN_EINVAL
+    assert b"A overlaps o" in lib.gdn_last_error() or b"o overlaps A" in lib.gdn_last_error()
+    ptrs = L.FwdPtrs(base, base * 2, base * 3, base * 4, base * 5, base * 6, None, base * 7, base * 8,
+                     base * 9, base * 9 + 4096)
+    assert lib.gdn_fwd(ctypes.byref(d), ctypes.byref(ptrs), ws, 4096, None) == L.GDN_EINVAL
+    assert b"overlaps" in lib.gdn_last_error()
 
 
 def test_python_api_refuses_cpu_tensors():
