@@ -18,6 +18,7 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
        [--cp auto|warmup|off] [--no-cpu-baseline] [--cpu-seconds 10]
+       python bench.py --sweep [--steps 20] [--warmup 5] [--cp auto]   (head-setting sweep)
 """
 import argparse
 import hashlib
@@ -117,6 +118,61 @@ def cpu_baseline(x, w, target_s: float):
             "sample": f"first {T} of {w.T} tokens, all {w.H_v} v-heads, fp64 per-token recurrence, {dt:.1f} s"}
 
 
+# The pages' model family at its tensor-parallel shares (blog, benchmark table;
+# wiki, benchmarks: head settings h in {64, 48, 32, 24, 16, 8} over TP1..TP8):
+# per-GPU (H_qk, H_v) and the model / TP they stand for.
+SWEEP_HEADS = [((2, 8), "397B/122B TP8"), ((4, 16), "397B/122B TP4"), ((8, 32), "397B/122B TP2"),
+               ((16, 64), "397B/122B TP1"), ((8, 24), "27B TP2"), ((16, 48), "27B TP1"), ((16, 16), "2B/0.8B TP1")]
+SWEEP_SHAPES = [(1, 8192), (1, 32768), (4, 32768), (1, 131072)]
+# pages' H200 FlashQLA forward latency at 1 x 32768 (blog, benchmark table): context only
+PAGES_H200_MS = {(2, 8): 0.310, (4, 16): 0.486, (8, 24): 0.659, (16, 16): 0.493}
+
+
+def sweep(steps: int, warmup: int, cp: str):
+    """Forward latency over the pages' head settings and several batch lengths:
+    one JSON line per case, then a markdown table on stderr."""
+    import torch
+    from gated_deltanet_chunked_chunk_amd import PreparedForward
+    from gated_deltanet_chunked_chunk_amd import workloads as W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows = []
+    for (hqk, hv), model in SWEEP_HEADS:
+        for B, T in SWEEP_SHAPES:
+            x = W.device_inputs(B, T, hqk, hv, seed=1000 + hqk * 100 + hv, device=dev)
+            call = PreparedForward(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
+                                   initial_state=x["initial_state"], output_final_state=True, cp=cp)
+            for _ in range(warmup):
+                call()
+            stream = torch.cuda.current_stream(dev)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(steps):
+                call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / steps
+            alg = algorithmic_bytes(x)
+            frac = alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+            ref = PAGES_H200_MS.get((hqk, hv)) if (B, T) == (1, 32768) else None
+            line = {"model": model, "H_qk": hqk, "H_v": hv, "B": B, "T": T, "cp": call.info["cp"],
+                    "segment_chunks": call.info["segment_chunks"], "workgroups": call.info["workgroups"],
+                    "ms": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+                    "hbm_roofline_frac": round(frac, 4), "pages_h200_ms": ref}
+            print(json.dumps(line), flush=True)
+            rows.append(line)
+            del call, x
+            torch.cuda.empty_cache()
+    print("| model / TP | H_qk | H_v | B x T | CP (L, workgroups) | ms | M tokens/s | HBM roofline | pages H200 ms |",
+          file=sys.stderr)
+    print("|---|---|---|---|---|---|---|---|---|", file=sys.stderr)
+    for r in rows:
+        print(f"| {r['model']} | {r['H_qk']} | {r['H_v']} | {r['B']} x {r['T']} | {r['cp']} ({r['segment_chunks']}, "
+              f"{r['workgroups']}) | {r['ms']:.3f} | {r['tokens_per_s'] / 1e6:.1f} | {r['hbm_roofline_frac']:.3f} | "
+              f"{r['pages_h200_ms'] if r['pages_h200_ms'] else ''} |", file=sys.stderr)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +183,8 @@ def main():
     ap.add_argument("--o-dtype", default="bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="forward latency over the pages' head settings and batch lengths (one JSON line each)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -139,6 +197,10 @@ def main():
         print("bench.py: this build measures one GPU only (the forward shards over (sequence, head-group) "
               "with no communication; see the design notes); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.sweep:
+        sweep(args.steps, args.warmup, args.cp)
+        return
 
     import torch
     from gated_deltanet_chunked_chunk_amd import PreparedForward

@@ -116,13 +116,13 @@ int make_plan(const gdn_fwd_desc *d, Plan *P) {
         total_chunks = d->B * (int64_t)gdn::seq_chunks(d->T);
     }
     if (total_chunks > INT32_MAX) return fail(GDN_EINVAL, "too many chunks");
-    // each sequence of each head is read (and its output written) through one
-    // buffer resource whose byte range must stay below 2^31
+    // every chunk of a sequence is read (and its outputs written) through
+    // buffer resources over its 64 rows, whose byte range must stay below 2^31
     const int64_t osz = d->o_dtype == GDN_DTYPE_F32 ? 4 : 2;
-    const int64_t row_bytes = std::max<int64_t>((int64_t)d->H_qk * d->K * 2, (int64_t)d->H_v * d->V * osz);
-    if ((max_len + gdn::kChunk) * row_bytes >= ((int64_t)1 << 31))
-        return fail(GDN_EUNSUPPORTED, "a sequence of %lld tokens exceeds the 2 GiB per-sequence range",
-                    (long long)max_len);
+    const int64_t row_bytes = std::max({(int64_t)d->H_qk * d->K * 2, (int64_t)d->H_v * d->V * osz,
+                                        (int64_t)d->H_v * gdn::kChunk * 4});
+    if ((int64_t)gdn::kChunk * row_bytes >= ((int64_t)1 << 31))
+        return fail(GDN_EUNSUPPORTED, "%d heads exceed the 2 GiB per-chunk range", d->H_v);
 
     P->rows = d->B * d->T;
     P->N = d->num_seqs;

@@ -124,16 +124,26 @@ __device__ __forceinline__ void split8(const f32x16 &acc, int s, bf16x8 &hi, bf1
 }
 
 // ---------------------------------------------------------------- chunk loads
-// Buffer resources span exactly one sequence of one head, so rows past the
-// sequence end come back as zeros (hardware range check): a partial last
-// chunk behaves as if padded with g = beta = 0, k = q = v = 0.
+// Every chunk of a sequence is read (and its output written) through buffer
+// resources that start at the chunk's first row and end at the chunk's last
+// row inside the sequence, so rows past the sequence end come back as zeros
+// and stores to them are dropped (hardware range check): a partial last chunk
+// behaves as if padded with g = beta = 0, k = q = v = 0.  Offsets stay below
+// 64 rows, whatever the sequence length.
 struct Inputs {
-    __amdgpu_buffer_rsrc_t k, q, v, g, b;
+    const char *k, *q, *v, *g, *b;       // this sequence's first row, this head
     unsigned kstride, vstride, gstride;  // bytes per token row
+    int seq_len;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Resource over chunk c's rows of a per-sequence tensor (no rows past the end).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void *base, unsigned stride, int c, int seq_len) {
+    const int rows = min(max(seq_len - c * CH, 0), CH);
+    return make_rsrc(static_cast<const char *>(base) + (int64_t)c * CH * stride, (int64_t)rows * stride);
 }
 
 // Thread t stages rows 4*(t % 16) .. +3, columns 8*(t / 16) .. +7 of each
@@ -145,20 +155,22 @@ struct Stage {
 
 __device__ __forceinline__ void load_chunk(const Inputs &in, Stage &st, int c, bool need_q, int t) {
     const int rg = t & 15, cg = t >> 4;
+    const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(in.k, in.kstride, c, in.seq_len);
+    const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(in.q, in.kstride, c, in.seq_len);
+    const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(in.v, in.vstride, c, in.seq_len);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        // offsets are unsigned: past the range they wrap to large values,
-        // which the range check also turns into zeros
-        const unsigned tok = (unsigned)(c * CH + 4 * rg + r);
-        st.k[r] = __builtin_amdgcn_raw_buffer_load_b128(in.k, (int)(tok * in.kstride + 16u * cg), 0, 0);
-        st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(in.v, (int)(tok * in.vstride + 16u * cg), 0, 0);
-        if (need_q) st.q[r] = __builtin_amdgcn_raw_buffer_load_b128(in.q, (int)(tok * in.kstride + 16u * cg), 0, 0);
+        const unsigned row = (unsigned)(4 * rg + r);
+        st.k[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(row * in.kstride + 16u * cg), 0, 0);
+        st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(row * in.vstride + 16u * cg), 0, 0);
+        if (need_q) st.q[r] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(row * in.kstride + 16u * cg), 0, 0);
     }
     if (t < CH) {
-        const unsigned tok = (unsigned)(c * CH + t);
         // the b32 loads return raw bits
-        st.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.g, (int)(tok * in.gstride), 0, 0));
-        st.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.b, (int)(tok * in.gstride), 0, 0));
+        const __amdgpu_buffer_rsrc_t rg_ = chunk_rsrc(in.g, in.gstride, c, in.seq_len);
+        const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(in.b, in.gstride, c, in.seq_len);
+        st.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg_, (int)(t * in.gstride), 0, 0));
+        st.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)(t * in.gstride), 0, 0));
     }
 }
 
@@ -630,26 +642,30 @@ struct Stage8 {
     float g, b;
 };
 
-constexpr unsigned kOutOfRange = 0x80000000u;  // beyond every buffer range (all are below 2^31 bytes)
+constexpr unsigned kOutOfRange = 0x80000000u;  // beyond every chunk's range (64 rows, below 2^31 bytes)
 
 __device__ __forceinline__ void load_chunk8(const Inputs &in, Stage8 &st, int c, bool need_q, int t, bool valid) {
     int rg, cg;
     stage_coords(t, rg, cg);
+    const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(in.k, in.kstride, c, in.seq_len);
+    const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(in.q, in.kstride, c, in.seq_len);
+    const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(in.v, in.vstride, c, in.seq_len);
+    const __amdgpu_buffer_rsrc_t rg_ = chunk_rsrc(in.g, in.gstride, c, in.seq_len);
+    const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(in.b, in.gstride, c, in.seq_len);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const unsigned tok = (unsigned)(c * CH + 4 * rg + r);
-        const unsigned ok = valid ? tok * in.kstride + 16u * cg : kOutOfRange;
-        const unsigned ov = valid ? tok * in.vstride + 16u * cg : kOutOfRange;
-        const unsigned oq = (valid && need_q) ? tok * in.kstride + 16u * cg : kOutOfRange;
-        st.k[r] = __builtin_amdgcn_raw_buffer_load_b128(in.k, (int)ok, 0, 0);
-        st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(in.v, (int)ov, 0, 0);
-        st.q[r] = __builtin_amdgcn_raw_buffer_load_b128(in.q, (int)oq, 0, 0);
+        const unsigned row = (unsigned)(4 * rg + r);
+        const unsigned ok = valid ? row * in.kstride + 16u * cg : kOutOfRange;
+        const unsigned ov = valid ? row * in.vstride + 16u * cg : kOutOfRange;
+        const unsigned oq = (valid && need_q) ? row * in.kstride + 16u * cg : kOutOfRange;
+        st.k[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)ok, 0, 0);
+        st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)ov, 0, 0);
+        st.q[r] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)oq, 0, 0);
     }
     const int tt = t & 255;
-    const unsigned tok = (unsigned)(c * CH + tt);
-    const unsigned goff = (valid && tt < CH) ? tok * in.gstride : kOutOfRange;
-    st.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.g, (int)goff, 0, 0));
-    st.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(in.b, (int)goff, 0, 0));
+    const unsigned goff = (valid && tt < CH) ? (unsigned)tt * in.gstride : kOutOfRange;
+    st.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg_, (int)goff, 0, 0));
+    st.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)goff, 0, 0));
 }
 
 // Four rows x eight columns as eight packed column pieces (4 bf16 each)
@@ -1126,9 +1142,9 @@ __device__ __forceinline__ void wh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f
 // the split v' tiles serve as A operands and the P fragments as B operands.
 // Lane (m, g) then holds four consecutive value columns 16 ct + 4 g .. +3 of
 // query row 16 rt + m, stored as one 16-byte (fp32) or 8-byte (bf16) piece
-// through a buffer resource that spans this sequence of this head (rows past
-// the sequence end are dropped by the hardware range check).
-__device__ __forceinline__ void out8(const Smem8 &s, const FwdParams &p, const __amdgpu_buffer_rsrc_t ro,
+// through a buffer resource over the chunk's rows (rows past the sequence end
+// are dropped by the hardware range check).
+__device__ __forceinline__ void out8(const Smem8 &s, const FwdParams &p, const char *obase, const int seq_len,
                                      const f32x4 (&vp)[4][2], f32x4 (&acc)[4][2], const int c, const int buf,
                                      const int sw, const int ln) {
     const int m = ln & 15, g = ln >> 4;
@@ -1158,12 +1174,13 @@ __device__ __forceinline__ void out8(const Smem8 &s, const FwdParams &p, const _
     }
     const unsigned es = p.o_f32 ? 4u : 2u;
     const unsigned rstride = (unsigned)p.Hv * DV * es;
+    const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(obase, rstride, c, seq_len);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
             const f32x4 w = p.scale * acc[rt][ct];
-            const unsigned off = (unsigned)(c * CH + 16 * rt + m) * rstride + (unsigned)(32 * sw + 16 * ct + 4 * g) * es;
+            const unsigned off = (unsigned)(16 * rt + m) * rstride + (unsigned)(32 * sw + 16 * ct + 4 * g) * es;
             if (p.o_f32) {
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (int)off, 0, 0);
             } else {
@@ -1230,19 +1247,20 @@ __device__ __forceinline__ int seq_chunk_base(const FwdParams &p, int n, int lan
 // One chunk's WY matrix T (s.a, complete) as rows of A: preparation wave pw,
 // thread t = 64 pw + lane stores row t / 4, columns 16 (t % 4) .. +15.  The
 // upper-right 32 x 32 block of s.a is never written by the inverse; its zeros
-// are supplied here.  Rows past the sequence end fall outside the buffer
-// resource and are dropped.
-__device__ __forceinline__ void store_t8(const Smem8 &s, const FwdParams &p, const __amdgpu_buffer_rsrc_t ra,
+// are supplied here.  Rows past the sequence end fall outside the chunk's
+// buffer resource and are dropped.
+__device__ __forceinline__ void store_t8(const Smem8 &s, const FwdParams &p, const char *abase, const int seq_len,
                                          const int c, const int pw, const int lane) {
     const int t = 64 * pw + lane;
     const int row = t >> 2, c0 = 16 * (t & 3);
     const unsigned rstride = (unsigned)p.Hv * CH * 4u;
+    const __amdgpu_buffer_rsrc_t ra = chunk_rsrc(abase, rstride, c, seq_len);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int col = c0 + 4 * i;
         f32x4 x = *reinterpret_cast<const f32x4 *>(&s.a[row * AS + col]);
         if (row < 32 && col >= 32) x = f32x4{};
-        const unsigned off = (unsigned)(c * CH + row) * rstride + (unsigned)col * 4u;
+        const unsigned off = (unsigned)row * rstride + (unsigned)col * 4u;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ra, (int)off, 0, 0);
     }
 }
@@ -1320,11 +1338,12 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
     in.kstride = (unsigned)p.Hqk * DK * 2;
     in.vstride = (unsigned)p.Hv * DV * 2;
     in.gstride = (unsigned)p.Hv * 4;
-    in.k = make_rsrc(p.k + (e.row0 * p.Hqk + i_qk) * DK, (int64_t)e.seq_len * in.kstride);
-    in.q = make_rsrc(p.q + (e.row0 * p.Hqk + i_qk) * DK, (int64_t)e.seq_len * in.kstride);
-    in.v = make_rsrc(p.v + (e.row0 * p.Hv + j) * DV, (int64_t)e.seq_len * in.vstride);
-    in.g = make_rsrc(p.g + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
-    in.b = make_rsrc(p.beta + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
+    in.k = reinterpret_cast<const char *>(p.k + (e.row0 * p.Hqk + i_qk) * DK);
+    in.q = reinterpret_cast<const char *>(p.q + (e.row0 * p.Hqk + i_qk) * DK);
+    in.v = reinterpret_cast<const char *>(p.v + (e.row0 * p.Hv + j) * DV);
+    in.g = reinterpret_cast<const char *>(p.g + e.row0 * p.Hv + j);
+    in.b = reinterpret_cast<const char *>(p.beta + e.row0 * p.Hv + j);
+    in.seq_len = e.seq_len;
 
     // Iteration c runs the state pass of chunk c (state waves) in step with the
     // preparation of chunk c + 1 (preparation waves); c = c_first - 1 only
@@ -1358,8 +1377,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             if (src) load_state8(hacc, src, wave, lane);
         }
         const int64_t oes = p.o_f32 ? 4 : 2;
-        const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes,
-                                                    (int64_t)e.seq_len * p.Hv * DV * oes);
+        const char *obase = static_cast<const char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes;
         f32x4 vp[4][2], qh[4][2];  // vp: U of the next chunk, then v' of this one
         const int cbase = p.h_out ? seq_chunk_base(p, e.n, lane) : 0;
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
@@ -1378,7 +1396,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             };
             if (chain) wh8(s, hacc, vp, lane_now());
             __syncthreads();
-            if (chain && out) out8(s, p, ro, vp, qh, c, b, wave, lane_now());
+            if (chain && out) out8(s, p, obase, e.seq_len, vp, qh, c, b, wave, lane_now());
             __syncthreads();
             if (chain) hupd8(s, hacc, vp, b, lane_now());
             __syncthreads();
@@ -1394,8 +1412,8 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
         if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
     } else {
         const int pw = wave - 4;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a_out ? p.a_out + ((int64_t)e.row0 * p.Hv + j) * CH : nullptr,
-                                                    p.a_out ? (int64_t)e.seq_len * p.Hv * CH * 4 : 0);
+        const char *abase = p.a_out ? reinterpret_cast<const char *>(p.a_out + ((int64_t)e.row0 * p.Hv + j) * CH)
+                                    : nullptr;
         Stage8 st;
         if (has_chunks) load_chunk8(in, st, c_first, c_first >= e.c_begin, threadIdx.x, true);
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
@@ -1420,7 +1438,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             __syncthreads();
             if (prep) inv8_l2b(s, ln, pw, l2);
             __syncthreads();
-            if (prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, ra, c + 1, pw, ln);
+            if (prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, abase, e.seq_len, c + 1, pw, ln);
             if (prep) wfrag8(s, ln, pw, nb);
             __syncthreads();
         }
@@ -1460,11 +1478,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_cp_prepass_kernel(FwdParams p
     in.kstride = (unsigned)p.Hqk * DK * 2;
     in.vstride = (unsigned)p.Hv * DV * 2;
     in.gstride = (unsigned)p.Hv * 4;
-    in.k = make_rsrc(p.k + (e.row0 * p.Hqk + i_qk) * DK, (int64_t)e.seq_len * in.kstride);
+    in.k = reinterpret_cast<const char *>(p.k + (e.row0 * p.Hqk + i_qk) * DK);
     in.q = in.k;  // not read: no output here
-    in.v = make_rsrc(p.v + (e.row0 * p.Hv + j) * DV, (int64_t)e.seq_len * in.vstride);
-    in.g = make_rsrc(p.g + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
-    in.b = make_rsrc(p.beta + e.row0 * p.Hv + j, (int64_t)e.seq_len * in.gstride);
+    in.v = reinterpret_cast<const char *>(p.v + (e.row0 * p.Hv + j) * DV);
+    in.g = reinterpret_cast<const char *>(p.g + e.row0 * p.Hv + j);
+    in.b = reinterpret_cast<const char *>(p.beta + e.row0 * p.Hv + j);
+    in.seq_len = e.seq_len;
 
     Stage st;
     load_chunk(in, st, e.c_begin, false, threadIdx.x);

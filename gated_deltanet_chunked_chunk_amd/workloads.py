@@ -176,3 +176,17 @@ def to_f32_numpy(x):
 
 def reduced(w: Workload, **kw) -> Workload:
     return replace(w, **kw)
+
+
+def device_inputs(B, T, H_qk, H_v, K=128, V=128, seed=0, g_mu=2.0, h0_std=0.1, device="cuda:0") -> dict:
+    """The same recipe drawn directly on the device (timing sweeps over large
+    shapes, where a CPU draw would dominate the run; values differ from
+    make_inputs' CPU draw)."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    q = _unit_bf16(torch.randn(B, T, H_qk, K, generator=gen, device=device))
+    k = _unit_bf16(torch.randn(B, T, H_qk, K, generator=gen, device=device))
+    v = torch.randn(B, T, H_v, V, generator=gen, device=device).to(torch.bfloat16)
+    g = torch.nn.functional.logsigmoid(torch.randn(B, T, H_v, generator=gen, device=device) + g_mu)
+    beta = torch.sigmoid(torch.randn(B, T, H_v, generator=gen, device=device))
+    h0 = None if h0_std is None else torch.randn(B, H_v, K, V, generator=gen, device=device) * h0_std
+    return dict(q=q, k=k, v=v, g=g.float(), beta=beta.float(), initial_state=h0, cu_seqlens=None, scale=K ** -0.5)

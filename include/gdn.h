@@ -31,9 +31,9 @@
  *   - Inputs are read-only.  o must not overlap any input; final_state must
  *     not overlap initial_state or any other tensor.
  *   - q, k, v and o must be 16-byte aligned, g and beta 4-byte aligned.
- *   - One sequence of one head must span less than 2 GiB of its tensor's rows
- *     ((longest sequence + 64) * max(H_qk * K * 2, H_v * V * sizeof(o element))
- *     bytes < 2^31), otherwise GDN_EUNSUPPORTED.
+ *   - One chunk (64 token rows) of every tensor must span less than 2 GiB
+ *     (64 * max(H_qk * K * 2, H_v * V * sizeof(o element), H_v * 64 * 4) bytes
+ *     < 2^31), otherwise GDN_EUNSUPPORTED.  Sequence length is not limited.
  *   - Return value: GDN_OK (0) or a negative gdn_status.  Arguments are fully
  *     validated before anything is enqueued, so a failed call launches
  *     nothing.  gdn_last_error() gives a message for the calling thread's

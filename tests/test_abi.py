@@ -156,3 +156,13 @@ def test_python_api_refuses_cpu_tensors():
     x = W.random_inputs(1, 64, 1, 1)
     with pytest.raises(ValueError):
         G.chunk_gated_delta_rule(x["q"], x["k"], x["v"], x["g"], x["beta"])
+
+
+def test_plan_has_no_sequence_length_limit():
+    """Buffer resources are per chunk: a sequence whose rows span more than
+    2 GiB of a tensor plans fine; only a single chunk must stay below 2 GiB."""
+    assert G.plan(desc(T=1 << 24, H_qk=16, H_v=64))["total_chunks"] == (1 << 24) // 64
+    d = desc(T=128, H_qk=1, H_v=70000)
+    d.o_dtype = L.GDN_DTYPE_F32
+    assert L.lib().gdn_fwd_plan(ctypes.byref(d), None) == L.GDN_EUNSUPPORTED
+    assert b"per-chunk range" in L.lib().gdn_last_error()
