@@ -16,9 +16,9 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
   cpu_baseline the fp64 oracle on a bounded prefix of the same workload, timed
                on this host's cores
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload NAME]
        [--cp auto|warmup|off] [--no-cpu-baseline] [--cpu-seconds 10]
-       python bench.py --sweep [--steps 20] [--warmup 5] [--cp auto]   (head-setting sweep)
+       python bench.py --sweep [--steps 200] [--warmup 100] [--cp auto]   (head-setting sweep)
 """
 import argparse
 import hashlib
@@ -176,8 +176,10 @@ def sweep(steps: int, warmup: int, cp: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # ~100 launches (~30 ms) bring the clocks to their steady state; fewer
+    # time part of the ramp (the first launches run up to 15 % slower)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="gdn_fwd_1x32768_h16x16")
     ap.add_argument("--cp", default="auto")
     ap.add_argument("--o-dtype", default="bf16")
