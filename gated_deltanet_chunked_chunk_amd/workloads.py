@@ -17,6 +17,9 @@ stand in for them:
 * g: logsigmoid(N(mu, 1)) in float32 (log-decay < 0), mu = 2 or 3.
 * beta: sigmoid(N(0,1)) in float32.
 * initial_state: N(0, 0.1^2) float32 [N, H_v, K, V] when the workload has one.
+* backward workload: dO N(0,1) rounded to bfloat16, d(final_state) N(0, 0.01^2)
+  float32 (the second argument of N(0, s) read as a standard deviation, as
+  for the initial state).
 * varlen lengths: log-uniform in [512, 16384], rescaled to the token total.
 
 Every draw comes from ``torch.Generator().manual_seed(seed)`` on the CPU in the
@@ -151,7 +154,7 @@ def make_inputs(w: Workload, device="cpu", T: Optional[int] = None, num_seqs: Op
                cu_seqlens=None if cu is None else torch.from_numpy(cu), scale=w.scale)
     if w.with_grads:
         out["dO"] = torch.randn(B, T, w.H_v, w.V, generator=gen).to(torch.bfloat16)
-        out["dht"] = torch.randn(N, w.H_v, w.K, w.V, generator=gen) * 0.1
+        out["dht"] = torch.randn(N, w.H_v, w.K, w.V, generator=gen) * 0.01
     if device != "cpu":
         for key, val in list(out.items()):
             if isinstance(val, torch.Tensor) and key != "cu_seqlens":

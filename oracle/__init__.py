@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the Gated DeltaNet forward.
+"""fp64 CPU oracle for the Gated DeltaNet forward and backward.
 
 TEST INFRASTRUCTURE ONLY: ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package; the product package
@@ -18,6 +18,16 @@ Functions and what pins them (tests under ``tests/test_oracle_*.py``):
   independence).
 * ``chunk_cumsum``   -- chunk-local running sum of g.  Pinned by constant-g
   closed forms and by numpy's cumsum per chunk.
+* ``chunk_states``, ``chunk_wy_inverse`` -- the low-level forward's h and A
+  by their definitions.  Pinned by beta = 0, a hand-worked two-token example
+  and the WY identity against ``fwd``'s states.
+* ``bwd``            -- reverse-mode derivative of the same per-token loop.
+  Pinned by central finite differences of ``fwd`` in double (directional,
+  and the full Jacobian on tiny shapes), by closed forms (one token with an
+  initial state; beta = 0), and by mutation checks of its C source.
+
+Inputs are widened to float64 before the call (exact for bf16 / float32
+values), so finite differences can perturb them below float32 resolution.
 """
 from __future__ import annotations
 
@@ -56,6 +66,11 @@ def load_library(path: str):
     lib.gdn_oracle_chunk_cumsum.restype = ctypes.c_int
     lib.gdn_oracle_chunk_cumsum.argtypes = [
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P]
+    if hasattr(lib, "gdn_oracle_bwd"):
+        lib.gdn_oracle_bwd.restype = ctypes.c_int
+        lib.gdn_oracle_bwd.argtypes = [
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            P, P, P, P, P, ctypes.c_double, P, P, ctypes.c_int, P, P, P, P, P, P, P, P, ctypes.c_int]
     return lib
 
 
@@ -68,8 +83,8 @@ def _load():
     return _lib
 
 
-def _f32(a):
-    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
 
 
 def _ptr(a):
@@ -90,7 +105,7 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
     [N,Hv,K,V] (K x V = S^T); cu_seqlens int [N+1] (B must be 1).
     Returns (o float64 [B,T,Hv,V], final_state float64 [N,Hv,K,V] or None).
     """
-    q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     B, T, Hqk, K = q.shape
     V = v.shape[-1]
     Hv = v.shape[2]
@@ -102,7 +117,7 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
     else:
         cu = None
         N = B
-    h0 = None if initial_state is None else _f32(initial_state)
+    h0 = None if initial_state is None else _f64(initial_state)
     if h0 is not None and h0.shape != (N, Hv, K, V):
         raise ValueError("oracle.fwd: initial_state must be [N,Hv,K,V]")
     if scale is None:
@@ -117,9 +132,52 @@ def fwd(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None,
     return o, ht
 
 
+def bwd(q, k, v, g, beta, do, dht=None, scale=None, initial_state=None, cu_seqlens=None,
+        n_threads=None, lib=None):
+    """Reference backward: the gradients of <do, o> + <dht, final_state>
+    through ``fwd``'s recurrence (``dht`` None = no gradient into the final
+    state).  Returns float64 (dq [B,T,Hqk,K], dk [B,T,Hqk,K], dv [B,T,Hv,V],
+    dg [B,T,Hv], dbeta [B,T,Hv], dh0 [N,Hv,K,V]); dq and dk sum the
+    contributions of the v-heads that share a key/query head."""
+    q, k, v, g, beta, do = (_f64(x) for x in (q, k, v, g, beta, do))
+    B, T, Hqk, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    if k.shape != q.shape or v.shape[:2] != (B, T) or g.shape != (B, T, Hv) or beta.shape != (B, T, Hv) \
+            or do.shape != v.shape:
+        raise ValueError("oracle.bwd: inconsistent shapes")
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        N = cu.shape[0] - 1
+    else:
+        cu, N = None, B
+    h0 = None if initial_state is None else _f64(initial_state)
+    dht = None if dht is None else _f64(dht)
+    for name, x in (("initial_state", h0), ("dht", dht)):
+        if x is not None and x.shape != (N, Hv, K, V):
+            raise ValueError(f"oracle.bwd: {name} must be [N,Hv,K,V]")
+    if scale is None:
+        scale = K ** -0.5
+    dq_v = np.zeros((B, T, Hv, K))
+    dk_v = np.zeros((B, T, Hv, K))
+    dv = np.zeros((B, T, Hv, V))
+    dg = np.zeros((B, T, Hv))
+    dbeta = np.zeros((B, T, Hv))
+    dh0 = np.zeros((N, Hv, K, V))
+    rc = (lib or _load()).gdn_oracle_bwd(B, T, Hqk, Hv, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         float(scale), _ptr(h0), _ptr(cu), N, _ptr(do), _ptr(dht), _ptr(dq_v),
+                                         _ptr(dk_v), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dh0),
+                                         int(n_threads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle.bwd failed with code {rc}")
+    grp = Hv // Hqk
+    dq = dq_v.reshape(B, T, Hqk, grp, K).sum(axis=3)
+    dk = dk_v.reshape(B, T, Hqk, grp, K).sum(axis=3)
+    return dq, dk, dv, dg, dbeta, dh0
+
+
 def chunk_cumsum(g, chunk=64, cu_seqlens=None, lib=None):
     """Chunk-local running sum of g [B,T,H] (float64 result)."""
-    g = _f32(g)
+    g = _f64(g)
     B, T, H = g.shape
     if cu_seqlens is not None:
         cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
@@ -148,10 +206,10 @@ def chunk_states(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=No
     final state of the token-by-token recurrence (`fwd`) run over that
     sequence's first c * chunk tokens from its initial state.  Chunks of all
     sequences in order.  Returns float64 [total_chunks, Hv, K, V] (S^T)."""
-    q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
+    q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     B, T, Hqk, K = q.shape
     Hv, V = v.shape[2], v.shape[3]
-    h0 = None if initial_state is None else _f32(initial_state)
+    h0 = None if initial_state is None else _f64(initial_state)
     out = []
     for n, (b, t0, L) in enumerate(_seqs(B, T, cu_seqlens)):
         start = np.zeros((Hv, K, V)) if h0 is None else h0[n].astype(np.float64)
@@ -177,7 +235,7 @@ def chunk_wy_inverse(k, g, beta, H_v, cu_seqlens=None, chunk=64):
     of T.  v-head j reads key head j // (H_v / H_qk).  A partial last chunk
     uses its own rows only (its T is the leading block of the padded one).
     Returns float64 [B, T, H_v, chunk]."""
-    k, g, beta = _f32(k), _f32(g), _f32(beta)
+    k, g, beta = _f64(k), _f64(g), _f64(beta)
     B, T, Hqk, K = k.shape
     grp = H_v // Hqk
     out = np.zeros((B, T, H_v, chunk))
