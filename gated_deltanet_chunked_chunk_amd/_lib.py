@@ -8,14 +8,15 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
-ABI_VERSION = 2  # GDN_ABI_VERSION of include/gdn.h this binding matches
+ABI_VERSION = 3  # GDN_ABI_VERSION of include/gdn.h this binding matches
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_DTYPE_BF16, GDN_DTYPE_F32 = 0, 1
 CP_MODES = {"off": 0, "exact": 1, "warmup": 2, "auto": 3}
 CP_NAMES = {v: k for k, v in CP_MODES.items()}
 
 # Every exported entry point of include/gdn.h.
-EXPORTS = ("gdn_abi_version", "gdn_status_str", "gdn_last_error", "gdn_fwd_plan", "gdn_fwd", "gdn_chunk_cumsum")
+EXPORTS = ("gdn_abi_version", "gdn_status_str", "gdn_last_error", "gdn_fwd_plan", "gdn_fwd", "gdn_chunk_cumsum",
+           "gdn_bwd_plan", "gdn_bwd")
 
 
 class FwdDesc(ctypes.Structure):
@@ -52,6 +53,36 @@ class FwdPtrs(ctypes.Structure):
     ]
 
 
+class BwdDesc(ctypes.Structure):
+    _fields_ = [
+        ("fwd", FwdDesc),
+        ("has_dht", ctypes.c_int32), ("grad_dtype", ctypes.c_int32), ("saved_fwd", ctypes.c_int32),
+    ]
+
+
+class BwdPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("workspace_bytes", ctypes.c_size_t),
+        ("total_chunks", ctypes.c_int32), ("segment_chunks", ctypes.c_int32),
+        ("num_segments", ctypes.c_int32), ("warmup_chunks", ctypes.c_int32),
+        ("cp_mode", ctypes.c_int32), ("workgroups_reverse", ctypes.c_int32),
+        ("workgroups_local", ctypes.c_int32),
+    ]
+
+
+class BwdPtrs(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("initial_state", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+        ("dO", ctypes.c_void_p), ("d_final_state", ctypes.c_void_p),
+        ("h", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dg", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
+        ("d_initial_state", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -81,6 +112,11 @@ def lib():
         L.gdn_chunk_cumsum.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.c_void_p]
+        L.gdn_bwd_plan.restype = ctypes.c_int
+        L.gdn_bwd_plan.argtypes = [ctypes.POINTER(BwdDesc), ctypes.POINTER(BwdPlanInfo)]
+        L.gdn_bwd.restype = ctypes.c_int
+        L.gdn_bwd.argtypes = [ctypes.POINTER(BwdDesc), ctypes.POINTER(BwdPtrs), ctypes.c_void_p, ctypes.c_size_t,
+                              ctypes.c_void_p]
         _lib = L
     return _lib
 

@@ -87,7 +87,17 @@ def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
     initial_state: fp32 [N, H_v, K, V] (S^T per head); cu_seqlens: int32 offsets
     [N + 1] (B must be 1).  Returns (o [B, T, H_v, V], final_state or None).
     ``cp`` selects the intra-GPU context parallelism: "auto", "warmup", "exact", "off".
+    Differentiable: when autograd records (an input requires grad), the call
+    keeps the forward's chunk states h and WY matrices A and its backward runs
+    gdn_bwd on them (dq, dk, dv in the inputs' bf16; dg, dbeta, d initial_state fp32).
     """
+    if torch.is_grad_enabled() and any(isinstance(t, torch.Tensor) and t.requires_grad
+                                       for t in (q, k, v, g, beta, initial_state)):
+        if out is not None:
+            raise ValueError("out= cannot be used when autograd records the call")
+        return _GDNFunction.apply(q, k, v, g, beta, initial_state, scale, output_final_state, cu_seqlens,
+                                  dict(cp=cp, o_dtype=o_dtype, cp_lambda=cp_lambda,
+                                       cp_segment_chunks=cp_segment_chunks, cp_warmup_chunks=cp_warmup_chunks))
     o, ht, _, _ = _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens, cp=cp,
                            o_dtype=o_dtype, cp_lambda=cp_lambda, cp_segment_chunks=cp_segment_chunks,
                            cp_warmup_chunks=cp_warmup_chunks, out=out, workspace=workspace)
@@ -170,6 +180,116 @@ def _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seql
         L.check(L.lib().gdn_fwd(ctypes.byref(desc), ctypes.byref(ptrs), ctypes.c_void_p(workspace.data_ptr()),
                                 workspace.numel(), ctypes.c_void_p(stream)))
     return out, ht, h, A
+
+
+def bwd_plan(desc: L.BwdDesc) -> dict:
+    """Host-only planning of the backward (no GPU needed)."""
+    info = L.BwdPlanInfo()
+    L.check(L.lib().gdn_bwd_plan(ctypes.byref(desc), ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in L.BwdPlanInfo._fields_} | {"cp": L.CP_NAMES[info.cp_mode]}
+
+
+def make_bwd_desc(fwd_desc: L.FwdDesc, *, has_dht=False, grad_dtype="bf16", saved_fwd=False) -> L.BwdDesc:
+    d = L.BwdDesc()
+    d.fwd = fwd_desc
+    d.has_dht = int(bool(has_dht))
+    d.grad_dtype = {"bf16": L.GDN_DTYPE_BF16, "f32": L.GDN_DTYPE_F32}[grad_dtype]
+    d.saved_fwd = int(bool(saved_fwd))
+    return d
+
+
+def chunk_gated_delta_rule_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                               beta: torch.Tensor, do: torch.Tensor, scale: Optional[float] = None,
+                               initial_state: Optional[torch.Tensor] = None, cu_seqlens=None,
+                               d_final_state: Optional[torch.Tensor] = None, h: Optional[torch.Tensor] = None,
+                               A: Optional[torch.Tensor] = None, *, cp: str = "auto", grad_dtype: str = "bf16",
+                               cp_lambda: float = 0.0, cp_segment_chunks: int = 0, cp_warmup_chunks: int = 0,
+                               workspace: Optional[torch.Tensor] = None):
+    """Chunked backward of ``chunk_gated_delta_rule``: the gradients of a loss
+    with upstream dO (bf16 [B, T, H_v, V]) and optionally d final_state (fp32
+    [N, H_v, K, V]).  ``h`` and ``A`` are the low-level forward's chunk states
+    and WY matrices (``chunk_gated_delta_rule_fwd`` with the same arguments and
+    CP settings); without them the backward recomputes both.  Returns
+    (dq, dk, dv, dg, dbeta, d_initial_state or None); dq, dk, dv in
+    ``grad_dtype`` ("bf16" or "f32"), the rest fp32."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("the backward runs on GPU tensors; there is no CPU path")
+    for t, name, dt in ((q, "q", torch.bfloat16), (k, "k", torch.bfloat16), (v, "v", torch.bfloat16),
+                        (g, "g", torch.float32), (beta, "beta", torch.float32), (do, "dO", torch.bfloat16)):
+        _need(t, name, dt, dev)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2] or do.shape != v.shape:
+        raise ValueError(f"bad shapes q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)} dO {tuple(do.shape)}")
+    B, T, Hqk, K = q.shape
+    Hv, V = v.shape[2], v.shape[3]
+    if g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise ValueError(f"g and beta must be [B, T, H_v] = {(B, T, Hv)}")
+    cu_host = _cu_host(cu_seqlens)
+    cu_dev = None
+    if cu_host is not None:
+        cu_dev = cu_seqlens if (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.device == dev
+                                and cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()) \
+            else cu_host.to(dev)
+    N = (cu_host.numel() - 1) if cu_host is not None else B
+    for t, name in ((initial_state, "initial_state"), (d_final_state, "d_final_state")):
+        if t is not None:
+            _need(t, name, torch.float32, dev)
+            if t.shape != (N, Hv, K, V):
+                raise ValueError(f"{name} must be [N, H_v, K, V] = {(N, Hv, K, V)}")
+    if (h is None) != (A is None):
+        raise ValueError("h and A must be given together")
+    if scale is None:
+        scale = K ** -0.5
+    fd = make_desc(B, T, Hqk, Hv, K, V, scale=scale, cu_host=cu_host, has_h0=initial_state is not None,
+                   cp=cp, cp_lambda=cp_lambda, cp_segment_chunks=cp_segment_chunks,
+                   cp_warmup_chunks=cp_warmup_chunks)
+    desc = make_bwd_desc(fd, has_dht=d_final_state is not None, grad_dtype=grad_dtype, saved_fwd=h is not None)
+    info = bwd_plan(desc)
+    if h is not None:
+        _need(h, "h", torch.float32, dev)
+        _need(A, "A", torch.float32, dev)
+        if h.shape != (info["total_chunks"], Hv, K, V) or A.shape != (B, T, Hv, 64):
+            raise ValueError("h / A do not match the forward's low-level output shapes")
+    gt = torch.float32 if grad_dtype == "f32" else torch.bfloat16
+    dq = torch.empty(B, T, Hqk, K, dtype=gt, device=dev)
+    dk = torch.empty(B, T, Hqk, K, dtype=gt, device=dev)
+    dv = torch.empty(B, T, Hv, V, dtype=gt, device=dev)
+    dg = torch.empty(B, T, Hv, dtype=torch.float32, device=dev)
+    dbeta = torch.empty(B, T, Hv, dtype=torch.float32, device=dev)
+    dh0 = torch.empty(N, Hv, K, V, dtype=torch.float32, device=dev) if initial_state is not None else None
+    if workspace is None or workspace.numel() < info["workspace_bytes"] or workspace.data_ptr() % 256:
+        workspace = _workspace(info["workspace_bytes"], dev)
+    opt = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    ptrs = L.BwdPtrs(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), opt(initial_state),
+                     opt(cu_dev), do.data_ptr(), opt(d_final_state), opt(h), opt(A), dq.data_ptr(), dk.data_ptr(),
+                     dv.data_ptr(), dg.data_ptr(), dbeta.data_ptr(), opt(dh0))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        L.check(L.lib().gdn_bwd(ctypes.byref(desc), ctypes.byref(ptrs), ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel(), ctypes.c_void_p(stream)))
+    return dq, dk, dv, dg, dbeta, dh0
+
+
+class _GDNFunction(torch.autograd.Function):
+    """Autograd node: the forward keeps h and A (the low-level outputs), the
+    backward hands them to gdn_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, g, beta, initial_state, scale, output_final_state, cu_seqlens, kw):
+        o, ht, h, A = _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                               want_h=True, want_a=True, **kw)
+        ctx.save_for_backward(q, k, v, g, beta, initial_state, h, A)
+        ctx.scale, ctx.cu_seqlens, ctx.kw = scale, cu_seqlens, kw
+        return o, ht
+
+    @staticmethod
+    def backward(ctx, do, dht):
+        q, k, v, g, beta, initial_state, h, A = ctx.saved_tensors
+        kw = {n: ctx.kw[n] for n in ("cp", "cp_lambda", "cp_segment_chunks", "cp_warmup_chunks")}
+        dq, dk, dv, dg, dbeta, dh0 = chunk_gated_delta_rule_bwd(
+            q, k, v, g, beta, do.to(torch.bfloat16).contiguous(), ctx.scale, initial_state, ctx.cu_seqlens,
+            None if dht is None else dht.float().contiguous(), h, A, **kw)
+        return dq, dk, dv, dg, dbeta, dh0, None, None, None, None
 
 
 class PreparedForward:

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = [os.path.join(CSRC, "gdn_api.hip"), os.path.join(CSRC, "gdn_fwd.hip")]
+SOURCES = [os.path.join(CSRC, "gdn_api.hip"), os.path.join(CSRC, "gdn_fwd.hip"), os.path.join(CSRC, "gdn_bwd.hip")]
 HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(CSRC, "gdn_internal.h")]
 
 HIPCC_FLAGS = [

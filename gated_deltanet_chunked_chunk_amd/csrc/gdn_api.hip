@@ -163,6 +163,105 @@ int make_plan(const gdn_fwd_desc *d, Plan *P) {
     return GDN_OK;
 }
 
+// Shape and plan fields of the forward's kernel parameters (pointers are the caller's).
+gdn::FwdParams fwd_params(const gdn_fwd_desc *d, const Plan &P) {
+    gdn::FwdParams fp{};
+    fp.T = d->T;
+    fp.rows = P.rows;
+    fp.B = (int32_t)d->B;
+    fp.N = d->num_seqs;
+    fp.Hqk = d->H_qk;
+    fp.Hv = d->H_v;
+    fp.group = d->H_v / d->H_qk;
+    fp.num_segments = P.num_segments;
+    fp.L = P.L;
+    fp.cp_mode = P.cp_mode;
+    fp.warmup_cap = P.warmup;
+    fp.o_f32 = d->o_dtype == GDN_DTYPE_F32;
+    fp.scale = d->scale;
+    return fp;
+}
+
+// ---- backward planning: the reverse pass runs one workgroup per (segment,
+// v-head, half of V); AUTO picks L for that grid the same way as the forward.
+struct BwdPlan {
+    Plan fwd;                 // the differentiated forward (validation, recompute)
+    int32_t L = 1, num_segments = 0, cp_mode = GDN_CP_OFF, warmup = 0;
+    int32_t entries = 0;      // chunk-local grid entries (chunks + one per empty sequence)
+    size_t off_o = 0, off_h = 0, off_a = 0;  // forward recompute (saved_fwd == 0 only)
+    size_t off_dh = 0, off_dvp = 0, off_dq = 0, off_dk = 0;
+    size_t workspace = 0;
+};
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+int make_bwd_plan(const gdn_bwd_desc *bd, BwdPlan *B) {
+    if (!bd) return fail(GDN_EINVAL, "descriptor is NULL");
+    const gdn_fwd_desc *d = &bd->fwd;
+    int rc = make_plan(d, &B->fwd);
+    if (rc != GDN_OK) return rc;
+    if (bd->grad_dtype != GDN_DTYPE_BF16 && bd->grad_dtype != GDN_DTYPE_F32)
+        return fail(GDN_EINVAL, "unknown grad_dtype %d", bd->grad_dtype);
+    if (d->cp_mode == GDN_CP_EXACT)
+        return fail(GDN_EUNSUPPORTED, "exact context parallelism is not built for the backward (use warmup, auto or off)");
+    const Plan &P = B->fwd;
+    int32_t L = std::max(1, P.max_chunks);
+    int32_t mode = d->cp_mode;
+    int32_t warmup = d->cp_warmup_chunks > 0 ? d->cp_warmup_chunks : gdn::kDefaultWarmup;
+    if (mode != GDN_CP_OFF) {
+        if (d->cp_segment_chunks > 0) {
+            L = d->cp_segment_chunks;
+        } else if (d->cp_lambda > 0.f) {
+            L = (int32_t)std::lround(d->cp_lambda * std::sqrt((double)P.max_chunks));
+        } else {
+            static const int32_t cands[] = {8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256};
+            double best = std::ceil(2.0 * d->H_v * count_segments(d, L) / gdn::kNumCUs) * L;
+            for (int32_t c : cands) {
+                if (c >= P.max_chunks) break;
+                const double cost = std::ceil(2.0 * d->H_v * count_segments(d, c) / gdn::kNumCUs) * (c + 2);
+                if (cost < best) {
+                    best = cost;
+                    L = c;
+                }
+            }
+        }
+        L = std::max(1, std::min(L, std::max(1, P.max_chunks)));
+        mode = GDN_CP_WARMUP;
+        if (L >= P.max_chunks) mode = GDN_CP_OFF;
+    }
+    if (mode == GDN_CP_OFF) warmup = 0;
+    B->L = L;
+    B->cp_mode = mode;
+    B->warmup = warmup;
+    B->num_segments = count_segments(d, L);
+    B->entries = count_segments(d, 1);
+    if ((int64_t)B->num_segments * d->H_v * 2 > INT32_MAX || (int64_t)B->entries * d->H_v > INT32_MAX)
+        return fail(GDN_EINVAL, "grid too large");
+
+    const size_t rows = (size_t)P.rows;
+    const size_t n_h = (size_t)P.total_chunks * d->H_v * d->K * d->V;
+    size_t off = 0;
+    if (!bd->saved_fwd) {
+        const size_t osz = d->o_dtype == GDN_DTYPE_F32 ? 4 : 2;
+        B->off_o = off;
+        off = align_up(off + rows * d->H_v * d->V * osz);
+        B->off_h = off;
+        off = align_up(off + n_h * 4);
+        B->off_a = off;
+        off = align_up(off + rows * d->H_v * gdn::kChunk * 4);
+    }
+    B->off_dh = off;
+    off = align_up(off + n_h * 4);
+    B->off_dvp = off;
+    off = align_up(off + (size_t)P.total_chunks * d->H_v * gdn::kChunk * d->V * 4);
+    B->off_dq = off;
+    off = align_up(off + rows * d->H_v * d->K * 4);
+    B->off_dk = off;
+    off = align_up(off + rows * d->H_v * d->K * 4);
+    B->workspace = off;
+    return GDN_OK;
+}
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     if (!a || !b || na == 0 || nb == 0) return false;
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
@@ -253,7 +352,7 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
     if (P.workspace > 0 && ((uintptr_t)workspace & (kAlign - 1)))
         return fail(GDN_EWORKSPACE, "workspace must be 256-byte aligned");
 
-    gdn::FwdParams fp{};
+    gdn::FwdParams fp = fwd_params(d, P);
     fp.q = (const uint16_t *)p->q;
     fp.k = (const uint16_t *)p->k;
     fp.v = (const uint16_t *)p->v;
@@ -263,19 +362,6 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
     fp.cu = p->cu_seqlens;
     fp.o = p->o;
     fp.ht = p->final_state;
-    fp.T = d->T;
-    fp.rows = P.rows;
-    fp.B = (int32_t)d->B;
-    fp.N = d->num_seqs;
-    fp.Hqk = d->H_qk;
-    fp.Hv = d->H_v;
-    fp.group = d->H_v / d->H_qk;
-    fp.num_segments = P.num_segments;
-    fp.L = P.L;
-    fp.cp_mode = P.cp_mode;
-    fp.warmup_cap = P.warmup;
-    fp.o_f32 = d->o_dtype == GDN_DTYPE_F32;
-    fp.scale = d->scale;
     fp.h_out = p->h;
     fp.a_out = p->A;
     if (P.cp_mode == GDN_CP_EXACT) {
@@ -294,6 +380,145 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
     }
     const int err = gdn::launch_fwd_main(fp, stream);
     if (err) return fail(GDN_EHIP, "forward launch failed: %s", gdn::hip_error_text(err));
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+int gdn_bwd_plan(const gdn_bwd_desc *d, gdn_bwd_plan_info *out) {
+    BwdPlan B;
+    const int rc = make_bwd_plan(d, &B);
+    if (rc != GDN_OK) return rc;
+    if (out) {
+        out->workspace_bytes = B.workspace;
+        out->total_chunks = B.fwd.total_chunks;
+        out->segment_chunks = B.L;
+        out->num_segments = B.num_segments;
+        out->warmup_chunks = B.cp_mode == GDN_CP_WARMUP ? B.warmup : 0;
+        out->cp_mode = B.cp_mode;
+        out->workgroups_reverse = B.num_segments * d->fwd.H_v * 2;
+        out->workgroups_local = B.entries * d->fwd.H_v;
+    }
+    g_last_error.clear();
+    return GDN_OK;
+}
+
+int gdn_bwd(const gdn_bwd_desc *bd, const gdn_bwd_ptrs *p, void *workspace, size_t workspace_bytes, void *stream) {
+    BwdPlan B;
+    int rc = make_bwd_plan(bd, &B);
+    if (rc != GDN_OK) return rc;
+    if (!p) return fail(GDN_EINVAL, "pointer struct is NULL");
+    const gdn_fwd_desc *d = &bd->fwd;
+    const Plan &P = B.fwd;
+    const bool varlen = d->cu_seqlens_host != nullptr;
+    if (varlen != (p->cu_seqlens != nullptr))
+        return fail(GDN_EINVAL, "device cu_seqlens and host cu_seqlens_host must be given together");
+    if ((d->has_h0 != 0) != (p->initial_state != nullptr))
+        return fail(GDN_EINVAL, "initial_state pointer must be given iff has_h0");
+    if ((bd->has_dht != 0) != (p->d_final_state != nullptr))
+        return fail(GDN_EINVAL, "d_final_state pointer must be given iff has_dht");
+    if ((bd->saved_fwd != 0) != (p->h != nullptr) || (p->h != nullptr) != (p->A != nullptr))
+        return fail(GDN_EINVAL, "h and A must both be given iff saved_fwd");
+
+    const size_t rows = (size_t)P.rows;
+    const size_t n_qk = rows * d->H_qk * d->K, n_v = rows * d->H_v * d->V, n_g = rows * d->H_v;
+    const size_t n_state = (size_t)d->num_seqs * d->H_v * d->K * d->V;
+    const size_t n_h = (size_t)P.total_chunks * d->H_v * d->K * d->V, n_a = rows * d->H_v * gdn::kChunk;
+    const size_t gsz = bd->grad_dtype == GDN_DTYPE_F32 ? 4 : 2;
+    if (rows > 0) {
+        if (!p->q || !p->k || !p->v || !p->g || !p->beta || !p->dO || !p->dq || !p->dk || !p->dv || !p->dg ||
+            !p->dbeta)
+            return fail(GDN_EINVAL, "q, k, v, g, beta, dO, dq, dk, dv, dg and dbeta must be non-NULL");
+        if (((uintptr_t)p->q | (uintptr_t)p->k | (uintptr_t)p->v | (uintptr_t)p->dO | (uintptr_t)p->dq |
+             (uintptr_t)p->dk | (uintptr_t)p->dv) & 15)
+            return fail(GDN_EINVAL, "q, k, v, dO, dq, dk and dv must be 16-byte aligned");
+        if (((uintptr_t)p->g | (uintptr_t)p->beta | (uintptr_t)p->dg | (uintptr_t)p->dbeta) & 3)
+            return fail(GDN_EINVAL, "g, beta, dg and dbeta must be 4-byte aligned");
+    }
+    if (((uintptr_t)p->h | (uintptr_t)p->A | (uintptr_t)p->initial_state | (uintptr_t)p->d_final_state |
+         (uintptr_t)p->d_initial_state) & 15)
+        return fail(GDN_EINVAL, "h, A and the state tensors must be 16-byte aligned");
+    struct Buf { const void *ptr; size_t bytes; const char *name; };
+    const Buf in[] = {{p->q, n_qk * 2, "q"}, {p->k, n_qk * 2, "k"}, {p->v, n_v * 2, "v"},
+                      {p->g, n_g * 4, "g"}, {p->beta, n_g * 4, "beta"},
+                      {p->initial_state, n_state * 4, "initial_state"},
+                      {p->cu_seqlens, varlen ? (size_t)(d->num_seqs + 1) * 4 : 0, "cu_seqlens"},
+                      {p->dO, n_v * 2, "dO"}, {p->d_final_state, n_state * 4, "d_final_state"},
+                      {p->h, p->h ? n_h * 4 : 0, "h"}, {p->A, p->A ? n_a * 4 : 0, "A"},
+                      {workspace, B.workspace, "workspace"}};
+    const Buf outs[] = {{p->dq, n_qk * gsz, "dq"}, {p->dk, n_qk * gsz, "dk"}, {p->dv, n_v * gsz, "dv"},
+                        {p->dg, n_g * 4, "dg"}, {p->dbeta, n_g * 4, "dbeta"},
+                        {p->d_initial_state, n_state * 4, "d_initial_state"}};
+    for (const Buf &ob : outs) {
+        for (const Buf &b : in)
+            if (overlaps(ob.ptr, ob.bytes, b.ptr, b.bytes)) return fail(GDN_EINVAL, "%s overlaps %s", ob.name, b.name);
+        for (const Buf &b : outs)
+            if (&b != &ob && overlaps(ob.ptr, ob.bytes, b.ptr, b.bytes))
+                return fail(GDN_EINVAL, "%s overlaps %s", ob.name, b.name);
+    }
+    if ((B.workspace > 0 && !workspace) || workspace_bytes < B.workspace)
+        return fail(GDN_EWORKSPACE, "workspace needs %zu bytes (got %zu at %p)", B.workspace, workspace_bytes,
+                    workspace);
+    if (B.workspace > 0 && ((uintptr_t)workspace & (kAlign - 1)))
+        return fail(GDN_EWORKSPACE, "workspace must be 256-byte aligned");
+    char *ws = static_cast<char *>(workspace);
+
+    const float *h = p->h, *A = p->A;
+    if (!bd->saved_fwd && P.num_segments > 0 && rows > 0) {
+        // recompute the forward's chunk-start states and WY matrices
+        gdn::FwdParams fp = fwd_params(d, P);
+        fp.q = (const uint16_t *)p->q;
+        fp.k = (const uint16_t *)p->k;
+        fp.v = (const uint16_t *)p->v;
+        fp.g = p->g;
+        fp.beta = p->beta;
+        fp.h0 = p->initial_state;
+        fp.cu = p->cu_seqlens;
+        fp.o = ws + B.off_o;
+        fp.ht = nullptr;
+        fp.h_out = reinterpret_cast<float *>(ws + B.off_h);
+        fp.a_out = reinterpret_cast<float *>(ws + B.off_a);
+        const int err = gdn::launch_fwd_main(fp, stream);
+        if (err) return fail(GDN_EHIP, "forward recompute launch failed: %s", gdn::hip_error_text(err));
+        h = fp.h_out;
+        A = fp.a_out;
+    }
+
+    gdn::BwdParams bp{};
+    bp.q = (const uint16_t *)p->q;
+    bp.k = (const uint16_t *)p->k;
+    bp.v = (const uint16_t *)p->v;
+    bp.dO = (const uint16_t *)p->dO;
+    bp.g = p->g;
+    bp.beta = p->beta;
+    bp.cu = p->cu_seqlens;
+    bp.h = h;
+    bp.A = A;
+    bp.dht = p->d_final_state;
+    bp.dh_ws = reinterpret_cast<float *>(ws + B.off_dh);
+    bp.dvp_ws = reinterpret_cast<float *>(ws + B.off_dvp);
+    bp.dq_ws = reinterpret_cast<float *>(ws + B.off_dq);
+    bp.dk_ws = reinterpret_cast<float *>(ws + B.off_dk);
+    bp.dq = p->dq;
+    bp.dk = p->dk;
+    bp.dv = p->dv;
+    bp.dg = p->dg;
+    bp.dbeta = p->dbeta;
+    bp.dh0 = p->d_initial_state;
+    bp.T = d->T;
+    bp.rows = P.rows;
+    bp.N = d->num_seqs;
+    bp.Hqk = d->H_qk;
+    bp.Hv = d->H_v;
+    bp.group = d->H_v / d->H_qk;
+    bp.num_segments = B.num_segments;
+    bp.L = B.L;
+    bp.cp_mode = B.cp_mode;
+    bp.warmup_cap = B.warmup;
+    bp.num_chunk_entries = B.entries;
+    bp.grad_f32 = bd->grad_dtype == GDN_DTYPE_F32;
+    bp.scale = d->scale;
+    const int err = gdn::launch_bwd(bp, stream);
+    if (err) return fail(GDN_EHIP, "backward launch failed: %s", gdn::hip_error_text(err));
     g_last_error.clear();
     return GDN_OK;
 }

@@ -60,11 +60,35 @@ struct FwdParams {
     float *h_out, *a_out;
 };
 
-// Launchers (gdn_fwd.hip).  Each returns the hipError_t of its launch as int.
+// Backward (gdn_bwd.hip): reverse pass over segments, then chunk-local gradients,
+// then the key-head sums of dq and dk.
+struct BwdParams {
+    const uint16_t *q, *k, *v, *dO;  // bf16 bits
+    const float *g, *beta;
+    const int32_t *cu;               // device offsets or nullptr
+    const float *h;                  // [total_chunks][Hv][K][V] chunk-start states (forward's low-level h)
+    const float *A;                  // [rows][Hv][64] WY matrices (forward's low-level A)
+    const float *dht;                // [N][Hv][K][V] or nullptr
+    float *dh_ws;                    // [total_chunks][Hv][K][V] gradient wrt the state after each chunk
+    float *dvp_ws;                   // [total_chunks][Hv][64][V] dv' (all 64 rows of every chunk)
+    float *dq_ws, *dk_ws;            // [rows][Hv][K] per-v-head dq, dk
+    void *dq, *dk, *dv;              // bf16 or fp32 per grad_f32
+    float *dg, *dbeta;               // [rows][Hv]
+    float *dh0;                      // [N][Hv][K][V] or nullptr
+    int64_t T, rows;
+    int32_t N, Hqk, Hv, group;
+    int32_t num_segments, L, cp_mode, warmup_cap;  // reverse pass
+    int32_t num_chunk_entries;       // chunk-local grid: chunks of all sequences + one per empty sequence
+    int32_t grad_f32;
+    float scale;
+};
+
+// Launchers (gdn_fwd.hip, gdn_bwd.hip).  Each returns the hipError_t of its launch as int.
 int launch_fwd_main(const FwdParams &p, void *stream);
 int launch_cp_exact(const FwdParams &p, void *stream);  // pre-pass + combine
 int launch_chunk_cumsum(const float *g, float *out, int64_t B, int64_t T, int32_t H, int32_t chunk,
                         const int32_t *cu, int32_t N, void *stream);
+int launch_bwd(const BwdParams &p, void *stream);
 const char *hip_error_text(int err);
 
 }  // namespace gdn

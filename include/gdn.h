@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum {
     GDN_OK = 0,
@@ -160,6 +160,69 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
  * NULL (then num_seqs must equal B).  out may equal g (in place). */
 int gdn_chunk_cumsum(const float *g, float *out, int64_t B, int64_t T, int32_t H, int32_t chunk,
                      const int32_t *cu_seqlens, int32_t num_seqs, void *stream);
+
+/* ------------------------------------------------------------------ backward
+ *
+ * The chunked backward the pages announce (agentlenshq.com blog, title and
+ * "performance benchmarks"; aisparkup.com wiki, "key features": a fused
+ * backward alongside the forward): the gradients of a scalar loss with
+ * respect to q, k, v, g, beta and initial_state, given dO = dL/do and
+ * optionally dL/d final_state.  The result is the exact derivative of the
+ * forward above, evaluated chunk by chunk: a reverse pass over the chunks
+ * (the adjoint of the state pass) followed by independent per-chunk
+ * gradients.  Gradients flow through every input; dq and dk of a key/query
+ * head sum the contributions of the value heads that share it; dg is the
+ * gradient with respect to the per-token log-gates (not their cumsum).
+ *
+ * Context parallelism of the reverse pass: OFF, or WARMUP / AUTO with the
+ * forward's window rule applied after each segment (the state gradient decays
+ * with the same gates); EXACT is not built for the backward (GDN_EUNSUPPORTED).
+ */
+typedef struct {
+    gdn_fwd_desc fwd;     /* the forward call being differentiated (want_ht and o_dtype are ignored) */
+    int32_t has_dht;      /* d_final_state given */
+    int32_t grad_dtype;   /* gdn_dtype of dq, dk, dv (dg, dbeta, d_initial_state are fp32) */
+    int32_t saved_fwd;    /* 1: the caller passes h and A from gdn_fwd under the same fwd descriptor;
+                             0: the backward recomputes them in its workspace */
+} gdn_bwd_desc;
+
+typedef struct {
+    size_t workspace_bytes;     /* bytes gdn_bwd needs at `workspace` (256-byte aligned) */
+    int32_t total_chunks;
+    int32_t segment_chunks;     /* L of the reverse pass */
+    int32_t num_segments;       /* reverse-pass segments over all sequences (per v-head) */
+    int32_t warmup_chunks;      /* window cap of the reverse pass, 0 when CP is off */
+    int32_t cp_mode;            /* resolved mode of the reverse pass (OFF or WARMUP) */
+    int32_t workgroups_reverse; /* reverse-pass workgroups = num_segments * H_v * 2 */
+    int32_t workgroups_local;   /* per-chunk workgroups = (total_chunks + empty sequences) * H_v */
+} gdn_bwd_plan_info;
+
+typedef struct {
+    const void *q, *k, *v;          /* bf16, as for gdn_fwd */
+    const float *g, *beta;          /* fp32 */
+    const float *initial_state;     /* fp32, NULL iff fwd.has_h0 == 0 */
+    const int32_t *cu_seqlens;      /* device offsets, NULL iff not varlen */
+    const void *dO;                 /* bf16 [B, T, H_v, V] */
+    const float *d_final_state;     /* fp32 [N, H_v, K, V], NULL iff has_dht == 0 */
+    const float *h;                 /* saved_fwd: gdn_fwd's h (fp32 [total_chunks, H_v, K, V]), else NULL */
+    const float *A;                 /* saved_fwd: gdn_fwd's A (fp32 [B * T, H_v, chunk]), else NULL */
+    void *dq, *dk;                  /* [B, T, H_qk, K], grad_dtype */
+    void *dv;                       /* [B, T, H_v, V], grad_dtype */
+    float *dg, *dbeta;              /* fp32 [B, T, H_v] */
+    float *d_initial_state;         /* fp32 [N, H_v, K, V], or NULL (not written) */
+} gdn_bwd_ptrs;
+
+/* Host-only planning of the backward: validates (as gdn_fwd_plan, plus the
+ * backward's own fields), resolves the reverse pass's CP layout and sizes the
+ * workspace.  No HIP call.  `out` may be NULL. */
+int gdn_bwd_plan(const gdn_bwd_desc *d, gdn_bwd_plan_info *out);
+
+/* Backward pass.  Same conventions as gdn_fwd: caller-owned buffers, inputs
+ * read-only, outputs must not overlap inputs or each other, full validation
+ * before anything is enqueued, asynchronous on `stream`.  dq, dk, dv, dO
+ * 16-byte aligned; g, beta, dg, dbeta 4-byte aligned; state tensors, h and A
+ * 16-byte aligned.  Every element of dq, dk, dv, dg and dbeta is written. */
+int gdn_bwd(const gdn_bwd_desc *d, const gdn_bwd_ptrs *p, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

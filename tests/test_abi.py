@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = L.lib()
-    assert lib.gdn_abi_version() == L.ABI_VERSION == 2
+    assert lib.gdn_abi_version() == L.ABI_VERSION == 3
     for st in (0, -1, -2, -3, -4):
         assert lib.gdn_status_str(st)
     assert b"unknown" in lib.gdn_status_str(42)
@@ -166,3 +166,69 @@ def test_plan_has_no_sequence_length_limit():
     d.o_dtype = L.GDN_DTYPE_F32
     assert L.lib().gdn_fwd_plan(ctypes.byref(d), None) == L.GDN_EUNSUPPORTED
     assert b"per-chunk range" in L.lib().gdn_last_error()
+
+
+def bdesc(**kw):
+    extra = {k: kw.pop(k) for k in ("has_dht", "grad_dtype", "saved_fwd") if k in kw}
+    return G.make_bwd_desc(desc(**kw), **extra)
+
+
+def test_bwd_plan_layout_and_workspace():
+    # backward workload shape: 1 x 32768 tokens, 4 key heads, 16 value heads
+    p = G.bwd_plan(bdesc(T=32768, H_qk=4, H_v=16, has_h0=True, has_dht=True))
+    assert p["total_chunks"] == 512 and p["cp"] == "warmup"
+    assert p["workgroups_reverse"] == p["num_segments"] * 16 * 2
+    assert p["workgroups_local"] == 512 * 16
+    rows, hv, K = 32768, 16, 128
+    n_h = 512 * hv * K * K * 4
+    dvp = 512 * hv * 64 * K * 4
+    dqk = 2 * rows * hv * K * 4
+    recompute = rows * hv * K * 2 + n_h + rows * hv * 64 * 4
+    assert p["workspace_bytes"] == n_h + dvp + dqk + recompute
+    saved = G.bwd_plan(bdesc(T=32768, H_qk=4, H_v=16, saved_fwd=True))
+    assert saved["workspace_bytes"] == n_h + dvp + dqk
+    off = G.bwd_plan(bdesc(T=32768, H_qk=4, H_v=16, cp="off"))
+    assert off["cp"] == "off" and off["num_segments"] == 1 and off["warmup_chunks"] == 0
+
+
+def test_bwd_plan_rejects():
+    for kw, st in ((dict(cp="exact"), L.GDN_EUNSUPPORTED), (dict(K=64), L.GDN_EUNSUPPORTED),
+                   (dict(H_v=3), L.GDN_EINVAL)):
+        d = bdesc(**kw)
+        assert L.lib().gdn_bwd_plan(ctypes.byref(d), None) == st
+        assert L.lib().gdn_last_error()
+    d = bdesc()
+    d.grad_dtype = 7
+    assert L.lib().gdn_bwd_plan(ctypes.byref(d), None) == L.GDN_EINVAL
+
+
+def test_bwd_plan_varlen_entries():
+    cu = torch.tensor([0, 100, 100, 300], dtype=torch.int32)
+    p = G.bwd_plan(bdesc(T=300, H_qk=1, H_v=2, cu_host=cu, cp="off"))
+    assert p["total_chunks"] == 2 + 0 + 4
+    assert p["workgroups_local"] == (6 + 1) * 2  # one entry for the empty sequence
+
+
+def test_bwd_validation_happens_before_any_launch():
+    lib = L.lib()
+    base = 0x100000
+    d = bdesc(T=128, has_h0=True, has_dht=True)
+    ws = ctypes.create_string_buffer(1 << 12)
+    mk = lambda **o: L.BwdPtrs(**{**dict(q=base, k=2 * base, v=3 * base, g=4 * base, beta=5 * base,  # noqa: E731
+                                         initial_state=6 * base, cu_seqlens=None, dO=7 * base,
+                                         d_final_state=8 * base, h=None, A=None, dq=9 * base, dk=10 * base,
+                                         dv=11 * base, dg=12 * base, dbeta=13 * base,
+                                         d_initial_state=14 * base), **o})
+    # d_final_state given without has_dht
+    d2 = bdesc(T=128, has_h0=True)
+    assert lib.gdn_bwd(ctypes.byref(d2), ctypes.byref(mk()), ws, 1 << 12, None) == L.GDN_EINVAL
+    # h without A
+    d3 = bdesc(T=128, has_h0=True, has_dht=True, saved_fwd=True)
+    assert lib.gdn_bwd(ctypes.byref(d3), ctypes.byref(mk(h=15 * base)), ws, 1 << 12, None) == L.GDN_EINVAL
+    # misaligned dO
+    assert lib.gdn_bwd(ctypes.byref(d), ctypes.byref(mk(dO=7 * base + 2)), ws, 1 << 12, None) == L.GDN_EINVAL
+    # dv overlapping v
+    assert lib.gdn_bwd(ctypes.byref(d), ctypes.byref(mk(dv=3 * base + 256)), ws, 1 << 12, None) == L.GDN_EINVAL
+    assert b"dv overlaps v" in lib.gdn_last_error()
+    # workspace too small
+    assert lib.gdn_bwd(ctypes.byref(d), ctypes.byref(mk()), ws, 1 << 12, None) == L.GDN_EWORKSPACE

@@ -1,0 +1,147 @@
+"""GPU parity of the chunked backward (gdn_bwd) against the oracle's
+reverse-mode recurrence (oracle.bwd, pinned by finite differences):
+relative L2 <= 5e-3 on each of dq, dk, dv, dg, dbeta and d initial_state,
+the gradient bar of the method's target, with fp32 gradients; bf16
+gradients are held to the same bar.  Cases span several chunks with ragged
+tails, grouped heads, varlen batches with empty and one-token sequences,
+CP off and warm-up segments, the saved-tensor and recompute paths, the
+autograd node, and sampled heads of the full backward workload."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_deltanet_chunked_chunk_amd import (chunk_gated_delta_rule, chunk_gated_delta_rule_bwd,
+                                              chunk_gated_delta_rule_fwd)
+from gated_deltanet_chunked_chunk_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BAR = 5e-3
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def _grad_inputs(w, **kw):
+    """The backward workload's recipe (dO and d final_state included) at another shape."""
+    assert w.with_grads
+    return W.make_inputs(w, device=DEV, **kw)
+
+
+def _oracle(x, with_dht=True):
+    f = W.to_f32_numpy
+    cu = None if x["cu_seqlens"] is None else x["cu_seqlens"].numpy()
+    return oracle.bwd(f(x["q"]), f(x["k"]), f(x["v"]), f(x["g"]), f(x["beta"]), f(x["dO"]),
+                      f(x["dht"]) if with_dht else None, scale=x["scale"], initial_state=f(x["initial_state"]),
+                      cu_seqlens=cu)
+
+
+def _check(name, got, ref, bar=BAR):
+    errs = {}
+    for n, a, b in zip(NAMES, got, ref):
+        if a is None:
+            continue
+        a = a.float().cpu().numpy()
+        assert a.shape == b.shape, (n, a.shape, b.shape)
+        assert np.isfinite(a).all(), n
+        errs[n] = rel_l2(a, b)
+    print(f"[{name}] " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= bar, (name, n, e)
+
+
+def _run(x, **kw):
+    out = chunk_gated_delta_rule_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["dO"], scale=x["scale"],
+                                     initial_state=x["initial_state"], cu_seqlens=x["cu_seqlens"],
+                                     d_final_state=x["dht"], **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+BASE = W.WORKLOADS["gdn_fwdbwd_1x32768_h4x16"]
+
+
+@pytest.mark.parametrize("cp", ["off", "warmup"])
+def test_bwd_ragged_batch(cp):
+    w = dataclasses.replace(BASE, name="b1", seed=41, B=2, T=200, H_qk=1, H_v=2)
+    x = _grad_inputs(w)
+    got = _run(x, cp=cp, cp_segment_chunks=1, grad_dtype="f32")
+    _check(f"ragged/{cp}", got, _oracle(x))
+
+
+def test_bwd_grouped_heads_several_chunks():
+    w = dataclasses.replace(BASE, name="b2", seed=42, B=1, T=1000, H_qk=2, H_v=8)
+    x = _grad_inputs(w)
+    got = _run(x, cp="warmup", cp_segment_chunks=4, grad_dtype="f32")
+    _check("grouped/warmup", got, _oracle(x))
+
+
+def test_bwd_varlen_with_empty_and_one_token_sequences():
+    w = dataclasses.replace(BASE, name="b3", seed=43, B=1, T=0, H_qk=2, H_v=4)
+    x = _grad_inputs(w, lengths=[130, 0, 1, 64, 300])
+    got = _run(x, cp="warmup", cp_segment_chunks=2, grad_dtype="f32")
+    _check("varlen/warmup", got, _oracle(x))
+    got = _run(x, cp="off", grad_dtype="f32")
+    _check("varlen/off", got, _oracle(x))
+
+
+def test_bwd_no_state_gradients_and_bf16_grads():
+    w = dataclasses.replace(BASE, name="b4", seed=44, B=1, T=333, H_qk=1, H_v=2, h0_std=None)
+    x = _grad_inputs(w)
+    x["dht"] = None
+    got = chunk_gated_delta_rule_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["dO"], scale=x["scale"],
+                                     cp="off")
+    torch.cuda.synchronize()
+    assert got[0].dtype == torch.bfloat16 and got[2].dtype == torch.bfloat16 and got[5] is None
+    _check("no-state/bf16", got, _oracle(x, with_dht=False))
+
+
+def test_bwd_saved_tensors_match_recompute():
+    w = dataclasses.replace(BASE, name="b5", seed=45, B=1, T=640, H_qk=1, H_v=4)
+    x = _grad_inputs(w)
+    _, A, _, h, _ = chunk_gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
+                                               initial_state=x["initial_state"], cp="warmup", cp_segment_chunks=3)
+    saved = _run(x, h=h, A=A, cp="warmup", cp_segment_chunks=3, grad_dtype="f32")
+    fresh = _run(x, cp="warmup", cp_segment_chunks=3, grad_dtype="f32")
+    for n, a, b in zip(NAMES, saved, fresh):
+        assert torch.equal(a, b), n
+    _check("saved", saved, _oracle(x))
+
+
+def test_autograd_node_matches_backward_call():
+    w = dataclasses.replace(BASE, name="b6", seed=46, B=1, T=260, H_qk=1, H_v=2)
+    x = _grad_inputs(w)
+    leaves = [x[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta", "initial_state")]
+    o, ht = chunk_gated_delta_rule(*leaves[:5], scale=x["scale"], initial_state=leaves[5], output_final_state=True,
+                                   cp="off")
+    grads = torch.autograd.grad((o, ht), leaves, (x["dO"], x["dht"]))
+    direct = _run(x, cp="off")
+    for n, a, b in zip(NAMES, grads, direct):
+        assert torch.equal(a, b), n
+
+
+def test_bwd_full_workload_sampled_key_head():
+    """The backward workload (1 x 32768 tokens, 4 key heads, 16 value heads,
+    initial state, d final_state) in the benchmark's launch configuration
+    (CP auto, bf16 gradients as autograd returns them, h and A saved by the
+    forward); the oracle checks key head 2 and its four value heads."""
+    x = W.make_inputs(BASE, device=DEV)
+    _, A, _, h, _ = chunk_gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
+                                               initial_state=x["initial_state"])
+    got = _run(x, h=h, A=A)
+    i = 2
+    sl = slice(4 * i, 4 * i + 4)
+    xs = dict(q=x["q"][:, :, i:i + 1], k=x["k"][:, :, i:i + 1], v=x["v"][:, :, sl], g=x["g"][:, :, sl],
+              beta=x["beta"][:, :, sl], dO=x["dO"][:, :, sl], dht=x["dht"][:, sl],
+              initial_state=x["initial_state"][:, sl], cu_seqlens=None, scale=x["scale"])
+    ref = _oracle(xs)
+    sub = (got[0][:, :, i:i + 1], got[1][:, :, i:i + 1], got[2][:, :, sl], got[3][:, :, sl], got[4][:, :, sl],
+           got[5][:, sl])
+    _check("full/sampled", sub, ref)
