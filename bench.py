@@ -118,11 +118,12 @@ def cpu_baseline(x, w, target_s: float):
             "sample": f"first {T} of {w.T} tokens, all {w.H_v} v-heads, fp64 per-token recurrence, {dt:.1f} s"}
 
 
-# The pages' model family at its tensor-parallel shares (blog, benchmark table;
-# wiki, benchmarks: head settings h in {64, 48, 32, 24, 16, 8} over TP1..TP8):
-# per-GPU (H_qk, H_v) and the model / TP they stand for.
-SWEEP_HEADS = [((2, 8), "397B/122B TP8"), ((4, 16), "397B/122B TP4"), ((8, 32), "397B/122B TP2"),
-               ((16, 64), "397B/122B TP1"), ((8, 24), "27B TP2"), ((16, 48), "27B TP1"), ((16, 16), "2B/0.8B TP1")]
+# The pages' head settings at their tensor-parallel shares (blog, benchmark
+# table; wiki, benchmarks: h in {64, 48, 32, 24, 16, 8} over TP1..TP8): per-GPU
+# (H_qk, H_v) and the full layer's heads / TP degree they stand for.
+SWEEP_HEADS = [((2, 8), "16/64 heads, TP8"), ((4, 16), "16/64 heads, TP4"), ((8, 32), "16/64 heads, TP2"),
+               ((16, 64), "16/64 heads, TP1"), ((8, 24), "16/48 heads, TP2"), ((16, 48), "16/48 heads, TP1"),
+               ((16, 16), "16/16 heads, TP1")]
 SWEEP_SHAPES = [(1, 8192), (1, 32768), (4, 32768), (1, 131072)]
 # pages' H200 FlashQLA forward latency at 1 x 32768 (blog, benchmark table): context only
 PAGES_H200_MS = {(2, 8): 0.310, (4, 16): 0.486, (8, 24): 0.659, (16, 16): 0.493}
@@ -164,7 +165,7 @@ def sweep(steps: int, warmup: int, cp: str):
             rows.append(line)
             del call, x
             torch.cuda.empty_cache()
-    print("| model / TP | H_qk | H_v | B x T | CP (L, workgroups) | ms | M tokens/s | HBM roofline | pages H200 ms |",
+    print("| layer heads / TP | H_qk | H_v | B x T | CP (L, workgroups) | ms | M tokens/s | HBM roofline | pages H200 ms |",
           file=sys.stderr)
     print("|---|---|---|---|---|---|---|---|---|", file=sys.stderr)
     for r in rows:

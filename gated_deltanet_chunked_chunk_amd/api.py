@@ -352,3 +352,61 @@ def chunk_cumsum(g: torch.Tensor, chunk: int = 64, cu_seqlens=None, out: Optiona
 
 __all__: Sequence[str] = ("chunk_gated_delta_rule", "chunk_gated_delta_rule_fwd", "chunk_cumsum", "plan", "make_desc",
                           "PreparedForward")
+
+
+class PreparedForwardBackward:
+    """A training step on fixed shapes with every buffer allocated once: the
+    forward (o, final_state, and the low-level h and A it keeps for the
+    backward) then the backward (dq, dk, dv, dg, dbeta, d initial_state) from
+    upstream dO and d final_state.  ``forward()`` and ``backward()`` only
+    enqueue gdn_fwd / gdn_bwd on the current stream."""
+
+    def __init__(self, q, k, v, g, beta, do, scale=None, initial_state=None, d_final_state=None, cu_seqlens=None,
+                 *, cp="auto", grad_dtype="bf16", **kw):
+        dev = q.device
+        self.device = dev
+        _, A, o, h, ht = chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=scale, initial_state=initial_state,
+                                                    cu_seqlens=cu_seqlens, output_final_state=True, cp=cp, **kw)
+        self.o, self.final_state, self.h, self.A = o, ht, h, A
+        self.grads = chunk_gated_delta_rule_bwd(q, k, v, g, beta, do, scale=scale, initial_state=initial_state,
+                                                cu_seqlens=cu_seqlens, d_final_state=d_final_state, h=h, A=A, cp=cp,
+                                                grad_dtype=grad_dtype, **kw)
+        cu_host = _cu_host(cu_seqlens)
+        B, T, Hqk, K = q.shape
+        Hv, V = v.shape[2], v.shape[3]
+        sc = scale if scale is not None else K ** -0.5
+        self.fdesc = make_desc(B, T, Hqk, Hv, K, V, scale=sc, cu_host=cu_host, has_h0=initial_state is not None,
+                               want_ht=True, cp=cp, **kw)
+        self.bdesc = make_bwd_desc(make_desc(B, T, Hqk, Hv, K, V, scale=sc, cu_host=cu_host,
+                                             has_h0=initial_state is not None, cp=cp, **kw),
+                                   has_dht=d_final_state is not None, grad_dtype=grad_dtype, saved_fwd=True)
+        self.finfo, self.binfo = plan(self.fdesc), bwd_plan(self.bdesc)
+        self.fws = _workspace(self.finfo["workspace_bytes"], dev)
+        self.bws = _workspace(self.binfo["workspace_bytes"], dev)
+        self.cu_dev = None if cu_host is None else cu_host.to(dev)
+        self._keep = (q, k, v, g, beta, do, initial_state, d_final_state, cu_host)
+        opt = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        self.fptrs = L.FwdPtrs(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                               opt(initial_state), opt(self.cu_dev), o.data_ptr(), ht.data_ptr(), h.data_ptr(),
+                               A.data_ptr())
+        dq, dk, dv, dg, db, dh0 = self.grads
+        self.bptrs = L.BwdPtrs(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+                               opt(initial_state), opt(self.cu_dev), do.data_ptr(), opt(d_final_state), h.data_ptr(),
+                               A.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(),
+                               db.data_ptr(), opt(dh0))
+
+    def forward(self):
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        L.check(L.lib().gdn_fwd(ctypes.byref(self.fdesc), ctypes.byref(self.fptrs),
+                                ctypes.c_void_p(self.fws.data_ptr()), self.fws.numel(), ctypes.c_void_p(stream)))
+
+    def backward(self):
+        stream = torch.cuda.current_stream(self.device).cuda_stream
+        L.check(L.lib().gdn_bwd(ctypes.byref(self.bdesc), ctypes.byref(self.bptrs),
+                                ctypes.c_void_p(self.bws.data_ptr()), self.bws.numel(), ctypes.c_void_p(stream)))
+
+    def __call__(self):
+        self.forward()
+        self.backward()
+        return self.grads
+
