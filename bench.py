@@ -19,6 +19,8 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload NAME]
        [--cp auto|warmup|off] [--no-cpu-baseline] [--cpu-seconds 10]
        python bench.py --sweep [--steps 200] [--warmup 100] [--cp auto]   (head-setting sweep)
+       python bench.py --workload gdn_fwdbwd_1x32768_h4x16   (training step: forward keeping h and A,
+              then the backward; roofline of the backward against the bf16 MFMA peak)
 """
 import argparse
 import hashlib
@@ -54,6 +56,33 @@ def algorithmic_bytes(x) -> int:
     if x["initial_state"] is not None:
         n += x["initial_state"].numel() * 4 * 2  # h0 read + final_state write
     return int(n)
+
+
+def bwd_algorithmic(x) -> tuple:
+    """Backward bytes and flops at minimum.  Bytes: read q, k, v, dO (bf16), g,
+    beta (fp32), initial_state and d final_state (fp32) once; write dq, dk, dv
+    (bf16), dg, dbeta, d initial_state (fp32) once.  Flops: every distinct
+    product of the chunked backward once per (chunk, v-head), counted as 2 m n k
+    (reverse pass: P^T dO, K dh', Q~^T dO, W^T dv'; chunk-local: W, Q K^T,
+    T diag(beta) V, W h, dO v'^T, dPm K, dO h^T, dPm^T Q, v' dh'^T, dv' h^T,
+    dW K^T, dv' V^T, T^T dW, T^T dv', T^T dT, (T^T dT) T^T, K K^T, M K, M^T K),
+    no hi/lo split terms; the forward's h and A are inputs, not recomputed."""
+    q, v, g = x["q"], x["v"], x["g"]
+    n = q.numel() * 2 * 2 * 2 + v.numel() * 2 * 3 + g.numel() * 4 * 4  # q, k, dq, dk; v, dO, dv; g, beta, dg, dbeta
+    if x["initial_state"] is not None:
+        n += x["initial_state"].numel() * 4 * 2
+    if x.get("dht") is not None:
+        n += x["dht"].numel() * 4
+    B, T, Hv, V = v.shape
+    K = q.shape[-1]
+    C = 64
+    chunk_heads = B * (-(-T // C)) * Hv
+    mm = lambda m, nn, k: 2 * m * nn * k  # noqa: E731
+    reverse = mm(C, V, C) + mm(C, V, K) + mm(K, V, C) + mm(K, V, C)
+    local = (mm(C, K, C) + mm(C, C, K) + mm(C, V, C) + mm(C, V, K) + mm(C, C, V) + mm(C, K, C) + mm(C, K, V)
+             + mm(C, K, C) + mm(C, K, V) + mm(C, K, V) + mm(C, C, K) + mm(C, C, V) + mm(C, K, C) + mm(C, V, C)
+             + mm(C, C, C) + mm(C, C, C) + mm(C, C, K) + mm(C, K, C) + mm(C, K, C))
+    return int(n), int(chunk_heads * (reverse + local))
 
 
 def stored_traffic(workload: str):
@@ -174,6 +203,81 @@ def sweep(steps: int, warmup: int, cp: str):
               f"{r['pages_h200_ms'] if r['pages_h200_ms'] else ''} |", file=sys.stderr)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def cpu_baseline_bwd(x, w, target_s: float):
+    """The oracle's forward + reverse-mode backward on a prefix of the workload."""
+    import oracle
+    from gated_deltanet_chunked_chunk_amd import workloads as W
+    threads = min(16, oracle.default_threads())
+    host = {k: W.to_f32_numpy(x[k]) for k in ("q", "k", "v", "g", "beta", "initial_state", "dO", "dht")}
+
+    def run(T):
+        t0 = time.perf_counter()
+        args = [host[n][:, :T] for n in ("q", "k", "v", "g", "beta")]
+        oracle.fwd(*args, scale=x["scale"], initial_state=host["initial_state"], n_threads=threads)
+        oracle.bwd(*args, host["dO"][:, :T], host["dht"], scale=x["scale"], initial_state=host["initial_state"],
+                   n_threads=threads)
+        return time.perf_counter() - t0
+
+    t_cal = run(256)
+    T = int(min(w.T, max(256, 256 * target_s / max(t_cal, 1e-6))))
+    T = max(256, T // 64 * 64)
+    dt = run(T)
+    return {"value": T * w.B / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {T} of {w.T} tokens, all {w.H_v} v-heads, fp64 per-token forward + reverse-mode "
+                      f"backward, {dt:.1f} s"}
+
+
+def fwd_bwd(args, w, x, dev):
+    """One step = the forward keeping h and A, then the backward on them."""
+    import torch
+    from gated_deltanet_chunked_chunk_amd import PreparedForwardBackward
+    call = PreparedForwardBackward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["dO"], scale=x["scale"],
+                                   initial_state=x["initial_state"], d_final_state=x["dht"], cp=args.cp)
+    tokens = w.B * w.T
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b, c in ev:
+        a.record(stream)
+        call.forward()
+        b.record(stream)
+        call.backward()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / len(ev)
+    bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / len(ev)
+    ms_per_step = wall * 1e3 / args.steps
+    value = tokens / (ms_per_step * 1e-3)
+    bwd_bytes, bwd_flops = bwd_algorithmic(x)
+    achieved = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "gdn_bwd (reverse pass + chunk-local gradients + key-head sums)",
+                "algorithmic_flops_per_launch": bwd_flops, "algorithmic_bytes_per_launch": bwd_bytes,
+                "mean_launch_ms": round(bwd_ms, 4), "forward_mean_launch_ms": round(fwd_ms, 4)}
+    cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(x, w, args.cpu_seconds)
+    line = {
+        "metric": "GDN fwd+bwd latency (ms) & tokens/s at 1x32768, 4/16 heads; % of MFMA roofline (backward)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded random q,k,v,g,beta,initial_state,dO,d_final_state)",
+        "config": {"workload": args.workload, "B": w.B, "T": w.T, "H_qk": w.H_qk, "H_v": w.H_v, "K": w.K,
+                   "V": w.V, "cp": call.finfo["cp"], "bwd_cp": call.binfo["cp"],
+                   "bwd_segment_chunks": call.binfo["segment_chunks"], "grad_dtype": "bf16"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +327,9 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     x = W.make_inputs(w, device=dev)
+    if w.with_grads:
+        fwd_bwd(args, w, x, dev)
+        return
     call = PreparedForward(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
                            initial_state=x["initial_state"], output_final_state=w.want_ht,
                            cu_seqlens=x["cu_seqlens"], cp=args.cp, o_dtype=args.o_dtype)

@@ -8,7 +8,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
-ABI_VERSION = 3  # GDN_ABI_VERSION of include/gdn.h this binding matches
+ABI_VERSION = 4  # GDN_ABI_VERSION of include/gdn.h this binding matches
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EWORKSPACE, GDN_EHIP = 0, -1, -2, -3, -4
 GDN_DTYPE_BF16, GDN_DTYPE_F32 = 0, 1
 CP_MODES = {"off": 0, "exact": 1, "warmup": 2, "auto": 3}
@@ -49,7 +49,7 @@ class FwdPtrs(ctypes.Structure):
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
         ("initial_state", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
         ("o", ctypes.c_void_p), ("final_state", ctypes.c_void_p),
-        ("h", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("h", ctypes.c_void_p), ("A", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
     ]
 
 
@@ -76,7 +76,7 @@ class BwdPtrs(ctypes.Structure):
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
         ("initial_state", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
         ("dO", ctypes.c_void_p), ("d_final_state", ctypes.c_void_p),
-        ("h", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("h", ctypes.c_void_p), ("A", ctypes.c_void_p), ("v_new", ctypes.c_void_p),
         ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
         ("dg", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
         ("d_initial_state", ctypes.c_void_p),

@@ -98,7 +98,7 @@ def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
         return _GDNFunction.apply(q, k, v, g, beta, initial_state, scale, output_final_state, cu_seqlens,
                                   dict(cp=cp, o_dtype=o_dtype, cp_lambda=cp_lambda,
                                        cp_segment_chunks=cp_segment_chunks, cp_warmup_chunks=cp_warmup_chunks))
-    o, ht, _, _ = _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens, cp=cp,
+    o, ht, _, _, _ = _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens, cp=cp,
                            o_dtype=o_dtype, cp_lambda=cp_lambda, cp_segment_chunks=cp_segment_chunks,
                            cp_warmup_chunks=cp_warmup_chunks, out=out, workspace=workspace)
     return o, ht
@@ -107,7 +107,7 @@ def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
 def chunk_gated_delta_rule_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                                beta: torch.Tensor, scale: Optional[float] = None,
                                initial_state: Optional[torch.Tensor] = None, cu_seqlens=None,
-                               output_final_state: bool = True, **kw):
+                               output_final_state: bool = True, output_v_new: bool = False, **kw):
     """The pages' low-level forward (aisparkup.com FlashQLA wiki, "low-level
     API"): returns (g, A, o, h, final_state) with
       g  fp32 [B, T, H_v]: the chunk-local running sum of the gates;
@@ -116,17 +116,22 @@ def chunk_gated_delta_rule_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
       o  [B, T, H_v, V] (bf16 unless o_dtype="f32");
       h  fp32 [total_chunks, H_v, K, V]: S^T at the start of every chunk;
       final_state fp32 [N, H_v, K, V] or None.
+    With output_v_new, a sixth element: v_new fp32 [total_chunks, H_v, 64, V],
+    every chunk's v' = U - W h (what the backward consumes with h and A).
     Everything except g comes from one gdn_fwd call; g from gdn_chunk_cumsum."""
-    o, ht, h, A = _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
-                           want_h=True, want_a=True, **kw)
+    o, ht, h, A, vn = _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                               want_h=True, want_a=True, want_vn=output_v_new, **kw)
     g_cum = chunk_cumsum(g, 64, cu_seqlens)
+    if output_v_new:
+        return g_cum, A, o, h, ht, vn
     return g_cum, A, o, h, ht
 
 
 def _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens, *, cp: str = "auto",
              o_dtype: Optional[str] = None, cp_lambda: float = 0.0, cp_segment_chunks: int = 0,
              cp_warmup_chunks: int = 0, out: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None, want_h: bool = False, want_a: bool = False):
+             workspace: Optional[torch.Tensor] = None, want_h: bool = False, want_a: bool = False,
+             want_vn: bool = False):
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("the forward runs on GPU tensors; there is no CPU path")
@@ -168,18 +173,20 @@ def _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seql
     ht = torch.empty(N, Hv, K, V, dtype=torch.float32, device=dev) if output_final_state else None
     h = torch.empty(info["total_chunks"], Hv, K, V, dtype=torch.float32, device=dev) if want_h else None
     A = torch.empty(B, T, Hv, 64, dtype=torch.float32, device=dev) if want_a else None
+    vn = torch.empty(info["total_chunks"], Hv, 64, V, dtype=torch.float32, device=dev) if want_vn else None
     if workspace is None or workspace.numel() < info["workspace_bytes"] or workspace.data_ptr() % 256:
         workspace = _workspace(info["workspace_bytes"], dev)
     ptrs = L.FwdPtrs(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                      initial_state.data_ptr() if initial_state is not None else None,
                      cu_dev.data_ptr() if cu_dev is not None else None,
                      out.data_ptr(), ht.data_ptr() if ht is not None else None,
-                     h.data_ptr() if h is not None else None, A.data_ptr() if A is not None else None)
+                     h.data_ptr() if h is not None else None, A.data_ptr() if A is not None else None,
+                     vn.data_ptr() if vn is not None else None)
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         L.check(L.lib().gdn_fwd(ctypes.byref(desc), ctypes.byref(ptrs), ctypes.c_void_p(workspace.data_ptr()),
                                 workspace.numel(), ctypes.c_void_p(stream)))
-    return out, ht, h, A
+    return out, ht, h, A, vn
 
 
 def bwd_plan(desc: L.BwdDesc) -> dict:
@@ -202,14 +209,16 @@ def chunk_gated_delta_rule_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
                                beta: torch.Tensor, do: torch.Tensor, scale: Optional[float] = None,
                                initial_state: Optional[torch.Tensor] = None, cu_seqlens=None,
                                d_final_state: Optional[torch.Tensor] = None, h: Optional[torch.Tensor] = None,
-                               A: Optional[torch.Tensor] = None, *, cp: str = "auto", grad_dtype: str = "bf16",
+                               A: Optional[torch.Tensor] = None, v_new: Optional[torch.Tensor] = None, *,
+                               cp: str = "auto", grad_dtype: str = "bf16",
                                cp_lambda: float = 0.0, cp_segment_chunks: int = 0, cp_warmup_chunks: int = 0,
                                workspace: Optional[torch.Tensor] = None):
     """Chunked backward of ``chunk_gated_delta_rule``: the gradients of a loss
     with upstream dO (bf16 [B, T, H_v, V]) and optionally d final_state (fp32
-    [N, H_v, K, V]).  ``h`` and ``A`` are the low-level forward's chunk states
-    and WY matrices (``chunk_gated_delta_rule_fwd`` with the same arguments and
-    CP settings); without them the backward recomputes both.  Returns
+    [N, H_v, K, V]).  ``h``, ``A`` and ``v_new`` are the low-level forward's
+    chunk states, WY matrices and residuals (``chunk_gated_delta_rule_fwd`` with
+    the same arguments and CP settings, ``output_v_new=True``); without them
+    the backward recomputes all three.  Returns
     (dq, dk, dv, dg, dbeta, d_initial_state or None); dq, dk, dv in
     ``grad_dtype`` ("bf16" or "f32"), the rest fp32."""
     dev = q.device
@@ -236,8 +245,8 @@ def chunk_gated_delta_rule_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
             _need(t, name, torch.float32, dev)
             if t.shape != (N, Hv, K, V):
                 raise ValueError(f"{name} must be [N, H_v, K, V] = {(N, Hv, K, V)}")
-    if (h is None) != (A is None):
-        raise ValueError("h and A must be given together")
+    if not ((h is None) == (A is None) == (v_new is None)):
+        raise ValueError("h, A and v_new must be given together")
     if scale is None:
         scale = K ** -0.5
     fd = make_desc(B, T, Hqk, Hv, K, V, scale=scale, cu_host=cu_host, has_h0=initial_state is not None,
@@ -248,8 +257,10 @@ def chunk_gated_delta_rule_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
     if h is not None:
         _need(h, "h", torch.float32, dev)
         _need(A, "A", torch.float32, dev)
-        if h.shape != (info["total_chunks"], Hv, K, V) or A.shape != (B, T, Hv, 64):
-            raise ValueError("h / A do not match the forward's low-level output shapes")
+        _need(v_new, "v_new", torch.float32, dev)
+        if h.shape != (info["total_chunks"], Hv, K, V) or A.shape != (B, T, Hv, 64) \
+                or v_new.shape != (info["total_chunks"], Hv, 64, V):
+            raise ValueError("h / A / v_new do not match the forward's low-level output shapes")
     gt = torch.float32 if grad_dtype == "f32" else torch.bfloat16
     dq = torch.empty(B, T, Hqk, K, dtype=gt, device=dev)
     dk = torch.empty(B, T, Hqk, K, dtype=gt, device=dev)
@@ -261,8 +272,8 @@ def chunk_gated_delta_rule_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor
         workspace = _workspace(info["workspace_bytes"], dev)
     opt = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
     ptrs = L.BwdPtrs(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), opt(initial_state),
-                     opt(cu_dev), do.data_ptr(), opt(d_final_state), opt(h), opt(A), dq.data_ptr(), dk.data_ptr(),
-                     dv.data_ptr(), dg.data_ptr(), dbeta.data_ptr(), opt(dh0))
+                     opt(cu_dev), do.data_ptr(), opt(d_final_state), opt(h), opt(A), opt(v_new), dq.data_ptr(),
+                     dk.data_ptr(), dv.data_ptr(), dg.data_ptr(), dbeta.data_ptr(), opt(dh0))
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
         L.check(L.lib().gdn_bwd(ctypes.byref(desc), ctypes.byref(ptrs), ctypes.c_void_p(workspace.data_ptr()),
@@ -276,19 +287,19 @@ class _GDNFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, g, beta, initial_state, scale, output_final_state, cu_seqlens, kw):
-        o, ht, h, A = _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
-                               want_h=True, want_a=True, **kw)
-        ctx.save_for_backward(q, k, v, g, beta, initial_state, h, A)
+        o, ht, h, A, vn = _forward(q, k, v, g, beta, scale, initial_state, output_final_state, cu_seqlens,
+                                   want_h=True, want_a=True, want_vn=True, **kw)
+        ctx.save_for_backward(q, k, v, g, beta, initial_state, h, A, vn)
         ctx.scale, ctx.cu_seqlens, ctx.kw = scale, cu_seqlens, kw
         return o, ht
 
     @staticmethod
     def backward(ctx, do, dht):
-        q, k, v, g, beta, initial_state, h, A = ctx.saved_tensors
+        q, k, v, g, beta, initial_state, h, A, vn = ctx.saved_tensors
         kw = {n: ctx.kw[n] for n in ("cp", "cp_lambda", "cp_segment_chunks", "cp_warmup_chunks")}
         dq, dk, dv, dg, dbeta, dh0 = chunk_gated_delta_rule_bwd(
             q, k, v, g, beta, do.to(torch.bfloat16).contiguous(), ctx.scale, initial_state, ctx.cu_seqlens,
-            None if dht is None else dht.float().contiguous(), h, A, **kw)
+            None if dht is None else dht.float().contiguous(), h, A, vn, **kw)
         return dq, dk, dv, dg, dbeta, dh0, None, None, None, None
 
 
@@ -365,12 +376,13 @@ class PreparedForwardBackward:
                  *, cp="auto", grad_dtype="bf16", **kw):
         dev = q.device
         self.device = dev
-        _, A, o, h, ht = chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=scale, initial_state=initial_state,
-                                                    cu_seqlens=cu_seqlens, output_final_state=True, cp=cp, **kw)
-        self.o, self.final_state, self.h, self.A = o, ht, h, A
+        _, A, o, h, ht, vn = chunk_gated_delta_rule_fwd(q, k, v, g, beta, scale=scale, initial_state=initial_state,
+                                                        cu_seqlens=cu_seqlens, output_final_state=True,
+                                                        output_v_new=True, cp=cp, **kw)
+        self.o, self.final_state, self.h, self.A, self.v_new = o, ht, h, A, vn
         self.grads = chunk_gated_delta_rule_bwd(q, k, v, g, beta, do, scale=scale, initial_state=initial_state,
-                                                cu_seqlens=cu_seqlens, d_final_state=d_final_state, h=h, A=A, cp=cp,
-                                                grad_dtype=grad_dtype, **kw)
+                                                cu_seqlens=cu_seqlens, d_final_state=d_final_state, h=h, A=A,
+                                                v_new=vn, cp=cp, grad_dtype=grad_dtype, **kw)
         cu_host = _cu_host(cu_seqlens)
         B, T, Hqk, K = q.shape
         Hv, V = v.shape[2], v.shape[3]
@@ -388,12 +400,12 @@ class PreparedForwardBackward:
         opt = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
         self.fptrs = L.FwdPtrs(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                                opt(initial_state), opt(self.cu_dev), o.data_ptr(), ht.data_ptr(), h.data_ptr(),
-                               A.data_ptr())
+                               A.data_ptr(), vn.data_ptr())
         dq, dk, dv, dg, db, dh0 = self.grads
         self.bptrs = L.BwdPtrs(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
                                opt(initial_state), opt(self.cu_dev), do.data_ptr(), opt(d_final_state), h.data_ptr(),
-                               A.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dg.data_ptr(),
-                               db.data_ptr(), opt(dh0))
+                               A.data_ptr(), vn.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               dg.data_ptr(), db.data_ptr(), opt(dh0))
 
     def forward(self):
         stream = torch.cuda.current_stream(self.device).cuda_stream

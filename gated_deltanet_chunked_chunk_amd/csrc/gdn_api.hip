@@ -188,7 +188,7 @@ struct BwdPlan {
     Plan fwd;                 // the differentiated forward (validation, recompute)
     int32_t L = 1, num_segments = 0, cp_mode = GDN_CP_OFF, warmup = 0;
     int32_t entries = 0;      // chunk-local grid entries (chunks + one per empty sequence)
-    size_t off_o = 0, off_h = 0, off_a = 0;  // forward recompute (saved_fwd == 0 only)
+    size_t off_o = 0, off_h = 0, off_a = 0, off_vn = 0;  // forward recompute (saved_fwd == 0 only)
     size_t off_dh = 0, off_dvp = 0, off_dq = 0, off_dk = 0;
     size_t workspace = 0;
 };
@@ -249,6 +249,8 @@ int make_bwd_plan(const gdn_bwd_desc *bd, BwdPlan *B) {
         off = align_up(off + n_h * 4);
         B->off_a = off;
         off = align_up(off + rows * d->H_v * gdn::kChunk * 4);
+        B->off_vn = off;
+        off = align_up(off + (size_t)P.total_chunks * d->H_v * gdn::kChunk * d->V * 4);
     }
     B->off_dh = off;
     off = align_up(off + n_h * 4);
@@ -330,15 +332,18 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
         if ((uintptr_t)p->o & 15) return fail(GDN_EINVAL, "o must be 16-byte aligned");
     }
     const size_t n_h = (size_t)P.total_chunks * d->H_v * d->K * d->V, n_a = rows * d->H_v * gdn::kChunk;
-    if (((uintptr_t)p->h | (uintptr_t)p->A) & 15) return fail(GDN_EINVAL, "h and A must be 16-byte aligned");
+    if (((uintptr_t)p->h | (uintptr_t)p->A | (uintptr_t)p->v_new) & 15)
+        return fail(GDN_EINVAL, "h, A and v_new must be 16-byte aligned");
     struct Buf { const void *ptr; size_t bytes; const char *name; };
     const Buf in[] = {{p->q, n_qk * 2, "q"}, {p->k, n_qk * 2, "k"}, {p->v, n_v * 2, "v"},
                       {p->g, n_g * 4, "g"}, {p->beta, n_g * 4, "beta"},
                       {p->initial_state, n_state * 4, "initial_state"},
                       {p->cu_seqlens, varlen ? (size_t)(d->num_seqs + 1) * 4 : 0, "cu_seqlens"},
                       {workspace, P.workspace, "workspace"}};
+    const size_t n_vn = (size_t)P.total_chunks * d->H_v * gdn::kChunk * d->V;
     const Buf outs[] = {{p->o, n_v * osz, "o"}, {p->final_state, n_state * 4, "final_state"},
-                        {p->h, p->h ? n_h * 4 : 0, "h"}, {p->A, p->A ? n_a * 4 : 0, "A"}};
+                        {p->h, p->h ? n_h * 4 : 0, "h"}, {p->A, p->A ? n_a * 4 : 0, "A"},
+                        {p->v_new, p->v_new ? n_vn * 4 : 0, "v_new"}};
     for (const Buf &ob : outs) {
         for (const Buf &b : in)
             if (overlaps(ob.ptr, ob.bytes, b.ptr, b.bytes)) return fail(GDN_EINVAL, "%s overlaps %s", ob.name, b.name);
@@ -364,6 +369,7 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
     fp.ht = p->final_state;
     fp.h_out = p->h;
     fp.a_out = p->A;
+    fp.vn_out = p->v_new;
     if (P.cp_mode == GDN_CP_EXACT) {
         fp.ws_s = (float *)workspace;
         fp.ws_m = (float *)((char *)workspace + P.state_bytes);
@@ -416,8 +422,9 @@ int gdn_bwd(const gdn_bwd_desc *bd, const gdn_bwd_ptrs *p, void *workspace, size
         return fail(GDN_EINVAL, "initial_state pointer must be given iff has_h0");
     if ((bd->has_dht != 0) != (p->d_final_state != nullptr))
         return fail(GDN_EINVAL, "d_final_state pointer must be given iff has_dht");
-    if ((bd->saved_fwd != 0) != (p->h != nullptr) || (p->h != nullptr) != (p->A != nullptr))
-        return fail(GDN_EINVAL, "h and A must both be given iff saved_fwd");
+    if ((bd->saved_fwd != 0) != (p->h != nullptr) || (p->h != nullptr) != (p->A != nullptr) ||
+        (p->h != nullptr) != (p->v_new != nullptr))
+        return fail(GDN_EINVAL, "h, A and v_new must all be given iff saved_fwd");
 
     const size_t rows = (size_t)P.rows;
     const size_t n_qk = rows * d->H_qk * d->K, n_v = rows * d->H_v * d->V, n_g = rows * d->H_v;
@@ -434,9 +441,10 @@ int gdn_bwd(const gdn_bwd_desc *bd, const gdn_bwd_ptrs *p, void *workspace, size
         if (((uintptr_t)p->g | (uintptr_t)p->beta | (uintptr_t)p->dg | (uintptr_t)p->dbeta) & 3)
             return fail(GDN_EINVAL, "g, beta, dg and dbeta must be 4-byte aligned");
     }
-    if (((uintptr_t)p->h | (uintptr_t)p->A | (uintptr_t)p->initial_state | (uintptr_t)p->d_final_state |
-         (uintptr_t)p->d_initial_state) & 15)
-        return fail(GDN_EINVAL, "h, A and the state tensors must be 16-byte aligned");
+    if (((uintptr_t)p->h | (uintptr_t)p->A | (uintptr_t)p->v_new | (uintptr_t)p->initial_state |
+         (uintptr_t)p->d_final_state | (uintptr_t)p->d_initial_state) & 15)
+        return fail(GDN_EINVAL, "h, A, v_new and the state tensors must be 16-byte aligned");
+    const size_t n_vn = (size_t)P.total_chunks * d->H_v * gdn::kChunk * d->V;
     struct Buf { const void *ptr; size_t bytes; const char *name; };
     const Buf in[] = {{p->q, n_qk * 2, "q"}, {p->k, n_qk * 2, "k"}, {p->v, n_v * 2, "v"},
                       {p->g, n_g * 4, "g"}, {p->beta, n_g * 4, "beta"},
@@ -444,7 +452,7 @@ int gdn_bwd(const gdn_bwd_desc *bd, const gdn_bwd_ptrs *p, void *workspace, size
                       {p->cu_seqlens, varlen ? (size_t)(d->num_seqs + 1) * 4 : 0, "cu_seqlens"},
                       {p->dO, n_v * 2, "dO"}, {p->d_final_state, n_state * 4, "d_final_state"},
                       {p->h, p->h ? n_h * 4 : 0, "h"}, {p->A, p->A ? n_a * 4 : 0, "A"},
-                      {workspace, B.workspace, "workspace"}};
+                      {p->v_new, p->v_new ? n_vn * 4 : 0, "v_new"}, {workspace, B.workspace, "workspace"}};
     const Buf outs[] = {{p->dq, n_qk * gsz, "dq"}, {p->dk, n_qk * gsz, "dk"}, {p->dv, n_v * gsz, "dv"},
                         {p->dg, n_g * 4, "dg"}, {p->dbeta, n_g * 4, "dbeta"},
                         {p->d_initial_state, n_state * 4, "d_initial_state"}};
@@ -462,7 +470,7 @@ int gdn_bwd(const gdn_bwd_desc *bd, const gdn_bwd_ptrs *p, void *workspace, size
         return fail(GDN_EWORKSPACE, "workspace must be 256-byte aligned");
     char *ws = static_cast<char *>(workspace);
 
-    const float *h = p->h, *A = p->A;
+    const float *h = p->h, *A = p->A, *vn = p->v_new;
     if (!bd->saved_fwd && P.num_segments > 0 && rows > 0) {
         // recompute the forward's chunk-start states and WY matrices
         gdn::FwdParams fp = fwd_params(d, P);
@@ -477,10 +485,12 @@ int gdn_bwd(const gdn_bwd_desc *bd, const gdn_bwd_ptrs *p, void *workspace, size
         fp.ht = nullptr;
         fp.h_out = reinterpret_cast<float *>(ws + B.off_h);
         fp.a_out = reinterpret_cast<float *>(ws + B.off_a);
+        fp.vn_out = reinterpret_cast<float *>(ws + B.off_vn);
         const int err = gdn::launch_fwd_main(fp, stream);
         if (err) return fail(GDN_EHIP, "forward recompute launch failed: %s", gdn::hip_error_text(err));
         h = fp.h_out;
         A = fp.a_out;
+        vn = fp.vn_out;
     }
 
     gdn::BwdParams bp{};
@@ -493,6 +503,7 @@ int gdn_bwd(const gdn_bwd_desc *bd, const gdn_bwd_ptrs *p, void *workspace, size
     bp.cu = p->cu_seqlens;
     bp.h = h;
     bp.A = A;
+    bp.vn = vn;
     bp.dht = p->d_final_state;
     bp.dh_ws = reinterpret_cast<float *>(ws + B.off_dh);
     bp.dvp_ws = reinterpret_cast<float *>(ws + B.off_dvp);

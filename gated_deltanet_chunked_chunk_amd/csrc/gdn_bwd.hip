@@ -62,68 +62,141 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float ldf(const float *p) { return *p; }
 __device__ __forceinline__ float ldf(const bf16 *p) { return (float)*p; }
 
-// eight k-consecutive values of one operand row / column (k stride ks)
-template <typename T, bool CONTIG>
-__device__ __forceinline__ void load8(const T *p, int ks, float (&x)[8]) {
-    if constexpr (CONTIG && sizeof(T) == 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+// Operand read modes.  CONTIG: k runs along the stored row (vector reads).
+// STRIDED: any strides (element reads).  TRANS: a bf16 LDS tile stored
+// [k][m or n] row-major, read with ds_read_b64_tr_b16: per 16 k-rows each lane
+// receives 4 consecutive k of its own column.
+enum { CONTIG = 0, STRIDED = 1, TRANS = 2 };
+
+// k slot e of lane group g inside a 32-wide k step.  A step that reads any
+// operand transposed uses the k order {4g..4g+3, 16+4g..16+4g+3} (what two
+// transposed 16-row reads deliver) for both operands; otherwise 8g..8g+7.
+__device__ __forceinline__ constexpr int kpos(int e, int g, bool perm) {
+    return perm ? ((e & 3) + 4 * g + 16 * (e >> 2)) : (8 * g + e);
+}
+
+__device__ __forceinline__ bf16x4 tr4(const bf16 *p) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// hi + lo bf16 split of fp32 values, two at a time: hi = RNE(x) by a packed
+// conversion, float(hi) by shifting / masking the packed word, lo = RNE(x - hi).
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+    uint32_t h[4], l[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x[e] = a[e];
-            x[4 + e] = b[e];
+    for (int i = 0; i < 4; ++i) {
+        const bf16x2 hh = {(bf16)x[2 * i], (bf16)x[2 * i + 1]};
+        h[i] = __builtin_bit_cast(uint32_t, hh);
+        asm("" : "+v"(h[i]));
+        const float h0 = __uint_as_float(h[i] << 16), h1 = __uint_as_float(h[i] & 0xffff0000u);
+        const bf16x2 ll = {(bf16)(x[2 * i] - h0), (bf16)(x[2 * i + 1] - h1)};
+        l[i] = __builtin_bit_cast(uint32_t, ll);
+    }
+    hi = __builtin_bit_cast(bf16x8, (u32x4{h[0], h[1], h[2], h[3]}));
+    lo = __builtin_bit_cast(bf16x8, (u32x4{l[0], l[1], l[2], l[3]}));
+}
+
+// One operand fragment of a 32-wide k step at k0.  CONTIG / STRIDED: p points
+// at the operand's first row / column (element (r, k) at p[r ms + k ks]);
+// TRANS: element (r, k) at p[k ks + r] in LDS.  EXACT: bf16 values used as
+// one term (hi only); otherwise scaled by sk[k] (if given) and split.
+template <typename T, int MODE, bool PERM, bool EXACT, bool SCALED>
+__device__ __forceinline__ void operand(const T *p, int ms, int ks, int k0, int lane, const float *sk, bf16x8 &hi,
+                                        bf16x8 &lo) {
+    const int r = lane & 15, g = lane >> 4;
+    if constexpr (MODE == TRANS) {
+        static_assert(sizeof(T) == 2, "transposed reads are 16-bit");
+        const T *q = p + (k0 + (lane >> 2)) * ks + 4 * (lane & 3);
+        const bf16x4 x0 = tr4(q), x1 = tr4(q + 16 * ks);
+        const bf16x8 v = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        if constexpr (EXACT) {
+            hi = v;
+        } else {
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = (float)v[e] * (SCALED ? sk[k0 + kpos(e, g, true)] : 1.f);
+            split8(f, hi, lo);
         }
-    } else if constexpr (CONTIG) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(p);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
     } else {
+        const T *q = p + r * ms;
+        if constexpr (EXACT) {
+            if constexpr (MODE == CONTIG && !PERM) {
+                hi = *reinterpret_cast<const bf16x8 *>(q + k0 + 8 * g);
+            } else if constexpr (MODE == CONTIG) {
+                const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(q + k0 + 4 * g);
+                const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(q + k0 + 16 + 4 * g);
+                hi = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = ldf(p + e * ks);
+                for (int e = 0; e < 8; ++e) hi[e] = q[(k0 + kpos(e, g, PERM)) * ks];
+            }
+        } else {
+            float f[8];
+            if constexpr (MODE == CONTIG && sizeof(T) == 4) {
+                const int o0 = k0 + (PERM ? 4 * g : 8 * g), o1 = k0 + (PERM ? 16 + 4 * g : 8 * g + 4);
+                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(q + o0);
+                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(q + o1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    f[e] = x0[e];
+                    f[4 + e] = x1[e];
+                }
+            } else if constexpr (MODE == CONTIG) {
+                const int o0 = k0 + (PERM ? 4 * g : 8 * g), o1 = k0 + (PERM ? 16 + 4 * g : 8 * g + 4);
+                const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(q + o0);
+                const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(q + o1);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    f[e] = (float)x0[e];
+                    f[4 + e] = (float)x1[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = ldf(q + (k0 + kpos(e, g, PERM)) * ks);
+            }
+            if constexpr (SCALED) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] *= sk[k0 + kpos(e, g, PERM)];
+            }
+            split8(f, hi, lo);
+        }
     }
 }
 
-__device__ __forceinline__ void to_bf16(const float (&x)[8], bf16x8 &h) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = (bf16)x[e];
-}
-
-__device__ __forceinline__ void split(const float (&x)[8], bf16x8 &h, bf16x8 &l) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        h[e] = (bf16)x[e];
-        l[e] = (bf16)(x[e] - (float)h[e]);
-    }
-}
-
-// acc += A (16 x kd) B (kd x 16) for one output tile, A(m, k) = a[m ams + k aks],
-// B(k, n) = b[k bks + n bns]; AC / BC: unit k stride (vector loads).  SA: A is
-// scaled by sa[k] along k (then split like an fp32 operand).
-template <typename TA, bool AC, typename TB, bool BC, bool SA = false>
+// acc += A (16 x KD) B (KD x 16) for one output tile, A(m, k) = a[m ams + k aks],
+// B(k, n) = b[k bks + n bns], operands read in modes AM / BM.  SA: A is scaled
+// by sa[k] along k (then split like an fp32 operand).  Exact bf16 operands
+// enter as one term, fp32 (or scaled) ones as hi + lo: hi*hi + lo*hi + hi*lo.
+// Every k step's operands are read before the first product (one memory
+// latency per tile, not one per k step).
+template <typename TA, int AM, typename TB, int BM, int KD, bool SA = false>
 __device__ __forceinline__ f32x4 mm16(f32x4 acc, const TA *a, int ams, int aks, const TB *b, int bns, int bks,
-                                      int kd, int lane, const float *sa = nullptr) {
+                                      int lane, const float *sa = nullptr) {
+    constexpr bool PERM = AM == TRANS || BM == TRANS;
     constexpr bool EA = sizeof(TA) == 2 && !SA;
     constexpr bool EB = sizeof(TB) == 2;
-    const int r = lane & 15, kq = (lane >> 4) * 8;
-    const TA *pa = a + r * ams + kq * aks;
-    const TB *pb = b + r * bns + kq * bks;
-    for (int k0 = 0; k0 < kd; k0 += 32) {
-        float xa[8], xb[8];
-        load8<TA, AC>(pa + k0 * aks, aks, xa);
-        load8<TB, BC>(pb + k0 * bks, bks, xb);
-        if constexpr (SA) {
+    constexpr int NS = KD / 32;
+    bf16x8 ah[NS], al[NS], bh[NS], bl[NS];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xa[e] *= sa[k0 + kq + e];
-        }
-        bf16x8 ah, al, bh, bl;
-        if constexpr (EA) to_bf16(xa, ah); else split(xa, ah, al);
-        if constexpr (EB) to_bf16(xb, bh); else split(xb, bh, bl);
-        acc = mfma(ah, bh, acc);
-        if constexpr (!EA) acc = mfma(al, bh, acc);
-        if constexpr (!EB) acc = mfma(ah, bl, acc);
+    for (int st = 0; st < NS; ++st) {
+        operand<TA, AM, PERM, EA, SA>(a, AM == TRANS ? 0 : ams, aks, 32 * st, lane, sa, ah[st], al[st]);
+        operand<TB, BM, PERM, EB, false>(b, BM == TRANS ? 0 : bns, bks, 32 * st, lane, nullptr, bh[st], bl[st]);
+    }
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        acc = mfma(ah[st], bh[st], acc);
+        if constexpr (!EA) acc = mfma(al[st], bh[st], acc);
+        if constexpr (!EB) acc = mfma(ah[st], bl[st], acc);
     }
     return acc;
 }
@@ -164,15 +237,34 @@ __device__ __forceinline__ float ld4(__amdgpu_buffer_rsrc_t r, unsigned off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
 
-// 64 rows x (16-byte pieces per row) from HBM rows into a dense LDS tile
-__device__ __forceinline__ void stage_rows(void *dst, const void *base, unsigned stride, int c, int seq_len,
-                                           int pieces_per_row, int tid) {
+// 64 rows x PPR 16-byte pieces of HBM rows, held in registers between their
+// loads and their LDS stores (a dense tile), so that every load of a chunk is
+// in flight before the first store.
+template <int PPR>
+struct Rows {
+    static constexpr int PER = (CH * PPR + NT - 1) / NT;
+    u32x4 x[PER];
+};
+
+template <int PPR>
+__device__ __forceinline__ void load_rows(Rows<PPR> &R, const void *base, unsigned stride, int c, int seq_len,
+                                          int tid) {
     const __amdgpu_buffer_rsrc_t r = chunk_rsrc(base, stride, c, seq_len);
+#pragma unroll
+    for (int i = 0; i < Rows<PPR>::PER; ++i) {
+        const int pc = tid + i * NT;
+        const int row = pc / PPR, col = pc - row * PPR;
+        R.x[i] = (pc < CH * PPR) ? ld16(r, (unsigned)row * stride + (unsigned)col * 16u) : u32x4{};
+    }
+}
+
+template <int PPR>
+__device__ __forceinline__ void store_rows(void *dst, const Rows<PPR> &R, int tid) {
     u32x4 *d = static_cast<u32x4 *>(dst);
-    const int total = CH * pieces_per_row;
-    for (int pc = tid; pc < total; pc += NT) {
-        const int row = pc / pieces_per_row, col = pc - row * pieces_per_row;
-        d[pc] = ld16(r, (unsigned)row * stride + (unsigned)col * 16u);
+#pragma unroll
+    for (int i = 0; i < Rows<PPR>::PER; ++i) {
+        const int pc = tid + i * NT;
+        if (pc < CH * PPR) d[pc] = R.x[i];
     }
 }
 
@@ -275,25 +367,44 @@ struct __attribute__((aligned(16))) SmemDh {
 };
 static_assert(sizeof(SmemDh) <= 160 * 1024, "reverse-pass LDS over 160 KB");
 
-__device__ __forceinline__ void stage_chunk_dh(SmemDh &s, const BwdParams &p, const Where &e, int j, int half, int c,
-                                               int tid) {
+// One chunk's inputs of the reverse pass, in registers between load and store.
+struct ChunkDh {
+    Rows<DK * 2 / 16> k, q;
+    Rows<HVC * 2 / 16> dO;
+    Rows<CH * 4 / 16> t;
+    float g, b;
+};
+
+__device__ __forceinline__ void load_chunk_dh(ChunkDh &R, const BwdParams &p, const Where &e, int j, int half, int c,
+                                              int tid) {
     const int iq = j / p.group;
     const unsigned kstride = (unsigned)p.Hqk * DK * 2, vstride = (unsigned)p.Hv * DV * 2;
     const unsigned astride = (unsigned)p.Hv * CH * 4, gstride = (unsigned)p.Hv * 4;
-    stage_rows(s.k, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, DK * 2 / 16, tid);
-    stage_rows(s.q, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, DK * 2 / 16, tid);
-    stage_rows(s.dO, p.dO + (e.row0 * p.Hv + j) * DV + half * HVC, vstride, c, e.seq_len, HVC * 2 / 16, tid);
-    stage_rows(s.t, p.A + (e.row0 * p.Hv + j) * CH, astride, c, e.seq_len, CH * 4 / 16, tid);
+    load_rows(R.k, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
+    load_rows(R.q, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
+    load_rows(R.dO, p.dO + (e.row0 * p.Hv + j) * DV + half * HVC, vstride, c, e.seq_len, tid);
+    load_rows(R.t, p.A + (e.row0 * p.Hv + j) * CH, astride, c, e.seq_len, tid);
+    R.g = R.b = 0.f;
     if (tid < 64) {
         const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(p.g + e.row0 * p.Hv + j, gstride, c, e.seq_len);
         const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(p.beta + e.row0 * p.Hv + j, gstride, c, e.seq_len);
-        const float g = ld4(rg, (unsigned)tid * gstride), b = ld4(rb, (unsigned)tid * gstride);
-        const float G = prefix64(g, tid);
+        R.g = ld4(rg, (unsigned)tid * gstride);
+        R.b = ld4(rb, (unsigned)tid * gstride);
+    }
+}
+
+__device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int tid) {
+    store_rows(s.k, R.k, tid);
+    store_rows(s.q, R.q, tid);
+    store_rows(s.dO, R.dO, tid);
+    store_rows(s.t, R.t, tid);
+    if (tid < 64) {
+        const float G = prefix64(R.g, tid);
         const float Gl = __shfl(G, 63, 64);
         const float gam = __expf(G);
         s.G[tid] = G;
         s.gam[tid] = gam;
-        s.bg[tid] = b * gam;
+        s.bg[tid] = R.b * gam;
         s.rl[tid] = __expf(Gl - G);
     }
 }
@@ -349,25 +460,26 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
     const int cbase = seq_chunk_base(p.cu, p.T, e.n, lane);
     const int g16 = lane >> 4, c16 = lane & 15;
 
+    ChunkDh R;
+    if (c_last - 1 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c_last - 1, tid);
     for (int c = c_last - 1; c >= e.c_begin; --c) {
         const bool own = c < c_end;
         __syncthreads();  // previous chunk's dh update done; tiles free
-        stage_chunk_dh(s, p, e, j, half, c, tid);
+        store_chunk_dh(s, R, tid);
+        if (c - 1 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c - 1, tid);  // next chunk's inputs in flight
         __syncthreads();
         const float gl = s.gam[CH - 1];
 
         // W = T diag(beta gamma) K: wave w -> value... key columns 16 w .. +15, all rows
         for (int rt = 0; rt < 4; ++rt) {
-            f32x4 acc = mm16<float, true, bf16, false, true>(f32x4{}, s.t + 16 * rt * CH, CH, 1, s.k + 16 * wave, 1, DK,
-                                                            CH, lane, s.bg);
+            f32x4 acc = mm16<float, CONTIG, bf16, TRANS, CH, true>(f32x4{}, s.t + 16 * rt * CH, CH, 1, s.k + 16 * wave, 1, DK, lane, s.bg);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) s.w[(16 * rt + 4 * g16 + jj) * DK + 16 * wave + c16] = acc[jj];
         }
         // P = (Q K^T) o Gamma, s <= i: wave w -> row tile w / 2, column tiles 2 (w % 2) + {0, 1}
         for (int ct2 = 0; ct2 < 2; ++ct2) {
             const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
-            f32x4 acc = mm16<bf16, true, bf16, true>(f32x4{}, s.q + 16 * rt * DK, DK, 1, s.k + 16 * ct * DK, DK, 1, DK,
-                                                    lane);
+            f32x4 acc = mm16<bf16, CONTIG, bf16, CONTIG, DK>(f32x4{}, s.q + 16 * rt * DK, DK, 1, s.k + 16 * ct * DK, DK, 1, lane);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int i = 16 * rt + 4 * g16 + jj, sc = 16 * ct + c16;
@@ -388,9 +500,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
         // dv' = scale P^T dO + diag(rl) K dh: wave w -> row tile w / 2, column tiles 2 (w % 2) + {0, 1}
         for (int ct2 = 0; ct2 < 2; ++ct2) {
             const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
-            f32x4 a1 = mm16<float, false, bf16, false>(f32x4{}, s.p + 16 * rt, 1, CH, s.dO + 16 * ct, 1, HVC, CH, lane);
-            f32x4 a2 = mm16<bf16, true, float, false>(f32x4{}, s.k + 16 * rt * DK, DK, 1, s.dh + 16 * ct, 1, HVC, DK,
-                                                     lane);
+            f32x4 a1 = mm16<float, STRIDED, bf16, TRANS, CH>(f32x4{}, s.p + 16 * rt, 1, CH, s.dO + 16 * ct, 1, HVC, lane);
+            f32x4 a2 = mm16<bf16, CONTIG, float, STRIDED, DK>(f32x4{}, s.k + 16 * rt * DK, DK, 1, s.dh + 16 * ct, 1, HVC, lane);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int i = 16 * rt + 4 * g16 + jj, v = 16 * ct + c16;
@@ -403,10 +514,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
 
         // dh <- gamma_last dh + scale (diag(gamma) Q)^T dO - W^T dv': wave w -> key rows 16 w .. +15
         for (int ct = 0; ct < 4; ++ct) {
-            f32x4 a1 = mm16<bf16, false, bf16, false, true>(f32x4{}, s.q + 16 * wave, 1, DK, s.dO + 16 * ct, 1, HVC, CH,
-                                                           lane, s.gam);
-            f32x4 a2 = mm16<float, false, float, false>(f32x4{}, s.w + 16 * wave, 1, DK, s.dvp + 16 * ct, 1, HVC, CH,
-                                                       lane);
+            f32x4 a1 = mm16<bf16, TRANS, bf16, TRANS, CH, true>(f32x4{}, s.q + 16 * wave, 1, DK, s.dO + 16 * ct, 1, HVC, lane, s.gam);
+            f32x4 a2 = mm16<float, STRIDED, float, STRIDED, CH>(f32x4{}, s.w + 16 * wave, 1, DK, s.dvp + 16 * ct, 1, HVC, lane);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int d = 16 * wave + 4 * g16 + jj, v = 16 * ct + c16;
@@ -425,19 +534,156 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- chunk-local gradients
+// Fragment readers.  A fragment is the 8 k-values lane l holds for row /
+// column r = l % 16 in a 32-wide k step: k = 8 g .. 8 g + 7 (g = l / 16), or
+// the permuted order {4g..4g+3, 16+4g..16+4g+3} when the step reads any
+// operand transposed (PERM).
+//   fr_row:  bf16, element (r, k) at p[r ld + k]           (16- or 8-byte reads)
+//   fr_tr:   bf16 LDS, element (r, k) at p[k ld + r]      (ds_read_b64_tr_b16, PERM order)
+//   fr_rowf: fp32, element (r, k) at p[r ld + k], split hi + lo
+//   fr_colf: fp32, element (r, k) at p[k ks + r], split hi + lo
+template <bool PERM>
+__device__ __forceinline__ bf16x8 fr_row(const bf16 *p, int ld, int k0, int lane) {
+    const int r = lane & 15, g = lane >> 4;
+    const bf16 *q = p + r * ld + k0;
+    if constexpr (!PERM) {
+        return *reinterpret_cast<const bf16x8 *>(q + 8 * g);
+    } else {
+        const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(q + 4 * g);
+        const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(q + 16 + 4 * g);
+        return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    }
+}
+
+__device__ __forceinline__ bf16x8 fr_tr(const bf16 *p, int ld, int k0, int lane) {
+    const bf16 *q = p + (k0 + (lane >> 2)) * ld + 4 * (lane & 3);
+    const bf16x4 x0 = tr4(q), x1 = tr4(q + 16 * ld);
+    return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+}
+
+template <bool PERM>
+__device__ __forceinline__ void fr_rowf(const float *p, int ld, int k0, int lane, bf16x8 &hi, bf16x8 &lo,
+                                        float (&raw)[8]) {
+    const int r = lane & 15, g = lane >> 4;
+    const float *q = p + r * ld + k0;
+    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(q + (PERM ? 4 * g : 8 * g));
+    const f32x4 x1 = *reinterpret_cast<const f32x4 *>(q + (PERM ? 16 + 4 * g : 8 * g + 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        raw[e] = x0[e];
+        raw[4 + e] = x1[e];
+    }
+    split8(raw, hi, lo);
+}
+
+template <bool PERM>
+__device__ __forceinline__ void fr_colf(const float *p, int ks, int k0, int lane, bf16x8 &hi, bf16x8 &lo) {
+    const int r = lane & 15, g = lane >> 4;
+    float raw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) raw[e] = p[(k0 + kpos(e, g, PERM)) * ks + r];
+    split8(raw, hi, lo);
+}
+
+// products of hi / lo pairs: exact x pair, pair x exact, pair x pair
+__device__ __forceinline__ f32x4 mm_ep(f32x4 c, bf16x8 a, bf16x8 bh, bf16x8 bl) {
+    return mfma(a, bl, mfma(a, bh, c));
+}
+__device__ __forceinline__ f32x4 mm_pe(f32x4 c, bf16x8 ah, bf16x8 al, bf16x8 b) {
+    return mfma(al, b, mfma(ah, b, c));
+}
+__device__ __forceinline__ f32x4 mm_pp(f32x4 c, bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl) {
+    return mfma(ah, bl, mfma(al, bh, mfma(ah, bh, c)));
+}
+
+// hi / lo bf16 of an accumulator tile (rows 4 (l / 16) + j, column l % 16) into
+// row-major [row][col] arrays (st_split) or, transposed, into [col][row]
+// arrays where the lane's four rows are contiguous (st_split_t).
+__device__ __forceinline__ void split4(f32x4 v, bf16x4 &h, bf16x4 &l) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        h[j] = (bf16)v[j];
+        l[j] = (bf16)(v[j] - (float)h[j]);
+    }
+}
+__device__ __forceinline__ void st_split(bf16 *hi, bf16 *lo, int ld, int r0, int c0, f32x4 v, int lane) {
+    bf16x4 h, l;
+    split4(v, h, l);
+    const int c = c0 + (lane & 15), r = r0 + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        hi[(r + j) * ld + c] = h[j];
+        lo[(r + j) * ld + c] = l[j];
+    }
+}
+__device__ __forceinline__ void st_split_t(bf16 *hi, bf16 *lo, int ld, int r0, int c0, f32x4 v, int lane) {
+    bf16x4 h, l;
+    split4(v, h, l);
+    const int c = c0 + (lane & 15), r = r0 + 4 * (lane >> 4);
+    *reinterpret_cast<bf16x4 *>(&hi[c * ld + r]) = h;
+    *reinterpret_cast<bf16x4 *>(&lo[c * ld + r]) = l;
+}
+
+// LDS row strides (bf16 elements) of 128- and 64-wide tiles: 272 and 144
+// bytes, so that the 16 rows one fragment read touches fall in distinct banks.
+constexpr int LK = DK + 8;
+constexpr int L64 = CH + 8;
+
 struct __attribute__((aligned(16))) SmemLoc {
-    bf16 k[CH * DK], q[CH * DK], v[CH * DV], dO[CH * DV];
-    float t[CH * CH];
-    float m1[CH * CH], m2[CH * CH];
-    float x[CH * DK];                    // W, then v', then dW
-    float G[CH], gam[CH], bt[CH], bg[CH], rl[CH];
-    float dGp[8][CH], dbp[8][CH];        // per-wave partial sums of dG and dbeta
+    bf16 k[CH * LK], q[CH * LK];
+    bf16 ov[CH * LK];                 // dO, then V
+    bf16 tH[CH * L64], tL[CH * L64];  // T
+    bf16 nH[CH * LK], nL[CH * LK];    // v' [token][v], then dW [token][key dim], then Y [64][64] (stride L64)
+    bf16 eH[CH * LK], eL[CH * LK];    // dv' [token][v]
+    bf16 pH[CH * L64], pL[CH * L64];  // dPm, then dT, then M   [row][col]
+    float G[CH], gam[CH], bt[CH];
+    float dGp[8][CH], dbp[8][CH];     // per-wave partial sums of dG and dbeta
 };
 static_assert(sizeof(SmemLoc) <= 160 * 1024, "local-gradient LDS over 160 KB");
 
-// One workgroup per (chunk, v-head).  Wave w owns, for 64 x 128 results, key
-// (or value) columns 16 w .. 16 w + 15 of all 64 rows; for 64 x 64 results the
-// row tile w / 2 and column tiles 2 (w % 2), 2 (w % 2) + 1.
+// bf16 16-byte pieces (eight values) of 64 rows into a tile of row stride ld
+template <int PPR>
+__device__ __forceinline__ void store_rows_ld(bf16 *dst, const Rows<PPR> &R, int ld, int tid) {
+#pragma unroll
+    for (int i = 0; i < Rows<PPR>::PER; ++i) {
+        const int pc = tid + i * NT;
+        const int row = pc / PPR, col = pc - row * PPR;
+        if (pc < CH * PPR) *reinterpret_cast<u32x4 *>(&dst[row * ld + 8 * col]) = R.x[i];
+    }
+}
+
+// fp32 16-byte pieces (four values) of 64 rows -> hi / lo bf16 tiles of row stride ld
+template <int PPR>
+__device__ __forceinline__ void store_rows_split(bf16 *hi, bf16 *lo, const Rows<PPR> &R, int ld, int tid) {
+#pragma unroll
+    for (int i = 0; i < Rows<PPR>::PER; ++i) {
+        const int pc = tid + i * NT;
+        const int row = pc / PPR, col = pc - row * PPR;
+        if (pc < CH * PPR) {
+            bf16x4 h, l;
+            split4(__builtin_bit_cast(f32x4, R.x[i]), h, l);
+            *reinterpret_cast<bf16x4 *>(&hi[row * ld + 4 * col]) = h;
+            *reinterpret_cast<bf16x4 *>(&lo[row * ld + 4 * col]) = l;
+        }
+    }
+}
+
+// 64 x 128 fp32 rows (a dense per-chunk workspace tile) as 16-byte pieces
+__device__ __forceinline__ void load_tile_f32(Rows<DV * 4 / 16> &R, const float *src, int tid) {
+#pragma unroll
+    for (int i = 0; i < Rows<DV * 4 / 16>::PER; ++i)
+        R.x[i] = *reinterpret_cast<const u32x4 *>(src + 4 * (tid + i * NT));
+}
+
+// One workgroup per (chunk, v-head).  The key-dim results dq, dk and dW are
+// computed transposed ((key dim, token) tiles): every product with h or dh'
+// then contracts over the value dim, and wave w owns key dims 16 w .. +15, so
+// it reads (and splits) its 16 rows of h and dh' once.  64 x 64 results: wave
+// w has row tile w / 2 and column tiles 2 (w % 2), 2 (w % 2) + 1.  Every HBM
+// read is issued at the start (the chunk's inputs, T, v' and dv' into LDS as
+// hi / lo pairs; the wave's h and dh' rows into registers during the first
+// products); fp32 intermediates are stored once as hi / lo bf16 pairs that
+// every consumer reads without further arithmetic.
 __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     SmemLoc &s = *reinterpret_cast<SmemLoc *>(smem_raw);
@@ -451,28 +697,45 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     const int c = e.c_begin;
     const int cg = seq_chunk_base(p.cu, p.T, e.n, lane) + c;
     const int iq = j / p.group;
-    const int g16 = lane >> 4, c16 = lane & 15;
+    const int g4 = lane >> 4, r16 = lane & 15;
+    const float *hc = p.h + ((int64_t)cg * p.Hv + j) * DK * DV;       // chunk-start state [d][v]
+    const float *dhc = p.dh_ws + ((int64_t)cg * p.Hv + j) * DK * DV;  // gradient wrt the state after the chunk
+    const float *dvc = p.dvp_ws + ((int64_t)cg * p.Hv + j) * CH * DV; // dv' [i][v]
+    const float *vnc = p.vn + ((int64_t)cg * p.Hv + j) * CH * DV;     // v'  [i][v]
+    const unsigned vstride = (unsigned)p.Hv * DV * 2;
 
+    Rows<DV * 2 / 16> rv;  // V, stored once dO is dead
     {
-        const unsigned kstride = (unsigned)p.Hqk * DK * 2, vstride = (unsigned)p.Hv * DV * 2;
+        const unsigned kstride = (unsigned)p.Hqk * DK * 2;
         const unsigned astride = (unsigned)p.Hv * CH * 4, gstride = (unsigned)p.Hv * 4;
-        stage_rows(s.k, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, DK * 2 / 16, tid);
-        stage_rows(s.q, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, DK * 2 / 16, tid);
-        stage_rows(s.v, p.v + (e.row0 * p.Hv + j) * DV, vstride, c, e.seq_len, DV * 2 / 16, tid);
-        stage_rows(s.dO, p.dO + (e.row0 * p.Hv + j) * DV, vstride, c, e.seq_len, DV * 2 / 16, tid);
-        stage_rows(s.t, p.A + (e.row0 * p.Hv + j) * CH, astride, c, e.seq_len, CH * 4 / 16, tid);
+        Rows<DK * 2 / 16> rk, rq, rdo;
+        Rows<CH * 4 / 16> rtm;
+        Rows<DV * 4 / 16> rn, rd;
+        load_rows(rk, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
+        load_rows(rq, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
+        load_rows(rdo, p.dO + (e.row0 * p.Hv + j) * DV, vstride, c, e.seq_len, tid);
+        load_rows(rtm, p.A + (e.row0 * p.Hv + j) * CH, astride, c, e.seq_len, tid);
+        load_tile_f32(rn, vnc, tid);
+        load_tile_f32(rd, dvc, tid);
+        float g = 0.f, b = 0.f;
         if (tid < 64) {
             const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(p.g + e.row0 * p.Hv + j, gstride, c, e.seq_len);
             const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(p.beta + e.row0 * p.Hv + j, gstride, c, e.seq_len);
-            const float g = ld4(rg, (unsigned)tid * gstride), b = ld4(rb, (unsigned)tid * gstride);
+            g = ld4(rg, (unsigned)tid * gstride);
+            b = ld4(rb, (unsigned)tid * gstride);
+        }
+        load_rows(rv, p.v + (e.row0 * p.Hv + j) * DV, vstride, c, e.seq_len, tid);
+        store_rows_ld(s.k, rk, LK, tid);
+        store_rows_ld(s.q, rq, LK, tid);
+        store_rows_ld(s.ov, rdo, LK, tid);
+        store_rows_split(s.tH, s.tL, rtm, L64, tid);
+        store_rows_split(s.nH, s.nL, rn, LK, tid);
+        store_rows_split(s.eH, s.eL, rd, LK, tid);
+        if (tid < 64) {
             const float G = prefix64(g, tid);
-            const float Gl = __shfl(G, 63, 64);
-            const float gam = __expf(G);
             s.G[tid] = G;
-            s.gam[tid] = gam;
+            s.gam[tid] = __expf(G);
             s.bt[tid] = b;
-            s.bg[tid] = b * gam;
-            s.rl[tid] = __expf(Gl - G);
         }
         for (int x = tid; x < 8 * CH; x += NT) {
             (&s.dGp[0][0])[x] = 0.f;
@@ -481,207 +744,281 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     }
     __syncthreads();
 
-    const float *hc = p.h + ((int64_t)cg * p.Hv + j) * DK * DV;       // chunk-start state
-    const float *dhc = p.dh_ws + ((int64_t)cg * p.Hv + j) * DK * DV;  // gradient wrt the state after the chunk
-    const float *dvc = p.dvp_ws + ((int64_t)cg * p.Hv + j) * CH * DV; // dv'
+    // this wave's 16 rows of h and dh' (A operands of the transposed products),
+    // in flight while the first products run
+    f32x4 hr[4][2], dr[4][2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int off = (16 * wave + r16) * DV + 32 * kk + 8 * g4 + 4 * hf;
+            hr[kk][hf] = *reinterpret_cast<const f32x4 *>(hc + off);
+            dr[kk][hf] = *reinterpret_cast<const f32x4 *>(dhc + off);
+        }
+
     float *dGw = s.dGp[wave];
     float *dbw = s.dbp[wave];
-    const int rt64 = wave >> 1;  // 64 x 64 results: row tile
+    const int rt64 = wave >> 1;
+    const int rows_valid = min(CH, e.seq_len - c * CH);
     const float gl = s.gam[CH - 1];
 
-    // S1: W = T diag(beta gamma) K -> x;  Q K^T -> m1
-    for (int rt = 0; rt < 4; ++rt) {
-        f32x4 acc = mm16<float, true, bf16, false, true>(f32x4{}, s.t + 16 * rt * CH, CH, 1, s.k + 16 * wave, 1, DK, CH,
-                                                        lane, s.bg);
+    // ---- 1: dPm = scale (dO v'^T) o Gamma (s <= i) -> p;  gate terms of P
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) s.x[(16 * rt + 4 * g16 + jj) * DK + 16 * wave + c16] = acc[jj];
-    }
     for (int ct2 = 0; ct2 < 2; ++ct2) {
         const int ct = 2 * (wave & 1) + ct2;
-        f32x4 acc = mm16<bf16, true, bf16, true>(f32x4{}, s.q + 16 * rt64 * DK, DK, 1, s.k + 16 * ct * DK, DK, 1, DK,
-                                                lane);
+        f32x4 acc = f32x4{}, qk = f32x4{};
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) s.m1[(16 * rt64 + 4 * g16 + jj) * CH + 16 * ct + c16] = acc[jj];
-    }
-    __syncthreads();
-
-    // S2: v' = T diag(beta) V - W h (value columns 16 w ..), held, then -> x
-    f32x4 vpt[4];
-    for (int rt = 0; rt < 4; ++rt) {
-        f32x4 a1 = mm16<float, true, bf16, false, true>(f32x4{}, s.t + 16 * rt * CH, CH, 1, s.v + 16 * wave, 1, DV, CH,
-                                                       lane, s.bt);
-        f32x4 a2 = mm16<float, true, float, false>(f32x4{}, s.x + 16 * rt * DK, DK, 1, hc + 16 * wave, 1, DV, DK, lane);
-        vpt[rt] = a1 - a2;
-    }
-    __syncthreads();
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) s.x[(16 * rt + 4 * g16 + jj) * DV + 16 * wave + c16] = vpt[rt][jj];
-    __syncthreads();
-
-    // S3: dPm = scale (dO v'^T) o Gamma (s <= i) -> m2; gate terms of P
-    for (int ct2 = 0; ct2 < 2; ++ct2) {
-        const int ct = 2 * (wave & 1) + ct2;
-        f32x4 acc = mm16<bf16, true, float, true>(f32x4{}, s.dO + 16 * rt64 * DV, DV, 1, s.x + 16 * ct * DV, DV, 1, DV,
-                                                 lane);
+        for (int kk = 0; kk < 4; ++kk) {
+            acc = mm_ep(acc, fr_row<false>(s.ov + 16 * rt64 * LK, LK, 32 * kk, lane),
+                        fr_row<false>(s.nH + 16 * ct * LK, LK, 32 * kk, lane),
+                        fr_row<false>(s.nL + 16 * ct * LK, LK, 32 * kk, lane));
+            qk = mfma(fr_row<false>(s.q + 16 * rt64 * LK, LK, 32 * kk, lane),
+                      fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane), qk);
+        }
+        f32x4 dpm;
         float colsum = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int i = 16 * rt64 + 4 * g16 + jj, sc = 16 * ct + c16;
-            const float dpm = sc <= i ? p.scale * acc[jj] * __expf(s.G[i] - s.G[sc]) : 0.f;
-            s.m2[i * CH + sc] = dpm;
-            const float d1 = dpm * s.m1[i * CH + sc];
+            const int i = 16 * rt64 + 4 * g4 + jj, sc = 16 * ct + r16;
+            dpm[jj] = sc <= i ? p.scale * acc[jj] * __expf(s.G[i] - s.G[sc]) : 0.f;
+            const float d1 = dpm[jj] * qk[jj];
             const float rs = sum16(d1);
-            if (c16 == 0) dGw[i] += rs;
+            if (r16 == 0) dGw[i] += rs;
             colsum += d1;
         }
         colsum = sum4g(colsum);
-        if (g16 == 0) dGw[16 * ct + c16] -= colsum;
+        if (g4 == 0) dGw[16 * ct + r16] -= colsum;
+        st_split(s.pH, s.pL, L64, 16 * rt64, 16 * ct, dpm, lane);
     }
     __syncthreads();
 
-    // S4: dQ, dK terms of P, h and h'; gate terms of O (inter) and h'
-    f32x4 dq[4], dk[4];
-    float lastacc = 0.f;
-    for (int rt = 0; rt < 4; ++rt) {
-        dq[rt] = mm16<float, true, bf16, false>(f32x4{}, s.m2 + 16 * rt * CH, CH, 1, s.k + 16 * wave, 1, DK, CH, lane);
-        const f32x4 t1 = mm16<bf16, true, float, true>(f32x4{}, s.dO + 16 * rt * DV, DV, 1, hc + 16 * wave * DV, DV, 1,
-                                                      DV, lane);
-        dk[rt] = mm16<float, false, bf16, false>(f32x4{}, s.m2 + 16 * rt, 1, CH, s.q + 16 * wave, 1, DK, CH, lane);
-        const f32x4 t2 = mm16<float, true, float, true>(f32x4{}, s.x + 16 * rt * DV, DV, 1, dhc + 16 * wave * DV, DV, 1,
-                                                       DV, lane);
-        const f32x4 t3 = mm16<bf16, true, float, false>(f32x4{}, s.k + 16 * rt * DK, DK, 1, dhc + 16 * wave, 1, DV, DK,
-                                                       lane);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int i = 16 * rt + 4 * g16 + jj, col = 16 * wave + c16;
-            const float sg = p.scale * s.gam[i];
-            dq[rt][jj] += sg * t1[jj];
-            const float qd = (float)s.q[i * DK + col] * t1[jj];
-            const float rq = sum16(qd);
-            if (c16 == 0) dGw[i] += sg * rq;
-            dk[rt][jj] += s.rl[i] * t2[jj];
-            // t3 is (K dh') over value columns 16 w ..: x_i = rl_i v'_i . (K dh')_i
-            const float xv = s.x[i * DV + col] * s.rl[i] * t3[jj];
-            const float rx = sum16(xv);
-            if (c16 == 0) dGw[i] -= rx;
-            lastacc += (c16 == 0) ? rx : 0.f;
-        }
-    }
+    // ---- 2: transposed dk, dq, dW over this wave's key dims 16 w ..
+    f32x4 dkt[4];
+    bf16x8 hH[4], hL[4];
     {
-        // gamma_last <dh', h>: this wave's share of the 128 x 128 products
+        bf16x8 dH[4], dL[4];
         float dot = 0.f;
-        for (int x = lane; x < DK * DV / 8; x += 64) {
-            const int idx = wave * (DK * DV / 8) + x;
-            dot += dhc[idx] * hc[idx];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            float rh[8], rd[8];
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                rh[e2] = hr[kk][0][e2];
+                rh[4 + e2] = hr[kk][1][e2];
+                rd[e2] = dr[kk][0][e2];
+                rd[4 + e2] = dr[kk][1][e2];
+            }
+#pragma unroll
+            for (int e2 = 0; e2 < 8; ++e2) dot += rh[e2] * rd[e2];
+            split8(rh, hH[kk], hL[kk]);
+            split8(rd, dH[kk], dL[kk]);
         }
-        dot = sum64(dot);
+        // dk: rl_s (dh' v'^T) + Q^T dPm;  gate terms of h'
+        float lastacc = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            f32x4 t2 = f32x4{}, qp = f32x4{};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                t2 = mm_pp(t2, dH[kk], dL[kk], fr_row<false>(s.nH + 16 * ct * LK, LK, 32 * kk, lane),
+                           fr_row<false>(s.nL + 16 * ct * LK, LK, 32 * kk, lane));
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                qp = mm_ep(qp, fr_tr(s.q + 16 * wave, LK, 32 * kk, lane), fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane),
+                           fr_tr(s.pL + 16 * ct, L64, 32 * kk, lane));
+            const int col = 16 * ct + r16;  // key token s
+            const float rl = __expf(s.G[CH - 1] - s.G[col]);
+            float ksum = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) ksum += (float)s.k[col * LK + 16 * wave + 4 * g4 + jj] * t2[jj];
+            ksum = sum4g(ksum);
+            if (g4 == 0) {
+                dGw[col] -= rl * ksum;
+                lastacc += rl * ksum;
+            }
+            dkt[ct] = rl * t2 + qp;
+        }
         lastacc = sum64(lastacc);
+        dot = sum64(dot);
         if (lane == 0) dGw[CH - 1] += lastacc + gl * dot;
     }
-    __syncthreads();
-
-    // S5: dW = -dv' h^T -> x
-    for (int rt = 0; rt < 4; ++rt) {
-        f32x4 acc = mm16<float, true, float, true>(f32x4{}, dvc + 16 * rt * DV, DV, 1, hc + 16 * wave * DV, DV, 1, DV,
-                                                  lane);
+    // dq: scale gamma_i (h dO^T) + K^T dPm^T;  gate term of O (inter); stored
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) s.x[(16 * rt + 4 * g16 + jj) * DK + 16 * wave + c16] = -acc[jj];
-    }
-    __syncthreads();
-
-    // S6: dT -> m1;  dK and dbeta / dG terms of W;  dV and the dbeta term of U
-    for (int ct2 = 0; ct2 < 2; ++ct2) {
-        const int ct = 2 * (wave & 1) + ct2;
-        f32x4 a1 = mm16<float, true, bf16, true>(f32x4{}, s.x + 16 * rt64 * DK, DK, 1, s.k + 16 * ct * DK, DK, 1, DK,
-                                                lane);
-        f32x4 a2 = mm16<float, true, bf16, true>(f32x4{}, dvc + 16 * rt64 * DV, DV, 1, s.v + 16 * ct * DV, DV, 1, DV,
-                                                lane);
+    for (int ct = 0; ct < 4; ++ct) {
+        f32x4 t1 = f32x4{}, kq = f32x4{};
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int i = 16 * rt64 + 4 * g16 + jj, sc = 16 * ct + c16;
-            s.m1[i * CH + sc] = s.bg[sc] * a1[jj] + s.bt[sc] * a2[jj];
+        for (int kk = 0; kk < 4; ++kk)
+            t1 = mm_pe(t1, hH[kk], hL[kk], fr_row<false>(s.ov + 16 * ct * LK, LK, 32 * kk, lane));
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            kq = mm_ep(kq, fr_tr(s.k + 16 * wave, LK, 32 * kk, lane), fr_row<true>(s.pH + 16 * ct * L64, L64, 32 * kk, lane),
+                       fr_row<true>(s.pL + 16 * ct * L64, L64, 32 * kk, lane));
+        const int col = 16 * ct + r16;  // query token i
+        const float sg = p.scale * s.gam[col];
+        float qsum = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) qsum += (float)s.q[col * LK + 16 * wave + 4 * g4 + jj] * t1[jj];
+        qsum = sum4g(qsum);
+        if (g4 == 0) dGw[col] += sg * qsum;
+        if (col < rows_valid) {
+            const int64_t off = ((e.row0 + (int64_t)c * CH + col) * p.Hv + j) * DK + 16 * wave + 4 * g4;
+            *reinterpret_cast<f32x4 *>(p.dq_ws + off) = sg * t1 + kq;
         }
     }
-    const int rows_valid = min(CH, e.seq_len - c * CH);
-    for (int rt = 0; rt < 4; ++rt) {
-        const f32x4 kb = mm16<float, false, float, false>(f32x4{}, s.t + 16 * rt, 1, CH, s.x + 16 * wave, 1, DK, CH,
-                                                         lane);
-        const f32x4 vb = mm16<float, false, float, false>(f32x4{}, s.t + 16 * rt, 1, CH, dvc + 16 * wave, 1, DV, CH,
-                                                         lane);
+    __syncthreads();  // v' and dO are dead: their tiles take dW and V
+
+    // dW = -(h dv'^T)^T -> n [token][key dim];  V -> ov
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int i = 16 * rt + 4 * g16 + jj, col = 16 * wave + c16;
-            dk[rt][jj] += s.bg[i] * kb[jj];
-            const float rk = sum16(kb[jj] * (float)s.k[i * DK + col]);
-            const float rv = sum16(vb[jj] * (float)s.v[i * DV + col]);
-            if (c16 == 0) {
-                dbw[i] += s.gam[i] * rk + rv;
-                dGw[i] += s.bg[i] * rk;
-            }
-            const float dvv = s.bt[i] * vb[jj];
-            if (i < rows_valid) {
-                const int64_t off = ((e.row0 + (int64_t)c * CH + i) * p.Hv + j) * DV + col;
-                if (p.grad_f32) static_cast<float *>(p.dv)[off] = dvv;
-                else static_cast<bf16 *>(p.dv)[off] = (bf16)dvv;
+    for (int ct = 0; ct < 4; ++ct) {
+        f32x4 tw = f32x4{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            tw = mm_pp(tw, hH[kk], hL[kk], fr_row<false>(s.eH + 16 * ct * LK, LK, 32 * kk, lane),
+                       fr_row<false>(s.eL + 16 * ct * LK, LK, 32 * kk, lane));
+        st_split_t(s.nH, s.nL, LK, 16 * wave, 16 * ct, -tw, lane);
+    }
+    store_rows_ld(s.ov, rv, LK, tid);
+    __syncthreads();
+
+    // ---- 3: dT -> p;  dK, dbeta, dG terms of W;  dV and the dbeta term of U
+#pragma unroll
+    for (int ct2 = 0; ct2 < 2; ++ct2) {
+        const int ct = 2 * (wave & 1) + ct2;
+        f32x4 a1 = f32x4{}, a2 = f32x4{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            a1 = mm_pe(a1, fr_row<false>(s.nH + 16 * rt64 * LK, LK, 32 * kk, lane),
+                       fr_row<false>(s.nL + 16 * rt64 * LK, LK, 32 * kk, lane),
+                       fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane));
+            a2 = mm_pe(a2, fr_row<false>(s.eH + 16 * rt64 * LK, LK, 32 * kk, lane),
+                       fr_row<false>(s.eL + 16 * rt64 * LK, LK, 32 * kk, lane),
+                       fr_row<false>(s.ov + 16 * ct * LK, LK, 32 * kk, lane));
+        }
+        const int sc = 16 * ct + r16;
+        st_split(s.pH, s.pL, L64, 16 * rt64, 16 * ct, s.bt[sc] * (s.gam[sc] * a1 + a2), lane);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        // T^T dW, transposed: (key dim, token s)
+        f32x4 acc = f32x4{};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            acc = mm_pp(acc, fr_tr(s.nH + 16 * wave, LK, 32 * kk, lane), fr_tr(s.nL + 16 * wave, LK, 32 * kk, lane),
+                        fr_tr(s.tH + 16 * ct, L64, 32 * kk, lane), fr_tr(s.tL + 16 * ct, L64, 32 * kk, lane));
+        const int sc = 16 * ct + r16;
+        float rk = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) rk += acc[jj] * (float)s.k[sc * LK + 16 * wave + 4 * g4 + jj];
+        rk = sum4g(rk);
+        const float bgs = s.bt[sc] * s.gam[sc];
+        if (g4 == 0) {
+            dbw[sc] += s.gam[sc] * rk;
+            dGw[sc] += bgs * rk;
+        }
+        dkt[ct] += bgs * acc;
+    }
+    {
+        // T^T dv' over value columns 16 w .., all token rows s
+        bf16x8 bh[2], bl[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bh[kk] = fr_tr(s.eH + 16 * wave, LK, 32 * kk, lane);
+            bl[kk] = fr_tr(s.eL + 16 * wave, LK, 32 * kk, lane);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                acc = mm_pp(acc, fr_tr(s.tH + 16 * rt, L64, 32 * kk, lane), fr_tr(s.tL + 16 * rt, L64, 32 * kk, lane),
+                            bh[kk], bl[kk]);
+            const int col = 16 * wave + r16;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int sr = 16 * rt + 4 * g4 + jj;
+                const float rvv = sum16(acc[jj] * (float)s.ov[sr * LK + col]);
+                if (r16 == 0) dbw[sr] += rvv;
+                const float dvv = s.bt[sr] * acc[jj];
+                if (sr < rows_valid) {
+                    const int64_t off = ((e.row0 + (int64_t)c * CH + sr) * p.Hv + j) * DV + col;
+                    if (p.grad_f32) static_cast<float *>(p.dv)[off] = dvv;
+                    else static_cast<bf16 *>(p.dv)[off] = (bf16)dvv;
+                }
             }
         }
     }
     __syncthreads();
 
-    // S7: Y = T^T dT -> m2
+    // ---- 4: Y = T^T dT -> n (as [64][64])
+#pragma unroll
     for (int ct2 = 0; ct2 < 2; ++ct2) {
         const int ct = 2 * (wave & 1) + ct2;
-        f32x4 acc = mm16<float, false, float, false>(f32x4{}, s.t + 16 * rt64, 1, CH, s.m1 + 16 * ct, 1, CH, CH, lane);
+        f32x4 acc = f32x4{};
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) s.m2[(16 * rt64 + 4 * g16 + jj) * CH + 16 * ct + c16] = acc[jj];
+        for (int kk = 0; kk < 2; ++kk)
+            acc = mm_pp(acc, fr_tr(s.tH + 16 * rt64, L64, 32 * kk, lane), fr_tr(s.tL + 16 * rt64, L64, 32 * kk, lane),
+                        fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane), fr_tr(s.pL + 16 * ct, L64, 32 * kk, lane));
+        st_split(s.nH, s.nL, L64, 16 * rt64, 16 * ct, acc, lane);
     }
     __syncthreads();
 
-    // S8: dA~ = -(Y T^T) strictly lower; M = dA~ o beta_i Gamma_is -> m1; gate / beta terms of A~
+    // ---- 5: dA~ = -(Y T^T) strictly lower;  M = dA~ o beta_i Gamma_is -> p;  gate / beta terms of A~
+#pragma unroll
     for (int ct2 = 0; ct2 < 2; ++ct2) {
         const int ct = 2 * (wave & 1) + ct2;
-        f32x4 ya = mm16<float, true, float, true>(f32x4{}, s.m2 + 16 * rt64 * CH, CH, 1, s.t + 16 * ct * CH, CH, 1, CH,
-                                                 lane);
-        f32x4 kk = mm16<bf16, true, bf16, true>(f32x4{}, s.k + 16 * rt64 * DK, DK, 1, s.k + 16 * ct * DK, DK, 1, DK,
-                                               lane);
+        f32x4 ya = f32x4{}, kk4 = f32x4{};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            ya = mm_pp(ya, fr_row<false>(s.nH + 16 * rt64 * L64, L64, 32 * kk, lane),
+                       fr_row<false>(s.nL + 16 * rt64 * L64, L64, 32 * kk, lane),
+                       fr_row<false>(s.tH + 16 * ct * L64, L64, 32 * kk, lane),
+                       fr_row<false>(s.tL + 16 * ct * L64, L64, 32 * kk, lane));
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            kk4 = mfma(fr_row<false>(s.k + 16 * rt64 * LK, LK, 32 * kk, lane),
+                       fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane), kk4);
+        f32x4 m;
         float colsum = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int i = 16 * rt64 + 4 * g16 + jj, sc = 16 * ct + c16;
-            float m = 0.f, d2 = 0.f, db = 0.f;
+            const int i = 16 * rt64 + 4 * g4 + jj, sc = 16 * ct + r16;
+            float d2 = 0.f, db = 0.f;
+            m[jj] = 0.f;
             if (sc < i) {
                 const float da = -ya[jj];
                 const float gm = __expf(s.G[i] - s.G[sc]);
-                m = da * s.bt[i] * gm;
-                d2 = m * kk[jj];
-                db = da * gm * kk[jj];
+                m[jj] = da * s.bt[i] * gm;
+                d2 = m[jj] * kk4[jj];
+                db = da * gm * kk4[jj];
             }
-            s.m1[i * CH + sc] = m;
             const float rs = sum16(d2), rb = sum16(db);
-            if (c16 == 0) {
+            if (r16 == 0) {
                 dGw[i] += rs;
                 dbw[i] += rb;
             }
             colsum += d2;
         }
         colsum = sum4g(colsum);
-        if (g16 == 0) dGw[16 * ct + c16] -= colsum;
+        if (g4 == 0) dGw[16 * ct + r16] -= colsum;
+        st_split(s.pH, s.pL, L64, 16 * rt64, 16 * ct, m, lane);
     }
     __syncthreads();
 
-    // S9: dK += M K + M^T K; store dq, dk of this v-head
-    for (int rt = 0; rt < 4; ++rt) {
-        dk[rt] = mm16<float, true, bf16, false>(dk[rt], s.m1 + 16 * rt * CH, CH, 1, s.k + 16 * wave, 1, DK, CH, lane);
-        dk[rt] = mm16<float, false, bf16, false>(dk[rt], s.m1 + 16 * rt, 1, CH, s.k + 16 * wave, 1, DK, CH, lane);
+    // ---- 6: dK += M K + M^T K (transposed: K^T M^T + K^T M); store dk of this v-head
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int i = 16 * rt + 4 * g16 + jj, col = 16 * wave + c16;
-            if (i < rows_valid) {
-                const int64_t off = ((e.row0 + (int64_t)c * CH + i) * p.Hv + j) * DK + col;
-                p.dq_ws[off] = dq[rt][jj];
-                p.dk_ws[off] = dk[rt][jj];
-            }
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 ak = fr_tr(s.k + 16 * wave, LK, 32 * kk, lane);
+            dkt[ct] = mm_ep(dkt[ct], ak, fr_row<true>(s.pH + 16 * ct * L64, L64, 32 * kk, lane),
+                            fr_row<true>(s.pL + 16 * ct * L64, L64, 32 * kk, lane));
+            dkt[ct] = mm_ep(dkt[ct], ak, fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane),
+                            fr_tr(s.pL + 16 * ct, L64, 32 * kk, lane));
+        }
+        const int tok = 16 * ct + r16;
+        if (tok < rows_valid) {
+            const int64_t off = ((e.row0 + (int64_t)c * CH + tok) * p.Hv + j) * DK + 16 * wave + 4 * g4;
+            *reinterpret_cast<f32x4 *>(p.dk_ws + off) = dkt[ct];
         }
     }
     __syncthreads();
@@ -694,7 +1031,6 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             dG += s.dGp[w][lane];
             db += s.dbp[w][lane];
         }
-        // suffix sum: sum over i >= lane
         float x = dG;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {

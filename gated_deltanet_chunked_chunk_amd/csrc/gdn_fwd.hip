@@ -1265,6 +1265,19 @@ __device__ __forceinline__ void store_t8(const Smem8 &s, const FwdParams &p, con
     }
 }
 
+// v' of one chunk (all 64 rows, chunk-padded) from state wave sw's registers:
+// vp[rt][ct] element jj is row 16 rt + 4 (l / 16) + jj, value column
+// 32 sw + 16 ct + l % 16.
+__device__ __forceinline__ void store_vn8(const f32x4 (&vp)[4][2], float *dst, const int sw, const int lane) {
+    const int m = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dst[(16 * rt + 4 * g + jj) * DV + 32 * sw + 16 * ct + m] = vp[rt][ct][jj];
+}
+
 // ---- state I/O: K x V fp32 state <-> state wave sw's two column tiles
 __device__ __forceinline__ void load_state8(f32x4 (&t)[2][8], const float *src, const int sw, const int lane) {
     const int m = lane & 15, g = lane >> 4;
@@ -1379,7 +1392,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int64_t oes = p.o_f32 ? 4 : 2;
         const char *obase = static_cast<const char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes;
         f32x4 vp[4][2], qh[4][2];  // vp: U of the next chunk, then v' of this one
-        const int cbase = p.h_out ? seq_chunk_base(p, e.n, lane) : 0;
+        const int cbase = (p.h_out || p.vn_out) ? seq_chunk_base(p, e.n, lane) : 0;
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
             const bool chain = c >= c_first;  // state pass of chunk c
             const bool prep = c + 1 < c_end;  // preparation of chunk c + 1
@@ -1395,6 +1408,8 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
                 return t & 63;
             };
             if (chain) wh8(s, hacc, vp, lane_now());
+            if (chain && out && p.vn_out)
+                store_vn8(vp, p.vn_out + ((int64_t)(cbase + c) * p.Hv + j) * CH * DV, wave, lane_now());
             __syncthreads();
             if (chain && out) out8(s, p, obase, e.seq_len, vp, qh, c, b, wave, lane_now());
             __syncthreads();

@@ -56,8 +56,9 @@ struct FwdParams {
     // exact context parallelism (workspace, each [num_segments][Hv][K][V] fp32):
     // per-segment zero-start state S, transition map M, and segment-start state H
     float *ws_s, *ws_m, *ws_h;
-    // optional low-level outputs: per-chunk start states, per-chunk WY matrices
-    float *h_out, *a_out;
+    // optional low-level outputs: per-chunk start states, per-chunk WY matrices,
+    // per-chunk v' = U - W h ([total_chunks][Hv][64][V], chunk-padded; for the backward)
+    float *h_out, *a_out, *vn_out;
 };
 
 // Backward (gdn_bwd.hip): reverse pass over segments, then chunk-local gradients,
@@ -68,6 +69,7 @@ struct BwdParams {
     const int32_t *cu;               // device offsets or nullptr
     const float *h;                  // [total_chunks][Hv][K][V] chunk-start states (forward's low-level h)
     const float *A;                  // [rows][Hv][64] WY matrices (forward's low-level A)
+    const float *vn;                 // [total_chunks][Hv][64][V] v' of every chunk (forward's v_new)
     const float *dht;                // [N][Hv][K][V] or nullptr
     float *dh_ws;                    // [total_chunks][Hv][K][V] gradient wrt the state after each chunk
     float *dvp_ws;                   // [total_chunks][Hv][64][V] dv' (all 64 rows of every chunk)

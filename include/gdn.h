@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum {
     GDN_OK = 0,
@@ -124,9 +124,13 @@ typedef struct {
      * With WARMUP/AUTO context parallelism, h at a segment's chunks carries
      * the warm-up approximation of the state (the same as o); h of a chunk
      * that is only a warm-up chunk of a later segment is written by the
-     * segment that owns it. */
+     * segment that owns it.
+     *   v_new fp32 [total_chunks, H_v, chunk, V]: v' = U - W h of every chunk
+     *      (the delta-rule residuals of the chunked form), all `chunk` rows,
+     *      zero past a sequence's end; kept for gdn_bwd. */
     float *h;
     float *A;
+    float *v_new;
 } gdn_fwd_ptrs;
 
 /* ABI version this library was built with (GDN_ABI_VERSION). */
@@ -182,8 +186,8 @@ typedef struct {
     gdn_fwd_desc fwd;     /* the forward call being differentiated (want_ht and o_dtype are ignored) */
     int32_t has_dht;      /* d_final_state given */
     int32_t grad_dtype;   /* gdn_dtype of dq, dk, dv (dg, dbeta, d_initial_state are fp32) */
-    int32_t saved_fwd;    /* 1: the caller passes h and A from gdn_fwd under the same fwd descriptor;
-                             0: the backward recomputes them in its workspace */
+    int32_t saved_fwd;    /* 1: the caller passes h, A and v_new from gdn_fwd under the same fwd
+                             descriptor; 0: the backward recomputes them in its workspace */
 } gdn_bwd_desc;
 
 typedef struct {
@@ -206,6 +210,7 @@ typedef struct {
     const float *d_final_state;     /* fp32 [N, H_v, K, V], NULL iff has_dht == 0 */
     const float *h;                 /* saved_fwd: gdn_fwd's h (fp32 [total_chunks, H_v, K, V]), else NULL */
     const float *A;                 /* saved_fwd: gdn_fwd's A (fp32 [B * T, H_v, chunk]), else NULL */
+    const float *v_new;             /* saved_fwd: gdn_fwd's v_new (fp32 [total_chunks, H_v, chunk, V]), else NULL */
     void *dq, *dk;                  /* [B, T, H_qk, K], grad_dtype */
     void *dv;                       /* [B, T, H_v, V], grad_dtype */
     float *dg, *dbeta;              /* fp32 [B, T, H_v] */

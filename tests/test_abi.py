@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = L.lib()
-    assert lib.gdn_abi_version() == L.ABI_VERSION == 3
+    assert lib.gdn_abi_version() == L.ABI_VERSION == 4
     for st in (0, -1, -2, -3, -4):
         assert lib.gdn_status_str(st)
     assert b"unknown" in lib.gdn_status_str(42)
@@ -183,7 +183,7 @@ def test_bwd_plan_layout_and_workspace():
     n_h = 512 * hv * K * K * 4
     dvp = 512 * hv * 64 * K * 4
     dqk = 2 * rows * hv * K * 4
-    recompute = rows * hv * K * 2 + n_h + rows * hv * 64 * 4
+    recompute = rows * hv * K * 2 + n_h + rows * hv * 64 * 4 + dvp
     assert p["workspace_bytes"] == n_h + dvp + dqk + recompute
     saved = G.bwd_plan(bdesc(T=32768, H_qk=4, H_v=16, saved_fwd=True))
     assert saved["workspace_bytes"] == n_h + dvp + dqk
@@ -222,9 +222,11 @@ def test_bwd_validation_happens_before_any_launch():
     # d_final_state given without has_dht
     d2 = bdesc(T=128, has_h0=True)
     assert lib.gdn_bwd(ctypes.byref(d2), ctypes.byref(mk()), ws, 1 << 12, None) == L.GDN_EINVAL
-    # h without A
+    # h without A and v_new
     d3 = bdesc(T=128, has_h0=True, has_dht=True, saved_fwd=True)
     assert lib.gdn_bwd(ctypes.byref(d3), ctypes.byref(mk(h=15 * base)), ws, 1 << 12, None) == L.GDN_EINVAL
+    assert lib.gdn_bwd(ctypes.byref(d3), ctypes.byref(mk(h=15 * base, A=16 * base)), ws, 1 << 12,
+                       None) == L.GDN_EINVAL
     # misaligned dO
     assert lib.gdn_bwd(ctypes.byref(d), ctypes.byref(mk(dO=7 * base + 2)), ws, 1 << 12, None) == L.GDN_EINVAL
     # dv overlapping v

@@ -106,9 +106,10 @@ def test_bwd_no_state_gradients_and_bf16_grads():
 def test_bwd_saved_tensors_match_recompute():
     w = dataclasses.replace(BASE, name="b5", seed=45, B=1, T=640, H_qk=1, H_v=4)
     x = _grad_inputs(w)
-    _, A, _, h, _ = chunk_gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
-                                               initial_state=x["initial_state"], cp="warmup", cp_segment_chunks=3)
-    saved = _run(x, h=h, A=A, cp="warmup", cp_segment_chunks=3, grad_dtype="f32")
+    _, A, _, h, _, vn = chunk_gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
+                                                   initial_state=x["initial_state"], cp="warmup", cp_segment_chunks=3,
+                                                   output_v_new=True)
+    saved = _run(x, h=h, A=A, v_new=vn, cp="warmup", cp_segment_chunks=3, grad_dtype="f32")
     fresh = _run(x, cp="warmup", cp_segment_chunks=3, grad_dtype="f32")
     for n, a, b in zip(NAMES, saved, fresh):
         assert torch.equal(a, b), n
@@ -130,12 +131,12 @@ def test_autograd_node_matches_backward_call():
 def test_bwd_full_workload_sampled_key_head():
     """The backward workload (1 x 32768 tokens, 4 key heads, 16 value heads,
     initial state, d final_state) in the benchmark's launch configuration
-    (CP auto, bf16 gradients as autograd returns them, h and A saved by the
-    forward); the oracle checks key head 2 and its four value heads."""
+    (CP auto, bf16 gradients as autograd returns them, h, A and v_new saved
+    by the forward); the oracle checks key head 2 and its four value heads."""
     x = W.make_inputs(BASE, device=DEV)
-    _, A, _, h, _ = chunk_gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
-                                               initial_state=x["initial_state"])
-    got = _run(x, h=h, A=A)
+    _, A, _, h, _, vn = chunk_gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
+                                                   initial_state=x["initial_state"], output_v_new=True)
+    got = _run(x, h=h, A=A, v_new=vn)
     i = 2
     sl = slice(4 * i, 4 * i + 4)
     xs = dict(q=x["q"][:, :, i:i + 1], k=x["k"][:, :, i:i + 1], v=x["v"][:, :, sl], g=x["g"][:, :, sl],

@@ -5,7 +5,10 @@ API": g, A, o, h, final_state) against the oracle's definitions:
   the exact paths (CP off / exact), <= 5e-3 under warm-up CP;
 * A (each chunk's WY matrix rows) vs oracle.chunk_wy_inverse: max-abs <= 1e-4
   (entries are O(1); the GPU inverts in fp32 with hi/lo bf16 MFMA merges);
-* g vs oracle.chunk_cumsum, o and final_state as in the main parity tests.
+* g vs oracle.chunk_cumsum, o and final_state as in the main parity tests;
+* v_new (each chunk's v' = U - W h, kept for the backward) vs the same
+  formula evaluated in fp64 from the oracle's h and A (whose composition the
+  oracle tests pin to the per-token recurrence): the bar of h.
 """
 import dataclasses
 
@@ -37,9 +40,10 @@ def _host(x):
 def _check(name, x, rel_h, **kw):
     q, k, v, g, b, h0, cu = _host(x)
     Hv = v.shape[2]
-    g_cum, A, o, h, ht = chunk_gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
-                                                    initial_state=x["initial_state"], cu_seqlens=x["cu_seqlens"],
-                                                    o_dtype="f32", **kw)
+    g_cum, A, o, h, ht, vn = chunk_gated_delta_rule_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"],
+                                                        scale=x["scale"], initial_state=x["initial_state"],
+                                                        cu_seqlens=x["cu_seqlens"], o_dtype="f32",
+                                                        output_v_new=True, **kw)
     torch.cuda.synchronize()
     o_ref, ht_ref = oracle.fwd(q, k, v, g, b, scale=x["scale"], initial_state=h0, cu_seqlens=cu)
     h_ref = oracle.chunk_states(q, k, v, g, b, scale=x["scale"], initial_state=h0, cu_seqlens=cu)
@@ -56,6 +60,32 @@ def _check(name, x, rel_h, **kw):
     assert eh <= rel_h and eo <= rel_h and et <= rel_h
     assert ea <= 1e-4
     assert eg <= 1e-4
+    vn_ref = _v_new_ref(k, v, g, b, h_ref, a_ref, cu)
+    ev = rel_l2(vn.cpu().numpy(), vn_ref)
+    print(f"[{name}] rel_l2(v_new)={ev:.3e}", flush=True)
+    assert ev <= rel_h
+
+
+def _v_new_ref(k, v, g, b, h_ref, a_ref, cu):
+    """v' = T diag(beta) V - T diag(beta gamma) K h per chunk (zero rows past a sequence end)."""
+    B, T, Hqk, K = k.shape
+    Hv, V = v.shape[2], v.shape[3]
+    seqs = [(bb, 0, T) for bb in range(B)] if cu is None else \
+        [(0, int(cu[n]), int(cu[n + 1] - cu[n])) for n in range(len(cu) - 1)]
+    out = np.zeros((h_ref.shape[0], Hv, 64, V))
+    idx = 0
+    for bb, t0, L in seqs:
+        for c in range((L + 63) // 64):
+            c0, c1 = t0 + 64 * c, min(t0 + 64 * c + 64, t0 + L)
+            m = c1 - c0
+            for j in range(Hv):
+                kc = k[bb, c0:c1, j // (Hv // Hqk)].astype(np.float64)
+                bc = b[bb, c0:c1, j].astype(np.float64)
+                gam = np.exp(np.cumsum(g[bb, c0:c1, j].astype(np.float64)))
+                Tm = a_ref[bb, c0:c1, j, :m]
+                out[idx + c, j, :m] = Tm @ (bc[:, None] * v[bb, c0:c1, j]) - Tm @ ((bc * gam)[:, None] * kc) @ h_ref[idx + c, j]
+        idx += (L + 63) // 64
+    return out
 
 
 def test_lowlevel_tiny():
