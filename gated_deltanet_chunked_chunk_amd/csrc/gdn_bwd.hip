@@ -66,15 +66,6 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float ldf(const float *p) { return *p; }
-__device__ __forceinline__ float ldf(const bf16 *p) { return (float)*p; }
-
-// Operand read modes.  CONTIG: k runs along the stored row (vector reads).
-// STRIDED: any strides (element reads).  TRANS: a bf16 LDS tile stored
-// [k][m or n] row-major, read with ds_read_b64_tr_b16: per 16 k-rows each lane
-// receives 4 consecutive k of its own column.
-enum { CONTIG = 0, STRIDED = 1, TRANS = 2 };
-
 // k slot e of lane group g inside a 32-wide k step.  A step that reads any
 // operand transposed uses the k order {4g..4g+3, 16+4g..16+4g+3} (what two
 // transposed 16-row reads deliver) for both operands; otherwise 8g..8g+7.
@@ -104,101 +95,6 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &
     }
     hi = __builtin_bit_cast(bf16x8, (u32x4{h[0], h[1], h[2], h[3]}));
     lo = __builtin_bit_cast(bf16x8, (u32x4{l[0], l[1], l[2], l[3]}));
-}
-
-// One operand fragment of a 32-wide k step at k0.  CONTIG / STRIDED: p points
-// at the operand's first row / column (element (r, k) at p[r ms + k ks]);
-// TRANS: element (r, k) at p[k ks + r] in LDS.  EXACT: bf16 values used as
-// one term (hi only); otherwise scaled by sk[k] (if given) and split.
-template <typename T, int MODE, bool PERM, bool EXACT, bool SCALED>
-__device__ __forceinline__ void operand(const T *p, int ms, int ks, int k0, int lane, const float *sk, bf16x8 &hi,
-                                        bf16x8 &lo) {
-    const int r = lane & 15, g = lane >> 4;
-    if constexpr (MODE == TRANS) {
-        static_assert(sizeof(T) == 2, "transposed reads are 16-bit");
-        const T *q = p + (k0 + (lane >> 2)) * ks + 4 * (lane & 3);
-        const bf16x4 x0 = tr4(q), x1 = tr4(q + 16 * ks);
-        const bf16x8 v = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        if constexpr (EXACT) {
-            hi = v;
-        } else {
-            float f[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = (float)v[e] * (SCALED ? sk[k0 + kpos(e, g, true)] : 1.f);
-            split8(f, hi, lo);
-        }
-    } else {
-        const T *q = p + r * ms;
-        if constexpr (EXACT) {
-            if constexpr (MODE == CONTIG && !PERM) {
-                hi = *reinterpret_cast<const bf16x8 *>(q + k0 + 8 * g);
-            } else if constexpr (MODE == CONTIG) {
-                const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(q + k0 + 4 * g);
-                const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(q + k0 + 16 + 4 * g);
-                hi = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) hi[e] = q[(k0 + kpos(e, g, PERM)) * ks];
-            }
-        } else {
-            float f[8];
-            if constexpr (MODE == CONTIG && sizeof(T) == 4) {
-                const int o0 = k0 + (PERM ? 4 * g : 8 * g), o1 = k0 + (PERM ? 16 + 4 * g : 8 * g + 4);
-                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(q + o0);
-                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(q + o1);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    f[e] = x0[e];
-                    f[4 + e] = x1[e];
-                }
-            } else if constexpr (MODE == CONTIG) {
-                const int o0 = k0 + (PERM ? 4 * g : 8 * g), o1 = k0 + (PERM ? 16 + 4 * g : 8 * g + 4);
-                const bf16x4 x0 = *reinterpret_cast<const bf16x4 *>(q + o0);
-                const bf16x4 x1 = *reinterpret_cast<const bf16x4 *>(q + o1);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    f[e] = (float)x0[e];
-                    f[4 + e] = (float)x1[e];
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] = ldf(q + (k0 + kpos(e, g, PERM)) * ks);
-            }
-            if constexpr (SCALED) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] *= sk[k0 + kpos(e, g, PERM)];
-            }
-            split8(f, hi, lo);
-        }
-    }
-}
-
-// acc += A (16 x KD) B (KD x 16) for one output tile, A(m, k) = a[m ams + k aks],
-// B(k, n) = b[k bks + n bns], operands read in modes AM / BM.  SA: A is scaled
-// by sa[k] along k (then split like an fp32 operand).  Exact bf16 operands
-// enter as one term, fp32 (or scaled) ones as hi + lo: hi*hi + lo*hi + hi*lo.
-// Every k step's operands are read before the first product (one memory
-// latency per tile, not one per k step).
-template <typename TA, int AM, typename TB, int BM, int KD, bool SA = false>
-__device__ __forceinline__ f32x4 mm16(f32x4 acc, const TA *a, int ams, int aks, const TB *b, int bns, int bks,
-                                      int lane, const float *sa = nullptr) {
-    constexpr bool PERM = AM == TRANS || BM == TRANS;
-    constexpr bool EA = sizeof(TA) == 2 && !SA;
-    constexpr bool EB = sizeof(TB) == 2;
-    constexpr int NS = KD / 32;
-    bf16x8 ah[NS], al[NS], bh[NS], bl[NS];
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-        operand<TA, AM, PERM, EA, SA>(a, AM == TRANS ? 0 : ams, aks, 32 * st, lane, sa, ah[st], al[st]);
-        operand<TB, BM, PERM, EB, false>(b, BM == TRANS ? 0 : bns, bks, 32 * st, lane, nullptr, bh[st], bl[st]);
-    }
-#pragma unroll
-    for (int st = 0; st < NS; ++st) {
-        acc = mfma(ah[st], bh[st], acc);
-        if constexpr (!EA) acc = mfma(al[st], bh[st], acc);
-        if constexpr (!EB) acc = mfma(ah[st], bl[st], acc);
-    }
-    return acc;
 }
 
 // sum over the 16 lanes that share l / 16 (one accumulator row group)
@@ -351,186 +247,6 @@ __device__ __forceinline__ float prefix64(float x, int lane) {
         if (lane >= off) x += y;
     }
     return x;
-}
-
-// ---------------------------------------------------------------- reverse pass
-struct __attribute__((aligned(16))) SmemDh {
-    bf16 k[CH * DK];     // K, row = token
-    bf16 q[CH * DK];     // Q
-    bf16 dO[CH * HVC];   // dO, this workgroup's 64 value columns
-    float t[CH * CH];    // T, row = token
-    float w[CH * DK];    // W
-    float p[CH * CH];    // P (masked, decayed)
-    float dvp[CH * HVC]; // dv'
-    float dh[DK * HVC];  // dh (key rows x this workgroup's value columns)
-    float G[CH], gam[CH], bg[CH], rl[CH];
-};
-static_assert(sizeof(SmemDh) <= 160 * 1024, "reverse-pass LDS over 160 KB");
-
-// One chunk's inputs of the reverse pass, in registers between load and store.
-struct ChunkDh {
-    Rows<DK * 2 / 16> k, q;
-    Rows<HVC * 2 / 16> dO;
-    Rows<CH * 4 / 16> t;
-    float g, b;
-};
-
-__device__ __forceinline__ void load_chunk_dh(ChunkDh &R, const BwdParams &p, const Where &e, int j, int half, int c,
-                                              int tid) {
-    const int iq = j / p.group;
-    const unsigned kstride = (unsigned)p.Hqk * DK * 2, vstride = (unsigned)p.Hv * DV * 2;
-    const unsigned astride = (unsigned)p.Hv * CH * 4, gstride = (unsigned)p.Hv * 4;
-    load_rows(R.k, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
-    load_rows(R.q, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
-    load_rows(R.dO, p.dO + (e.row0 * p.Hv + j) * DV + half * HVC, vstride, c, e.seq_len, tid);
-    load_rows(R.t, p.A + (e.row0 * p.Hv + j) * CH, astride, c, e.seq_len, tid);
-    R.g = R.b = 0.f;
-    if (tid < 64) {
-        const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(p.g + e.row0 * p.Hv + j, gstride, c, e.seq_len);
-        const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(p.beta + e.row0 * p.Hv + j, gstride, c, e.seq_len);
-        R.g = ld4(rg, (unsigned)tid * gstride);
-        R.b = ld4(rb, (unsigned)tid * gstride);
-    }
-}
-
-__device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int tid) {
-    store_rows(s.k, R.k, tid);
-    store_rows(s.q, R.q, tid);
-    store_rows(s.dO, R.dO, tid);
-    store_rows(s.t, R.t, tid);
-    if (tid < 64) {
-        const float G = prefix64(R.g, tid);
-        const float Gl = __shfl(G, 63, 64);
-        const float gam = __expf(G);
-        s.G[tid] = G;
-        s.gam[tid] = gam;
-        s.bg[tid] = R.b * gam;
-        s.rl[tid] = __expf(Gl - G);
-    }
-}
-
-// One workgroup per (segment, v-head, value half).  Walks the segment's chunks
-// last to first, carrying dh (K x 64 fp32) in LDS; first runs a warm-up over
-// the chunks after the segment when the segment does not end its sequence
-// (gate-driven window, as in the forward).  Stores, for each own chunk c, dh'
-// (the gradient with respect to the state after c) and dv'.
-__global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    SmemDh &s = *reinterpret_cast<SmemDh *>(smem_raw);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int seg = blockIdx.x / (2 * p.Hv);
-    const int rem = blockIdx.x - seg * 2 * p.Hv;
-    const int j = rem >> 1, half = rem & 1;
-    if (seg >= p.num_segments) return;
-    const Where e = find_segment(p.cu, p.N, p.T, p.L, seg, lane);
-    if (e.n < 0) return;
-    const int nt = seq_chunks(e.seq_len);
-    const int c_end = e.c_begin + e.c_count;
-
-    // where the reverse walk starts: the sequence end (from d final_state) or
-    // a warm-up window after the segment (from zero)
-    int c_last = c_end;
-    if (!e.last && p.cp_mode == 2 /* WARMUP */) {
-        float acc = 0.f;
-        int w = 0;
-        while (w < p.warmup_cap && c_last < nt) {
-            const int tok = c_last * CH + lane;
-            float gv = 0.f;
-            if (tok < e.seq_len) gv = p.g[(e.row0 + tok) * p.Hv + j];
-            gv = sum64(gv);
-            acc += __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gv)));
-            ++c_last;
-            ++w;
-            if (acc <= kLnNoiseFloor) break;
-        }
-    } else {
-        c_last = nt;
-    }
-    const bool from_end = (c_last == nt);
-
-    // dh at the start of the walk
-    const int64_t sbase = ((int64_t)e.n * p.Hv + j) * DK * DV + half * HVC;
-    for (int x = tid; x < DK * HVC / 4; x += NT) {
-        const int d = x / (HVC / 4), v4 = x - d * (HVC / 4);
-        f32x4 val = f32x4{};
-        if (from_end && p.dht) val = *reinterpret_cast<const f32x4 *>(p.dht + sbase + (int64_t)d * DV + 4 * v4);
-        *reinterpret_cast<f32x4 *>(&s.dh[d * HVC + 4 * v4]) = val;
-    }
-    const int cbase = seq_chunk_base(p.cu, p.T, e.n, lane);
-    const int g16 = lane >> 4, c16 = lane & 15;
-
-    ChunkDh R;
-    if (c_last - 1 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c_last - 1, tid);
-    for (int c = c_last - 1; c >= e.c_begin; --c) {
-        const bool own = c < c_end;
-        __syncthreads();  // previous chunk's dh update done; tiles free
-        store_chunk_dh(s, R, tid);
-        if (c - 1 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c - 1, tid);  // next chunk's inputs in flight
-        __syncthreads();
-        const float gl = s.gam[CH - 1];
-
-        // W = T diag(beta gamma) K: wave w -> value... key columns 16 w .. +15, all rows
-        for (int rt = 0; rt < 4; ++rt) {
-            f32x4 acc = mm16<float, CONTIG, bf16, TRANS, CH, true>(f32x4{}, s.t + 16 * rt * CH, CH, 1, s.k + 16 * wave, 1, DK, lane, s.bg);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) s.w[(16 * rt + 4 * g16 + jj) * DK + 16 * wave + c16] = acc[jj];
-        }
-        // P = (Q K^T) o Gamma, s <= i: wave w -> row tile w / 2, column tiles 2 (w % 2) + {0, 1}
-        for (int ct2 = 0; ct2 < 2; ++ct2) {
-            const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
-            f32x4 acc = mm16<bf16, CONTIG, bf16, CONTIG, DK>(f32x4{}, s.q + 16 * rt * DK, DK, 1, s.k + 16 * ct * DK, DK, 1, lane);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int i = 16 * rt + 4 * g16 + jj, sc = 16 * ct + c16;
-                s.p[i * CH + sc] = sc <= i ? acc[jj] * __expf(s.G[i] - s.G[sc]) : 0.f;
-            }
-        }
-        // dh' of chunk c (unchanged so far in this step) -> HBM
-        if (own) {
-            float *dst = p.dh_ws + ((int64_t)(cbase + c) * p.Hv + j) * DK * DV + half * HVC;
-            for (int x = tid; x < DK * HVC / 4; x += NT) {
-                const int d = x / (HVC / 4), v4 = x - d * (HVC / 4);
-                *reinterpret_cast<f32x4 *>(dst + (int64_t)d * DV + 4 * v4) =
-                    *reinterpret_cast<const f32x4 *>(&s.dh[d * HVC + 4 * v4]);
-            }
-        }
-        __syncthreads();
-
-        // dv' = scale P^T dO + diag(rl) K dh: wave w -> row tile w / 2, column tiles 2 (w % 2) + {0, 1}
-        for (int ct2 = 0; ct2 < 2; ++ct2) {
-            const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
-            f32x4 a1 = mm16<float, STRIDED, bf16, TRANS, CH>(f32x4{}, s.p + 16 * rt, 1, CH, s.dO + 16 * ct, 1, HVC, lane);
-            f32x4 a2 = mm16<bf16, CONTIG, float, STRIDED, DK>(f32x4{}, s.k + 16 * rt * DK, DK, 1, s.dh + 16 * ct, 1, HVC, lane);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int i = 16 * rt + 4 * g16 + jj, v = 16 * ct + c16;
-                const float x = p.scale * a1[jj] + s.rl[i] * a2[jj];
-                s.dvp[i * HVC + v] = x;
-                if (own) p.dvp_ws[(((int64_t)(cbase + c) * p.Hv + j) * CH + i) * DV + half * HVC + v] = x;
-            }
-        }
-        __syncthreads();
-
-        // dh <- gamma_last dh + scale (diag(gamma) Q)^T dO - W^T dv': wave w -> key rows 16 w .. +15
-        for (int ct = 0; ct < 4; ++ct) {
-            f32x4 a1 = mm16<bf16, TRANS, bf16, TRANS, CH, true>(f32x4{}, s.q + 16 * wave, 1, DK, s.dO + 16 * ct, 1, HVC, lane, s.gam);
-            f32x4 a2 = mm16<float, STRIDED, float, STRIDED, CH>(f32x4{}, s.w + 16 * wave, 1, DK, s.dvp + 16 * ct, 1, HVC, lane);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int d = 16 * wave + 4 * g16 + jj, v = 16 * ct + c16;
-                s.dh[d * HVC + v] = gl * s.dh[d * HVC + v] + p.scale * a1[jj] - a2[jj];
-            }
-        }
-    }
-    __syncthreads();
-    if (e.c_begin == 0 && p.dh0) {
-        for (int x = tid; x < DK * HVC / 4; x += NT) {
-            const int d = x / (HVC / 4), v4 = x - d * (HVC / 4);
-            *reinterpret_cast<f32x4 *>(p.dh0 + sbase + (int64_t)d * DV + 4 * v4) =
-                *reinterpret_cast<const f32x4 *>(&s.dh[d * HVC + 4 * v4]);
-        }
-    }
 }
 
 // ---------------------------------------------------------------- chunk-local gradients
@@ -1042,6 +758,259 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             p.dg[off] = x;
             p.dbeta[off] = db;
         }
+    }
+}
+
+// ---------------------------------------------------------------- reverse pass
+struct __attribute__((aligned(16))) SmemDh {
+    bf16 k[CH * LK], q[CH * LK];      // K, Q   [token][key dim]
+    bf16 dO[CH * L64];                // dO, this workgroup's 64 value columns
+    bf16 aH[CH * L64], aL[CH * L64];  // T diag(beta gamma), then dv'   [token][col]
+    bf16 wH[CH * LK], wL[CH * LK];    // W   [token][key dim]
+    bf16 pH[CH * L64], pL[CH * L64];  // P   [query token][key token]
+    bf16 hH[DK * L64], hL[DK * L64];  // dh  [key dim][value column]
+    float G[CH], gam[CH];
+};
+static_assert(sizeof(SmemDh) <= 160 * 1024, "reverse-pass LDS over 160 KB");
+
+// One chunk's inputs of the reverse pass, in registers between load and store.
+struct ChunkDh {
+    Rows<DK * 2 / 16> k, q;
+    Rows<HVC * 2 / 16> dO;
+    Rows<CH * 4 / 16> t;
+    float g, b;  // lane l: token l (every wave)
+};
+
+__device__ __forceinline__ void load_chunk_dh(ChunkDh &R, const BwdParams &p, const Where &e, int j, int half, int c,
+                                              int tid) {
+    const int iq = j / p.group;
+    const unsigned kstride = (unsigned)p.Hqk * DK * 2, vstride = (unsigned)p.Hv * DV * 2;
+    const unsigned astride = (unsigned)p.Hv * CH * 4, gstride = (unsigned)p.Hv * 4;
+    load_rows(R.k, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
+    load_rows(R.q, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
+    load_rows(R.dO, p.dO + (e.row0 * p.Hv + j) * DV + half * HVC, vstride, c, e.seq_len, tid);
+    load_rows(R.t, p.A + (e.row0 * p.Hv + j) * CH, astride, c, e.seq_len, tid);
+    const int lane = tid & 63;
+    const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(p.g + e.row0 * p.Hv + j, gstride, c, e.seq_len);
+    const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(p.beta + e.row0 * p.Hv + j, gstride, c, e.seq_len);
+    R.g = ld4(rg, (unsigned)lane * gstride);
+    R.b = ld4(rb, (unsigned)lane * gstride);
+}
+
+// Tiles of one chunk into LDS: K, Q, dO as bf16; T with its columns scaled by
+// beta gamma as a hi / lo pair.  Every wave forms the gate prefix sums itself
+// (lane = token) for the column scales.
+__device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int tid) {
+    const int lane = tid & 63;
+    const float G = prefix64(R.g, lane);
+    const float gam = __expf(G);
+    const float bg = R.b * gam;
+    if (tid < 64) {
+        s.G[lane] = G;
+        s.gam[lane] = gam;
+    }
+    store_rows_ld(s.k, R.k, LK, tid);
+    store_rows_ld(s.q, R.q, LK, tid);
+    store_rows_ld(s.dO, R.dO, L64, tid);
+    constexpr int PPR = CH * 4 / 16;
+#pragma unroll
+    for (int i = 0; i < Rows<PPR>::PER; ++i) {
+        const int pc = tid + i * NT;
+        const int row = pc / PPR, col = 4 * (pc - row * PPR);
+        f32x4 x = __builtin_bit_cast(f32x4, R.t.x[i]);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) x[e2] *= __shfl(bg, col + e2, 64);
+        bf16x4 h, l;
+        split4(x, h, l);
+        *reinterpret_cast<bf16x4 *>(&s.aH[row * L64 + col]) = h;
+        *reinterpret_cast<bf16x4 *>(&s.aL[row * L64 + col]) = l;
+    }
+}
+
+// One workgroup per (segment, v-head, value half).  Walks the segment's chunks
+// last to first, carrying dh (K x 64 fp32) in registers -- wave w holds key
+// dims 16 w .. 16 w + 15 -- with a hi / lo copy in LDS for the K dh product;
+// first runs a warm-up over the chunks after the segment when the segment
+// does not end its sequence (gate-driven window, as in the forward).  Stores,
+// for each own chunk c, dh' (the gradient with respect to the state after c)
+// and dv'.
+__global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    SmemDh &s = *reinterpret_cast<SmemDh *>(smem_raw);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int seg = blockIdx.x / (2 * p.Hv);
+    const int rem = blockIdx.x - seg * 2 * p.Hv;
+    const int j = rem >> 1, half = rem & 1;
+    if (seg >= p.num_segments) return;
+    const Where e = find_segment(p.cu, p.N, p.T, p.L, seg, lane);
+    if (e.n < 0) return;
+    const int nt = seq_chunks(e.seq_len);
+    const int c_end = e.c_begin + e.c_count;
+    const int g4 = lane >> 4, r16 = lane & 15;
+
+    // where the reverse walk starts: the sequence end (from d final_state) or
+    // a warm-up window after the segment (from zero)
+    int c_last = c_end;
+    if (!e.last && p.cp_mode == 2 /* WARMUP */) {
+        float acc = 0.f;
+        int w = 0;
+        while (w < p.warmup_cap && c_last < nt) {
+            const int tok = c_last * CH + lane;
+            float gv = 0.f;
+            if (tok < e.seq_len) gv = p.g[(e.row0 + tok) * p.Hv + j];
+            gv = sum64(gv);
+            acc += __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gv)));
+            ++c_last;
+            ++w;
+            if (acc <= kLnNoiseFloor) break;
+        }
+    } else {
+        c_last = nt;
+    }
+    const bool from_end = (c_last == nt);
+
+    // dh at the start of the walk: rows 16 w + 4 g + jj, value column 16 ct + r
+    const int64_t sbase = ((int64_t)e.n * p.Hv + j) * DK * DV + half * HVC;
+    f32x4 dh[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            dh[ct][jj] = (from_end && p.dht) ? p.dht[sbase + (int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16]
+                                             : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) st_split(s.hH, s.hL, L64, 16 * wave, 16 * ct, dh[ct], lane);
+    const int cbase = seq_chunk_base(p.cu, p.T, e.n, lane);
+
+    ChunkDh R;
+    if (c_last - 1 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c_last - 1, tid);
+    for (int c = c_last - 1; c >= e.c_begin; --c) {
+        const bool own = c < c_end;
+        __syncthreads();  // previous chunk's products done; tiles free
+        store_chunk_dh(s, R, tid);
+        if (c - 1 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c - 1, tid);  // next chunk's inputs in flight
+        __syncthreads();
+        const float gl = s.gam[CH - 1];
+
+        // W = T diag(beta gamma) K: key columns 16 w .., all token rows
+        {
+            bf16x8 bk[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) bk[kk] = fr_tr(s.k + 16 * wave, LK, 32 * kk, lane);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f32x4 acc = f32x4{};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    acc = mm_pe(acc, fr_row<true>(s.aH + 16 * rt * L64, L64, 32 * kk, lane),
+                                fr_row<true>(s.aL + 16 * rt * L64, L64, 32 * kk, lane), bk[kk]);
+                st_split(s.wH, s.wL, LK, 16 * rt, 16 * wave, acc, lane);
+            }
+        }
+        // P = (Q K^T) o Gamma, s <= i: row tile w / 2, column tiles 2 (w % 2) + {0, 1}
+#pragma unroll
+        for (int ct2 = 0; ct2 < 2; ++ct2) {
+            const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                acc = mfma(fr_row<false>(s.q + 16 * rt * LK, LK, 32 * kk, lane),
+                           fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane), acc);
+            f32x4 pv;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int i = 16 * rt + 4 * g4 + jj, sc = 16 * ct + r16;
+                pv[jj] = sc <= i ? acc[jj] * __expf(s.G[i] - s.G[sc]) : 0.f;
+            }
+            st_split(s.pH, s.pL, L64, 16 * rt, 16 * ct, pv, lane);
+        }
+        // dh' of chunk c (unchanged so far in this step) -> HBM
+        if (own) {
+            float *dst = p.dh_ws + ((int64_t)(cbase + c) * p.Hv + j) * DK * DV + half * HVC;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    dst[(int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16] = dh[ct][jj];
+        }
+        __syncthreads();
+
+        // dv' = scale P^T dO + diag(rl) K dh: token row tile w / 2, value column tiles 2 (w % 2) + {0, 1};
+        // and this wave's key rows of Q^T diag(gamma) dO
+#pragma unroll
+        for (int ct2 = 0; ct2 < 2; ++ct2) {
+            const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
+            f32x4 a1 = f32x4{}, a2 = f32x4{};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                a1 = mm_pe(a1, fr_tr(s.pH + 16 * rt, L64, 32 * kk, lane), fr_tr(s.pL + 16 * rt, L64, 32 * kk, lane),
+                           fr_tr(s.dO + 16 * ct, L64, 32 * kk, lane));
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                a2 = mm_ep(a2, fr_row<true>(s.k + 16 * rt * LK, LK, 32 * kk, lane),
+                           fr_tr(s.hH + 16 * ct, L64, 32 * kk, lane), fr_tr(s.hL + 16 * ct, L64, 32 * kk, lane));
+            f32x4 x;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int i = 16 * rt + 4 * g4 + jj;
+                x[jj] = p.scale * a1[jj] + __expf(s.G[CH - 1] - s.G[i]) * a2[jj];
+            }
+            st_split(s.aH, s.aL, L64, 16 * rt, 16 * ct, x, lane);
+            if (own) {
+                float *dst = p.dvp_ws + ((int64_t)(cbase + c) * p.Hv + j) * CH * DV + half * HVC;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * rt + 4 * g4 + jj) * DV + 16 * ct + r16] = x[jj];
+            }
+        }
+        f32x4 u[4];
+        {
+            bf16x8 aq[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) aq[kk] = fr_tr(s.q + 16 * wave, LK, 32 * kk, lane);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                u[ct] = f32x4{};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8 d = fr_tr(s.dO + 16 * ct, L64, 32 * kk, lane);
+                    float f[8];
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; ++e2) f[e2] = (float)d[e2] * s.gam[32 * kk + kpos(e2, g4, true)];
+                    bf16x8 bh, bl;
+                    split8(f, bh, bl);
+                    u[ct] = mm_ep(u[ct], aq[kk], bh, bl);
+                }
+            }
+        }
+        __syncthreads();
+
+        // dh <- gamma_last dh + scale Q^T diag(gamma) dO - W^T dv'
+        {
+            bf16x8 awh[2], awl[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                awh[kk] = fr_tr(s.wH + 16 * wave, LK, 32 * kk, lane);
+                awl[kk] = fr_tr(s.wL + 16 * wave, LK, 32 * kk, lane);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                f32x4 acc = f32x4{};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    acc = mm_pp(acc, awh[kk], awl[kk], fr_tr(s.aH + 16 * ct, L64, 32 * kk, lane),
+                                fr_tr(s.aL + 16 * ct, L64, 32 * kk, lane));
+                dh[ct] = gl * dh[ct] + p.scale * u[ct] - acc;
+                st_split(s.hH, s.hL, L64, 16 * wave, 16 * ct, dh[ct], lane);
+            }
+        }
+    }
+    if (e.c_begin == 0 && p.dh0) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                p.dh0[sbase + (int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16] = dh[ct][jj];
     }
 }
 
