@@ -188,8 +188,9 @@ struct BwdPlan {
     Plan fwd;                 // the differentiated forward (validation, recompute)
     int32_t L = 1, num_segments = 0, cp_mode = GDN_CP_OFF, warmup = 0;
     int32_t entries = 0;      // chunk-local grid entries (chunks + one per empty sequence)
-    size_t off_o = 0, off_h = 0, off_a = 0, off_vn = 0;  // forward recompute (saved_fwd == 0 only)
+    size_t off_o = 0, off_h = 0, off_a = 0, off_vn = 0, off_fws = 0;  // forward recompute (saved_fwd == 0 only)
     size_t off_dh = 0, off_dvp = 0, off_dq = 0, off_dk = 0;
+    size_t off_cs = 0, off_cm = 0, off_ch = 0;  // exact CP: per-segment S, M, start gradient
     size_t workspace = 0;
 };
 
@@ -202,8 +203,6 @@ int make_bwd_plan(const gdn_bwd_desc *bd, BwdPlan *B) {
     if (rc != GDN_OK) return rc;
     if (bd->grad_dtype != GDN_DTYPE_BF16 && bd->grad_dtype != GDN_DTYPE_F32)
         return fail(GDN_EINVAL, "unknown grad_dtype %d", bd->grad_dtype);
-    if (d->cp_mode == GDN_CP_EXACT)
-        return fail(GDN_EUNSUPPORTED, "exact context parallelism is not built for the backward (use warmup, auto or off)");
     const Plan &P = B->fwd;
     int32_t L = std::max(1, P.max_chunks);
     int32_t mode = d->cp_mode;
@@ -226,7 +225,7 @@ int make_bwd_plan(const gdn_bwd_desc *bd, BwdPlan *B) {
             }
         }
         L = std::max(1, std::min(L, std::max(1, P.max_chunks)));
-        mode = GDN_CP_WARMUP;
+        if (mode == GDN_CP_AUTO) mode = GDN_CP_WARMUP;
         if (L >= P.max_chunks) mode = GDN_CP_OFF;
     }
     if (mode == GDN_CP_OFF) warmup = 0;
@@ -251,6 +250,8 @@ int make_bwd_plan(const gdn_bwd_desc *bd, BwdPlan *B) {
         off = align_up(off + rows * d->H_v * gdn::kChunk * 4);
         B->off_vn = off;
         off = align_up(off + (size_t)P.total_chunks * d->H_v * gdn::kChunk * d->V * 4);
+        B->off_fws = off;  // the forward's own workspace (exact CP: S, M, start states)
+        off = align_up(off + P.workspace);
     }
     B->off_dh = off;
     off = align_up(off + n_h * 4);
@@ -260,6 +261,15 @@ int make_bwd_plan(const gdn_bwd_desc *bd, BwdPlan *B) {
     off = align_up(off + rows * d->H_v * d->K * 4);
     B->off_dk = off;
     off = align_up(off + rows * d->H_v * d->K * 4);
+    if (mode == GDN_CP_EXACT) {
+        const size_t st = (size_t)B->num_segments * d->H_v * d->K * d->V * 4;
+        B->off_cs = off;
+        off = align_up(off + st);
+        B->off_cm = off;
+        off = align_up(off + st);
+        B->off_ch = off;
+        off = align_up(off + st);
+    }
     B->workspace = off;
     return GDN_OK;
 }
@@ -486,6 +496,13 @@ int gdn_bwd(const gdn_bwd_desc *bd, const gdn_bwd_ptrs *p, void *workspace, size
         fp.h_out = reinterpret_cast<float *>(ws + B.off_h);
         fp.a_out = reinterpret_cast<float *>(ws + B.off_a);
         fp.vn_out = reinterpret_cast<float *>(ws + B.off_vn);
+        if (P.cp_mode == GDN_CP_EXACT) {
+            fp.ws_s = reinterpret_cast<float *>(ws + B.off_fws);
+            fp.ws_m = reinterpret_cast<float *>(ws + B.off_fws + P.state_bytes);
+            fp.ws_h = reinterpret_cast<float *>(ws + B.off_fws + 2 * P.state_bytes);
+            const int e1 = gdn::launch_cp_exact(fp, stream);
+            if (e1) return fail(GDN_EHIP, "forward recompute pre-pass launch failed: %s", gdn::hip_error_text(e1));
+        }
         const int err = gdn::launch_fwd_main(fp, stream);
         if (err) return fail(GDN_EHIP, "forward recompute launch failed: %s", gdn::hip_error_text(err));
         h = fp.h_out;
@@ -526,6 +543,11 @@ int gdn_bwd(const gdn_bwd_desc *bd, const gdn_bwd_ptrs *p, void *workspace, size
     bp.cp_mode = B.cp_mode;
     bp.warmup_cap = B.warmup;
     bp.num_chunk_entries = B.entries;
+    if (B.cp_mode == GDN_CP_EXACT) {
+        bp.ws_s = reinterpret_cast<float *>(ws + B.off_cs);
+        bp.ws_m = reinterpret_cast<float *>(ws + B.off_cm);
+        bp.ws_h = reinterpret_cast<float *>(ws + B.off_ch);
+    }
     bp.grad_f32 = bd->grad_dtype == GDN_DTYPE_F32;
     bp.scale = d->scale;
     const int err = gdn::launch_bwd(bp, stream);

@@ -829,30 +829,41 @@ __device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int 
 
 // One workgroup per (segment, v-head, value half).  Walks the segment's chunks
 // last to first, carrying dh (K x 64 fp32) in registers -- wave w holds key
-// dims 16 w .. 16 w + 15 -- with a hi / lo copy in LDS for the K dh product;
-// first runs a warm-up over the chunks after the segment when the segment
-// does not end its sequence (gate-driven window, as in the forward).  Stores,
-// for each own chunk c, dh' (the gradient with respect to the state after c)
-// and dv'.
+// dims 16 w .. 16 w + 15 -- with a hi / lo copy in LDS for the K dh product.
+// Main pass (p.pass == 0): a segment that does not end its sequence starts
+// after a warm-up over the chunks that follow it (WARMUP, gate-driven window as
+// in the forward) or from its exact start gradient (EXACT, from the combine);
+// stores, for each own chunk c, dh' (the gradient with respect to the state
+// after c) and dv'.  Pre-pass (p.pass == 1, EXACT; two workgroups per
+// (segment, v-head, half)): for every segment that is not the first of its
+// sequence, the zero-start result S (which = 0) and the transition map M
+// (which = 1: the walk applied to the identity with the dO terms left out).
 __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     SmemDh &s = *reinterpret_cast<SmemDh *>(smem_raw);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int seg = blockIdx.x / (2 * p.Hv);
-    const int rem = blockIdx.x - seg * 2 * p.Hv;
-    const int j = rem >> 1, half = rem & 1;
+    const bool pre = p.pass == 1;
+    const int per = pre ? 4 * p.Hv : 2 * p.Hv;
+    const int seg = blockIdx.x / per;
+    const int rem = blockIdx.x - seg * per;
+    const int j = rem / (pre ? 4 : 2), half = rem & 1;
+    const bool mmap = pre && ((rem >> 1) & 1);  // pre-pass: transition map M
     if (seg >= p.num_segments) return;
     const Where e = find_segment(p.cu, p.N, p.T, p.L, seg, lane);
     if (e.n < 0) return;
+    if (pre && e.c_begin == 0) return;  // the first segment needs no map
     const int nt = seq_chunks(e.seq_len);
     const int c_end = e.c_begin + e.c_count;
     const int g4 = lane >> 4, r16 = lane & 15;
+    const bool exact_start = !pre && !e.last && p.cp_mode == 1 /* EXACT */;
 
-    // where the reverse walk starts: the sequence end (from d final_state) or
-    // a warm-up window after the segment (from zero)
+    // where the reverse walk starts: the sequence end (from d final_state), a
+    // warm-up window after the segment (from zero), or the segment end (EXACT)
     int c_last = c_end;
-    if (!e.last && p.cp_mode == 2 /* WARMUP */) {
+    if (pre || exact_start) {
+        c_last = c_end;
+    } else if (!e.last && p.cp_mode == 2 /* WARMUP */) {
         float acc = 0.f;
         int w = 0;
         while (w < p.warmup_cap && c_last < nt) {
@@ -868,17 +879,23 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
     } else {
         c_last = nt;
     }
-    const bool from_end = (c_last == nt);
+    const bool from_end = !pre && !exact_start && (c_last == nt);
 
     // dh at the start of the walk: rows 16 w + 4 g + jj, value column 16 ct + r
     const int64_t sbase = ((int64_t)e.n * p.Hv + j) * DK * DV + half * HVC;
+    const int64_t wbase = ((int64_t)seg * p.Hv + j) * DK * DV + half * HVC;  // exact-CP workspace
     f32x4 dh[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            dh[ct][jj] = (from_end && p.dht) ? p.dht[sbase + (int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16]
-                                             : 0.f;
+        for (int jj = 0; jj < 4; ++jj) {
+            const int d = 16 * wave + 4 * g4 + jj, v = 16 * ct + r16;
+            float x = 0.f;
+            if (from_end && p.dht) x = p.dht[sbase + (int64_t)d * DV + v];
+            if (exact_start) x = p.ws_h[wbase + (int64_t)d * DV + v];
+            if (mmap) x = (d == half * HVC + v) ? 1.f : 0.f;  // identity columns of this half
+            dh[ct][jj] = x;
+        }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) st_split(s.hH, s.hL, L64, 16 * wave, 16 * ct, dh[ct], lane);
     const int cbase = seq_chunk_base(p.cu, p.T, e.n, lane);
@@ -886,7 +903,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
     ChunkDh R;
     if (c_last - 1 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c_last - 1, tid);
     for (int c = c_last - 1; c >= e.c_begin; --c) {
-        const bool own = c < c_end;
+        const bool own = !pre && c < c_end;
         __syncthreads();  // previous chunk's products done; tiles free
         store_chunk_dh(s, R, tid);
         if (c - 1 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c - 1, tid);  // next chunk's inputs in flight
@@ -942,10 +959,12 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
         for (int ct2 = 0; ct2 < 2; ++ct2) {
             const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
             f32x4 a1 = f32x4{}, a2 = f32x4{};
+            if (!mmap) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                a1 = mm_pe(a1, fr_tr(s.pH + 16 * rt, L64, 32 * kk, lane), fr_tr(s.pL + 16 * rt, L64, 32 * kk, lane),
-                           fr_tr(s.dO + 16 * ct, L64, 32 * kk, lane));
+                for (int kk = 0; kk < 2; ++kk)
+                    a1 = mm_pe(a1, fr_tr(s.pH + 16 * rt, L64, 32 * kk, lane),
+                               fr_tr(s.pL + 16 * rt, L64, 32 * kk, lane), fr_tr(s.dO + 16 * ct, L64, 32 * kk, lane));
+            }
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 a2 = mm_ep(a2, fr_row<true>(s.k + 16 * rt * LK, LK, 32 * kk, lane),
@@ -963,14 +982,13 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
                 for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * rt + 4 * g4 + jj) * DV + 16 * ct + r16] = x[jj];
             }
         }
-        f32x4 u[4];
-        {
+        f32x4 u[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+        if (!mmap) {
             bf16x8 aq[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) aq[kk] = fr_tr(s.q + 16 * wave, LK, 32 * kk, lane);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
-                u[ct] = f32x4{};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) {
                     const bf16x8 d = fr_tr(s.dO + 16 * ct, L64, 32 * kk, lane);
@@ -1005,12 +1023,92 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
             }
         }
     }
-    if (e.c_begin == 0 && p.dh0) {
+    if (pre) {
+        float *dst = (mmap ? p.ws_m : p.ws_s) + wbase;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16] = dh[ct][jj];
+    } else if (e.c_begin == 0 && p.dh0) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
                 p.dh0[sbase + (int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16] = dh[ct][jj];
+    }
+}
+
+// Exact context parallelism, combine: per (sequence, v-head), from the end of
+// the sequence backwards, the gradient each segment starts from:
+// G_in(R-1) = d final_state (or 0), G_in(r) = M_{r+1} G_in(r+1) + S_{r+1}.
+// Wave w computes key rows 16 w .. +15 (eight value column tiles); M rows are
+// split from HBM, G_in is read as a hi / lo pair from LDS.
+struct __attribute__((aligned(16))) SmemComb {
+    bf16 gH[DK * LK], gL[DK * LK];  // G_in [key dim][value]
+};
+
+__global__ void __launch_bounds__(NT, 1) gdn_bwd_cp_combine_kernel(BwdParams p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    SmemComb &s = *reinterpret_cast<SmemComb *>(smem_raw);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, r16 = lane & 15;
+    const int n = blockIdx.x / p.Hv;
+    const int j = blockIdx.x - n * p.Hv;
+    if (n >= p.N) return;
+    int seg0 = 0, R = 0;
+    if (!p.cu) {
+        R = seq_segments(p.T, p.L);
+        seg0 = n * R;
+    } else {
+        int base = 0;
+        for (int n0 = 0; n0 < n; n0 += 64) {
+            const int nn = n0 + lane;
+            int cnt = (nn < n) ? seq_segments((int64_t)p.cu[nn + 1] - p.cu[nn], p.L) : 0;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+            base += __builtin_amdgcn_readfirstlane(cnt);
+        }
+        seg0 = base;
+        R = seq_segments((int64_t)p.cu[n + 1] - p.cu[n], p.L);
+    }
+    if (R <= 1) return;
+    f32x4 gin[8];
+    const int64_t sbase = ((int64_t)n * p.Hv + j) * DK * DV;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            gin[ct][jj] = p.dht ? p.dht[sbase + (int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16] : 0.f;
+    for (int r = R - 2; r >= 0; --r) {
+        __syncthreads();  // previous products done reading the pair
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) st_split(s.gH, s.gL, LK, 16 * wave, 16 * ct, gin[ct], lane);
+        __syncthreads();
+        const int64_t off = ((int64_t)(seg0 + r + 1) * p.Hv + j) * DK * DV;
+        const float *M = p.ws_m + off, *S = p.ws_s + off;
+        bf16x8 mh[4], ml[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            float raw[8];
+            fr_rowf<true>(M + 16 * wave * DK, DK, 32 * kk, lane, mh[kk], ml[kk], raw);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            f32x4 acc;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) acc[jj] = S[(int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                acc = mm_pp(acc, mh[kk], ml[kk], fr_tr(s.gH + 16 * ct, LK, 32 * kk, lane),
+                            fr_tr(s.gL + 16 * ct, LK, 32 * kk, lane));
+            gin[ct] = acc;
+        }
+        float *dst = p.ws_h + ((int64_t)(seg0 + r) * p.Hv + j) * DK * DV;
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16] = gin[ct][jj];
     }
 }
 
@@ -1055,9 +1153,26 @@ int launch_bwd(const BwdParams &p, void *stream) {
     err = hipFuncSetAttribute(reinterpret_cast<const void *>(bwdk::gdn_bwd_local_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(bwdk::SmemLoc));
     if (err != hipSuccess) return (int)err;
+    if (p.num_segments > 0 && p.cp_mode == 1 /* EXACT */ && p.rows > 0) {
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(bwdk::gdn_bwd_cp_combine_kernel),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(bwdk::SmemComb));
+        if (err != hipSuccess) return (int)err;
+        BwdParams pre = p;
+        pre.pass = 1;
+        hipLaunchKernelGGL(bwdk::gdn_bwd_dh_kernel, dim3((unsigned)(p.num_segments * p.Hv * 4)), dim3(bwdk::NT),
+                           sizeof(bwdk::SmemDh), st, pre);
+        err = hipGetLastError();
+        if (err != hipSuccess) return (int)err;
+        hipLaunchKernelGGL(bwdk::gdn_bwd_cp_combine_kernel, dim3((unsigned)(p.N * p.Hv)), dim3(bwdk::NT),
+                           sizeof(bwdk::SmemComb), st, p);
+        err = hipGetLastError();
+        if (err != hipSuccess) return (int)err;
+    }
     if (p.num_segments > 0) {
+        BwdParams mp = p;
+        mp.pass = 0;
         hipLaunchKernelGGL(bwdk::gdn_bwd_dh_kernel, dim3((unsigned)(p.num_segments * p.Hv * 2)), dim3(bwdk::NT),
-                           sizeof(bwdk::SmemDh), st, p);
+                           sizeof(bwdk::SmemDh), st, mp);
         err = hipGetLastError();
         if (err != hipSuccess) return (int)err;
     }

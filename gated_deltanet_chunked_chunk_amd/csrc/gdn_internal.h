@@ -80,6 +80,11 @@ struct BwdParams {
     int64_t T, rows;
     int32_t N, Hqk, Hv, group;
     int32_t num_segments, L, cp_mode, warmup_cap;  // reverse pass
+    // exact context parallelism of the reverse pass (workspace, each
+    // [num_segments][Hv][K][V] fp32): per-segment zero-start result S, transition
+    // map M (K x K), and the segment-end gradient each segment starts from
+    float *ws_s, *ws_m, *ws_h;
+    int32_t pass;                    // reverse-pass kernel: 0 main, 1 exact-CP pre-pass (S and M)
     int32_t num_chunk_entries;       // chunk-local grid: chunks of all sequences + one per empty sequence
     int32_t grad_f32;
     float scale;

@@ -178,9 +178,13 @@ int gdn_chunk_cumsum(const float *g, float *out, int64_t B, int64_t T, int32_t H
  * head sum the contributions of the value heads that share it; dg is the
  * gradient with respect to the per-token log-gates (not their cumsum).
  *
- * Context parallelism of the reverse pass: OFF, or WARMUP / AUTO with the
- * forward's window rule applied after each segment (the state gradient decays
- * with the same gates); EXACT is not built for the backward (GDN_EUNSUPPORTED).
+ * Context parallelism of the reverse pass, with the forward's segment rule:
+ * OFF; WARMUP / AUTO, a segment that does not end its sequence starts from zero
+ * after a warm-up over the chunks that follow it (the forward's gate window:
+ * the state gradient decays with the same gates); EXACT, a pre-pass computes
+ * each segment's zero-start result and transition map (K x K), a combine pass
+ * chains them from the sequence end, and every segment starts from its exact
+ * gradient.
  */
 typedef struct {
     gdn_fwd_desc fwd;     /* the forward call being differentiated (want_ht and o_dtype are ignored) */
@@ -196,7 +200,7 @@ typedef struct {
     int32_t segment_chunks;     /* L of the reverse pass */
     int32_t num_segments;       /* reverse-pass segments over all sequences (per v-head) */
     int32_t warmup_chunks;      /* window cap of the reverse pass, 0 when CP is off */
-    int32_t cp_mode;            /* resolved mode of the reverse pass (OFF or WARMUP) */
+    int32_t cp_mode;            /* resolved mode of the reverse pass (OFF, EXACT or WARMUP) */
     int32_t workgroups_reverse; /* reverse-pass workgroups = num_segments * H_v * 2 */
     int32_t workgroups_local;   /* per-chunk workgroups = (total_chunks + empty sequences) * H_v */
 } gdn_bwd_plan_info;

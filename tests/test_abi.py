@@ -189,11 +189,18 @@ def test_bwd_plan_layout_and_workspace():
     assert saved["workspace_bytes"] == n_h + dvp + dqk
     off = G.bwd_plan(bdesc(T=32768, H_qk=4, H_v=16, cp="off"))
     assert off["cp"] == "off" and off["num_segments"] == 1 and off["warmup_chunks"] == 0
+    # exact CP: three [segments][H_v][K][V] fp32 arrays for the reverse pass; when
+    # the forward is recomputed, the forward's own three as well
+    ex = G.bwd_plan(bdesc(T=32768, H_qk=4, H_v=16, cp="exact", cp_segment_chunks=64, saved_fwd=True))
+    st = 8 * hv * K * K * 4
+    assert ex["cp"] == "exact" and ex["num_segments"] == 8
+    assert ex["workspace_bytes"] == n_h + dvp + dqk + 3 * st
+    exr = G.bwd_plan(bdesc(T=32768, H_qk=4, H_v=16, cp="exact", cp_segment_chunks=64))
+    assert exr["workspace_bytes"] == n_h + dvp + dqk + 3 * st + recompute + 3 * st
 
 
 def test_bwd_plan_rejects():
-    for kw, st in ((dict(cp="exact"), L.GDN_EUNSUPPORTED), (dict(K=64), L.GDN_EUNSUPPORTED),
-                   (dict(H_v=3), L.GDN_EINVAL)):
+    for kw, st in ((dict(K=64), L.GDN_EUNSUPPORTED), (dict(H_v=3), L.GDN_EINVAL)):
         d = bdesc(**kw)
         assert L.lib().gdn_bwd_plan(ctypes.byref(d), None) == st
         assert L.lib().gdn_last_error()
