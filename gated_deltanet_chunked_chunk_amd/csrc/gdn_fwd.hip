@@ -136,8 +136,17 @@ struct Inputs {
     int seq_len;
 };
 
+// A buffer resource over [base, base + bytes).  Every caller passes values that
+// are the same in all lanes; taking them through readfirstlane lets the
+// compiler keep the resource in scalar registers instead of looping over the
+// distinct values of lanes it cannot prove equal.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, n,
+                                             0x00020000);
 }
 
 // Resource over chunk c's rows of a per-sequence tensor (no rows past the end).
@@ -546,28 +555,34 @@ __device__ __forceinline__ void store_state(const f32x16 (&t)[4], float *dst, co
 // lane l holds A row / B column l % 16 with the 8 k-slots 8 (l / 16) .. +7;
 // accumulator element j holds row 4 (l / 16) + j, column l % 16).  Two
 // accumulator tiles stacked along k read as one B operand see, in a 32-wide k
-// step, the k indices 4g..4g+3 and 16+4g..16+4g+3 (g = l / 16); A operands
-// that meet such a B use the same permutation.  Every A operand a state wave
-// reads from LDS (W, P, Q, K^T fragments) serves both of its column tiles, so
-// each shared tile is read by four waves per chunk.  Waves 4..7, the
-// preparation waves, hold no state: they run the chunk-local preparation of
-// the next chunk (products, inverse, W) in step with the state pass of the
-// current one, one barrier-separated step at a time.
+// step, the k indices 4g..4g+3 and 16+4g..16+4g+3 (g = l / 16), which is also
+// the order two transposing LDS reads (ds_read_b64_tr_b16) of 16 rows each
+// deliver; every operand of such a k step uses that order.  Every A operand a
+// state wave reads from LDS serves both of its column tiles, so each shared
+// tile is read by four waves per chunk.  Waves 4..7, the preparation waves,
+// hold no state: they load every chunk straight from HBM into LDS and run the
+// chunk-local preparation of the next chunk (gate scan, K K^T, inverse, W,
+// T diag(beta), P) in step with the state pass of the current one, one
+// barrier-separated step at a time, at a raised wave priority (their chain of
+// small dependent steps is the longer of the two).
 constexpr int NT8 = 512;
-constexpr int TS8 = 32 + 4;  // fp32 row stride of the transposed 32 x 32 diagonal blocks
+constexpr int TS8 = 32 + 4;    // fp32 row stride of the transposed 32 x 32 diagonal blocks
+constexpr int TILE = CH * DK;  // bf16 elements of one 64-token x 128 tile (K, Q and V alike)
+static_assert(DK == DV, "K, Q and V tiles share one layout");
 
 struct __attribute__((aligned(16))) Smem8 {
-    bf16 k[CH * KS];                  // K, row = token
-    bf16 q[CH * KS];                  // Q
-    bf16 kt[2][DK * CS];              // K^T, row = key dim (two chunks in flight)
-    bf16 vt[DV * CS];                 // V^T, row = value dim
+    bf16 k[2][TILE];                  // K by chunk parity (row = token, pieces swizzled)
+    bf16 q[2][TILE];                  // Q by chunk parity
+    bf16 v[TILE];                     // V of the state pass's next chunk
     float a[CH * AS];                 // A, inverted in place into T
     bf16x8 wf[4][4][64];              // -W as A fragments [row tile][k step][lane]
-    bf16x8 pf[2][2][6][64];           // P as A fragments [chunk parity][hi, lo][fragment][lane]
+    bf16x8 tf[2][6][64];              // T diag(beta) as A fragments [hi, lo][fragment][lane]
+    bf16x8 pf[2][6][64];              // scale P as A fragments [hi, lo][fragment][lane]
     // the two 32 x 32 diagonal blocks of A, then of T, transposed ([block][col][row])
     float tt[2][32 * TS8];
     float gam[2][CH], dec[2][CH];     // e^{G}, e^{G_last - G} (two chunks in flight)
-    float graw[CH], beta[CH], gcum[CH], bg[CH];
+    float graw[2][CH], braw[2][CH];   // g and beta as loaded, by chunk parity
+    float gcum[CH], bg[CH];
     float ep[CH], em[CH], rowa[CH];   // e^{G - G_31}, e^{G_31 - G}, beta e^{G - G_31}
 };
 static_assert(sizeof(Smem8) <= 160 * 1024, "one workgroup's LDS must fit a CU");
@@ -577,6 +592,8 @@ static_assert(sizeof(Smem8) <= 160 * 1024, "one workgroup's LDS must fit a CU");
 __device__ __forceinline__ int frag_rt(int f) { return f < 4 ? f : f - 2; }
 __device__ __forceinline__ int frag_ks(int f) { return f < 4 ? 0 : 1; }
 __device__ __forceinline__ int frag_of(int rt, int ks) { return ks == 0 ? rt : rt + 2; }
+// k slot e of lane group g in the transposed-read order
+__device__ __forceinline__ constexpr int kperm(int e, int g) { return (e & 3) + 4 * g + 16 * (e >> 2); }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -588,13 +605,83 @@ __device__ __forceinline__ void split_pair(const f32x4 &t0, const f32x4 &t1, bf1
     split8v(x, hi, lo);
 }
 
-// A-operand read matching split_pair's k order: row + base + 4g .. +3 and
-// row + base + 16 + 4g .. +3.
-__device__ __forceinline__ bf16x8 lds8_perm16(const bf16 *row, int base, int g) {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row + base + 4 * g);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(row + base + 16 + 4 * g);
+// ---- 64 x 128 bf16 tiles in LDS.  Row r (256 bytes) keeps its sixteen
+// 16-byte pieces in the order piece ^ swz(r): sixteen consecutive rows at one
+// piece (row-fragment reads) and eight aligned rows at one pair of pieces
+// (transposing reads) fall in distinct banks, while four rows stay 1 KB of
+// contiguous LDS, the footprint of one wave's direct load.
+__device__ __forceinline__ int swz(int r) { return (2 * r + (r >> 3)) & 15; }
+__device__ __forceinline__ int tix(int r, int c) { return r * DK + (((c >> 3) ^ swz(r)) << 3) + (c & 7); }
+
+__device__ __forceinline__ bf16x4 tr4(const bf16 *p) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// Fragment (r, k) = X[k0 + k][c0 + r] of a tile X (r = l % 16, k in the
+// transposed-read order): lane l reads four columns of row k0 + l / 4 and of
+// row k0 + 16 + l / 4, and each transposing read hands every lane its column.
+__device__ __forceinline__ bf16x8 frag_t(const bf16 *X, const int c0, const int k0, const int lane) {
+    const int r = k0 + (lane >> 2), c = c0 + 4 * (lane & 3);
+    const bf16x4 x0 = tr4(X + tix(r, c)), x1 = tr4(X + tix(r + 16, c));
+    return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+}
+
+// Row fragment X[r0 + l % 16][k0 + 8 (l / 16) .. +7]
+__device__ __forceinline__ bf16x8 frag_r(const bf16 *X, const int r0, const int k0, const int lane) {
+    return lds8(X + tix(r0 + (lane & 15), k0 + 8 * (lane >> 4)));
+}
+
+// The same rows at the transposed-read k order: k0 + 4g .. +3, k0 + 16 + 4g .. +3
+__device__ __forceinline__ bf16x8 frag_rp(const bf16 *X, const int r0, const int k0, const int lane) {
+    const int r = r0 + (lane & 15), g = lane >> 4;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(X + tix(r, k0 + 4 * g));
+    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(X + tix(r, k0 + 16 + 4 * g));
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
+
+// ---- direct HBM -> LDS loads (buffer_load ... lds: lane l of a wave writes
+// LDS bytes 16 l .. 16 l + 15, or 4 l .. 4 l + 3, past the wave-uniform base).
+// Rows beyond a chunk's buffer resource (past the sequence end) arrive as zeros.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Rows 4 i .. 4 i + 3 of a 64 x 128 bf16 tile: lane l fills LDS piece l % 16 of
+// row 4 i + l / 16, i.e. logical piece (l % 16) ^ swz(row).
+__device__ __forceinline__ void dma_rows(bf16 *tile, const __amdgpu_buffer_rsrc_t r, const unsigned stride, const int i,
+                                         const int lane) {
+    const int row = 4 * i + (lane >> 4);
+    const unsigned off = (unsigned)row * stride + 16u * (unsigned)((lane & 15) ^ swz(row));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + 4 * i * DK), 16, (int)off, 0, 0, 0);
+}
+
+// Preparation wave pw's quarter (rows 16 pw .. 16 pw + 15) of chunk c's tile.
+__device__ __forceinline__ void dma_tile(bf16 *tile, const char *base, const unsigned stride, const int c,
+                                         const int seq_len, const int pw, const int lane) {
+    const __amdgpu_buffer_rsrc_t r = chunk_rsrc(base, stride, c, seq_len);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_rows(tile, r, stride, 4 * pw + i, lane);
+}
+
+// g (preparation wave 0) and beta (wave 1) of chunk c, one token per lane.
+__device__ __forceinline__ void dma_gb(Smem8 &s, const Inputs &in, const int c, const int pw, const int lane) {
+    if (pw >= 2) return;
+    const __amdgpu_buffer_rsrc_t r = chunk_rsrc(pw == 0 ? in.g : in.b, in.gstride, c, in.seq_len);
+    float *dst = (pw == 0) ? s.graw[c & 1] : s.braw[c & 1];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, (int)((unsigned)lane * in.gstride), 0, 0, 0);
+}
+
+// This wave's direct loads have landed in LDS (vmcnt(0); other counters untouched).
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Workgroup barrier for LDS traffic: this wave's own LDS reads and writes are
+// complete (lgkmcnt(0)) when it arrives, but its direct HBM -> LDS loads may
+// still be in flight (a fenced barrier would wait for them too); the issuing
+// wave waits for those itself (dma_wait) before the barrier that publishes
+// them.  The memory clobber keeps the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Inclusive wave-wide prefix sum with DPP (row shifts inside each 16-lane row,
 // then row broadcasts across rows).
@@ -619,105 +706,22 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     return x;
 }
 
-// ---- staging of one chunk, by the preparation waves only (the state waves
-// keep their registers for the state).  Thread t' = t mod 256 holds rows
-// 4 rg .. +3, columns 8 cg .. +7 of K, V and Q, with cg = t' mod 8 +
-// 8 (t' / 128) and rg = (t' / 8) mod 16, so eight consecutive lanes cover one
-// 128-byte row segment; the first 64 threads also hold g and beta.  K goes to
-// LDS natural and transposed, V transposed, Q natural.
-// Every load is issued unconditionally: a piece that is not wanted (no next
-// chunk, a warm-up chunk's Q, threads past 64 for g and beta) gets an offset
-// beyond the buffer range and comes back as zeros without a memory access.
-// With no branch around them, the staging registers keep one allocation
-// across the loop, and no copy of in-flight load results (which would wait
-// for every outstanding memory operation) is ever needed.
-__device__ __forceinline__ void stage_coords(int t, int &rg, int &cg) {
-    const int tt = t & 255;
-    cg = (tt & 7) | ((tt >> 4) & 8);
-    rg = (tt >> 3) & 15;
-}
-
-struct Stage8 {
-    u32x4 k[4], v[4], q[4];
-    float g, b;
-};
-
-constexpr unsigned kOutOfRange = 0x80000000u;  // beyond every chunk's range (64 rows, below 2^31 bytes)
-
-__device__ __forceinline__ void load_chunk8(const Inputs &in, Stage8 &st, int c, bool need_q, int t, bool valid) {
-    int rg, cg;
-    stage_coords(t, rg, cg);
-    const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(in.k, in.kstride, c, in.seq_len);
-    const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(in.q, in.kstride, c, in.seq_len);
-    const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(in.v, in.vstride, c, in.seq_len);
-    const __amdgpu_buffer_rsrc_t rg_ = chunk_rsrc(in.g, in.gstride, c, in.seq_len);
-    const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(in.b, in.gstride, c, in.seq_len);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const unsigned row = (unsigned)(4 * rg + r);
-        const unsigned ok = valid ? row * in.kstride + 16u * cg : kOutOfRange;
-        const unsigned ov = valid ? row * in.vstride + 16u * cg : kOutOfRange;
-        const unsigned oq = (valid && need_q) ? row * in.kstride + 16u * cg : kOutOfRange;
-        st.k[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)ok, 0, 0);
-        st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)ov, 0, 0);
-        st.q[r] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)oq, 0, 0);
-    }
-    const int tt = t & 255;
-    const unsigned goff = (valid && tt < CH) ? (unsigned)tt * in.gstride : kOutOfRange;
-    st.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg_, (int)goff, 0, 0));
-    st.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)goff, 0, 0));
-}
-
-// Four rows x eight columns as eight packed column pieces (4 bf16 each)
-__device__ __forceinline__ void transpose4x8(const u32x4 (&x)[4], uint2 (&tr)[8]) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        tr[e] = make_uint2(half_of(x[0], e) | (half_of(x[1], e) << 16), half_of(x[2], e) | (half_of(x[3], e) << 16));
-}
-
-__device__ __forceinline__ void store_chunk8(Smem8 &s, const Stage8 &st, int t, int buf) {
-    int rg, cg;
-    stage_coords(t, rg, cg);
-    uint2 tr[8];
-    transpose4x8(st.k, tr);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4 *>(&s.k[(4 * rg + r) * KS + 8 * cg]) = st.k[r];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.kt[buf][(8 * cg + e) * CS + 4 * rg]) = tr[e];
-    transpose4x8(st.v, tr);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2 *>(&s.vt[(8 * cg + e) * CS + 4 * rg]) = tr[e];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) *reinterpret_cast<u32x4 *>(&s.q[(4 * rg + r) * KS + 8 * cg]) = st.q[r];
-    const int tt = t & 255;
-    if (tt < CH) {
-        s.graw[tt] = st.g;
-        s.beta[tt] = st.b;
-    }
-}
-
 // ---- preparation step 1 (waves 4..7, pw = wave - 4): the chunk's gate scan
 // and decay factors (every preparation wave forms them itself, lane = token,
 // and writes identical values to the shared arrays; each reads back only what
-// it wrote, so no barrier separates the scan from the products), then
-//   pw 0..2: one masked, beta-weighted K K^T 32 x 32 tile each ((0,0) (1,0)
-//            (1,1)) into s.a, the diagonal ones also transposed into s.tt;
-//   the causal decayed P as hi/lo A fragments of the ten non-zero 16 x 16
-//   tiles: pw 0 fragment 0, pw 1 fragment 4, pw 2 fragment 1, pw 3 fragments
-//   2, 3 and 5.
-// A P fragment (rt, ks) stacks the P^T = K Q^T tiles (s tile 2 ks, i tile rt)
-// and (2 ks + 1, rt); the accumulator of each tile is the fragment half.
-__device__ __forceinline__ void prod8(Smem8 &s, const int lane, const int pw, const bool out, const int buf) {
+// it wrote, so no barrier separates the scan from the products), then for
+// pw 0..2 one masked, beta-weighted K K^T 32 x 32 tile each ((0,0) (1,0)
+// (1,1)) into s.a, the diagonal ones also transposed into s.tt.
+__device__ __forceinline__ void prod9(Smem8 &s, const int lane, const int pw, const int buf) {
     const int m32 = lane & 31, h32 = lane >> 5;
-    const int m = lane & 15, g = lane >> 4;
     bool fact;
     {
-        const float x = wave_prefix_sum(s.graw[lane]);
+        const float x = wave_prefix_sum(s.graw[buf][lane]);
         const float glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
         const float gref = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
         const float gm = __expf(x);
         const float d = x - gref;
-        const float bt = s.beta[lane];
+        const float bt = s.braw[buf][lane];
         const float epv = __expf(d);
         s.gcum[lane] = x;
         s.gam[buf][lane] = gm;
@@ -728,113 +732,110 @@ __device__ __forceinline__ void prod8(Smem8 &s, const int lane, const int pw, co
         s.rowa[lane] = bt * epv;
         fact = __all(fabsf(d) < 80.f);  // the factored decays are finite
     }
-    if (pw < 3) {
-        const int rbi = (pw >= 1) ? 1 : 0, rbs = (pw == 2) ? 1 : 0;
-        f32x16 acck = {};
-        const bf16 *ra = &s.k[(32 * rbi + m32) * KS + 8 * h32];
-        const bf16 *rb = &s.k[(32 * rbs + m32) * KS + 8 * h32];
+    if (pw >= 3) return;
+    const bf16 *K = s.k[buf];
+    const int rbi = (pw >= 1) ? 1 : 0, rbs = (pw == 2) ? 1 : 0;
+    f32x16 acck = {};
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            bf16x8 xa[4], xb[4];
+    for (int k2 = 0; k2 < 2; ++k2) {
+        bf16x8 xa[4], xb[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                xa[kk] = lds8(ra + 16 * (4 * k2 + kk));
-                xb[kk] = lds8(rb + 16 * (4 * k2 + kk));
-            }
-            __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acck = mfma(xa[kk], xb[kk], acck);
+        for (int kk = 0; kk < 4; ++kk) {
+            const int col = 8 * h32 + 16 * (4 * k2 + kk);
+            xa[kk] = lds8(K + tix(32 * rbi + m32, col));
+            xb[kk] = lds8(K + tix(32 * rbs + m32, col));
         }
-        const int col = 32 * rbs + m32;
-        float v[16];
-        if (fact) {
-            const float cf = s.em[col];
+        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const f32x4 ra4 = *reinterpret_cast<const f32x4 *>(&s.rowa[32 * rbi + 8 * ii + 4 * h32]);
+        for (int kk = 0; kk < 4; ++kk) acck = mfma(xa[kk], xb[kk], acck);
+    }
+    const int col = 32 * rbs + m32;
+    float v[16];
+    if (fact) {
+        const float cf = s.em[col];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[4 * ii + j] = ra4[j] * cf * acck[4 * ii + j];
-            }
-        } else {
-            const float gs = s.gcum[col];
+        for (int ii = 0; ii < 4; ++ii) {
+            const f32x4 ra4 = *reinterpret_cast<const f32x4 *>(&s.rowa[32 * rbi + 8 * ii + 4 * h32]);
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[32 * rbi + 8 * ii + 4 * h32]);
-                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&s.beta[32 * rbi + 8 * ii + 4 * h32]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[4 * ii + j] = b4[j] * __expf(g4[j] - gs) * acck[4 * ii + j];
-            }
+            for (int j = 0; j < 4; ++j) v[4 * ii + j] = ra4[j] * cf * acck[4 * ii + j];
         }
+    } else {
+        const float gs = s.gcum[col];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = 32 * rbi + 8 * (e >> 2) + 4 * h32 + (e & 3);
-            v[e] = (col < row) ? v[e] : 0.f;
-            s.a[row * AS + col] = v[e];
-        }
-        if (rbi == rbs) {  // diagonal 32 x 32 block: also store it transposed
+        for (int ii = 0; ii < 4; ++ii) {
+            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[32 * rbi + 8 * ii + 4 * h32]);
+            const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&s.braw[buf][32 * rbi + 8 * ii + 4 * h32]);
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                *reinterpret_cast<f32x4 *>(&s.tt[rbi][m32 * TS8 + 8 * ii + 4 * h32]) =
-                    f32x4{v[4 * ii], v[4 * ii + 1], v[4 * ii + 2], v[4 * ii + 3]};
+            for (int j = 0; j < 4; ++j) v[4 * ii + j] = b4[j] * __expf(g4[j] - gs) * acck[4 * ii + j];
         }
     }
-    if (out) {
-        int pfr[3] = {-1, -1, -1};
-        if (pw == 0) pfr[0] = 0;
-        if (pw == 1) pfr[0] = 4;
-        if (pw == 2) pfr[0] = 1;
-        if (pw == 3) {
-            pfr[0] = 2;
-            pfr[1] = 3;
-            pfr[2] = 5;
-        }
 #pragma unroll
-        for (int pi = 0; pi < 3; ++pi) {
-            if (pfr[pi] < 0) continue;
-            const int rt = frag_rt(pfr[pi]), ks = frag_ks(pfr[pi]);
-            f32x4 accp[2] = {f32x4{}, f32x4{}};
+    for (int e = 0; e < 16; ++e) {
+        const int row = 32 * rbi + 8 * (e >> 2) + 4 * h32 + (e & 3);
+        v[e] = (col < row) ? v[e] : 0.f;
+        s.a[row * AS + col] = v[e];
+    }
+    if (rbi == rbs) {  // diagonal 32 x 32 block: also store it transposed
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int st = 2 * ks + half;
-                if (st > rt) continue;  // tile entirely above the diagonal
-                const bf16 *ra = &s.k[(16 * st + m) * KS + 8 * g];
-                const bf16 *rb = &s.q[(16 * rt + m) * KS + 8 * g];
-                bf16x8 xa[4], xb[4];
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) {
-                    xa[kk] = lds8(ra + 32 * kk);
-                    xb[kk] = lds8(rb + 32 * kk);
-                }
-                __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-                for (int kk = 0; kk < DK / 32; ++kk) accp[half] = mfma16(xa[kk], xb[kk], accp[half]);
-            }
-            const int i = 16 * rt + m;  // this lane's query row
-            float pv[8];
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int s0 = 32 * ks + 16 * half + 4 * g;  // key rows of this lane's 4 slots
-                if (fact) {
-                    const float cf = s.ep[i];
-                    const f32x4 e4 = *reinterpret_cast<const f32x4 *>(&s.em[s0]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) pv[4 * half + j] = (s0 + j <= i) ? cf * e4[j] * accp[half][j] : 0.f;
-                } else {
-                    const float gi = s.gcum[i];
-                    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[s0]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        pv[4 * half + j] = (s0 + j <= i) ? __expf(gi - g4[j]) * accp[half][j] : 0.f;
-                }
-            }
-            bf16x8 hi, lo;
-            split8v(pv, hi, lo);
-            s.pf[buf][0][pfr[pi]][lane] = hi;
-            s.pf[buf][1][pfr[pi]][lane] = lo;
-        }
+        for (int ii = 0; ii < 4; ++ii)
+            *reinterpret_cast<f32x4 *>(&s.tt[rbi][m32 * TS8 + 8 * ii + 4 * h32]) =
+                f32x4{v[4 * ii], v[4 * ii + 1], v[4 * ii + 2], v[4 * ii + 3]};
     }
 }
 
+// ---- preparation step 3, waves pw = 2 and 3 (the state pass has consumed the
+// previous chunk's P by then): scale * P, causal and decayed, as hi/lo A
+// fragments of its ten non-zero 16 x 16 tiles; pw 2 makes fragments 0, 1, 2
+// and pw 3 fragments 3, 4, 5.  A P fragment (rt, ks) stacks the P^T = K Q^T
+// tiles (s tile 2 ks, i tile rt) and (2 ks + 1, rt); the accumulator of each
+// tile is the fragment half.
+__device__ __forceinline__ void pfrag9(Smem8 &s, const int lane, const int pw, const int buf, const float scale) {
+    const int m = lane & 15, g = lane >> 4;
+    const bf16 *K = s.k[buf], *Q = s.q[buf];
+    const bool fact = __all(fabsf(s.gcum[lane] - s.gcum[31]) < 80.f);  // as in the gate scan
+#pragma unroll
+    for (int pi = 0; pi < 3; ++pi) {
+        const int f = 3 * (pw - 2) + pi;
+        const int rt = frag_rt(f), ks = frag_ks(f);
+        f32x4 accp[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int st = 2 * ks + half;
+            if (st > rt) continue;  // tile entirely above the diagonal
+            bf16x8 xa[4], xb[4];
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                xa[kk] = frag_r(K, 16 * st, 32 * kk, lane);
+                xb[kk] = frag_r(Q, 16 * rt, 32 * kk, lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+            for (int kk = 0; kk < DK / 32; ++kk) accp[half] = mfma16(xa[kk], xb[kk], accp[half]);
+        }
+        const int i = 16 * rt + m;  // this lane's query row
+        float pv[8];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int s0 = 32 * ks + 16 * half + 4 * g;  // key rows of this lane's 4 slots
+            if (fact) {
+                const float cf = scale * s.ep[i];
+                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(&s.em[s0]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) pv[4 * half + j] = (s0 + j <= i) ? cf * e4[j] * accp[half][j] : 0.f;
+            } else {
+                const float gi = s.gcum[i];
+                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[s0]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    pv[4 * half + j] = (s0 + j <= i) ? scale * __expf(gi - g4[j]) * accp[half][j] : 0.f;
+            }
+        }
+        bf16x8 hi, lo;
+        split8v(pv, hi, lo);
+        s.pf[0][f][lane] = hi;
+        s.pf[1][f][lane] = lo;
+    }
+}
 // ---- T = (I + A)^{-1} in place in s.a (row-major), with the diagonal 32 x 32
 // blocks also kept transposed in s.tt for the merges.
 // Level 0 (preparation wave pw: diagonal 16 x 16 block pw): forward
@@ -978,20 +979,40 @@ __device__ __forceinline__ void inv8_l2b(Smem8 &s, const int lane, const int pw,
     for (int j = 0; j < 4; ++j) s.a[(32 + 16 * r + 4 * g + j) * AS + 16 * cq + m] = -z[j];
 }
 
-// ---- -W A fragments (preparation wave pw: row tile rt = pw, all four key-dim
-// steps) from W^T = K^T (T diag(beta gamma))^T tiles.
-__device__ __forceinline__ void wfrag8(Smem8 &s, const int lane, const int pw, const int buf) {
+// ---- preparation step 6 (pw: row tile rt = pw): the -W A fragments of the row
+// tile, all four key-dim steps, from W^T = K^T (T diag(beta gamma))^T, and
+// its T diag(beta) hi/lo A fragments for U.  K^T comes from transposing reads
+// of K, so T is read at the transposed-read token order.
+__device__ __forceinline__ void wfrag9(Smem8 &s, const int lane, const int pw, const int buf) {
     const int m = lane & 15, g = lane >> 4;
     const int rt = pw;
     const int nks = (rt < 2) ? 1 : 2;  // T is lower triangular
+    const bf16 *K = s.k[buf];
     bf16x8 tw[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         if (ks >= nks) continue;
-        const float *tr = &s.a[(16 * rt + m) * AS + 32 * ks + 8 * g];
-        const float *bgp = &s.bg[32 * ks + 8 * g];
+        const int c0 = 32 * ks + 4 * g;
+        const float *tr = &s.a[(16 * rt + m) * AS];
+        const f32x4 t0 = *reinterpret_cast<const f32x4 *>(tr + c0);
+        const f32x4 t1 = *reinterpret_cast<const f32x4 *>(tr + c0 + 16);
+        const f32x4 bg0 = *reinterpret_cast<const f32x4 *>(&s.bg[c0]);
+        const f32x4 bg1 = *reinterpret_cast<const f32x4 *>(&s.bg[c0 + 16]);
+        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&s.braw[buf][c0]);
+        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&s.braw[buf][c0 + 16]);
+        float tb[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) tw[ks][e] = (bf16)(tr[e] * bgp[e]);
+        for (int e = 0; e < 4; ++e) {
+            tw[ks][e] = (bf16)(t0[e] * bg0[e]);
+            tw[ks][4 + e] = (bf16)(t1[e] * bg1[e]);
+            tb[e] = t0[e] * b0[e];
+            tb[4 + e] = t1[e] * b1[e];
+        }
+        bf16x8 hi, lo;
+        split8v(tb, hi, lo);
+        const int f = frag_of(rt, ks);
+        s.tf[0][f][lane] = hi;
+        s.tf[1][f][lane] = lo;
     }
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -1002,8 +1023,8 @@ __device__ __forceinline__ void wfrag8(Smem8 &s, const int lane, const int pw, c
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks >= nks) continue;
                 const int kk = 2 * k2 + f;
-                ka[f][ks][0] = lds8(&s.kt[buf][(32 * kk + m) * CS + 32 * ks + 8 * g]);
-                ka[f][ks][1] = lds8(&s.kt[buf][(32 * kk + 16 + m) * CS + 32 * ks + 8 * g]);
+                ka[f][ks][0] = frag_t(K, 32 * kk, 32 * ks, lane);
+                ka[f][ks][1] = frag_t(K, 32 * kk + 16, 32 * ks, lane);
             }
         __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
@@ -1023,52 +1044,30 @@ __device__ __forceinline__ void wfrag8(Smem8 &s, const int lane, const int pw, c
 }
 
 // ---- U = (T diag(beta)) V for state wave sw's 32 value columns (two column
-// tiles); the six T diag(beta) fragments are formed in registers (hi/lo).
-__device__ __forceinline__ void u8(const Smem8 &s, const int lane, const int sw, f32x4 (&u)[4][2]) {
-    const int m = lane & 15, g = lane >> 4;
-    bf16x8 vv[2][2];
+// tiles), from the prepared hi/lo fragments and transposing reads of V.
+__device__ __forceinline__ void u9(const Smem8 &s, const int lane, const int sw, f32x4 (&u)[4][2]) {
+    bf16x8 vv[2][2], th[6], tl[6];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int fks = 0; fks < 2; ++fks) vv[ct][fks] = lds8(&s.vt[(32 * sw + 16 * ct + m) * CS + 32 * fks + 8 * g]);
-    f32x4 bp[2][2];
+        for (int ks = 0; ks < 2; ++ks) vv[ct][ks] = frag_t(s.v, 32 * sw + 16 * ct, 32 * ks, lane);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        bp[ks][0] = *reinterpret_cast<const f32x4 *>(&s.beta[32 * ks + 8 * g]);
-        bp[ks][1] = *reinterpret_cast<const f32x4 *>(&s.beta[32 * ks + 8 * g + 4]);
+    for (int f = 0; f < 6; ++f) {
+        th[f] = s.tf[0][f][lane];
+        tl[f] = s.tf[1][f][lane];
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) u[rt][ct] = f32x4{};
 #pragma unroll
-    for (int f3 = 0; f3 < 2; ++f3) {  // three fragments per batch of T reads
-        f32x4 tr[3][2];
+    for (int f = 0; f < 6; ++f) {
+        const int rt = frag_rt(f), ks = frag_ks(f);
 #pragma unroll
-        for (int fq = 0; fq < 3; ++fq) {
-            const int f = 3 * f3 + fq;
-            const int rt = frag_rt(f), ks = frag_ks(f);
-            tr[fq][0] = *reinterpret_cast<const f32x4 *>(&s.a[(16 * rt + m) * AS + 32 * ks + 8 * g]);
-            tr[fq][1] = *reinterpret_cast<const f32x4 *>(&s.a[(16 * rt + m) * AS + 32 * ks + 8 * g + 4]);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-        for (int fq = 0; fq < 3; ++fq) {
-            const int f = 3 * f3 + fq;
-            const int rt = frag_rt(f), ks = frag_ks(f);
-            float tb[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                tb[e] = tr[fq][0][e] * bp[ks][0][e];
-                tb[4 + e] = tr[fq][1][e] * bp[ks][1][e];
-            }
-            bf16x8 th, tl;
-            split8v(tb, th, tl);
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                u[rt][ct] = mfma16(th, vv[ct][ks], u[rt][ct]);
-                u[rt][ct] = mfma16(tl, vv[ct][ks], u[rt][ct]);
-            }
+        for (int ct = 0; ct < 2; ++ct) {
+            u[rt][ct] = mfma16(th[f], vv[ct][ks], u[rt][ct]);
+            u[rt][ct] = mfma16(tl[f], vv[ct][ks], u[rt][ct]);
         }
     }
 }
@@ -1076,19 +1075,20 @@ __device__ __forceinline__ void u8(const Smem8 &s, const int lane, const int sw,
 // ---- state-wave pieces of the state pass (two column tiles each).  Every
 // piece issues all of its LDS operand reads in one batch before its first
 // MFMA, so the LDS latency is paid once per piece.
-// (diag(gamma) Q H)^T of a chunk from the state at its start, i.e. H^T Q^T
-// with the state split as the A operand and the Q fragments as the B operand:
-// qh[rt][ct] lane (m, g) holds value column 16 ct + 4 g + j (of this wave's 32)
-// of query row 16 rt + m.  It later accumulates (P v')^T in place, and each
-// lane then owns four consecutive output columns of one row.
-__device__ __forceinline__ void qh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int buf,
-                                   const int ln) {
-    const int m = ln & 15, g = ln >> 4;
+// (scale diag(gamma) Q H)^T of a chunk from the state at its start, i.e.
+// H^T Q^T with the state split as the A operand and the Q fragments as the B
+// operand: qh[rt][ct] lane (m, g) holds value column 16 ct + 4 g + j (of this
+// wave's 32) of query row 16 rt + m.  It later accumulates (scale P v')^T in
+// place, and each lane then owns four consecutive output columns of one row.
+__device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int buf,
+                                    const float scale, const int ln) {
+    const int m = ln & 15;
+    const bf16 *Q = s.q[buf];
     bf16x8 qa[4][4];  // [k step][row tile]
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) qa[kk][rt] = lds8_perm16(&s.q[(16 * rt + m) * KS], 32 * kk, g);
+        for (int rt = 0; rt < 4; ++rt) qa[kk][rt] = frag_rp(Q, 16 * rt, 32 * kk, ln);
     __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -1109,7 +1109,7 @@ __device__ __forceinline__ void qh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-        const float gm = s.gam[buf][16 * rt + m];  // this lane's query row
+        const float gm = scale * s.gam[buf][16 * rt + m];  // this lane's query row
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) qh[rt][ct] *= gm;
     }
@@ -1138,21 +1138,22 @@ __device__ __forceinline__ void wh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f
     }
 }
 
-// O^T = scale ((diag(gamma) Q H)^T + v'^T P^T) for the two column tiles:
+
+// O^T = (scale diag(gamma) Q H)^T + v'^T (scale P)^T for the two column tiles:
 // the split v' tiles serve as A operands and the P fragments as B operands.
 // Lane (m, g) then holds four consecutive value columns 16 ct + 4 g .. +3 of
 // query row 16 rt + m, stored as one 16-byte (fp32) or 8-byte (bf16) piece
 // through a buffer resource over the chunk's rows (rows past the sequence end
 // are dropped by the hardware range check).
-__device__ __forceinline__ void out8(const Smem8 &s, const FwdParams &p, const char *obase, const int seq_len,
-                                     const f32x4 (&vp)[4][2], f32x4 (&acc)[4][2], const int c, const int buf,
-                                     const int sw, const int ln) {
+__device__ __forceinline__ void out9(const Smem8 &s, const FwdParams &p, const char *obase, const int seq_len,
+                                     const f32x4 (&vp)[4][2], f32x4 (&acc)[4][2], const int c, const int sw,
+                                     const int ln) {
     const int m = ln & 15, g = ln >> 4;
     bf16x8 pa[6][2];  // the six P fragments, hi and lo
 #pragma unroll
     for (int f = 0; f < 6; ++f) {
-        pa[f][0] = s.pf[buf][0][f][ln];
-        pa[f][1] = s.pf[buf][1][f][ln];
+        pa[f][0] = s.pf[0][f][ln];
+        pa[f][1] = s.pf[1][f][ln];
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
@@ -1179,7 +1180,7 @@ __device__ __forceinline__ void out8(const Smem8 &s, const FwdParams &p, const c
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-            const f32x4 w = p.scale * acc[rt][ct];
+            const f32x4 w = acc[rt][ct];
             const unsigned off = (unsigned)(16 * rt + m) * rstride + (unsigned)(32 * sw + 16 * ct + 4 * g) * es;
             if (p.o_f32) {
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (int)off, 0, 0);
@@ -1191,14 +1192,15 @@ __device__ __forceinline__ void out8(const Smem8 &s, const FwdParams &p, const c
 }
 
 // H <- gamma_last H + K^T diag(gamma_last / gamma) v'
-__device__ __forceinline__ void hupd8(const Smem8 &s, f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int buf,
+__device__ __forceinline__ void hupd9(const Smem8 &s, f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int buf,
                                       const int ln) {
-    const int m = ln & 15, g = ln >> 4;
+    const int g = ln >> 4;
+    const bf16 *K = s.k[buf];
     bf16x8 ka[2][8];  // [token step][key-dim tile]
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) ka[ks][dt] = lds8_perm16(&s.kt[buf][(16 * dt + m) * CS], 32 * ks, g);
+        for (int dt = 0; dt < 8; ++dt) ka[ks][dt] = frag_t(K, 16 * dt, 32 * ks, ln);
     f32x4 d4[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) d4[rt] = *reinterpret_cast<const f32x4 *>(&s.dec[buf][16 * rt + 4 * g]);
@@ -1360,22 +1362,23 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
 
     // Iteration c runs the state pass of chunk c (state waves) in step with the
     // preparation of chunk c + 1 (preparation waves); c = c_first - 1 only
-    // prepares the first chunk.  K^T, the P fragments and the decays are
-    // double-buffered by chunk parity; U and Q H of the next chunk wait in the
-    // state waves' registers.
-    //   step  state waves                      preparation waves
-    //   top   store chunk c + 1 (all waves)
-    //   1     v' = U - W H                     gate scan, K K^T, P fragments
-    //   2     O = scale (gamma Q H + P v')     inverse level 0
-    //   3     H update                         inverse level 1
-    //   4a    Q H of chunk c + 1               inverse level 2 reads
-    //   4b    -                                inverse level 2 writes
-    //   5     U of chunk c + 1                 -W fragments of chunk c + 1
-    // Both roles run their own copy of the loop with the same seven barriers
-    // per iteration (a barrier counts arrivals, wherever they come from), so
-    // each role's registers are allocated for its own live values only.
-    // The preparation waves stage every chunk: its loads are issued in step 4a
-    // two chunks ahead and its tiles stored at the top of the iteration.
+    // prepares the first chunk.
+    //   step  state waves                        preparation waves
+    //   1     v' = U - W H                       gate scan, K K^T; load Q, g, beta of c + 2
+    //   2     O = scale (gamma Q H + P v')       inverse level 0; load V of c + 1
+    //   3     H update                           inverse level 1 (pw 0, 1), P (pw 2, 3)
+    //   4     scale gamma Q H of chunk c + 1;    inverse level 2 reads
+    //         load K of c + 2
+    //   5     -                                  inverse level 2 writes
+    //   6     -                                  -W and T diag(beta) fragments
+    // K and Q sit in LDS by chunk parity and V for one chunk; each load is
+    // issued once the step that last reads its slot is behind a barrier, and
+    // every wave waits for its own loads before the iteration's first barrier.
+    // K goes out from the state waves: a transposing LDS read is compiled with
+    // a wait for every direct load the wave has in flight, and the preparation
+    // waves read K transposed in step 6, two steps after the K slot frees up.  Both roles run their own copy of the loop with the same six
+    // barriers per iteration (a barrier counts arrivals, wherever they come
+    // from), so each role's registers are allocated for its own live values.
     if (state_wave) {
         // ---- state: value columns 32 wave .. +31
         f32x4 hacc[2][8];
@@ -1391,14 +1394,15 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
         }
         const int64_t oes = p.o_f32 ? 4 : 2;
         const char *obase = static_cast<const char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes;
-        f32x4 vp[4][2], qh[4][2];  // vp: U of the next chunk, then v' of this one
+        f32x4 vp[4][2], qh[4][2];  // vp: U, then v' of this chunk
         const int cbase = (p.h_out || p.vn_out) ? seq_chunk_base(p, e.n, lane) : 0;
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
             const bool chain = c >= c_first;  // state pass of chunk c
             const bool prep = c + 1 < c_end;  // preparation of chunk c + 1
             const bool out = c >= e.c_begin;  // chunk c produces output (not a warm-up chunk)
             const int b = c & 1, nb = (c + 1) & 1;
-            __syncthreads();
+            dma_wait();
+            lds_barrier();
             // A fresh opaque lane index per step keeps the compiler from
             // hoisting lane-derived LDS addresses out of their steps and
             // holding them all live at once.
@@ -1407,55 +1411,66 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
                 asm volatile("" : "+v"(t));
                 return t & 63;
             };
-            if (chain) wh8(s, hacc, vp, lane_now());
+            if (chain) {
+                u9(s, lane_now(), wave, vp);
+                wh8(s, hacc, vp, lane_now());
+            }
             if (chain && out && p.vn_out)
                 store_vn8(vp, p.vn_out + ((int64_t)(cbase + c) * p.Hv + j) * CH * DV, wave, lane_now());
-            __syncthreads();
-            if (chain && out) out8(s, p, obase, e.seq_len, vp, qh, c, b, wave, lane_now());
-            __syncthreads();
-            if (chain) hupd8(s, hacc, vp, b, lane_now());
-            __syncthreads();
+            lds_barrier();
+            if (chain && out) out9(s, p, obase, e.seq_len, vp, qh, c, wave, lane_now());
+            lds_barrier();
+            if (chain) hupd9(s, hacc, vp, b, lane_now());
+            lds_barrier();
+            if (c + 2 < c_end) dma_tile(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, lane_now());
             if (prep && c + 1 >= e.c_begin) {
-                qh8(s, hacc, qh, nb, lane_now());
+                qh9(s, hacc, qh, nb, p.scale, lane_now());
                 if (p.h_out) store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
             }
-            __syncthreads();
-            __syncthreads();
-            if (prep) u8(s, lane_now(), wave, vp);
-            __syncthreads();
+            lds_barrier();
+            lds_barrier();
         }
         if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
     } else {
+        __builtin_amdgcn_s_setprio(2);
         const int pw = wave - 4;
         const char *abase = p.a_out ? reinterpret_cast<const char *>(p.a_out + ((int64_t)e.row0 * p.Hv + j) * CH)
                                     : nullptr;
-        Stage8 st;
-        if (has_chunks) load_chunk8(in, st, c_first, c_first >= e.c_begin, threadIdx.x, true);
+        if (has_chunks) {
+            dma_tile(s.k[c_first & 1], in.k, in.kstride, c_first, e.seq_len, pw, lane);
+            if (c_first >= e.c_begin) dma_tile(s.q[c_first & 1], in.q, in.kstride, c_first, e.seq_len, pw, lane);
+            dma_gb(s, in, c_first, pw, lane);
+        }
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
             // opaque thread index, once per chunk: lane-derived LDS addresses
             // are recomputed inside the loop rather than hoisted
             int tid = threadIdx.x;
             asm volatile("" : "+v"(tid));
             const int ln = tid & 63;
-            const bool prep = c + 1 < c_end;  // preparation of chunk c + 1
+            const bool prep = c + 1 < c_end;   // preparation of chunk c + 1
+            const bool ahead = c + 2 < c_end;  // loads of chunk c + 2
             const int nb = (c + 1) & 1;
-            if (prep) store_chunk8(s, st, tid, nb);
-            __syncthreads();
-            if (prep) prod8(s, ln, pw, c + 1 >= e.c_begin, nb);
-            __syncthreads();
+            dma_wait();
+            lds_barrier();
+            if (ahead) {
+                if (c + 2 >= e.c_begin) dma_tile(s.q[c & 1], in.q, in.kstride, c + 2, e.seq_len, pw, ln);
+                dma_gb(s, in, c + 2, pw, ln);
+            }
+            if (prep) prod9(s, ln, pw, nb);
+            lds_barrier();
+            if (prep) dma_tile(s.v, in.v, in.vstride, c + 1, e.seq_len, pw, ln);
             if (prep) inv8_l0(s, ln, pw);
-            __syncthreads();
+            lds_barrier();
             if (prep && pw < 2) inv8_l1(s, ln, pw);
-            __syncthreads();
-            load_chunk8(in, st, c + 2, c + 2 >= e.c_begin, tid, c + 2 < c_end);
+            if (prep && pw >= 2 && c + 1 >= e.c_begin) pfrag9(s, ln, pw, nb, p.scale);
+            lds_barrier();
             L2Regs l2;
             if (prep) inv8_l2a(s, ln, pw, l2);
-            __syncthreads();
+            lds_barrier();
             if (prep) inv8_l2b(s, ln, pw, l2);
-            __syncthreads();
+            lds_barrier();
             if (prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, abase, e.seq_len, c + 1, pw, ln);
-            if (prep) wfrag8(s, ln, pw, nb);
-            __syncthreads();
+            if (prep) wfrag9(s, ln, pw, nb);
         }
     }
 }
