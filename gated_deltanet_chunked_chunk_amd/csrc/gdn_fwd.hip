@@ -580,6 +580,7 @@ struct __attribute__((aligned(16))) Smem8 {
     bf16x8 pf[2][6][64];              // scale P as A fragments [hi, lo][fragment][lane]
     // the two 32 x 32 diagonal blocks of A, then of T, transposed ([block][col][row])
     float tt[2][32 * TS8];
+    float tlo[32 * TS8];              // rows 32..63, columns 0..31 of T (inverse level 2)
     float gam[2][CH], dec[2][CH];     // e^{G}, e^{G_last - G} (two chunks in flight)
     float graw[2][CH], braw[2][CH];   // g and beta as loaded, by chunk parity
     float gcum[CH], bg[CH];
@@ -783,58 +784,57 @@ __device__ __forceinline__ void prod9(Smem8 &s, const int lane, const int pw, co
     }
 }
 
-// ---- preparation step 3, waves pw = 2 and 3 (the state pass has consumed the
-// previous chunk's P by then): scale * P, causal and decayed, as hi/lo A
-// fragments of its ten non-zero 16 x 16 tiles; pw 2 makes fragments 0, 1, 2
-// and pw 3 fragments 3, 4, 5.  A P fragment (rt, ks) stacks the P^T = K Q^T
+// ---- preparation: scale * P, causal and decayed, as the hi/lo A fragment f
+// of its non-zero 16 x 16 tiles.  A P fragment (rt, ks) stacks the P^T = K Q^T
 // tiles (s tile 2 ks, i tile rt) and (2 ks + 1, rt); the accumulator of each
-// tile is the fragment half.
-__device__ __forceinline__ void pfrag9(Smem8 &s, const int lane, const int pw, const int buf, const float scale) {
+// tile is the fragment half.  Written once the state pass has consumed the
+// previous chunk's P.
+__device__ __forceinline__ bool decays_factor(const Smem8 &s, const int lane) {
+    return __all(fabsf(s.gcum[lane] - s.gcum[31]) < 80.f);  // as in the gate scan
+}
+
+__device__ __forceinline__ void pfrag9(Smem8 &s, const int lane, const int f, const int buf, const float scale,
+                                       const bool fact) {
     const int m = lane & 15, g = lane >> 4;
     const bf16 *K = s.k[buf], *Q = s.q[buf];
-    const bool fact = __all(fabsf(s.gcum[lane] - s.gcum[31]) < 80.f);  // as in the gate scan
+    const int rt = frag_rt(f), ks = frag_ks(f);
+    f32x4 accp[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-    for (int pi = 0; pi < 3; ++pi) {
-        const int f = 3 * (pw - 2) + pi;
-        const int rt = frag_rt(f), ks = frag_ks(f);
-        f32x4 accp[2] = {f32x4{}, f32x4{}};
+    for (int half = 0; half < 2; ++half) {
+        const int st = 2 * ks + half;
+        if (st > rt) continue;  // tile entirely above the diagonal
+        bf16x8 xa[4], xb[4];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int st = 2 * ks + half;
-            if (st > rt) continue;  // tile entirely above the diagonal
-            bf16x8 xa[4], xb[4];
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) {
-                xa[kk] = frag_r(K, 16 * st, 32 * kk, lane);
-                xb[kk] = frag_r(Q, 16 * rt, 32 * kk, lane);
-            }
-            __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-            for (int kk = 0; kk < DK / 32; ++kk) accp[half] = mfma16(xa[kk], xb[kk], accp[half]);
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            xa[kk] = frag_r(K, 16 * st, 32 * kk, lane);
+            xb[kk] = frag_r(Q, 16 * rt, 32 * kk, lane);
         }
-        const int i = 16 * rt + m;  // this lane's query row
-        float pv[8];
+        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int s0 = 32 * ks + 16 * half + 4 * g;  // key rows of this lane's 4 slots
-            if (fact) {
-                const float cf = scale * s.ep[i];
-                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(&s.em[s0]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) pv[4 * half + j] = (s0 + j <= i) ? cf * e4[j] * accp[half][j] : 0.f;
-            } else {
-                const float gi = s.gcum[i];
-                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[s0]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    pv[4 * half + j] = (s0 + j <= i) ? scale * __expf(gi - g4[j]) * accp[half][j] : 0.f;
-            }
-        }
-        bf16x8 hi, lo;
-        split8v(pv, hi, lo);
-        s.pf[0][f][lane] = hi;
-        s.pf[1][f][lane] = lo;
+        for (int kk = 0; kk < DK / 32; ++kk) accp[half] = mfma16(xa[kk], xb[kk], accp[half]);
     }
+    const int i = 16 * rt + m;  // this lane's query row
+    float pv[8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int s0 = 32 * ks + 16 * half + 4 * g;  // key rows of this lane's 4 slots
+        if (fact) {
+            const float cf = scale * s.ep[i];
+            const f32x4 e4 = *reinterpret_cast<const f32x4 *>(&s.em[s0]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pv[4 * half + j] = (s0 + j <= i) ? cf * e4[j] * accp[half][j] : 0.f;
+        } else {
+            const float gi = s.gcum[i];
+            const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[s0]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                pv[4 * half + j] = (s0 + j <= i) ? scale * __expf(gi - g4[j]) * accp[half][j] : 0.f;
+        }
+    }
+    bf16x8 hi, lo;
+    split8v(pv, hi, lo);
+    s.pf[0][f][lane] = hi;
+    s.pf[1][f][lane] = lo;
 }
 // ---- T = (I + A)^{-1} in place in s.a (row-major), with the diagonal 32 x 32
 // blocks also kept transposed in s.tt for the merges.
@@ -922,8 +922,9 @@ __device__ __forceinline__ void inv8_l1(Smem8 &s, const int lane, const int blk)
 // lower-left 32 x 32 block each, pw = 2 r + cq):
 //   T_lo,hi = -T_lo,lo (A_lo,hi T_hi,hi)
 // Part a reads every operand (Y = A_lo,hi T_hi,hi[:, 16 cq ..] as two 16 x 16
-// tiles, and the T_lo,lo rows of this quadrant); part b, after a barrier,
-// writes the quadrant over A_lo,hi's storage.
+// tiles, and the T_lo,lo rows of this quadrant); part b writes the quadrant to
+// s.tlo, not over A_lo,hi, which the other waves' part a may still be reading,
+// so both parts run in one step.
 struct L2Regs {
     f32x4 y0, y1;
     bf16x8 th, tl;
@@ -976,70 +977,78 @@ __device__ __forceinline__ void inv8_l2b(Smem8 &s, const int lane, const int pw,
     z = mfma16(r2.th, yl, z);
     z = mfma16(r2.tl, yh, z);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s.a[(32 + 16 * r + 4 * g + j) * AS + 16 * cq + m] = -z[j];
+    for (int j = 0; j < 4; ++j) s.tlo[(16 * r + 4 * g + j) * TS8 + 16 * cq + m] = -z[j];
 }
 
-// ---- preparation step 6 (pw: row tile rt = pw): the -W A fragments of the row
-// tile, all four key-dim steps, from W^T = K^T (T diag(beta gamma))^T, and
-// its T diag(beta) hi/lo A fragments for U.  K^T comes from transposing reads
-// of K, so T is read at the transposed-read token order.
-__device__ __forceinline__ void wfrag9(Smem8 &s, const int lane, const int pw, const int buf) {
+// Four consecutive entries T[row][c0 .. c0 + 3] (c0 a multiple of 4): the
+// lower-left 32 x 32 block of T sits in s.tlo, the rest in s.a.
+__device__ __forceinline__ f32x4 trow4(const Smem8 &s, const int row, const int c0) {
+    const float *p = (row >= 32 && c0 < 32) ? &s.tlo[(row - 32) * TS8 + c0] : &s.a[row * AS + c0];
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+
+// ---- preparation: for the row tiles rt0 and rt0 + 1, the -W A fragments of
+// key-dim step kk (W^T = K^T (T diag(beta gamma))^T, two 16-row halves), and
+// the T diag(beta) hi/lo A fragment tf_frag of those rows for U (-1: none).
+// K^T comes from transposing reads of K, so T is read at the transposed-read
+// token order.  Rows 0..31 of T are final after inverse level 1, rows 32..63
+// after level 2.
+__device__ __forceinline__ void wfrag9(Smem8 &s, const int lane, const int rt0, const int kk, const int tf_frag,
+                                       const int buf) {
     const int m = lane & 15, g = lane >> 4;
-    const int rt = pw;
-    const int nks = (rt < 2) ? 1 : 2;  // T is lower triangular
+    const int nks = (rt0 < 2) ? 1 : 2;  // T is lower triangular
     const bf16 *K = s.k[buf];
-    bf16x8 tw[2];
+    bf16x8 ka[2][2];  // [token step][key-dim half]
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         if (ks >= nks) continue;
-        const int c0 = 32 * ks + 4 * g;
-        const float *tr = &s.a[(16 * rt + m) * AS];
-        const f32x4 t0 = *reinterpret_cast<const f32x4 *>(tr + c0);
-        const f32x4 t1 = *reinterpret_cast<const f32x4 *>(tr + c0 + 16);
-        const f32x4 bg0 = *reinterpret_cast<const f32x4 *>(&s.bg[c0]);
-        const f32x4 bg1 = *reinterpret_cast<const f32x4 *>(&s.bg[c0 + 16]);
+        ka[ks][0] = frag_t(K, 32 * kk, 32 * ks, lane);
+        ka[ks][1] = frag_t(K, 32 * kk + 16, 32 * ks, lane);
+    }
+    bf16x8 tw[2][2];  // [row tile][token step]
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks >= nks) continue;
+            const int c0 = 32 * ks + 4 * g, row = 16 * (rt0 + r) + m;
+            const f32x4 t0 = trow4(s, row, c0), t1 = trow4(s, row, c0 + 16);
+            const f32x4 bg0 = *reinterpret_cast<const f32x4 *>(&s.bg[c0]);
+            const f32x4 bg1 = *reinterpret_cast<const f32x4 *>(&s.bg[c0 + 16]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                tw[r][ks][e] = (bf16)(t0[e] * bg0[e]);
+                tw[r][ks][4 + e] = (bf16)(t1[e] * bg1[e]);
+            }
+        }
+    if (tf_frag >= 0) {
+        const int rt = frag_rt(tf_frag), ks = frag_ks(tf_frag);
+        const int c0 = 32 * ks + 4 * g, row = 16 * rt + m;
+        const f32x4 t0 = trow4(s, row, c0), t1 = trow4(s, row, c0 + 16);
         const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&s.braw[buf][c0]);
         const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&s.braw[buf][c0 + 16]);
         float tb[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            tw[ks][e] = (bf16)(t0[e] * bg0[e]);
-            tw[ks][4 + e] = (bf16)(t1[e] * bg1[e]);
             tb[e] = t0[e] * b0[e];
             tb[4 + e] = t1[e] * b1[e];
         }
         bf16x8 hi, lo;
         split8v(tb, hi, lo);
-        const int f = frag_of(rt, ks);
-        s.tf[0][f][lane] = hi;
-        s.tf[1][f][lane] = lo;
+        s.tf[0][tf_frag][lane] = hi;
+        s.tf[1][tf_frag][lane] = lo;
     }
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-        bf16x8 ka[2][2][2];
+    for (int r = 0; r < 2; ++r) {
+        f32x4 w0 = {}, w1 = {};
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks >= nks) continue;
-                const int kk = 2 * k2 + f;
-                ka[f][ks][0] = frag_t(K, 32 * kk, 32 * ks, lane);
-                ka[f][ks][1] = frag_t(K, 32 * kk + 16, 32 * ks, lane);
-            }
-        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            const int kk = 2 * k2 + f;  // key-dim step of 32: W^T tiles dt = 2 kk and 2 kk + 1
-            f32x4 w0 = {}, w1 = {};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks >= nks) continue;
-                w0 = mfma16(ka[f][ks][0], tw[ks], w0);
-                w1 = mfma16(ka[f][ks][1], tw[ks], w1);
-            }
-            s.wf[rt][kk][lane] = bf16x8{(bf16)(-w0[0]), (bf16)(-w0[1]), (bf16)(-w0[2]), (bf16)(-w0[3]),
-                                        (bf16)(-w1[0]), (bf16)(-w1[1]), (bf16)(-w1[2]), (bf16)(-w1[3])};
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks >= nks) continue;
+            w0 = mfma16(ka[ks][0], tw[r][ks], w0);
+            w1 = mfma16(ka[ks][1], tw[r][ks], w1);
         }
+        s.wf[rt0 + r][kk][lane] = bf16x8{(bf16)(-w0[0]), (bf16)(-w0[1]), (bf16)(-w0[2]), (bf16)(-w0[3]),
+                                         (bf16)(-w1[0]), (bf16)(-w1[1]), (bf16)(-w1[2]), (bf16)(-w1[3])};
     }
 }
 
@@ -1077,11 +1086,11 @@ __device__ __forceinline__ void u9(const Smem8 &s, const int lane, const int sw,
 // MFMA, so the LDS latency is paid once per piece.
 // (scale diag(gamma) Q H)^T of a chunk from the state at its start, i.e.
 // H^T Q^T with the state split as the A operand and the Q fragments as the B
-// operand: qh[rt][ct] lane (m, g) holds value column 16 ct + 4 g + j (of this
-// wave's 32) of query row 16 rt + m.  It later accumulates (scale P v')^T in
+// operand, one column tile ct per call: qh[rt][ct] lane (m, g) holds value
+// column 16 ct + 4 g + j (of this wave's 32) of query row 16 rt + m.  It later accumulates (scale P v')^T in
 // place, and each lane then owns four consecutive output columns of one row.
-__device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int buf,
-                                    const float scale, const int ln) {
+__device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int ct,
+                                    const int buf, const float scale, const int ln) {
     const int m = ln & 15;
     const bf16 *Q = s.q[buf];
     bf16x8 qa[4][4];  // [k step][row tile]
@@ -1091,28 +1100,19 @@ __device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f
         for (int rt = 0; rt < 4; ++rt) qa[kk][rt] = frag_rp(Q, 16 * rt, 32 * kk, ln);
     __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] = f32x4{};
+    for (int rt = 0; rt < 4; ++rt) qh[rt][ct] = f32x4{};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 hh[2], hl[2];
+        bf16x8 hh, hl;
+        split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh, hl);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh[ct], hl[ct]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                qh[rt][ct] = mfma16(hh[ct], qa[kk][rt], qh[rt][ct]);
-                qh[rt][ct] = mfma16(hl[ct], qa[kk][rt], qh[rt][ct]);
-            }
+        for (int rt = 0; rt < 4; ++rt) {
+            qh[rt][ct] = mfma16(hh, qa[kk][rt], qh[rt][ct]);
+            qh[rt][ct] = mfma16(hl, qa[kk][rt], qh[rt][ct]);
+        }
     }
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const float gm = scale * s.gam[buf][16 * rt + m];  // this lane's query row
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] *= gm;
-    }
+    for (int rt = 0; rt < 4; ++rt) qh[rt][ct] *= scale * s.gam[buf][16 * rt + m];  // this lane's query row
 }
 
 // v' = U - W H (vp enters holding U)
@@ -1260,7 +1260,7 @@ __device__ __forceinline__ void store_t8(const Smem8 &s, const FwdParams &p, con
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int col = c0 + 4 * i;
-        f32x4 x = *reinterpret_cast<const f32x4 *>(&s.a[row * AS + col]);
+        f32x4 x = trow4(s, row, col);
         if (row < 32 && col >= 32) x = f32x4{};
         const unsigned off = (unsigned)row * rstride + (unsigned)col * 4u;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), ra, (int)off, 0, 0);
@@ -1366,19 +1366,19 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
     //   step  state waves                        preparation waves
     //   1     v' = U - W H                       gate scan, K K^T; load Q, g, beta of c + 2
     //   2     O = scale (gamma Q H + P v')       inverse level 0; load V of c + 1
-    //   3     H update                           inverse level 1 (pw 0, 1), P (pw 2, 3)
-    //   4     scale gamma Q H of chunk c + 1;    inverse level 2 reads
-    //         load K of c + 2
-    //   5     -                                  inverse level 2 writes
-    //   6     -                                  -W and T diag(beta) fragments
+    //   3     H update                           inverse level 1 (pw 0, 1), P
+    //   4     scale gamma Q H of chunk c + 1,    inverse level 2; W, T diag(beta),
+    //         column tile 0; load K of c + 2     rows 0..31
+    //   5     the same, column tile 1            W, T diag(beta), rows 32..63
     // K and Q sit in LDS by chunk parity and V for one chunk; each load is
     // issued once the step that last reads its slot is behind a barrier, and
     // every wave waits for its own loads before the iteration's first barrier.
     // K goes out from the state waves: a transposing LDS read is compiled with
     // a wait for every direct load the wave has in flight, and the preparation
-    // waves read K transposed in step 6, two steps after the K slot frees up.  Both roles run their own copy of the loop with the same six
-    // barriers per iteration (a barrier counts arrivals, wherever they come
-    // from), so each role's registers are allocated for its own live values.
+    // waves read K transposed right after the K slot frees up.  Both roles run
+    // their own copy of the loop with the same five barriers per iteration (a
+    // barrier counts arrivals, wherever they come from), so each role's
+    // registers are allocated for its own live values.
     if (state_wave) {
         // ---- state: value columns 32 wave .. +31
         f32x4 hacc[2][8];
@@ -1423,12 +1423,12 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             if (chain) hupd9(s, hacc, vp, b, lane_now());
             lds_barrier();
             if (c + 2 < c_end) dma_tile(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, lane_now());
+            if (prep && c + 1 >= e.c_begin) qh9(s, hacc, qh, 0, nb, p.scale, lane_now());
+            lds_barrier();
             if (prep && c + 1 >= e.c_begin) {
-                qh9(s, hacc, qh, nb, p.scale, lane_now());
+                qh9(s, hacc, qh, 1, nb, p.scale, lane_now());
                 if (p.h_out) store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
             }
-            lds_barrier();
-            lds_barrier();
         }
         if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
     } else {
@@ -1461,16 +1461,26 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             if (prep) dma_tile(s.v, in.v, in.vstride, c + 1, e.seq_len, pw, ln);
             if (prep) inv8_l0(s, ln, pw);
             lds_barrier();
-            if (prep && pw < 2) inv8_l1(s, ln, pw);
-            if (prep && pw >= 2 && c + 1 >= e.c_begin) pfrag9(s, ln, pw, nb, p.scale);
+            const bool pout = prep && c + 1 >= e.c_begin;  // chunk c + 1 produces output: P needed
+            if (prep && pw < 2) {
+                inv8_l1(s, ln, pw);
+                if (pout) pfrag9(s, ln, pw + 1, nb, p.scale, decays_factor(s, ln));  // fragments 1, 2
+            }
+            if (pout && pw >= 2) {
+                const bool fact = decays_factor(s, ln);
+                pfrag9(s, ln, pw == 2 ? 5 : 3, nb, p.scale, fact);
+                pfrag9(s, ln, pw == 2 ? 0 : 4, nb, p.scale, fact);
+            }
             lds_barrier();
-            L2Regs l2;
-            if (prep) inv8_l2a(s, ln, pw, l2);
-            lds_barrier();
-            if (prep) inv8_l2b(s, ln, pw, l2);
+            if (prep) {
+                L2Regs l2;
+                inv8_l2a(s, ln, pw, l2);
+                inv8_l2b(s, ln, pw, l2);
+            }
+            if (prep) wfrag9(s, ln, 0, pw, pw < 2 ? pw : -1, nb);  // rows 0..31, final since level 1
             lds_barrier();
             if (prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, abase, e.seq_len, c + 1, pw, ln);
-            if (prep) wfrag9(s, ln, pw, nb);
+            if (prep) wfrag9(s, ln, 2, pw, 2 + pw, nb);  // rows 32..63
         }
     }
 }
