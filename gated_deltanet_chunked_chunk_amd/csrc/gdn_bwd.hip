@@ -97,23 +97,31 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &
     lo = __builtin_bit_cast(bf16x8, (u32x4{l[0], l[1], l[2], l[3]}));
 }
 
+// Cross-lane sums without the LDS crossbar.  A DPP row is 16 lanes: two quad
+// permutations, then the half-row and row mirrors leave the row's sum in every
+// lane of the row.  Across rows, v_permlane16_swap exchanges the odd rows of
+// one operand with the even rows of the other (rows 0+1 and 2+3 after an
+// add), v_permlane32_swap the upper half with the lower.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 // sum over the 16 lanes that share l / 16 (one accumulator row group)
 __device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 64);
+    x += dpp_row<0xb1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_row<0x4e>(x);   // quad_perm [2,3,0,1]
+    x += dpp_row<0x141>(x);  // row_half_mirror
+    x += dpp_row<0x140>(x);  // row_mirror
     return x;
 }
 // sum over the four lane groups l / 16 (lanes l % 16 equal)
 __device__ __forceinline__ float sum4g(float x) {
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    x = __int_as_float(a[0]) + __int_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(b[0]) + __int_as_float(b[1]);
 }
-__device__ __forceinline__ float sum64(float x) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-    return x;
-}
+__device__ __forceinline__ float sum64(float x) { return sum4g(sum16(x)); }
 
 // ---------------------------------------------------------------- rows of a chunk
 // Buffer resource over chunk c's rows of one sequence: rows past the sequence
@@ -240,12 +248,19 @@ __device__ __forceinline__ int seq_chunk_base(const int32_t *cu, int64_t T, int 
 
 // in-chunk gate vectors from the staged raw g (lane i = token i; wave 0 only):
 // G prefix sums, gamma, and the last-token ratios rl_i = e^{G_last - G_i}
-__device__ __forceinline__ float prefix64(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+// Inclusive prefix sum over the 64 lanes with DPP: row shifts inside each
+// 16-lane row, then the row broadcasts of lanes 15 and 31 into the rows after.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_scan(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float prefix64(float x) {
+    x += dpp_scan<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_scan<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_scan<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_scan<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_scan<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_scan<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
     return x;
 }
 
@@ -448,7 +463,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         store_rows_split(s.nH, s.nL, rn, LK, tid);
         store_rows_split(s.eH, s.eL, rd, LK, tid);
         if (tid < 64) {
-            const float G = prefix64(g, tid);
+            const float G = prefix64(g);
             s.G[tid] = G;
             s.gam[tid] = __expf(G);
             s.bt[tid] = b;
@@ -769,7 +784,7 @@ struct __attribute__((aligned(16))) SmemDh {
     bf16 wH[CH * LK], wL[CH * LK];    // W   [token][key dim]
     bf16 pH[CH * L64], pL[CH * L64];  // P   [query token][key token]
     bf16 hH[DK * L64], hL[DK * L64];  // dh  [key dim][value column]
-    float G[CH], gam[CH];
+    float G[CH], gam[CH], bg[CH];
 };
 static_assert(sizeof(SmemDh) <= 160 * 1024, "reverse-pass LDS over 160 KB");
 
@@ -802,13 +817,15 @@ __device__ __forceinline__ void load_chunk_dh(ChunkDh &R, const BwdParams &p, co
 // (lane = token) for the column scales.
 __device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int tid) {
     const int lane = tid & 63;
-    const float G = prefix64(R.g, lane);
+    const float G = prefix64(R.g);
     const float gam = __expf(G);
     const float bg = R.b * gam;
     if (tid < 64) {
         s.G[lane] = G;
         s.gam[lane] = gam;
     }
+    // every wave writes the same column scales and reads back only its own writes
+    s.bg[lane] = bg;
     store_rows_ld(s.k, R.k, LK, tid);
     store_rows_ld(s.q, R.q, LK, tid);
     store_rows_ld(s.dO, R.dO, L64, tid);
@@ -819,7 +836,7 @@ __device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int 
         const int row = pc / PPR, col = 4 * (pc - row * PPR);
         f32x4 x = __builtin_bit_cast(f32x4, R.t.x[i]);
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) x[e2] *= __shfl(bg, col + e2, 64);
+        for (int e2 = 0; e2 < 4; ++e2) x[e2] *= s.bg[col + e2];
         bf16x4 h, l;
         split4(x, h, l);
         *reinterpret_cast<bf16x4 *>(&s.aH[row * L64 + col]) = h;
