@@ -1592,15 +1592,88 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_cp_prepass_kernel(FwdParams p
 }
 
 // Combine (sequential over a sequence's segments): H_start[0] = initial state,
-// H_start[r+1] = M_r H_start[r] + S_r.  One workgroup per (sequence, v-head);
-// wave w owns value columns 32w..32w+31, M_r H on MFMA with hi/lo operands.
+// H_start[r+1] = M_r H_start[r] + S_r.  The value columns of H never mix, so
+// one workgroup of 4 waves takes one block of 32 value columns of one
+// (sequence, v-head): wave w computes rows 32 w .. 32 w + 31 of the block
+// (v_mfma_f32_32x32x16_bf16, M rows split hi + lo as the A operand, H as the
+// hi / lo B operand from LDS, stored transposed [column][key]).  Step r's
+// operands M_{r+1} rows and S_{r+1} are loaded into registers while step r
+// runs, so each step waits on the previous one's products, not on HBM.
+constexpr int CB_COLS = 32;            // value columns per combine workgroup
+constexpr int CB_LD = DK + 8;          // bf16 row stride of the transposed H block (272 B)
+
+struct CombRegs {
+    f32x4 m[8][2];   // this lane's M row (32 w + l % 32), k = 16 kk + 8 h .. +7
+    float x[16];     // S block entries (rows 32 w + 8 i + 4 h + j, column l % 32)
+};
+
+__device__ __forceinline__ void comb_load(CombRegs &R, const float *M, const float *S, const int wave, const int lane,
+                                          const int col0) {
+    const int m = lane & 31, h = lane >> 5;
+    const float *row = M + (int64_t)(32 * wave + m) * DK + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        R.m[kk][0] = *reinterpret_cast<const f32x4 *>(row + 16 * kk);
+        R.m[kk][1] = *reinterpret_cast<const f32x4 *>(row + 16 * kk + 4);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        R.x[e] = S[(int64_t)(32 * wave + 8 * (e >> 2) + 4 * h + (e & 3)) * DV + col0 + m];
+}
+
+// X (rows of this wave, the block's columns) = S + M H, H from LDS (hi / lo, transposed)
+__device__ __forceinline__ f32x16 comb_step(const CombRegs &R, const bf16 *hH, const bf16 *hL, const int lane) {
+    const int m = lane & 31, h = lane >> 5;
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = R.x[e];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const float av[8] = {R.m[kk][0][0], R.m[kk][0][1], R.m[kk][0][2], R.m[kk][0][3],
+                             R.m[kk][1][0], R.m[kk][1][1], R.m[kk][1][2], R.m[kk][1][3]};
+        bf16x8 ah, al;
+        split8v(av, ah, al);
+        const bf16x8 bh = lds8(hH + m * CB_LD + 16 * kk + 8 * h);
+        const bf16x8 bl = lds8(hL + m * CB_LD + 16 * kk + 8 * h);
+        acc = mfma(ah, bh, acc);
+        acc = mfma(ah, bl, acc);
+        acc = mfma(al, bh, acc);
+    }
+    return acc;
+}
+
+// The wave's rows of the block into LDS (hi / lo, transposed) and, if dst,
+// into HBM ([key][value] fp32).
+__device__ __forceinline__ void comb_put(const f32x16 &x, bf16 *hH, bf16 *hL, float *dst, const int wave,
+                                         const int lane, const int col0) {
+    const int m = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float v4[4] = {x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
+        uint32_t hi0, lo0, hi1, lo1;
+        split2(v4[0], v4[1], hi0, lo0);
+        split2(v4[2], v4[3], hi1, lo1);
+        const int k = 32 * wave + 8 * i + 4 * h;
+        *reinterpret_cast<u32x2 *>(hH + m * CB_LD + k) = u32x2{hi0, hi1};
+        *reinterpret_cast<u32x2 *>(hL + m * CB_LD + k) = u32x2{lo0, lo1};
+        if (dst) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dst[(int64_t)(k + j) * DV + col0 + m] = v4[j];
+        }
+    }
+}
+
 __global__ void __launch_bounds__(NTHREADS, 1) gdn_cp_combine_kernel(FwdParams p) {
+    __shared__ __attribute__((aligned(16))) bf16 hH[CB_COLS * CB_LD], hL[CB_COLS * CB_LD];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int m = lane & 31, h = lane >> 5;
-    const int n = blockIdx.x / p.Hv;
-    const int j = blockIdx.x % p.Hv;
+    constexpr int NCB = DV / CB_COLS;
+    const int cb = blockIdx.x % NCB;
+    const int nj = blockIdx.x / NCB;
+    const int n = nj / p.Hv;
+    const int j = nj % p.Hv;
     if (n >= p.N) return;
+    const int col0 = CB_COLS * cb;
     // first segment of sequence n and its segment count
     int seg0 = 0, R = 0;
     if (!p.cu) {
@@ -1619,33 +1692,32 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_cp_combine_kernel(FwdParams p
         R = seq_segments((int64_t)p.cu[n + 1] - p.cu[n], p.L);
     }
     if (R <= 1) return;
-    f32x16 H[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-    if (p.h0) load_state(H, p.h0 + ((int64_t)n * p.Hv + j) * DK * DV, wave, lane);
-    for (int r = 0; r + 1 < R; ++r) {
-        const int64_t off = ((int64_t)(seg0 + r) * p.Hv + j) * DK * DV;
-        const float *M = p.ws_m + off;
-        f32x16 X[4];
-        load_state(X, p.ws_s + off, wave, lane);  // start from S_r, accumulate M_r H
+    {
+        // H_start[0]: the initial state's block (or zeros)
+        f32x16 h0v;
+        const int m = lane & 31, h = lane >> 5;
+        const float *src = p.h0 ? p.h0 + ((int64_t)n * p.Hv + j) * DK * DV : nullptr;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            bf16x8 bh, bl;
-            split8(H[kk >> 1], kk & 1, bh, bl);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const float *row = M + (int64_t)(32 * mb + m) * DK + 16 * kk + 4 * h;
-                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(row);
-                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(row + 8);
-                const float av[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-                bf16x8 ah, al;
-                split8v(av, ah, al);
-                X[mb] = mfma(ah, bh, X[mb]);
-                X[mb] = mfma(ah, bl, X[mb]);
-                X[mb] = mfma(al, bh, X[mb]);
-            }
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) H[mb] = X[mb];
-        store_state(H, p.ws_h + ((int64_t)(seg0 + r + 1) * p.Hv + j) * DK * DV, wave, lane);
+        for (int e = 0; e < 16; ++e)
+            h0v[e] = src ? src[(int64_t)(32 * wave + 8 * (e >> 2) + 4 * h + (e & 3)) * DV + col0 + m] : 0.f;
+        comb_put(h0v, hH, hL, nullptr, wave, lane, col0);
+    }
+    CombRegs A, B;
+    auto seg_off = [&](int r) { return ((int64_t)(seg0 + r) * p.Hv + j) * DK * DV; };
+    comb_load(A, p.ws_m + seg_off(0), p.ws_s + seg_off(0), wave, lane, col0);
+    // two steps per trip so that the register sets alternate without copies
+    for (int r = 0; r + 1 < R; r += 2) {
+        if (r + 2 < R) comb_load(B, p.ws_m + seg_off(r + 1), p.ws_s + seg_off(r + 1), wave, lane, col0);
+        __syncthreads();  // H_start[r] complete in LDS
+        f32x16 x = comb_step(A, hH, hL, lane);
+        __syncthreads();  // every wave has read H_start[r]
+        comb_put(x, hH, hL, p.ws_h + seg_off(r + 1), wave, lane, col0);
+        if (r + 2 >= R) break;
+        if (r + 3 < R) comb_load(A, p.ws_m + seg_off(r + 2), p.ws_s + seg_off(r + 2), wave, lane, col0);
+        __syncthreads();
+        x = comb_step(B, hH, hL, lane);
+        __syncthreads();
+        comb_put(x, hH, hL, p.ws_h + seg_off(r + 2), wave, lane, col0);
     }
 }
 
@@ -1705,7 +1777,8 @@ int launch_cp_exact(const FwdParams &p, void *stream) {
     hipLaunchKernelGGL(gdn_cp_prepass_kernel, dim3(grid), dim3(NTHREADS), smem, (hipStream_t)stream, p);
     int err = (int)hipGetLastError();
     if (err) return err;
-    hipLaunchKernelGGL(gdn_cp_combine_kernel, dim3((unsigned)p.N * (unsigned)p.Hv), dim3(NTHREADS), 0,
+    hipLaunchKernelGGL(gdn_cp_combine_kernel, dim3((unsigned)p.N * (unsigned)p.Hv * (unsigned)(DV / CB_COLS)),
+                       dim3(NTHREADS), 0,
                        (hipStream_t)stream, p);
     return (int)hipGetLastError();
 }
