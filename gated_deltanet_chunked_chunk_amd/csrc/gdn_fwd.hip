@@ -657,12 +657,14 @@ __device__ __forceinline__ void dma_rows(bf16 *tile, const __amdgpu_buffer_rsrc_
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + 4 * i * DK), 16, (int)off, 0, 0, 0);
 }
 
-// Preparation wave pw's quarter (rows 16 pw .. 16 pw + 15) of chunk c's tile.
+// Part `part` of PARTS (rows 64 part / PARTS ..) of chunk c's tile.
+template <int PARTS = 4>
 __device__ __forceinline__ void dma_tile(bf16 *tile, const char *base, const unsigned stride, const int c,
-                                         const int seq_len, const int pw, const int lane) {
+                                         const int seq_len, const int part, const int lane) {
+    constexpr int GROUPS = 16 / PARTS;  // 4-row groups per part
     const __amdgpu_buffer_rsrc_t r = chunk_rsrc(base, stride, c, seq_len);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma_rows(tile, r, stride, 4 * pw + i, lane);
+    for (int i = 0; i < GROUPS; ++i) dma_rows(tile, r, stride, GROUPS * part + i, lane);
 }
 
 // g (preparation wave 0) and beta (wave 1) of chunk c, one token per lane.
@@ -1081,6 +1083,29 @@ __device__ __forceinline__ void u9(const Smem8 &s, const int lane, const int sw,
     }
 }
 
+// The same with the T diag(beta) fragments read one at a time.
+__device__ __forceinline__ void u9_lean(const Smem8 &s, const int lane, const int sw, f32x4 (&u)[4][2]) {
+    bf16x8 vv[2][2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vv[ct][ks] = frag_t(s.v, 32 * sw + 16 * ct, 32 * ks, lane);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) u[rt][ct] = f32x4{};
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        const int rt = frag_rt(f), ks = frag_ks(f);
+        const bf16x8 th = s.tf[0][f][lane], tl = s.tf[1][f][lane];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            u[rt][ct] = mfma16(th, vv[ct][ks], u[rt][ct]);
+            u[rt][ct] = mfma16(tl, vv[ct][ks], u[rt][ct]);
+        }
+    }
+}
+
 // ---- state-wave pieces of the state pass (two column tiles each).  Every
 // piece issues all of its LDS operand reads in one batch before its first
 // MFMA, so the LDS latency is paid once per piece.
@@ -1134,6 +1159,27 @@ __device__ __forceinline__ void wh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f
             for (int ct = 0; ct < 2; ++ct) {
                 vp[rt][ct] = mfma16(wa[kk][rt], hh[ct], vp[rt][ct]);
                 vp[rt][ct] = mfma16(wa[kk][rt], hl[ct], vp[rt][ct]);
+            }
+    }
+}
+
+// The same with the W fragments read one k step at a time (fewer live
+// registers; for the pre-pass, which runs three waves per SIMD).
+__device__ __forceinline__ void wh8_lean(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int ln) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 wa[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) wa[rt] = s.wf[rt][kk][ln];
+        bf16x8 hh[2], hl[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh[ct], hl[ct]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                vp[rt][ct] = mfma16(wa[rt], hh[ct], vp[rt][ct]);
+                vp[rt][ct] = mfma16(wa[rt], hl[ct], vp[rt][ct]);
             }
     }
 }
@@ -1231,6 +1277,45 @@ __device__ __forceinline__ void hupd9(const Smem8 &s, f32x4 (&hacc)[2][8], f32x4
     }
 }
 
+// The same with the K^T fragments read four at a time.
+__device__ __forceinline__ void hupd9_lean(const Smem8 &s, f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int buf,
+                                           const int ln) {
+    const int g = ln >> 4;
+    const bf16 *K = s.k[buf];
+    const float glast = s.gam[buf][CH - 1];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s.dec[buf][16 * rt + 4 * g]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) vp[rt][ct][jj] *= d4[jj];
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) hacc[ct][dt] *= glast;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 vh[2], vl[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) split_pair(vp[2 * ks][ct], vp[2 * ks + 1][ct], vh[ct], vl[ct]);
+#pragma unroll
+        for (int d4i = 0; d4i < 2; ++d4i) {
+            bf16x8 ka[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) ka[d] = frag_t(K, 16 * (4 * d4i + d), 32 * ks, ln);
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    hacc[ct][4 * d4i + d] = mfma16(ka[d], vh[ct], hacc[ct][4 * d4i + d]);
+                    hacc[ct][4 * d4i + d] = mfma16(ka[d], vl[ct], hacc[ct][4 * d4i + d]);
+                }
+        }
+    }
+}
+
 // ---- low-level outputs
 // First global chunk index of sequence n (chunks of all sequences in order).
 __device__ __forceinline__ int seq_chunk_base(const FwdParams &p, int n, int lane) {
@@ -1305,25 +1390,38 @@ __device__ __forceinline__ void store_state8(const f32x4 (&t)[2][8], float *dst,
     }
 }
 
-// One workgroup per CU (its LDS footprint), two waves per SIMD: schedule for that.
-__global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) gdn_fwd_main_kernel(FwdParams p) {
+// The chunk loop of one (segment, v-head).  PRE = false: the forward proper
+// (4 state waves, 4 preparation waves).  PRE = true: the exact-CP pre-pass
+// (blog, AutoCP: the per-segment M and S) for a segment that does not end its
+// sequence -- waves 0..3 run the state pass from a zero state (S), waves 4..7
+// the same pass without inputs (U = 0) from the identity (M, the product of the
+// chunk maps X -> gamma_last X - K^T diag(gamma_last / gamma) W X; K = V, so M
+// has the state's shape), both on the chunk operands the preparation waves
+// 8..11 build once; no output, no warm-up.  The segment's end state is then
+// M H_start + S.
+template <bool PRE>
+__device__ __forceinline__ void fwd_pass(const FwdParams &p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     Smem8 &s = *reinterpret_cast<Smem8 *>(smem_raw);
+    constexpr int NSTATE = PRE ? 8 : 4;  // state waves
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const bool state_wave = wave < 4;  // waves 0..3 hold the state, 4..7 prepare chunks
+    const bool state_wave = wave < NSTATE;  // the first NSTATE waves hold states, the rest prepare chunks
+    const int sw = PRE ? (wave & 3) : wave;  // column block of a state wave
+    const bool mwave = PRE && wave >= 4 && wave < 8;  // pre-pass: this wave carries M
     const int seg = blockIdx.x / p.Hv;
     const int j = blockIdx.x % p.Hv;
     if (seg >= p.num_segments) return;
     const SegEntry e = find_segment(p, seg, lane);
     if (e.n < 0) return;  // beyond the planned segments: nothing to do
+    if (PRE && e.last) return;  // a last segment's map is never used
     const int i_qk = j / p.group;
 
     // ---- where this segment's state pass starts
     int c_first = e.c_begin;
     bool from_h0 = (e.c_begin == 0);
-    if (!from_h0 && p.cp_mode == 2 /* WARMUP */) {
+    if (!PRE && !from_h0 && p.cp_mode == 2 /* WARMUP */) {
         // gate-driven window: walk back chunk by chunk until the summed
         // log-gates drop below the fp32 noise floor, the cap, or the start
         float acc = 0.f;
@@ -1347,7 +1445,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const int c_end = e.c_begin + e.c_count;
 
     const bool has_chunks = c_first < c_end;  // wave-uniform and equal across the workgroup
-    if (!has_chunks && !(state_wave && e.last && p.ht)) return;
+    if (!has_chunks && !(!PRE && state_wave && e.last && p.ht)) return;
 
     Inputs in;
     in.kstride = (unsigned)p.Hqk * DK * 2;
@@ -1386,7 +1484,18 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) hacc[ct][dt] = f32x4{};
-        {
+        if (PRE) {
+            if (mwave) {  // identity: key row 16 dt + 4 g + jj, column 32 sw + 16 ct + l % 16
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            hacc[ct][dt][jj] =
+                                (16 * dt + 4 * (lane >> 4) + jj == 32 * sw + 16 * ct + (lane & 15)) ? 1.f : 0.f;
+            }
+        } else {
             const float *src = nullptr;
             if (from_h0 && p.h0) src = p.h0 + ((int64_t)e.n * p.Hv + j) * DK * DV;
             if (!from_h0 && p.cp_mode == 1 /* EXACT */) src = p.ws_h + ((int64_t)seg * p.Hv + j) * DK * DV;
@@ -1395,7 +1504,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int64_t oes = p.o_f32 ? 4 : 2;
         const char *obase = static_cast<const char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes;
         f32x4 vp[4][2], qh[4][2];  // vp: U, then v' of this chunk
-        const int cbase = (p.h_out || p.vn_out) ? seq_chunk_base(p, e.n, lane) : 0;
+        const int cbase = (!PRE && (p.h_out || p.vn_out)) ? seq_chunk_base(p, e.n, lane) : 0;
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
             const bool chain = c >= c_first;  // state pass of chunk c
             const bool prep = c + 1 < c_end;  // preparation of chunk c + 1
@@ -1412,33 +1521,50 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
                 return t & 63;
             };
             if (chain) {
-                u9(s, lane_now(), wave, vp);
-                wh8(s, hacc, vp, lane_now());
+                if (mwave) {
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                        for (int ct = 0; ct < 2; ++ct) vp[rt][ct] = f32x4{};
+                } else if (PRE) {
+                    u9_lean(s, lane_now(), sw, vp);
+                } else {
+                    u9(s, lane_now(), sw, vp);
+                }
+                if (PRE) wh8_lean(s, hacc, vp, lane_now());
+                else wh8(s, hacc, vp, lane_now());
             }
-            if (chain && out && p.vn_out)
+            if (!PRE && chain && out && p.vn_out)
                 store_vn8(vp, p.vn_out + ((int64_t)(cbase + c) * p.Hv + j) * CH * DV, wave, lane_now());
             lds_barrier();
-            if (chain && out) out9(s, p, obase, e.seq_len, vp, qh, c, wave, lane_now());
+            if (!PRE && chain && out) out9(s, p, obase, e.seq_len, vp, qh, c, wave, lane_now());
             lds_barrier();
-            if (chain) hupd9(s, hacc, vp, b, lane_now());
+            if (chain) {
+                if (PRE) hupd9_lean(s, hacc, vp, b, lane_now());
+                else hupd9(s, hacc, vp, b, lane_now());
+            }
             lds_barrier();
-            if (c + 2 < c_end) dma_tile(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, lane_now());
-            if (prep && c + 1 >= e.c_begin) qh9(s, hacc, qh, 0, nb, p.scale, lane_now());
+            if (c + 2 < c_end) dma_tile<NSTATE>(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, lane_now());
+            if (!PRE && prep && c + 1 >= e.c_begin) qh9(s, hacc, qh, 0, nb, p.scale, lane_now());
             lds_barrier();
-            if (prep && c + 1 >= e.c_begin) {
+            if (!PRE && prep && c + 1 >= e.c_begin) {
                 qh9(s, hacc, qh, 1, nb, p.scale, lane_now());
                 if (p.h_out) store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
             }
         }
-        if (e.last && p.ht) store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
+        if (PRE) {
+            store_state8(hacc, (mwave ? p.ws_m : p.ws_s) + ((int64_t)seg * p.Hv + j) * DK * DV, sw, lane);
+        } else if (e.last && p.ht) {
+            store_state8(hacc, p.ht + ((int64_t)e.n * p.Hv + j) * DK * DV, wave, lane);
+        }
     } else {
         __builtin_amdgcn_s_setprio(2);
-        const int pw = wave - 4;
-        const char *abase = p.a_out ? reinterpret_cast<const char *>(p.a_out + ((int64_t)e.row0 * p.Hv + j) * CH)
+        const int pw = wave - NSTATE;
+        const char *abase = (!PRE && p.a_out) ? reinterpret_cast<const char *>(p.a_out + ((int64_t)e.row0 * p.Hv + j) * CH)
                                     : nullptr;
         if (has_chunks) {
             dma_tile(s.k[c_first & 1], in.k, in.kstride, c_first, e.seq_len, pw, lane);
-            if (c_first >= e.c_begin) dma_tile(s.q[c_first & 1], in.q, in.kstride, c_first, e.seq_len, pw, lane);
+            if (!PRE && c_first >= e.c_begin) dma_tile(s.q[c_first & 1], in.q, in.kstride, c_first, e.seq_len, pw, lane);
             dma_gb(s, in, c_first, pw, lane);
         }
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
@@ -1453,7 +1579,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             dma_wait();
             lds_barrier();
             if (ahead) {
-                if (c + 2 >= e.c_begin) dma_tile(s.q[c & 1], in.q, in.kstride, c + 2, e.seq_len, pw, ln);
+                if (!PRE && c + 2 >= e.c_begin) dma_tile(s.q[c & 1], in.q, in.kstride, c + 2, e.seq_len, pw, ln);
                 dma_gb(s, in, c + 2, pw, ln);
             }
             if (prep) prod9(s, ln, pw, nb);
@@ -1461,7 +1587,7 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             if (prep) dma_tile(s.v, in.v, in.vstride, c + 1, e.seq_len, pw, ln);
             if (prep) inv8_l0(s, ln, pw);
             lds_barrier();
-            const bool pout = prep && c + 1 >= e.c_begin;  // chunk c + 1 produces output: P needed
+            const bool pout = !PRE && prep && c + 1 >= e.c_begin;  // chunk c + 1 produces output: P needed
             if (prep && pw < 2) {
                 inv8_l1(s, ln, pw);
                 if (pout) pfrag9(s, ln, pw + 1, nb, p.scale, decays_factor(s, ln));  // fragments 1, 2
@@ -1479,118 +1605,22 @@ __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 
             }
             if (prep) wfrag9(s, ln, 0, pw, pw < 2 ? pw : -1, nb);  // rows 0..31, final since level 1
             lds_barrier();
-            if (prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, abase, e.seq_len, c + 1, pw, ln);
+            if (!PRE && prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, abase, e.seq_len, c + 1, pw, ln);
             if (prep) wfrag9(s, ln, 2, pw, 2 + pw, nb);  // rows 32..63
         }
     }
 }
 
-// ---------------------------------------------------------------- exact context parallelism
-// Pre-pass (blog, AutoCP: the per-segment M and S).  For every segment that is
-// not the last of its sequence: S = the state pass over the segment from a
-// zero state, and M = the same pass without inputs (U = 0) from the identity,
-// i.e. the product of the chunk maps X -> gamma_last X - K^T diag(gamma_last /
-// gamma) W X.  Then the segment's end state is M H_start + S.
-__global__ void __launch_bounds__(NTHREADS, 1) gdn_cp_prepass_kernel(FwdParams p) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-    Smem &s = *reinterpret_cast<Smem *>(smem_raw);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int seg = blockIdx.x / p.Hv;
-    const int j = blockIdx.x % p.Hv;
-    if (seg >= p.num_segments) return;
-    const SegEntry e = find_segment(p, seg, lane);
-    if (e.n < 0 || e.last) return;  // a last segment's map is never used
-    const int i_qk = j / p.group;
 
-    f32x16 hs[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
-    f32x16 hm[4];
-    {
-        const int m = lane & 31, h = lane >> 5;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                hm[mb][r] = (32 * mb + 8 * (r >> 2) + 4 * h + (r & 3) == 32 * wave + m) ? 1.f : 0.f;
-    }
-    const int c_end = e.c_begin + e.c_count;
-    Inputs in;
-    in.kstride = (unsigned)p.Hqk * DK * 2;
-    in.vstride = (unsigned)p.Hv * DV * 2;
-    in.gstride = (unsigned)p.Hv * 4;
-    in.k = reinterpret_cast<const char *>(p.k + (e.row0 * p.Hqk + i_qk) * DK);
-    in.q = in.k;  // not read: no output here
-    in.v = reinterpret_cast<const char *>(p.v + (e.row0 * p.Hv + j) * DV);
-    in.g = reinterpret_cast<const char *>(p.g + e.row0 * p.Hv + j);
-    in.b = reinterpret_cast<const char *>(p.beta + e.row0 * p.Hv + j);
-    in.seq_len = e.seq_len;
-
-    Stage st;
-    load_chunk(in, st, e.c_begin, false, threadIdx.x);
-    for (int c = e.c_begin; c < c_end; ++c) {
-        int tid = threadIdx.x;
-        asm volatile("" : "+v"(tid));
-        const int ln = tid & 63;
-        const int m = ln & 31, h = ln >> 5;
-        store_chunk(s, st, false, tid);
-        __syncthreads();
-        if (c + 1 < c_end) load_chunk(in, st, c + 1, false, tid);
-        prep_products(s, tid, false);
-        prep_inverse(s, tid);
-        f32x16 u[2];
-        prep_wu(s, tid, u);
-
-        f32x16 vs[2] = {u[0], u[1]};
-        f32x16 vm[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            bf16x8 sh, sl, mh, ml;
-            split8(hs[kk >> 1], kk & 1, sh, sl);
-            split8(hm[kk >> 1], kk & 1, mh, ml);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                const bf16x8 a = s.wf[rb][kk][ln];
-                vs[rb] = mfma(a, sh, vs[rb]);
-                vs[rb] = mfma(a, sl, vs[rb]);
-                vm[rb] = mfma(a, mh, vm[rb]);
-                vm[rb] = mfma(a, ml, vm[rb]);
-            }
-        }
-        const float glast = s.gam[CH - 1];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float d = s.dec[32 * rb + 8 * (r >> 2) + 4 * h + (r & 3)];
-                vs[rb][r] *= d;
-                vm[rb][r] *= d;
-            }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            hs[mb] *= glast;
-            hm[mb] *= glast;
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 sh, sl, mh, ml;
-            split8(vs[kk >> 1], kk & 1, sh, sl);
-            split8(vm[kk >> 1], kk & 1, mh, ml);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const bf16x8 a = lds8_perm(&s.kt[(32 * mb + m) * CS], 16 * kk, h);
-                hs[mb] = mfma(a, sh, hs[mb]);
-                hs[mb] = mfma(a, sl, hs[mb]);
-                hm[mb] = mfma(a, mh, hm[mb]);
-                hm[mb] = mfma(a, ml, hm[mb]);
-            }
-        }
-        __syncthreads();
-    }
-    const int64_t off = ((int64_t)seg * p.Hv + j) * DK * DV;
-    store_state(hs, p.ws_s + off, wave, lane);
-    store_state(hm, p.ws_m + off, wave, lane);
+// One workgroup per CU (its LDS footprint): two waves per SIMD for the forward,
+// three for the pre-pass.
+__global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) gdn_fwd_main_kernel(FwdParams p) {
+    fwd_pass<false>(p);
 }
+constexpr int NT_PRE = 768;
+__global__ void __launch_bounds__(NT_PRE, 1) gdn_cp_prepass_kernel(FwdParams p) { fwd_pass<true>(p); }
 
+// ---------------------------------------------------------------- exact context parallelism
 // Combine (sequential over a sequence's segments): H_start[0] = initial state,
 // H_start[r+1] = M_r H_start[r] + S_r.  The value columns of H never mix, so
 // one workgroup of 4 waves takes one block of 32 value columns of one
@@ -1768,13 +1798,13 @@ int launch_fwd_main(const FwdParams &p, void *stream) {
 }
 
 int launch_cp_exact(const FwdParams &p, void *stream) {
-    static const size_t smem = sizeof(Smem);
+    static const size_t smem = sizeof(Smem8);
     static const int attr_rc =
         (int)hipFuncSetAttribute((const void *)gdn_cp_prepass_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)smem);
     if (attr_rc != 0) return attr_rc;
     const unsigned grid = (unsigned)p.num_segments * (unsigned)p.Hv;
-    hipLaunchKernelGGL(gdn_cp_prepass_kernel, dim3(grid), dim3(NTHREADS), smem, (hipStream_t)stream, p);
+    hipLaunchKernelGGL(gdn_cp_prepass_kernel, dim3(grid), dim3(NT_PRE), smem, (hipStream_t)stream, p);
     int err = (int)hipGetLastError();
     if (err) return err;
     hipLaunchKernelGGL(gdn_cp_combine_kernel, dim3((unsigned)p.N * (unsigned)p.Hv * (unsigned)(DV / CB_COLS)),
