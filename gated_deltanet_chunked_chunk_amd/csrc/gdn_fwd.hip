@@ -13,28 +13,27 @@
 //   O    = scale [ diag(gamma) Q H + P v' ],   P_is = e^{G_i-G_s} q_i.k_s (s <= i)
 //   H   <- gamma_last H + K^T diag(gamma_last / gamma) v'
 //
-// One workgroup (4 waves) owns one (segment, v-head): it walks the segment's
-// chunks in order with H resident in MFMA accumulators, split by V columns
-// across the waves (column j of H only ever mixes with column j of v, so the
-// split is exact).  Everything chunk-local (cumsum, K K^T, inverse, W, U, P) is
-// recomputed on chip; W, U and S never touch HBM.
+// One workgroup owns one (segment, v-head): it walks the segment's chunks in
+// order with H resident in MFMA accumulators, split by V columns across its
+// state waves (column j of H only ever mixes with column j of v, so the split
+// is exact), while its preparation waves build the next chunk's operands
+// (cumsum, K K^T, inverse, W, T diag(beta), P) on chip; W, U and S never touch
+// HBM.  The exact context-parallel mode adds a pre-pass on the same chunk loop
+// (per-segment S and transition map M) and a combine over segments.
 //
 // Precision (the pages' "restructure without losing precision", summarylog.com
 // essay, "formula restructuring"): products of two exact bf16 inputs (K K^T,
-// Q K^T, K^T T~^T, Q H) use one bf16 MFMA; operands that carry fp32 values
-// which feed the output with full weight are split into hi + lo bf16 pairs:
-// T diag(beta), P, v', the decayed v', and H.  Decays and beta are fp32
+// Q K^T, K^T T~^T) use one bf16 MFMA; operands that carry fp32 values which
+// feed the output or the state with full weight are split into hi + lo bf16
+// pairs: T diag(beta), P, v', the decayed v', and H.  Decays and beta are fp32
 // row/column scales; every exponent is a non-positive difference G_i - G_s
 // (masked before the exp), so nothing overflows.
 //
-// MFMA: v_mfma_f32_32x32x16_bf16.  Lane l holds A row (l % 32) / B column
-// (l % 32), 8 k-slots for lane half h = l / 32; accumulator element 4i + j
-// holds row 8i + 4h + j, column l % 32.  An accumulator tile read as a B
-// operand therefore sees, in k-step s, the k indices 16s + {4h..4h+3,
-// 8+4h..8+4h+3}; A operands that meet such a B are read with the same
-// permutation.  W and P are produced transposed (W^T = K^T T~^T, P^T = K Q^T)
-// so that each lane's accumulator already is its A fragment for W H and P v';
-// those fragments go through LDS fragment-major (16 bytes per lane).
+// MFMA shapes: v_mfma_f32_16x16x32_bf16 for the chunk loop's products
+// (fragment layouts described with the kernel), v_mfma_f32_32x32x16_bf16 for
+// K K^T and the combine (lane l holds A row / B column l % 32 with 8 k-slots
+// for lane half l / 32; accumulator element 4i + j holds row 8i + 4(l / 32) + j,
+// column l % 32).
 #include <hip/hip_runtime.h>
 
 #include "gdn_internal.h"
@@ -53,30 +52,7 @@ constexpr int CH = kChunk;   // 64
 constexpr int DK = kDimK;    // 128
 constexpr int DV = kDimV;    // 128
 constexpr int NTHREADS = 256;
-constexpr int KS = DK + 8;   // bf16 row stride of 128-wide tiles (272 B)
-constexpr int CS = CH + 8;   // bf16 row stride of 64-wide tiles (144 B)
 constexpr int AS = CH + 4;   // fp32 row stride of the 64 x 64 A / T tile (16-byte aligned rows)
-constexpr int OS = 32 + 4;   // fp32 row stride of a wave's 64 x 32 output staging tile
-
-struct __attribute__((aligned(16))) Smem {
-    bf16 k[CH * KS];       // K, row = token
-    bf16 q[CH * KS];       // Q
-    bf16 kt[DK * CS];      // K^T, row = key dim
-    bf16 vt[DV * CS];      // V^T, row = value dim
-    union {
-        float a[CH * AS];             // A, inverted in place into T
-        float ostage[4][CH * OS];     // per-wave output tile on its way to HBM
-    };
-    bf16x8 wf[2][8][64];              // -W as A fragments [row block][k step][lane]
-    bf16x8 pf[2][3][2][64];           // P as A fragments [hi, lo][tile][k step][lane]
-    float scr[2][16 * 17];            // inverse scratch, one per merging wave
-    float graw[CH], beta[CH], gcum[CH], gam[CH], dec[CH], bg[CH];
-    // e^{G_i - G_s} = ep[i] * em[s] with ep = e^{G - G_ref}, em = e^{G_ref - G},
-    // G_ref = G_31; rowa = beta * ep.  Used when every |G - G_ref| < 80 (no
-    // overflow in either factor), flagged by fact_ok.
-    float ep[CH], em[CH], rowa[CH];
-    int fact_ok;
-};
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -84,14 +60,6 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 lds8(const bf16 *p) {   // 16-byte LDS read
     return *reinterpret_cast<const bf16x8 *>(p);
-}
-
-// A-operand read matching an accumulator-sourced B operand: k indices
-// base + 4h .. base + 4h + 3 and base + 8 + 4h .. base + 8 + 4h + 3.
-__device__ __forceinline__ bf16x8 lds8_perm(const bf16 *row, int base, int h) {
-    bf16x4 lo = *reinterpret_cast<const bf16x4 *>(row + base + 4 * h);
-    bf16x4 hi = *reinterpret_cast<const bf16x4 *>(row + base + 8 + 4 * h);
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // hi + lo bf16 split of fp32 values, two at a time: hi = RNE(x) for both in
@@ -113,14 +81,6 @@ __device__ __forceinline__ void split8v(const float *x, bf16x8 &hi, bf16x8 &lo) 
     for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], h[i], l[i]);
     hi = __builtin_bit_cast(bf16x8, (u32x4{h[0], h[1], h[2], h[3]}));
     lo = __builtin_bit_cast(bf16x8, (u32x4{l[0], l[1], l[2], l[3]}));
-}
-
-// Accumulator registers 8s .. 8s+7 of a tile as bf16 hi and lo B operands.
-__device__ __forceinline__ void split8(const f32x16 &acc, int s, bf16x8 &hi, bf16x8 &lo) {
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = acc[8 * s + e];
-    split8v(x, hi, lo);
 }
 
 // ---------------------------------------------------------------- chunk loads
@@ -153,324 +113,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void *base, unsigned stride, int c, int seq_len) {
     const int rows = min(max(seq_len - c * CH, 0), CH);
     return make_rsrc(static_cast<const char *>(base) + (int64_t)c * CH * stride, (int64_t)rows * stride);
-}
-
-// Thread t stages rows 4*(t % 16) .. +3, columns 8*(t / 16) .. +7 of each
-// 64 x 128 tile (16-byte loads).
-struct Stage {
-    u32x4 k[4], q[4], v[4];
-    float g, b;
-};
-
-__device__ __forceinline__ void load_chunk(const Inputs &in, Stage &st, int c, bool need_q, int t) {
-    const int rg = t & 15, cg = t >> 4;
-    const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(in.k, in.kstride, c, in.seq_len);
-    const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(in.q, in.kstride, c, in.seq_len);
-    const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(in.v, in.vstride, c, in.seq_len);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const unsigned row = (unsigned)(4 * rg + r);
-        st.k[r] = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(row * in.kstride + 16u * cg), 0, 0);
-        st.v[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(row * in.vstride + 16u * cg), 0, 0);
-        if (need_q) st.q[r] = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)(row * in.kstride + 16u * cg), 0, 0);
-    }
-    if (t < CH) {
-        // the b32 loads return raw bits
-        const __amdgpu_buffer_rsrc_t rg_ = chunk_rsrc(in.g, in.gstride, c, in.seq_len);
-        const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(in.b, in.gstride, c, in.seq_len);
-        st.g = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rg_, (int)(t * in.gstride), 0, 0));
-        st.b = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, (int)(t * in.gstride), 0, 0));
-    }
-}
-
-__device__ __forceinline__ uint32_t half_of(const u32x4 &x, int e) {
-    return (x[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-}
-
-__device__ __forceinline__ void store_chunk(Smem &s, const Stage &st, bool need_q, const int t) {
-    const int rg = t & 15, cg = t >> 4;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<u32x4 *>(&s.k[(4 * rg + r) * KS + 8 * cg]) = st.k[r];
-        if (need_q) *reinterpret_cast<u32x4 *>(&s.q[(4 * rg + r) * KS + 8 * cg]) = st.q[r];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t k01 = half_of(st.k[0], e) | (half_of(st.k[1], e) << 16);
-        const uint32_t k23 = half_of(st.k[2], e) | (half_of(st.k[3], e) << 16);
-        *reinterpret_cast<uint2 *>(&s.kt[(8 * cg + e) * CS + 4 * rg]) = make_uint2(k01, k23);
-        const uint32_t v01 = half_of(st.v[0], e) | (half_of(st.v[1], e) << 16);
-        const uint32_t v23 = half_of(st.v[2], e) | (half_of(st.v[3], e) << 16);
-        *reinterpret_cast<uint2 *>(&s.vt[(8 * cg + e) * CS + 4 * rg]) = make_uint2(v01, v23);
-    }
-    if (t < CH) {
-        s.graw[t] = st.g;
-        s.beta[t] = st.b;
-    }
-}
-
-// ---------------------------------------------------------------- chunk prep
-// Cumsum (wave 0), masked beta-weighted K K^T into s.a (waves 1..3), and the
-// causal decayed P^T = K Q^T as hi/lo A fragments (waves 0..2, output chunks).
-// P^T tile t covers (s block, i block) = (0,0), (0,1), (1,1).
-__device__ __forceinline__ void prep_products(Smem &s, const int tid, const bool out) {
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int m = lane & 31, h = lane >> 5;
-    f32x16 acck = {}, accp = {};
-    const int rbi = (wave >= 2) ? 1 : 0, rbs = (wave == 3) ? 1 : 0;  // K K^T tile of waves 1..3
-    const int psb = (wave == 2) ? 1 : 0, prb = (wave >= 1) ? 1 : 0;  // P^T tile of waves 0..2
-    if (wave == 0) {
-        float x = s.graw[lane];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
-        }
-        const float glast = __shfl(x, 63, 64);
-        const float gref = __shfl(x, 31, 64);
-        const float gm = __expf(x);
-        const float d = x - gref;
-        const float bt = s.beta[lane];
-        const float epv = __expf(d);
-        s.gcum[lane] = x;
-        s.gam[lane] = gm;
-        s.dec[lane] = __expf(glast - x);
-        s.bg[lane] = bt * gm;
-        s.ep[lane] = epv;
-        s.em[lane] = __expf(-d);
-        s.rowa[lane] = bt * epv;
-        const bool ok = __all(fabsf(d) < 80.f);
-        if (lane == 0) s.fact_ok = ok ? 1 : 0;
-    } else {
-        const bf16 *ra = &s.k[(32 * rbi + m) * KS + 8 * h];
-        const bf16 *rb = &s.k[(32 * rbs + m) * KS + 8 * h];
-#pragma unroll
-        for (int kk = 0; kk < DK / 16; ++kk) acck = mfma(lds8(ra + 16 * kk), lds8(rb + 16 * kk), acck);
-    }
-    if (out && wave <= 2) {
-        const bf16 *ra = &s.k[(32 * psb + m) * KS + 8 * h];
-        const bf16 *rb = &s.q[(32 * prb + m) * KS + 8 * h];
-#pragma unroll
-        for (int kk = 0; kk < DK / 16; ++kk) accp = mfma(lds8(ra + 16 * kk), lds8(rb + 16 * kk), accp);
-    }
-    __syncthreads();
-    const bool fact = __builtin_amdgcn_readfirstlane(s.fact_ok) != 0;
-    if (wave != 0) {
-        // A_is = beta_i e^{G_i - G_s} k_i.k_s for s < i (rows of this lane: 4 runs of 4)
-        const int col = 32 * rbs + m;
-        float v[16];
-        if (fact) {
-            const float cf = s.em[col];
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const f32x4 ra4 = *reinterpret_cast<const f32x4 *>(&s.rowa[32 * rbi + 8 * ii + 4 * h]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) v[4 * ii + j] = ra4[j] * cf * acck[4 * ii + j];
-            }
-        } else {
-            const float gs = s.gcum[col];
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[32 * rbi + 8 * ii + 4 * h]);
-                const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&s.beta[32 * rbi + 8 * ii + 4 * h]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = 32 * rbi + 8 * ii + 4 * h + j;
-                    v[4 * ii + j] = (col < row) ? b4[j] * __expf(g4[j] - gs) * acck[4 * ii + j] : 0.f;
-                }
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = 32 * rbi + 8 * (e >> 2) + 4 * h + (e & 3);
-            s.a[row * AS + col] = (col < row) ? v[e] : 0.f;
-        }
-    }
-    if (out && wave <= 2) {
-        // P^T_si = e^{G_i - G_s} q_i.k_s for s <= i (i = this lane's column)
-        const int i = 32 * prb + m;
-        float pv[16];
-        if (fact) {
-            const float cf = s.ep[i];
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const f32x4 e4 = *reinterpret_cast<const f32x4 *>(&s.em[32 * psb + 8 * ii + 4 * h]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int srow = 32 * psb + 8 * ii + 4 * h + j;
-                    pv[4 * ii + j] = (srow <= i) ? cf * e4[j] * accp[4 * ii + j] : 0.f;
-                }
-            }
-        } else {
-            const float gi = s.gcum[i];
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const f32x4 g4 = *reinterpret_cast<const f32x4 *>(&s.gcum[32 * psb + 8 * ii + 4 * h]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int srow = 32 * psb + 8 * ii + 4 * h + j;
-                    pv[4 * ii + j] = (srow <= i) ? __expf(gi - g4[j]) * accp[4 * ii + j] : 0.f;
-                }
-            }
-        }
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-            bf16x8 hi, lo;
-            split8v(pv + 8 * kp, hi, lo);
-            s.pf[0][wave][kp][lane] = hi;
-            s.pf[1][wave][kp][lane] = lo;
-        }
-    }
-    __syncthreads();
-}
-
-// In-place inverse of the unit lower-triangular (I + A) held as A in s.a.
-// Level 0: the four 16 x 16 diagonal blocks by forward substitution (one lane
-// per column).  Level 1: T_10 = -T_11 A_10 T_00 inside each 32 x 32 diagonal
-// block.  Level 2 (MFMA, hi/lo bf16): T_lo,hi = -T_lo,lo A_lo,hi T_hi,hi.
-// Entries above the diagonal of each diagonal block hold zeros throughout.
-__device__ __forceinline__ void prep_inverse(Smem &s, const int tid) {
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    if (wave < 2 && lane < 32) {
-        const int o = 32 * wave + 16 * (lane >> 4), c = lane & 15;
-        float t[16];
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-            float ar[16];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                if (4 * q4 < ii) {
-                    const f32x4 x = *reinterpret_cast<const f32x4 *>(&s.a[(o + ii) * AS + o + 4 * q4]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) ar[4 * q4 + j] = x[j];
-                }
-            }
-            float acc = (ii == c) ? 1.f : 0.f;
-#pragma unroll
-            for (int ss = 0; ss < ii; ++ss) acc -= ar[ss] * t[ss];
-            t[ii] = acc;
-        }
-#pragma unroll
-        for (int ii = 0; ii < 16; ++ii) s.a[(o + ii) * AS + o + c] = t[ii];
-    }
-    __syncthreads();
-    const int c = lane & 15, r4 = 4 * (lane >> 4);
-    if (wave < 2) {
-        const int b = 32 * wave;
-        float tc[16];  // column c of T_00
-#pragma unroll
-        for (int ss = 0; ss < 16; ++ss) tc[ss] = s.a[(b + ss) * AS + b + c];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            float acc = 0.f;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + r4 + rr) * AS + b + 4 * q4]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc += x[j] * tc[4 * q4 + j];
-            }
-            s.scr[wave][(r4 + rr) * 17 + c] = acc;
-        }
-    }
-    __syncthreads();
-    if (wave < 2) {
-        const int b = 32 * wave;
-        float xc[16];  // column c of X = A_10 T_00
-#pragma unroll
-        for (int ss = 0; ss < 16; ++ss) xc[ss] = s.scr[wave][ss * 17 + c];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            float acc = 0.f;
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(&s.a[(b + 16 + r4 + rr) * AS + b + 16 + 4 * q4]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc += x[j] * xc[4 * q4 + j];
-            }
-            s.a[(b + 16 + r4 + rr) * AS + b + c] = -acc;
-        }
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const int m = lane & 31, h = lane >> 5;
-        f32x16 y = {};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const float *ar = &s.a[(32 + m) * AS + 16 * kk + 8 * h];
-            float av[8], bv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                av[e] = ar[e];
-                bv[e] = s.a[(16 * kk + 8 * h + e) * AS + m];
-            }
-            bf16x8 ah, al, bh, bl;
-            split8v(av, ah, al);
-            split8v(bv, bh, bl);
-            y = mfma(ah, bh, y);
-            y = mfma(ah, bl, y);
-            y = mfma(al, bh, y);
-        }
-        f32x16 z = {};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const float *tr = &s.a[(32 + m) * AS + 32 + 16 * kk + 4 * h];
-            float av[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                av[e] = tr[e];
-                av[4 + e] = tr[8 + e];
-            }
-            bf16x8 ah, al, bh, bl;
-            split8v(av, ah, al);
-            split8(y, kk, bh, bl);
-            z = mfma(ah, bh, z);
-            z = mfma(ah, bl, z);
-            z = mfma(al, bh, z);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s.a[(32 + 8 * (e >> 2) + 4 * h + (e & 3)) * AS + m] = -z[e];
-    }
-    __syncthreads();
-}
-
-// W^T = K^T (T diag(beta gamma))^T for this wave's 32 key dims -> -W A
-// fragments in LDS; U = (T diag(beta)) V for this wave's 32 value columns.
-__device__ __forceinline__ void prep_wu(Smem &s, const int tid, f32x16 (&u)[2]) {
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int m = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        f32x16 w = {};
-        u[rb] = f32x16{};
-        const int nk = (rb == 0) ? 2 : 4;  // T is lower triangular
-#pragma unroll
-        for (int kk = 0; kk < nk; ++kk) {
-            const float *tr = &s.a[(32 * rb + m) * AS + 16 * kk + 8 * h];
-            const float *bgp = &s.bg[16 * kk + 8 * h];
-            const float *bp = &s.beta[16 * kk + 8 * h];
-            bf16x8 tw, th, tl;
-            float tb[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float tv = tr[e];
-                tw[e] = (bf16)(tv * bgp[e]);
-                tb[e] = tv * bp[e];
-            }
-            split8v(tb, th, tl);
-            w = mfma(lds8(&s.kt[(32 * wave + m) * CS + 16 * kk + 8 * h]), tw, w);
-            const bf16x8 vv = lds8(&s.vt[(32 * wave + m) * CS + 16 * kk + 8 * h]);
-            u[rb] = mfma(th, vv, u[rb]);
-            u[rb] = mfma(tl, vv, u[rb]);
-        }
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-            bf16x8 f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = (bf16)(-w[8 * kp + e]);
-            s.wf[rb][2 * wave + kp][lane] = f;
-        }
-    }
-    __syncthreads();
 }
 
 // ---------------------------------------------------------------- segment lookup
@@ -525,27 +167,6 @@ __device__ __forceinline__ SegEntry find_segment(const FwdParams &p, int seg, in
     e.last = (r == cnt - 1);
     e.pad = 0;
     return e;
-}
-
-// ---------------------------------------------------------------- state I/O
-// A K x V fp32 state (row = key dim) <-> this wave's four accumulator tiles
-// (value columns 32 wave .. 32 wave + 31); each access is one 128-byte row piece.
-__device__ __forceinline__ void load_state(f32x16 (&t)[4], const float *src, const int wave, const int lane) {
-    const int m = lane & 31, h = lane >> 5;
-    const float *b = src + 32 * wave + m;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t[mb][r] = b[(32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * DV];
-}
-
-__device__ __forceinline__ void store_state(const f32x16 (&t)[4], float *dst, const int wave, const int lane) {
-    const int m = lane & 31, h = lane >> 5;
-    float *b = dst + 32 * wave + m;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) b[(32 * mb + 8 * (r >> 2) + 4 * h + (r & 3)) * DV] = t[mb][r];
 }
 
 // ---------------------------------------------------------------- the forward kernel (8 waves)
