@@ -51,7 +51,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int CH = kChunk;   // 64
 constexpr int DK = kDimK;    // 128
 constexpr int DV = kDimV;    // 128
-constexpr int NTHREADS = 256;
 constexpr int AS = CH + 4;   // fp32 row stride of the 64 x 64 A / T tile (16-byte aligned rows)
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -1244,77 +1243,90 @@ __global__ void __launch_bounds__(NT_PRE, 1) gdn_cp_prepass_kernel(FwdParams p) 
 // ---------------------------------------------------------------- exact context parallelism
 // Combine (sequential over a sequence's segments): H_start[0] = initial state,
 // H_start[r+1] = M_r H_start[r] + S_r.  The value columns of H never mix, so
-// one workgroup of 4 waves takes one block of 32 value columns of one
-// (sequence, v-head): wave w computes rows 32 w .. 32 w + 31 of the block
-// (v_mfma_f32_32x32x16_bf16, M rows split hi + lo as the A operand, H as the
-// hi / lo B operand from LDS, stored transposed [column][key]).  Step r's
-// operands M_{r+1} rows and S_{r+1} are loaded into registers while step r
-// runs, so each step waits on the previous one's products, not on HBM.
+// one workgroup of 8 waves takes one block of 32 value columns of one
+// (sequence, v-head): wave w computes rows 16 w .. 16 w + 15 of the block
+// (v_mfma_f32_16x16x32_bf16, M rows split hi + lo as the A operand, H as the
+// hi / lo B operand from LDS, stored transposed [column][key]).  The operands
+// of steps r + 1 and r + 2 (this wave's M rows and S entries, 40 registers a
+// step) are in flight while step r runs, so a step waits on the previous
+// one's products, not on HBM.
 constexpr int CB_COLS = 32;            // value columns per combine workgroup
 constexpr int CB_LD = DK + 8;          // bf16 row stride of the transposed H block (272 B)
+constexpr int NT_COMB = 512;
 
 struct CombRegs {
-    f32x4 m[8][2];   // this lane's M row (32 w + l % 32), k = 16 kk + 8 h .. +7
-    float x[16];     // S block entries (rows 32 w + 8 i + 4 h + j, column l % 32)
+    f32x4 m[4][2];   // M row 16 w + l % 16, k = 32 kk + 8 g .. +7 (g = l / 16)
+    float x[2][4];   // S entries: rows 16 w + 4 g + j, column 16 ct + l % 16
 };
 
 __device__ __forceinline__ void comb_load(CombRegs &R, const float *M, const float *S, const int wave, const int lane,
                                           const int col0) {
-    const int m = lane & 31, h = lane >> 5;
-    const float *row = M + (int64_t)(32 * wave + m) * DK + 8 * h;
+    const int m = lane & 15, g = lane >> 4;
+    const float *row = M + (int64_t)(16 * wave + m) * DK + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        R.m[kk][0] = *reinterpret_cast<const f32x4 *>(row + 16 * kk);
-        R.m[kk][1] = *reinterpret_cast<const f32x4 *>(row + 16 * kk + 4);
+    for (int kk = 0; kk < 4; ++kk) {
+        R.m[kk][0] = *reinterpret_cast<const f32x4 *>(row + 32 * kk);
+        R.m[kk][1] = *reinterpret_cast<const f32x4 *>(row + 32 * kk + 4);
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e)
-        R.x[e] = S[(int64_t)(32 * wave + 8 * (e >> 2) + 4 * h + (e & 3)) * DV + col0 + m];
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            R.x[ct][jj] = S[(int64_t)(16 * wave + 4 * g + jj) * DV + col0 + 16 * ct + m];
 }
 
-// X (rows of this wave, the block's columns) = S + M H, H from LDS (hi / lo, transposed)
-__device__ __forceinline__ f32x16 comb_step(const CombRegs &R, const bf16 *hH, const bf16 *hL, const int lane) {
-    const int m = lane & 31, h = lane >> 5;
-    f32x16 acc;
+// The wave's rows of S + M H for the block's two column tiles (all H operand
+// reads issued before the first product, so their latency is paid once)
+__device__ __forceinline__ void comb_step(const CombRegs &R, const bf16 *hH, const bf16 *hL, const int lane,
+                                          f32x4 (&acc)[2]) {
+    const int m = lane & 15, g = lane >> 4;
+    bf16x8 bh[4][2], bl[4][2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = R.x[e];
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
+        for (int ct = 0; ct < 2; ++ct) {
+            bh[kk][ct] = lds8(hH + (16 * ct + m) * CB_LD + 32 * kk + 8 * g);
+            bl[kk][ct] = lds8(hL + (16 * ct + m) * CB_LD + 32 * kk + 8 * g);
+        }
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) acc[ct] = f32x4{R.x[ct][0], R.x[ct][1], R.x[ct][2], R.x[ct][3]};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
         const float av[8] = {R.m[kk][0][0], R.m[kk][0][1], R.m[kk][0][2], R.m[kk][0][3],
                              R.m[kk][1][0], R.m[kk][1][1], R.m[kk][1][2], R.m[kk][1][3]};
         bf16x8 ah, al;
         split8v(av, ah, al);
-        const bf16x8 bh = lds8(hH + m * CB_LD + 16 * kk + 8 * h);
-        const bf16x8 bl = lds8(hL + m * CB_LD + 16 * kk + 8 * h);
-        acc = mfma(ah, bh, acc);
-        acc = mfma(ah, bl, acc);
-        acc = mfma(al, bh, acc);
-    }
-    return acc;
-}
-
-// The wave's rows of the block into LDS (hi / lo, transposed) and, if dst,
-// into HBM ([key][value] fp32).
-__device__ __forceinline__ void comb_put(const f32x16 &x, bf16 *hH, bf16 *hL, float *dst, const int wave,
-                                         const int lane, const int col0) {
-    const int m = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float v4[4] = {x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]};
-        uint32_t hi0, lo0, hi1, lo1;
-        split2(v4[0], v4[1], hi0, lo0);
-        split2(v4[2], v4[3], hi1, lo1);
-        const int k = 32 * wave + 8 * i + 4 * h;
-        *reinterpret_cast<u32x2 *>(hH + m * CB_LD + k) = u32x2{hi0, hi1};
-        *reinterpret_cast<u32x2 *>(hL + m * CB_LD + k) = u32x2{lo0, lo1};
-        if (dst) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dst[(int64_t)(k + j) * DV + col0 + m] = v4[j];
+        for (int ct = 0; ct < 2; ++ct) {
+            acc[ct] = mfma16(ah, bh[kk][ct], acc[ct]);
+            acc[ct] = mfma16(ah, bl[kk][ct], acc[ct]);
+            acc[ct] = mfma16(al, bh[kk][ct], acc[ct]);
         }
     }
 }
 
-__global__ void __launch_bounds__(NTHREADS, 1) gdn_cp_combine_kernel(FwdParams p) {
+// The wave's rows of the block into LDS (hi / lo, transposed) and, if dst,
+// into HBM ([key][value] fp32).
+__device__ __forceinline__ void comb_put(const f32x4 (&x)[2], bf16 *hH, bf16 *hL, float *dst, const int wave,
+                                         const int lane, const int col0) {
+    const int m = lane & 15, g = lane >> 4;
+    const int k = 16 * wave + 4 * g;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        uint32_t hi0, lo0, hi1, lo1;
+        split2(x[ct][0], x[ct][1], hi0, lo0);
+        split2(x[ct][2], x[ct][3], hi1, lo1);
+        *reinterpret_cast<u32x2 *>(hH + (16 * ct + m) * CB_LD + k) = u32x2{hi0, hi1};
+        *reinterpret_cast<u32x2 *>(hL + (16 * ct + m) * CB_LD + k) = u32x2{lo0, lo1};
+        if (dst) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(k + jj) * DV + col0 + 16 * ct + m] = x[ct][jj];
+        }
+    }
+}
+
+__global__ void __launch_bounds__(NT_COMB, 1) gdn_cp_combine_kernel(FwdParams p) {
     __shared__ __attribute__((aligned(16))) bf16 hH[CB_COLS * CB_LD], hL[CB_COLS * CB_LD];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -1345,30 +1357,50 @@ __global__ void __launch_bounds__(NTHREADS, 1) gdn_cp_combine_kernel(FwdParams p
     if (R <= 1) return;
     {
         // H_start[0]: the initial state's block (or zeros)
-        f32x16 h0v;
-        const int m = lane & 31, h = lane >> 5;
+        f32x4 h0v[2];
+        const int m = lane & 15, g = lane >> 4;
         const float *src = p.h0 ? p.h0 + ((int64_t)n * p.Hv + j) * DK * DV : nullptr;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            h0v[e] = src ? src[(int64_t)(32 * wave + 8 * (e >> 2) + 4 * h + (e & 3)) * DV + col0 + m] : 0.f;
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                h0v[ct][jj] = src ? src[(int64_t)(16 * wave + 4 * g + jj) * DV + col0 + 16 * ct + m] : 0.f;
         comb_put(h0v, hH, hL, nullptr, wave, lane, col0);
     }
-    CombRegs A, B;
     auto seg_off = [&](int r) { return ((int64_t)(seg0 + r) * p.Hv + j) * DK * DV; };
-    comb_load(A, p.ws_m + seg_off(0), p.ws_s + seg_off(0), wave, lane, col0);
-    // two steps per trip so that the register sets alternate without copies
-    for (int r = 0; r + 1 < R; r += 2) {
-        if (r + 2 < R) comb_load(B, p.ws_m + seg_off(r + 1), p.ws_s + seg_off(r + 1), wave, lane, col0);
+    const int steps = R - 1;  // step r makes H_start[r + 1]
+    CombRegs C[3];
+    // Loads are issued unconditionally (past the last step they re-read the
+    // last step's operands, unused): with no branch around them the compiler
+    // can count them and waits only for the set a step consumes.
+    auto load = [&](CombRegs &X, int r) {
+        const int rr = min(r, steps - 1);
+        comb_load(X, p.ws_m + seg_off(rr), p.ws_s + seg_off(rr), wave, lane, col0);
+    };
+    auto step = [&](const CombRegs &X, int r) {
         __syncthreads();  // H_start[r] complete in LDS
-        f32x16 x = comb_step(A, hH, hL, lane);
+        f32x4 acc[2];
+        comb_step(X, hH, hL, lane, acc);
         __syncthreads();  // every wave has read H_start[r]
-        comb_put(x, hH, hL, p.ws_h + seg_off(r + 1), wave, lane, col0);
-        if (r + 2 >= R) break;
-        if (r + 3 < R) comb_load(A, p.ws_m + seg_off(r + 2), p.ws_s + seg_off(r + 2), wave, lane, col0);
-        __syncthreads();
-        x = comb_step(B, hH, hL, lane);
-        __syncthreads();
-        comb_put(x, hH, hL, p.ws_h + seg_off(r + 2), wave, lane, col0);
+        comb_put(acc, hH, hL, p.ws_h + seg_off(r + 1), wave, lane, col0);
+    };
+    load(C[0], 0);
+    load(C[1], 1);
+    // three register sets in rotation (unrolled by three so that the sets are
+    // fixed registers): the loads of step r + 2 go out before step r
+    int r = 0;
+    for (; r + 3 <= steps; r += 3) {
+        load(C[2], r + 2);
+        step(C[0], r);
+        load(C[0], r + 3);
+        step(C[1], r + 1);
+        load(C[1], r + 4);
+        step(C[2], r + 2);
+    }
+    if (r < steps) step(C[0], r);
+    if (r + 1 < steps) {
+        load(C[2], r + 2);
+        step(C[1], r + 1);
     }
 }
 
@@ -1429,7 +1461,7 @@ int launch_cp_exact(const FwdParams &p, void *stream) {
     int err = (int)hipGetLastError();
     if (err) return err;
     hipLaunchKernelGGL(gdn_cp_combine_kernel, dim3((unsigned)p.N * (unsigned)p.Hv * (unsigned)(DV / CB_COLS)),
-                       dim3(NTHREADS), 0,
+                       dim3(NT_COMB), 0,
                        (hipStream_t)stream, p);
     return (int)hipGetLastError();
 }
