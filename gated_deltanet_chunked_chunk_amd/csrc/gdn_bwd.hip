@@ -64,6 +64,7 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // k slot e of lane group g inside a 32-wide k step.  A step that reads any
@@ -331,11 +332,18 @@ __device__ __forceinline__ f32x4 mm_pp(f32x4 c, bf16x8 ah, bf16x8 al, bf16x8 bh,
 // row-major [row][col] arrays (st_split) or, transposed, into [col][row]
 // arrays where the lane's four rows are contiguous (st_split_t).
 __device__ __forceinline__ void split4(f32x4 v, bf16x4 &h, bf16x4 &l) {
+    uint32_t hw[2], lw[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        h[j] = (bf16)v[j];
-        l[j] = (bf16)(v[j] - (float)h[j]);
+    for (int i = 0; i < 2; ++i) {
+        const bf16x2 hh = {(bf16)v[2 * i], (bf16)v[2 * i + 1]};
+        hw[i] = __builtin_bit_cast(uint32_t, hh);
+        asm("" : "+v"(hw[i]));
+        const float h0 = __uint_as_float(hw[i] << 16), h1 = __uint_as_float(hw[i] & 0xffff0000u);
+        const bf16x2 ll = {(bf16)(v[2 * i] - h0), (bf16)(v[2 * i + 1] - h1)};
+        lw[i] = __builtin_bit_cast(uint32_t, ll);
     }
+    h = __builtin_bit_cast(bf16x4, (u32x2{hw[0], hw[1]}));
+    l = __builtin_bit_cast(bf16x4, (u32x2{lw[0], lw[1]}));
 }
 __device__ __forceinline__ void st_split(bf16 *hi, bf16 *lo, int ld, int r0, int c0, f32x4 v, int lane) {
     bf16x4 h, l;
@@ -434,6 +442,12 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     const float *dvc = p.dvp_ws + ((int64_t)cg * p.Hv + j) * CH * DV; // dv' [i][v]
     const float *vnc = p.vn + ((int64_t)cg * p.Hv + j) * CH * DV;     // v'  [i][v]
     const unsigned vstride = (unsigned)p.Hv * DV * 2;
+    // this chunk's first row of the per-(token, v-head) outputs; a row of token t
+    // lies t * Hv * 128 elements further (32-bit offsets inside a chunk)
+    const int64_t row_c = (e.row0 + (int64_t)c * CH) * p.Hv + j;
+    float *const dq_c = p.dq_ws + row_c * DK;
+    float *const dk_c = p.dk_ws + row_c * DK;
+    const unsigned tstride = (unsigned)p.Hv * DV;  // elements per token row (DK == DV)
 
     Rows<DV * 2 / 16> rv;  // V, stored once dO is dead
     {
@@ -592,8 +606,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         qsum = sum4g(qsum);
         if (g4 == 0) dGw[col] += sg * qsum;
         if (col < rows_valid) {
-            const int64_t off = ((e.row0 + (int64_t)c * CH + col) * p.Hv + j) * DK + 16 * wave + 4 * g4;
-            *reinterpret_cast<f32x4 *>(p.dq_ws + off) = sg * t1 + kq;
+            const unsigned off = (unsigned)col * tstride + 16 * wave + 4 * g4;
+            *reinterpret_cast<f32x4 *>(dq_c + off) = sg * t1 + kq;
         }
     }
     __syncthreads();  // v' and dO are dead: their tiles take dW and V
@@ -671,9 +685,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
                 if (r16 == 0) dbw[sr] += rvv;
                 const float dvv = s.bt[sr] * acc[jj];
                 if (sr < rows_valid) {
-                    const int64_t off = ((e.row0 + (int64_t)c * CH + sr) * p.Hv + j) * DV + col;
-                    if (p.grad_f32) static_cast<float *>(p.dv)[off] = dvv;
-                    else static_cast<bf16 *>(p.dv)[off] = (bf16)dvv;
+                    const unsigned off = (unsigned)sr * tstride + col;
+                    if (p.grad_f32) static_cast<float *>(p.dv)[row_c * DV + off] = dvv;
+                    else static_cast<bf16 *>(p.dv)[row_c * DV + off] = (bf16)dvv;
                 }
             }
         }
@@ -748,8 +762,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         }
         const int tok = 16 * ct + r16;
         if (tok < rows_valid) {
-            const int64_t off = ((e.row0 + (int64_t)c * CH + tok) * p.Hv + j) * DK + 16 * wave + 4 * g4;
-            *reinterpret_cast<f32x4 *>(p.dk_ws + off) = dkt[ct];
+            const unsigned off = (unsigned)tok * tstride + 16 * wave + 4 * g4;
+            *reinterpret_cast<f32x4 *>(dk_c + off) = dkt[ct];
         }
     }
     __syncthreads();
