@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <queue>
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
@@ -54,17 +55,67 @@ int32_t count_segments(const gdn_fwd_desc *d, int32_t L) {
     return total > INT32_MAX ? INT32_MAX : (int32_t)total;
 }
 
-// AUTO: pick L minimising (waves of workgroups over the CUs) x (L + expected
-// warm-up), assuming one resident workgroup per CU and a two-chunk warm-up.
-int32_t auto_segment_chunks(const gdn_fwd_desc *d, int32_t max_chunks) {
+// AUTO's cost of a segment length L: the makespan of the kernel's grid when
+// workgroups start in grid order on the first free CU (one resident per CU),
+// each taking its segment's chunks plus an expected warm-up (two chunks,
+// fewer near a sequence edge) plus half a chunk of fixed cost, in chunk units.
+// Varlen batches have segments of unequal length, which a count of workgroup
+// waves misses.  Grids too large to simulate cheaply fall back to
+// waves x (L + 2).  REVERSE: the warm-up lies after the segment (the backward's
+// reverse pass); per_segment: workgroups per (segment, v-head).
+double segment_cost(const gdn_fwd_desc *d, int32_t L, int32_t per_segment, bool reverse, double bound) {
+    const int64_t wgs = (int64_t)count_segments(d, L) * d->H_v * per_segment;
+    if (wgs > 16384) return std::ceil((double)wgs / gdn::kNumCUs) * (L + 2);
+    const int32_t nseq = d->cu_seqlens_host ? d->num_seqs : (int32_t)d->B;
+    auto seq_len = [&](int32_t n) {
+        return d->cu_seqlens_host ? (int64_t)d->cu_seqlens_host[n + 1] - d->cu_seqlens_host[n] : (int64_t)d->T;
+    };
+    auto job = [&](int32_t nt, int32_t r) {
+        const int32_t c0 = r * L, cnt = std::max(0, std::min(L, nt - c0));
+        const int32_t warm = reverse ? std::min(2, std::max(0, nt - c0 - cnt)) : std::min(2, c0);
+        return cnt + warm + 0.5;
+    };
+    // a lower bound first (all CUs busy to the end, and the longest job): a
+    // candidate that cannot beat the best so far is not simulated
+    double total = 0.0, longest = 0.0;
+    for (int32_t n = 0; n < nseq; ++n) {
+        const int64_t len = seq_len(n);
+        const int32_t nt = gdn::seq_chunks(len), ns = gdn::seq_segments(len, L);
+        for (int32_t r = 0; r < ns; ++r) {
+            const double t = job(nt, r);
+            total += t * d->H_v * per_segment;
+            longest = std::max(longest, t);
+        }
+    }
+    const double lb = std::max(total / gdn::kNumCUs, longest);
+    if (lb >= bound) return lb;
+    std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+    for (int i = 0; i < gdn::kNumCUs; ++i) free_at.push(0.0);
+    double end = 0.0;
+    for (int32_t n = 0; n < nseq; ++n) {
+        const int64_t len = seq_len(n);
+        const int32_t nt = gdn::seq_chunks(len), ns = gdn::seq_segments(len, L);
+        for (int32_t r = 0; r < ns; ++r) {
+            const double t = job(nt, r);
+            for (int64_t w = 0; w < (int64_t)d->H_v * per_segment; ++w) {
+                const double s0 = free_at.top();
+                free_at.pop();
+                free_at.push(s0 + t);
+                end = std::max(end, s0 + t);
+            }
+        }
+    }
+    return end;
+}
+
+// AUTO: the candidate segment length with the smallest cost.
+int32_t auto_segment_chunks(const gdn_fwd_desc *d, int32_t max_chunks, int32_t per_segment, bool reverse) {
     static const int32_t cands[] = {8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256};
     int32_t bestL = std::max(1, max_chunks);
-    double best = (double)((int64_t)d->H_v * count_segments(d, bestL) + gdn::kNumCUs - 1) / gdn::kNumCUs;
-    best = std::ceil(best) * bestL;
+    double best = segment_cost(d, bestL, per_segment, reverse, 1e300);
     for (int32_t L : cands) {
         if (L >= max_chunks) break;
-        const double waves = std::ceil((double)d->H_v * count_segments(d, L) / gdn::kNumCUs);
-        const double cost = waves * (L + 2);
+        const double cost = segment_cost(d, L, per_segment, reverse, best);
         if (cost < best) {
             best = cost;
             bestL = L;
@@ -140,7 +191,7 @@ int make_plan(const gdn_fwd_desc *d, Plan *P) {
         } else if (d->cp_lambda > 0.f) {
             L = (int32_t)std::lround(d->cp_lambda * std::sqrt((double)P->max_chunks));
         } else {
-            L = auto_segment_chunks(d, P->max_chunks);
+            L = auto_segment_chunks(d, P->max_chunks, 1, false);
         }
         L = std::max(1, std::min(L, std::max(1, P->max_chunks)));
         if (mode == GDN_CP_AUTO) mode = GDN_CP_WARMUP;
@@ -213,16 +264,7 @@ int make_bwd_plan(const gdn_bwd_desc *bd, BwdPlan *B) {
         } else if (d->cp_lambda > 0.f) {
             L = (int32_t)std::lround(d->cp_lambda * std::sqrt((double)P.max_chunks));
         } else {
-            static const int32_t cands[] = {8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256};
-            double best = std::ceil(2.0 * d->H_v * count_segments(d, L) / gdn::kNumCUs) * L;
-            for (int32_t c : cands) {
-                if (c >= P.max_chunks) break;
-                const double cost = std::ceil(2.0 * d->H_v * count_segments(d, c) / gdn::kNumCUs) * (c + 2);
-                if (cost < best) {
-                    best = cost;
-                    L = c;
-                }
-            }
+            L = auto_segment_chunks(d, P.max_chunks, 2, true);
         }
         L = std::max(1, std::min(L, std::max(1, P.max_chunks)));
         if (mode == GDN_CP_AUTO) mode = GDN_CP_WARMUP;
