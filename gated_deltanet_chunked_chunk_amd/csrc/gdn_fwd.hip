@@ -25,7 +25,9 @@
 // essay, "formula restructuring"): products of two exact bf16 inputs (K K^T,
 // Q K^T, K^T T~^T) use one bf16 MFMA; operands that carry fp32 values which
 // feed the output or the state with full weight are split into hi + lo bf16
-// pairs: T diag(beta), P, v', the decayed v', and H.  Decays and beta are fp32
+// pairs: T diag(beta), P, v', the decayed v', and H (in Q H only when o is
+// fp32: a bf16 o takes Q times the bf16-rounded H, whose error stays below
+// the output's own rounding and never reaches the state).  Decays and beta are fp32
 // row/column scales; every exponent is a non-positive difference G_i - G_s
 // (masked before the exp), so nothing overflows.
 //
@@ -734,6 +736,10 @@ __device__ __forceinline__ void u9_lean(const Smem8 &s, const int lane, const in
 // operand, one column tile ct per call: qh[rt][ct] lane (m, g) holds value
 // column 16 ct + 4 g + j (of this wave's 32) of query row 16 rt + m.  It later accumulates (scale P v')^T in
 // place, and each lane then owns four consecutive output columns of one row.
+// SPLIT: the state enters as hi + lo bf16 parts (fp32-class product, for fp32
+// outputs); otherwise as its bf16 rounding alone, one MFMA per step, for bf16
+// outputs, whose own rounding is the larger error.
+template <bool SPLIT>
 __device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int ct,
                                     const int buf, const float scale, const int ln) {
     const int m = ln & 15;
@@ -748,16 +754,58 @@ __device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f
     for (int rt = 0; rt < 4; ++rt) qh[rt][ct] = f32x4{};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 hh, hl;
-        split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh, hl);
+        if (SPLIT) {
+            bf16x8 hh, hl;
+            split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh, hl);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            qh[rt][ct] = mfma16(hh, qa[kk][rt], qh[rt][ct]);
-            qh[rt][ct] = mfma16(hl, qa[kk][rt], qh[rt][ct]);
+            for (int rt = 0; rt < 4; ++rt) {
+                qh[rt][ct] = mfma16(hh, qa[kk][rt], qh[rt][ct]);
+                qh[rt][ct] = mfma16(hl, qa[kk][rt], qh[rt][ct]);
+            }
+        } else {
+            const f32x4 &t0 = hacc[ct][2 * kk], &t1 = hacc[ct][2 * kk + 1];
+            const bf16x8 hh = {(bf16)t0[0], (bf16)t0[1], (bf16)t0[2], (bf16)t0[3],
+                               (bf16)t1[0], (bf16)t1[1], (bf16)t1[2], (bf16)t1[3]};
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) qh[rt][ct] = mfma16(hh, qa[kk][rt], qh[rt][ct]);
         }
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) qh[rt][ct] *= scale * s.gam[buf][16 * rt + m];  // this lane's query row
+}
+
+// Both column tiles at once from the bf16-rounded state (bf16 outputs): the
+// Q fragments are read once for the two tiles.
+__device__ __forceinline__ void qh9_both(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2],
+                                         const int buf, const float scale, const int ln) {
+    const int m = ln & 15;
+    const bf16 *Q = s.q[buf];
+    bf16x8 qa[4][4];  // [k step][row tile]
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) qa[kk][rt] = frag_rp(Q, 16 * rt, 32 * kk, ln);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] = f32x4{};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const f32x4 &t0 = hacc[ct][2 * kk], &t1 = hacc[ct][2 * kk + 1];
+            const bf16x8 hh = {(bf16)t0[0], (bf16)t0[1], (bf16)t0[2], (bf16)t0[3],
+                               (bf16)t1[0], (bf16)t1[1], (bf16)t1[2], (bf16)t1[3]};
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) qh[rt][ct] = mfma16(hh, qa[kk][rt], qh[rt][ct]);
+        }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const float f = scale * s.gam[buf][16 * rt + m];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] *= f;
+    }
 }
 
 // v' = U - W H (vp enters holding U)
@@ -811,6 +859,7 @@ __device__ __forceinline__ void wh8_lean(const Smem8 &s, const f32x4 (&hacc)[2][
 // query row 16 rt + m, stored as one 16-byte (fp32) or 8-byte (bf16) piece
 // through a buffer resource over the chunk's rows (rows past the sequence end
 // are dropped by the hardware range check).
+template <bool OF32>
 __device__ __forceinline__ void out9(const Smem8 &s, const FwdParams &p, const char *obase, const int seq_len,
                                      const f32x4 (&vp)[4][2], f32x4 (&acc)[4][2], const int c, const int sw,
                                      const int ln) {
@@ -839,7 +888,7 @@ __device__ __forceinline__ void out9(const Smem8 &s, const FwdParams &p, const c
             }
         }
     }
-    const unsigned es = p.o_f32 ? 4u : 2u;
+    const unsigned es = OF32 ? 4u : 2u;
     const unsigned rstride = (unsigned)p.Hv * DV * es;
     const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(obase, rstride, c, seq_len);
 #pragma unroll
@@ -848,7 +897,7 @@ __device__ __forceinline__ void out9(const Smem8 &s, const FwdParams &p, const c
         for (int ct = 0; ct < 2; ++ct) {
             const f32x4 w = acc[rt][ct];
             const unsigned off = (unsigned)(16 * rt + m) * rstride + (unsigned)(32 * sw + 16 * ct + 4 * g) * es;
-            if (p.o_f32) {
+            if (OF32) {
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), ro, (int)off, 0, 0);
             } else {
                 const bf16x4 h = {(bf16)w[0], (bf16)w[1], (bf16)w[2], (bf16)w[3]};
@@ -1019,7 +1068,7 @@ __device__ __forceinline__ void store_state8(const f32x4 (&t)[2][8], float *dst,
 // has the state's shape), both on the chunk operands the preparation waves
 // 8..11 build once; no output, no warm-up.  The segment's end state is then
 // M H_start + S.
-template <bool PRE>
+template <bool PRE, bool OF32>
 __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     Smem8 &s = *reinterpret_cast<Smem8 *>(smem_raw);
@@ -1121,7 +1170,7 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             if (!from_h0 && p.cp_mode == 1 /* EXACT */) src = p.ws_h + ((int64_t)seg * p.Hv + j) * DK * DV;
             if (src) load_state8(hacc, src, wave, lane);
         }
-        const int64_t oes = p.o_f32 ? 4 : 2;
+        const int64_t oes = OF32 ? 4 : 2;
         const char *obase = static_cast<const char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes;
         f32x4 vp[4][2], qh[4][2];  // vp: U, then v' of this chunk
         const int cbase = (!PRE && (p.h_out || p.vn_out)) ? seq_chunk_base(p, e.n, lane) : 0;
@@ -1157,7 +1206,7 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             if (!PRE && chain && out && p.vn_out)
                 store_vn8(vp, p.vn_out + ((int64_t)(cbase + c) * p.Hv + j) * CH * DV, wave, lane_now());
             lds_barrier();
-            if (!PRE && chain && out) out9(s, p, obase, e.seq_len, vp, qh, c, wave, lane_now());
+            if (!PRE && chain && out) out9<OF32>(s, p, obase, e.seq_len, vp, qh, c, wave, lane_now());
             lds_barrier();
             if (chain) {
                 if (PRE) hupd9_lean(s, hacc, vp, b, lane_now());
@@ -1165,10 +1214,13 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             }
             lds_barrier();
             if (c + 2 < c_end) dma_tile<NSTATE>(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, lane_now());
-            if (!PRE && prep && c + 1 >= e.c_begin) qh9(s, hacc, qh, 0, nb, p.scale, lane_now());
+            if (!PRE && prep && c + 1 >= e.c_begin) {
+                if (OF32) qh9<true>(s, hacc, qh, 0, nb, p.scale, lane_now());
+                else qh9_both(s, hacc, qh, nb, p.scale, lane_now());
+            }
             lds_barrier();
             if (!PRE && prep && c + 1 >= e.c_begin) {
-                qh9(s, hacc, qh, 1, nb, p.scale, lane_now());
+                if (OF32) qh9<true>(s, hacc, qh, 1, nb, p.scale, lane_now());
                 if (p.h_out) store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
             }
         }
@@ -1234,11 +1286,12 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
 
 // One workgroup per CU (its LDS footprint): two waves per SIMD for the forward,
 // three for the pre-pass.
+template <bool OF32>
 __global__ void __launch_bounds__(NT8, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) gdn_fwd_main_kernel(FwdParams p) {
-    fwd_pass<false>(p);
+    fwd_pass<false, OF32>(p);
 }
 constexpr int NT_PRE = 768;
-__global__ void __launch_bounds__(NT_PRE, 1) gdn_cp_prepass_kernel(FwdParams p) { fwd_pass<true>(p); }
+__global__ void __launch_bounds__(NT_PRE, 1) gdn_cp_prepass_kernel(FwdParams p) { fwd_pass<true, true>(p); }
 
 // ---------------------------------------------------------------- exact context parallelism
 // Combine (sequential over a sequence's segments): H_start[0] = initial state,
@@ -1441,12 +1494,19 @@ __global__ void __launch_bounds__(256) gdn_chunk_cumsum_kernel(const float *g, f
 // ---------------------------------------------------------------- launchers
 int launch_fwd_main(const FwdParams &p, void *stream) {
     static const size_t smem = sizeof(Smem8);
-    static const int attr_rc =
-        (int)hipFuncSetAttribute((const void *)gdn_fwd_main_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)smem);
+    static const int attr_rc = [] {
+        const int rc = (int)hipFuncSetAttribute((const void *)gdn_fwd_main_kernel<false>,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        return rc ? rc
+                  : (int)hipFuncSetAttribute((const void *)gdn_fwd_main_kernel<true>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    }();
     if (attr_rc != 0) return attr_rc;
     const unsigned grid = (unsigned)p.num_segments * (unsigned)p.Hv;
-    hipLaunchKernelGGL(gdn_fwd_main_kernel, dim3(grid), dim3(NT8), smem, (hipStream_t)stream, p);
+    if (p.o_f32)
+        hipLaunchKernelGGL(gdn_fwd_main_kernel<true>, dim3(grid), dim3(NT8), smem, (hipStream_t)stream, p);
+    else
+        hipLaunchKernelGGL(gdn_fwd_main_kernel<false>, dim3(grid), dim3(NT8), smem, (hipStream_t)stream, p);
     return (int)hipGetLastError();
 }
 
