@@ -189,11 +189,15 @@ __device__ __forceinline__ SegEntry find_segment(const FwdParams &p, int seg, in
 // small dependent steps is the longer of the two).
 constexpr int NT8 = 512;
 constexpr int TS8 = 32 + 4;    // fp32 row stride of the transposed 32 x 32 diagonal blocks
-constexpr int TILE = CH * DK;  // bf16 elements of one 64-token x 128 tile (K, Q and V alike)
+constexpr int TLD = DK + 8;    // bf16 row stride of the K, Q and V tiles: 272 bytes
+constexpr int TSLOT = TLD / 8;  // 16-byte slots per tile row: 16 of data, 1 of padding
+constexpr int TILE = CH * TLD;  // bf16 elements of one 64-token x 128 tile (K, Q and V alike)
+constexpr int TLOADS = CH * TSLOT / 64;  // 1 KB wave loads per tile (17)
+static_assert(CH * TSLOT % 64 == 0, "a tile is a whole number of wave loads");
 static_assert(DK == DV, "K, Q and V tiles share one layout");
 
 struct __attribute__((aligned(16))) Smem8 {
-    bf16 k[2][TILE];                  // K by chunk parity (row = token, pieces swizzled)
+    bf16 k[2][TILE];                  // K by chunk parity (row = token, padded rows)
     bf16 q[2][TILE];                  // Q by chunk parity
     bf16 v[TILE];                     // V of the state pass's next chunk
     float a[CH * AS];                 // A, inverted in place into T
@@ -228,13 +232,13 @@ __device__ __forceinline__ void split_pair(const f32x4 &t0, const f32x4 &t1, bf1
     split8v(x, hi, lo);
 }
 
-// ---- 64 x 128 bf16 tiles in LDS.  Row r (256 bytes) keeps its sixteen
-// 16-byte pieces in the order piece ^ swz(r): sixteen consecutive rows at one
-// piece (row-fragment reads) and eight aligned rows at one pair of pieces
-// (transposing reads) fall in distinct banks, while four rows stay 1 KB of
-// contiguous LDS, the footprint of one wave's direct load.
-__device__ __forceinline__ int swz(int r) { return (2 * r + (r >> 3)) & 15; }
-__device__ __forceinline__ int tix(int r, int c) { return r * DK + (((c >> 3) ^ swz(r)) << 3) + (c & 7); }
+// ---- 64 x 128 bf16 tiles in LDS with rows of 272 bytes (256 of data and one
+// 16-byte pad slot): a row starts 4 banks after the previous one, so sixteen
+// consecutive rows at one column (row-fragment reads, 16 bytes a lane) and
+// sixteen rows at four column offsets (transposing or 8-byte reads) spread
+// over all banks at the minimum number of LDS cycles, and every fragment read
+// is a per-lane base address plus a constant offset.
+__device__ __forceinline__ int tix(int r, int c) { return r * TLD + c; }
 
 __device__ __forceinline__ bf16x4 tr4(const bf16 *p) {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -270,23 +274,25 @@ __device__ __forceinline__ bf16x8 frag_rp(const bf16 *X, const int r0, const int
 // Rows beyond a chunk's buffer resource (past the sequence end) arrive as zeros.
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Rows 4 i .. 4 i + 3 of a 64 x 128 bf16 tile: lane l fills LDS piece l % 16 of
-// row 4 i + l / 16, i.e. logical piece (l % 16) ^ swz(row).
-__device__ __forceinline__ void dma_rows(bf16 *tile, const __amdgpu_buffer_rsrc_t r, const unsigned stride, const int i,
-                                         const int lane) {
-    const int row = 4 * i + (lane >> 4);
-    const unsigned off = (unsigned)row * stride + 16u * (unsigned)((lane & 15) ^ swz(row));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + 4 * i * DK), 16, (int)off, 0, 0, 0);
-}
-
-// Part `part` of PARTS (rows 64 part / PARTS ..) of chunk c's tile.
+// Part `part` of PARTS of chunk c's tile: wave loads part, part + PARTS, ...
+// of the tile's 17.  Lane l of load i fills 16-byte slot 64 i + l of the
+// padded tile, i.e. row (64 i + l) / 17 and piece (64 i + l) % 17; the pad
+// piece takes an offset past any buffer and arrives as zeros.
 template <int PARTS = 4>
 __device__ __forceinline__ void dma_tile(bf16 *tile, const char *base, const unsigned stride, const int c,
                                          const int seq_len, const int part, const int lane) {
-    constexpr int GROUPS = 16 / PARTS;  // 4-row groups per part
+    constexpr int NI = (TLOADS + PARTS - 1) / PARTS;
     const __amdgpu_buffer_rsrc_t r = chunk_rsrc(base, stride, c, seq_len);
 #pragma unroll
-    for (int i = 0; i < GROUPS; ++i) dma_rows(tile, r, stride, GROUPS * part + i, lane);
+    for (int n = 0; n < NI; ++n) {
+        const int i = part + n * PARTS;
+        if (i < TLOADS) {
+            const int slot = 64 * i + lane;
+            const int row = slot / TSLOT, piece = slot - TSLOT * row;
+            const unsigned off = piece < 16 ? (unsigned)row * stride + 16u * (unsigned)piece : 0x80000000u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + 512 * i), 16, (int)off, 0, 0, 0);
+        }
+    }
 }
 
 // g (preparation wave 0) and beta (wave 1) of chunk c, one token per lane.
