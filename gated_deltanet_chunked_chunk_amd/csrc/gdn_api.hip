@@ -299,10 +299,10 @@ int make_bwd_plan(const gdn_bwd_desc *bd, BwdPlan *B) {
     off = align_up(off + n_h * 4);
     B->off_dvp = off;
     off = align_up(off + (size_t)P.total_chunks * d->H_v * gdn::kChunk * d->V * 4);
-    B->off_dq = off;
-    off = align_up(off + rows * d->H_v * d->K * 4);
+    B->off_dq = off;  // partial key-head sums of dq and dk (fp32 [rows][H_qk][K])
+    off = align_up(off + rows * d->H_qk * d->K * 4);
     B->off_dk = off;
-    off = align_up(off + rows * d->H_v * d->K * 4);
+    off = align_up(off + rows * d->H_qk * d->K * 4);
     if (mode == GDN_CP_EXACT) {
         const size_t st = (size_t)B->num_segments * d->H_v * d->K * d->V * 4;
         B->off_cs = off;
@@ -454,7 +454,7 @@ int gdn_bwd_plan(const gdn_bwd_desc *d, gdn_bwd_plan_info *out) {
         out->warmup_chunks = B.cp_mode == GDN_CP_WARMUP ? B.warmup : 0;
         out->cp_mode = B.cp_mode;
         out->workgroups_reverse = B.num_segments * d->fwd.H_v * 2;
-        out->workgroups_local = B.entries * d->fwd.H_v;
+        out->workgroups_local = B.entries * d->fwd.H_qk;
     }
     g_last_error.clear();
     return GDN_OK;

@@ -27,9 +27,10 @@
 //         in-chunk cumsum of dG.
 //
 // Kernels: gdn_bwd_dh_kernel (reverse pass, one workgroup per (segment,
-// v-head, half of V): the V columns of dh are independent), gdn_bwd_local_kernel
-// (one workgroup per (chunk, v-head)), gdn_bwd_group_sum_kernel (dq, dk of a
-// key head = sum over its v-heads).  h and T come from the forward (its
+// v-head, half of V): the V columns of dh are independent) and
+// gdn_bwd_local_kernel (one workgroup per (chunk, key head), running the key
+// head's v-heads in turn, so that dq and dk of the key head, the sums over its
+// v-heads, add up in the workgroup).  h and T come from the forward (its
 // low-level outputs); dh' and dv' of every chunk go through the workspace.
 //
 // Products: v_mfma_f32_16x16x32_bf16 on 16 x 16 output tiles.  Operands that
@@ -414,7 +415,24 @@ __device__ __forceinline__ void load_tile_f32(Rows<DV * 4 / 16> &R, const float 
         R.x[i] = *reinterpret_cast<const u32x4 *>(src + 4 * (tid + i * NT));
 }
 
-// One workgroup per (chunk, v-head).  The key-dim results dq, dk and dW are
+// dq or dk of a key head = the sum over its v-heads: the workgroup runs them
+// one after another and every lane adds its four values to what it stored for
+// the previous v-head (fp32 workspace, the same lane and address); the last
+// v-head writes the output in its dtype.
+__device__ __forceinline__ void group_put(const BwdParams &p, float *ws, void *out, int64_t idx, f32x4 v, bool first,
+                                          bool last) {
+    if (!first) v += *reinterpret_cast<const f32x4 *>(ws + idx);
+    if (!last) {
+        *reinterpret_cast<f32x4 *>(ws + idx) = v;
+    } else if (p.grad_f32) {
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(out) + idx) = v;
+    } else {
+        *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(out) + idx) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    }
+}
+
+// One workgroup per (chunk, key head), running the key head's v-heads in turn.
+// The key-dim results dq, dk and dW are
 // computed transposed ((key dim, token) tiles): every product with h or dh'
 // then contracts over the value dim, and wave w owns key dims 16 w .. +15, so
 // it reads (and splits) its 16 rows of h and dh' once.  64 x 64 results: wave
@@ -426,28 +444,36 @@ __device__ __forceinline__ void load_tile_f32(Rows<DV * 4 / 16> &R, const float 
 __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     SmemLoc &s = *reinterpret_cast<SmemLoc *>(smem_raw);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int ent = blockIdx.x / p.Hv;
-    const int j = blockIdx.x - ent * p.Hv;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ent = blockIdx.x / p.Hqk;
+    const int iq = blockIdx.x - ent * p.Hqk;
     if (ent >= p.num_chunk_entries) return;
-    const Where e = find_segment(p.cu, p.N, p.T, 1, ent, lane);
+    const Where e = find_segment(p.cu, p.N, p.T, 1, ent, threadIdx.x & 63);
     if (e.n < 0 || e.c_count == 0) return;
     const int c = e.c_begin;
-    const int cg = seq_chunk_base(p.cu, p.T, e.n, lane) + c;
-    const int iq = j / p.group;
-    const int g4 = lane >> 4, r16 = lane & 15;
+    const int cg = seq_chunk_base(p.cu, p.T, e.n, threadIdx.x & 63) + c;
+    const unsigned vstride = (unsigned)p.Hv * DV * 2;
+    const unsigned tstride = (unsigned)p.Hv * DV;   // per-v-head outputs (dv): elements per token row
+    const unsigned qstride = (unsigned)p.Hqk * DK;  // per-key-head sums (dq, dk): elements per token row
+    // this chunk's first row of the key-head sums, in the workspace and the output alike
+    const int64_t rowq_c = (e.row0 + (int64_t)c * CH) * p.Hqk + iq;
+
+    // the key head's v-heads one after another; dq and dk add up across them
+    for (int jj = 0; jj < p.group; ++jj) {
+    // an opaque thread index per v-head: lane-derived addresses are computed
+    // inside the loop, not hoisted out of it and held live across all of it
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, g4 = lane >> 4, r16 = lane & 15;
+    const int j = iq * p.group + jj;
+    const bool first = jj == 0, last = jj == p.group - 1;
     const float *hc = p.h + ((int64_t)cg * p.Hv + j) * DK * DV;       // chunk-start state [d][v]
     const float *dhc = p.dh_ws + ((int64_t)cg * p.Hv + j) * DK * DV;  // gradient wrt the state after the chunk
     const float *dvc = p.dvp_ws + ((int64_t)cg * p.Hv + j) * CH * DV; // dv' [i][v]
     const float *vnc = p.vn + ((int64_t)cg * p.Hv + j) * CH * DV;     // v'  [i][v]
-    const unsigned vstride = (unsigned)p.Hv * DV * 2;
     // this chunk's first row of the per-(token, v-head) outputs; a row of token t
     // lies t * Hv * 128 elements further (32-bit offsets inside a chunk)
     const int64_t row_c = (e.row0 + (int64_t)c * CH) * p.Hv + j;
-    float *const dq_c = p.dq_ws + row_c * DK;
-    float *const dk_c = p.dk_ws + row_c * DK;
-    const unsigned tstride = (unsigned)p.Hv * DV;  // elements per token row (DK == DV)
 
     Rows<DV * 2 / 16> rv;  // V, stored once dO is dead
     {
@@ -605,10 +631,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         for (int jj = 0; jj < 4; ++jj) qsum += (float)s.q[col * LK + 16 * wave + 4 * g4 + jj] * t1[jj];
         qsum = sum4g(qsum);
         if (g4 == 0) dGw[col] += sg * qsum;
-        if (col < rows_valid) {
-            const unsigned off = (unsigned)col * tstride + 16 * wave + 4 * g4;
-            *reinterpret_cast<f32x4 *>(dq_c + off) = sg * t1 + kq;
-        }
+        if (col < rows_valid)
+            group_put(p, p.dq_ws, p.dq, rowq_c * DK + (unsigned)col * qstride + 16 * wave + 4 * g4, sg * t1 + kq,
+                      first, last);
     }
     __syncthreads();  // v' and dO are dead: their tiles take dW and V
 
@@ -761,10 +786,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
                             fr_tr(s.pL + 16 * ct, L64, 32 * kk, lane));
         }
         const int tok = 16 * ct + r16;
-        if (tok < rows_valid) {
-            const unsigned off = (unsigned)tok * tstride + 16 * wave + 4 * g4;
-            *reinterpret_cast<f32x4 *>(dk_c + off) = dkt[ct];
-        }
+        if (tok < rows_valid)
+            group_put(p, p.dk_ws, p.dk, rowq_c * DK + (unsigned)tok * qstride + 16 * wave + 4 * g4, dkt[ct], first,
+                      last);
     }
     __syncthreads();
 
@@ -787,6 +811,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             p.dg[off] = x;
             p.dbeta[off] = db;
         }
+    }
+    __syncthreads();  // the next v-head's tiles overwrite LDS
     }
 }
 
@@ -1143,36 +1169,6 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_cp_combine_kernel(BwdParams p) 
     }
 }
 
-// ---------------------------------------------------------------- key-head sums
-// dq, dk of key head i = sum over its v-heads i G .. i G + G - 1 of the per-v-head
-// partials; four elements per thread.
-__global__ void __launch_bounds__(256) gdn_bwd_group_sum_kernel(BwdParams p) {
-    const int64_t n4 = p.rows * p.Hqk * DK / 4;
-    for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < n4; x += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t e0 = 4 * x;
-        const int64_t row = e0 / ((int64_t)p.Hqk * DK);
-        const int rem = (int)(e0 - row * p.Hqk * DK);
-        const int iq = rem / DK, d = rem - iq * DK;
-        f32x4 sq = f32x4{}, sk = f32x4{};
-        for (int jj = 0; jj < p.group; ++jj) {
-            const int64_t src = (row * p.Hv + iq * p.group + jj) * DK + d;
-            sq += *reinterpret_cast<const f32x4 *>(p.dq_ws + src);
-            sk += *reinterpret_cast<const f32x4 *>(p.dk_ws + src);
-        }
-        if (p.grad_f32) {
-            *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dq) + e0) = sq;
-            *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dk) + e0) = sk;
-        } else {
-            bf16 *oq = static_cast<bf16 *>(p.dq) + e0, *ok = static_cast<bf16 *>(p.dk) + e0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                oq[t] = (bf16)sq[t];
-                ok[t] = (bf16)sk[t];
-            }
-        }
-    }
-}
-
 }  // namespace bwdk
 
 int launch_bwd(const BwdParams &p, void *stream) {
@@ -1208,13 +1204,8 @@ int launch_bwd(const BwdParams &p, void *stream) {
         if (err != hipSuccess) return (int)err;
     }
     if (p.num_chunk_entries > 0 && p.rows > 0) {
-        hipLaunchKernelGGL(bwdk::gdn_bwd_local_kernel, dim3((unsigned)(p.num_chunk_entries * p.Hv)), dim3(bwdk::NT),
+        hipLaunchKernelGGL(bwdk::gdn_bwd_local_kernel, dim3((unsigned)(p.num_chunk_entries * p.Hqk)), dim3(bwdk::NT),
                            sizeof(bwdk::SmemLoc), st, p);
-        err = hipGetLastError();
-        if (err != hipSuccess) return (int)err;
-        const int64_t n4 = p.rows * p.Hqk * kDimK / 4;
-        const unsigned blocks = (unsigned)std::min<int64_t>((n4 + 255) / 256, 16384);
-        hipLaunchKernelGGL(bwdk::gdn_bwd_group_sum_kernel, dim3(blocks), dim3(256), 0, st, p);
         err = hipGetLastError();
         if (err != hipSuccess) return (int)err;
     }

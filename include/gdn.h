@@ -202,7 +202,7 @@ typedef struct {
     int32_t warmup_chunks;      /* window cap of the reverse pass, 0 when CP is off */
     int32_t cp_mode;            /* resolved mode of the reverse pass (OFF, EXACT or WARMUP) */
     int32_t workgroups_reverse; /* reverse-pass workgroups = num_segments * H_v * 2 */
-    int32_t workgroups_local;   /* per-chunk workgroups = (total_chunks + empty sequences) * H_v */
+    int32_t workgroups_local;   /* per-chunk workgroups = (total_chunks + empty sequences) * H_qk */
 } gdn_bwd_plan_info;
 
 typedef struct {

@@ -178,11 +178,11 @@ def test_bwd_plan_layout_and_workspace():
     p = G.bwd_plan(bdesc(T=32768, H_qk=4, H_v=16, has_h0=True, has_dht=True))
     assert p["total_chunks"] == 512 and p["cp"] == "warmup"
     assert p["workgroups_reverse"] == p["num_segments"] * 16 * 2
-    assert p["workgroups_local"] == 512 * 16
-    rows, hv, K = 32768, 16, 128
+    assert p["workgroups_local"] == 512 * 4  # one per (chunk, key head): its v-heads run in turn
+    rows, hv, hqk, K = 32768, 16, 4, 128
     n_h = 512 * hv * K * K * 4
     dvp = 512 * hv * 64 * K * 4
-    dqk = 2 * rows * hv * K * 4
+    dqk = 2 * rows * hqk * K * 4  # partial key-head sums of dq and dk
     recompute = rows * hv * K * 2 + n_h + rows * hv * 64 * 4 + dvp
     assert p["workspace_bytes"] == n_h + dvp + dqk + recompute
     saved = G.bwd_plan(bdesc(T=32768, H_qk=4, H_v=16, saved_fwd=True))
@@ -213,7 +213,7 @@ def test_bwd_plan_varlen_entries():
     cu = torch.tensor([0, 100, 100, 300], dtype=torch.int32)
     p = G.bwd_plan(bdesc(T=300, H_qk=1, H_v=2, cu_host=cu, cp="off"))
     assert p["total_chunks"] == 2 + 0 + 4
-    assert p["workgroups_local"] == (6 + 1) * 2  # one entry for the empty sequence
+    assert p["workgroups_local"] == (6 + 1) * 1  # one entry for the empty sequence, one workgroup per key head
 
 
 def test_bwd_validation_happens_before_any_launch():
