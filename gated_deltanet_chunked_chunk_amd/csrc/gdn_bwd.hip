@@ -458,6 +458,18 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     // this chunk's first row of the key-head sums, in the workspace and the output alike
     const int64_t rowq_c = (e.row0 + (int64_t)c * CH) * p.Hqk + iq;
 
+    // K and Q belong to the key head: loaded once into LDS, where they stay for
+    // all of its v-heads (the first barrier below publishes them)
+    {
+        const unsigned kstride = (unsigned)p.Hqk * DK * 2;
+        const int tid = threadIdx.x;
+        Rows<DK * 2 / 16> rk, rq;
+        load_rows(rk, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
+        load_rows(rq, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
+        store_rows_ld(s.k, rk, LK, tid);
+        store_rows_ld(s.q, rq, LK, tid);
+    }
+
     // the key head's v-heads one after another; dq and dk add up across them
     for (int jj = 0; jj < p.group; ++jj) {
     // an opaque thread index per v-head: lane-derived addresses are computed
@@ -477,13 +489,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
 
     Rows<DV * 2 / 16> rv;  // V, stored once dO is dead
     {
-        const unsigned kstride = (unsigned)p.Hqk * DK * 2;
         const unsigned astride = (unsigned)p.Hv * CH * 4, gstride = (unsigned)p.Hv * 4;
-        Rows<DK * 2 / 16> rk, rq, rdo;
+        Rows<DK * 2 / 16> rdo;
         Rows<CH * 4 / 16> rtm;
         Rows<DV * 4 / 16> rn, rd;
-        load_rows(rk, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
-        load_rows(rq, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
         load_rows(rdo, p.dO + (e.row0 * p.Hv + j) * DV, vstride, c, e.seq_len, tid);
         load_rows(rtm, p.A + (e.row0 * p.Hv + j) * CH, astride, c, e.seq_len, tid);
         load_tile_f32(rn, vnc, tid);
@@ -496,8 +505,6 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             b = ld4(rb, (unsigned)tid * gstride);
         }
         load_rows(rv, p.v + (e.row0 * p.Hv + j) * DV, vstride, c, e.seq_len, tid);
-        store_rows_ld(s.k, rk, LK, tid);
-        store_rows_ld(s.q, rq, LK, tid);
         store_rows_ld(s.ov, rdo, LK, tid);
         store_rows_split(s.tH, s.tL, rtm, L64, tid);
         store_rows_split(s.nH, s.nL, rn, LK, tid);
