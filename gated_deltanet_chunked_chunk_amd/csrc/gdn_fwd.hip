@@ -274,24 +274,39 @@ __device__ __forceinline__ bf16x8 frag_rp(const bf16 *X, const int r0, const int
 // Rows beyond a chunk's buffer resource (past the sequence end) arrive as zeros.
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Part `part` of PARTS of chunk c's tile: wave loads part, part + PARTS, ...
+// Part `part` of PARTS of a tile: the wave issues loads part, part + PARTS, ...
 // of the tile's 17.  Lane l of load i fills 16-byte slot 64 i + l of the
 // padded tile, i.e. row (64 i + l) / 17 and piece (64 i + l) % 17; the pad
-// piece takes an offset past any buffer and arrives as zeros.
-template <int PARTS = 4>
+// piece takes an offset past any buffer and arrives as zeros.  The per-lane
+// byte offsets depend only on the row stride, so each wave computes its share
+// once and reuses it for every chunk.
+template <int PARTS>
+struct TileOffs {
+    static constexpr int NI = (TLOADS + PARTS - 1) / PARTS;
+    unsigned o[NI];
+};
+
+template <int PARTS>
+__device__ __forceinline__ TileOffs<PARTS> tile_offsets(const unsigned stride, const int part, const int lane) {
+    TileOffs<PARTS> t;
+#pragma unroll
+    for (int n = 0; n < TileOffs<PARTS>::NI; ++n) {
+        const int slot = 64 * (part + n * PARTS) + lane;
+        const int row = slot / TSLOT, piece = slot - TSLOT * row;
+        t.o[n] = (piece < 16 && row < CH) ? (unsigned)row * stride + 16u * (unsigned)piece : 0x80000000u;
+    }
+    return t;
+}
+
+// Chunk c's tile through a buffer resource over the chunk's rows.
+template <int PARTS>
 __device__ __forceinline__ void dma_tile(bf16 *tile, const char *base, const unsigned stride, const int c,
-                                         const int seq_len, const int part, const int lane) {
-    constexpr int NI = (TLOADS + PARTS - 1) / PARTS;
+                                         const int seq_len, const int part, const TileOffs<PARTS> &t) {
     const __amdgpu_buffer_rsrc_t r = chunk_rsrc(base, stride, c, seq_len);
 #pragma unroll
-    for (int n = 0; n < NI; ++n) {
+    for (int n = 0; n < TileOffs<PARTS>::NI; ++n) {
         const int i = part + n * PARTS;
-        if (i < TLOADS) {
-            const int slot = 64 * i + lane;
-            const int row = slot / TSLOT, piece = slot - TSLOT * row;
-            const unsigned off = piece < 16 ? (unsigned)row * stride + 16u * (unsigned)piece : 0x80000000u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + 512 * i), 16, (int)off, 0, 0, 0);
-        }
+        if (i < TLOADS) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + 512 * i), 16, (int)t.o[n], 0, 0, 0);
     }
 }
 
@@ -1180,6 +1195,7 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
         const char *obase = static_cast<const char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes;
         f32x4 vp[4][2], qh[4][2];  // vp: U, then v' of this chunk
         const int cbase = (!PRE && (p.h_out || p.vn_out)) ? seq_chunk_base(p, e.n, lane) : 0;
+        const TileOffs<NSTATE> koffs = tile_offsets<NSTATE>(in.kstride, wave, lane);  // this wave's share of K
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
             const bool chain = c >= c_first;  // state pass of chunk c
             const bool prep = c + 1 < c_end;  // preparation of chunk c + 1
@@ -1219,7 +1235,7 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 else hupd9(s, hacc, vp, b, lane_now());
             }
             lds_barrier();
-            if (c + 2 < c_end) dma_tile<NSTATE>(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, lane_now());
+            if (c + 2 < c_end) dma_tile<NSTATE>(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, koffs);
             if (!PRE && prep && c + 1 >= e.c_begin) {
                 if (OF32) qh9<true>(s, hacc, qh, 0, nb, p.scale, lane_now());
                 else qh9_both(s, hacc, qh, nb, p.scale, lane_now());
@@ -1238,11 +1254,13 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
     } else {
         __builtin_amdgcn_s_setprio(2);
         const int pw = wave - NSTATE;
+        const TileOffs<4> kqoffs = tile_offsets<4>(in.kstride, pw, lane);  // this wave's share of K and Q
+        const TileOffs<4> voffs = tile_offsets<4>(in.vstride, pw, lane);   // and of V
         const char *abase = (!PRE && p.a_out) ? reinterpret_cast<const char *>(p.a_out + ((int64_t)e.row0 * p.Hv + j) * CH)
                                     : nullptr;
         if (has_chunks) {
-            dma_tile(s.k[c_first & 1], in.k, in.kstride, c_first, e.seq_len, pw, lane);
-            if (!PRE && c_first >= e.c_begin) dma_tile(s.q[c_first & 1], in.q, in.kstride, c_first, e.seq_len, pw, lane);
+            dma_tile<4>(s.k[c_first & 1], in.k, in.kstride, c_first, e.seq_len, pw, kqoffs);
+            if (!PRE && c_first >= e.c_begin) dma_tile<4>(s.q[c_first & 1], in.q, in.kstride, c_first, e.seq_len, pw, kqoffs);
             dma_gb(s, in, c_first, pw, lane);
         }
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
@@ -1257,12 +1275,12 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             dma_wait();
             lds_barrier();
             if (ahead) {
-                if (!PRE && c + 2 >= e.c_begin) dma_tile(s.q[c & 1], in.q, in.kstride, c + 2, e.seq_len, pw, ln);
+                if (!PRE && c + 2 >= e.c_begin) dma_tile<4>(s.q[c & 1], in.q, in.kstride, c + 2, e.seq_len, pw, kqoffs);
                 dma_gb(s, in, c + 2, pw, ln);
             }
             if (prep) prod9(s, ln, pw, nb);
             lds_barrier();
-            if (prep) dma_tile(s.v, in.v, in.vstride, c + 1, e.seq_len, pw, ln);
+            if (prep) dma_tile<4>(s.v, in.v, in.vstride, c + 1, e.seq_len, pw, voffs);
             if (prep) inv8_l0(s, ln, pw);
             lds_barrier();
             const bool pout = !PRE && prep && c + 1 >= e.c_begin;  // chunk c + 1 produces output: P needed
