@@ -356,6 +356,12 @@ __device__ __forceinline__ void st_split(bf16 *hi, bf16 *lo, int ld, int r0, int
         lo[(r + j) * ld + c] = l[j];
     }
 }
+// bf16 of an accumulator tile into a row-major [row][col] array
+__device__ __forceinline__ void st_bf16(bf16 *dst, int ld, int r0, int c0, f32x4 v, int lane) {
+    const int c = c0 + (lane & 15), r = r0 + 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[(r + j) * ld + c] = (bf16)v[j];
+}
 __device__ __forceinline__ void st_split_t(bf16 *hi, bf16 *lo, int ld, int r0, int c0, f32x4 v, int lane) {
     bf16x4 h, l;
     split4(v, h, l);
@@ -828,7 +834,8 @@ struct __attribute__((aligned(16))) SmemDh {
     bf16 k[CH * LK], q[CH * LK];      // K, Q   [token][key dim]
     bf16 dO[CH * L64];                // dO, this workgroup's 64 value columns
     bf16 aH[CH * L64], aL[CH * L64];  // T diag(beta gamma), then dv'   [token][col]
-    bf16 wH[CH * LK], wL[CH * LK];    // W   [token][key dim]
+    bf16 wH[CH * LK];                 // W   [token][key dim], bf16 (the forward's precision for W)
+    bf16 oH[CH * L64], oL[CH * L64];  // diag(gamma) dO, hi / lo   [token][col]
     bf16 pH[CH * L64], pL[CH * L64];  // P   [query token][key token]
     bf16 hH[DK * L64], hL[DK * L64];  // dh  [key dim][value column]
     float G[CH], gam[CH], bg[CH];
@@ -867,15 +874,29 @@ __device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int 
     const float G = prefix64(R.g);
     const float gam = __expf(G);
     const float bg = R.b * gam;
-    if (tid < 64) {
-        s.G[lane] = G;
-        s.gam[lane] = gam;
-    }
-    // every wave writes the same column scales and reads back only its own writes
+    if (tid < 64) s.G[lane] = G;
+    // every wave writes the same scales and reads back only its own writes
     s.bg[lane] = bg;
+    s.gam[lane] = gam;
     store_rows_ld(s.k, R.k, LK, tid);
     store_rows_ld(s.q, R.q, LK, tid);
     store_rows_ld(s.dO, R.dO, L64, tid);
+    // diag(gamma) dO as a hi / lo pair, formed once here for every wave's Q^T diag(gamma) dO
+    constexpr int OPR = HVC * 2 / 16;
+#pragma unroll
+    for (int i = 0; i < Rows<OPR>::PER; ++i) {
+        const int pc = tid + i * NT;
+        const int row = pc / OPR, col = 8 * (pc - row * OPR);
+        const bf16x8 d = __builtin_bit_cast(bf16x8, R.dO.x[i]);
+        const float gr = s.gam[row];
+        float f[8];
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) f[e2] = (float)d[e2] * gr;
+        bf16x8 h, l;
+        split8(f, h, l);
+        *reinterpret_cast<bf16x8 *>(&s.oH[row * L64 + col]) = h;
+        *reinterpret_cast<bf16x8 *>(&s.oL[row * L64 + col]) = l;
+    }
     constexpr int PPR = CH * 4 / 16;
 #pragma unroll
     for (int i = 0; i < Rows<PPR>::PER; ++i) {
@@ -986,7 +1007,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
                 for (int kk = 0; kk < 2; ++kk)
                     acc = mm_pe(acc, fr_row<true>(s.aH + 16 * rt * L64, L64, 32 * kk, lane),
                                 fr_row<true>(s.aL + 16 * rt * L64, L64, 32 * kk, lane), bk[kk]);
-                st_split(s.wH, s.wL, LK, 16 * rt, 16 * wave, acc, lane);
+                st_bf16(s.wH, LK, 16 * rt, 16 * wave, acc, lane);
             }
         }
         // P = (Q K^T) o Gamma, s <= i: row tile w / 2, column tiles 2 (w % 2) + {0, 1}
@@ -1054,33 +1075,24 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const bf16x8 d = fr_tr(s.dO + 16 * ct, L64, 32 * kk, lane);
-                    float f[8];
-#pragma unroll
-                    for (int e2 = 0; e2 < 8; ++e2) f[e2] = (float)d[e2] * s.gam[32 * kk + kpos(e2, g4, true)];
-                    bf16x8 bh, bl;
-                    split8(f, bh, bl);
-                    u[ct] = mm_ep(u[ct], aq[kk], bh, bl);
-                }
+                for (int kk = 0; kk < 2; ++kk)
+                    u[ct] = mm_ep(u[ct], aq[kk], fr_tr(s.oH + 16 * ct, L64, 32 * kk, lane),
+                                  fr_tr(s.oL + 16 * ct, L64, 32 * kk, lane));
             }
         }
         __syncthreads();
 
         // dh <- gamma_last dh + scale Q^T diag(gamma) dO - W^T dv'
         {
-            bf16x8 awh[2], awl[2];
+            bf16x8 awh[2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                awh[kk] = fr_tr(s.wH + 16 * wave, LK, 32 * kk, lane);
-                awl[kk] = fr_tr(s.wL + 16 * wave, LK, 32 * kk, lane);
-            }
+            for (int kk = 0; kk < 2; ++kk) awh[kk] = fr_tr(s.wH + 16 * wave, LK, 32 * kk, lane);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 f32x4 acc = f32x4{};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    acc = mm_pp(acc, awh[kk], awl[kk], fr_tr(s.aH + 16 * ct, L64, 32 * kk, lane),
+                    acc = mm_ep(acc, awh[kk], fr_tr(s.aH + 16 * ct, L64, 32 * kk, lane),
                                 fr_tr(s.aL + 16 * ct, L64, 32 * kk, lane));
                 dh[ct] = gl * dh[ct] + p.scale * u[ct] - acc;
                 st_split(s.hH, s.hL, L64, 16 * wave, 16 * ct, dh[ct], lane);
