@@ -38,6 +38,8 @@
 // column l % 32).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -1253,56 +1255,67 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
         }
     } else {
         __builtin_amdgcn_s_setprio(2);
-        const int pw = wave - NSTATE;
-        const TileOffs<4> kqoffs = tile_offsets<4>(in.kstride, pw, lane);  // this wave's share of K and Q
-        const TileOffs<4> voffs = tile_offsets<4>(in.vstride, pw, lane);   // and of V
-        const char *abase = (!PRE && p.a_out) ? reinterpret_cast<const char *>(p.a_out + ((int64_t)e.row0 * p.Hv + j) * CH)
-                                    : nullptr;
-        if (has_chunks) {
-            dma_tile<4>(s.k[c_first & 1], in.k, in.kstride, c_first, e.seq_len, pw, kqoffs);
-            if (!PRE && c_first >= e.c_begin) dma_tile<4>(s.q[c_first & 1], in.q, in.kstride, c_first, e.seq_len, pw, kqoffs);
-            dma_gb(s, in, c_first, pw, lane);
-        }
-        for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
-            // opaque thread index, once per chunk: lane-derived LDS addresses
-            // are recomputed inside the loop rather than hoisted
-            int tid = threadIdx.x;
-            asm volatile("" : "+v"(tid));
-            const int ln = tid & 63;
-            const bool prep = c + 1 < c_end;   // preparation of chunk c + 1
-            const bool ahead = c + 2 < c_end;  // loads of chunk c + 2
-            const int nb = (c + 1) & 1;
-            dma_wait();
-            lds_barrier();
-            if (ahead) {
-                if (!PRE && c + 2 >= e.c_begin) dma_tile<4>(s.q[c & 1], in.q, in.kstride, c + 2, e.seq_len, pw, kqoffs);
-                dma_gb(s, in, c + 2, pw, ln);
+        // Each preparation wave's share (tile rows, k steps, fragments) is
+        // fixed by its index pw; the loop is compiled once per pw, so that the
+        // share's LDS offsets and branches are constants.
+        auto prep_role = [&](auto pw_c) {
+            constexpr int pw = decltype(pw_c)::value;
+            const TileOffs<4> kqoffs = tile_offsets<4>(in.kstride, pw, lane);  // this wave's share of K and Q
+            const TileOffs<4> voffs = tile_offsets<4>(in.vstride, pw, lane);   // and of V
+            const char *abase = (!PRE && p.a_out) ? reinterpret_cast<const char *>(p.a_out + ((int64_t)e.row0 * p.Hv + j) * CH)
+                                        : nullptr;
+            if (has_chunks) {
+                dma_tile<4>(s.k[c_first & 1], in.k, in.kstride, c_first, e.seq_len, pw, kqoffs);
+                if (!PRE && c_first >= e.c_begin) dma_tile<4>(s.q[c_first & 1], in.q, in.kstride, c_first, e.seq_len, pw, kqoffs);
+                dma_gb(s, in, c_first, pw, lane);
             }
-            if (prep) prod9(s, ln, pw, nb);
-            lds_barrier();
-            if (prep) dma_tile<4>(s.v, in.v, in.vstride, c + 1, e.seq_len, pw, voffs);
-            if (prep) inv8_l0(s, ln, pw);
-            lds_barrier();
-            const bool pout = !PRE && prep && c + 1 >= e.c_begin;  // chunk c + 1 produces output: P needed
-            if (prep && pw < 2) {
-                inv8_l1(s, ln, pw);
-                if (pout) pfrag9(s, ln, pw + 1, nb, p.scale, decays_factor(s, ln));  // fragments 1, 2
+            for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
+                // opaque thread index, once per chunk: lane-derived LDS addresses
+                // are recomputed inside the loop rather than hoisted
+                int tid = threadIdx.x;
+                asm volatile("" : "+v"(tid));
+                const int ln = tid & 63;
+                const bool prep = c + 1 < c_end;   // preparation of chunk c + 1
+                const bool ahead = c + 2 < c_end;  // loads of chunk c + 2
+                const int nb = (c + 1) & 1;
+                dma_wait();
+                lds_barrier();
+                if (ahead) {
+                    if (!PRE && c + 2 >= e.c_begin) dma_tile<4>(s.q[c & 1], in.q, in.kstride, c + 2, e.seq_len, pw, kqoffs);
+                    dma_gb(s, in, c + 2, pw, ln);
+                }
+                if (prep) prod9(s, ln, pw, nb);
+                lds_barrier();
+                if (prep) dma_tile<4>(s.v, in.v, in.vstride, c + 1, e.seq_len, pw, voffs);
+                if (prep) inv8_l0(s, ln, pw);
+                lds_barrier();
+                const bool pout = !PRE && prep && c + 1 >= e.c_begin;  // chunk c + 1 produces output: P needed
+                if (prep && pw < 2) {
+                    inv8_l1(s, ln, pw);
+                    if (pout) pfrag9(s, ln, pw + 1, nb, p.scale, decays_factor(s, ln));  // fragments 1, 2
+                }
+                if (pout && pw >= 2) {
+                    const bool fact = decays_factor(s, ln);
+                    pfrag9(s, ln, pw == 2 ? 5 : 3, nb, p.scale, fact);
+                    pfrag9(s, ln, pw == 2 ? 0 : 4, nb, p.scale, fact);
+                }
+                lds_barrier();
+                if (prep) {
+                    L2Regs l2;
+                    inv8_l2a(s, ln, pw, l2);
+                    inv8_l2b(s, ln, pw, l2);
+                }
+                if (prep) wfrag9(s, ln, 0, pw, pw < 2 ? pw : -1, nb);  // rows 0..31, final since level 1
+                lds_barrier();
+                if (!PRE && prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, abase, e.seq_len, c + 1, pw, ln);
+                if (prep) wfrag9(s, ln, 2, pw, 2 + pw, nb);  // rows 32..63
             }
-            if (pout && pw >= 2) {
-                const bool fact = decays_factor(s, ln);
-                pfrag9(s, ln, pw == 2 ? 5 : 3, nb, p.scale, fact);
-                pfrag9(s, ln, pw == 2 ? 0 : 4, nb, p.scale, fact);
-            }
-            lds_barrier();
-            if (prep) {
-                L2Regs l2;
-                inv8_l2a(s, ln, pw, l2);
-                inv8_l2b(s, ln, pw, l2);
-            }
-            if (prep) wfrag9(s, ln, 0, pw, pw < 2 ? pw : -1, nb);  // rows 0..31, final since level 1
-            lds_barrier();
-            if (!PRE && prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, abase, e.seq_len, c + 1, pw, ln);
-            if (prep) wfrag9(s, ln, 2, pw, 2 + pw, nb);  // rows 32..63
+        };
+        switch (wave - NSTATE) {
+        case 0: prep_role(std::integral_constant<int, 0>{}); break;
+        case 1: prep_role(std::integral_constant<int, 1>{}); break;
+        case 2: prep_role(std::integral_constant<int, 2>{}); break;
+        default: prep_role(std::integral_constant<int, 3>{}); break;
         }
     }
 }
