@@ -1270,11 +1270,10 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 dma_gb(s, in, c_first, pw, lane);
             }
             for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
-                // opaque thread index, once per chunk: lane-derived LDS addresses
-                // are recomputed inside the loop rather than hoisted
-                int tid = threadIdx.x;
-                asm volatile("" : "+v"(tid));
-                const int ln = tid & 63;
+                // with the wave's share fixed at compile time, its lane-derived
+                // LDS addresses are few enough to stay in registers across the
+                // loop (the state loop re-derives its own every step instead)
+                const int ln = lane;
                 const bool prep = c + 1 < c_end;   // preparation of chunk c + 1
                 const bool ahead = c + 2 < c_end;  // loads of chunk c + 2
                 const int nb = (c + 1) & 1;
