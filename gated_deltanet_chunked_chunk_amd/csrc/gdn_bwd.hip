@@ -833,7 +833,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
 struct __attribute__((aligned(16))) SmemDh {
     bf16 k[CH * LK], q[CH * LK];      // K, Q   [token][key dim]
     bf16 dO[CH * L64];                // dO, this workgroup's 64 value columns
-    bf16 aH[CH * L64], aL[CH * L64];  // T diag(beta gamma), then dv'   [token][col]
+    bf16 aH[CH * L64], aL[CH * L64];  // dv'   [token][col]
+    bf16 tH[CH * L64];                // T diag(beta gamma), bf16 (it only feeds the bf16 W)
     bf16 wH[CH * LK];                 // W   [token][key dim], bf16 (the forward's precision for W)
     bf16 oH[CH * L64], oL[CH * L64];  // diag(gamma) dO, hi / lo   [token][col]
     bf16 pH[CH * L64], pL[CH * L64];  // P   [query token][key token]
@@ -905,10 +906,7 @@ __device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int 
         f32x4 x = __builtin_bit_cast(f32x4, R.t.x[i]);
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) x[e2] *= s.bg[col + e2];
-        bf16x4 h, l;
-        split4(x, h, l);
-        *reinterpret_cast<bf16x4 *>(&s.aH[row * L64 + col]) = h;
-        *reinterpret_cast<bf16x4 *>(&s.aL[row * L64 + col]) = l;
+        *reinterpret_cast<bf16x4 *>(&s.tH[row * L64 + col]) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
     }
 }
 
@@ -985,14 +983,18 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
     for (int ct = 0; ct < 4; ++ct) st_split(s.hH, s.hL, L64, 16 * wave, 16 * ct, dh[ct], lane);
     const int cbase = seq_chunk_base(p.cu, p.T, e.n, lane);
 
+    // The tiles of the next chunk (walking backwards) go into LDS during the dh
+    // update of the current one, which reads none of them; its inputs are
+    // loaded into registers one chunk ahead of that.
     ChunkDh R;
-    if (c_last - 1 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c_last - 1, tid);
+    if (c_last - 1 >= e.c_begin) {
+        load_chunk_dh(R, p, e, j, half, c_last - 1, tid);
+        store_chunk_dh(s, R, tid);
+    }
+    if (c_last - 2 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c_last - 2, tid);
     for (int c = c_last - 1; c >= e.c_begin; --c) {
         const bool own = !pre && c < c_end;
-        __syncthreads();  // previous chunk's products done; tiles free
-        store_chunk_dh(s, R, tid);
-        if (c - 1 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c - 1, tid);  // next chunk's inputs in flight
-        __syncthreads();
+        __syncthreads();  // chunk c's tiles in LDS; the previous dh update done
         const float gl = s.gam[CH - 1];
 
         // W = T diag(beta gamma) K: key columns 16 w .., all token rows
@@ -1005,8 +1007,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
                 f32x4 acc = f32x4{};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    acc = mm_pe(acc, fr_row<true>(s.aH + 16 * rt * L64, L64, 32 * kk, lane),
-                                fr_row<true>(s.aL + 16 * rt * L64, L64, 32 * kk, lane), bk[kk]);
+                    acc = mfma(fr_row<true>(s.tH + 16 * rt * L64, L64, 32 * kk, lane), bk[kk], acc);
                 st_bf16(s.wH, LK, 16 * rt, 16 * wave, acc, lane);
             }
         }
@@ -1097,6 +1098,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
                 dh[ct] = gl * dh[ct] + p.scale * u[ct] - acc;
                 st_split(s.hH, s.hL, L64, 16 * wave, 16 * ct, dh[ct], lane);
             }
+        }
+        if (c - 1 >= e.c_begin) {
+            store_chunk_dh(s, R, tid);
+            if (c - 2 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c - 2, tid);
         }
     }
     if (pre) {
