@@ -613,8 +613,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             const int col = 16 * ct + r16;  // key token s
             const float rl = __expf(s.G[CH - 1] - s.G[col]);
             float ksum = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) ksum += (float)s.k[col * LK + 16 * wave + 4 * g4 + jj] * t2[jj];
+            {
+                const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(&s.k[col * LK + 16 * wave + 4 * g4]);
+                for (int jj = 0; jj < 4; ++jj) ksum += (float)k4[jj] * t2[jj];
+            }
             ksum = sum4g(ksum);
             if (g4 == 0) {
                 dGw[col] -= rl * ksum;
@@ -640,8 +642,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         const int col = 16 * ct + r16;  // query token i
         const float sg = p.scale * s.gam[col];
         float qsum = 0.f;
+        {
+            const bf16x4 q4 = *reinterpret_cast<const bf16x4 *>(&s.q[col * LK + 16 * wave + 4 * g4]);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) qsum += (float)s.q[col * LK + 16 * wave + 4 * g4 + jj] * t1[jj];
+            for (int jj = 0; jj < 4; ++jj) qsum += (float)q4[jj] * t1[jj];
+        }
         qsum = sum4g(qsum);
         if (g4 == 0) dGw[col] += sg * qsum;
         if (col < rows_valid)
@@ -690,8 +695,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
                         fr_tr(s.tH + 16 * ct, L64, 32 * kk, lane), fr_tr(s.tL + 16 * ct, L64, 32 * kk, lane));
         const int sc = 16 * ct + r16;
         float rk = 0.f;
+        {
+            const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(&s.k[sc * LK + 16 * wave + 4 * g4]);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) rk += acc[jj] * (float)s.k[sc * LK + 16 * wave + 4 * g4 + jj];
+            for (int jj = 0; jj < 4; ++jj) rk += acc[jj] * (float)k4[jj];
+        }
         rk = sum4g(rk);
         const float bgs = s.bt[sc] * s.gam[sc];
         if (g4 == 0) {
@@ -701,7 +709,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         dkt[ct] += bgs * acc;
     }
     {
-        // T^T dv' over value columns 16 w .., all token rows s
+        // (T^T dv')^T = dv'^T T over value columns 16 w .., all token columns
+        // s: lane (m, g) holds value columns 16 w + 4 g .. +3 of token
+        // 16 rt + m, so dv goes out as four contiguous values per lane and the
+        // dbeta term is a four-term dot product with V plus a sum over g.
         bf16x8 bh[2], bl[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -713,20 +724,24 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             f32x4 acc = f32x4{};
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                acc = mm_pp(acc, fr_tr(s.tH + 16 * rt, L64, 32 * kk, lane), fr_tr(s.tL + 16 * rt, L64, 32 * kk, lane),
-                            bh[kk], bl[kk]);
-            const int col = 16 * wave + r16;
+                acc = mm_pp(acc, bh[kk], bl[kk], fr_tr(s.tH + 16 * rt, L64, 32 * kk, lane),
+                            fr_tr(s.tL + 16 * rt, L64, 32 * kk, lane));
+            const int sr = 16 * rt + r16;      // token s
+            const int v0 = 16 * wave + 4 * g4;  // value columns v0 .. v0 + 3
+            const bf16x4 vv4 = *reinterpret_cast<const bf16x4 *>(&s.ov[sr * LK + v0]);
+            float rvv = 0.f;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int sr = 16 * rt + 4 * g4 + jj;
-                const float rvv = sum16(acc[jj] * (float)s.ov[sr * LK + col]);
-                if (r16 == 0) dbw[sr] += rvv;
-                const float dvv = s.bt[sr] * acc[jj];
-                if (sr < rows_valid) {
-                    const unsigned off = (unsigned)sr * tstride + col;
-                    if (p.grad_f32) static_cast<float *>(p.dv)[row_c * DV + off] = dvv;
-                    else static_cast<bf16 *>(p.dv)[row_c * DV + off] = (bf16)dvv;
-                }
+            for (int jj = 0; jj < 4; ++jj) rvv += acc[jj] * (float)vv4[jj];
+            rvv = sum4g(rvv);
+            if (g4 == 0) dbw[sr] += rvv;
+            const f32x4 dvv = s.bt[sr] * acc;
+            if (sr < rows_valid) {
+                const int64_t off = row_c * DV + (int64_t)sr * tstride + v0;
+                if (p.grad_f32)
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dv) + off) = dvv;
+                else
+                    *reinterpret_cast<bf16x4 *>(static_cast<bf16 *>(p.dv) + off) =
+                        bf16x4{(bf16)dvv[0], (bf16)dvv[1], (bf16)dvv[2], (bf16)dvv[3]};
             }
         }
     }
