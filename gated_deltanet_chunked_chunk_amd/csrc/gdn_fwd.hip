@@ -184,11 +184,12 @@ __device__ __forceinline__ SegEntry find_segment(const FwdParams &p, int seg, in
 // deliver; every operand of such a k step uses that order.  Every A operand a
 // state wave reads from LDS serves both of its column tiles, so each shared
 // tile is read by four waves per chunk.  Waves 4..7, the preparation waves,
-// hold no state: they load every chunk straight from HBM into LDS and run the
-// chunk-local preparation of the next chunk (gate scan, K K^T, inverse, W,
-// T diag(beta), P) in step with the state pass of the current one, one
-// barrier-separated step at a time, at a raised wave priority (their chain of
-// small dependent steps is the longer of the two).
+// hold no state: they load Q, V, g and beta of every chunk straight from HBM
+// into LDS (the state waves load K) and run the chunk-local preparation of the
+// next chunk (gate scan, K K^T, inverse, W, T diag(beta), P) in step with the
+// state pass of the current one, one barrier-separated step at a time, at a
+// raised wave priority: their chain of small dependent steps has the longer
+// latency, and the state wave that shares their SIMD fills its stalls.
 constexpr int NT8 = 512;
 constexpr int TS8 = 32 + 4;    // fp32 row stride of the transposed 32 x 32 diagonal blocks
 constexpr int TLD = DK + 8;    // bf16 row stride of the K, Q and V tiles: 272 bytes
