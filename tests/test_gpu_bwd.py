@@ -76,6 +76,16 @@ def test_bwd_ragged_batch(cp):
     _check(f"ragged/{cp}", got, _oracle(x))
 
 
+@pytest.mark.parametrize("grad_dtype", ["f32", "bf16"])
+def test_bwd_ungrouped_heads(grad_dtype):
+    # H_qk == H_v: each key head has one v-head, so the local kernel writes dq and dk
+    # straight to the output without a partial sum in the workspace
+    w = dataclasses.replace(BASE, name="b7", seed=47, B=1, T=300, H_qk=2, H_v=2)
+    x = _grad_inputs(w)
+    got = _run(x, cp="warmup", cp_segment_chunks=2, grad_dtype=grad_dtype)
+    _check(f"ungrouped/{grad_dtype}", got, _oracle(x))
+
+
 def test_bwd_grouped_heads_several_chunks():
     w = dataclasses.replace(BASE, name="b2", seed=42, B=1, T=1000, H_qk=2, H_v=8)
     x = _grad_inputs(w)
