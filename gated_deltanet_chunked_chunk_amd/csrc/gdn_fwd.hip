@@ -931,7 +931,7 @@ __device__ __forceinline__ void out9(const Smem8 &s, const FwdParams &p, const c
 }
 
 // H <- gamma_last H + K^T diag(gamma_last / gamma) v'
-__device__ __forceinline__ void hupd9(const Smem8 &s, f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int buf,
+__device__ __forceinline__ void hupd9(const Smem8 &s, f32x4 (&hacc)[2][8], const f32x4 (&vp)[4][2], const int buf,
                                       const int ln) {
     const int g = ln >> 4;
     const bf16 *K = s.k[buf];
@@ -946,20 +946,15 @@ __device__ __forceinline__ void hupd9(const Smem8 &s, f32x4 (&hacc)[2][8], f32x4
     const float glast = s.gam[buf][CH - 1];
     __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) vp[rt][ct][jj] *= d4[rt][jj];
-#pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) hacc[ct][dt] *= glast;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 vh[2], vl[2];
+        bf16x8 vh[2], vl[2];  // the decayed v' (v' itself stays for the optional v' store)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) split_pair(vp[2 * ks][ct], vp[2 * ks + 1][ct], vh[ct], vl[ct]);
+        for (int ct = 0; ct < 2; ++ct)
+            split_pair(vp[2 * ks][ct] * d4[2 * ks], vp[2 * ks + 1][ct] * d4[2 * ks + 1], vh[ct], vl[ct]);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -1228,8 +1223,6 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 if (PRE) wh8_lean(s, hacc, vp, lane_now());
                 else wh8(s, hacc, vp, lane_now());
             }
-            if (!PRE && chain && out && p.vn_out)
-                store_vn8(vp, p.vn_out + ((int64_t)(cbase + c) * p.Hv + j) * CH * DV, wave, lane_now());
             lds_barrier();
             if (!PRE && chain && out) out9<OF32>(s, p, obase, e.seq_len, vp, qh, c, wave, lane_now());
             lds_barrier();
@@ -1248,6 +1241,10 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 if (OF32) qh9<true>(s, hacc, qh, 1, nb, p.scale, lane_now());
                 if (p.h_out) store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
             }
+            // v' of chunk c, out of the first step's way (the state waves have no
+            // other work here for a bf16 o)
+            if (!PRE && chain && out && p.vn_out)
+                store_vn8(vp, p.vn_out + ((int64_t)(cbase + c) * p.Hv + j) * CH * DV, wave, lane_now());
         }
         if (PRE) {
             store_state8(hacc, (mwave ? p.ws_m : p.ws_s) + ((int64_t)seg * p.Hv + j) * DK * DV, sw, lane);
