@@ -850,7 +850,6 @@ struct __attribute__((aligned(16))) SmemDh {
     bf16 dO[CH * L64];                // dO, this workgroup's 64 value columns
     bf16 aH[CH * L64], aL[CH * L64];  // dv'   [token][col]
     bf16 tH[CH * L64];                // T diag(beta gamma), bf16 (it only feeds the bf16 W)
-    bf16 wH[CH * LK];                 // W   [token][key dim], bf16 (the forward's precision for W)
     bf16 oH[CH * L64], oL[CH * L64];  // diag(gamma) dO, hi / lo   [token][col]
     bf16 pH[CH * L64], pL[CH * L64];  // P   [query token][key token]
     bf16 hH[DK * L64], hL[DK * L64];  // dh  [key dim][value column]
@@ -1012,19 +1011,28 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
         __syncthreads();  // chunk c's tiles in LDS; the previous dh update done
         const float gl = s.gam[CH - 1];
 
-        // W = T diag(beta gamma) K: key columns 16 w .., all token rows
+        // W = T diag(beta gamma) K: key columns 16 w .., all token rows.  Only
+        // this wave reads these columns back (as the A operand of W^T dv'), and
+        // two stacked accumulator tiles are already that operand at the
+        // transposed-read k order, so W stays in registers as bf16.
+        bf16x8 wa[2];
         {
             bf16x8 bk[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) bk[kk] = fr_tr(s.k + 16 * wave, LK, 32 * kk, lane);
+            f32x4 wt[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                f32x4 acc = f32x4{};
+                wt[rt] = f32x4{};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    acc = mfma(fr_row<true>(s.tH + 16 * rt * L64, L64, 32 * kk, lane), bk[kk], acc);
-                st_bf16(s.wH, LK, 16 * rt, 16 * wave, acc, lane);
+                    wt[rt] = mfma(fr_row<true>(s.tH + 16 * rt * L64, L64, 32 * kk, lane), bk[kk], wt[rt]);
             }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                wa[kk] = bf16x8{(bf16)wt[2 * kk][0], (bf16)wt[2 * kk][1], (bf16)wt[2 * kk][2], (bf16)wt[2 * kk][3],
+                                (bf16)wt[2 * kk + 1][0], (bf16)wt[2 * kk + 1][1], (bf16)wt[2 * kk + 1][2],
+                                (bf16)wt[2 * kk + 1][3]};
         }
         // P = (Q K^T) o Gamma, s <= i: row tile w / 2, column tiles 2 (w % 2) + {0, 1}
 #pragma unroll
@@ -1100,15 +1108,12 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
 
         // dh <- gamma_last dh + scale Q^T diag(gamma) dO - W^T dv'
         {
-            bf16x8 awh[2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) awh[kk] = fr_tr(s.wH + 16 * wave, LK, 32 * kk, lane);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
                 f32x4 acc = f32x4{};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    acc = mm_ep(acc, awh[kk], fr_tr(s.aH + 16 * ct, L64, 32 * kk, lane),
+                    acc = mm_ep(acc, wa[kk], fr_tr(s.aH + 16 * ct, L64, 32 * kk, lane),
                                 fr_tr(s.aL + 16 * ct, L64, 32 * kk, lane));
                 dh[ct] = gl * dh[ct] + p.scale * u[ct] - acc;
                 st_split(s.hH, s.hL, L64, 16 * wave, 16 * ct, dh[ct], lane);
