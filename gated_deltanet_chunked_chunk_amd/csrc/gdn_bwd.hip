@@ -849,7 +849,7 @@ struct __attribute__((aligned(16))) SmemDh {
     bf16 k[CH * LK], q[CH * LK];      // K, Q   [token][key dim]
     bf16 dO[CH * L64];                // dO, this workgroup's 64 value columns
     bf16 aH[CH * L64], aL[CH * L64];  // dv'   [token][col]
-    bf16 tH[CH * L64];                // T diag(beta gamma), bf16 (it only feeds the bf16 W)
+    bf16 tH[CH * L64], tL[CH * L64];  // T diag(beta gamma), hi / lo
     bf16 oH[CH * L64], oL[CH * L64];  // diag(gamma) dO, hi / lo   [token][col]
     bf16 pH[CH * L64], pL[CH * L64];  // P   [query token][key token]
     bf16 hH[DK * L64], hL[DK * L64];  // dh  [key dim][value column]
@@ -920,7 +920,10 @@ __device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int 
         f32x4 x = __builtin_bit_cast(f32x4, R.t.x[i]);
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) x[e2] *= s.bg[col + e2];
-        *reinterpret_cast<bf16x4 *>(&s.tH[row * L64 + col]) = bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+        bf16x4 h, l;
+        split4(x, h, l);
+        *reinterpret_cast<bf16x4 *>(&s.tH[row * L64 + col]) = h;
+        *reinterpret_cast<bf16x4 *>(&s.tL[row * L64 + col]) = l;
     }
 }
 
@@ -1014,8 +1017,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
         // W = T diag(beta gamma) K: key columns 16 w .., all token rows.  Only
         // this wave reads these columns back (as the A operand of W^T dv'), and
         // two stacked accumulator tiles are already that operand at the
-        // transposed-read k order, so W stays in registers as bf16.
-        bf16x8 wa[2];
+        // transposed-read k order, so W stays in registers (hi / lo).
+        bf16x8 wa[2], wl[2];
         {
             bf16x8 bk[2];
 #pragma unroll
@@ -1026,13 +1029,15 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
                 wt[rt] = f32x4{};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    wt[rt] = mfma(fr_row<true>(s.tH + 16 * rt * L64, L64, 32 * kk, lane), bk[kk], wt[rt]);
+                    wt[rt] = mm_pe(wt[rt], fr_row<true>(s.tH + 16 * rt * L64, L64, 32 * kk, lane),
+                                   fr_row<true>(s.tL + 16 * rt * L64, L64, 32 * kk, lane), bk[kk]);
             }
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                wa[kk] = bf16x8{(bf16)wt[2 * kk][0], (bf16)wt[2 * kk][1], (bf16)wt[2 * kk][2], (bf16)wt[2 * kk][3],
-                                (bf16)wt[2 * kk + 1][0], (bf16)wt[2 * kk + 1][1], (bf16)wt[2 * kk + 1][2],
-                                (bf16)wt[2 * kk + 1][3]};
+            for (int kk = 0; kk < 2; ++kk) {
+                const float x[8] = {wt[2 * kk][0],     wt[2 * kk][1],     wt[2 * kk][2],     wt[2 * kk][3],
+                                    wt[2 * kk + 1][0], wt[2 * kk + 1][1], wt[2 * kk + 1][2], wt[2 * kk + 1][3]};
+                split8(x, wa[kk], wl[kk]);
+            }
         }
         // P = (Q K^T) o Gamma, s <= i: row tile w / 2, column tiles 2 (w % 2) + {0, 1}
 #pragma unroll
@@ -1113,7 +1118,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
                 f32x4 acc = f32x4{};
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    acc = mm_ep(acc, wa[kk], fr_tr(s.aH + 16 * ct, L64, 32 * kk, lane),
+                    acc = mm_pp(acc, wa[kk], wl[kk], fr_tr(s.aH + 16 * ct, L64, 32 * kk, lane),
                                 fr_tr(s.aL + 16 * ct, L64, 32 * kk, lane));
                 dh[ct] = gl * dh[ct] + p.scale * u[ct] - acc;
                 st_split(s.hH, s.hL, L64, 16 * wave, 16 * ct, dh[ct], lane);
