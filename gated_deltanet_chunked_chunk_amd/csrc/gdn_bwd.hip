@@ -356,12 +356,6 @@ __device__ __forceinline__ void st_split(bf16 *hi, bf16 *lo, int ld, int r0, int
         lo[(r + j) * ld + c] = l[j];
     }
 }
-// bf16 of an accumulator tile into a row-major [row][col] array
-__device__ __forceinline__ void st_bf16(bf16 *dst, int ld, int r0, int c0, f32x4 v, int lane) {
-    const int c = c0 + (lane & 15), r = r0 + 4 * (lane >> 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dst[(r + j) * ld + c] = (bf16)v[j];
-}
 __device__ __forceinline__ void st_split_t(bf16 *hi, bf16 *lo, int ld, int r0, int c0, f32x4 v, int lane) {
     bf16x4 h, l;
     split4(v, h, l);

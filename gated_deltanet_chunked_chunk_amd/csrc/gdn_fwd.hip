@@ -760,10 +760,8 @@ __device__ __forceinline__ void u9_lean(const Smem8 &s, const int lane, const in
 // operand, one column tile ct per call: qh[rt][ct] lane (m, g) holds value
 // column 16 ct + 4 g + j (of this wave's 32) of query row 16 rt + m.  It later accumulates (scale P v')^T in
 // place, and each lane then owns four consecutive output columns of one row.
-// SPLIT: the state enters as hi + lo bf16 parts (fp32-class product, for fp32
-// outputs); otherwise as its bf16 rounding alone, one MFMA per step, for bf16
-// outputs, whose own rounding is the larger error.
-template <bool SPLIT>
+// The state enters as hi + lo bf16 parts (fp32-class product): the path for
+// fp32 outputs; bf16 outputs use qh9_both below.
 __device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int ct,
                                     const int buf, const float scale, const int ln) {
     const int m = ln & 15;
@@ -778,28 +776,21 @@ __device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f
     for (int rt = 0; rt < 4; ++rt) qh[rt][ct] = f32x4{};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        if (SPLIT) {
-            bf16x8 hh, hl;
-            split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh, hl);
+        bf16x8 hh, hl;
+        split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh, hl);
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                qh[rt][ct] = mfma16(hh, qa[kk][rt], qh[rt][ct]);
-                qh[rt][ct] = mfma16(hl, qa[kk][rt], qh[rt][ct]);
-            }
-        } else {
-            const f32x4 &t0 = hacc[ct][2 * kk], &t1 = hacc[ct][2 * kk + 1];
-            const bf16x8 hh = {(bf16)t0[0], (bf16)t0[1], (bf16)t0[2], (bf16)t0[3],
-                               (bf16)t1[0], (bf16)t1[1], (bf16)t1[2], (bf16)t1[3]};
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) qh[rt][ct] = mfma16(hh, qa[kk][rt], qh[rt][ct]);
+        for (int rt = 0; rt < 4; ++rt) {
+            qh[rt][ct] = mfma16(hh, qa[kk][rt], qh[rt][ct]);
+            qh[rt][ct] = mfma16(hl, qa[kk][rt], qh[rt][ct]);
         }
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) qh[rt][ct] *= scale * s.gam[buf][16 * rt + m];  // this lane's query row
 }
 
-// Both column tiles at once from the bf16-rounded state (bf16 outputs): the
-// Q fragments are read once for the two tiles.
+// Both column tiles at once from the bf16-rounded state alone, one MFMA per
+// step (bf16 outputs, whose own rounding is the larger error): the Q fragments
+// are read once for the two tiles.
 __device__ __forceinline__ void qh9_both(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2],
                                          const int buf, const float scale, const int ln) {
     const int m = ln & 15;
@@ -1233,12 +1224,12 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             lds_barrier();
             if (c + 2 < c_end) dma_tile<NSTATE>(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, koffs);
             if (!PRE && prep && c + 1 >= e.c_begin) {
-                if (OF32) qh9<true>(s, hacc, qh, 0, nb, p.scale, lane_now());
+                if (OF32) qh9(s, hacc, qh, 0, nb, p.scale, lane_now());
                 else qh9_both(s, hacc, qh, nb, p.scale, lane_now());
             }
             lds_barrier();
             if (!PRE && prep && c + 1 >= e.c_begin) {
-                if (OF32) qh9<true>(s, hacc, qh, 1, nb, p.scale, lane_now());
+                if (OF32) qh9(s, hacc, qh, 1, nb, p.scale, lane_now());
                 if (p.h_out) store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
             }
             // v' of chunk c, out of the first step's way (the state waves have no
