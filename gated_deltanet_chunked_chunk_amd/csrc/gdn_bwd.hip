@@ -266,6 +266,18 @@ __device__ __forceinline__ float prefix64(float x) {
     return x;
 }
 
+// Lane l takes lane 63 - l's value: the halves swap (v_permlane32_swap), then
+// the rows of each half (v_permlane16_swap), then the lanes of each row
+// (row_mirror).
+__device__ __forceinline__ float reverse64(float x) {
+    const int lane = threadIdx.x & 63;
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    x = __int_as_float(lane < 32 ? a[1] : a[0]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    x = __int_as_float(((lane >> 4) & 1) ? b[0] : b[1]);
+    return dpp_row<0x140>(x);  // row_mirror
+}
+
 // ---------------------------------------------------------------- chunk-local gradients
 // Fragment readers.  A fragment is the 8 k-values lane l holds for row /
 // column r = l % 16 in a 32-wide k step: k = 8 g .. 8 g + 7 (g = l / 16), or
@@ -822,12 +834,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             dG += s.dGp[w][lane];
             db += s.dbp[w][lane];
         }
-        float x = dG;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_down(x, off, 64);
-            if (lane + off < 64) x += y;
-        }
+        const float x = reverse64(prefix64(reverse64(dG)));  // sum over tokens >= lane
         if (lane < rows_valid) {
             const int64_t off = (e.row0 + (int64_t)c * CH + lane) * p.Hv + j;
             p.dg[off] = x;
