@@ -492,7 +492,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     const int j = iq * p.group + jj;
     const bool first = jj == 0, last = jj == p.group - 1;
     const float *hc = p.h + ((int64_t)cg * p.Hv + j) * DK * DV;       // chunk-start state [d][v]
-    const float *dhc = p.dh_ws + ((int64_t)cg * p.Hv + j) * DK * DV;  // gradient wrt the state after the chunk
+    // gradient wrt the state after the chunk, as bf16 hi and lo planes [2][d][v]
+    const bf16 *dhc = reinterpret_cast<const bf16 *>(p.dh_ws) + ((int64_t)cg * p.Hv + j) * 2 * DK * DV;
     const float *dvc = p.dvp_ws + ((int64_t)cg * p.Hv + j) * CH * DV; // dv' [i][v]
     const float *vnc = p.vn + ((int64_t)cg * p.Hv + j) * CH * DV;     // v'  [i][v]
     // this chunk's first row of the per-(token, v-head) outputs; a row of token t
@@ -536,15 +537,16 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
 
     // this wave's 16 rows of h and dh' (A operands of the transposed products),
     // in flight while the first products run
-    f32x4 hr[4][2], dr[4][2];
+    f32x4 hr[4][2];
+    bf16x8 dH[4], dL[4];  // dh' arrives already split
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 4; ++kk) {
+        const int off = (16 * wave + r16) * DV + 32 * kk + 8 * g4;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const int off = (16 * wave + r16) * DV + 32 * kk + 8 * g4 + 4 * hf;
-            hr[kk][hf] = *reinterpret_cast<const f32x4 *>(hc + off);
-            dr[kk][hf] = *reinterpret_cast<const f32x4 *>(dhc + off);
-        }
+        for (int hf = 0; hf < 2; ++hf) hr[kk][hf] = *reinterpret_cast<const f32x4 *>(hc + off + 4 * hf);
+        dH[kk] = *reinterpret_cast<const bf16x8 *>(dhc + off);
+        dL[kk] = *reinterpret_cast<const bf16x8 *>(dhc + DK * DV + off);
+    }
 
     float *dGw = s.dGp[wave];
     float *dbw = s.dbp[wave];
@@ -586,22 +588,18 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     f32x4 dkt[4];
     bf16x8 hH[4], hL[4];
     {
-        bf16x8 dH[4], dL[4];
         float dot = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            float rh[8], rd[8];
+            float rh[8];
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
                 rh[e2] = hr[kk][0][e2];
                 rh[4 + e2] = hr[kk][1][e2];
-                rd[e2] = dr[kk][0][e2];
-                rd[4 + e2] = dr[kk][1][e2];
             }
 #pragma unroll
-            for (int e2 = 0; e2 < 8; ++e2) dot += rh[e2] * rd[e2];
+            for (int e2 = 0; e2 < 8; ++e2) dot += rh[e2] * ((float)dH[kk][e2] + (float)dL[kk][e2]);
             split8(rh, hH[kk], hL[kk]);
-            split8(rd, dH[kk], dL[kk]);
         }
         // dk: rl_s (dh' v'^T) + Q^T dPm;  gate terms of h'
         float lastacc = 0.f;
@@ -1059,12 +1057,18 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
         }
         // dh' of chunk c (unchanged so far in this step) -> HBM
         if (own) {
-            float *dst = p.dh_ws + ((int64_t)(cbase + c) * p.Hv + j) * DK * DV + half * HVC;
+            // the hi / lo copy of dh in LDS is dh' of chunk c: written out as two
+            // bf16 planes [d][v] (the chunk-local kernel's split operands), 16
+            // bytes per thread and plane row piece
+            bf16 *dst = reinterpret_cast<bf16 *>(p.dh_ws) + ((int64_t)(cbase + c) * p.Hv + j) * 2 * DK * DV + half * HVC;
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    dst[(int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16] = dh[ct][jj];
+            for (int i = 0; i < DK * HVC / 8 / NT; ++i) {
+                const int pc = tid + i * NT;
+                const int row = pc / (HVC / 8), col = 8 * (pc % (HVC / 8));
+                *reinterpret_cast<bf16x8 *>(dst + row * DV + col) = *reinterpret_cast<const bf16x8 *>(&s.hH[row * L64 + col]);
+                *reinterpret_cast<bf16x8 *>(dst + DK * DV + row * DV + col) =
+                    *reinterpret_cast<const bf16x8 *>(&s.hL[row * L64 + col]);
+            }
         }
         __syncthreads();
 

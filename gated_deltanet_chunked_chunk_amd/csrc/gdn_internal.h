@@ -71,7 +71,7 @@ struct BwdParams {
     const float *A;                  // [rows][Hv][64] WY matrices (forward's low-level A)
     const float *vn;                 // [total_chunks][Hv][64][V] v' of every chunk (forward's v_new)
     const float *dht;                // [N][Hv][K][V] or nullptr
-    float *dh_ws;                    // [total_chunks][Hv][K][V] gradient wrt the state after each chunk
+    float *dh_ws;                    // [total_chunks][Hv][2][K][V] bf16 (hi, lo): gradient wrt the state after each chunk
     float *dvp_ws;                   // [total_chunks][Hv][64][V] dv' (all 64 rows of every chunk)
     float *dq_ws, *dk_ws;            // [rows][Hv][K] per-v-head dq, dk
     void *dq, *dk, *dv;              // bf16 or fp32 per grad_f32
