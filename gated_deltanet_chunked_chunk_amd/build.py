@@ -8,6 +8,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -21,11 +22,18 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source code-generation options.  The forward's chunk loop runs one
+# workgroup per CU whatever the register count (its LDS decides that), so the
+# scheduler is asked for instruction-level parallelism instead of occupancy
+# (measured: 1.4 % faster at 16/16 heads, 2.9 % at 2/8; the same option makes
+# the backward kernels 1.5 % slower, so they keep the default).
+SOURCE_FLAGS = {
+    "gdn_fwd.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"],
+}
 
 
 def hipcc() -> str:
@@ -35,10 +43,7 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompiles; writes to a temp name and renames (atomic)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"), "-o", tmp] + SOURCES
+def _run(cmd, verbose: bool) -> None:
     res = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
                     if "is not a recognized feature for this target" not in line)
@@ -46,6 +51,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles (one object per source, with its own options, then one
+    shared library); writes to a temp name and renames (atomic)."""
+    with tempfile.TemporaryDirectory() as td:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(td, os.path.basename(src) + ".o")
+            _run([hipcc()] + HIPCC_FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) +
+                 ["-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj], verbose)
+            objs.append(obj)
+        tmp = LIB + ".tmp"
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
     return LIB
 
