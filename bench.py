@@ -261,7 +261,7 @@ def fwd_bwd(args, w, x, dev):
     achieved = bwd_flops / (bwd_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "gdn_bwd (reverse pass + chunk-local gradients + key-head sums)",
+                "kernel": "gdn_bwd (reverse pass + chunk-local gradients, key-head sums fused)",
                 "algorithmic_flops_per_launch": bwd_flops, "algorithmic_bytes_per_launch": bwd_bytes,
                 "mean_launch_ms": round(bwd_ms, 4), "forward_mean_launch_ms": round(fwd_ms, 4)}
     cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(x, w, args.cpu_seconds)
