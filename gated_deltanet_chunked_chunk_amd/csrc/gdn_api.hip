@@ -299,7 +299,7 @@ int make_bwd_plan(const gdn_bwd_desc *bd, BwdPlan *B) {
     off = align_up(off + n_h * 4);
     B->off_dvp = off;
     off = align_up(off + (size_t)P.total_chunks * d->H_v * gdn::kChunk * d->V * 4);
-    B->off_dq = off;  // partial key-head sums of dq and dk (fp32 [rows][H_qk][K])
+    B->off_dq = off;  // running key-head sums of dq and dk (fp32 [rows][H_qk][K])
     off = align_up(off + rows * d->H_qk * d->K * 4);
     B->off_dk = off;
     off = align_up(off + rows * d->H_qk * d->K * 4);

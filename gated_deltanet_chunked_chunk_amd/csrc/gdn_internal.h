@@ -61,8 +61,8 @@ struct FwdParams {
     float *h_out, *a_out, *vn_out;
 };
 
-// Backward (gdn_bwd.hip): reverse pass over segments, then chunk-local gradients,
-// then the key-head sums of dq and dk.
+// Backward (gdn_bwd.hip): reverse pass over segments, then chunk-local gradients
+// (which also sum dq and dk over each key head's v-heads).
 struct BwdParams {
     const uint16_t *q, *k, *v, *dO;  // bf16 bits
     const float *g, *beta;
@@ -73,7 +73,7 @@ struct BwdParams {
     const float *dht;                // [N][Hv][K][V] or nullptr
     float *dh_ws;                    // [total_chunks][Hv][2][K][V] bf16 (hi, lo): gradient wrt the state after each chunk
     float *dvp_ws;                   // [total_chunks][Hv][64][V] dv' (all 64 rows of every chunk)
-    float *dq_ws, *dk_ws;            // [rows][Hv][K] per-v-head dq, dk
+    float *dq_ws, *dk_ws;            // [rows][H_qk][K] fp32 running sums of dq, dk over a key head's v-heads
     void *dq, *dk, *dv;              // bf16 or fp32 per grad_f32
     float *dg, *dbeta;               // [rows][Hv]
     float *dh0;                      // [N][Hv][K][V] or nullptr
