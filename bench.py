@@ -19,6 +19,7 @@ inputs resident in HBM.  Prints ONE JSON line on stdout:
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload NAME]
        [--cp auto|warmup|off] [--no-cpu-baseline] [--cpu-seconds 10]
        python bench.py --sweep [--steps 200] [--warmup 100] [--cp auto]   (head-setting sweep)
+       python bench.py --sweep-bwd [--steps 200] [--warmup 100]   (training step against total tokens)
        python bench.py --workload gdn_fwdbwd_1x32768_h4x16   (training step: forward keeping h and A,
               then the backward; roofline of the backward against the bf16 MFMA peak)
 """
@@ -231,6 +232,65 @@ def cpu_baseline_bwd(x, w, target_s: float):
                       f"backward, {dt:.1f} s"}
 
 
+SWEEP_BWD_TOKENS = [(1, 8192), (1, 32768), (4, 32768), (1, 131072)]
+
+
+def sweep_bwd(steps: int, warmup: int, cp: str):
+    """Training-step latency (the forward keeping h, A and v', then the
+    backward) against total tokens over the pages' head settings: one JSON line
+    per case, then a markdown table on stderr.  Inputs: the forward's sweep
+    inputs plus dO N(0, 1) rounded to bfloat16 and d final_state N(0, 0.01^2),
+    drawn on the device from a seeded generator."""
+    import torch
+    from gated_deltanet_chunked_chunk_amd import PreparedForwardBackward
+    from gated_deltanet_chunked_chunk_amd import workloads as W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows = []
+    for (hqk, hv), model in SWEEP_HEADS:
+        for B, T in SWEEP_BWD_TOKENS:
+            seed = 2000 + hqk * 100 + hv
+            x = W.device_inputs(B, T, hqk, hv, seed=seed, device=dev)
+            gen = torch.Generator(device=dev).manual_seed(seed)
+            V, K = x["v"].shape[-1], x["q"].shape[-1]
+            x["dO"] = torch.randn(B, T, hv, V, generator=gen, device=dev).to(torch.bfloat16)
+            x["dht"] = torch.randn(B, hv, K, V, generator=gen, device=dev) * 0.01
+            call = PreparedForwardBackward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["dO"], scale=x["scale"],
+                                           initial_state=x["initial_state"], d_final_state=x["dht"], cp=cp)
+            for _ in range(warmup):
+                call()
+            stream = torch.cuda.current_stream(dev)
+            ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+            torch.cuda.synchronize()
+            for a, b, c in ev:
+                a.record(stream)
+                call.forward()
+                b.record(stream)
+                call.backward()
+                c.record(stream)
+            torch.cuda.synchronize()
+            fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / steps
+            bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / steps
+            _, flops = bwd_algorithmic(x)
+            frac = flops / (bwd_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+            line = {"model": model, "H_qk": hqk, "H_v": hv, "B": B, "T": T, "total_tokens": B * T,
+                    "bwd_cp": call.binfo["cp"], "bwd_segment_chunks": call.binfo["segment_chunks"],
+                    "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4), "step_ms": round(fwd_ms + bwd_ms, 4),
+                    "step_tokens_per_s": round(B * T / ((fwd_ms + bwd_ms) * 1e-3), 1),
+                    "bwd_mfma_frac": round(frac, 4)}
+            print(json.dumps(line), flush=True)
+            rows.append(line)
+            del call, x
+            torch.cuda.empty_cache()
+    print("| layer heads / TP | H_qk | H_v | B x T | reverse-pass CP (L) | forward ms | backward ms | step ms | "
+          "M tokens/s | backward MFMA frac |", file=sys.stderr)
+    print("|---|---|---|---|---|---|---|---|---|---|", file=sys.stderr)
+    for r in rows:
+        print(f"| {r['model']} | {r['H_qk']} | {r['H_v']} | {r['B']} x {r['T']} | {r['bwd_cp']} "
+              f"({r['bwd_segment_chunks']}) | {r['fwd_ms']:.3f} | {r['bwd_ms']:.3f} | {r['step_ms']:.3f} | "
+              f"{r['step_tokens_per_s'] / 1e6:.1f} | {r['bwd_mfma_frac']:.3f} |", file=sys.stderr)
+
+
 def fwd_bwd(args, w, x, dev):
     """One step = the forward keeping h and A, then the backward on them."""
     import torch
@@ -293,6 +353,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true",
                     help="forward latency over the pages' head settings and batch lengths (one JSON line each)")
+    ap.add_argument("--sweep-bwd", action="store_true",
+                    help="training-step latency against total tokens over the pages' head settings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -308,6 +370,9 @@ def main():
 
     if args.sweep:
         sweep(args.steps, args.warmup, args.cp)
+        return
+    if args.sweep_bwd:
+        sweep_bwd(args.steps, args.warmup, args.cp)
         return
 
     import torch
