@@ -15,8 +15,9 @@ CP_MODES = {"off": 0, "exact": 1, "warmup": 2, "auto": 3}
 CP_NAMES = {v: k for k, v in CP_MODES.items()}
 
 # Every exported entry point of include/gdn.h.
-EXPORTS = ("gdn_abi_version", "gdn_status_str", "gdn_last_error", "gdn_fwd_plan", "gdn_fwd", "gdn_chunk_cumsum",
-           "gdn_bwd_plan", "gdn_bwd")
+EXPORTS = ("gdn_abi_version", "gdn_status_str", "gdn_last_error", "gdn_fwd_plan", "gdn_fwd", "gdn_fwd_noalloc",
+           "gdn_chunk_cumsum", "gdn_bwd_plan", "gdn_bwd")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
 
 
 class FwdDesc(ctypes.Structure):
@@ -105,6 +106,8 @@ def lib():
         L.gdn_fwd.restype = ctypes.c_int
         L.gdn_fwd.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(FwdPtrs), ctypes.c_void_p, ctypes.c_size_t,
                               ctypes.c_void_p]
+        L.gdn_fwd_noalloc.restype = ctypes.c_int
+        L.gdn_fwd_noalloc.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(FwdPtrs), ctypes.c_void_p]
         if L.gdn_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} has ABI version {L.gdn_abi_version()}, this binding expects "
                                f"{ABI_VERSION}; rebuild it")

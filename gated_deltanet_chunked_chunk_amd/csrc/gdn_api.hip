@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -322,6 +323,42 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// ---- the allocation-free forward's workspace: one static device array per
+// GPU (each device holds its own copy, at its own address, from the time the
+// library's code object is loaded on it until the process ends).  Host code
+// never passes `scratch` itself (its host-side name is a stand-in, not a
+// device address): the address is looked up once per device with that device
+// current and kept in g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// This thread's current device, the stream's device (they must agree), and the
+// device address of that device's scratch array.
+int scratch_for_stream(void *stream, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GDN_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDN_EHIP, "device index %d out of range", dev);
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) return fail(GDN_EHIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if ((int)sdev != dev)
+        return fail(GDN_EINVAL, "the stream belongs to device %d but device %d is current", (int)sdev, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(GDN_EHIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -440,6 +477,23 @@ int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_
     if (err) return fail(GDN_EHIP, "forward launch failed: %s", gdn::hip_error_text(err));
     g_last_error.clear();
     return GDN_OK;
+}
+
+int gdn_fwd_noalloc(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *stream) {
+    Plan P;
+    const int rc = make_plan(d, &P);
+    if (rc != GDN_OK) return rc;
+    if (P.workspace > (size_t)GDN_NOALLOC_SCRATCH_BYTES)
+        return fail(GDN_EWORKSPACE,
+                    "this call needs %zu bytes of workspace; the allocation-free entry point has %zu (use gdn_fwd "
+                    "with a caller workspace, or a longer segment length)",
+                    P.workspace, (size_t)GDN_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if (P.workspace > 0) {
+        const int rs = scratch_for_stream(stream, &ws);
+        if (rs != GDN_OK) return rs;
+    }
+    return gdn_fwd(d, p, ws, P.workspace, stream);
 }
 
 int gdn_bwd_plan(const gdn_bwd_desc *d, gdn_bwd_plan_info *out) {

@@ -156,6 +156,26 @@ int gdn_fwd_plan(const gdn_fwd_desc *d, gdn_fwd_plan_info *out);
 int gdn_fwd(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *workspace, size_t workspace_bytes,
             void *stream);
 
+/* Forward pass that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, validation, kernels and results as
+ * gdn_fwd, without the workspace arguments: the workspace gdn_fwd_plan sizes
+ * (non-zero only for GDN_CP_EXACT: per-segment S, M and start states) lives in
+ * a static device array of GDN_NOALLOC_SCRATCH_BYTES owned by the library, one
+ * per GPU, held from the library's load until the process ends.  The caller
+ * still passes every input and output.
+ *   - A call whose plan needs more than GDN_NOALLOC_SCRATCH_BYTES returns
+ *     GDN_EWORKSPACE and launches nothing.
+ *   - The calling thread's current device must be the device `stream` belongs
+ *     to (GDN_EINVAL otherwise).
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap in
+ *     time on one GPU (different streams, or host threads) race and must be
+ *     serialised by the caller.  Nothing in the array needs to start at zero
+ *     (every word a call reads was written earlier in the same call).
+ *   - Calls no hipMalloc, hipFree or other allocating routine. */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gdn_fwd_noalloc(const gdn_fwd_desc *d, const gdn_fwd_ptrs *p, void *stream);
+
 /* Chunk-local running sum of the log-gates (the transformed g returned by the
  * pages' low-level forward, aisparkup.com wiki "low-level API"):
  * out[t] = sum of g over the tokens of t's chunk up to and including t.
