@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 PAGES_MS = {"gdn_fwd_1x32768_h16x16": 0.493, "gdn_fwd_1x32768_h2x8": 0.310}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "gated_deltanet_chunked_chunk_amd", "csrc", f)
-                  for f in ("gdn_fwd.hip", "gdn_internal.h")] + [
+                  for f in ("gdn_fwd.hip", "gdn_internal.h", "gdn_window.h")] + [
                   os.path.join(ROOT, "gated_deltanet_chunked_chunk_amd", "build.py")]  # its code-generation options
 
 

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = [os.path.join(CSRC, "gdn_api.hip"), os.path.join(CSRC, "gdn_fwd.hip"), os.path.join(CSRC, "gdn_bwd.hip")]
-HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(CSRC, "gdn_internal.h")]
+HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(CSRC, "gdn_internal.h"), os.path.join(CSRC, "gdn_window.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -180,7 +180,7 @@ int make_plan(const gdn_fwd_desc *d, Plan *P) {
     P->N = d->num_seqs;
     P->total_chunks = (int32_t)total_chunks;
     P->max_chunks = gdn::seq_chunks(max_len);
-    P->warmup = d->cp_warmup_chunks > 0 ? d->cp_warmup_chunks : gdn::kDefaultWarmup;
+    P->warmup = d->cp_warmup_chunks > 0 ? d->cp_warmup_chunks : 0;  // 0: no cap (gate-driven window)
 
     int32_t mode = d->cp_mode;
     int32_t L = std::max(1, P->max_chunks);
@@ -258,7 +258,7 @@ int make_bwd_plan(const gdn_bwd_desc *bd, BwdPlan *B) {
     const Plan &P = B->fwd;
     int32_t L = std::max(1, P.max_chunks);
     int32_t mode = d->cp_mode;
-    int32_t warmup = d->cp_warmup_chunks > 0 ? d->cp_warmup_chunks : gdn::kDefaultWarmup;
+    int32_t warmup = d->cp_warmup_chunks > 0 ? d->cp_warmup_chunks : 0;  // 0: no cap
     if (mode != GDN_CP_OFF) {
         if (d->cp_segment_chunks > 0) {
             L = d->cp_segment_chunks;

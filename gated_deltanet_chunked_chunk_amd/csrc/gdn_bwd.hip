@@ -44,6 +44,7 @@
 #include <algorithm>
 
 #include "gdn_internal.h"
+#include "gdn_window.h"
 
 namespace gdn {
 namespace bwdk {
@@ -963,18 +964,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
     if (pre || exact_start) {
         c_last = c_end;
     } else if (!e.last && p.cp_mode == 2 /* WARMUP */) {
-        float acc = 0.f;
-        int w = 0;
-        while (w < p.warmup_cap && c_last < nt) {
-            const int tok = c_last * CH + lane;
-            float gv = 0.f;
-            if (tok < e.seq_len) gv = p.g[(e.row0 + tok) * p.Hv + j];
-            gv = sum64(gv);
-            acc += __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gv)));
-            ++c_last;
-            ++w;
-            if (acc <= kLnNoiseFloor) break;
-        }
+        // gate-driven window after the segment, until the summed log-gates
+        // reach the fp32 noise floor, or to the sequence end (then the walk
+        // begins from d final_state and is exact)
+        const int w = gate_window(p.g + e.row0 * p.Hv, p.Hv, j, e.seq_len, c_end, 1, nt - c_end, p.warmup_cap, lane);
+        c_last = __builtin_amdgcn_readfirstlane(c_end + w);
     } else {
         c_last = nt;
     }

@@ -23,11 +23,11 @@
 //
 // Precision (the pages' "restructure without losing precision", summarylog.com
 // essay, "formula restructuring"): products of two exact bf16 inputs (K K^T,
-// Q K^T, K^T T~^T) use one bf16 MFMA; operands that carry fp32 values which
-// feed the output or the state with full weight are split into hi + lo bf16
-// pairs: T diag(beta), P, v', the decayed v', and H (in Q H only when o is
-// fp32: a bf16 o takes Q times the bf16-rounded H, whose error stays below
-// the output's own rounding and never reaches the state).  Decays and beta are fp32
+// Q K^T) use one bf16 MFMA; operands that carry fp32 values which feed the
+// output or the state with full weight are split into hi + lo bf16 pairs:
+// T diag(beta), T diag(beta gamma), W, P, v', the decayed v', and H (in Q H
+// only when o is fp32: a bf16 o takes Q times the bf16-rounded H, whose error
+// stays below the output's own rounding and never reaches the state).  Decays and beta are fp32
 // row/column scales; every exponent is a non-positive difference G_i - G_s
 // (masked before the exp), so nothing overflows.
 //
@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "gdn_internal.h"
+#include "gdn_window.h"
 
 namespace gdn {
 
@@ -201,10 +202,10 @@ static_assert(DK == DV, "K, Q and V tiles share one layout");
 
 struct __attribute__((aligned(16))) Smem8 {
     bf16 k[2][TILE];                  // K by chunk parity (row = token, padded rows)
-    bf16 q[2][TILE];                  // Q by chunk parity
+    bf16 q[TILE];                     // Q of the chunk being prepared
     bf16 v[TILE];                     // V of the state pass's next chunk
     float a[CH * AS];                 // A, inverted in place into T
-    bf16x8 wf[4][4][64];              // -W as A fragments [row tile][k step][lane]
+    bf16x8 wf[2][4][4][64];           // -W as hi / lo A fragments [hi, lo][row tile][k step][lane]
     bf16x8 tf[2][6][64];              // T diag(beta) as A fragments [hi, lo][fragment][lane]
     bf16x8 pf[2][6][64];              // scale P as A fragments [hi, lo][fragment][lane]
     // the two 32 x 32 diagonal blocks of A, then of T, transposed ([block][col][row])
@@ -277,6 +278,14 @@ __device__ __forceinline__ bf16x8 frag_rp(const bf16 *X, const int r0, const int
 // Rows beyond a chunk's buffer resource (past the sequence end) arrive as zeros.
 typedef __attribute__((address_space(3))) void lds_void;
 
+// The LDS address of a generic pointer into this workgroup's LDS: its low 32
+// bits (the shared aperture sits in the high half).  Taken through integers
+// rather than an address-space cast, whose null check this compiler can fold
+// into an illegal compare against the aperture register.
+__device__ __forceinline__ lds_void *lds_ptr(const void *p) {
+    return (lds_void *)(uintptr_t)(uint32_t)(uintptr_t)p;
+}
+
 // Part `part` of PARTS of a tile: the wave issues loads part, part + PARTS, ...
 // of the tile's 17.  Lane l of load i fills 16-byte slot 64 i + l of the
 // padded tile, i.e. row (64 i + l) / 17 and piece (64 i + l) % 17; the pad
@@ -309,7 +318,7 @@ __device__ __forceinline__ void dma_tile(bf16 *tile, const char *base, const uns
 #pragma unroll
     for (int n = 0; n < TileOffs<PARTS>::NI; ++n) {
         const int i = part + n * PARTS;
-        if (i < TLOADS) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(tile + 512 * i), 16, (int)t.o[n], 0, 0, 0);
+        if (i < TLOADS) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(tile + 512 * i), 16, (int)t.o[n], 0, 0, 0);
     }
 }
 
@@ -318,11 +327,19 @@ __device__ __forceinline__ void dma_gb(Smem8 &s, const Inputs &in, const int c, 
     if (pw >= 2) return;
     const __amdgpu_buffer_rsrc_t r = chunk_rsrc(pw == 0 ? in.g : in.b, in.gstride, c, in.seq_len);
     float *dst = (pw == 0) ? s.graw[c & 1] : s.braw[c & 1];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 4, (int)((unsigned)lane * in.gstride), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(dst), 4, (int)((unsigned)lane * in.gstride), 0, 0, 0);
 }
 
 // This wave's direct loads have landed in LDS (vmcnt(0); other counters untouched).
 __device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// All but this wave's N most recent vector memory operations have completed
+// (vmcnt(N); they complete in issue order).
+template <int N>
+__device__ __forceinline__ void dma_wait_but() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
 
 // Workgroup barrier for LDS traffic: this wave's own LDS reads and writes are
 // complete (lgkmcnt(0)) when it arrives, but its direct HBM -> LDS loads may
@@ -444,7 +461,7 @@ __device__ __forceinline__ bool decays_factor(const Smem8 &s, const int lane) {
 __device__ __forceinline__ void pfrag9(Smem8 &s, const int lane, const int f, const int buf, const float scale,
                                        const bool fact) {
     const int m = lane & 15, g = lane >> 4;
-    const bf16 *K = s.k[buf], *Q = s.q[buf];
+    const bf16 *K = s.k[buf], *Q = s.q;
     const int rt = frag_rt(f), ks = frag_ks(f);
     f32x4 accp[2] = {f32x4{}, f32x4{}};
 #pragma unroll
@@ -635,12 +652,15 @@ __device__ __forceinline__ f32x4 trow4(const Smem8 &s, const int row, const int 
     return *reinterpret_cast<const f32x4 *>(p);
 }
 
-// ---- preparation: for the row tiles rt0 and rt0 + 1, the -W A fragments of
-// key-dim step kk (W^T = K^T (T diag(beta gamma))^T, two 16-row halves), and
-// the T diag(beta) hi/lo A fragment tf_frag of those rows for U (-1: none).
-// K^T comes from transposing reads of K, so T is read at the transposed-read
-// token order.  Rows 0..31 of T are final after inverse level 1, rows 32..63
-// after level 2.
+// ---- preparation: for the row tiles rt0 and rt0 + 1, the -W hi / lo A
+// fragments of key-dim step kk (W^T = K^T (T diag(beta gamma))^T, two 16-row
+// halves), and the T diag(beta) hi/lo A fragment tf_frag of those rows for U
+// (-1: none).  K^T comes from transposing reads of K, so T is read at the
+// transposed-read token order.  Rows 0..31 of T are final after inverse level
+// 1, rows 32..63 after level 2.  T diag(beta gamma) enters as hi + lo bf16 and
+// W leaves as hi + lo: W H is the term v' = U - W H nearly cancels when the
+// state already predicts v well (gates near 1), so W's own rounding would
+// reach v', and through it the state, amplified.
 __device__ __forceinline__ void wfrag9(Smem8 &s, const int lane, const int rt0, const int kk, const int tf_frag,
                                        const int buf) {
     const int m = lane & 15, g = lane >> 4;
@@ -653,7 +673,7 @@ __device__ __forceinline__ void wfrag9(Smem8 &s, const int lane, const int rt0, 
         ka[ks][0] = frag_t(K, 32 * kk, 32 * ks, lane);
         ka[ks][1] = frag_t(K, 32 * kk + 16, 32 * ks, lane);
     }
-    bf16x8 tw[2][2];  // [row tile][token step]
+    bf16x8 twh[2][2], twl[2][2];  // [row tile][token step]
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -663,11 +683,13 @@ __device__ __forceinline__ void wfrag9(Smem8 &s, const int lane, const int rt0, 
             const f32x4 t0 = trow4(s, row, c0), t1 = trow4(s, row, c0 + 16);
             const f32x4 bg0 = *reinterpret_cast<const f32x4 *>(&s.bg[c0]);
             const f32x4 bg1 = *reinterpret_cast<const f32x4 *>(&s.bg[c0 + 16]);
+            float x[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                tw[r][ks][e] = (bf16)(t0[e] * bg0[e]);
-                tw[r][ks][4 + e] = (bf16)(t1[e] * bg1[e]);
+                x[e] = t0[e] * bg0[e];
+                x[4 + e] = t1[e] * bg1[e];
             }
+            split8v(x, twh[r][ks], twl[r][ks]);
         }
     if (tf_frag >= 0) {
         const int rt = frag_rt(tf_frag), ks = frag_ks(tf_frag);
@@ -692,11 +714,16 @@ __device__ __forceinline__ void wfrag9(Smem8 &s, const int lane, const int rt0, 
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             if (ks >= nks) continue;
-            w0 = mfma16(ka[ks][0], tw[r][ks], w0);
-            w1 = mfma16(ka[ks][1], tw[r][ks], w1);
+            w0 = mfma16(ka[ks][0], twh[r][ks], w0);
+            w0 = mfma16(ka[ks][0], twl[r][ks], w0);
+            w1 = mfma16(ka[ks][1], twh[r][ks], w1);
+            w1 = mfma16(ka[ks][1], twl[r][ks], w1);
         }
-        s.wf[rt0 + r][kk][lane] = bf16x8{(bf16)(-w0[0]), (bf16)(-w0[1]), (bf16)(-w0[2]), (bf16)(-w0[3]),
-                                         (bf16)(-w1[0]), (bf16)(-w1[1]), (bf16)(-w1[2]), (bf16)(-w1[3])};
+        const float nw[8] = {-w0[0], -w0[1], -w0[2], -w0[3], -w1[0], -w1[1], -w1[2], -w1[3]};
+        bf16x8 hi, lo;
+        split8v(nw, hi, lo);
+        s.wf[0][rt0 + r][kk][lane] = hi;
+        s.wf[1][rt0 + r][kk][lane] = lo;
     }
 }
 
@@ -765,7 +792,7 @@ __device__ __forceinline__ void u9_lean(const Smem8 &s, const int lane, const in
 __device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int ct,
                                     const int buf, const float scale, const int ln) {
     const int m = ln & 15;
-    const bf16 *Q = s.q[buf];
+    const bf16 *Q = s.q;
     bf16x8 qa[4][4];  // [k step][row tile]
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -794,7 +821,7 @@ __device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f
 __device__ __forceinline__ void qh9_both(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2],
                                          const int buf, const float scale, const int ln) {
     const int m = ln & 15;
-    const bf16 *Q = s.q[buf];
+    const bf16 *Q = s.q;
     bf16x8 qa[4][4];  // [k step][row tile]
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -823,16 +850,28 @@ __device__ __forceinline__ void qh9_both(const Smem8 &s, const f32x4 (&hacc)[2][
     }
 }
 
-// v' = U - W H (vp enters holding U)
+// v' = U - W H (vp enters holding U), with W and H as hi + lo bf16 (the lo x
+// lo term, below fp32 resolution of the product, is left out).  The W
+// fragments of one k step (hi and lo, 32 registers) are read while the
+// previous step's products run.
 __device__ __forceinline__ void wh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int ln) {
-    bf16x8 wa[4][4];  // [k step][row tile]
+    bf16x8 wa[2][4], wl[2][4];  // [k step parity][row tile]
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) wa[kk][rt] = s.wf[rt][kk][ln];
-    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+    for (int rt = 0; rt < 4; ++rt) {
+        wa[0][rt] = s.wf[0][rt][0][ln];
+        wl[0][rt] = s.wf[1][rt][0][ln];
+    }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
+        const int b = kk & 1;
+        if (kk + 1 < 4) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                wa[b ^ 1][rt] = s.wf[0][rt][kk + 1][ln];
+                wl[b ^ 1][rt] = s.wf[1][rt][kk + 1][ln];
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the next step's reads go out ahead of this step's products
         bf16x8 hh[2], hl[2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh[ct], hl[ct]);
@@ -840,8 +879,9 @@ __device__ __forceinline__ void wh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                vp[rt][ct] = mfma16(wa[kk][rt], hh[ct], vp[rt][ct]);
-                vp[rt][ct] = mfma16(wa[kk][rt], hl[ct], vp[rt][ct]);
+                vp[rt][ct] = mfma16(wa[b][rt], hh[ct], vp[rt][ct]);
+                vp[rt][ct] = mfma16(wa[b][rt], hl[ct], vp[rt][ct]);
+                vp[rt][ct] = mfma16(wl[b][rt], hh[ct], vp[rt][ct]);
             }
     }
 }
@@ -851,9 +891,12 @@ __device__ __forceinline__ void wh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f
 __device__ __forceinline__ void wh8_lean(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int ln) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 wa[4];
+        bf16x8 wa[4], wl[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) wa[rt] = s.wf[rt][kk][ln];
+        for (int rt = 0; rt < 4; ++rt) {
+            wa[rt] = s.wf[0][rt][kk][ln];
+            wl[rt] = s.wf[1][rt][kk][ln];
+        }
         bf16x8 hh[2], hl[2];
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh[ct], hl[ct]);
@@ -863,6 +906,7 @@ __device__ __forceinline__ void wh8_lean(const Smem8 &s, const f32x4 (&hacc)[2][
             for (int ct = 0; ct < 2; ++ct) {
                 vp[rt][ct] = mfma16(wa[rt], hh[ct], vp[rt][ct]);
                 vp[rt][ct] = mfma16(wa[rt], hl[ct], vp[rt][ct]);
+                vp[rt][ct] = mfma16(wl[rt], hh[ct], vp[rt][ct]);
             }
     }
 }
@@ -1101,24 +1145,12 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
     int c_first = e.c_begin;
     bool from_h0 = (e.c_begin == 0);
     if (!PRE && !from_h0 && p.cp_mode == 2 /* WARMUP */) {
-        // gate-driven window: walk back chunk by chunk until the summed
-        // log-gates drop below the fp32 noise floor, the cap, or the start
-        float acc = 0.f;
-        int w = 0;
-        while (w < p.warmup_cap && c_first > 0) {
-            const int c = c_first - 1;
-            const int tok = c * CH + lane;
-            float gv = 0.f;
-            if (tok < e.seq_len) gv = p.g[(e.row0 + tok) * p.Hv + j];
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) gv += __shfl_xor(gv, off, 64);
-            // every lane holds the same sum; make that explicit so the loop
-            // bounds below stay wave-uniform (scalar) values
-            acc += __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gv)));
-            c_first = c;
-            ++w;
-            if (acc <= kLnNoiseFloor) break;
-        }
+        // gate-driven window: back from the segment start until the summed
+        // log-gates reach the fp32 noise floor, or to the sequence start (then
+        // the walk begins from the initial state and is exact)
+        const int w = gate_window(p.g + e.row0 * p.Hv, p.Hv, j, e.seq_len, e.c_begin - 1, -1, e.c_begin,
+                                  p.warmup_cap, lane);
+        c_first = __builtin_amdgcn_readfirstlane(e.c_begin - w);
         from_h0 = (c_first == 0);
     }
     const int c_end = e.c_begin + e.c_count;
@@ -1141,15 +1173,19 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
     // preparation of chunk c + 1 (preparation waves); c = c_first - 1 only
     // prepares the first chunk.
     //   step  state waves                        preparation waves
-    //   1     v' = U - W H                       gate scan, K K^T; load Q, g, beta of c + 2
+    //   1     v' = U - W H                       gate scan, K K^T; load g, beta of c + 2
     //   2     O = scale (gamma Q H + P v')       inverse level 0; load V of c + 1
     //   3     H update                           inverse level 1 (pw 0, 1), P
-    //   4     scale gamma Q H of chunk c + 1,    inverse level 2; W, T diag(beta),
-    //         column tile 0; load K of c + 2     rows 0..31
-    //   5     the same, column tile 1            W, T diag(beta), rows 32..63
-    // K and Q sit in LDS by chunk parity and V for one chunk; each load is
-    // issued once the step that last reads its slot is behind a barrier, and
-    // every wave waits for its own loads before the iteration's first barrier.
+    //   4     scale gamma Q H of chunk c + 1     inverse level 2; W, T diag(beta),
+    //         (the last reads of its Q tile);    rows 0..31
+    //         load K of c + 2
+    //   5     (optional h store)                 W, T diag(beta), rows 32..63;
+    //                                            load Q of c + 2
+    // K sits in LDS by chunk parity, Q and V for one chunk each; each load is
+    // issued once the step that last reads its slot is behind a barrier.  Every
+    // wave waits for its own loads before the iteration's first barrier, except
+    // that the Q loads of the last step stay in flight until the barrier before
+    // P (step 3 of the next iteration), the first step that reads them.
     // K goes out from the state waves: a transposing LDS read is compiled with
     // a wait for every direct load the wave has in flight, and the preparation
     // waves read K transposed right after the K slot frees up.  Both roles run
@@ -1223,15 +1259,17 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             }
             lds_barrier();
             if (c + 2 < c_end) dma_tile<NSTATE>(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, koffs);
-            if (!PRE && prep && c + 1 >= e.c_begin) {
-                if (OF32) qh9(s, hacc, qh, 0, nb, p.scale, lane_now());
-                else qh9_both(s, hacc, qh, nb, p.scale, lane_now());
+            if (!PRE && prep && c + 1 >= e.c_begin) {  // the last reads of this Q tile
+                if (OF32) {
+                    qh9(s, hacc, qh, 0, nb, p.scale, lane_now());
+                    qh9(s, hacc, qh, 1, nb, p.scale, lane_now());
+                } else {
+                    qh9_both(s, hacc, qh, nb, p.scale, lane_now());
+                }
             }
             lds_barrier();
-            if (!PRE && prep && c + 1 >= e.c_begin) {
-                if (OF32) qh9(s, hacc, qh, 1, nb, p.scale, lane_now());
-                if (p.h_out) store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
-            }
+            if (!PRE && prep && c + 1 >= e.c_begin && p.h_out)
+                store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
             // v' of chunk c, out of the first step's way (the state waves have no
             // other work here for a bf16 o)
             if (!PRE && chain && out && p.vn_out)
@@ -1255,9 +1293,16 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                                         : nullptr;
             if (has_chunks) {
                 dma_tile<4>(s.k[c_first & 1], in.k, in.kstride, c_first, e.seq_len, pw, kqoffs);
-                if (!PRE && c_first >= e.c_begin) dma_tile<4>(s.q[c_first & 1], in.q, in.kstride, c_first, e.seq_len, pw, kqoffs);
+                if (!PRE && c_first >= e.c_begin) dma_tile<4>(s.q, in.q, in.kstride, c_first, e.seq_len, pw, kqoffs);
                 dma_gb(s, in, c_first, pw, lane);
             }
+            // this wave's loads per tile, and of g or beta per chunk
+            constexpr int NTILE = (TLOADS - pw + 3) / 4, NGB = pw < 2 ? 1 : 0;
+            // Q sits in one LDS tile: the tile of chunk c + 2 is loaded in the
+            // last step of iteration c (after the state waves' last read of
+            // chunk c + 1's), and only P (step 3 of iteration c + 1) waits for
+            // it; the waits before that leave these loads in flight.
+            bool q_pending = false;
             for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
                 // with the wave's share fixed at compile time, its lane-derived
                 // LDS addresses are few enough to stay in registers across the
@@ -1266,16 +1311,21 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 const bool prep = c + 1 < c_end;   // preparation of chunk c + 1
                 const bool ahead = c + 2 < c_end;  // loads of chunk c + 2
                 const int nb = (c + 1) & 1;
-                dma_wait();
+                if (q_pending) dma_wait_but<NTILE>();  // g, beta and V of the previous iteration
+                else dma_wait();
                 lds_barrier();
-                if (ahead) {
-                    if (!PRE && c + 2 >= e.c_begin) dma_tile<4>(s.q[c & 1], in.q, in.kstride, c + 2, e.seq_len, pw, kqoffs);
-                    dma_gb(s, in, c + 2, pw, ln);
-                }
+                if (ahead) dma_gb(s, in, c + 2, pw, ln);
                 if (prep) prod9(s, ln, pw, nb);
                 lds_barrier();
                 if (prep) dma_tile<4>(s.v, in.v, in.vstride, c + 1, e.seq_len, pw, voffs);
                 if (prep) inv8_l0(s, ln, pw);
+                // Q of chunk c + 1: every load this wave issued after it is
+                // this iteration's g or beta (if ahead) and V (q_pending
+                // implies prep)
+                if (q_pending) {
+                    if (ahead) dma_wait_but<NGB + NTILE>();
+                    else dma_wait_but<NTILE>();
+                }
                 lds_barrier();
                 const bool pout = !PRE && prep && c + 1 >= e.c_begin;  // chunk c + 1 produces output: P needed
                 if (prep && pw < 2) {
@@ -1297,6 +1347,8 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 lds_barrier();
                 if (!PRE && prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, abase, e.seq_len, c + 1, pw, ln);
                 if (prep) wfrag9(s, ln, 2, pw, 2 + pw, nb);  // rows 32..63
+                q_pending = !PRE && ahead && c + 2 >= e.c_begin;
+                if (q_pending) dma_tile<4>(s.q, in.q, in.kstride, c + 2, e.seq_len, pw, kqoffs);
             }
         };
         switch (wave - NSTATE) {

@@ -11,9 +11,9 @@ constexpr int kChunk = 64;     // chunk length C
 constexpr int kDimK = 128;     // key/query head dim K
 constexpr int kDimV = 128;     // value head dim V
 constexpr int kNumCUs = 256;   // MI355X compute units (occupancy model of the AUTO planner)
-constexpr int kDefaultWarmup = 8;
-// ln(2^-24): once the summed log-gates of a warm-up window fall below this, the
-// zero-start state differs from the true one by less than fp32 resolution.
+// ln(2^-24): once the summed log-gates of a warm-up window fall to this, the
+// zero-start state differs from the true one by less than fp32 resolution
+// (relative to the state at the window's far end).
 constexpr float kLnNoiseFloor = -16.635532333438686f;
 
 // One context-parallel segment of one sequence: chunks [c_begin, c_begin + c_count).
@@ -50,7 +50,7 @@ struct FwdParams {
     int32_t num_segments;
     int32_t L;                   // segment length in chunks
     int32_t cp_mode;             // resolved gdn_cp_mode
-    int32_t warmup_cap;
+    int32_t warmup_cap;          // WARMUP window cap in chunks; 0: none (gate-driven)
     int32_t o_f32;
     float scale;
     // exact context parallelism (workspace, each [num_segments][Hv][K][V] fp32):

@@ -65,17 +65,22 @@ typedef enum { GDN_DTYPE_BF16 = 0, GDN_DTYPE_F32 = 1 } gdn_dtype;
 /* Intra-GPU context parallelism over the chunk axis.
  *   OFF    one workgroup per (sequence, v-head) runs every chunk in order.
  *   WARMUP segments of L chunks; a segment not at its sequence start first
- *          runs the state pass (no output) from a zero state over up to
- *          cp_warmup_chunks preceding chunks, stopping early once the summed
- *          log-gates of the window fall below ln(2^-24) (the fp32 noise floor);
- *          a window that reaches the sequence start begins from
- *          initial_state and is then exact.  Approximate otherwise: the state
- *          error is at most exp(sum of window gates) times the state norm.
+ *          runs the state pass (no output) from a zero state over the chunks
+ *          before it, as many as it takes for the summed log-gates of the
+ *          window to reach ln(2^-24) (the fp32 noise floor), or back to the
+ *          sequence start, where the walk begins from initial_state and is
+ *          exact.  The state error a window leaves is at most exp(sum of its
+ *          log-gates) times the state norm at its far end (unit keys, beta in
+ *          [0, 2]), so it sits below fp32 resolution whatever the gates; weak
+ *          gates only make the windows (and the call) longer.  A positive
+ *          cp_warmup_chunks caps the window, and then that bound, not fp32
+ *          resolution, is the error guarantee.
  *   EXACT  segments of L chunks; a pre-pass computes each segment's
  *          zero-start state S and transition map M, a combine pass chains
  *          H <- M H + S across segments, and the main pass starts every
  *          segment from its exact state.
- *   AUTO   WARMUP with L chosen from the occupancy of the GPU. */
+ *   AUTO   WARMUP with L chosen from the occupancy of the GPU (OFF when one
+ *          segment per sequence fills it). */
 typedef enum { GDN_CP_OFF = 0, GDN_CP_EXACT = 1, GDN_CP_WARMUP = 2, GDN_CP_AUTO = 3 } gdn_cp_mode;
 
 typedef struct {
@@ -93,7 +98,7 @@ typedef struct {
     int32_t cp_mode;            /* gdn_cp_mode */
     float cp_lambda;            /* >0: segment length L = round(lambda * sqrt(chunks of the longest sequence)) */
     int32_t cp_segment_chunks;  /* >0: fixed L (overrides cp_lambda and AUTO) */
-    int32_t cp_warmup_chunks;   /* WARMUP/AUTO window cap; <=0 means 8 */
+    int32_t cp_warmup_chunks;   /* WARMUP/AUTO window cap in chunks; <= 0: no cap (gate-driven window) */
 } gdn_fwd_desc;
 
 typedef struct {
@@ -101,7 +106,7 @@ typedef struct {
     int32_t total_chunks;       /* sum over sequences of ceil(len / chunk) */
     int32_t segment_chunks;     /* L actually used (= longest sequence's chunk count when CP is off) */
     int32_t num_segments;       /* segments over all sequences (per v-head) */
-    int32_t warmup_chunks;      /* window cap used by WARMUP/AUTO, 0 otherwise */
+    int32_t warmup_chunks;      /* window cap used by WARMUP/AUTO; 0: none, or CP off */
     int32_t cp_mode;            /* resolved mode (AUTO becomes WARMUP or OFF) */
     int32_t workgroups;         /* main-kernel workgroups = num_segments * H_v */
 } gdn_fwd_plan_info;
@@ -219,7 +224,7 @@ typedef struct {
     int32_t total_chunks;
     int32_t segment_chunks;     /* L of the reverse pass */
     int32_t num_segments;       /* reverse-pass segments over all sequences (per v-head) */
-    int32_t warmup_chunks;      /* window cap of the reverse pass, 0 when CP is off */
+    int32_t warmup_chunks;      /* window cap of the reverse pass; 0: none, or CP off */
     int32_t cp_mode;            /* resolved mode of the reverse pass (OFF, EXACT or WARMUP) */
     int32_t workgroups_reverse; /* reverse-pass workgroups = num_segments * H_v * 2 */
     int32_t workgroups_local;   /* per-chunk workgroups = (total_chunks + empty sequences) * H_qk */

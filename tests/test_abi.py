@@ -81,7 +81,9 @@ def test_plan_for_workloads():
     assert p["cp"] == "off" and p["num_segments"] == 1 and p["segment_chunks"] == 512
     d = desc(T=32768, H_qk=2, H_v=8, cp="warmup", cp_segment_chunks=16)
     p = G.plan(d)
-    assert p["num_segments"] == 32 and p["warmup_chunks"] == 8
+    assert p["num_segments"] == 32 and p["warmup_chunks"] == 0  # no cap: the window is gate-driven
+    d = desc(T=32768, H_qk=2, H_v=8, cp="warmup", cp_segment_chunks=16, cp_warmup_chunks=6)
+    assert G.plan(d)["warmup_chunks"] == 6
     d = desc(T=32768, H_qk=2, H_v=8, cp="warmup", cp_lambda=1.0)
     assert G.plan(d)["segment_chunks"] == 23  # round(1.0 * sqrt(512))
 

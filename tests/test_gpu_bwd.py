@@ -176,14 +176,25 @@ def test_bwd_exact_context_parallelism(case):
     _check(f"exact/{case}", got, _oracle(x))
 
 
-def test_bwd_exact_under_weak_decay():
-    """Gates close to 1 (logsigmoid(N(6, 1)), ~ -0.0025 per token): an 8-chunk
-    warm-up window keeps ~e^-1.3 of the truncated gradient, so only the exact
-    mode can meet the bar; the warm-up error is printed for reference."""
+@pytest.mark.parametrize("cp", ["exact", "warmup", "auto"])
+def test_bwd_under_weak_decay(cp):
+    """Gates close to 1 (logsigmoid(N(6, 1)), about -0.004 a token) and one
+    v-head without decay (g = 0): the reverse pass's warm-up window runs until
+    its summed log-gates reach the fp32 noise floor or the sequence end
+    (agentlenshq.com blog, AutoCP), so every mode holds the gradient bar.  A
+    window capped at 8 chunks would keep about e^-2 of the truncated gradient
+    here; that case is the explicit cap's trade, checked separately."""
     x = _grad_inputs(dataclasses.replace(BASE, name="e4", seed=54, B=1, T=1024, H_qk=1, H_v=2, g_mu=6.0))
+    x["g"][:, :, 1] = 0.0
     ref = _oracle(x)
-    got = _run(x, cp="exact", cp_segment_chunks=2, grad_dtype="f32")
-    _check("weak-decay/exact", got, ref)
-    approx = _run(x, cp="warmup", cp_segment_chunks=2, grad_dtype="f32")
-    print("[weak-decay/warmup] " + " ".join(f"{n}={rel_l2(a.float().cpu().numpy(), b):.2e}"
-                                            for n, a, b in zip(NAMES, approx, ref)), flush=True)
+    got = _run(x, cp=cp, cp_segment_chunks=2, grad_dtype="f32")
+    _check(f"weak-decay/{cp}", got, ref)
+
+
+def test_bwd_capped_window_is_an_explicit_approximation():
+    x = _grad_inputs(dataclasses.replace(BASE, name="e5", seed=55, B=1, T=1024, H_qk=1, H_v=2, g_mu=6.0))
+    ref = _oracle(x)
+    approx = _run(x, cp="warmup", cp_segment_chunks=2, cp_warmup_chunks=2, grad_dtype="f32")
+    errs = [rel_l2(a.float().cpu().numpy(), b) for a, b in zip(approx, ref)]
+    print("[weak-decay/cap 2] " + " ".join(f"{n}={e:.2e}" for n, e in zip(NAMES, errs)), flush=True)
+    assert max(errs) > BAR
