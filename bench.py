@@ -5,16 +5,23 @@ One step = one gdn_fwd call (the whole forward: every chunk of every v-head,
 o and final_state) over the 1 x 32768-token, 16 qk / 16 v-head workload, with
 inputs resident in HBM.  Prints ONE JSON line on stdout:
 
-  value        tokens per second over the timed steps (higher is better)
-  ms_per_step  mean latency of one forward
+  value        tokens per second: tokens per step over ms_per_step
+  ms_per_step  mean duration of one forward (HIP events on the launch stream
+               around each call); before every timed call the bench writes a
+               1 GiB buffer (four times the 256 MB Infinity Cache), so each
+               call reads its inputs from HBM, as a call inside a model would
   roofline     the forward kernel's algorithmic HBM bytes per launch over its
-               mean launch duration (HIP events on the launch stream), against
-               the 8 TB/s HBM peak; `traffic` = measured HBM bytes per launch
-               from rocprofv3 FETCH_SIZE + WRITE_SIZE (scaled by a copy-kernel
-               calibration) when the stored counters match the current kernel
-               source, else null
+               mean launch duration, against the 8 TB/s HBM peak; `traffic` =
+               measured HBM bytes per launch from rocprofv3 FETCH_SIZE +
+               WRITE_SIZE (scaled by a copy-kernel calibration) when the stored
+               counters match the current kernel source, else null
+  mfma         the forward's algorithmic MFMA flops over the same duration,
+               against the published 2.5 PFLOP/s bf16 peak and against the
+               rate a probe kernel of the same MFMA instruction sustains on this GPU
   cpu_baseline the fp64 oracle on a bounded prefix of the same workload, timed
                on this host's cores
+Before the warm-up steps the bench writes the flush buffer for about 0.3 s,
+which brings the GPU's clocks out of idle (untimed).
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload NAME]
        [--cp auto|warmup|off] [--no-cpu-baseline] [--cpu-seconds 10]
@@ -34,6 +41,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 1 << 30
+SETTLE_S = 0.3
 # Pages' FlashQLA forward latency for this exact workload (1 x 32768, h_qk=16, h_v=16)
 # on an NVIDIA H200 (agentlenshq.com FlashQLA blog, benchmark table): context only.
 PAGES_MS = {"gdn_fwd_1x32768_h16x16": 0.493, "gdn_fwd_1x32768_h2x8": 0.310}
@@ -128,6 +137,115 @@ def ingest_counters(workload: str, fetch_csv: str, write_csv: str, copy_fetch_cs
     print(json.dumps(d[workload]))
 
 
+class Flusher:
+    """A 1 GiB device buffer, rewritten before every timed call so that no input
+    of the call is still in the 256 MB Infinity Cache (or the L2)."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(float(self.n & 7))
+
+    def settle(self, seconds: float = SETTLE_S):
+        """Keep the GPU busy writing the buffer for `seconds` (untimed): the
+        clocks leave their idle state before the warm-up steps."""
+        import torch
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                self()
+            torch.cuda.synchronize()
+
+
+def time_steps(fns, steps: int, flush, stream):
+    """Run `steps` steps; each step flushes the caches, then runs the callables
+    in `fns` in order, each bracketed by HIP events on `stream`.  Returns the
+    per-step durations of each callable (ms) and the wall time of the whole
+    timed region (flushes included), bracketed by device synchronisation."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        flush()
+        e[0].record(stream)
+        for i, fn in enumerate(fns):
+            fn()
+            e[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [[e[i].elapsed_time(e[i + 1]) for e in ev] for i in range(len(fns))]
+    return per, wall
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PROBE_LIB = os.path.join(ROOT, "gated_deltanet_chunked_chunk_amd", "libgdn_probe.so")
+
+
+def measured_mfma_peak(dev) -> float:
+    """bf16 MFMA rate (TFLOP/s) the probe kernel sustains: v_mfma_f32_16x16x32_bf16
+    in eight independent chains per wave, four waves per block, 1024 blocks;
+    the best of ten launches after three untimed ones."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.probe_mfma_bf16.restype = ctypes.c_int
+    lib.probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.probe_mfma_bf16_flops.restype = ctypes.c_double
+    lib.probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    blocks, iters = 1024, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    best = 0.0
+    for i in range(13):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rc = lib.probe_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, iters, ctypes.c_void_p(stream.cuda_stream))
+        b.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"MFMA probe launch failed ({rc})")
+        torch.cuda.synchronize()
+        if i >= 3:
+            best = max(best, lib.probe_mfma_bf16_flops(blocks, iters) / (a.elapsed_time(b) * 1e-3) / 1e12)
+    return best
+
+
+def measured_gemm_rate(dev) -> float:
+    """bf16 rate (TFLOP/s) of a large library GEMM (torch.matmul, 8192^3, on
+    hipBLASLt): what a plain dense product reaches on this GPU; the best of five
+    calls after two untimed ones."""
+    import torch
+    n = 8192
+    gen = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(n, n, device=dev, generator=gen).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev, generator=gen).to(torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+    best = 0.0
+    for i in range(7):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        c = torch.matmul(a, b)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            best = max(best, 2.0 * n ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    del a, b, c
+    return best
+
+
+def fwd_flops(x) -> int:
+    """Algorithmic MFMA flops of the forward: 2 (3 C K + 2 C V + 3 K V) per token
+    and v-head (K K^T, W, Q K^T; U, P v'; W h, K^T v', Q h at chunk C = 64)."""
+    v, q = x["v"], x["q"]
+    K, V, C = q.shape[-1], v.shape[-1], 64
+    tokens = v.shape[0] * v.shape[1]
+    return int(2 * (3 * C * K + 2 * C * V + 3 * K * V) * tokens * v.shape[2])
+
+
 def cpu_baseline(x, w, target_s: float):
     import numpy as np  # noqa: F401
     import oracle
@@ -168,6 +286,8 @@ def sweep(steps: int, warmup: int, cp: str):
     from gated_deltanet_chunked_chunk_amd import workloads as W
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    flush = Flusher(dev)
+    flush.settle()
     rows = []
     for (hqk, hv), model in SWEEP_HEADS:
         for B, T in SWEEP_SHAPES:
@@ -175,16 +295,11 @@ def sweep(steps: int, warmup: int, cp: str):
             call = PreparedForward(x["q"], x["k"], x["v"], x["g"], x["beta"], scale=x["scale"],
                                    initial_state=x["initial_state"], output_final_state=True, cp=cp)
             for _ in range(warmup):
+                flush()
                 call()
             stream = torch.cuda.current_stream(dev)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a.record(stream)
-            for _ in range(steps):
-                call()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b) / steps
+            (per,), _ = time_steps([call], steps, flush, stream)
+            ms = sum(per) / len(per)
             alg = algorithmic_bytes(x)
             frac = alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
             ref = PAGES_H200_MS.get((hqk, hv)) if (B, T) == (1, 32768) else None
@@ -203,9 +318,6 @@ def sweep(steps: int, warmup: int, cp: str):
         print(f"| {r['model']} | {r['H_qk']} | {r['H_v']} | {r['B']} x {r['T']} | {r['cp']} ({r['segment_chunks']}, "
               f"{r['workgroups']}) | {r['ms']:.3f} | {r['tokens_per_s'] / 1e6:.1f} | {r['hbm_roofline_frac']:.3f} | "
               f"{r['pages_h200_ms'] if r['pages_h200_ms'] else ''} |", file=sys.stderr)
-
-
-MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def cpu_baseline_bwd(x, w, target_s: float):
@@ -246,6 +358,8 @@ def sweep_bwd(steps: int, warmup: int, cp: str):
     from gated_deltanet_chunked_chunk_amd import workloads as W
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    flush = Flusher(dev)
+    flush.settle()
     rows = []
     for (hqk, hv), model in SWEEP_HEADS:
         for B, T in SWEEP_BWD_TOKENS:
@@ -258,19 +372,12 @@ def sweep_bwd(steps: int, warmup: int, cp: str):
             call = PreparedForwardBackward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["dO"], scale=x["scale"],
                                            initial_state=x["initial_state"], d_final_state=x["dht"], cp=cp)
             for _ in range(warmup):
+                flush()
                 call()
             stream = torch.cuda.current_stream(dev)
-            ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
-            torch.cuda.synchronize()
-            for a, b, c in ev:
-                a.record(stream)
-                call.forward()
-                b.record(stream)
-                call.backward()
-                c.record(stream)
-            torch.cuda.synchronize()
-            fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / steps
-            bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / steps
+            (pf, pb), _ = time_steps([call.forward, call.backward], steps, flush, stream)
+            fwd_ms = sum(pf) / steps
+            bwd_ms = sum(pb) / steps
             _, flops = bwd_algorithmic(x)
             frac = flops / (bwd_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
             line = {"model": model, "H_qk": hqk, "H_v": hv, "B": B, "T": T, "total_tokens": B * T,
@@ -298,24 +405,17 @@ def fwd_bwd(args, w, x, dev):
     call = PreparedForwardBackward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["dO"], scale=x["scale"],
                                    initial_state=x["initial_state"], d_final_state=x["dht"], cp=args.cp)
     tokens = w.B * w.T
+    flush = Flusher(dev)
+    flush.settle()
     for _ in range(args.warmup):
+        flush()
         call()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b, c in ev:
-        a.record(stream)
-        call.forward()
-        b.record(stream)
-        call.backward()
-        c.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / len(ev)
-    bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / len(ev)
-    ms_per_step = wall * 1e3 / args.steps
+    (pf, pb), wall = time_steps([call.forward, call.backward], args.steps, flush, stream)
+    fwd_ms = sum(pf) / len(pf)
+    bwd_ms = sum(pb) / len(pb)
+    ms_per_step = fwd_ms + bwd_ms
     value = tokens / (ms_per_step * 1e-3)
     bwd_bytes, bwd_flops = bwd_algorithmic(x)
     achieved = bwd_flops / (bwd_ms * 1e-3) / 1e12
@@ -329,6 +429,7 @@ def fwd_bwd(args, w, x, dev):
         "metric": "GDN fwd+bwd latency (ms) & tokens/s at 1x32768, 4/16 heads; % of MFMA roofline (backward)",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "wall_ms_per_step_with_flush": round(wall * 1e3 / args.steps, 4),
         "dtype": "bf16", "data": "synthetic (seeded random q,k,v,g,beta,initial_state,dO,d_final_state)",
         "config": {"workload": args.workload, "B": w.B, "T": w.T, "H_qk": w.H_qk, "H_v": w.H_v, "K": w.K,
                    "V": w.V, "cp": call.finfo["cp"], "bwd_cp": call.binfo["cp"],
@@ -402,23 +503,17 @@ def main():
     info = call.info
     tokens = w.B * w.T if x["cu_seqlens"] is None else int(x["cu_seqlens"][-1])
 
+    flush = Flusher(dev)
+    flush.settle()
     for _ in range(args.warmup):
+        flush()
         call()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
-        call()
-        b.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    (per_launch_ms,), wall = time_steps([call], args.steps, flush, stream)
     kern_ms = sum(per_launch_ms) / len(per_launch_ms)
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = kern_ms
     value = tokens / (ms_per_step * 1e-3)
 
     alg = algorithmic_bytes(x)
@@ -427,22 +522,31 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.workload),
                 "kernel": "gdn_fwd_main_kernel", "algorithmic_bytes_per_launch": alg,
                 "mean_launch_ms": round(kern_ms, 4)}
+    flops = fwd_flops(x)
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    peak_meas = measured_mfma_peak(dev)
+    gemm = measured_gemm_rate(dev)
+    mfma = {"achieved": round(tflops, 1), "unit": "TFLOP/s", "algorithmic_flops_per_launch": flops,
+            "peak_published": MFMA_BF16_PEAK_TFLOPS, "frac_published": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "peak_measured": round(peak_meas, 1), "frac_measured": round(tflops / peak_meas, 4) if peak_meas else None,
+            "library_gemm_8192": round(gemm, 1)}
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(x, w, args.cpu_seconds)
 
-    pages = PAGES_MS.get(args.workload)
     line = {
         "metric": "GDN fwd latency (ms) & tokens/s at 1x32768; % of HBM/MFMA roofline",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": round(value / (tokens / (pages * 1e-3)), 3) if pages else None,
+        "vs_baseline": None, "wall_ms_per_step_with_flush": round(wall * 1e3 / args.steps, 4),
+        "pages_h200_ms_context": PAGES_MS.get(args.workload),
         "dtype": "bf16", "data": "synthetic (seeded random q,k,v,g,beta,initial_state of the workload's shapes)",
         "config": {"workload": args.workload, "B": w.B, "T": w.T, "H_qk": w.H_qk, "H_v": w.H_v, "K": w.K,
                    "V": w.V, "cp": info["cp"], "segment_chunks": info["segment_chunks"],
                    "workgroups": info["workgroups"], "o_dtype": args.o_dtype},
         "roofline": roofline,
+        "mfma": mfma,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -27,6 +27,18 @@ def _cu_host(cu_seqlens) -> Optional[torch.Tensor]:
     return torch.as_tensor(list(cu_seqlens), dtype=torch.int32)
 
 
+def _check_offsets(cu_host: torch.Tensor, B: int, T: int) -> None:
+    """The packed-sequence contract: B == 1, at least one sequence, offsets
+    starting at 0, non-decreasing, ending at T."""
+    if B != 1:
+        raise ValueError(f"cu_seqlens requires B == 1 (got {B})")
+    if cu_host.dim() != 1 or cu_host.numel() < 2:
+        raise ValueError("cu_seqlens needs at least two offsets (one sequence)")
+    c = cu_host.tolist()
+    if c[0] != 0 or c[-1] != T or any(b < a for a, b in zip(c, c[1:])):
+        raise ValueError(f"cu_seqlens must start at 0, be non-decreasing and end at T={T} (got {c[:4]}...{c[-2:]})")
+
+
 def make_desc(B, T, H_qk, H_v, K, V, *, scale, cu_host=None, has_h0=False, want_ht=False, o_dtype="bf16",
               cp="auto", cp_lambda=0.0, cp_segment_chunks=0, cp_warmup_chunks=0, chunk=64) -> L.FwdDesc:
     d = L.FwdDesc()
@@ -349,8 +361,10 @@ def chunk_cumsum(g: torch.Tensor, chunk: int = 64, cu_seqlens=None, out: Optiona
     B, T, H = g.shape
     cu_dev, N = None, B
     if cu_seqlens is not None:
-        cu_dev = torch.as_tensor(cu_seqlens, dtype=torch.int32).to(dev).contiguous()
-        N = cu_dev.numel() - 1
+        cu_host = _cu_host(cu_seqlens)  # a device tensor is copied to the host once (a sync)
+        _check_offsets(cu_host, B, T)
+        cu_dev = cu_host.to(dev)
+        N = cu_host.numel() - 1
     if out is None:
         out = torch.empty_like(g)
     stream = torch.cuda.current_stream(dev).cuda_stream

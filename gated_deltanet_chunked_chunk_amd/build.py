@@ -15,6 +15,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
 SOURCES = [os.path.join(CSRC, "gdn_api.hip"), os.path.join(CSRC, "gdn_fwd.hip"), os.path.join(CSRC, "gdn_bwd.hip")]
+# measurement probe for the benchmark (the sustained bf16 MFMA rate), kept out of libgdn
+PROBE_LIB = os.path.join(PKG, "libgdn_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "probe_mfma.hip")]
 HEADERS = [os.path.join(ROOT, "include", "gdn.h"), os.path.join(CSRC, "gdn_internal.h"), os.path.join(CSRC, "gdn_window.h")]
 
 HIPCC_FLAGS = [
@@ -53,20 +56,26 @@ def _run(cmd, verbose: bool) -> None:
         print(out, file=sys.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompiles (one object per source, with its own options, then one
-    shared library); writes to a temp name and renames (atomic)."""
+def _link(sources, lib, verbose: bool) -> str:
     with tempfile.TemporaryDirectory() as td:
         objs = []
-        for src in SOURCES:
+        for src in sources:
             obj = os.path.join(td, os.path.basename(src) + ".o")
             _run([hipcc()] + HIPCC_FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) +
                  ["-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj], verbose)
             objs.append(obj)
-        tmp = LIB + ".tmp"
+        tmp = lib + ".tmp"
         _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles (one object per source, with its own options, then one
+    shared library; the benchmark's probe library likewise); writes to temp
+    names and renames (atomic)."""
+    _link(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _link(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -658,6 +658,7 @@ int gdn_chunk_cumsum(const float *g, float *out, int64_t B, int64_t T, int32_t H
                                               (long long)T, H);
     if (chunk <= 0) return fail(GDN_EINVAL, "chunk must be > 0");
     if (cu_seqlens && B != 1) return fail(GDN_EINVAL, "cu_seqlens requires B == 1");
+    if (cu_seqlens && num_seqs < 1) return fail(GDN_EINVAL, "cu_seqlens needs num_seqs >= 1 (got %d)", num_seqs);
     if (!cu_seqlens && num_seqs != B) return fail(GDN_EINVAL, "num_seqs must equal B without cu_seqlens");
     if (B * T > 0 && (!g || !out)) return fail(GDN_EINVAL, "g and out must be non-NULL");
     const size_t bytes = (size_t)(B * T * H) * 4;

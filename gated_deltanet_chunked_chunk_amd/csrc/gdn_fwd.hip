@@ -1537,11 +1537,14 @@ __global__ void __launch_bounds__(NT_COMB, 1) gdn_cp_combine_kernel(FwdParams p)
 // ---------------------------------------------------------------- chunk cumsum
 // One thread per (row, head); the thread whose row starts a chunk scans that
 // chunk in order, reading each g before writing its sum, so out may equal g.
+// Offsets are the caller's device data: every range taken from them is
+// clamped to the B * T rows of the buffers, so offsets that break the
+// contract (past T, decreasing) give wrong sums, never an access outside g or out.
 __global__ void __launch_bounds__(256) gdn_chunk_cumsum_kernel(const float *g, float *out, int64_t B, int64_t T,
                                                                int32_t H, int32_t chunk, const int32_t *cu,
                                                                int32_t N) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = B * T * H;
+    const int64_t total = B * T * H, total_rows = B * T;
     if (idx >= total) return;
     const int64_t row = idx / H;
     const int hh = (int)(idx % H);
@@ -1553,14 +1556,14 @@ __global__ void __launch_bounds__(256) gdn_chunk_cumsum_kernel(const float *g, f
             if (cu[mid] <= row) lo = mid; else hi = mid;
         }
         while (lo + 1 < N && cu[lo + 1] <= row) ++lo;  // skip empty sequences
-        seq0 = cu[lo];
-        seq1 = cu[lo + 1];
+        seq0 = min(max((int64_t)cu[lo], (int64_t)0), row);
+        seq1 = min((int64_t)cu[lo + 1], total_rows);
     } else {
         seq0 = (row / T) * T;
         seq1 = seq0 + T;
     }
     if ((row - seq0) % chunk != 0) return;
-    const int64_t end = row + chunk < seq1 ? row + chunk : seq1;
+    const int64_t end = min(row + chunk < seq1 ? row + chunk : seq1, total_rows);
     float acc = 0.f;
     for (int64_t r = row; r < end; ++r) {
         acc += g[r * H + hh];

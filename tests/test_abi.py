@@ -243,3 +243,21 @@ def test_bwd_validation_happens_before_any_launch():
     assert b"dv overlaps v" in lib.gdn_last_error()
     # workspace too small
     assert lib.gdn_bwd(ctypes.byref(d), ctypes.byref(mk()), ws, 1 << 12, None) == L.GDN_EWORKSPACE
+
+
+def test_chunk_cumsum_rejects_bad_offsets_on_the_host():
+    """gdn_chunk_cumsum: offsets without a sequence are rejected before any
+    launch; the Python wrapper validates a host copy of the offsets (the
+    forward's contract) before handing them to the kernel."""
+    lib = L.lib()
+    base = 0x100000
+    assert lib.gdn_chunk_cumsum(ctypes.c_void_p(base), ctypes.c_void_p(2 * base), 1, 10, 2, 64,
+                                ctypes.c_void_p(3 * base), 0, None) == L.GDN_EINVAL
+    assert b"num_seqs" in lib.gdn_last_error()
+    assert lib.gdn_chunk_cumsum(ctypes.c_void_p(base), ctypes.c_void_p(2 * base), 2, 10, 2, 64,
+                                ctypes.c_void_p(3 * base), 1, None) == L.GDN_EINVAL
+    from gated_deltanet_chunked_chunk_amd import api
+    for cu, B, T in (([0, 5, 12], 1, 10), ([1, 10], 1, 10), ([0, 6, 4, 10], 1, 10), ([0], 1, 0), ([0, 10], 2, 10)):
+        with pytest.raises(ValueError):
+            api._check_offsets(torch.tensor(cu, dtype=torch.int32), B, T)
+    api._check_offsets(torch.tensor([0, 0, 4, 10], dtype=torch.int32), 1, 10)
