@@ -203,14 +203,16 @@ static_assert(DK == DV, "K, Q and V tiles share one layout");
 struct __attribute__((aligned(16))) Smem8 {
     bf16 k[2][TILE];                  // K by chunk parity (row = token, padded rows)
     bf16 q[TILE];                     // Q of the chunk being prepared
-    bf16 v[TILE];                     // V of the state pass's next chunk
+    bf16 v[TILE];                     // V of the chunk being prepared
     float a[CH * AS];                 // A, inverted in place into T
-    bf16x8 wf[2][4][4][64];           // -W as hi / lo A fragments [hi, lo][row tile][k step][lane]
-    bf16x8 tf[2][6][64];              // T diag(beta) as A fragments [hi, lo][fragment][lane]
-    bf16x8 pf[2][6][64];              // scale P as A fragments [hi, lo][fragment][lane]
+    bf16x8 tdf[2][6][64];             // diag(dec) T diag(beta) as A fragments [hi, lo][fragment][lane]
+    bf16x8 zf[2][6][64];              // (scale P T diag(beta))^T as B fragments [hi, lo][fragment][lane]
+    bf16x8 tf[2][6][64];              // T diag(beta) as A fragments (only when v' is stored)
+    bf16x8 pf[2][6][64];              // (scale P)^T as B fragments [hi, lo][fragment][lane]
     // the two 32 x 32 diagonal blocks of A, then of T, transposed ([block][col][row])
     float tt[2][32 * TS8];
     float tlo[32 * TS8];              // rows 32..63, columns 0..31 of T (inverse level 2)
+    float tlot[32 * TS8];             // the same block transposed ([col][row - 32])
     float gam[2][CH], dec[2][CH];     // e^{G}, e^{G_last - G} (two chunks in flight)
     float graw[2][CH], braw[2][CH];   // g and beta as loaded, by chunk parity
     float gcum[CH], bg[CH];
@@ -340,6 +342,22 @@ __device__ __forceinline__ void dma_wait_but() {
     static_assert(N >= 0 && N < 16, "vmcnt field");
     __builtin_amdgcn_s_waitcnt(0x0f70 | N);
 }
+
+// The same for a wave-uniform run-time N (0..15; larger waits for everything).
+__device__ __forceinline__ void dma_wait_upto(const int n) {
+    switch (n) {
+#define GDN_WAIT_CASE(N) \
+    case N: dma_wait_but<N>(); break;
+        GDN_WAIT_CASE(1) GDN_WAIT_CASE(2) GDN_WAIT_CASE(3) GDN_WAIT_CASE(4) GDN_WAIT_CASE(5)
+        GDN_WAIT_CASE(6) GDN_WAIT_CASE(7) GDN_WAIT_CASE(8) GDN_WAIT_CASE(9) GDN_WAIT_CASE(10)
+        GDN_WAIT_CASE(11) GDN_WAIT_CASE(12) GDN_WAIT_CASE(13) GDN_WAIT_CASE(14) GDN_WAIT_CASE(15)
+#undef GDN_WAIT_CASE
+    default: dma_wait(); break;
+    }
+}
+
+// Wave loads of one tile issued by preparation wave pw (loads pw, pw + 4, ... of 17).
+__host__ __device__ constexpr int NTILE4(int pw) { return (TLOADS - pw + 3) / 4; }
 
 // Workgroup barrier for LDS traffic: this wave's own LDS reads and writes are
 // complete (lgkmcnt(0)) when it arrives, but its direct HBM -> LDS loads may
@@ -643,6 +661,7 @@ __device__ __forceinline__ void inv8_l2b(Smem8 &s, const int lane, const int pw,
     z = mfma16(r2.tl, yh, z);
 #pragma unroll
     for (int j = 0; j < 4; ++j) s.tlo[(16 * r + 4 * g + j) * TS8 + 16 * cq + m] = -z[j];
+    *reinterpret_cast<f32x4 *>(&s.tlot[(16 * cq + m) * TS8 + 16 * r + 4 * g]) = f32x4{-z[0], -z[1], -z[2], -z[3]};
 }
 
 // Four consecutive entries T[row][c0 .. c0 + 3] (c0 a multiple of 4): the
@@ -652,224 +671,116 @@ __device__ __forceinline__ f32x4 trow4(const Smem8 &s, const int row, const int 
     return *reinterpret_cast<const f32x4 *>(p);
 }
 
-// ---- preparation: for the row tiles rt0 and rt0 + 1, the -W hi / lo A
-// fragments of key-dim step kk (W^T = K^T (T diag(beta gamma))^T, two 16-row
-// halves), and the T diag(beta) hi/lo A fragment tf_frag of those rows for U
-// (-1: none).  K^T comes from transposing reads of K, so T is read at the
-// transposed-read token order.  Rows 0..31 of T are final after inverse level
-// 1, rows 32..63 after level 2.  T diag(beta gamma) enters as hi + lo bf16 and
-// W leaves as hi + lo: W H is the term v' = U - W H nearly cancels when the
-// state already predicts v well (gates near 1), so W's own rounding would
-// reach v', and through it the state, amplified.
-__device__ __forceinline__ void wfrag9(Smem8 &s, const int lane, const int rt0, const int kk, const int tf_frag,
-                                       const int buf) {
+// ---- preparation: fragment f of the chunk's WY matrix as MFMA A fragments
+// (rows i = 16 rt + l % 16, k = tokens s of token step ks in the
+// transposed-read order), hi / lo:
+//   s.tdf  diag(dec) T diag(beta)   (the decayed v' of the state update)
+//   s.tf   T diag(beta)             (v' itself, only when v' is stored)
+// Rows 0..31 of T are final after inverse level 1, rows 32..63 after level 2.
+__device__ __forceinline__ void tdfrag(Smem8 &s, const int lane, const int f, const int buf, const bool with_tf) {
     const int m = lane & 15, g = lane >> 4;
-    const int nks = (rt0 < 2) ? 1 : 2;  // T is lower triangular
-    const bf16 *K = s.k[buf];
-    bf16x8 ka[2][2];  // [token step][key-dim half]
+    const int rt = frag_rt(f), ks = frag_ks(f);
+    const int c0 = 32 * ks + 4 * g, row = 16 * rt + m;
+    const f32x4 t0 = trow4(s, row, c0), t1 = trow4(s, row, c0 + 16);
+    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&s.braw[buf][c0]);
+    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&s.braw[buf][c0 + 16]);
+    const float d = s.dec[buf][row];
+    float tb[8], td[8];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        if (ks >= nks) continue;
-        ka[ks][0] = frag_t(K, 32 * kk, 32 * ks, lane);
-        ka[ks][1] = frag_t(K, 32 * kk + 16, 32 * ks, lane);
+    for (int e = 0; e < 4; ++e) {
+        tb[e] = t0[e] * b0[e];
+        tb[4 + e] = t1[e] * b1[e];
     }
-    bf16x8 twh[2][2], twl[2][2];  // [row tile][token step]
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ks >= nks) continue;
-            const int c0 = 32 * ks + 4 * g, row = 16 * (rt0 + r) + m;
-            const f32x4 t0 = trow4(s, row, c0), t1 = trow4(s, row, c0 + 16);
-            const f32x4 bg0 = *reinterpret_cast<const f32x4 *>(&s.bg[c0]);
-            const f32x4 bg1 = *reinterpret_cast<const f32x4 *>(&s.bg[c0 + 16]);
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x[e] = t0[e] * bg0[e];
-                x[4 + e] = t1[e] * bg1[e];
-            }
-            split8v(x, twh[r][ks], twl[r][ks]);
-        }
-    if (tf_frag >= 0) {
-        const int rt = frag_rt(tf_frag), ks = frag_ks(tf_frag);
-        const int c0 = 32 * ks + 4 * g, row = 16 * rt + m;
-        const f32x4 t0 = trow4(s, row, c0), t1 = trow4(s, row, c0 + 16);
-        const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&s.braw[buf][c0]);
-        const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&s.braw[buf][c0 + 16]);
-        float tb[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            tb[e] = t0[e] * b0[e];
-            tb[4 + e] = t1[e] * b1[e];
-        }
-        bf16x8 hi, lo;
+    for (int e = 0; e < 8; ++e) td[e] = d * tb[e];
+    bf16x8 hi, lo;
+    split8v(td, hi, lo);
+    s.tdf[0][f][lane] = hi;
+    s.tdf[1][f][lane] = lo;
+    if (with_tf) {
         split8v(tb, hi, lo);
-        s.tf[0][tf_frag][lane] = hi;
-        s.tf[1][tf_frag][lane] = lo;
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        f32x4 w0 = {}, w1 = {};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ks >= nks) continue;
-            w0 = mfma16(ka[ks][0], twh[r][ks], w0);
-            w0 = mfma16(ka[ks][0], twl[r][ks], w0);
-            w1 = mfma16(ka[ks][1], twh[r][ks], w1);
-            w1 = mfma16(ka[ks][1], twl[r][ks], w1);
-        }
-        const float nw[8] = {-w0[0], -w0[1], -w0[2], -w0[3], -w1[0], -w1[1], -w1[2], -w1[3]};
-        bf16x8 hi, lo;
-        split8v(nw, hi, lo);
-        s.wf[0][rt0 + r][kk][lane] = hi;
-        s.wf[1][rt0 + r][kk][lane] = lo;
+        s.tf[0][f][lane] = hi;
+        s.tf[1][f][lane] = lo;
     }
 }
 
-// ---- U = (T diag(beta)) V for state wave sw's 32 value columns (two column
-// tiles), from the prepared hi/lo fragments and transposing reads of V.
-__device__ __forceinline__ void u9(const Smem8 &s, const int lane, const int sw, f32x4 (&u)[4][2]) {
-    bf16x8 vv[2][2], th[6], tl[6];
+// ---- preparation: Z^T = (scale P T diag(beta))^T as the hi / lo B fragment f
+// of the output product O^T = ... + Y^T Z^T (k = tokens s of token step ks in
+// the transposed-read order, columns = query rows i of tile rt).  P v' = P T
+// diag(beta) Y, so the output takes the same Y as the state update instead of
+// v'.  Each of the fragment's two 16-token tiles st is the MFMA product of
+// (T diag(beta))^T (rows s, k = s') and the (scale P)^T fragments (k = s',
+// columns i) over the token steps s' between s and i (both factors are
+// triangular), hi / lo on both sides.  The columns of T come from its
+// transposed blocks (s.tt diagonal blocks, s.tlot lower-left block).
+__device__ __forceinline__ void zfrag(Smem8 &s, const int lane, const int f, const int buf) {
+    const int m = lane & 15, g = lane >> 4;
+    const int rt = frag_rt(f), ks = frag_ks(f);
+    f32x4 acc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int h = 0; h < 2; ++h) {
+        const int st = 2 * ks + h;  // token tile of the rows s
+        if (st > rt) continue;      // above the diagonal: zero
+        const int sr = 16 * st + m;
+        const float bs = s.braw[buf][sr];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) vv[ct][ks] = frag_t(s.v, 32 * sw + 16 * ct, 32 * ks, lane);
-#pragma unroll
-    for (int f = 0; f < 6; ++f) {
-        th[f] = s.tf[0][f][lane];
-        tl[f] = s.tf[1][f][lane];
+        for (int kq = 0; kq < 2; ++kq) {
+            if (kq < ks || kq > (rt >> 1)) continue;
+            const float *src = (kq == 0) ? &s.tt[0][sr * TS8]
+                               : (st >= 2) ? &s.tt[1][(sr - 32) * TS8]
+                                           : &s.tlot[sr * TS8];
+            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(src + 4 * g);
+            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(src + 16 + 4 * g);
+            const float av[8] = {x0[0] * bs, x0[1] * bs, x0[2] * bs, x0[3] * bs,
+                                 x1[0] * bs, x1[1] * bs, x1[2] * bs, x1[3] * bs};
+            bf16x8 ah, al;
+            split8v(av, ah, al);
+            const int pfr = frag_of(rt, kq);
+            const bf16x8 ph = s.pf[0][pfr][lane], pl = s.pf[1][pfr][lane];
+            acc[h] = mfma16(ah, ph, acc[h]);
+            acc[h] = mfma16(ah, pl, acc[h]);
+            acc[h] = mfma16(al, ph, acc[h]);
+        }
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+    bf16x8 hi, lo;
+    split_pair(acc[0], acc[1], hi, lo);
+    s.zf[0][f][lane] = hi;
+    s.zf[1][f][lane] = lo;
+}
+
+// ---- state-wave pieces, two column tiles each.  Y = V - diag(gamma) K H of
+// a chunk (tokens x this wave's 32 value columns) is held as hi / lo bf16
+// pairs [token step ks][column tile ct]: a pair is the B operand of a product
+// over tokens (k = tokens in the transposed-read order, columns = value
+// columns) and, as the same registers, the A operand of the transposed one
+// (rows = value columns, k = tokens).
+struct YSplit {
+    bf16x8 h[2][2], l[2][2];
+};
+
+__device__ __forceinline__ void zero_tiles(f32x4 (&t)[4][2]) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) u[rt][ct] = f32x4{};
-#pragma unroll
-    for (int f = 0; f < 6; ++f) {
-        const int rt = frag_rt(f), ks = frag_ks(f);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            u[rt][ct] = mfma16(th[f], vv[ct][ks], u[rt][ct]);
-            u[rt][ct] = mfma16(tl[f], vv[ct][ks], u[rt][ct]);
-        }
-    }
+        for (int ct = 0; ct < 2; ++ct) t[rt][ct] = f32x4{};
 }
 
-// The same with the T diag(beta) fragments read one at a time.
-__device__ __forceinline__ void u9_lean(const Smem8 &s, const int lane, const int sw, f32x4 (&u)[4][2]) {
-    bf16x8 vv[2][2];
+// X = K H for the chunk in buffers nb (token rows x this wave's value
+// columns), from one hi / lo split of the state per k step; the K fragments of
+// the next k step are read while the current one's products run.
+__device__ __forceinline__ void xk(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&X)[4][2], const int nb,
+                                   const int ln) {
+    const bf16 *K = s.k[nb];
+    zero_tiles(X);
+    bf16x8 ka[2][4];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) vv[ct][ks] = frag_t(s.v, 32 * sw + 16 * ct, 32 * ks, lane);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) u[rt][ct] = f32x4{};
-#pragma unroll
-    for (int f = 0; f < 6; ++f) {
-        const int rt = frag_rt(f), ks = frag_ks(f);
-        const bf16x8 th = s.tf[0][f][lane], tl = s.tf[1][f][lane];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            u[rt][ct] = mfma16(th, vv[ct][ks], u[rt][ct]);
-            u[rt][ct] = mfma16(tl, vv[ct][ks], u[rt][ct]);
-        }
-    }
-}
-
-// ---- state-wave pieces of the state pass (two column tiles each).  Every
-// piece issues all of its LDS operand reads in one batch before its first
-// MFMA, so the LDS latency is paid once per piece.
-// (scale diag(gamma) Q H)^T of a chunk from the state at its start, i.e.
-// H^T Q^T with the state split as the A operand and the Q fragments as the B
-// operand, one column tile ct per call: qh[rt][ct] lane (m, g) holds value
-// column 16 ct + 4 g + j (of this wave's 32) of query row 16 rt + m.  It later accumulates (scale P v')^T in
-// place, and each lane then owns four consecutive output columns of one row.
-// The state enters as hi + lo bf16 parts (fp32-class product): the path for
-// fp32 outputs; bf16 outputs use qh9_both below.
-__device__ __forceinline__ void qh9(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int ct,
-                                    const int buf, const float scale, const int ln) {
-    const int m = ln & 15;
-    const bf16 *Q = s.q;
-    bf16x8 qa[4][4];  // [k step][row tile]
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) qa[kk][rt] = frag_rp(Q, 16 * rt, 32 * kk, ln);
-    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) qh[rt][ct] = f32x4{};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 hh, hl;
-        split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh, hl);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            qh[rt][ct] = mfma16(hh, qa[kk][rt], qh[rt][ct]);
-            qh[rt][ct] = mfma16(hl, qa[kk][rt], qh[rt][ct]);
-        }
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) qh[rt][ct] *= scale * s.gam[buf][16 * rt + m];  // this lane's query row
-}
-
-// Both column tiles at once from the bf16-rounded state alone, one MFMA per
-// step (bf16 outputs, whose own rounding is the larger error): the Q fragments
-// are read once for the two tiles.
-__device__ __forceinline__ void qh9_both(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2],
-                                         const int buf, const float scale, const int ln) {
-    const int m = ln & 15;
-    const bf16 *Q = s.q;
-    bf16x8 qa[4][4];  // [k step][row tile]
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) qa[kk][rt] = frag_rp(Q, 16 * rt, 32 * kk, ln);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] = f32x4{};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const f32x4 &t0 = hacc[ct][2 * kk], &t1 = hacc[ct][2 * kk + 1];
-            const bf16x8 hh = {(bf16)t0[0], (bf16)t0[1], (bf16)t0[2], (bf16)t0[3],
-                               (bf16)t1[0], (bf16)t1[1], (bf16)t1[2], (bf16)t1[3]};
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) qh[rt][ct] = mfma16(hh, qa[kk][rt], qh[rt][ct]);
-        }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const float f = scale * s.gam[buf][16 * rt + m];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] *= f;
-    }
-}
-
-// v' = U - W H (vp enters holding U), with W and H as hi + lo bf16 (the lo x
-// lo term, below fp32 resolution of the product, is left out).  The W
-// fragments of one k step (hi and lo, 32 registers) are read while the
-// previous step's products run.
-__device__ __forceinline__ void wh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int ln) {
-    bf16x8 wa[2][4], wl[2][4];  // [k step parity][row tile]
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        wa[0][rt] = s.wf[0][rt][0][ln];
-        wl[0][rt] = s.wf[1][rt][0][ln];
-    }
+    for (int rt = 0; rt < 4; ++rt) ka[0][rt] = frag_rp(K, 16 * rt, 0, ln);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const int b = kk & 1;
         if (kk + 1 < 4) {
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                wa[b ^ 1][rt] = s.wf[0][rt][kk + 1][ln];
-                wl[b ^ 1][rt] = s.wf[1][rt][kk + 1][ln];
-            }
+            for (int rt = 0; rt < 4; ++rt) ka[b ^ 1][rt] = frag_rp(K, 16 * rt, 32 * (kk + 1), ln);
         }
         __builtin_amdgcn_sched_barrier(0);  // the next step's reads go out ahead of this step's products
         bf16x8 hh[2], hl[2];
@@ -879,74 +790,146 @@ __device__ __forceinline__ void wh8(const Smem8 &s, const f32x4 (&hacc)[2][8], f
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                vp[rt][ct] = mfma16(wa[b][rt], hh[ct], vp[rt][ct]);
-                vp[rt][ct] = mfma16(wa[b][rt], hl[ct], vp[rt][ct]);
-                vp[rt][ct] = mfma16(wl[b][rt], hh[ct], vp[rt][ct]);
+                X[rt][ct] = mfma16(ka[b][rt], hh[ct], X[rt][ct]);
+                X[rt][ct] = mfma16(ka[b][rt], hl[ct], X[rt][ct]);
             }
     }
 }
 
-// The same with the W fragments read one k step at a time (fewer live
-// registers; for the pre-pass, which runs three waves per SIMD).
-__device__ __forceinline__ void wh8_lean(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int ln) {
+// The state term of the output of the chunk in buffers nb,
+// qh = (scale diag(gamma) Q H)^T (this wave's value columns x query rows): H
+// as the A operand (its bf16 rounding alone for bf16 o: that term reaches only
+// o, whose own rounding is the larger error; hi + lo for fp32 o), the Q
+// fragments as B operands, read one k step ahead.  Lane (m, g) of tile
+// (rt, ct) ends up holding value columns 16 ct + 4 g .. +3 of query row 16 rt + m.
+template <bool OF32>
+__device__ __forceinline__ void qhq(const Smem8 &s, const f32x4 (&hacc)[2][8], f32x4 (&qh)[4][2], const int nb,
+                                    const float scale, const int ln) {
+    const int m = ln & 15;
+    const bf16 *Q = s.q;
+    zero_tiles(qh);
+    bf16x8 qa[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) qa[0][rt] = frag_rp(Q, 16 * rt, 0, ln);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 wa[4], wl[4];
+        const int b = kk & 1;
+        if (kk + 1 < 4) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            wa[rt] = s.wf[0][rt][kk][ln];
-            wl[rt] = s.wf[1][rt][kk][ln];
+            for (int rt = 0; rt < 4; ++rt) qa[b ^ 1][rt] = frag_rp(Q, 16 * rt, 32 * (kk + 1), ln);
         }
-        bf16x8 hh[2], hl[2];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) split_pair(hacc[ct][2 * kk], hacc[ct][2 * kk + 1], hh[ct], hl[ct]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                vp[rt][ct] = mfma16(wa[rt], hh[ct], vp[rt][ct]);
-                vp[rt][ct] = mfma16(wa[rt], hl[ct], vp[rt][ct]);
-                vp[rt][ct] = mfma16(wl[rt], hh[ct], vp[rt][ct]);
+        for (int ct = 0; ct < 2; ++ct) {
+            const f32x4 &t0 = hacc[ct][2 * kk], &t1 = hacc[ct][2 * kk + 1];
+            bf16x8 hh, hl;
+            if (OF32) {
+                split_pair(t0, t1, hh, hl);
+            } else {
+                hh = bf16x8{(bf16)t0[0], (bf16)t0[1], (bf16)t0[2], (bf16)t0[3],
+                            (bf16)t1[0], (bf16)t1[1], (bf16)t1[2], (bf16)t1[3]};
             }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                qh[rt][ct] = mfma16(hh, qa[b][rt], qh[rt][ct]);
+                if (OF32) qh[rt][ct] = mfma16(hl, qa[b][rt], qh[rt][ct]);
+            }
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+        const float f = scale * s.gam[nb][16 * rt + m];  // this lane's query row
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) qh[rt][ct] *= f;
     }
 }
 
+// Y = V - diag(gamma) X of the chunk in buffers nb (the transition-map pass
+// has no V: Y = -diag(gamma) X), as hi / lo pairs.  V comes from transposing
+// reads of its tile, which hand each lane the rows of its X elements.
+__device__ __forceinline__ void yform(const Smem8 &s, const f32x4 (&X)[4][2], YSplit &y, const bool with_v, const int sw,
+                                      const int nb, const int ln) {
+    const int g = ln >> 4;
+    bf16x8 vv[2][2];  // [token step][column tile]
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+            vv[ks][ct] = with_v ? frag_t(s.v, 32 * sw + 16 * ct, 32 * ks, ln) : bf16x8{};
+    f32x4 gm[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) gm[rt] = *reinterpret_cast<const f32x4 *>(&s.gam[nb][16 * rt + 4 * g]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            float yv[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                yv[e] = (float)vv[ks][ct][e] - gm[2 * ks][e] * X[2 * ks][ct][e];
+                yv[4 + e] = (float)vv[ks][ct][4 + e] - gm[2 * ks + 1][e] * X[2 * ks + 1][ct][e];
+            }
+            split8v(yv, y.h[ks][ct], y.l[ks][ct]);
+        }
+}
 
-// O^T = (scale diag(gamma) Q H)^T + v'^T (scale P)^T for the two column tiles:
-// the split v' tiles serve as A operands and the P fragments as B operands.
-// Lane (m, g) then holds four consecutive value columns 16 ct + 4 g .. +3 of
-// query row 16 rt + m, stored as one 16-byte (fp32) or 8-byte (bf16) piece
-// through a buffer resource over the chunk's rows (rows past the sequence end
-// are dropped by the hardware range check).
-template <bool OF32>
-__device__ __forceinline__ void out9(const Smem8 &s, const FwdParams &p, const char *obase, const int seq_len,
-                                     const f32x4 (&vp)[4][2], f32x4 (&acc)[4][2], const int c, const int sw,
-                                     const int ln) {
-    const int m = ln & 15, g = ln >> 4;
-    bf16x8 pa[6][2];  // the six P fragments, hi and lo
+// vd = F Y for the hi / lo A fragments F of s.tdf (DECAYED: diag(dec) T
+// diag(beta), the decayed v') or s.tf (T diag(beta), v' itself).
+__device__ __forceinline__ void tdy(const Smem8 &s, const bool decayed, const YSplit &y, f32x4 (&vd)[4][2],
+                                    const int ln) {
+    bf16x8 th[6], tl[6];
 #pragma unroll
     for (int f = 0; f < 6; ++f) {
-        pa[f][0] = s.pf[0][f][ln];
-        pa[f][1] = s.pf[1][f][ln];
+        th[f] = decayed ? s.tdf[0][f][ln] : s.tf[0][f][ln];
+        tl[f] = decayed ? s.tdf[1][f][ln] : s.tf[1][f][ln];
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 vh[2], vl[2];
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) split_pair(vp[2 * ks][ct], vp[2 * ks + 1][ct], vh[ct], vl[ct]);
+        for (int ct = 0; ct < 2; ++ct) vd[rt][ct] = f32x4{};
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        const int rt = frag_rt(f), ks = frag_ks(f);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            vd[rt][ct] = mfma16(th[f], y.h[ks][ct], vd[rt][ct]);
+            vd[rt][ct] = mfma16(th[f], y.l[ks][ct], vd[rt][ct]);
+            vd[rt][ct] = mfma16(tl[f], y.h[ks][ct], vd[rt][ct]);
+        }
+    }
+}
+
+// O^T = (scale diag(gamma) Q H)^T + Y^T Z^T for the two column tiles (acc
+// enters holding the first term): the Y pairs serve as A operands and the Z^T
+// fragments as B operands.  Lane (m, g) then holds four consecutive value
+// columns 16 ct + 4 g .. +3 of query row 16 rt + m, stored as one 16-byte
+// (fp32) or 8-byte (bf16) piece through a buffer resource over the chunk's rows
+// (rows past the sequence end are dropped by the hardware range check).
+template <bool OF32>
+__device__ __forceinline__ void outz(const Smem8 &s, const FwdParams &p, const char *obase, const int seq_len,
+                                     const YSplit &y, f32x4 (&acc)[4][2], const int c, const int sw, const int ln) {
+    const int m = ln & 15, g = ln >> 4;
+    bf16x8 za[6][2];
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        za[f][0] = s.zf[0][f][ln];
+        za[f][1] = s.zf[1][f][ln];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-            if (ks == 1 && rt < 2) continue;  // P is lower triangular
+            if (ks == 1 && rt < 2) continue;  // Z is lower triangular
             const int f = frag_of(rt, ks);
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-                acc[rt][ct] = mfma16(vh[ct], pa[f][0], acc[rt][ct]);
-                acc[rt][ct] = mfma16(vl[ct], pa[f][0], acc[rt][ct]);
-                acc[rt][ct] = mfma16(vh[ct], pa[f][1], acc[rt][ct]);
+                acc[rt][ct] = mfma16(y.h[ks][ct], za[f][0], acc[rt][ct]);
+                acc[rt][ct] = mfma16(y.l[ks][ct], za[f][0], acc[rt][ct]);
+                acc[rt][ct] = mfma16(y.h[ks][ct], za[f][1], acc[rt][ct]);
             }
         }
-    }
     const unsigned es = OF32 ? 4u : 2u;
     const unsigned rstride = (unsigned)p.Hv * DV * es;
     const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(obase, rstride, c, seq_len);
@@ -965,76 +948,61 @@ __device__ __forceinline__ void out9(const Smem8 &s, const FwdParams &p, const c
         }
 }
 
-// H <- gamma_last H + K^T diag(gamma_last / gamma) v'
-__device__ __forceinline__ void hupd9(const Smem8 &s, f32x4 (&hacc)[2][8], const f32x4 (&vp)[4][2], const int buf,
-                                      const int ln) {
-    const int g = ln >> 4;
-    const bf16 *K = s.k[buf];
-    bf16x8 ka[2][8];  // [token step][key-dim tile]
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) ka[ks][dt] = frag_t(K, 16 * dt, 32 * ks, ln);
-    f32x4 d4[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) d4[rt] = *reinterpret_cast<const f32x4 *>(&s.dec[buf][16 * rt + 4 * g]);
-    const float glast = s.gam[buf][CH - 1];
-    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) hacc[ct][dt] *= glast;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 vh[2], vl[2];  // the decayed v' (v' itself stays for the optional v' store)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-            split_pair(vp[2 * ks][ct] * d4[2 * ks], vp[2 * ks + 1][ct] * d4[2 * ks + 1], vh[ct], vl[ct]);
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                hacc[ct][dt] = mfma16(ka[ks][dt], vh[ct], hacc[ct][dt]);
-                hacc[ct][dt] = mfma16(ka[ks][dt], vl[ct], hacc[ct][dt]);
-            }
-    }
-}
-
-// The same with the K^T fragments read four at a time.
-__device__ __forceinline__ void hupd9_lean(const Smem8 &s, f32x4 (&hacc)[2][8], f32x4 (&vp)[4][2], const int buf,
-                                           const int ln) {
-    const int g = ln >> 4;
+// H <- gamma_last H + K^T vd, vd = diag(gamma_last / gamma) v' (as hi / lo).
+// LEAN reads the K^T fragments four at a time (the transition-map pass runs
+// three waves per SIMD and has fewer registers).
+template <bool LEAN>
+__device__ __forceinline__ void upd(const Smem8 &s, f32x4 (&hacc)[2][8], const f32x4 (&vd)[4][2], const int buf,
+                                    const int ln) {
     const bf16 *K = s.k[buf];
     const float glast = s.gam[buf][CH - 1];
+    if (!LEAN) {
+        bf16x8 ka[2][8];  // [token step][key-dim tile]
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(&s.dec[buf][16 * rt + 4 * g]);
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) ka[ks][dt] = frag_t(K, 16 * dt, 32 * ks, ln);
+        __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) vp[rt][ct][jj] *= d4[jj];
-    }
+            for (int dt = 0; dt < 8; ++dt) hacc[ct][dt] *= glast;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 vh[2], vl[2];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) hacc[ct][dt] *= glast;
+            for (int ct = 0; ct < 2; ++ct) split_pair(vd[2 * ks][ct], vd[2 * ks + 1][ct], vh[ct], vl[ct]);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 vh[2], vl[2];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) split_pair(vp[2 * ks][ct], vp[2 * ks + 1][ct], vh[ct], vl[ct]);
-#pragma unroll
-        for (int d4i = 0; d4i < 2; ++d4i) {
-            bf16x8 ka[4];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) ka[d] = frag_t(K, 16 * (4 * d4i + d), 32 * ks, ln);
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
+            for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct) {
-                    hacc[ct][4 * d4i + d] = mfma16(ka[d], vh[ct], hacc[ct][4 * d4i + d]);
-                    hacc[ct][4 * d4i + d] = mfma16(ka[d], vl[ct], hacc[ct][4 * d4i + d]);
+                    hacc[ct][dt] = mfma16(ka[ks][dt], vh[ct], hacc[ct][dt]);
+                    hacc[ct][dt] = mfma16(ka[ks][dt], vl[ct], hacc[ct][dt]);
                 }
+        }
+    } else {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) hacc[ct][dt] *= glast;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 vh[2], vl[2];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) split_pair(vd[2 * ks][ct], vd[2 * ks + 1][ct], vh[ct], vl[ct]);
+#pragma unroll
+            for (int d4i = 0; d4i < 2; ++d4i) {
+                bf16x8 ka[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) ka[d] = frag_t(K, 16 * (4 * d4i + d), 32 * ks, ln);
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        hacc[ct][4 * d4i + d] = mfma16(ka[d], vh[ct], hacc[ct][4 * d4i + d]);
+                        hacc[ct][4 * d4i + d] = mfma16(ka[d], vl[ct], hacc[ct][4 * d4i + d]);
+                    }
+            }
         }
     }
 }
@@ -1171,27 +1139,25 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
 
     // Iteration c runs the state pass of chunk c (state waves) in step with the
     // preparation of chunk c + 1 (preparation waves); c = c_first - 1 only
-    // prepares the first chunk.
-    //   step  state waves                        preparation waves
-    //   1     v' = U - W H                       gate scan, K K^T; load g, beta of c + 2
-    //   2     O = scale (gamma Q H + P v')       inverse level 0; load V of c + 1
-    //   3     H update                           inverse level 1 (pw 0, 1), P
-    //   4     scale gamma Q H of chunk c + 1     inverse level 2; W, T diag(beta),
-    //         (the last reads of its Q tile);    rows 0..31
-    //         load K of c + 2
-    //   5     (optional h store)                 W, T diag(beta), rows 32..63;
-    //                                            load Q of c + 2
+    // prepares the first chunk.  With Y = V - diag(gamma) K H (the chunk's
+    // v' = U - W H is T diag(beta) Y):
+    //   step  state waves                          preparation waves
+    //   1     O = scale gamma Q H + Z Y, decayed    gate scan, K K^T; load g, beta of c + 2
+    //         v' = diag(dec) T diag(beta) Y
+    //   2     H update                             inverse level 0
+    //   3     X = K H and Q H of chunk c + 1       inverse level 1 (pw 0, 1), P
+    //   4     Y of chunk c + 1; load K of c + 2    inverse level 2; WY fragments of rows 0..31
+    //                                              (diag(dec) T diag(beta), Z); load Q of c + 2
+    //   5     (optional h store)                   the same for rows 32..63; load V of c + 2
     // K sits in LDS by chunk parity, Q and V for one chunk each; each load is
-    // issued once the step that last reads its slot is behind a barrier.  Every
-    // wave waits for its own loads before the iteration's first barrier, except
-    // that the Q loads of the last step stay in flight until the barrier before
-    // P (step 3 of the next iteration), the first step that reads them.
-    // K goes out from the state waves: a transposing LDS read is compiled with
-    // a wait for every direct load the wave has in flight, and the preparation
-    // waves read K transposed right after the K slot frees up.  Both roles run
-    // their own copy of the loop with the same five barriers per iteration (a
-    // barrier counts arrivals, wherever they come from), so each role's
-    // registers are allocated for its own live values.
+    // issued once the step that last reads its slot is behind a barrier.  The
+    // state waves wait for their K loads before the next iteration's first
+    // barrier; the preparation waves wait before the first barrier for their g
+    // and beta loads only (the Q and V tiles of steps 4 and 5 stay in flight)
+    // and before the third for everything but this iteration's g and beta.
+    // Both roles run their own copy of the loop with the same five barriers per
+    // iteration (a barrier counts arrivals, wherever they come from), so each
+    // role's registers are allocated for its own live values.
     if (state_wave) {
         // ---- state: value columns 32 wave .. +31
         f32x4 hacc[2][8];
@@ -1218,13 +1184,17 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
         }
         const int64_t oes = OF32 ? 4 : 2;
         const char *obase = static_cast<const char *>(p.o) + ((int64_t)e.row0 * p.Hv + j) * DV * oes;
-        f32x4 vp[4][2], qh[4][2];  // vp: U, then v' of this chunk
+        f32x4 qh[4][2];  // scale diag(gamma) Q H of the next chunk, transposed
+        f32x4 vd[4][2];  // decayed v' of this chunk
+        f32x4 X[4][2];   // K H of the next chunk
+        YSplit ysp;      // Y of the chunk whose state pass comes next
         const int cbase = (!PRE && (p.h_out || p.vn_out)) ? seq_chunk_base(p, e.n, lane) : 0;
         const TileOffs<NSTATE> koffs = tile_offsets<NSTATE>(in.kstride, wave, lane);  // this wave's share of K
         for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
             const bool chain = c >= c_first;  // state pass of chunk c
-            const bool prep = c + 1 < c_end;  // preparation of chunk c + 1
-            const bool out = c >= e.c_begin;  // chunk c produces output (not a warm-up chunk)
+            const bool prep = c + 1 < c_end;  // chunk c + 1 follows
+            const bool out = !PRE && c >= e.c_begin;             // chunk c produces output
+            const bool qnext = !PRE && prep && c + 1 >= e.c_begin;  // chunk c + 1 produces output
             const int b = c & 1, nb = (c + 1) & 1;
             dma_wait();
             lds_barrier();
@@ -1236,44 +1206,41 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 asm volatile("" : "+v"(t));
                 return t & 63;
             };
+            // Every value carried from one step to a later one is defined on
+            // both sides of its step's branch: a value defined on one side only
+            // would stay live around the whole loop (the compiler cannot tell
+            // that the later step's branch takes the same side), and the
+            // registers would spill.
             if (chain) {
-                if (mwave) {
-#pragma unroll
-                    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                        for (int ct = 0; ct < 2; ++ct) vp[rt][ct] = f32x4{};
-                } else if (PRE) {
-                    u9_lean(s, lane_now(), sw, vp);
-                } else {
-                    u9(s, lane_now(), sw, vp);
+                if (out) outz<OF32>(s, p, obase, e.seq_len, ysp, qh, c, wave, lane_now());
+                __builtin_amdgcn_sched_barrier(0);  // the two products' operand batches one after the other
+                tdy(s, true, ysp, vd, lane_now());
+                if (out && p.vn_out) {
+                    f32x4 vp[4][2];
+                    tdy(s, false, ysp, vp, lane_now());
+                    store_vn8(vp, p.vn_out + ((int64_t)(cbase + c) * p.Hv + j) * CH * DV, wave, lane_now());
                 }
-                if (PRE) wh8_lean(s, hacc, vp, lane_now());
-                else wh8(s, hacc, vp, lane_now());
+            } else {
+                zero_tiles(vd);
             }
             lds_barrier();
-            if (!PRE && chain && out) out9<OF32>(s, p, obase, e.seq_len, vp, qh, c, wave, lane_now());
+            if (chain) upd<PRE>(s, hacc, vd, b, lane_now());
             lds_barrier();
-            if (chain) {
-                if (PRE) hupd9_lean(s, hacc, vp, b, lane_now());
-                else hupd9(s, hacc, vp, b, lane_now());
-            }
+            if (prep) xk(s, hacc, X, nb, lane_now());
+            else zero_tiles(X);
             lds_barrier();
+            if (prep) yform(s, X, ysp, !mwave, sw, nb, lane_now());
+            else ysp = YSplit{};
+            // the K tile of chunk c is free since the H update; its loads go out
+            // after this step's transposing reads of V (the compiler waits for
+            // every direct load in flight before such a read)
+            __builtin_amdgcn_sched_barrier(0);
             if (c + 2 < c_end) dma_tile<NSTATE>(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, koffs);
-            if (!PRE && prep && c + 1 >= e.c_begin) {  // the last reads of this Q tile
-                if (OF32) {
-                    qh9(s, hacc, qh, 0, nb, p.scale, lane_now());
-                    qh9(s, hacc, qh, 1, nb, p.scale, lane_now());
-                } else {
-                    qh9_both(s, hacc, qh, nb, p.scale, lane_now());
-                }
-            }
             lds_barrier();
-            if (!PRE && prep && c + 1 >= e.c_begin && p.h_out)
+            if (qnext) qhq<OF32>(s, hacc, qh, nb, p.scale, lane_now());
+            else zero_tiles(qh);
+            if (qnext && p.h_out)
                 store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
-            // v' of chunk c, out of the first step's way (the state waves have no
-            // other work here for a bf16 o)
-            if (!PRE && chain && out && p.vn_out)
-                store_vn8(vp, p.vn_out + ((int64_t)(cbase + c) * p.Hv + j) * CH * DV, wave, lane_now());
         }
         if (PRE) {
             store_state8(hacc, (mwave ? p.ws_m : p.ws_s) + ((int64_t)seg * p.Hv + j) * DK * DV, sw, lane);
@@ -1291,18 +1258,16 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             const TileOffs<4> voffs = tile_offsets<4>(in.vstride, pw, lane);   // and of V
             const char *abase = (!PRE && p.a_out) ? reinterpret_cast<const char *>(p.a_out + ((int64_t)e.row0 * p.Hv + j) * CH)
                                         : nullptr;
+            const bool with_tf = !PRE && p.vn_out;
             if (has_chunks) {
                 dma_tile<4>(s.k[c_first & 1], in.k, in.kstride, c_first, e.seq_len, pw, kqoffs);
-                if (!PRE && c_first >= e.c_begin) dma_tile<4>(s.q, in.q, in.kstride, c_first, e.seq_len, pw, kqoffs);
                 dma_gb(s, in, c_first, pw, lane);
+                dma_tile<4>(s.v, in.v, in.vstride, c_first, e.seq_len, pw, voffs);
             }
-            // this wave's loads per tile, and of g or beta per chunk
-            constexpr int NTILE = (TLOADS - pw + 3) / 4, NGB = pw < 2 ? 1 : 0;
-            // Q sits in one LDS tile: the tile of chunk c + 2 is loaded in the
-            // last step of iteration c (after the state waves' last read of
-            // chunk c + 1's), and only P (step 3 of iteration c + 1) waits for
-            // it; the waits before that leave these loads in flight.
-            bool q_pending = false;
+            // vector memory operations this wave issued after its g / beta load
+            // of the previous iteration (the A stores and the V tile of its last
+            // step): left in flight by the wait before the first barrier
+            int after_gb = 0;
             for (int c = c_first - 1; has_chunks && c < c_end; ++c) {
                 // with the wave's share fixed at compile time, its lane-derived
                 // LDS addresses are few enough to stay in registers across the
@@ -1311,27 +1276,24 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 const bool prep = c + 1 < c_end;   // preparation of chunk c + 1
                 const bool ahead = c + 2 < c_end;  // loads of chunk c + 2
                 const int nb = (c + 1) & 1;
-                if (q_pending) dma_wait_but<NTILE>();  // g, beta and V of the previous iteration
-                else dma_wait();
+                const bool pout = !PRE && prep && c + 1 >= e.c_begin;  // chunk c + 1 produces output: P, Z needed
+                dma_wait_upto(after_gb);
                 lds_barrier();
+                // Q of chunk c + 1: its tile is free since the state waves' Q H
+                // of chunk c (the previous iteration's last step)
+                if (pout) dma_tile<4>(s.q, in.q, in.kstride, c + 1, e.seq_len, pw, kqoffs);
                 if (ahead) dma_gb(s, in, c + 2, pw, ln);
                 if (prep) prod9(s, ln, pw, nb);
                 lds_barrier();
-                if (prep) dma_tile<4>(s.v, in.v, in.vstride, c + 1, e.seq_len, pw, voffs);
                 if (prep) inv8_l0(s, ln, pw);
-                // Q of chunk c + 1: every load this wave issued after it is
-                // this iteration's g or beta (if ahead) and V (q_pending
-                // implies prep)
-                if (q_pending) {
-                    if (ahead) dma_wait_but<NGB + NTILE>();
-                    else dma_wait_but<NTILE>();
-                }
+                // Q of chunk c + 1 (read by P in the next step) and V of chunk
+                // c + 1 (read by the state waves' Y in step 4): every load but
+                // this iteration's g or beta
+                if (ahead && pw < 2) dma_wait_but<1>();
+                else dma_wait();
                 lds_barrier();
-                const bool pout = !PRE && prep && c + 1 >= e.c_begin;  // chunk c + 1 produces output: P needed
-                if (prep && pw < 2) {
-                    inv8_l1(s, ln, pw);
-                    if (pout) pfrag9(s, ln, pw + 1, nb, p.scale, decays_factor(s, ln));  // fragments 1, 2
-                }
+                if (prep && pw < 2) inv8_l1(s, ln, pw);
+                if (pout && pw < 2) pfrag9(s, ln, pw + 1, nb, p.scale, decays_factor(s, ln));  // fragments 1, 2
                 if (pout && pw >= 2) {
                     const bool fact = decays_factor(s, ln);
                     pfrag9(s, ln, pw == 2 ? 5 : 3, nb, p.scale, fact);
@@ -1342,13 +1304,29 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                     L2Regs l2;
                     inv8_l2a(s, ln, pw, l2);
                     inv8_l2b(s, ln, pw, l2);
+                    // rows 0..31 (final since level 1): fragments 0 and 1
+                    if (pw < 2) {
+                        tdfrag(s, ln, pw, nb, with_tf);
+                        if (pout) zfrag(s, ln, pw, nb);
+                    }
                 }
-                if (prep) wfrag9(s, ln, 0, pw, pw < 2 ? pw : -1, nb);  // rows 0..31, final since level 1
                 lds_barrier();
-                if (!PRE && prep && p.a_out && c + 1 >= e.c_begin) store_t8(s, p, abase, e.seq_len, c + 1, pw, ln);
-                if (prep) wfrag9(s, ln, 2, pw, 2 + pw, nb);  // rows 32..63
-                q_pending = !PRE && ahead && c + 2 >= e.c_begin;
-                if (q_pending) dma_tile<4>(s.q, in.q, in.kstride, c + 2, e.seq_len, pw, kqoffs);
+                const bool astore = !PRE && prep && p.a_out && c + 1 >= e.c_begin;
+                if (astore) store_t8(s, p, abase, e.seq_len, c + 1, pw, ln);
+                if (ahead) dma_tile<4>(s.v, in.v, in.vstride, c + 2, e.seq_len, pw, voffs);
+                after_gb = ahead ? ((astore ? 4 : 0) + NTILE4(pw)) : 0;
+                if (prep) {
+                    // rows 32..63: fragments 2..5 (Z fragments 2 and 3 are the
+                    // larger ones: one each on waves 0 and 1, 4 and 5 together on wave 2)
+                    tdfrag(s, ln, 2 + pw, nb, with_tf);
+                    if (pout) {
+                        if (pw < 2) zfrag(s, ln, 2 + pw, nb);
+                        if (pw == 2) {
+                            zfrag(s, ln, 4, nb);
+                            zfrag(s, ln, 5, nb);
+                        }
+                    }
+                }
             }
         };
         switch (wave - NSTATE) {
