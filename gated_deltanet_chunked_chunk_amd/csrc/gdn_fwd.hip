@@ -712,11 +712,13 @@ __device__ __forceinline__ void tdfrag(Smem8 &s, const int lane, const int f, co
 // (T diag(beta))^T (rows s, k = s') and the (scale P)^T fragments (k = s',
 // columns i) over the token steps s' between s and i (both factors are
 // triangular), hi / lo on both sides.  The columns of T come from its
-// transposed blocks (s.tt diagonal blocks, s.tlot lower-left block).
-__device__ __forceinline__ void zfrag(Smem8 &s, const int lane, const int f, const int buf) {
+// transposed blocks (s.tt diagonal blocks, s.tlot lower-left block).  The
+// token steps KQ0 <= kq <= KQ1 of the sum are added to acc; zstore splits the
+// two tiles and stores the fragment.
+template <int KQ0, int KQ1>
+__device__ __forceinline__ void zsum(const Smem8 &s, const int lane, const int f, const int buf, f32x4 (&acc)[2]) {
     const int m = lane & 15, g = lane >> 4;
     const int rt = frag_rt(f), ks = frag_ks(f);
-    f32x4 acc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int st = 2 * ks + h;  // token tile of the rows s
@@ -724,7 +726,7 @@ __device__ __forceinline__ void zfrag(Smem8 &s, const int lane, const int f, con
         const int sr = 16 * st + m;
         const float bs = s.braw[buf][sr];
 #pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
+        for (int kq = KQ0; kq <= KQ1; ++kq) {
             if (kq < ks || kq > (rt >> 1)) continue;
             const float *src = (kq == 0) ? &s.tt[0][sr * TS8]
                                : (st >= 2) ? &s.tt[1][(sr - 32) * TS8]
@@ -742,6 +744,9 @@ __device__ __forceinline__ void zfrag(Smem8 &s, const int lane, const int f, con
             acc[h] = mfma16(al, ph, acc[h]);
         }
     }
+}
+
+__device__ __forceinline__ void zstore(Smem8 &s, const int lane, const int f, const f32x4 (&acc)[2]) {
     bf16x8 hi, lo;
     split_pair(acc[0], acc[1], hi, lo);
     s.zf[0][f][lane] = hi;
@@ -900,36 +905,55 @@ __device__ __forceinline__ void tdy(const Smem8 &s, const bool decayed, const YS
     }
 }
 
-// O^T = (scale diag(gamma) Q H)^T + Y^T Z^T for the two column tiles (acc
-// enters holding the first term): the Y pairs serve as A operands and the Z^T
-// fragments as B operands.  Lane (m, g) then holds four consecutive value
-// columns 16 ct + 4 g .. +3 of query row 16 rt + m, stored as one 16-byte
-// (fp32) or 8-byte (bf16) piece through a buffer resource over the chunk's rows
-// (rows past the sequence end are dropped by the hardware range check).
+// Step 1 of a chunk's state pass, one loop over the six non-zero fragments
+// f = (row tile rt, token step ks), each read one fragment ahead:
+//   O^T = (scale diag(gamma) Q H)^T + Y^T Z^T for the two column tiles
+//        (acc enters holding the first term; the Y pairs are the A operands,
+//        the Z^T fragments the B operands), then stored: lane (m, g) holds value
+//        columns 16 ct + 4 g .. +3 of query row 16 rt + m, one 16-byte (fp32) or
+//        8-byte (bf16) piece through a buffer resource over the chunk's rows
+//        (rows past the sequence end are dropped by the hardware range check),
+//        when STORE (a warm-up chunk computes it and stores nothing: one copy
+//        of this code in the loop allocates registers without spilling, two
+//        copies did not);
+//   vd = diag(dec) T diag(beta) Y, the decayed v' of the state update (the
+//        fragments of s.tdf as A operands, the Y pairs as B operands).
 template <bool OF32>
-__device__ __forceinline__ void outz(const Smem8 &s, const FwdParams &p, const char *obase, const int seq_len,
-                                     const YSplit &y, f32x4 (&acc)[4][2], const int c, const int sw, const int ln) {
+__device__ __forceinline__ void out_vd(const Smem8 &s, const FwdParams &p, const char *obase, const int seq_len,
+                                       const YSplit &y, f32x4 (&acc)[4][2], f32x4 (&vd)[4][2], const bool store,
+                                       const int c, const int sw, const int ln) {
     const int m = ln & 15, g = ln >> 4;
-    bf16x8 za[6][2];
+    zero_tiles(vd);
+    bf16x8 zr[2][2], tr[2][2];  // [fragment parity][hi, lo]
+    zr[0][0] = s.zf[0][0][ln];
+    zr[0][1] = s.zf[1][0][ln];
+    tr[0][0] = s.tdf[0][0][ln];
+    tr[0][1] = s.tdf[1][0][ln];
 #pragma unroll
     for (int f = 0; f < 6; ++f) {
-        za[f][0] = s.zf[0][f][ln];
-        za[f][1] = s.zf[1][f][ln];
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the batch of reads ahead of its products
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            if (ks == 1 && rt < 2) continue;  // Z is lower triangular
-            const int f = frag_of(rt, ks);
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                acc[rt][ct] = mfma16(y.h[ks][ct], za[f][0], acc[rt][ct]);
-                acc[rt][ct] = mfma16(y.l[ks][ct], za[f][0], acc[rt][ct]);
-                acc[rt][ct] = mfma16(y.h[ks][ct], za[f][1], acc[rt][ct]);
-            }
+        const int b = f & 1;
+        if (f + 1 < 6) {
+            zr[b ^ 1][0] = s.zf[0][f + 1][ln];
+            zr[b ^ 1][1] = s.zf[1][f + 1][ln];
+            tr[b ^ 1][0] = s.tdf[0][f + 1][ln];
+            tr[b ^ 1][1] = s.tdf[1][f + 1][ln];
         }
+        // the next fragment's reads go out ahead of this one's products, and
+        // no further (registers)
+        __builtin_amdgcn_sched_barrier(0);
+        const int rt = frag_rt(f), ks = frag_ks(f);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            acc[rt][ct] = mfma16(y.h[ks][ct], zr[b][0], acc[rt][ct]);
+            acc[rt][ct] = mfma16(y.l[ks][ct], zr[b][0], acc[rt][ct]);
+            acc[rt][ct] = mfma16(y.h[ks][ct], zr[b][1], acc[rt][ct]);
+            vd[rt][ct] = mfma16(tr[b][0], y.h[ks][ct], vd[rt][ct]);
+            vd[rt][ct] = mfma16(tr[b][0], y.l[ks][ct], vd[rt][ct]);
+            vd[rt][ct] = mfma16(tr[b][1], y.h[ks][ct], vd[rt][ct]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (!store) return;
     const unsigned es = OF32 ? 4u : 2u;
     const unsigned rstride = (unsigned)p.Hv * DV * es;
     const __amdgpu_buffer_rsrc_t ro = chunk_rsrc(obase, rstride, c, seq_len);
@@ -1212,9 +1236,8 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             // that the later step's branch takes the same side), and the
             // registers would spill.
             if (chain) {
-                if (out) outz<OF32>(s, p, obase, e.seq_len, ysp, qh, c, wave, lane_now());
-                __builtin_amdgcn_sched_barrier(0);  // the two products' operand batches one after the other
-                tdy(s, true, ysp, vd, lane_now());
+                if (PRE) tdy(s, true, ysp, vd, lane_now());  // the pre-pass has no output
+                else out_vd<OF32>(s, p, obase, e.seq_len, ysp, qh, vd, out, c, wave, lane_now());
                 if (out && p.vn_out) {
                     f32x4 vp[4][2];
                     tdy(s, false, ysp, vp, lane_now());
@@ -1226,16 +1249,15 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             lds_barrier();
             if (chain) upd<PRE>(s, hacc, vd, b, lane_now());
             lds_barrier();
+            // the K tile of chunk c is free since the H update: the loads of
+            // chunk c + 2 have three steps to land (the compiler makes this
+            // wave wait for them before its next transposing LDS read, in step 4)
+            if (c + 2 < c_end) dma_tile<NSTATE>(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, koffs);
             if (prep) xk(s, hacc, X, nb, lane_now());
             else zero_tiles(X);
             lds_barrier();
             if (prep) yform(s, X, ysp, !mwave, sw, nb, lane_now());
             else ysp = YSplit{};
-            // the K tile of chunk c is free since the H update; its loads go out
-            // after this step's transposing reads of V (the compiler waits for
-            // every direct load in flight before such a read)
-            __builtin_amdgcn_sched_barrier(0);
-            if (c + 2 < c_end) dma_tile<NSTATE>(s.k[b], in.k, in.kstride, c + 2, e.seq_len, wave, koffs);
             lds_barrier();
             if (qnext) qhq<OF32>(s, hacc, qh, nb, p.scale, lane_now());
             else zero_tiles(qh);
@@ -1300,14 +1322,27 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                     pfrag9(s, ln, pw == 2 ? 0 : 4, nb, p.scale, fact);
                 }
                 lds_barrier();
+                // Z^T fragment 2 + pw (pw < 2) over two steps: the token step
+                // of T's first diagonal block now, the lower-left block (level
+                // 2) in the next step
+                f32x4 zacc[2] = {f32x4{}, f32x4{}};
                 if (prep) {
                     L2Regs l2;
                     inv8_l2a(s, ln, pw, l2);
                     inv8_l2b(s, ln, pw, l2);
-                    // rows 0..31 (final since level 1): fragments 0 and 1
-                    if (pw < 2) {
-                        tdfrag(s, ln, pw, nb, with_tf);
-                        if (pout) zfrag(s, ln, pw, nb);
+                    // rows 0..31 (final since level 1): fragments 0 and 1;
+                    // Z^T fragments 4 and 5 read only T's diagonal blocks
+                    if (pw < 2) tdfrag(s, ln, pw, nb, with_tf);
+                    if (pout) {
+                        f32x4 z[2] = {f32x4{}, f32x4{}};
+                        if (pw < 2) {
+                            zsum<0, 1>(s, ln, pw, nb, z);
+                            zstore(s, ln, pw, z);
+                            zsum<0, 0>(s, ln, 2 + pw, nb, zacc);
+                        } else {
+                            zsum<1, 1>(s, ln, 2 + pw, nb, z);
+                            zstore(s, ln, 2 + pw, z);
+                        }
                     }
                 }
                 lds_barrier();
@@ -1316,15 +1351,11 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 if (ahead) dma_tile<4>(s.v, in.v, in.vstride, c + 2, e.seq_len, pw, voffs);
                 after_gb = ahead ? ((astore ? 4 : 0) + NTILE4(pw)) : 0;
                 if (prep) {
-                    // rows 32..63: fragments 2..5 (Z fragments 2 and 3 are the
-                    // larger ones: one each on waves 0 and 1, 4 and 5 together on wave 2)
+                    // rows 32..63: fragments 2..5
                     tdfrag(s, ln, 2 + pw, nb, with_tf);
-                    if (pout) {
-                        if (pw < 2) zfrag(s, ln, 2 + pw, nb);
-                        if (pw == 2) {
-                            zfrag(s, ln, 4, nb);
-                            zfrag(s, ln, 5, nb);
-                        }
+                    if (pout && pw < 2) {
+                        zsum<1, 1>(s, ln, 2 + pw, nb, zacc);
+                        zstore(s, ln, 2 + pw, zacc);
                     }
                 }
             }
