@@ -96,12 +96,16 @@ def bwd_algorithmic(x) -> tuple:
     return int(n), int(chunk_heads * (reverse + local))
 
 
-def stored_traffic(workload: str):
+def traffic_key(workload: str, cp: str) -> str:
+    return workload if cp == "auto" else f"{workload}:{cp}"
+
+
+def stored_traffic(workload: str, cp: str = "auto"):
     try:
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    e = d.get(workload)
+    e = d.get(traffic_key(workload, cp))
     if not e or e.get("kernel_source_sha") != kernel_source_hash():
         return None
     return e.get("bytes_per_launch")
@@ -116,7 +120,7 @@ def _counter_mean(csv_path: str, counter: str, kernel_substr: str) -> float:
     return sum(vals) / len(vals)
 
 
-def ingest_counters(workload: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str):
+def ingest_counters(workload: str, cp: str, fetch_csv: str, write_csv: str, copy_fetch_csv: str, copy_write_csv: str):
     """Turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs (KiB per dispatch) of the
     forward and of the 1 GiB copy calibration into HBM bytes per launch, and
     store them with the hash of the kernel source they were taken on."""
@@ -129,12 +133,13 @@ def ingest_counters(workload: str, fetch_csv: str, write_csv: str, copy_fetch_cs
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         d = {}
-    d[workload] = {"bytes_per_launch": int(round(fetch + write)), "fetch_bytes": int(round(fetch)),
-                   "write_bytes": int(round(write)), "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4),
-                   "kernel_source_sha": kernel_source_hash()}
+    key = traffic_key(workload, cp)
+    d[key] = {"bytes_per_launch": int(round(fetch + write)), "fetch_bytes": int(round(fetch)),
+              "write_bytes": int(round(write)), "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4),
+              "kernel_source_sha": kernel_source_hash()}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     json.dump(d, open(TRAFFIC_FILE, "w"), indent=2, sort_keys=True)
-    print(json.dumps(d[workload]))
+    print(json.dumps(d[key]))
 
 
 class Flusher:
@@ -451,6 +456,8 @@ def main():
     ap.add_argument("--cp", default="auto")
     ap.add_argument("--o-dtype", default="bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the MFMA probe and the library GEMM (short profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--sweep", action="store_true",
                     help="forward latency over the pages' head settings and batch lengths (one JSON line each)")
@@ -462,7 +469,7 @@ def main():
                     help="store HBM bytes per launch from rocprofv3 counter CSVs (no GPU needed)")
     args = ap.parse_args()
     if args.ingest_counters:
-        ingest_counters(args.workload, *args.ingest_counters)
+        ingest_counters(args.workload, args.cp, *args.ingest_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the forward shards over (sequence, head-group) "
@@ -519,17 +526,18 @@ def main():
     alg = algorithmic_bytes(x)
     achieved = alg / (kern_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.workload),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(args.workload, args.cp),
                 "kernel": "gdn_fwd_main_kernel", "algorithmic_bytes_per_launch": alg,
                 "mean_launch_ms": round(kern_ms, 4)}
     flops = fwd_flops(x)
     tflops = flops / (kern_ms * 1e-3) / 1e12
-    peak_meas = measured_mfma_peak(dev)
-    gemm = measured_gemm_rate(dev)
+    peak_meas = None if args.no_mfma_probe else measured_mfma_peak(dev)
+    gemm = None if args.no_mfma_probe else measured_gemm_rate(dev)
     mfma = {"achieved": round(tflops, 1), "unit": "TFLOP/s", "algorithmic_flops_per_launch": flops,
             "peak_published": MFMA_BF16_PEAK_TFLOPS, "frac_published": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "peak_measured": round(peak_meas, 1), "frac_measured": round(tflops / peak_meas, 4) if peak_meas else None,
-            "library_gemm_8192": round(gemm, 1)}
+            "peak_measured": round(peak_meas, 1) if peak_meas else None,
+            "frac_measured": round(tflops / peak_meas, 4) if peak_meas else None,
+            "library_gemm_8192": round(gemm, 1) if gemm else None}
 
     cpu = None
     if not args.no_cpu_baseline:
