@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn.so")
-SOURCES = [os.path.join(CSRC, "gdn_api.hip"), os.path.join(CSRC, "gdn_fwd.hip"), os.path.join(CSRC, "gdn_bwd.hip")]
+SOURCES = [os.path.join(CSRC, "gdn_plan.cpp"), os.path.join(CSRC, "gdn_api.hip"), os.path.join(CSRC, "gdn_fwd.hip"),
+           os.path.join(CSRC, "gdn_bwd.hip")]
 # measurement probe for the benchmark (the sustained bf16 MFMA rate), kept out of libgdn
 PROBE_LIB = os.path.join(PKG, "libgdn_probe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "probe_mfma.hip")]
@@ -29,6 +30,7 @@ HIPCC_FLAGS = [
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 # Per-source code-generation options.  The forward's chunk loop runs one
 # workgroup per CU whatever the register count (its LDS decides that), so the
 # scheduler is asked for instruction-level parallelism instead of occupancy
@@ -61,8 +63,11 @@ def _link(sources, lib, verbose: bool) -> str:
         objs = []
         for src in sources:
             obj = os.path.join(td, os.path.basename(src) + ".o")
-            _run([hipcc()] + HIPCC_FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) +
-                 ["-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj], verbose)
+            if src.endswith(".cpp"):  # host-only C++ (the planner): the host compiler
+                _run(["g++"] + HOST_FLAGS + ["-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj], verbose)
+            else:
+                _run([hipcc()] + HIPCC_FLAGS + SOURCE_FLAGS.get(os.path.basename(src), []) +
+                     ["-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj], verbose)
             objs.append(obj)
         tmp = lib + ".tmp"
         _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)

@@ -1,9 +1,19 @@
-// Internal declarations shared by the host planner (gdn_api.cpp) and the
-// kernels (gdn_fwd.hip).  Not part of the public ABI.
+// Internal declarations shared by the host planner (gdn_plan.cpp) and the
+// kernels (gdn_fwd.hip, gdn_bwd.hip).  Not part of the public ABI.
 #pragma once
 
 #include <stddef.h>
 #include <stdint.h>
+
+#include "../../include/gdn.h"
+
+// Functions the planner and the kernels share; host-only when the planner is
+// built by the host compiler alone (the sanitizer tests).
+#if defined(__HIPCC__)
+#define GDN_HD __host__ __device__
+#else
+#define GDN_HD
+#endif
 
 namespace gdn {
 
@@ -29,10 +39,10 @@ struct SegEntry {
 
 // Integer segment rule, identical on host and device: a sequence of `len`
 // tokens has ceil(len / C) chunks and max(1, ceil(chunks / L)) segments.
-__host__ __device__ inline int32_t seq_chunks(int64_t len) {
+GDN_HD inline int32_t seq_chunks(int64_t len) {
     return (int32_t)((len + kChunk - 1) / kChunk);
 }
-__host__ __device__ inline int32_t seq_segments(int64_t len, int32_t L) {
+GDN_HD inline int32_t seq_segments(int64_t len, int32_t L) {
     const int32_t nt = seq_chunks(len);
     const int32_t s = (nt + L - 1) / L;
     return s > 0 ? s : 1;
@@ -97,5 +107,10 @@ int launch_chunk_cumsum(const float *g, float *out, int64_t B, int64_t T, int32_
                         const int32_t *cu, int32_t N, void *stream);
 int launch_bwd(const BwdParams &p, void *stream);
 const char *hip_error_text(int err);
+
+// Planner helpers for the allocation-free entry point (gdn_api.hip): the
+// thread's error message, and the workspace a forward call plans (validating it).
+int set_error(int status, const char *msg);
+int fwd_workspace_bytes(const gdn_fwd_desc *d, size_t *bytes);
 
 }  // namespace gdn

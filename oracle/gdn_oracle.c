@@ -203,7 +203,13 @@ int gdn_oracle_chunk_cumsum(int64_t B, int64_t T, int H, int chunk,
                             double *out)
 {
     if (B < 0 || T < 0 || H <= 0 || chunk <= 0 || N < 0) return -1;
-    if (!cu_seqlens && N != B) return -1;
+    if (cu_seqlens) {
+        if (B != 1 || cu_seqlens[0] != 0 || cu_seqlens[N] != T) return -1;
+        for (int n = 0; n < N; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+    } else if (N != B) {
+        return -1;
+    }
     for (int n = 0; n < N; ++n) {
         int64_t r0 = cu_seqlens ? cu_seqlens[n] : (int64_t)n * T;
         int64_t r1 = cu_seqlens ? cu_seqlens[n + 1] : (int64_t)(n + 1) * T;
