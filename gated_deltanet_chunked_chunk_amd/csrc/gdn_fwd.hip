@@ -1266,6 +1266,11 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             lds_barrier();
             if (chain) upd<PRE>(s, hacc, vd, b, lane_now());
             lds_barrier();
+            // h of chunk c + 1 (the state is final after the update) goes out
+            // before the K loads below, whose wait then also covers these
+            // stores, two steps later than a store after the Q H product
+            if (qnext && p.h_out)
+                store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
             // the K tile of chunk c is free since the H update: the loads of
             // chunk c + 2 have three steps to land (the compiler makes this
             // wave wait for them before its next transposing LDS read, in step 4)
@@ -1278,8 +1283,6 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
             lds_barrier();
             if (qnext) qhq<OF32>(s, hacc, qh, nb, p.scale, lane_now());
             else zero_tiles(qh);
-            if (qnext && p.h_out)
-                store_state8(hacc, p.h_out + ((int64_t)(cbase + c + 1) * p.Hv + j) * DK * DV, wave, lane_now());
         }
         if (PRE) {
             store_state8(hacc, (mwave ? p.ws_m : p.ws_s) + ((int64_t)seg * p.Hv + j) * DK * DV, sw, lane);
@@ -1533,11 +1536,13 @@ __global__ void __launch_bounds__(NT_COMB, 1) gdn_cp_combine_kernel(FwdParams p)
         const int rr = min(r, steps - 1);
         comb_load(X, p.ws_m + seg_off(rr), p.ws_s + seg_off(rr), wave, lane, col0);
     };
+    // LDS-only barriers: a __syncthreads would also wait for every global
+    // access in flight, the operand loads of the next two steps included
     auto step = [&](const CombRegs &X, int r) {
-        __syncthreads();  // H_start[r] complete in LDS
+        lds_barrier();  // H_start[r] complete in LDS
         f32x4 acc[2];
         comb_step(X, hH, hL, lane, acc);
-        __syncthreads();  // every wave has read H_start[r]
+        lds_barrier();  // every wave has read H_start[r]
         comb_put(acc, hH, hL, p.ws_h + seg_off(r + 1), wave, lane, col0);
     };
     load(C[0], 0);
