@@ -1486,7 +1486,9 @@ __device__ __forceinline__ void comb_put(const f32x4 (&x)[2], bf16 *hH, bf16 *hL
 }
 
 __global__ void __launch_bounds__(NT_COMB, 1) gdn_cp_combine_kernel(FwdParams p) {
-    __shared__ __attribute__((aligned(16))) bf16 hH[CB_COLS * CB_LD], hL[CB_COLS * CB_LD];
+    // H_start[r] by the parity of r: step r reads one pair and writes the
+    // other, so one barrier per step orders both hand-offs
+    __shared__ __attribute__((aligned(16))) bf16 hH[2][CB_COLS * CB_LD], hL[2][CB_COLS * CB_LD];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     constexpr int NCB = DV / CB_COLS;
@@ -1524,7 +1526,7 @@ __global__ void __launch_bounds__(NT_COMB, 1) gdn_cp_combine_kernel(FwdParams p)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
                 h0v[ct][jj] = src ? src[(int64_t)(16 * wave + 4 * g + jj) * DV + col0 + 16 * ct + m] : 0.f;
-        comb_put(h0v, hH, hL, nullptr, wave, lane, col0);
+        comb_put(h0v, hH[0], hL[0], nullptr, wave, lane, col0);
     }
     auto seg_off = [&](int r) { return ((int64_t)(seg0 + r) * p.Hv + j) * DK * DV; };
     const int steps = R - 1;  // step r makes H_start[r + 1]
@@ -1536,14 +1538,15 @@ __global__ void __launch_bounds__(NT_COMB, 1) gdn_cp_combine_kernel(FwdParams p)
         const int rr = min(r, steps - 1);
         comb_load(X, p.ws_m + seg_off(rr), p.ws_s + seg_off(rr), wave, lane, col0);
     };
-    // LDS-only barriers: a __syncthreads would also wait for every global
-    // access in flight, the operand loads of the next two steps included
+    // An LDS-only barrier: a __syncthreads would also wait for every global
+    // access in flight, the operand loads of the next two steps included.
+    // After it, H_start[r] is complete and every wave is done reading
+    // H_start[r - 1], whose pair takes H_start[r + 1].
     auto step = [&](const CombRegs &X, int r) {
-        lds_barrier();  // H_start[r] complete in LDS
+        lds_barrier();
         f32x4 acc[2];
-        comb_step(X, hH, hL, lane, acc);
-        lds_barrier();  // every wave has read H_start[r]
-        comb_put(acc, hH, hL, p.ws_h + seg_off(r + 1), wave, lane, col0);
+        comb_step(X, hH[r & 1], hL[r & 1], lane, acc);
+        comb_put(acc, hH[(r + 1) & 1], hL[(r + 1) & 1], p.ws_h + seg_off(r + 1), wave, lane, col0);
     };
     load(C[0], 0);
     load(C[1], 1);
