@@ -52,11 +52,26 @@ KERNEL_SOURCES = [os.path.join(ROOT, "gated_deltanet_chunked_chunk_amd", "csrc",
                   os.path.join(ROOT, "gated_deltanet_chunked_chunk_amd", "build.py")]  # its code-generation options
 
 
-def kernel_source_hash() -> str:
+# the training step's kernels: the forward (keeping h, A, v') and the backward
+BWD_SOURCES = KERNEL_SOURCES + [os.path.join(ROOT, "gated_deltanet_chunked_chunk_amd", "csrc", "gdn_bwd.hip")]
+# (role, kernel name) of each kernel of one training step whose HBM bytes are stored
+TRAINING_KERNELS = (("forward", "gdn_fwd_main_kernel"), ("reverse", "gdn_bwd_dh_kernel"),
+                    ("local", "gdn_bwd_local_kernel"))
+
+
+def is_training(workload: str) -> bool:
+    return workload.startswith("gdn_fwdbwd")
+
+
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in (sources or KERNEL_SOURCES):
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
+
+
+def workload_source_hash(workload: str) -> str:
+    return kernel_source_hash(BWD_SOURCES if is_training(workload) else None)
 
 
 def algorithmic_bytes(x) -> int:
@@ -100,15 +115,21 @@ def traffic_key(workload: str, cp: str) -> str:
     return workload if cp == "auto" else f"{workload}:{cp}"
 
 
-def stored_traffic(workload: str, cp: str = "auto"):
+def stored_traffic_entry(workload: str, cp: str = "auto"):
+    """The stored counter entry of a workload, or None once its kernels changed."""
     try:
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
     e = d.get(traffic_key(workload, cp))
-    if not e or e.get("kernel_source_sha") != kernel_source_hash():
+    if not e or e.get("kernel_source_sha") != workload_source_hash(workload):
         return None
-    return e.get("bytes_per_launch")
+    return e
+
+
+def stored_traffic(workload: str, cp: str = "auto"):
+    e = stored_traffic_entry(workload, cp)
+    return None if e is None else e.get("bytes_per_launch")
 
 
 def _counter_mean(csv_path: str, counter: str, kernel_substr: str) -> float:
@@ -127,16 +148,28 @@ def ingest_counters(workload: str, cp: str, fetch_csv: str, write_csv: str, copy
     gib = float(1 << 30)
     f_fac = gib / (_counter_mean(copy_fetch_csv, "FETCH_SIZE", "copyBuffer") * 1024.0)
     w_fac = gib / (_counter_mean(copy_write_csv, "WRITE_SIZE", "copyBuffer") * 1024.0)
-    fetch = _counter_mean(fetch_csv, "FETCH_SIZE", "gdn_fwd_main_kernel") * 1024.0 * f_fac
-    write = _counter_mean(write_csv, "WRITE_SIZE", "gdn_fwd_main_kernel") * 1024.0 * w_fac
     try:
         d = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         d = {}
     key = traffic_key(workload, cp)
-    d[key] = {"bytes_per_launch": int(round(fetch + write)), "fetch_bytes": int(round(fetch)),
-              "write_bytes": int(round(write)), "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4),
-              "kernel_source_sha": kernel_source_hash()}
+    if is_training(workload):
+        # per kernel of the step; bytes_per_launch is one backward call (reverse
+        # pass + chunk-local gradients), the forward with saved tensors apart
+        kern = {}
+        for role, name in TRAINING_KERNELS:
+            fetch = _counter_mean(fetch_csv, "FETCH_SIZE", name) * 1024.0 * f_fac
+            write = _counter_mean(write_csv, "WRITE_SIZE", name) * 1024.0 * w_fac
+            kern[role] = {"kernel": name, "fetch_bytes": int(round(fetch)), "write_bytes": int(round(write))}
+        bwd = sum(kern[r]["fetch_bytes"] + kern[r]["write_bytes"] for r in ("reverse", "local"))
+        d[key] = {"bytes_per_launch": int(bwd), "kernels": kern, "fetch_scale": round(f_fac, 4),
+                  "write_scale": round(w_fac, 4), "kernel_source_sha": workload_source_hash(workload)}
+    else:
+        fetch = _counter_mean(fetch_csv, "FETCH_SIZE", "gdn_fwd_main_kernel") * 1024.0 * f_fac
+        write = _counter_mean(write_csv, "WRITE_SIZE", "gdn_fwd_main_kernel") * 1024.0 * w_fac
+        d[key] = {"bytes_per_launch": int(round(fetch + write)), "fetch_bytes": int(round(fetch)),
+                  "write_bytes": int(round(write)), "fetch_scale": round(f_fac, 4), "write_scale": round(w_fac, 4),
+                  "kernel_source_sha": workload_source_hash(workload)}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     json.dump(d, open(TRAFFIC_FILE, "w"), indent=2, sort_keys=True)
     print(json.dumps(d[key]))
@@ -424,11 +457,17 @@ def fwd_bwd(args, w, x, dev):
     value = tokens / (ms_per_step * 1e-3)
     bwd_bytes, bwd_flops = bwd_algorithmic(x)
     achieved = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    tr = stored_traffic_entry(args.workload, args.cp)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None if tr is None else tr["bytes_per_launch"],
                 "kernel": "gdn_bwd (reverse pass + chunk-local gradients, key-head sums fused)",
                 "algorithmic_flops_per_launch": bwd_flops, "algorithmic_bytes_per_launch": bwd_bytes,
                 "mean_launch_ms": round(bwd_ms, 4), "forward_mean_launch_ms": round(fwd_ms, 4)}
+    if tr is not None:
+        # HBM bytes per call of each kernel of the step (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled)
+        roofline["traffic_by_kernel"] = {r: e["fetch_bytes"] + e["write_bytes"] for r, e in tr["kernels"].items()}
+        roofline["traffic_over_algorithmic"] = round(tr["bytes_per_launch"] / bwd_bytes, 2)
     cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(x, w, args.cpu_seconds)
     line = {
         "metric": "GDN fwd+bwd latency (ms) & tokens/s at 1x32768, 4/16 heads; % of MFMA roofline (backward)",
