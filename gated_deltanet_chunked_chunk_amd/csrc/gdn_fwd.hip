@@ -1334,7 +1334,14 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 if (ahead && pw < 2) dma_wait_but<1>();
                 else dma_wait();
                 lds_barrier();
-                if (prep && pw < 2) inv8_l1(s, ln, pw);
+                if (prep && pw < 2) {
+                    inv8_l1(s, ln, pw);
+                    // rows 0..31 of T are final once block 0's level 1 (this
+                    // step, wave 0's own writes) and level 0 (the last step)
+                    // are: wave 0 forms fragment 1 (rows 16..31) after its
+                    // level 1, wave 1 fragment 0 (rows 0..15, level 0 only)
+                    tdfrag(s, ln, 1 - pw, nb, with_tf);
+                }
                 if (pout && pw < 2) pfrag9(s, ln, pw + 1, nb, p.scale, decays_factor(s, ln));  // fragments 1, 2
                 if (pout && pw >= 2) {
                     const bool fact = decays_factor(s, ln);
@@ -1350,9 +1357,7 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                     L2Regs l2;
                     inv8_l2a(s, ln, pw, l2);
                     inv8_l2b(s, ln, pw, l2);
-                    // rows 0..31 (final since level 1): fragments 0 and 1;
                     // Z^T fragments 4 and 5 read only T's diagonal blocks
-                    if (pw < 2) tdfrag(s, ln, pw, nb, with_tf);
                     if (pout) {
                         f32x4 z[2] = {f32x4{}, f32x4{}};
                         if (pw < 2) {
