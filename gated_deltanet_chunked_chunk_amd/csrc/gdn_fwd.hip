@@ -693,7 +693,8 @@ __device__ __forceinline__ f32x4 trow4(const Smem8 &s, const int row, const int 
 //   s.tdf  diag(dec) T diag(beta)   (the decayed v' of the state update)
 //   s.tf   T diag(beta)             (v' itself, only when v' is stored)
 // Rows 0..31 of T are final after inverse level 1, rows 32..63 after level 2.
-__device__ __forceinline__ void tdfrag(Smem8 &s, const int lane, const int f, const int buf, const bool with_tf) {
+__device__ __forceinline__ void tdfrag(Smem8 &s, const int lane, const int f, const int buf, const bool with_tf,
+                                       const bool with_td = true) {
     const int m = lane & 15, g = lane >> 4;
     const int rt = frag_rt(f), ks = frag_ks(f);
     const int c0 = 32 * ks + 4 * g, row = 16 * rt + m;
@@ -710,9 +711,11 @@ __device__ __forceinline__ void tdfrag(Smem8 &s, const int lane, const int f, co
 #pragma unroll
     for (int e = 0; e < 8; ++e) td[e] = d * tb[e];
     bf16x8 hi, lo;
-    split8v(td, hi, lo);
-    s.tdf[0][f][lane] = hi;
-    s.tdf[1][f][lane] = lo;
+    if (with_td) {
+        split8v(td, hi, lo);
+        s.tdf[0][f][lane] = hi;
+        s.tdf[1][f][lane] = lo;
+    }
     if (with_tf) {
         split8v(tb, hi, lo);
         s.tf[0][f][lane] = hi;
@@ -1339,8 +1342,9 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                     // rows 0..31 of T are final once block 0's level 1 (this
                     // step, wave 0's own writes) and level 0 (the last step)
                     // are: wave 0 forms fragment 1 (rows 16..31) after its
-                    // level 1, wave 1 fragment 0 (rows 0..15, level 0 only)
-                    tdfrag(s, ln, 1 - pw, nb, with_tf);
+                    // level 1, wave 1 fragment 0 (rows 0..15, level 0 only);
+                    // their T diag(beta) copies (v' stored) wait for the next step
+                    tdfrag(s, ln, 1 - pw, nb, false);
                 }
                 if (pout && pw < 2) pfrag9(s, ln, pw + 1, nb, p.scale, decays_factor(s, ln));  // fragments 1, 2
                 if (pout && pw >= 2) {
@@ -1357,6 +1361,7 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                     L2Regs l2;
                     inv8_l2a(s, ln, pw, l2);
                     inv8_l2b(s, ln, pw, l2);
+                    if (with_tf && pw < 2) tdfrag(s, ln, 1 - pw, nb, true, false);
                     // Z^T fragments 4 and 5 read only T's diagonal blocks
                     if (pout) {
                         f32x4 z[2] = {f32x4{}, f32x4{}};
