@@ -129,12 +129,19 @@ __device__ __forceinline__ float sum64(float x) { return sum4g(sum16(x)); }
 // ---------------------------------------------------------------- rows of a chunk
 // Buffer resource over chunk c's rows of one sequence: rows past the sequence
 // end read as zeros and stores to them are dropped (hardware range check), so
-// a partial last chunk behaves as if padded with zero inputs.
+// a partial last chunk behaves as if padded with zero inputs.  Every caller
+// passes values that are the same in all lanes of the wave; taking them
+// through readfirstlane keeps the resource in scalar registers (otherwise
+// the compiler cannot prove them uniform and wraps every load in a loop over
+// the lanes' distinct resources).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void *base, unsigned stride, int c, int seq_len) {
     const int rows = min(max(seq_len - c * CH, 0), CH);
-    return __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(static_cast<const char *>(base) + (int64_t)c * CH * stride), (short)0,
-        (int)(rows * stride), 0x00020000);
+    const uint64_t a = reinterpret_cast<uint64_t>(static_cast<const char *>(base) + (int64_t)c * CH * stride);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)(rows * stride));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, n,
+                                             0x00020000);
 }
 
 __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, unsigned off) {
