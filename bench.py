@@ -519,8 +519,8 @@ def main():
         ingest_counters(args.workload, args.cp, *args.ingest_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the forward shards over (sequence, head-group) "
-              "with no communication; see the design notes); run with --gpus 1", file=sys.stderr)
+        print("bench.py: measures one GPU only (the forward shards over (sequence, head-group) "
+              "with no communication); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     if args.sweep:

@@ -348,7 +348,7 @@ const char *gdn_status_str(int status) {
     switch (status) {
         case GDN_OK: return "GDN_OK";
         case GDN_EINVAL: return "GDN_EINVAL: invalid argument";
-        case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED: not supported by this build";
+        case GDN_EUNSUPPORTED: return "GDN_EUNSUPPORTED: not supported by this library";
         case GDN_EWORKSPACE: return "GDN_EWORKSPACE: workspace too small or misaligned";
         case GDN_EHIP: return "GDN_EHIP: HIP runtime error";
         default: return "unknown gdn status";

@@ -55,7 +55,7 @@ extern "C" {
 typedef enum {
     GDN_OK = 0,
     GDN_EINVAL = -1,        /* bad shape, pointer, offsets or aliasing */
-    GDN_EUNSUPPORTED = -2,  /* valid request this build does not implement (K, V, chunk) */
+    GDN_EUNSUPPORTED = -2,  /* valid request this library does not implement (K, V, chunk) */
     GDN_EWORKSPACE = -3,    /* workspace missing or smaller than gdn_fwd_plan asked for */
     GDN_EHIP = -4           /* a HIP launch or query failed; message has the HIP text */
 } gdn_status;
@@ -87,7 +87,7 @@ typedef struct {
     int64_t B;                  /* batch rows (1 when cu_seqlens is used) */
     int64_t T;                  /* tokens per row (total packed tokens when varlen) */
     int32_t H_qk, H_v;          /* key/query heads, value heads; H_v % H_qk == 0 */
-    int32_t K, V;               /* head dims; this build supports K = V = 128 */
+    int32_t K, V;               /* head dims; this library supports K = V = 128 */
     int32_t num_seqs;           /* N: B, or len(cu_seqlens) - 1 when varlen */
     const int32_t *cu_seqlens_host; /* host copy of the offsets, required for varlen planning; NULL otherwise */
     float scale;                /* output scale (callers usually pass K^-1/2) */
