@@ -1381,9 +1381,14 @@ __device__ __forceinline__ void fwd_pass(const FwdParams &p) {
                 if (ahead) dma_tile<4>(s.v, in.v, in.vstride, c + 2, e.seq_len, pw, voffs);
                 after_gb = ahead ? ((astore ? 4 : 0) + NTILE4(pw)) : 0;
                 if (prep) {
-                    // rows 32..63: fragments 2..5
-                    tdfrag(s, ln, 2 + pw, nb, with_tf);
-                    if (pout && pw < 2) {
+                    // rows 32..63: fragments 2..5 on waves 2 and 3, while waves
+                    // 0 and 1 finish their Z^T fragments (the waves share SIMDs
+                    // with the state waves one to one, so each step's work is
+                    // spread evenly over them)
+                    if (pw >= 2) {
+                        tdfrag(s, ln, pw, nb, with_tf);
+                        tdfrag(s, ln, pw + 2, nb, with_tf);
+                    } else if (pout) {
                         zsum<1, 1>(s, ln, 2 + pw, nb, zacc);
                         zstore(s, ln, 2 + pw, zacc);
                     }
