@@ -126,6 +126,10 @@ __device__ __forceinline__ float sum4g(float x) {
 }
 __device__ __forceinline__ float sum64(float x) { return sum4g(sum16(x)); }
 
+// Workgroup barrier for LDS hand-offs only: the wave's own LDS operations
+// complete first, its global loads and stores stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---------------------------------------------------------------- rows of a chunk
 // Buffer resource over chunk c's rows of one sequence: rows past the sequence
 // end read as zeros and stores to them are dropped (hardware range check), so
@@ -150,6 +154,19 @@ __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, unsigned off) {
 __device__ __forceinline__ float ld4(__amdgpu_buffer_rsrc_t r, unsigned off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }
+
+// ---- direct HBM -> LDS loads (buffer_load ... lds: lane l of a wave writes
+// LDS bytes 16 l .. 16 l + 15 past the wave-uniform base).
+typedef __attribute__((address_space(3))) void lds_void;
+
+// The LDS address of a generic pointer into this workgroup's LDS (its low 32
+// bits), taken through integers rather than an address-space cast.
+__device__ __forceinline__ lds_void *lds_ptr(const void *p) {
+    return (lds_void *)(uintptr_t)(uint32_t)(uintptr_t)p;
+}
+
+// This wave's direct loads have landed in LDS (vmcnt(0); other counters untouched).
+__device__ __forceinline__ void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // 64 rows x PPR 16-byte pieces of HBM rows, held in registers between their
 // loads and their LDS stores (a dense tile), so that every load of a chunk is
@@ -389,6 +406,29 @@ __device__ __forceinline__ void st_split_t(bf16 *hi, bf16 *lo, int ld, int r0, i
 constexpr int LK = DK + 8;
 constexpr int L64 = CH + 8;
 
+// 64 rows of 256 bytes (bf16 x 128) through resource r (row stride `stride`
+// bytes) into an LDS tile with rows of LK elements (272 bytes = 17 pieces of
+// 16): 17 wave loads of 1 KB, spread over the 8 waves.  Lane l of load i
+// fills piece 64 i + l of the tile, i.e. row (64 i + l) / 17 and piece
+// (64 i + l) % 17; the pad piece reads past the resource and arrives as zeros,
+// as do rows the resource does not cover.
+constexpr int TSLOT = LK * 2 / 16;
+constexpr int TLOADS = CH * TSLOT / 64;
+static_assert(CH * TSLOT % 64 == 0, "a padded tile is a whole number of wave loads");
+__device__ __forceinline__ void dma_tile(bf16 *tile, const __amdgpu_buffer_rsrc_t r, const unsigned stride,
+                                         const int wave, const int lane) {
+#pragma unroll
+    for (int n = 0; n < (TLOADS + 7) / 8; ++n) {
+        const int i = wave + 8 * n;
+        if (i < TLOADS) {
+            const int slot = 64 * i + lane;
+            const int row = slot / TSLOT, piece = slot - TSLOT * row;
+            const unsigned off = piece < 16 ? (unsigned)row * stride + 16u * (unsigned)piece : 0x80000000u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(tile + 512 * i), 16, (int)off, 0, 0, 0);
+        }
+    }
+}
+
 struct __attribute__((aligned(16))) SmemLoc {
     bf16 k[CH * LK], q[CH * LK];
     bf16 ov[CH * LK];                 // dO, then V
@@ -437,11 +477,13 @@ __device__ __forceinline__ void load_tile_f32(Rows<DV * 4 / 16> &R, const float 
 
 // dq or dk of a key head = the sum over its v-heads: the workgroup runs them
 // one after another and every lane adds its four values to what it stored for
-// the previous v-head (fp32 workspace, the same lane and address); the last
-// v-head writes the output in its dtype.
-__device__ __forceinline__ void group_put(const BwdParams &p, float *ws, void *out, int64_t idx, f32x4 v, bool first,
-                                          bool last) {
-    if (!first) v += *reinterpret_cast<const f32x4 *>(ws + idx);
+// the previous v-head (fp32 workspace, the same lane and address: group_prev
+// reads that sum ahead of the products it is added to); the last v-head writes
+// the output in its dtype.
+__device__ __forceinline__ f32x4 group_prev(const float *ws, int64_t idx, bool first, bool valid) {
+    return (!first && valid) ? *reinterpret_cast<const f32x4 *>(ws + idx) : f32x4{};
+}
+__device__ __forceinline__ void group_put(const BwdParams &p, float *ws, void *out, int64_t idx, f32x4 v, bool last) {
     if (!last) {
         *reinterpret_cast<f32x4 *>(ws + idx) = v;
     } else if (p.grad_f32) {
@@ -456,11 +498,15 @@ __device__ __forceinline__ void group_put(const BwdParams &p, float *ws, void *o
 // computed transposed ((key dim, token) tiles): every product with h or dh'
 // then contracts over the value dim, and wave w owns key dims 16 w .. +15, so
 // it reads (and splits) its 16 rows of h and dh' once.  64 x 64 results: wave
-// w has row tile w / 2 and column tiles 2 (w % 2), 2 (w % 2) + 1.  Every HBM
-// read is issued at the start (the chunk's inputs, T, v' and dv' into LDS as
-// hi / lo pairs; the wave's h and dh' rows into registers during the first
-// products); fp32 intermediates are stored once as hi / lo bf16 pairs that
-// every consumer reads without further arithmetic.
+// w has row tile w / 2 and column tiles 2 (w % 2), 2 (w % 2) + 1.  A v-head's
+// HBM reads: V, T, v', g and beta at its start, through registers (T and v'
+// split into hi / lo pairs on the way to LDS); dO and the dv' planes straight
+// into LDS, and the wave's h rows into registers, during the previous v-head
+// (at the start for the first); the dh' rows after the tiles, in flight during
+// the first products.  fp32 intermediates are stored once as hi / lo bf16
+// pairs that every consumer reads without further arithmetic.  The barriers
+// hand over LDS only: no data passes between waves through global memory, so
+// loads issued for later phases stay in flight across them.
 __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     SmemLoc &s = *reinterpret_cast<SmemLoc *>(smem_raw);
@@ -490,6 +536,44 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         store_rows_ld(s.q, rq, LK, tid);
     }
 
+    // this wave's 16 rows of h and dh' of v-head jn (A operands of the
+    // transposed products), issued after the v-head's tiles; h of every v-head
+    // but the first is issued already at the previous v-head's third phase and
+    // waits in these registers (dh' as well would spill)
+    f32x4 hr[4][2];
+    bf16x8 dH[4], dL[4];  // dh' arrives already split
+    auto load_h = [&](const int jn, const int wv, const int l) {
+        const float *hn = p.h + ((int64_t)cg * p.Hv + jn) * DK * DV;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int off = (16 * wv + (l & 15)) * DV + 32 * kk + 8 * (l >> 4);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) hr[kk][hf] = *reinterpret_cast<const f32x4 *>(hn + off + 4 * hf);
+        }
+    };
+    auto load_d = [&](const int jn, const int wv, const int l) {
+        const bf16 *dn = reinterpret_cast<const bf16 *>(p.dh_ws) + ((int64_t)cg * p.Hv + jn) * 2 * DK * DV;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int off = (16 * wv + (l & 15)) * DV + 32 * kk + 8 * (l >> 4);
+            dH[kk] = *reinterpret_cast<const bf16x8 *>(dn + off);
+            dL[kk] = *reinterpret_cast<const bf16x8 *>(dn + DK * DV + off);
+        }
+    };
+
+    // dO of v-head jn -> ov and its dv' (hi / lo planes) -> eH / eL, straight
+    // into LDS: for the first v-head with its other loads, for each later one
+    // during the previous v-head's fifth phase (its third phase is the last to
+    // read those tiles; issued there, right after the h rows, the loads held
+    // up the fourth phase)
+    auto dma_do_dv = [&](const int jn, const int wv, const int l) {
+        const unsigned vs = (unsigned)p.Hv * DV * 2;
+        dma_tile(s.ov, chunk_rsrc(p.dO + (e.row0 * p.Hv + jn) * DV, vs, c, e.seq_len), vs, wv, l);
+        const bf16 *dvn = reinterpret_cast<const bf16 *>(p.dvp_ws) + ((int64_t)cg * p.Hv + jn) * 2 * CH * DV;
+        dma_tile(s.eH, chunk_rsrc(dvn, DV * 2, 0, CH), DV * 2, wv, l);
+        dma_tile(s.eL, chunk_rsrc(dvn + CH * DV, DV * 2, 0, CH), DV * 2, wv, l);
+    };
+
     // the key head's v-heads one after another; dq and dk add up across them
     for (int jj = 0; jj < p.group; ++jj) {
     // an opaque thread index per v-head: lane-derived addresses are computed
@@ -499,25 +583,20 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     const int lane = tid & 63, g4 = lane >> 4, r16 = lane & 15;
     const int j = iq * p.group + jj;
     const bool first = jj == 0, last = jj == p.group - 1;
-    const float *hc = p.h + ((int64_t)cg * p.Hv + j) * DK * DV;       // chunk-start state [d][v]
-    // gradient wrt the state after the chunk, as bf16 hi and lo planes [2][d][v]
-    const bf16 *dhc = reinterpret_cast<const bf16 *>(p.dh_ws) + ((int64_t)cg * p.Hv + j) * 2 * DK * DV;
-    const float *dvc = p.dvp_ws + ((int64_t)cg * p.Hv + j) * CH * DV; // dv' [i][v]
     const float *vnc = p.vn + ((int64_t)cg * p.Hv + j) * CH * DV;     // v'  [i][v]
     // this chunk's first row of the per-(token, v-head) outputs; a row of token t
     // lies t * Hv * 128 elements further (32-bit offsets inside a chunk)
     const int64_t row_c = (e.row0 + (int64_t)c * CH) * p.Hv + j;
 
+    if (first) dma_do_dv(j, wave, lane);
     Rows<DV * 2 / 16> rv;  // V, stored once dO is dead
     {
         const unsigned astride = (unsigned)p.Hv * CH * 4, gstride = (unsigned)p.Hv * 4;
-        Rows<DK * 2 / 16> rdo;
         Rows<CH * 4 / 16> rtm;
-        Rows<DV * 4 / 16> rn, rd;
-        load_rows(rdo, p.dO + (e.row0 * p.Hv + j) * DV, vstride, c, e.seq_len, tid);
+        Rows<DV * 4 / 16> rn;
+        load_rows(rv, p.v + (e.row0 * p.Hv + j) * DV, vstride, c, e.seq_len, tid);
         load_rows(rtm, p.A + (e.row0 * p.Hv + j) * CH, astride, c, e.seq_len, tid);
         load_tile_f32(rn, vnc, tid);
-        load_tile_f32(rd, dvc, tid);
         float g = 0.f, b = 0.f;
         if (tid < 64) {
             const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(p.g + e.row0 * p.Hv + j, gstride, c, e.seq_len);
@@ -525,11 +604,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             g = ld4(rg, (unsigned)tid * gstride);
             b = ld4(rb, (unsigned)tid * gstride);
         }
-        load_rows(rv, p.v + (e.row0 * p.Hv + j) * DV, vstride, c, e.seq_len, tid);
-        store_rows_ld(s.ov, rdo, LK, tid);
         store_rows_split(s.tH, s.tL, rtm, L64, tid);
         store_rows_split(s.nH, s.nL, rn, LK, tid);
-        store_rows_split(s.eH, s.eL, rd, LK, tid);
         if (tid < 64) {
             const float G = prefix64(g);
             s.G[tid] = G;
@@ -541,20 +617,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             (&s.dbp[0][0])[x] = 0.f;
         }
     }
-    __syncthreads();
-
-    // this wave's 16 rows of h and dh' (A operands of the transposed products),
-    // in flight while the first products run
-    f32x4 hr[4][2];
-    bf16x8 dH[4], dL[4];  // dh' arrives already split
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int off = (16 * wave + r16) * DV + 32 * kk + 8 * g4;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) hr[kk][hf] = *reinterpret_cast<const f32x4 *>(hc + off + 4 * hf);
-        dH[kk] = *reinterpret_cast<const bf16x8 *>(dhc + off);
-        dL[kk] = *reinterpret_cast<const bf16x8 *>(dhc + DK * DV + off);
-    }
+    dma_wait();  // this wave's direct loads of dO and dv' have landed
+    lds_barrier();
+    if (first) load_h(j, wave, lane);
+    load_d(j, wave, lane);
 
     float *dGw = s.dGp[wave];
     float *dbw = s.dbp[wave];
@@ -590,7 +656,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         if (g4 == 0) dGw[16 * ct + r16] -= colsum;
         st_split(s.pH, s.pL, L64, 16 * rt64, 16 * ct, dpm, lane);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 2: transposed dk, dq, dW over this wave's key dims 16 w ..
     f32x4 dkt[4];
@@ -641,6 +707,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         if (lane == 0) dGw[CH - 1] += lastacc + gl * dot;
     }
     // dq: scale gamma_i (h dO^T) + K^T dPm^T;  gate term of O (inter); stored
+    f32x4 qprev[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+        qprev[ct] = group_prev(p.dq_ws, rowq_c * DK + (unsigned)(16 * ct + r16) * qstride + 16 * wave + 4 * g4, first,
+                               16 * ct + r16 < rows_valid);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
         f32x4 t1 = f32x4{}, kq = f32x4{};
@@ -662,10 +733,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         qsum = sum4g(qsum);
         if (g4 == 0) dGw[col] += sg * qsum;
         if (col < rows_valid)
-            group_put(p, p.dq_ws, p.dq, rowq_c * DK + (unsigned)col * qstride + 16 * wave + 4 * g4, sg * t1 + kq,
-                      first, last);
+            group_put(p, p.dq_ws, p.dq, rowq_c * DK + (unsigned)col * qstride + 16 * wave + 4 * g4,
+                      sg * t1 + kq + qprev[ct], last);
     }
-    __syncthreads();  // v' and dO are dead: their tiles take dW and V
+    lds_barrier();  // v' and dO are dead: their tiles take dW and V
 
     // dW = -(h dv'^T)^T -> n [token][key dim];  V -> ov
 #pragma unroll
@@ -678,7 +749,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         st_split_t(s.nH, s.nL, LK, 16 * wave, 16 * ct, -tw, lane);
     }
     store_rows_ld(s.ov, rv, LK, tid);
-    __syncthreads();
+    lds_barrier();
+    if (!last) load_h(j + 1, wave, lane);
 
     // ---- 3: dT -> p;  dK, dbeta, dG terms of W;  dV and the dbeta term of U
 #pragma unroll
@@ -757,7 +829,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 4: Y = T^T dT -> n (as [64][64])
 #pragma unroll
@@ -770,7 +842,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
                         fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane), fr_tr(s.pL + 16 * ct, L64, 32 * kk, lane));
         st_split(s.nH, s.nL, L64, 16 * rt64, 16 * ct, acc, lane);
     }
-    __syncthreads();
+    lds_barrier();
+
+    if (!last) dma_do_dv(j + 1, wave, lane);  // ov, eH and eL are dead from here on
 
     // ---- 5: dA~ = -(Y T^T) strictly lower;  M = dA~ o beta_i Gamma_is -> p;  gate / beta terms of A~
 #pragma unroll
@@ -812,9 +886,14 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         if (g4 == 0) dGw[16 * ct + r16] -= colsum;
         st_split(s.pH, s.pL, L64, 16 * rt64, 16 * ct, m, lane);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 6: dK += M K + M^T K (transposed: K^T M^T + K^T M); store dk of this v-head
+    f32x4 kprev[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+        kprev[ct] = group_prev(p.dk_ws, rowq_c * DK + (unsigned)(16 * ct + r16) * qstride + 16 * wave + 4 * g4, first,
+                              16 * ct + r16 < rows_valid);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
@@ -827,10 +906,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         }
         const int tok = 16 * ct + r16;
         if (tok < rows_valid)
-            group_put(p, p.dk_ws, p.dk, rowq_c * DK + (unsigned)tok * qstride + 16 * wave + 4 * g4, dkt[ct], first,
+            group_put(p, p.dk_ws, p.dk, rowq_c * DK + (unsigned)tok * qstride + 16 * wave + 4 * g4, dkt[ct] + kprev[ct],
                       last);
     }
-    __syncthreads();
+    lds_barrier();
 
     // dg = reverse in-chunk cumsum of dG; dbeta
     if (wave == 0) {
@@ -847,7 +926,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             p.dbeta[off] = db;
         }
     }
-    __syncthreads();  // the next v-head's tiles overwrite LDS
+    lds_barrier();  // the next v-head's tiles overwrite LDS
     }
 }
 
@@ -1096,11 +1175,6 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
                 x[jj] = p.scale * a1[jj] + __expf(s.G[CH - 1] - s.G[i]) * a2[jj];
             }
             st_split(s.aH, s.aL, L64, 16 * rt, 16 * ct, x, lane);
-            if (own) {
-                float *dst = p.dvp_ws + ((int64_t)(cbase + c) * p.Hv + j) * CH * DV + half * HVC;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * rt + 4 * g4 + jj) * DV + 16 * ct + r16] = x[jj];
-            }
         }
         f32x4 u[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
         if (!mmap) {
@@ -1117,6 +1191,19 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
         }
         __syncthreads();
 
+        if (own) {
+            // dv' of chunk c -> HBM as two bf16 planes [token][v] (hi, lo): the
+            // chunk-local kernel's split operands, 16 bytes per thread and plane
+            bf16 *dst = reinterpret_cast<bf16 *>(p.dvp_ws) + ((int64_t)(cbase + c) * p.Hv + j) * 2 * CH * DV + half * HVC;
+#pragma unroll
+            for (int i = 0; i < CH * HVC / 8 / NT; ++i) {
+                const int pc = tid + i * NT;
+                const int row = pc / (HVC / 8), col = 8 * (pc % (HVC / 8));
+                *reinterpret_cast<bf16x8 *>(dst + row * DV + col) = *reinterpret_cast<const bf16x8 *>(&s.aH[row * L64 + col]);
+                *reinterpret_cast<bf16x8 *>(dst + CH * DV + row * DV + col) =
+                    *reinterpret_cast<const bf16x8 *>(&s.aL[row * L64 + col]);
+            }
+        }
         // dh <- gamma_last dh + scale Q^T diag(gamma) dO - W^T dv'
         {
 #pragma unroll

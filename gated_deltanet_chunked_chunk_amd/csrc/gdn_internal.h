@@ -82,7 +82,7 @@ struct BwdParams {
     const float *vn;                 // [total_chunks][Hv][64][V] v' of every chunk (forward's v_new)
     const float *dht;                // [N][Hv][K][V] or nullptr
     float *dh_ws;                    // [total_chunks][Hv][2][K][V] bf16 (hi, lo): gradient wrt the state after each chunk
-    float *dvp_ws;                   // [total_chunks][Hv][64][V] dv' (all 64 rows of every chunk)
+    float *dvp_ws;                   // [total_chunks][Hv][2][64][V] bf16 (hi, lo): dv' (all 64 rows of every chunk)
     float *dq_ws, *dk_ws;            // [rows][H_qk][K] fp32 running sums of dq, dk over a key head's v-heads
     void *dq, *dk, *dv;              // bf16 or fp32 per grad_f32
     float *dg, *dbeta;               // [rows][Hv]
