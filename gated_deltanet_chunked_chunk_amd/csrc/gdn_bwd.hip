@@ -28,9 +28,10 @@
 //
 // Kernels: gdn_bwd_dh_kernel (reverse pass, one workgroup per (segment,
 // v-head, half of V): the V columns of dh are independent) and
-// gdn_bwd_local_kernel (one workgroup per (chunk, key head), running the key
-// head's v-heads in turn, so that dq and dk of the key head, the sums over its
-// v-heads, add up in the workgroup).  h and T come from the forward (its
+// gdn_bwd_local_kernel (persistent workgroups, one per compute unit, taking
+// (chunk, key head) items in turn and running each key head's v-heads one
+// after another, so that dq and dk of the key head, the sums over its v-heads,
+// add up in the workgroup).  h and T come from the forward (its
 // low-level outputs); dh' and dv' of every chunk go through the workspace.
 //
 // Products: v_mfma_f32_16x16x32_bf16 on 16 x 16 output tiles.  Operands that
@@ -493,8 +494,46 @@ __device__ __forceinline__ void group_put(const BwdParams &p, float *ws, void *o
     }
 }
 
-// One workgroup per (chunk, key head), running the key head's v-heads in turn.
-// The key-dim results dq, dk and dW are
+// A work item of the chunk-local kernel: one (chunk, key head) pair.
+struct LocItem {
+    Where e;
+    int c, cg, iq;   // chunk within its sequence, among all chunks, key head
+    int64_t rowq_c;  // the chunk's first row of the key-head sums
+    bool ok;         // false: an empty sequence's entry, or past the last item
+};
+
+__device__ __forceinline__ LocItem loc_item(const BwdParams &p, const int it, const int lane) {
+    LocItem r;
+    r.ok = false;
+    const int ent = it / p.Hqk;
+    r.iq = it - ent * p.Hqk;
+    if (ent >= p.num_chunk_entries) return r;
+    r.e = find_segment(p.cu, p.N, p.T, 1, ent, lane);
+    if (r.e.n < 0 || r.e.c_count == 0) return r;
+    r.c = r.e.c_begin;
+    r.cg = seq_chunk_base(p.cu, p.T, r.e.n, lane) + r.c;
+    r.rowq_c = (r.e.row0 + (int64_t)r.c * CH) * p.Hqk + r.iq;
+    r.ok = true;
+    return r;
+}
+
+// The first item at or after `it` in this workgroup's share (it, it + gridDim.x, ...)
+// that has rows; `it` is left at that item.
+__device__ __forceinline__ LocItem next_item(const BwdParams &p, int &it, const int lane) {
+    const int n_items = p.num_chunk_entries * p.Hqk;
+    for (; it < n_items; it += (int)gridDim.x) {
+        const LocItem r = loc_item(p, it, lane);
+        if (r.ok) return r;
+    }
+    LocItem r;
+    r.ok = false;
+    return r;
+}
+
+// Persistent workgroups (one per compute unit) take the (chunk, key head)
+// items b, b + gridDim.x, ... and run each key head's v-heads in turn; the
+// next item's K, Q and first-v-head loads go out during the current item's
+// last v-head.  The key-dim results dq, dk and dW are
 // computed transposed ((key dim, token) tiles): every product with h or dh'
 // then contracts over the value dim, and wave w owns key dims 16 w .. +15, so
 // it reads (and splits) its 16 rows of h and dh' once.  64 x 64 results: wave
@@ -511,30 +550,26 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     SmemLoc &s = *reinterpret_cast<SmemLoc *>(smem_raw);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int ent = blockIdx.x / p.Hqk;
-    const int iq = blockIdx.x - ent * p.Hqk;
-    if (ent >= p.num_chunk_entries) return;
-    const Where e = find_segment(p.cu, p.N, p.T, 1, ent, threadIdx.x & 63);
-    if (e.n < 0 || e.c_count == 0) return;
-    const int c = e.c_begin;
-    const int cg = seq_chunk_base(p.cu, p.T, e.n, threadIdx.x & 63) + c;
+    const int lane0 = threadIdx.x & 63;
+    // persistent: workgroup b takes items b, b + gridDim.x, ... in turn, and the
+    // next item's first loads go out during the current item's last v-head
+    int it = blockIdx.x;
+    LocItem cur = next_item(p, it, lane0);
+    if (!cur.ok) return;
     const unsigned vstride = (unsigned)p.Hv * DV * 2;
     const unsigned tstride = (unsigned)p.Hv * DV;   // per-v-head outputs (dv): elements per token row
     const unsigned qstride = (unsigned)p.Hqk * DK;  // per-key-head sums (dq, dk): elements per token row
-    // this chunk's first row of the key-head sums, in the workspace and the output alike
-    const int64_t rowq_c = (e.row0 + (int64_t)c * CH) * p.Hqk + iq;
+    const unsigned kstride = (unsigned)p.Hqk * DK * 2;
 
-    // K and Q belong to the key head: loaded once into LDS, where they stay for
-    // all of its v-heads (the first barrier below publishes them)
-    {
-        const unsigned kstride = (unsigned)p.Hqk * DK * 2;
-        const int tid = threadIdx.x;
-        Rows<DK * 2 / 16> rk, rq;
-        load_rows(rk, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
-        load_rows(rq, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
-        store_rows_ld(s.k, rk, LK, tid);
-        store_rows_ld(s.q, rq, LK, tid);
-    }
+    // K and Q of item I straight into LDS, where they stay for all of its v-heads
+    auto dma_k = [&](const LocItem &I, const int wv, const int l) {
+        dma_tile(s.k, chunk_rsrc(p.k + (I.e.row0 * p.Hqk + I.iq) * DK, kstride, I.c, I.e.seq_len), kstride, wv, l);
+    };
+    auto dma_q = [&](const LocItem &I, const int wv, const int l) {
+        dma_tile(s.q, chunk_rsrc(p.q + (I.e.row0 * p.Hqk + I.iq) * DK, kstride, I.c, I.e.seq_len), kstride, wv, l);
+    };
+    dma_k(cur, wave, lane0);
+    dma_q(cur, wave, lane0);
 
     // this wave's 16 rows of h and dh' of v-head jn (A operands of the
     // transposed products), issued after the v-head's tiles; h of every v-head
@@ -542,8 +577,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     // waits in these registers (dh' as well would spill)
     f32x4 hr[4][2];
     bf16x8 dH[4], dL[4];  // dh' arrives already split
-    auto load_h = [&](const int jn, const int wv, const int l) {
-        const float *hn = p.h + ((int64_t)cg * p.Hv + jn) * DK * DV;
+    auto load_h = [&](const LocItem &I, const int jn, const int wv, const int l) {
+        const float *hn = p.h + ((int64_t)I.cg * p.Hv + jn) * DK * DV;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int off = (16 * wv + (l & 15)) * DV + 32 * kk + 8 * (l >> 4);
@@ -551,8 +586,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             for (int hf = 0; hf < 2; ++hf) hr[kk][hf] = *reinterpret_cast<const f32x4 *>(hn + off + 4 * hf);
         }
     };
-    auto load_d = [&](const int jn, const int wv, const int l) {
-        const bf16 *dn = reinterpret_cast<const bf16 *>(p.dh_ws) + ((int64_t)cg * p.Hv + jn) * 2 * DK * DV;
+    auto load_d = [&](const LocItem &I, const int jn, const int wv, const int l) {
+        const bf16 *dn = reinterpret_cast<const bf16 *>(p.dh_ws) + ((int64_t)I.cg * p.Hv + jn) * 2 * DK * DV;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int off = (16 * wv + (l & 15)) * DV + 32 * kk + 8 * (l >> 4);
@@ -566,13 +601,21 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     // during the previous v-head's fifth phase (its third phase is the last to
     // read those tiles; issued there, right after the h rows, the loads held
     // up the fourth phase)
-    auto dma_do_dv = [&](const int jn, const int wv, const int l) {
-        const unsigned vs = (unsigned)p.Hv * DV * 2;
-        dma_tile(s.ov, chunk_rsrc(p.dO + (e.row0 * p.Hv + jn) * DV, vs, c, e.seq_len), vs, wv, l);
-        const bf16 *dvn = reinterpret_cast<const bf16 *>(p.dvp_ws) + ((int64_t)cg * p.Hv + jn) * 2 * CH * DV;
+    auto dma_do_dv = [&](const LocItem &I, const int jn, const int wv, const int l) {
+        dma_tile(s.ov, chunk_rsrc(p.dO + (I.e.row0 * p.Hv + jn) * DV, vstride, I.c, I.e.seq_len), vstride, wv, l);
+        const bf16 *dvn = reinterpret_cast<const bf16 *>(p.dvp_ws) + ((int64_t)I.cg * p.Hv + jn) * 2 * CH * DV;
         dma_tile(s.eH, chunk_rsrc(dvn, DV * 2, 0, CH), DV * 2, wv, l);
         dma_tile(s.eL, chunk_rsrc(dvn + CH * DV, DV * 2, 0, CH), DV * 2, wv, l);
     };
+
+    bool fresh = true;  // the workgroup's first item: nothing was loaded ahead for it
+    while (true) {
+    const Where e = cur.e;
+    const int c = cur.c, cg = cur.cg, iq = cur.iq;
+    const int64_t rowq_c = cur.rowq_c;
+    int it_nx = it;  // the next item, found at the start of the last v-head
+    LocItem nx;
+    nx.ok = false;
 
     // the key head's v-heads one after another; dq and dk add up across them
     for (int jj = 0; jj < p.group; ++jj) {
@@ -583,12 +626,17 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     const int lane = tid & 63, g4 = lane >> 4, r16 = lane & 15;
     const int j = iq * p.group + jj;
     const bool first = jj == 0, last = jj == p.group - 1;
+    if (last) {
+        it_nx = it + (int)gridDim.x;
+        nx = next_item(p, it_nx, lane0);
+    }
+    const int j_nx = nx.iq * p.group;  // the next item's first v-head
     const float *vnc = p.vn + ((int64_t)cg * p.Hv + j) * CH * DV;     // v'  [i][v]
     // this chunk's first row of the per-(token, v-head) outputs; a row of token t
     // lies t * Hv * 128 elements further (32-bit offsets inside a chunk)
     const int64_t row_c = (e.row0 + (int64_t)c * CH) * p.Hv + j;
 
-    if (first) dma_do_dv(j, wave, lane);
+    if (first && fresh) dma_do_dv(cur, j, wave, lane);
     Rows<DV * 2 / 16> rv;  // V, stored once dO is dead
     {
         const unsigned astride = (unsigned)p.Hv * CH * 4, gstride = (unsigned)p.Hv * 4;
@@ -617,10 +665,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             (&s.dbp[0][0])[x] = 0.f;
         }
     }
-    dma_wait();  // this wave's direct loads of dO and dv' have landed
+    dma_wait();  // this wave's direct loads (dO, dv', for a new item K and Q) have landed
     lds_barrier();
-    if (first) load_h(j, wave, lane);
-    load_d(j, wave, lane);
+    if (first && fresh) load_h(cur, j, wave, lane);
+    load_d(cur, j, wave, lane);
 
     float *dGw = s.dGp[wave];
     float *dbw = s.dbp[wave];
@@ -750,7 +798,10 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     }
     store_rows_ld(s.ov, rv, LK, tid);
     lds_barrier();
-    if (!last) load_h(j + 1, wave, lane);
+    if (!last)
+        load_h(cur, j + 1, wave, lane);
+    else if (nx.ok)
+        load_h(nx, j_nx, wave, lane);
 
     // ---- 3: dT -> p;  dK, dbeta, dG terms of W;  dV and the dbeta term of U
 #pragma unroll
@@ -844,7 +895,13 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     }
     lds_barrier();
 
-    if (!last) dma_do_dv(j + 1, wave, lane);  // ov, eH and eL are dead from here on
+    // ov, eH and eL are dead from here on, and q since the second phase
+    if (!last) {
+        dma_do_dv(cur, j + 1, wave, lane);
+    } else if (nx.ok) {
+        dma_do_dv(nx, j_nx, wave, lane);
+        dma_q(nx, wave, lane);
+    }
 
     // ---- 5: dA~ = -(Y T^T) strictly lower;  M = dA~ o beta_i Gamma_is -> p;  gate / beta terms of A~
 #pragma unroll
@@ -910,6 +967,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
                       last);
     }
     lds_barrier();
+    if (last && nx.ok) dma_k(nx, wave, lane);  // k was last read in the sixth phase
 
     // dg = reverse in-chunk cumsum of dG; dbeta
     if (wave == 0) {
@@ -927,6 +985,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         }
     }
     lds_barrier();  // the next v-head's tiles overwrite LDS
+    }
+    if (!nx.ok) break;
+    cur = nx;
+    it = it_nx;
+    fresh = false;
     }
 }
 
@@ -1346,7 +1409,15 @@ int launch_bwd(const BwdParams &p, void *stream) {
         if (err != hipSuccess) return (int)err;
     }
     if (p.num_chunk_entries > 0 && p.rows > 0) {
-        hipLaunchKernelGGL(bwdk::gdn_bwd_local_kernel, dim3((unsigned)(p.num_chunk_entries * p.Hqk)), dim3(bwdk::NT),
+        // one persistent workgroup per compute unit (its LDS allows one), at most one per item
+        int dev = 0, cus = 0;
+        err = hipGetDevice(&dev);
+        if (err != hipSuccess) return (int)err;
+        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return (int)err;
+        const int64_t items = (int64_t)p.num_chunk_entries * p.Hqk;
+        const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(items, cus));
+        hipLaunchKernelGGL(bwdk::gdn_bwd_local_kernel, dim3(grid), dim3(bwdk::NT),
                            sizeof(bwdk::SmemLoc), st, p);
         err = hipGetLastError();
         if (err != hipSuccess) return (int)err;
