@@ -124,6 +124,26 @@ def test_bwd_varlen_with_empty_and_one_token_sequences():
     _check("varlen/off", got, _oracle(x))
 
 
+@pytest.mark.parametrize("case", ["ungrouped", "varlen"])
+def test_bwd_more_items_than_workgroups(case):
+    # The chunk-local kernel runs one persistent workgroup per compute unit over
+    # (chunk, key head) items; with more items than workgroups each one loads
+    # its next item's tiles during the current item's last v-head (here every
+    # v-head is the last: one v-head per key head), and skips the items of
+    # empty sequences on the way.
+    if case == "ungrouped":
+        w = dataclasses.replace(BASE, name="b9", seed=49, B=1, T=4096, H_qk=8, H_v=8)
+        x = _grad_inputs(w)
+    else:
+        w = dataclasses.replace(BASE, name="b10", seed=50, B=1, T=0, H_qk=8, H_v=8)
+        x = _grad_inputs(w, lengths=[1000, 0, 3000, 0, 0, 64, 1])
+    items = sum(-(-int(n) // 64) or 1 for n in np.diff(x["cu_seqlens"].numpy())) if x["cu_seqlens"] is not None \
+        else x["q"].shape[1] // 64
+    assert items * w.H_qk > torch.cuda.get_device_properties(0).multi_processor_count
+    got = _run(x, cp="warmup", cp_segment_chunks=8, grad_dtype="f32")
+    _check(f"items/{case}", got, _oracle(x))
+
+
 def test_bwd_no_state_gradients_and_bf16_grads():
     w = dataclasses.replace(BASE, name="b4", seed=44, B=1, T=333, H_qk=1, H_v=2, h0_std=None)
     x = _grad_inputs(w)
