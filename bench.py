@@ -452,7 +452,7 @@ def fwd_bwd(args, w, x, dev):
                                    initial_state=x["initial_state"], d_final_state=x["dht"], cp=args.cp)
     tokens = w.B * w.T
     flush = Flusher(dev)
-    flush.settle(call)
+    flush.settle(call, seconds=args.settle_seconds)
     for _ in range(args.warmup):
         flush()
         call()
@@ -506,6 +506,8 @@ def main():
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the MFMA probe and the library GEMM (short profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--settle-seconds", type=float, default=SETTLE_S,
+                    help="untimed run of the measured call before the warm-up steps (clock settle)")
     ap.add_argument("--sweep", action="store_true",
                     help="forward latency over the pages' head settings and batch lengths (one JSON line each)")
     ap.add_argument("--sweep-bwd", action="store_true",
@@ -558,7 +560,7 @@ def main():
     tokens = w.B * w.T if x["cu_seqlens"] is None else int(x["cu_seqlens"][-1])
 
     flush = Flusher(dev)
-    flush.settle(call)
+    flush.settle(call, seconds=args.settle_seconds)
     for _ in range(args.warmup):
         flush()
         call()
