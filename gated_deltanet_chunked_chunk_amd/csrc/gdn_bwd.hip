@@ -677,18 +677,24 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     const float gl = s.gam[CH - 1];
 
     // ---- 1: dPm = scale (dO v'^T) o Gamma (s <= i) -> p;  gate terms of P
+    // both column tiles per k step: the dO and Q rows of row tile rt64 are read once
+    f32x4 acc1[2] = {f32x4{}, f32x4{}}, qk1[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 od = fr_row<false>(s.ov + 16 * rt64 * LK, LK, 32 * kk, lane);
+        const bf16x8 qr = fr_row<false>(s.q + 16 * rt64 * LK, LK, 32 * kk, lane);
+#pragma unroll
+        for (int ct2 = 0; ct2 < 2; ++ct2) {
+            const int ct = 2 * (wave & 1) + ct2;
+            acc1[ct2] = mm_ep(acc1[ct2], od, fr_row<false>(s.nH + 16 * ct * LK, LK, 32 * kk, lane),
+                              fr_row<false>(s.nL + 16 * ct * LK, LK, 32 * kk, lane));
+            qk1[ct2] = mfma(qr, fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane), qk1[ct2]);
+        }
+    }
 #pragma unroll
     for (int ct2 = 0; ct2 < 2; ++ct2) {
         const int ct = 2 * (wave & 1) + ct2;
-        f32x4 acc = f32x4{}, qk = f32x4{};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            acc = mm_ep(acc, fr_row<false>(s.ov + 16 * rt64 * LK, LK, 32 * kk, lane),
-                        fr_row<false>(s.nH + 16 * ct * LK, LK, 32 * kk, lane),
-                        fr_row<false>(s.nL + 16 * ct * LK, LK, 32 * kk, lane));
-            qk = mfma(fr_row<false>(s.q + 16 * rt64 * LK, LK, 32 * kk, lane),
-                      fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane), qk);
-        }
+        const f32x4 acc = acc1[ct2], qk = qk1[ct2];
         f32x4 dpm;
         float colsum = 0.f;
 #pragma unroll
@@ -725,6 +731,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         }
         // dk: rl_s (dh' v'^T) + Q^T dPm;  gate terms of h'
         float lastacc = 0.f;
+        bf16x8 qa[2];  // this wave's rows of Q^T, read once for the four column tiles
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) qa[kk] = fr_tr(s.q + 16 * wave, LK, 32 * kk, lane);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             f32x4 t2 = f32x4{}, qp = f32x4{};
@@ -734,7 +743,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
                            fr_row<false>(s.nL + 16 * ct * LK, LK, 32 * kk, lane));
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                qp = mm_ep(qp, fr_tr(s.q + 16 * wave, LK, 32 * kk, lane), fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane),
+                qp = mm_ep(qp, qa[kk], fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane),
                            fr_tr(s.pL + 16 * ct, L64, 32 * kk, lane));
             const int col = 16 * ct + r16;  // key token s
             const float rl = __expf(s.G[CH - 1] - s.G[col]);
@@ -760,6 +769,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     for (int ct = 0; ct < 4; ++ct)
         qprev[ct] = group_prev(p.dq_ws, rowq_c * DK + (unsigned)(16 * ct + r16) * qstride + 16 * wave + 4 * g4, first,
                                16 * ct + r16 < rows_valid);
+    bf16x8 ka[2];  // this wave's rows of K^T, read once for the four column tiles
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) ka[kk] = fr_tr(s.k + 16 * wave, LK, 32 * kk, lane);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
         f32x4 t1 = f32x4{}, kq = f32x4{};
@@ -768,7 +780,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             t1 = mm_pe(t1, hH[kk], hL[kk], fr_row<false>(s.ov + 16 * ct * LK, LK, 32 * kk, lane));
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-            kq = mm_ep(kq, fr_tr(s.k + 16 * wave, LK, 32 * kk, lane), fr_row<true>(s.pH + 16 * ct * L64, L64, 32 * kk, lane),
+            kq = mm_ep(kq, ka[kk], fr_row<true>(s.pH + 16 * ct * L64, L64, 32 * kk, lane),
                        fr_row<true>(s.pL + 16 * ct * L64, L64, 32 * kk, lane));
         const int col = 16 * ct + r16;  // query token i
         const float sg = p.scale * s.gam[col];
@@ -804,74 +816,84 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         load_h(nx, j_nx, wave, lane);
 
     // ---- 3: dT -> p;  dK, dbeta, dG terms of W;  dV and the dbeta term of U
+    // both column tiles per k step: the dW and dv' rows of row tile rt64 are read once
+    f32x4 a1t[2] = {f32x4{}, f32x4{}}, a2t[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 nh = fr_row<false>(s.nH + 16 * rt64 * LK, LK, 32 * kk, lane);
+        const bf16x8 nl = fr_row<false>(s.nL + 16 * rt64 * LK, LK, 32 * kk, lane);
+        const bf16x8 eh = fr_row<false>(s.eH + 16 * rt64 * LK, LK, 32 * kk, lane);
+        const bf16x8 el = fr_row<false>(s.eL + 16 * rt64 * LK, LK, 32 * kk, lane);
+#pragma unroll
+        for (int ct2 = 0; ct2 < 2; ++ct2) {
+            const int ct = 2 * (wave & 1) + ct2;
+            a1t[ct2] = mm_pe(a1t[ct2], nh, nl, fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane));
+            a2t[ct2] = mm_pe(a2t[ct2], eh, el, fr_row<false>(s.ov + 16 * ct * LK, LK, 32 * kk, lane));
+        }
+    }
 #pragma unroll
     for (int ct2 = 0; ct2 < 2; ++ct2) {
         const int ct = 2 * (wave & 1) + ct2;
-        f32x4 a1 = f32x4{}, a2 = f32x4{};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            a1 = mm_pe(a1, fr_row<false>(s.nH + 16 * rt64 * LK, LK, 32 * kk, lane),
-                       fr_row<false>(s.nL + 16 * rt64 * LK, LK, 32 * kk, lane),
-                       fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane));
-            a2 = mm_pe(a2, fr_row<false>(s.eH + 16 * rt64 * LK, LK, 32 * kk, lane),
-                       fr_row<false>(s.eL + 16 * rt64 * LK, LK, 32 * kk, lane),
-                       fr_row<false>(s.ov + 16 * ct * LK, LK, 32 * kk, lane));
-        }
+        const f32x4 a1 = a1t[ct2], a2 = a2t[ct2];
         const int sc = 16 * ct + r16;
         st_split(s.pH, s.pL, L64, 16 * rt64, 16 * ct, s.bt[sc] * (s.gam[sc] * a1 + a2), lane);
     }
+    // T^T dW and (T^T dv')^T over the four token tiles x of T: both take the
+    // transposed T fragments of tile x, read once for the two products
+    //   T^T dW, transposed: (key dim, token s): this wave's key columns of dW;
+    //   (T^T dv')^T = dv'^T T over value columns 16 w .., all token columns s:
+    //   lane (m, g) holds value columns 16 w + 4 g .. +3 of token 16 x + m,
+    //   so dv goes out as four contiguous values per lane and the dbeta term
+    //   is a four-term dot product with V plus a sum over g.
+    bf16x8 wH[2], wL[2], bh[2], bl[2];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-        // T^T dW, transposed: (key dim, token s)
-        f32x4 acc = f32x4{};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            acc = mm_pp(acc, fr_tr(s.nH + 16 * wave, LK, 32 * kk, lane), fr_tr(s.nL + 16 * wave, LK, 32 * kk, lane),
-                        fr_tr(s.tH + 16 * ct, L64, 32 * kk, lane), fr_tr(s.tL + 16 * ct, L64, 32 * kk, lane));
-        const int sc = 16 * ct + r16;
-        float rk = 0.f;
-        {
-            const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(&s.k[sc * LK + 16 * wave + 4 * g4]);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) rk += acc[jj] * (float)k4[jj];
-        }
-        rk = sum4g(rk);
-        const float bgs = s.bt[sc] * s.gam[sc];
-        if (g4 == 0) {
-            dbw[sc] += s.gam[sc] * rk;
-            dGw[sc] += bgs * rk;
-        }
-        dkt[ct] += bgs * acc;
+    for (int kk = 0; kk < 2; ++kk) {
+        wH[kk] = fr_tr(s.nH + 16 * wave, LK, 32 * kk, lane);
+        wL[kk] = fr_tr(s.nL + 16 * wave, LK, 32 * kk, lane);
+        bh[kk] = fr_tr(s.eH + 16 * wave, LK, 32 * kk, lane);
+        bl[kk] = fr_tr(s.eL + 16 * wave, LK, 32 * kk, lane);
     }
-    {
-        // (T^T dv')^T = dv'^T T over value columns 16 w .., all token columns
-        // s: lane (m, g) holds value columns 16 w + 4 g .. +3 of token
-        // 16 rt + m, so dv goes out as four contiguous values per lane and the
-        // dbeta term is a four-term dot product with V plus a sum over g.
-        bf16x8 bh[2], bl[2];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        bf16x8 th[2], tl[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            bh[kk] = fr_tr(s.eH + 16 * wave, LK, 32 * kk, lane);
-            bl[kk] = fr_tr(s.eL + 16 * wave, LK, 32 * kk, lane);
+            th[kk] = fr_tr(s.tH + 16 * x, L64, 32 * kk, lane);
+            tl[kk] = fr_tr(s.tL + 16 * x, L64, 32 * kk, lane);
         }
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        const int sc = 16 * x + r16;  // token s of this lane's column
+        {
             f32x4 acc = f32x4{};
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                acc = mm_pp(acc, bh[kk], bl[kk], fr_tr(s.tH + 16 * rt, L64, 32 * kk, lane),
-                            fr_tr(s.tL + 16 * rt, L64, 32 * kk, lane));
-            const int sr = 16 * rt + r16;      // token s
+            for (int kk = 0; kk < 2; ++kk) acc = mm_pp(acc, wH[kk], wL[kk], th[kk], tl[kk]);
+            float rk = 0.f;
+            {
+                const bf16x4 k4 = *reinterpret_cast<const bf16x4 *>(&s.k[sc * LK + 16 * wave + 4 * g4]);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) rk += acc[jj] * (float)k4[jj];
+            }
+            rk = sum4g(rk);
+            const float bgs = s.bt[sc] * s.gam[sc];
+            if (g4 == 0) {
+                dbw[sc] += s.gam[sc] * rk;
+                dGw[sc] += bgs * rk;
+            }
+            dkt[x] += bgs * acc;
+        }
+        {
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) acc = mm_pp(acc, bh[kk], bl[kk], th[kk], tl[kk]);
             const int v0 = 16 * wave + 4 * g4;  // value columns v0 .. v0 + 3
-            const bf16x4 vv4 = *reinterpret_cast<const bf16x4 *>(&s.ov[sr * LK + v0]);
+            const bf16x4 vv4 = *reinterpret_cast<const bf16x4 *>(&s.ov[sc * LK + v0]);
             float rvv = 0.f;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) rvv += acc[jj] * (float)vv4[jj];
             rvv = sum4g(rvv);
-            if (g4 == 0) dbw[sr] += rvv;
-            const f32x4 dvv = s.bt[sr] * acc;
-            if (sr < rows_valid) {
-                const int64_t off = row_c * DV + (int64_t)sr * tstride + v0;
+            if (g4 == 0) dbw[sc] += rvv;
+            const f32x4 dvv = s.bt[sc] * acc;
+            if (sc < rows_valid) {
+                const int64_t off = row_c * DV + (int64_t)sc * tstride + v0;
                 if (p.grad_f32)
                     *reinterpret_cast<f32x4 *>(static_cast<float *>(p.dv) + off) = dvv;
                 else
@@ -883,15 +905,24 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     lds_barrier();
 
     // ---- 4: Y = T^T dT -> n (as [64][64])
+    {
+        // T^T rows of tile rt64, read once for both column tiles
+        bf16x8 th[2], tl[2];
 #pragma unroll
-    for (int ct2 = 0; ct2 < 2; ++ct2) {
-        const int ct = 2 * (wave & 1) + ct2;
-        f32x4 acc = f32x4{};
+        for (int kk = 0; kk < 2; ++kk) {
+            th[kk] = fr_tr(s.tH + 16 * rt64, L64, 32 * kk, lane);
+            tl[kk] = fr_tr(s.tL + 16 * rt64, L64, 32 * kk, lane);
+        }
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            acc = mm_pp(acc, fr_tr(s.tH + 16 * rt64, L64, 32 * kk, lane), fr_tr(s.tL + 16 * rt64, L64, 32 * kk, lane),
-                        fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane), fr_tr(s.pL + 16 * ct, L64, 32 * kk, lane));
-        st_split(s.nH, s.nL, L64, 16 * rt64, 16 * ct, acc, lane);
+        for (int ct2 = 0; ct2 < 2; ++ct2) {
+            const int ct = 2 * (wave & 1) + ct2;
+            f32x4 acc = f32x4{};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                acc = mm_pp(acc, th[kk], tl[kk], fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane),
+                            fr_tr(s.pL + 16 * ct, L64, 32 * kk, lane));
+            st_split(s.nH, s.nL, L64, 16 * rt64, 16 * ct, acc, lane);
+        }
     }
     lds_barrier();
 
@@ -904,20 +935,30 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     }
 
     // ---- 5: dA~ = -(Y T^T) strictly lower;  M = dA~ o beta_i Gamma_is -> p;  gate / beta terms of A~
+    // both column tiles per k step: the Y and K rows of row tile rt64 are read once
+    f32x4 yat[2] = {f32x4{}, f32x4{}}, kkt[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 yh = fr_row<false>(s.nH + 16 * rt64 * L64, L64, 32 * kk, lane);
+        const bf16x8 yl = fr_row<false>(s.nL + 16 * rt64 * L64, L64, 32 * kk, lane);
+#pragma unroll
+        for (int ct2 = 0; ct2 < 2; ++ct2) {
+            const int ct = 2 * (wave & 1) + ct2;
+            yat[ct2] = mm_pp(yat[ct2], yh, yl, fr_row<false>(s.tH + 16 * ct * L64, L64, 32 * kk, lane),
+                             fr_row<false>(s.tL + 16 * ct * L64, L64, 32 * kk, lane));
+        }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 kr = fr_row<false>(s.k + 16 * rt64 * LK, LK, 32 * kk, lane);
+#pragma unroll
+        for (int ct2 = 0; ct2 < 2; ++ct2)
+            kkt[ct2] = mfma(kr, fr_row<false>(s.k + 16 * (2 * (wave & 1) + ct2) * LK, LK, 32 * kk, lane), kkt[ct2]);
+    }
 #pragma unroll
     for (int ct2 = 0; ct2 < 2; ++ct2) {
         const int ct = 2 * (wave & 1) + ct2;
-        f32x4 ya = f32x4{}, kk4 = f32x4{};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            ya = mm_pp(ya, fr_row<false>(s.nH + 16 * rt64 * L64, L64, 32 * kk, lane),
-                       fr_row<false>(s.nL + 16 * rt64 * L64, L64, 32 * kk, lane),
-                       fr_row<false>(s.tH + 16 * ct * L64, L64, 32 * kk, lane),
-                       fr_row<false>(s.tL + 16 * ct * L64, L64, 32 * kk, lane));
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            kk4 = mfma(fr_row<false>(s.k + 16 * rt64 * LK, LK, 32 * kk, lane),
-                       fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane), kk4);
+        const f32x4 ya = yat[ct2], kk4 = kkt[ct2];
         f32x4 m;
         float colsum = 0.f;
 #pragma unroll
@@ -951,14 +992,16 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     for (int ct = 0; ct < 4; ++ct)
         kprev[ct] = group_prev(p.dk_ws, rowq_c * DK + (unsigned)(16 * ct + r16) * qstride + 16 * wave + 4 * g4, first,
                               16 * ct + r16 < rows_valid);
+    bf16x8 ak6[2];  // this wave's rows of K^T, read once for the four token tiles
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) ak6[kk] = fr_tr(s.k + 16 * wave, LK, 32 * kk, lane);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 ak = fr_tr(s.k + 16 * wave, LK, 32 * kk, lane);
-            dkt[ct] = mm_ep(dkt[ct], ak, fr_row<true>(s.pH + 16 * ct * L64, L64, 32 * kk, lane),
+            dkt[ct] = mm_ep(dkt[ct], ak6[kk], fr_row<true>(s.pH + 16 * ct * L64, L64, 32 * kk, lane),
                             fr_row<true>(s.pL + 16 * ct * L64, L64, 32 * kk, lane));
-            dkt[ct] = mm_ep(dkt[ct], ak, fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane),
+            dkt[ct] = mm_ep(dkt[ct], ak6[kk], fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane),
                             fr_tr(s.pL + 16 * ct, L64, 32 * kk, lane));
         }
         const int tok = 16 * ct + r16;
@@ -1182,14 +1225,19 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
             }
         }
         // P = (Q K^T) o Gamma, s <= i: row tile w / 2, column tiles 2 (w % 2) + {0, 1}
+        // (both column tiles per k step: the Q rows are read once)
+        f32x4 pacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 qr = fr_row<false>(s.q + 16 * (wave >> 1) * LK, LK, 32 * kk, lane);
+#pragma unroll
+            for (int ct2 = 0; ct2 < 2; ++ct2)
+                pacc[ct2] = mfma(qr, fr_row<false>(s.k + 16 * (2 * (wave & 1) + ct2) * LK, LK, 32 * kk, lane), pacc[ct2]);
+        }
 #pragma unroll
         for (int ct2 = 0; ct2 < 2; ++ct2) {
             const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
-            f32x4 acc = f32x4{};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                acc = mfma(fr_row<false>(s.q + 16 * rt * LK, LK, 32 * kk, lane),
-                           fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane), acc);
+            const f32x4 acc = pacc[ct2];
             f32x4 pv;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -1217,20 +1265,31 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
 
         // dv' = scale P^T dO + diag(rl) K dh: token row tile w / 2, value column tiles 2 (w % 2) + {0, 1};
         // and this wave's key rows of Q^T diag(gamma) dO
+        // (the P^T and K fragments of row tile w / 2 are read once for both column tiles)
+        f32x4 a1t[2] = {f32x4{}, f32x4{}}, a2t[2] = {f32x4{}, f32x4{}};
+        if (!mmap) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 ph = fr_tr(s.pH + 16 * (wave >> 1), L64, 32 * kk, lane);
+                const bf16x8 pl = fr_tr(s.pL + 16 * (wave >> 1), L64, 32 * kk, lane);
+#pragma unroll
+                for (int ct2 = 0; ct2 < 2; ++ct2)
+                    a1t[ct2] = mm_pe(a1t[ct2], ph, pl, fr_tr(s.dO + 16 * (2 * (wave & 1) + ct2), L64, 32 * kk, lane));
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 kr = fr_row<true>(s.k + 16 * (wave >> 1) * LK, LK, 32 * kk, lane);
+#pragma unroll
+            for (int ct2 = 0; ct2 < 2; ++ct2) {
+                const int ct = 2 * (wave & 1) + ct2;
+                a2t[ct2] = mm_ep(a2t[ct2], kr, fr_tr(s.hH + 16 * ct, L64, 32 * kk, lane), fr_tr(s.hL + 16 * ct, L64, 32 * kk, lane));
+            }
+        }
 #pragma unroll
         for (int ct2 = 0; ct2 < 2; ++ct2) {
             const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
-            f32x4 a1 = f32x4{}, a2 = f32x4{};
-            if (!mmap) {
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    a1 = mm_pe(a1, fr_tr(s.pH + 16 * rt, L64, 32 * kk, lane),
-                               fr_tr(s.pL + 16 * rt, L64, 32 * kk, lane), fr_tr(s.dO + 16 * ct, L64, 32 * kk, lane));
-            }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                a2 = mm_ep(a2, fr_row<true>(s.k + 16 * rt * LK, LK, 32 * kk, lane),
-                           fr_tr(s.hH + 16 * ct, L64, 32 * kk, lane), fr_tr(s.hL + 16 * ct, L64, 32 * kk, lane));
+            const f32x4 a1 = a1t[ct2], a2 = a2t[ct2];
             f32x4 x;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
