@@ -1042,7 +1042,6 @@ struct __attribute__((aligned(16))) SmemDh {
     bf16 dO[CH * L64];                // dO, this workgroup's 64 value columns
     bf16 aH[CH * L64], aL[CH * L64];  // dv'   [token][col]
     bf16 tH[CH * L64], tL[CH * L64];  // T diag(beta gamma), hi / lo
-    bf16 oH[CH * L64], oL[CH * L64];  // diag(gamma) dO, hi / lo   [token][col]
     bf16 pH[CH * L64], pL[CH * L64];  // P   [query token][key token]
     bf16 hH[DK * L64], hL[DK * L64];  // dh  [key dim][value column]
     float G[CH], gam[CH], bg[CH];
@@ -1088,22 +1087,6 @@ __device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int 
     store_rows_ld(s.k, R.k, LK, tid);
     store_rows_ld(s.q, R.q, LK, tid);
     store_rows_ld(s.dO, R.dO, L64, tid);
-    // diag(gamma) dO as a hi / lo pair, formed once here for every wave's Q^T diag(gamma) dO
-    constexpr int OPR = HVC * 2 / 16;
-#pragma unroll
-    for (int i = 0; i < Rows<OPR>::PER; ++i) {
-        const int pc = tid + i * NT;
-        const int row = pc / OPR, col = 8 * (pc - row * OPR);
-        const bf16x8 d = __builtin_bit_cast(bf16x8, R.dO.x[i]);
-        const float gr = s.gam[row];
-        float f[8];
-#pragma unroll
-        for (int e2 = 0; e2 < 8; ++e2) f[e2] = (float)d[e2] * gr;
-        bf16x8 h, l;
-        split8(f, h, l);
-        *reinterpret_cast<bf16x8 *>(&s.oH[row * L64 + col]) = h;
-        *reinterpret_cast<bf16x8 *>(&s.oL[row * L64 + col]) = l;
-    }
     constexpr int PPR = CH * 4 / 16;
 #pragma unroll
     for (int i = 0; i < Rows<PPR>::PER; ++i) {
@@ -1300,15 +1283,29 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
         }
         f32x4 u[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
         if (!mmap) {
-            bf16x8 aq[2];
+            // (diag(gamma) Q)^T dO: this wave's key rows of Q^T (transposing
+            // reads, k = tokens in the transposed-read order) scaled per token
+            // by gamma and split hi / lo, against the exact dO tile (a split of
+            // diag(gamma) dO instead would double the LDS reads of every wave)
+            bf16x8 aqh[2], aql[2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) aq[kk] = fr_tr(s.q + 16 * wave, LK, 32 * kk, lane);
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16x8 qf = fr_tr(s.q + 16 * wave, LK, 32 * kk, lane);
+                const f32x4 ga = *reinterpret_cast<const f32x4 *>(&s.gam[32 * kk + 4 * g4]);
+                const f32x4 gb = *reinterpret_cast<const f32x4 *>(&s.gam[32 * kk + 16 + 4 * g4]);
+                float f[8];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    f[e2] = (float)qf[e2] * ga[e2];
+                    f[4 + e2] = (float)qf[4 + e2] * gb[e2];
+                }
+                split8(f, aqh[kk], aql[kk]);
+            }
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk)
-                    u[ct] = mm_ep(u[ct], aq[kk], fr_tr(s.oH + 16 * ct, L64, 32 * kk, lane),
-                                  fr_tr(s.oL + 16 * ct, L64, 32 * kk, lane));
+                    u[ct] = mm_pe(u[ct], aqh[kk], aql[kk], fr_tr(s.dO + 16 * ct, L64, 32 * kk, lane));
             }
         }
         __syncthreads();
