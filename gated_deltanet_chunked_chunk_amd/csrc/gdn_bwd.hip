@@ -402,6 +402,27 @@ __device__ __forceinline__ void st_split_t(bf16 *hi, bf16 *lo, int ld, int r0, i
     *reinterpret_cast<bf16x4 *>(&lo[c * ld + r]) = l;
 }
 
+// The diagonal 16 x 16 tile (rows and columns from r0) of S = M + M^T for a
+// strictly lower M given as an accumulator tile v: each element below the
+// diagonal goes to its place and, mirrored, above it; the diagonal is zero.
+__device__ __forceinline__ void st_sym_diag(bf16 *hi, bf16 *lo, int ld, int r0, f32x4 v, int lane) {
+    bf16x4 h, l;
+    split4(v, h, l);
+    const int c = lane & 15, r = 4 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (c < r + j) {
+            hi[(r0 + r + j) * ld + r0 + c] = h[j];
+            lo[(r0 + r + j) * ld + r0 + c] = l[j];
+            hi[(r0 + c) * ld + r0 + r + j] = h[j];
+            lo[(r0 + c) * ld + r0 + r + j] = l[j];
+        } else if (c == r + j) {
+            hi[(r0 + c) * ld + r0 + c] = bf16(0.f);
+            lo[(r0 + c) * ld + r0 + c] = bf16(0.f);
+        }
+    }
+}
+
 // LDS row strides (bf16 elements) of 128- and 64-wide tiles: 272 and 144
 // bytes, so that the 16 rows one fragment read touches fall in distinct banks.
 constexpr int LK = DK + 8;
@@ -934,7 +955,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         dma_q(nx, wave, lane);
     }
 
-    // ---- 5: dA~ = -(Y T^T) strictly lower;  M = dA~ o beta_i Gamma_is -> p;  gate / beta terms of A~
+    // ---- 5: dA~ = -(Y T^T) strictly lower;  M = dA~ o beta_i Gamma_is;  S = M + M^T -> p;
+    //      gate / beta terms of A~
     // both column tiles per k step: the Y and K rows of row tile rt64 are read once
     f32x4 yat[2] = {f32x4{}, f32x4{}}, kkt[2] = {f32x4{}, f32x4{}};
 #pragma unroll
@@ -982,11 +1004,19 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         }
         colsum = sum4g(colsum);
         if (g4 == 0) dGw[16 * ct + r16] -= colsum;
-        st_split(s.pH, s.pL, L64, 16 * rt64, 16 * ct, m, lane);
+        // S = M + M^T (the sixth phase needs only K^T S): a tile below the
+        // diagonal goes to its place and, transposed, to the mirrored one; a
+        // tile above it is zero in M and is written by its mirror's wave
+        if (ct < rt64) {
+            st_split(s.pH, s.pL, L64, 16 * rt64, 16 * ct, m, lane);
+            st_split_t(s.pH, s.pL, L64, 16 * rt64, 16 * ct, m, lane);
+        } else if (ct == rt64) {
+            st_sym_diag(s.pH, s.pL, L64, 16 * ct, m, lane);
+        }
     }
     lds_barrier();
 
-    // ---- 6: dK += M K + M^T K (transposed: K^T M^T + K^T M); store dk of this v-head
+    // ---- 6: dK += M K + M^T K = S K (transposed: K^T S, S symmetric); store dk of this v-head
     f32x4 kprev[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
@@ -998,12 +1028,9 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            dkt[ct] = mm_ep(dkt[ct], ak6[kk], fr_row<true>(s.pH + 16 * ct * L64, L64, 32 * kk, lane),
-                            fr_row<true>(s.pL + 16 * ct * L64, L64, 32 * kk, lane));
+        for (int kk = 0; kk < 2; ++kk)
             dkt[ct] = mm_ep(dkt[ct], ak6[kk], fr_tr(s.pH + 16 * ct, L64, 32 * kk, lane),
                             fr_tr(s.pL + 16 * ct, L64, 32 * kk, lane));
-        }
         const int tok = 16 * ct + r16;
         if (tok < rows_valid)
             group_put(p, p.dk_ws, p.dk, rowq_c * DK + (unsigned)tok * qstride + 16 * wave + 4 * g4, dkt[ct] + kprev[ct],
