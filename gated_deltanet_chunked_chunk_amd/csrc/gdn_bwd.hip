@@ -457,7 +457,7 @@ struct __attribute__((aligned(16))) SmemLoc {
     bf16 tH[CH * L64], tL[CH * L64];  // T
     bf16 nH[CH * LK], nL[CH * LK];    // v' [token][v], then dW [token][key dim], then Y [64][64] (stride L64)
     bf16 eH[CH * LK], eL[CH * LK];    // dv' [token][v]
-    bf16 pH[CH * L64], pL[CH * L64];  // dPm, then dT, then M   [row][col]
+    bf16 pH[CH * L64], pL[CH * L64];  // dPm, then dT, then S = M + M^T   [row][col]
     float G[CH], gam[CH], bt[CH];
     float dGp[8][CH], dbp[8][CH];     // per-wave partial sums of dG and dbeta
 };
