@@ -563,7 +563,10 @@ __device__ __forceinline__ LocItem next_item(const BwdParams &p, int &it, const 
 // split into hi / lo pairs on the way to LDS); dO and the dv' planes straight
 // into LDS, and the wave's h rows into registers, during the previous v-head
 // (at the start for the first); the dh' rows after the tiles, in flight during
-// the first products.  fp32 intermediates are stored once as hi / lo bf16
+// the first products; dk's running sum one phase before its products, ahead
+// of the next v-head's direct loads.  Wave 0 reduces a v-head's dg and dbeta
+// partial sums at the next v-head's start, while the loads are in flight (no
+// phase of their own).  fp32 intermediates are stored once as hi / lo bf16
 // pairs that every consumer reads without further arithmetic.  The barriers
 // hand over LDS only: no data passes between waves through global memory, so
 // loads issued for later phases stay in flight across them.
@@ -629,6 +632,26 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         dma_tile(s.eL, chunk_rsrc(dvn + CH * DV, DV * 2, 0, CH), DV * 2, wv, l);
     };
 
+    // dg = reverse in-chunk cumsum of dG, and dbeta, of a finished v-head:
+    // wave 0 sums the eight waves' partials and writes them at the next
+    // v-head's start (its loads are in flight there), or after the last one
+    int64_t dg_row = -1;  // first output row of the v-head whose dg is pending
+    int dg_rows = 0;
+    auto flush_dg = [&]() {
+        float dG = 0.f, db = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            dG += s.dGp[w][lane0];
+            db += s.dbp[w][lane0];
+        }
+        const float x = reverse64(prefix64(reverse64(dG)));  // sum over tokens >= lane
+        if (lane0 < dg_rows) {
+            const int64_t off = dg_row + (int64_t)lane0 * p.Hv;
+            p.dg[off] = x;
+            p.dbeta[off] = db;
+        }
+    };
+
     bool fresh = true;  // the workgroup's first item: nothing was loaded ahead for it
     while (true) {
     const Where e = cur.e;
@@ -681,9 +704,13 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             s.gam[tid] = __expf(G);
             s.bt[tid] = b;
         }
-        for (int x = tid; x < 8 * CH; x += NT) {
-            (&s.dGp[0][0])[x] = 0.f;
-            (&s.dbp[0][0])[x] = 0.f;
+        if (wave == 0) {
+            if (dg_row >= 0) flush_dg();
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                s.dGp[w][lane0] = 0.f;
+                s.dbp[w][lane0] = 0.f;
+            }
         }
     }
     dma_wait();  // this wave's direct loads (dO, dv', for a new item K and Q) have landed
@@ -947,6 +974,13 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     }
     lds_barrier();
 
+    // dk's running sum, read before the direct loads below: a wait for it then
+    // leaves those loads in flight (the count of memory operations is in order)
+    f32x4 kprev[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+        kprev[ct] = group_prev(p.dk_ws, rowq_c * DK + (unsigned)(16 * ct + r16) * qstride + 16 * wave + 4 * g4, first,
+                              16 * ct + r16 < rows_valid);
     // ov, eH and eL are dead from here on, and q since the second phase
     if (!last) {
         dma_do_dv(cur, j + 1, wave, lane);
@@ -1017,11 +1051,6 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     lds_barrier();
 
     // ---- 6: dK += M K + M^T K = S K (transposed: K^T S, S symmetric); store dk of this v-head
-    f32x4 kprev[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-        kprev[ct] = group_prev(p.dk_ws, rowq_c * DK + (unsigned)(16 * ct + r16) * qstride + 16 * wave + 4 * g4, first,
-                              16 * ct + r16 < rows_valid);
     bf16x8 ak6[2];  // this wave's rows of K^T, read once for the four token tiles
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) ak6[kk] = fr_tr(s.k + 16 * wave, LK, 32 * kk, lane);
@@ -1039,28 +1068,15 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
     lds_barrier();
     if (last && nx.ok) dma_k(nx, wave, lane);  // k was last read in the sixth phase
 
-    // dg = reverse in-chunk cumsum of dG; dbeta
-    if (wave == 0) {
-        float dG = 0.f, db = 0.f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            dG += s.dGp[w][lane];
-            db += s.dbp[w][lane];
-        }
-        const float x = reverse64(prefix64(reverse64(dG)));  // sum over tokens >= lane
-        if (lane < rows_valid) {
-            const int64_t off = (e.row0 + (int64_t)c * CH + lane) * p.Hv + j;
-            p.dg[off] = x;
-            p.dbeta[off] = db;
-        }
-    }
-    lds_barrier();  // the next v-head's tiles overwrite LDS
+    dg_row = row_c;
+    dg_rows = rows_valid;
     }
     if (!nx.ok) break;
     cur = nx;
     it = it_nx;
     fresh = false;
     }
+    if (wave == 0) flush_dg();  // the eight waves' partials are complete since the sixth phase's barrier
 }
 
 // ---------------------------------------------------------------- reverse pass
