@@ -739,24 +739,31 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             qk1[ct2] = mfma(qr, fr_row<false>(s.k + 16 * ct * LK, LK, 32 * kk, lane), qk1[ct2]);
         }
     }
+    {
+        float rsum[4] = {0.f, 0.f, 0.f, 0.f};  // row terms of both column tiles, reduced once
 #pragma unroll
-    for (int ct2 = 0; ct2 < 2; ++ct2) {
-        const int ct = 2 * (wave & 1) + ct2;
-        const f32x4 acc = acc1[ct2], qk = qk1[ct2];
-        f32x4 dpm;
-        float colsum = 0.f;
+        for (int ct2 = 0; ct2 < 2; ++ct2) {
+            const int ct = 2 * (wave & 1) + ct2;
+            const f32x4 acc = acc1[ct2], qk = qk1[ct2];
+            f32x4 dpm;
+            float colsum = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int i = 16 * rt64 + 4 * g4 + jj, sc = 16 * ct + r16;
+                dpm[jj] = sc <= i ? p.scale * acc[jj] * __expf(s.G[i] - s.G[sc]) : 0.f;
+                const float d1 = dpm[jj] * qk[jj];
+                rsum[jj] += d1;
+                colsum += d1;
+            }
+            colsum = sum4g(colsum);
+            if (g4 == 0) dGw[16 * ct + r16] -= colsum;
+            st_split(s.pH, s.pL, L64, 16 * rt64, 16 * ct, dpm, lane);
+        }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const int i = 16 * rt64 + 4 * g4 + jj, sc = 16 * ct + r16;
-            dpm[jj] = sc <= i ? p.scale * acc[jj] * __expf(s.G[i] - s.G[sc]) : 0.f;
-            const float d1 = dpm[jj] * qk[jj];
-            const float rs = sum16(d1);
-            if (r16 == 0) dGw[i] += rs;
-            colsum += d1;
+            const float rs = sum16(rsum[jj]);
+            if (r16 == 0) dGw[16 * rt64 + 4 * g4 + jj] += rs;
         }
-        colsum = sum4g(colsum);
-        if (g4 == 0) dGw[16 * ct + r16] -= colsum;
-        st_split(s.pH, s.pL, L64, 16 * rt64, 16 * ct, dpm, lane);
     }
     lds_barrier();
 
@@ -1011,6 +1018,7 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
         for (int ct2 = 0; ct2 < 2; ++ct2)
             kkt[ct2] = mfma(kr, fr_row<false>(s.k + 16 * (2 * (wave & 1) + ct2) * LK, LK, 32 * kk, lane), kkt[ct2]);
     }
+    float rsum[4] = {0.f, 0.f, 0.f, 0.f}, bsum[4] = {0.f, 0.f, 0.f, 0.f};  // row terms of both column tiles
 #pragma unroll
     for (int ct2 = 0; ct2 < 2; ++ct2) {
         const int ct = 2 * (wave & 1) + ct2;
@@ -1029,11 +1037,8 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
                 d2 = m[jj] * kk4[jj];
                 db = da * gm * kk4[jj];
             }
-            const float rs = sum16(d2), rb = sum16(db);
-            if (r16 == 0) {
-                dGw[i] += rs;
-                dbw[i] += rb;
-            }
+            rsum[jj] += d2;
+            bsum[jj] += db;
             colsum += d2;
         }
         colsum = sum4g(colsum);
@@ -1046,6 +1051,14 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_local_kernel(BwdParams p) {
             st_split_t(s.pH, s.pL, L64, 16 * rt64, 16 * ct, m, lane);
         } else if (ct == rt64) {
             st_sym_diag(s.pH, s.pL, L64, 16 * ct, m, lane);
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+        const float rs = sum16(rsum[jj]), rb = sum16(bsum[jj]);
+        if (r16 == 0) {
+            dGw[16 * rt64 + 4 * g4 + jj] += rs;
+            dbw[16 * rt64 + 4 * g4 + jj] += rb;
         }
     }
     lds_barrier();
