@@ -1104,49 +1104,80 @@ struct __attribute__((aligned(16))) SmemDh {
 };
 static_assert(sizeof(SmemDh) <= 160 * 1024, "reverse-pass LDS over 160 KB");
 
-// One chunk's inputs of the reverse pass, in registers between load and store.
+// One chunk's inputs of the reverse pass, in the registers of waves 0-3 (the
+// waves that stage tiles) between load and store.
+constexpr int NTD = NT / 2;  // threads of waves 0-3
+template <int PPR>
+struct RowsD {
+    static_assert(CH * PPR % NTD == 0, "a tile is a whole number of pieces per staging thread");
+    static constexpr int PER = CH * PPR / NTD;
+    u32x4 x[PER];
+};
 struct ChunkDh {
-    Rows<DK * 2 / 16> k, q;
-    Rows<HVC * 2 / 16> dO;
-    Rows<CH * 4 / 16> t;
-    float g, b;  // lane l: token l (every wave)
+    RowsD<DK * 2 / 16> k, q;
+    RowsD<HVC * 2 / 16> dO;
+    RowsD<CH * 4 / 16> t;
+    float g, b;  // lane l: token l (every staging wave)
 };
 
+template <int PPR>
+__device__ __forceinline__ void load_rows_d(RowsD<PPR> &R, const void *base, unsigned stride, int c, int seq_len,
+                                            int td) {
+    const __amdgpu_buffer_rsrc_t r = chunk_rsrc(base, stride, c, seq_len);
+#pragma unroll
+    for (int i = 0; i < RowsD<PPR>::PER; ++i) {
+        const int pc = td + i * NTD;
+        const int row = pc / PPR, col = pc - row * PPR;
+        R.x[i] = ld16(r, (unsigned)row * stride + (unsigned)col * 16u);
+    }
+}
+
+template <int PPR>
+__device__ __forceinline__ void store_rows_d(bf16 *dst, const RowsD<PPR> &R, int ld, int td) {
+#pragma unroll
+    for (int i = 0; i < RowsD<PPR>::PER; ++i) {
+        const int pc = td + i * NTD;
+        const int row = pc / PPR, col = pc - row * PPR;
+        *reinterpret_cast<u32x4 *>(&dst[row * ld + 8 * col]) = R.x[i];
+    }
+}
+
+// td: thread index among waves 0-3
 __device__ __forceinline__ void load_chunk_dh(ChunkDh &R, const BwdParams &p, const Where &e, int j, int half, int c,
-                                              int tid) {
+                                              int td) {
     const int iq = j / p.group;
     const unsigned kstride = (unsigned)p.Hqk * DK * 2, vstride = (unsigned)p.Hv * DV * 2;
     const unsigned astride = (unsigned)p.Hv * CH * 4, gstride = (unsigned)p.Hv * 4;
-    load_rows(R.k, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
-    load_rows(R.q, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, tid);
-    load_rows(R.dO, p.dO + (e.row0 * p.Hv + j) * DV + half * HVC, vstride, c, e.seq_len, tid);
-    load_rows(R.t, p.A + (e.row0 * p.Hv + j) * CH, astride, c, e.seq_len, tid);
-    const int lane = tid & 63;
+    load_rows_d(R.k, p.k + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, td);
+    load_rows_d(R.q, p.q + (e.row0 * p.Hqk + iq) * DK, kstride, c, e.seq_len, td);
+    load_rows_d(R.dO, p.dO + (e.row0 * p.Hv + j) * DV + half * HVC, vstride, c, e.seq_len, td);
+    load_rows_d(R.t, p.A + (e.row0 * p.Hv + j) * CH, astride, c, e.seq_len, td);
+    const int lane = td & 63;
     const __amdgpu_buffer_rsrc_t rg = chunk_rsrc(p.g + e.row0 * p.Hv + j, gstride, c, e.seq_len);
     const __amdgpu_buffer_rsrc_t rb = chunk_rsrc(p.beta + e.row0 * p.Hv + j, gstride, c, e.seq_len);
     R.g = ld4(rg, (unsigned)lane * gstride);
     R.b = ld4(rb, (unsigned)lane * gstride);
 }
 
-// Tiles of one chunk into LDS: K, Q, dO as bf16; T with its columns scaled by
-// beta gamma as a hi / lo pair.  Every wave forms the gate prefix sums itself
-// (lane = token) for the column scales.
-__device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int tid) {
-    const int lane = tid & 63;
+// Tiles of one chunk into LDS (waves 0-3): K, Q, dO as bf16; T with its columns
+// scaled by beta gamma as a hi / lo pair.  Every staging wave forms the gate
+// prefix sums itself (lane = token) for the column scales.
+__device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int td) {
+    const int lane = td & 63;
     const float G = prefix64(R.g);
     const float gam = __expf(G);
     const float bg = R.b * gam;
-    if (tid < 64) s.G[lane] = G;
-    // every wave writes the same scales and reads back only its own writes
+    if (td < 64) s.G[lane] = G;
+    // every staging wave writes the same scales and reads back only its own writes
     s.bg[lane] = bg;
     s.gam[lane] = gam;
-    store_rows_ld(s.k, R.k, LK, tid);
-    store_rows_ld(s.q, R.q, LK, tid);
-    store_rows_ld(s.dO, R.dO, L64, tid);
+    store_rows_d(s.k, R.k, LK, td);
+    store_rows_d(s.q, R.q, LK, td);
+    store_rows_d(s.dO, R.dO, L64, td);
     constexpr int PPR = CH * 4 / 16;
 #pragma unroll
-    for (int i = 0; i < Rows<PPR>::PER; ++i) {
-        const int pc = tid + i * NT;
+    for (int i = 0; i < RowsD<PPR>::PER; ++i) {
+        const int pc = td + i * NTD;
         const int row = pc / PPR, col = 4 * (pc - row * PPR);
         f32x4 x = __builtin_bit_cast(f32x4, R.t.x[i]);
 #pragma unroll
@@ -1159,8 +1190,15 @@ __device__ __forceinline__ void store_chunk_dh(SmemDh &s, const ChunkDh &R, int 
 }
 
 // One workgroup per (segment, v-head, value half).  Walks the segment's chunks
-// last to first, carrying dh (K x 64 fp32) in registers -- wave w holds key
-// dims 16 w .. 16 w + 15 -- with a hi / lo copy in LDS for the K dh product.
+// last to first.  The waves have two roles, so that each 64 x 64 product is
+// tiled into 32 x 32 blocks and a shared operand is read by fewer waves:
+// waves 0-3 form P and dv' (wave q: token row tiles 2 (q / 2) + {0, 1}, column
+// tiles 2 (q % 2) + {0, 1}), copy dh' and dv' to HBM and stage the next chunk's
+// tiles; waves 4-7 carry dh (K x 64 fp32) in registers -- wave 4 + q holds key
+// dims 32 q .. 32 q + 31 -- and form W and Q^T diag(gamma) dO for those key
+// dims and the dh update, with a hi / lo copy of dh in LDS for the K dh
+// product.  Per chunk: (1) P | W; (2) dv' | Q^T diag(gamma) dO; (3) tile
+// staging | dh update.
 // Main pass (p.pass == 0): a segment that does not end its sequence starts
 // after a warm-up over the chunks that follow it (WARMUP, gate-driven window as
 // in the forward) or from its exact start gradient (EXACT, from the combine);
@@ -1188,6 +1226,11 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
     const int c_end = e.c_begin + e.c_count;
     const int g4 = lane >> 4, r16 = lane & 15;
     const bool exact_start = !pre && !e.last && p.cp_mode == 1 /* EXACT */;
+    const bool prod = wave < 4;  // waves 0-3: P, dv', copies and staging; 4-7: dh
+    const int q4 = wave & 3;
+    const int td = tid & (NTD - 1);
+    const int rt0 = 2 * (q4 >> 1), ct0 = 2 * (q4 & 1);  // a product wave's 32 x 32 block
+    const int kt0 = 2 * q4;                              // a dh wave's first key tile
 
     // where the reverse walk starts: the sequence end (from d final_state), a
     // warm-up window after the segment (from zero), or the segment end (EXACT)
@@ -1205,210 +1248,282 @@ __global__ void __launch_bounds__(NT, 1) gdn_bwd_dh_kernel(BwdParams p) {
     }
     const bool from_end = !pre && !exact_start && (c_last == nt);
 
-    // dh at the start of the walk: rows 16 w + 4 g + jj, value column 16 ct + r
-    const int64_t sbase = ((int64_t)e.n * p.Hv + j) * DK * DV + half * HVC;
-    const int64_t wbase = ((int64_t)seg * p.Hv + j) * DK * DV + half * HVC;  // exact-CP workspace
-    f32x4 dh[4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int d = 16 * wave + 4 * g4 + jj, v = 16 * ct + r16;
-            float x = 0.f;
-            if (from_end && p.dht) x = p.dht[sbase + (int64_t)d * DV + v];
-            if (exact_start) x = p.ws_h[wbase + (int64_t)d * DV + v];
-            if (mmap) x = (d == half * HVC + v) ? 1.f : 0.f;  // identity columns of this half
-            dh[ct][jj] = x;
-        }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) st_split(s.hH, s.hL, L64, 16 * wave, 16 * ct, dh[ct], lane);
     const int cbase = seq_chunk_base(p.cu, p.T, e.n, lane);
 
-    // The tiles of the next chunk (walking backwards) go into LDS during the dh
-    // update of the current one, which reads none of them; its inputs are
-    // loaded into registers one chunk ahead of that.
-    ChunkDh R;
-    if (c_last - 1 >= e.c_begin) {
-        load_chunk_dh(R, p, e, j, half, c_last - 1, tid);
-        store_chunk_dh(s, R, tid);
+    // The two roles run their own copies of the chunk loop, with the same three
+    // barriers per chunk (a barrier counts arrivals, so the copies stay in step);
+    // apart, each copy's registers are allocated for its role alone.
+    if (prod) {
+        // The tiles of the next chunk (walking backwards) go into LDS during the
+        // dh update of the current one, which reads none of them; their inputs
+        // are loaded into these waves' registers one chunk ahead of that.
+        ChunkDh R;
+        if (c_last - 1 >= e.c_begin) {
+            load_chunk_dh(R, p, e, j, half, c_last - 1, td);
+            store_chunk_dh(s, R, td);
+        }
+        if (c_last - 2 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c_last - 2, td);
+        for (int c = c_last - 1; c >= e.c_begin; --c) {
+            const bool own = !pre && c < c_end;
+            __syncthreads();  // chunk c's tiles in LDS; the previous dh update done
+            // P = (Q K^T) o Gamma, s <= i: query row tiles rt0 + {0, 1}, key
+            // column tiles ct0 + {0, 1} (each fragment read once for two products)
+            f32x4 pacc[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 qr[2], kf[2];
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    qr[a] = fr_row<false>(s.q + 16 * (rt0 + a) * LK, LK, 32 * kk, lane);
+                    kf[a] = fr_row<false>(s.k + 16 * (ct0 + a) * LK, LK, 32 * kk, lane);
+                }
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) pacc[a][b] = mfma(qr[a], kf[b], pacc[a][b]);
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int rt = rt0 + a, ct = ct0 + b;
+                    const f32x4 acc = pacc[a][b];
+                    f32x4 pv;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int i = 16 * rt + 4 * g4 + jj, sc = 16 * ct + r16;
+                        pv[jj] = sc <= i ? acc[jj] * __expf(s.G[i] - s.G[sc]) : 0.f;
+                    }
+                    st_split(s.pH, s.pL, L64, 16 * rt, 16 * ct, pv, lane);
+                }
+            // dh' of chunk c (the hi / lo copy of dh in LDS, unchanged in this
+            // step) -> HBM as two bf16 planes [d][v], 16 bytes per thread and plane piece
+            if (own) {
+                bf16 *dst = reinterpret_cast<bf16 *>(p.dh_ws) + ((int64_t)(cbase + c) * p.Hv + j) * 2 * DK * DV + half * HVC;
+#pragma unroll
+                for (int i = 0; i < DK * HVC / 8 / NTD; ++i) {
+                    const int pc = td + i * NTD;
+                    const int row = pc / (HVC / 8), col = 8 * (pc % (HVC / 8));
+                    *reinterpret_cast<bf16x8 *>(dst + row * DV + col) = *reinterpret_cast<const bf16x8 *>(&s.hH[row * L64 + col]);
+                    *reinterpret_cast<bf16x8 *>(dst + DK * DV + row * DV + col) =
+                        *reinterpret_cast<const bf16x8 *>(&s.hL[row * L64 + col]);
+                }
+            }
+            __syncthreads();
+
+            // dv' = scale P^T dO + diag(rl) K dh: token row tiles rt0 + {0, 1},
+            // value column tiles ct0 + {0, 1}
+            f32x4 a1[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
+            f32x4 a2[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
+            if (!mmap) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    bf16x8 ph[2], pl[2], of[2];
+#pragma unroll
+                    for (int a = 0; a < 2; ++a) {
+                        ph[a] = fr_tr(s.pH + 16 * (rt0 + a), L64, 32 * kk, lane);
+                        pl[a] = fr_tr(s.pL + 16 * (rt0 + a), L64, 32 * kk, lane);
+                        of[a] = fr_tr(s.dO + 16 * (ct0 + a), L64, 32 * kk, lane);
+                    }
+#pragma unroll
+                    for (int a = 0; a < 2; ++a)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b) a1[a][b] = mm_pe(a1[a][b], ph[a], pl[a], of[b]);
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 kr[2], hf[2], hl[2];
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    kr[a] = fr_row<true>(s.k + 16 * (rt0 + a) * LK, LK, 32 * kk, lane);
+                    hf[a] = fr_tr(s.hH + 16 * (ct0 + a), L64, 32 * kk, lane);
+                    hl[a] = fr_tr(s.hL + 16 * (ct0 + a), L64, 32 * kk, lane);
+                }
+#pragma unroll
+                for (int a = 0; a < 2; ++a)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b) a2[a][b] = mm_ep(a2[a][b], kr[a], hf[b], hl[b]);
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int rt = rt0 + a, ct = ct0 + b;
+                    f32x4 x;
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int i = 16 * rt + 4 * g4 + jj;
+                        x[jj] = p.scale * a1[a][b][jj] + __expf(s.G[CH - 1] - s.G[i]) * a2[a][b][jj];
+                    }
+                    st_split(s.aH, s.aL, L64, 16 * rt, 16 * ct, x, lane);
+                }
+            __syncthreads();
+
+            if (own) {
+                // dv' of chunk c -> HBM as two bf16 planes [token][v] (hi, lo): the
+                // chunk-local kernel's split operands, 16 bytes per thread and plane
+                bf16 *dst = reinterpret_cast<bf16 *>(p.dvp_ws) + ((int64_t)(cbase + c) * p.Hv + j) * 2 * CH * DV + half * HVC;
+#pragma unroll
+                for (int i = 0; i < CH * HVC / 8 / NTD; ++i) {
+                    const int pc = td + i * NTD;
+                    const int row = pc / (HVC / 8), col = 8 * (pc % (HVC / 8));
+                    *reinterpret_cast<bf16x8 *>(dst + row * DV + col) = *reinterpret_cast<const bf16x8 *>(&s.aH[row * L64 + col]);
+                    *reinterpret_cast<bf16x8 *>(dst + CH * DV + row * DV + col) =
+                        *reinterpret_cast<const bf16x8 *>(&s.aL[row * L64 + col]);
+                }
+            }
+            if (c - 1 >= e.c_begin) {
+                store_chunk_dh(s, R, td);
+                if (c - 2 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c - 2, td);
+            }
+        }
+        return;
     }
-    if (c_last - 2 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c_last - 2, tid);
+
+    // dh at the start of the walk (waves 4-7): rows 16 (kt0 + t) + 4 g + jj, value column 16 ct + r
+    const int64_t sbase = ((int64_t)e.n * p.Hv + j) * DK * DV + half * HVC;
+    const int64_t wbase = ((int64_t)seg * p.Hv + j) * DK * DV + half * HVC;  // exact-CP workspace
+    f32x4 dh[2][4];
+    {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int d = 16 * (kt0 + t) + 4 * g4 + jj, v = 16 * ct + r16;
+                    float x = 0.f;
+                    if (from_end && p.dht) x = p.dht[sbase + (int64_t)d * DV + v];
+                    if (exact_start) x = p.ws_h[wbase + (int64_t)d * DV + v];
+                    if (mmap) x = (d == half * HVC + v) ? 1.f : 0.f;  // identity columns of this half
+                    dh[t][ct][jj] = x;
+                }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) st_split(s.hH, s.hL, L64, 16 * (kt0 + t), 16 * ct, dh[t][ct], lane);
+    }
     for (int c = c_last - 1; c >= e.c_begin; --c) {
-        const bool own = !pre && c < c_end;
         __syncthreads();  // chunk c's tiles in LDS; the previous dh update done
         const float gl = s.gam[CH - 1];
-
-        // W = T diag(beta gamma) K: key columns 16 w .., all token rows.  Only
-        // this wave reads these columns back (as the A operand of W^T dv'), and
-        // two stacked accumulator tiles are already that operand at the
-        // transposed-read k order, so W stays in registers (hi / lo).
-        bf16x8 wa[2], wl[2];
+        // W^T operand fragments: [key tile t][token k step]
+        bf16x8 wa[2][2], wl[2][2];
         {
-            bf16x8 bk[2];
+            // W = T diag(beta gamma) K: key columns of tiles kt0 + {0, 1}, all token
+            // rows.  Only this wave reads these columns back (as the A operand of
+            // W^T dv'), and two stacked accumulator tiles are already that operand
+            // at the transposed-read k order, so W stays in registers (hi / lo).
+            bf16x8 bk[2][2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) bk[kk] = fr_tr(s.k + 16 * wave, LK, 32 * kk, lane);
-            f32x4 wt[4];
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) bk[t][kk] = fr_tr(s.k + 16 * (kt0 + t), LK, 32 * kk, lane);
+            f32x4 wt[2][4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                wt[rt] = f32x4{};
+                bf16x8 th[2], tl[2];
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    wt[rt] = mm_pe(wt[rt], fr_row<true>(s.tH + 16 * rt * L64, L64, 32 * kk, lane),
-                                   fr_row<true>(s.tL + 16 * rt * L64, L64, 32 * kk, lane), bk[kk]);
-            }
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const float x[8] = {wt[2 * kk][0],     wt[2 * kk][1],     wt[2 * kk][2],     wt[2 * kk][3],
-                                    wt[2 * kk + 1][0], wt[2 * kk + 1][1], wt[2 * kk + 1][2], wt[2 * kk + 1][3]};
-                split8(x, wa[kk], wl[kk]);
-            }
-        }
-        // P = (Q K^T) o Gamma, s <= i: row tile w / 2, column tiles 2 (w % 2) + {0, 1}
-        // (both column tiles per k step: the Q rows are read once)
-        f32x4 pacc[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 qr = fr_row<false>(s.q + 16 * (wave >> 1) * LK, LK, 32 * kk, lane);
-#pragma unroll
-            for (int ct2 = 0; ct2 < 2; ++ct2)
-                pacc[ct2] = mfma(qr, fr_row<false>(s.k + 16 * (2 * (wave & 1) + ct2) * LK, LK, 32 * kk, lane), pacc[ct2]);
-        }
-#pragma unroll
-        for (int ct2 = 0; ct2 < 2; ++ct2) {
-            const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
-            const f32x4 acc = pacc[ct2];
-            f32x4 pv;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int i = 16 * rt + 4 * g4 + jj, sc = 16 * ct + r16;
-                pv[jj] = sc <= i ? acc[jj] * __expf(s.G[i] - s.G[sc]) : 0.f;
-            }
-            st_split(s.pH, s.pL, L64, 16 * rt, 16 * ct, pv, lane);
-        }
-        // dh' of chunk c (unchanged so far in this step) -> HBM
-        if (own) {
-            // the hi / lo copy of dh in LDS is dh' of chunk c: written out as two
-            // bf16 planes [d][v] (the chunk-local kernel's split operands), 16
-            // bytes per thread and plane row piece
-            bf16 *dst = reinterpret_cast<bf16 *>(p.dh_ws) + ((int64_t)(cbase + c) * p.Hv + j) * 2 * DK * DV + half * HVC;
-#pragma unroll
-            for (int i = 0; i < DK * HVC / 8 / NT; ++i) {
-                const int pc = tid + i * NT;
-                const int row = pc / (HVC / 8), col = 8 * (pc % (HVC / 8));
-                *reinterpret_cast<bf16x8 *>(dst + row * DV + col) = *reinterpret_cast<const bf16x8 *>(&s.hH[row * L64 + col]);
-                *reinterpret_cast<bf16x8 *>(dst + DK * DV + row * DV + col) =
-                    *reinterpret_cast<const bf16x8 *>(&s.hL[row * L64 + col]);
-            }
-        }
-        __syncthreads();
-
-        // dv' = scale P^T dO + diag(rl) K dh: token row tile w / 2, value column tiles 2 (w % 2) + {0, 1};
-        // and this wave's key rows of Q^T diag(gamma) dO
-        // (the P^T and K fragments of row tile w / 2 are read once for both column tiles)
-        f32x4 a1t[2] = {f32x4{}, f32x4{}}, a2t[2] = {f32x4{}, f32x4{}};
-        if (!mmap) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 ph = fr_tr(s.pH + 16 * (wave >> 1), L64, 32 * kk, lane);
-                const bf16x8 pl = fr_tr(s.pL + 16 * (wave >> 1), L64, 32 * kk, lane);
-#pragma unroll
-                for (int ct2 = 0; ct2 < 2; ++ct2)
-                    a1t[ct2] = mm_pe(a1t[ct2], ph, pl, fr_tr(s.dO + 16 * (2 * (wave & 1) + ct2), L64, 32 * kk, lane));
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 kr = fr_row<true>(s.k + 16 * (wave >> 1) * LK, LK, 32 * kk, lane);
-#pragma unroll
-            for (int ct2 = 0; ct2 < 2; ++ct2) {
-                const int ct = 2 * (wave & 1) + ct2;
-                a2t[ct2] = mm_ep(a2t[ct2], kr, fr_tr(s.hH + 16 * ct, L64, 32 * kk, lane), fr_tr(s.hL + 16 * ct, L64, 32 * kk, lane));
-            }
-        }
-#pragma unroll
-        for (int ct2 = 0; ct2 < 2; ++ct2) {
-            const int rt = wave >> 1, ct = 2 * (wave & 1) + ct2;
-            const f32x4 a1 = a1t[ct2], a2 = a2t[ct2];
-            f32x4 x;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int i = 16 * rt + 4 * g4 + jj;
-                x[jj] = p.scale * a1[jj] + __expf(s.G[CH - 1] - s.G[i]) * a2[jj];
-            }
-            st_split(s.aH, s.aL, L64, 16 * rt, 16 * ct, x, lane);
-        }
-        f32x4 u[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-        if (!mmap) {
-            // (diag(gamma) Q)^T dO: this wave's key rows of Q^T (transposing
-            // reads, k = tokens in the transposed-read order) scaled per token
-            // by gamma and split hi / lo, against the exact dO tile (a split of
-            // diag(gamma) dO instead would double the LDS reads of every wave)
-            bf16x8 aqh[2], aql[2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 qf = fr_tr(s.q + 16 * wave, LK, 32 * kk, lane);
-                const f32x4 ga = *reinterpret_cast<const f32x4 *>(&s.gam[32 * kk + 4 * g4]);
-                const f32x4 gb = *reinterpret_cast<const f32x4 *>(&s.gam[32 * kk + 16 + 4 * g4]);
-                float f[8];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    f[e2] = (float)qf[e2] * ga[e2];
-                    f[4 + e2] = (float)qf[4 + e2] * gb[e2];
+                for (int kk = 0; kk < 2; ++kk) {
+                    th[kk] = fr_row<true>(s.tH + 16 * rt * L64, L64, 32 * kk, lane);
+                    tl[kk] = fr_row<true>(s.tL + 16 * rt * L64, L64, 32 * kk, lane);
                 }
-                split8(f, aqh[kk], aql[kk]);
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    wt[t][rt] = f32x4{};
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) wt[t][rt] = mm_pe(wt[t][rt], th[kk], tl[kk], bk[t][kk]);
+                }
             }
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    u[ct] = mm_pe(u[ct], aqh[kk], aql[kk], fr_tr(s.dO + 16 * ct, L64, 32 * kk, lane));
-            }
+                for (int kk = 0; kk < 2; ++kk) {
+                    const float x[8] = {wt[t][2 * kk][0],     wt[t][2 * kk][1],     wt[t][2 * kk][2],
+                                        wt[t][2 * kk][3],     wt[t][2 * kk + 1][0], wt[t][2 * kk + 1][1],
+                                        wt[t][2 * kk + 1][2], wt[t][2 * kk + 1][3]};
+                    split8(x, wa[t][kk], wl[t][kk]);
+                }
         }
         __syncthreads();
 
-        if (own) {
-            // dv' of chunk c -> HBM as two bf16 planes [token][v] (hi, lo): the
-            // chunk-local kernel's split operands, 16 bytes per thread and plane
-            bf16 *dst = reinterpret_cast<bf16 *>(p.dvp_ws) + ((int64_t)(cbase + c) * p.Hv + j) * 2 * CH * DV + half * HVC;
-#pragma unroll
-            for (int i = 0; i < CH * HVC / 8 / NT; ++i) {
-                const int pc = tid + i * NT;
-                const int row = pc / (HVC / 8), col = 8 * (pc % (HVC / 8));
-                *reinterpret_cast<bf16x8 *>(dst + row * DV + col) = *reinterpret_cast<const bf16x8 *>(&s.aH[row * L64 + col]);
-                *reinterpret_cast<bf16x8 *>(dst + CH * DV + row * DV + col) =
-                    *reinterpret_cast<const bf16x8 *>(&s.aL[row * L64 + col]);
-            }
-        }
-        // dh <- gamma_last dh + scale Q^T diag(gamma) dO - W^T dv'
+        f32x4 u[2][4];
         {
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-                f32x4 acc = f32x4{};
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    acc = mm_pp(acc, wa[kk], wl[kk], fr_tr(s.aH + 16 * ct, L64, 32 * kk, lane),
-                                fr_tr(s.aL + 16 * ct, L64, 32 * kk, lane));
-                dh[ct] = gl * dh[ct] + p.scale * u[ct] - acc;
-                st_split(s.hH, s.hL, L64, 16 * wave, 16 * ct, dh[ct], lane);
+                for (int ct = 0; ct < 4; ++ct) u[t][ct] = f32x4{};
+            if (!mmap) {
+                // (diag(gamma) Q)^T dO: this wave's key rows of Q^T (transposing
+                // reads, k = tokens in the transposed-read order) scaled per token
+                // by gamma and split hi / lo, against the exact dO tile
+                bf16x8 aqh[2][2], aql[2][2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const f32x4 ga = *reinterpret_cast<const f32x4 *>(&s.gam[32 * kk + 4 * g4]);
+                    const f32x4 gb = *reinterpret_cast<const f32x4 *>(&s.gam[32 * kk + 16 + 4 * g4]);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const bf16x8 qf = fr_tr(s.q + 16 * (kt0 + t), LK, 32 * kk, lane);
+                        float f[8];
+#pragma unroll
+                        for (int e2 = 0; e2 < 4; ++e2) {
+                            f[e2] = (float)qf[e2] * ga[e2];
+                            f[4 + e2] = (float)qf[4 + e2] * gb[e2];
+                        }
+                        split8(f, aqh[t][kk], aql[t][kk]);
+                    }
+                }
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const bf16x8 of = fr_tr(s.dO + 16 * ct, L64, 32 * kk, lane);
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) u[t][ct] = mm_pe(u[t][ct], aqh[t][kk], aql[t][kk], of);
+                    }
             }
         }
-        if (c - 1 >= e.c_begin) {
-            store_chunk_dh(s, R, tid);
-            if (c - 2 >= e.c_begin) load_chunk_dh(R, p, e, j, half, c - 2, tid);
+        __syncthreads();
+
+        {
+            // dh <- gamma_last dh + scale Q^T diag(gamma) dO - W^T dv' (each dv'
+            // fragment read once for both key tiles)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                f32x4 acc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const bf16x8 af = fr_tr(s.aH + 16 * ct, L64, 32 * kk, lane);
+                    const bf16x8 al = fr_tr(s.aL + 16 * ct, L64, 32 * kk, lane);
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) acc[t] = mm_pp(acc[t], wa[t][kk], wl[t][kk], af, al);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    dh[t][ct] = gl * dh[t][ct] + p.scale * u[t][ct] - acc[t];
+                    st_split(s.hH, s.hL, L64, 16 * (kt0 + t), 16 * ct, dh[t][ct], lane);
+                }
+            }
         }
     }
     if (pre) {
         float *dst = (mmap ? p.ws_m : p.ws_s) + wbase;
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) dst[(int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16] = dh[ct][jj];
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    dst[(int64_t)(16 * (kt0 + t) + 4 * g4 + jj) * DV + 16 * ct + r16] = dh[t][ct][jj];
     } else if (e.c_begin == 0 && p.dh0) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                p.dh0[sbase + (int64_t)(16 * wave + 4 * g4 + jj) * DV + 16 * ct + r16] = dh[ct][jj];
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    p.dh0[sbase + (int64_t)(16 * (kt0 + t) + 4 * g4 + jj) * DV + 16 * ct + r16] = dh[t][ct][jj];
     }
 }
 
